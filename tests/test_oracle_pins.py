@@ -1,0 +1,408 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each check compares the oracle with a library routine, a closed form, an
+invariant the method implies, or a second formulation.  The pages print no
+worked example or numeric value for this layer, so there are no page values
+to pin against; see tests/golden/README.md.
+
+The `check_*` helpers take the oracle module so that test_oracle_mutations.py
+can run them against copies with planted mistakes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.spatial.distance import cdist
+from scipy.special import expit
+
+import oracle.kvm_oracle as O
+from kvm_inputs import WORKLOADS, LayerConfig, make_inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def rand_seq(N, seed, d=64, clustered=0, scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    ell = rng.standard_normal(N)
+    if clustered:
+        cen = rng.standard_normal((clustered, d))
+        cen /= np.linalg.norm(cen, axis=1, keepdims=True)
+        k = cen[rng.integers(0, clustered, N)] + 0.05 * rng.standard_normal((N, d))
+    else:
+        k = rng.standard_normal((N, d))
+    return q * scale, k * scale, v, ell
+
+
+def rope_complex(x, pos, rope_dims=32, theta=10000.0):
+    """Independent RoPE formulation: pairs (j, j+half) as one complex number times e^{i*pos*f_j}."""
+    x = np.asarray(x, dtype=np.float64)
+    half = rope_dims // 2
+    z = x[:, :half] + 1j * x[:, half:rope_dims]
+    f = np.power(theta, -np.arange(half) / half)
+    z = z * np.exp(1j * np.outer(pos, f))
+    out = x.copy()
+    out[:, :half] = z.real
+    out[:, half:rope_dims] = z.imag
+    return out
+
+
+def sdpa(qm, km, vm, mask):
+    """torch scaled_dot_product_attention in float64 on the CPU."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    m = torch.from_numpy(mask)[None, None]
+    return F.scaled_dot_product_attention(t(qm), t(km), t(vm), attn_mask=m)[0, 0].numpy()
+
+
+# ---------------------------------------------------------------- gate
+
+def check_gate(mod):
+    x = np.linspace(-30, 30, 241)
+    np.testing.assert_allclose(mod.gate(x), expit(x), rtol=1e-14, atol=1e-300)
+    assert mod.gate(-1e4) == 0.0 and mod.gate(1e4) == 1.0 and mod.gate(0.0) == 0.5
+    np.testing.assert_allclose(mod.gate(x) + mod.gate(-x), 1.0, atol=1e-15)
+
+
+def test_gate_is_logistic_sigmoid():
+    check_gate(O)
+
+
+# ---------------------------------------------------------------- RoPE
+
+def check_rope(mod):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((50, 64))
+    pos = rng.integers(0, 200000, 50)
+    np.testing.assert_allclose(mod.rope(x, pos), rope_complex(x, pos), rtol=0, atol=1e-9)
+    # relative-position property: <R_m q, R_n k> depends on m - n only
+    qv, kv = rng.standard_normal((1, 64)), rng.standard_normal((1, 64))
+    a = mod.rope(qv, [17])[0] @ mod.rope(kv, [5])[0]
+    b = mod.rope(qv, [1017])[0] @ mod.rope(kv, [1005])[0]
+    assert abs(a - b) < 1e-9
+    # non-rotary dims untouched, rotation preserves the norm, position 0 is the identity
+    np.testing.assert_array_equal(mod.rope(x, pos)[:, 32:], x[:, 32:])
+    np.testing.assert_allclose(np.linalg.norm(mod.rope(x, pos), axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    np.testing.assert_allclose(mod.rope(x, np.zeros(50)), x, atol=0)
+
+
+def test_rope_matches_complex_rotation():
+    check_rope(O)
+
+
+# ---------------------------------------------------------------- schedule
+
+def test_capacity_integer_ceiling_matches_float_formula():
+    for cfg in WORKLOADS:
+        p = O.Params.of(cfg)
+        for j in range(0, 600):
+            T = (j + 1) * cfg.chunk
+            if cfg.sched == "fixed":
+                want = cfg.max_slots
+            else:
+                want = math.ceil(cfg.alpha * math.sqrt(T))
+                if cfg.sched == "saturating":
+                    want = min(cfg.max_slots, want)
+            assert O.capacity(T, p) == want
+
+
+def test_schedule_row_counts_of_the_workloads():
+    # 350M-shaped workload: "~1.4k slots at end" after 253 absorbed chunks
+    p2 = O.Params.of(WORKLOADS[2])
+    s2 = O.schedule(253, p2)
+    assert s2[-1][2] == 1440
+    assert [m for (_, m, _) in s2[:5]] == [87, 37, 29, 25, 21]
+    assert s2[0][0] == 4 and all(s == 0 for (s, _, _) in s2[1:])
+    assert all(m >= 2 for (_, m, _) in s2[64:253])     # room for up to 2 planted keys per chunk
+    # tiny fixed-32 workload: 4 sinks + 28 appends in the first absorbed chunk, merge-only after
+    s0 = O.schedule(13, O.Params.of(WORKLOADS[0]))
+    assert s0[0] == (4, 28, 32) and all(r == (0, 0, 32) for r in s0[1:])
+    # 120M-shaped fixed 256
+    s1 = O.schedule(61, O.Params.of(WORKLOADS[1]))
+    assert [m for (_, m, _) in s1[:3]] == [124, 128, 0] and s1[-1][2] == 256
+    # long saturating workload: reaches 4096 once 65536 tokens are absorbed (absorbed chunk 255,
+    # first read by query chunk 258) and stays
+    s3 = O.schedule(509, O.Params.of(WORKLOADS[3]))
+    first_full = next(j for j, (_, _, r) in enumerate(s3) if r == 4096)
+    assert first_full == 255 and all(r == 4096 for (_, _, r) in s3[first_full:])
+    # decode workload: "~1k slots": 1012 rows after the 16384-token prefill (125 chunks), 1016 after one more
+    s4 = O.schedule(126, O.Params.of(WORKLOADS[4]))
+    assert s4[124][2] == 1012 and s4[125][2] == 1016
+
+
+# ---------------------------------------------------------------- I1: window covers everything
+
+def check_window_covers_all(mod):
+    N, C = 93, 16
+    p = mod.Params(chunk=C, window=96, n_sinks=2, sched="fixed", max_slots=8)
+    q, k, v, ell = rand_seq(N, 11)
+    res = mod.prefill(q, k, v, ell, p)
+    assert res.state.rows == 0 and np.all(res.kind == mod.KIND_NONE)
+    pos = np.arange(N)
+    qr, kr = rope_complex(q, pos), rope_complex(k, pos)
+    want = sdpa(qr, kr, v, np.tril(np.ones((N, N), dtype=bool)))
+    np.testing.assert_allclose(res.out, want, rtol=0, atol=1e-12)
+
+
+def test_I1_window_covering_the_sequence_is_causal_rope_attention():
+    check_window_covers_all(O)
+
+
+# ---------------------------------------------------------------- I2: append everything
+
+def check_append_everything(mod):
+    N, C, W, ns = 75, 8, 16, 3
+    p = mod.Params(chunk=C, window=W, n_sinks=ns, sched="fixed", max_slots=10_000)
+    q, k, v, ell = rand_seq(N, 12)
+    res = mod.prefill(q, k, v, ell, p)
+    n_abs = len(res.rows_after) * C
+    assert res.state.rows == n_abs and all(n == 1 for n in res.state.n)
+    pos = np.arange(N)
+    qr, kr = rope_complex(q, pos), rope_complex(k, pos)
+    kt = torch.from_numpy(k[:, 32:])
+    khat = np.hstack([np.zeros((N, 32)), F.layer_norm(kt, (32,), eps=1e-5).numpy()])
+    mask = np.zeros((N, 2 * N), dtype=bool)
+    for t in range(N):
+        lo = max(0, (t // C) * C - W)
+        mask[t, :lo] = True                 # absorbed tokens, one row each
+        mask[t, N + lo:N + t + 1] = True    # window
+    want = sdpa(qr, np.vstack([khat, kr]), np.vstack([v, v]), mask)
+    np.testing.assert_allclose(res.out, want, rtol=0, atol=1e-12)
+
+
+def test_I2_append_everything_is_dense_attention_on_normalised_keys():
+    check_append_everything(O)
+
+
+# ---------------------------------------------------------------- I3 / read form
+
+def check_read_form(mod):
+    N, C, W = 300, 8, 16
+    p = mod.Params(chunk=C, window=W, n_sinks=2, sched="fixed", max_slots=12)
+    q, k, v, ell = rand_seq(N, 13, clustered=5)
+    res = mod.prefill(q, k, v, ell, p)
+    st = res.state
+    K, V, n, rho, sink = st.arrays()
+    khat, vhat = mod.read_form(st, p)
+    want_k = F.layer_norm(torch.from_numpy(K / n[:, None]), (32,), eps=1e-5).numpy()
+    np.testing.assert_allclose(khat[:, 32:], want_k, rtol=0, atol=1e-12)
+    assert np.all(khat[:, :32] == 0)
+    np.testing.assert_allclose(np.linalg.norm(vhat, axis=1), rho, rtol=1e-13)
+    cosv = np.sum(vhat * V, axis=1) / (np.linalg.norm(vhat, axis=1) * np.linalg.norm(V, axis=1))
+    np.testing.assert_allclose(cosv, 1.0, atol=1e-13)
+    # rho is the norm of the creating token's value; a one-token row reads back that value
+    creators = {int(s): t for t, s in enumerate(res.slot) if res.kind[t] in (mod.KIND_SINK, mod.KIND_APPEND)}
+    for i in range(st.rows):
+        assert rho[i] == pytest.approx(np.linalg.norm(v[creators[i]]), rel=1e-15)
+        if n[i] == 1:
+            np.testing.assert_allclose(vhat[i], v[creators[i]], rtol=1e-13, atol=1e-14)
+
+
+def test_I3_read_form_is_layernorm_and_radius():
+    check_read_form(O)
+
+
+# ---------------------------------------------------------------- I4 I6 I7 I8: sums and counts
+
+def check_sums_and_counts(mod, ell_mode="random"):
+    N, C, W, ns = 260, 8, 16, 2
+    p = mod.Params(chunk=C, window=W, n_sinks=ns, sched="fixed", max_slots=12)
+    q, k, v, ell = rand_seq(N, 14, clustered=4)
+    if ell_mode == "closed":
+        ell = np.full(N, -1e4)
+    elif ell_mode == "open":
+        ell = np.full(N, 1e4)
+    res = mod.prefill(q, k, v, ell, p, keep_snapshots=True)
+    g = expit(ell)
+    kt = k[:, 32:]
+    for j, snap in enumerate(res.snapshots):
+        Kj, Vj, nj, _, sinkj = snap.arrays()
+        absorbed = (j + 1) * C
+        assert nj.sum() == absorbed                                 # I4: one count per absorbed token
+        assert np.all(nj[:ns] == 1) and np.all(sinkj[:ns]) and not np.any(sinkj[ns:])
+        np.testing.assert_array_equal(Kj[:ns], kt[:ns])             # I6: sinks never change
+        np.testing.assert_array_equal(Vj[:ns], v[:ns])
+        # every row = creator (ungated) + gated merged tokens, from the per-position log
+        mine = np.arange(N) < absorbed
+        for i in range(snap.rows):
+            members = np.where(mine & (res.slot == i))[0]
+            creators = [t for t in members if res.kind[t] != mod.KIND_MERGE]
+            merged = [t for t in members if res.kind[t] == mod.KIND_MERGE]
+            assert len(creators) == 1 and nj[i] == len(members)
+            wk = kt[creators[0]] + (g[merged, None] * kt[merged]).sum(axis=0)
+            wv = v[creators[0]] + (g[merged, None] * v[merged]).sum(axis=0)
+            np.testing.assert_allclose(Kj[i], wk, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(Vj[i], wv, rtol=1e-12, atol=1e-12)
+            if ell_mode == "closed":                                # I7: g = 0 exactly
+                np.testing.assert_array_equal(Kj[i], kt[creators[0]])
+            if ell_mode == "open":                                  # I8: g = 1, plain sums
+                np.testing.assert_allclose(Kj[i], kt[members].sum(axis=0), rtol=1e-12, atol=1e-12)
+    assert sum(1 for t in range(N) if res.kind[t] == mod.KIND_MERGE) > 100
+
+
+@pytest.mark.parametrize("mode", ["random", "closed", "open"])
+def test_I4_I6_I7_I8_sums_counts_sinks_gates(mode):
+    check_sums_and_counts(O, mode)
+
+
+# ---------------------------------------------------------------- assignment and append rules
+
+def check_assignment_rules(mod):
+    N, C, W, ns = 480, 16, 32, 2
+    p = mod.Params(chunk=C, window=W, n_sinks=ns, sched="sqrt", alpha=3)
+    q, k, v, ell = rand_seq(N, 15, clustered=9)
+    res = mod.prefill(q, k, v, ell, p, keep_snapshots=True)
+    kt = k[:, 32:]
+    sched = mod.schedule(len(res.snapshots), p)
+    for j in range(1, len(res.snapshots)):
+        prev = res.snapshots[j - 1]
+        Kp, _, _, _, sinkp = prev.arrays()
+        old = np.where(~sinkp)[0]
+        toks = np.arange(j * C, (j + 1) * C)
+        mu = (1.0 - cdist(kt[toks], Kp[old], metric="cosine")).max(axis=1)
+        app = toks[res.kind[toks] == mod.KIND_APPEND]
+        m = sched[j][1]
+        assert len(app) == m
+        order = np.lexsort((toks, mu))                  # smallest surprise first, then position
+        assert set(app) == set(toks[order[:m]])
+        # appended rows get consecutive new indices in position order
+        assert list(res.slot[app]) == list(range(prev.rows, prev.rows + m))
+        # merged tokens go to the best cosine among old non-sink rows and this chunk's new rows
+        cand_rows = list(old) + list(range(prev.rows, prev.rows + m))
+        cand_keys = np.vstack([Kp[old], kt[app]]) if m else Kp[old]
+        mer = toks[res.kind[toks] == mod.KIND_MERGE]
+        sims = 1.0 - cdist(kt[mer], cand_keys, metric="cosine")
+        for a, t in enumerate(mer):
+            best = np.flatnonzero(sims[a] >= sims[a].max() - 1e-12)
+            assert res.slot[t] == cand_rows[best[0]]
+
+
+def test_assignment_is_max_cosine_and_appends_are_least_similar():
+    check_assignment_rules(O)
+
+
+def test_I9_tie_rules():
+    # Chunk 0 (positions 0-3) is appended whole; chunk 1 (4-7) may append one row.
+    # Rows 1 and 2 are duplicates; token 4 duplicates them -> the lower row (1).
+    # Tokens 5 and 6 are identical and orthogonal to every row -> equal surprise,
+    # the earlier one (5) is appended; token 6 then merges into it (cosine 1).
+    # Token 7 has a zero key: cosine 0 to every candidate -> lowest candidate row (0).
+    p = O.Params(chunk=4, window=4, n_sinks=0, sched="fixed", max_slots=5)
+    N = 16
+    k = np.zeros((N, 64))
+    e = np.eye(32)
+    k[0, 32:] = e[0]
+    k[1, 32:] = e[1]
+    k[2, 32:] = e[1]
+    k[3, 32:] = e[2]
+    k[4, 32:] = e[1]
+    k[5, 32:] = e[5]
+    k[6, 32:] = e[5]
+    k[7, 32:] = 0.0
+    rng = np.random.default_rng(0)
+    q, v = rng.standard_normal((N, 64)), rng.standard_normal((N, 64))
+    res = O.prefill(q, k, v, np.zeros(N), p)
+    assert list(res.kind[:8]) == [1, 1, 1, 1, 2, 1, 2, 2]
+    assert list(res.slot[:8]) == [0, 1, 2, 3, 1, 4, 4, 0]
+
+
+# ---------------------------------------------------------------- attention with a live state
+
+def check_attention_with_state(mod):
+    N, C, W, ns = 200, 8, 16, 2
+    p = mod.Params(chunk=C, window=W, n_sinks=ns, sched="fixed", max_slots=10)
+    q, k, v, ell = rand_seq(N, 16, clustered=3)
+    res = mod.prefill(q, k, v, ell, p, keep_snapshots=True)
+    pos = np.arange(N)
+    qr, kr = rope_complex(q, pos), rope_complex(k, pos)
+    for c in range(W // C + 1, -(-N // C)):
+        snap = res.snapshots[c - W // C - 1]
+        K, V, n, rho, _ = snap.arrays()
+        x = torch.from_numpy(K / n[:, None])
+        kh = np.hstack([np.zeros((len(K), 32)), F.layer_norm(x, (32,), eps=1e-5).numpy()])
+        vh = rho[:, None] * V / np.linalg.norm(V, axis=1, keepdims=True)
+        rows = np.arange(c * C, min(N, (c + 1) * C))
+        keys = np.arange(c * C - W, rows[-1] + 1)
+        mask = np.ones((len(rows), len(K) + len(keys)), dtype=bool)
+        mask[:, len(K):] = keys[None, :] <= rows[:, None]
+        # the unrotated query scores the state; the rotated one the window
+        Ls = q[rows] @ kh.T
+        Lw = qr[rows] @ kr[keys].T
+        L = np.where(mask, np.hstack([Ls, Lw]), -np.inf) / 8.0
+        want = torch.softmax(torch.from_numpy(L), dim=1).numpy() @ np.vstack([vh, v[keys]])
+        np.testing.assert_allclose(res.out[rows], want, rtol=0, atol=1e-12)
+        # I10: the rotated query gives the same state logits
+        np.testing.assert_allclose(qr[rows] @ kh.T, Ls, rtol=0, atol=1e-12)
+
+
+def test_joint_softmax_over_state_and_window():
+    check_attention_with_state(O)
+
+
+# ---------------------------------------------------------------- I11 / I13
+
+CASES = [
+    dict(chunk=8, window=16, n_sinks=2, sched="sqrt", alpha=2),
+    dict(chunk=8, window=8, n_sinks=1, sched="fixed", max_slots=6),
+    dict(chunk=4, window=12, n_sinks=0, sched="saturating", alpha=3, max_slots=10),
+    dict(chunk=16, window=32, n_sinks=16, sched="sqrt", alpha=3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_I13_brute_force_agrees(case):
+    p = O.Params(**CASES[case])
+    for N, seed, clus in [(77, 21, 0), (130, 22, 4)]:
+        q, k, v, ell = rand_seq(N, seed + case, clustered=clus)
+        np.testing.assert_allclose(O.prefill(q, k, v, ell, p).out, O.brute_force(q, k, v, ell, p),
+                                   rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_I11_decode_reproduces_prefill(case):
+    p = O.Params(**CASES[case])
+    q, k, v, ell = rand_seq(97, 31 + case, clustered=3)
+    np.testing.assert_allclose(O.decode(q, k, v, ell, p), O.prefill(q, k, v, ell, p).out, rtol=0, atol=1e-12)
+    # continuing a prefill token by token
+    N0 = 48
+    res = O.prefill(q[:N0], k[:N0], v[:N0], ell[:N0], p)
+    dec = O.Decoder(p)
+    dec.prime(res, q[:N0], k[:N0], v[:N0], ell[:N0])
+    outs = np.array([dec.step(q[t], k[t], v[t], ell[t]) for t in range(N0, 97)])
+    np.testing.assert_allclose(outs, O.prefill(q, k, v, ell, p).out[N0:], rtol=0, atol=1e-12)
+
+
+def test_teacher_forcing_with_own_decisions_is_identity():
+    p = O.Params(**CASES[0])
+    q, k, v, ell = rand_seq(120, 41, clustered=3)
+    free = O.prefill(q, k, v, ell, p)
+    forced = {t: (int(free.kind[t]), int(free.slot[t])) for t in range(120) if free.kind[t] >= 0}
+    again = O.prefill(q, k, v, ell, p, forced=forced)
+    np.testing.assert_array_equal(again.out, free.out)
+    np.testing.assert_array_equal(again.slot, free.slot)
+
+
+# ---------------------------------------------------------------- I12 planted keys (workload generator)
+
+@pytest.mark.slow
+def test_I12_planted_keys_are_appended_350m_workload():
+    cfg = WORKLOADS[2]
+    inp = make_inputs(cfg, seqs=[3])
+    pp = inp.planted_pos[0]
+    assert len(pp) == 256 and len(np.unique(pp)) == 256
+    ch = pp // cfg.chunk
+    assert ch.min() >= 64 and ch.max() <= 252 and np.bincount(ch).max() <= 2
+    r = O.prefill(*(t[0].double().numpy() for t in (inp.q, inp.k, inp.v, inp.gate_logits)), O.Params.of(cfg))
+    assert np.all(r.kind[pp] == O.KIND_APPEND)
+    assert r.rows_after[-1] == 1440
+
+
+def test_generator_is_seeded_and_rounded():
+    cfg = WORKLOADS[1].replace(n_tokens=512, batch=1, heads=2)
+    a, b = make_inputs(cfg), make_inputs(cfg, seqs=[1])
+    assert a.q.dtype == torch.bfloat16 and a.gate_logits.dtype == torch.float32
+    assert torch.equal(a.k[1], b.k[0])
+    kn = a.k[0].float().numpy()
+    assert 0.9 < np.median(np.linalg.norm(kn, axis=1)) < 1.15
