@@ -1,0 +1,458 @@
+// C-ABI host library of the Key-Value Means attention layer (see include/kvm.h).
+//
+// Host responsibilities: argument checks (before anything is queued), the
+// data-independent size schedule, carving the caller's workspace, and queueing
+// the gfx950 kernels on the caller's stream.  No device allocation, no host
+// synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvm.h"
+#include "kvm_internal.h"
+
+struct kvm_state {
+  kvm_config cfg;
+  kvm::Dims m;
+  kvm::Dev d;
+  std::vector<int32_t> sched;      // 4 ints per absorbable chunk: sinks, appends, rows_before, idx_off
+  int64_t pos = 0;
+  int64_t absorbed = 0;
+  bool poisoned = false;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+kvm_status fail(kvm_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+// Smallest integer r with r*r >= x.
+uint64_t ceil_sqrt_u64(uint64_t x) {
+  uint64_t r = (uint64_t)std::sqrt((long double)x);
+  while (r > 0 && r * r > x) --r;
+  while ((r + 1) * (r + 1) <= x) ++r;
+  return r * r == x ? r : r + 1;
+}
+
+// Rows the schedule wants (sinks included) once T tokens have been absorbed.
+int64_t capacity(const kvm_config& c, int64_t T) {
+  if (c.sched == KVM_SCHED_FIXED) return c.max_slots;
+  const uint64_t a = (uint64_t)c.alpha;
+  const int64_t s = (int64_t)ceil_sqrt_u64(a * a * (uint64_t)T);
+  if (c.sched == KVM_SCHED_SQRT) return s;
+  return s < c.max_slots ? s : c.max_slots;
+}
+
+int64_t max_absorbable_chunks(const kvm_config& c) {
+  const int64_t n_chunks = (c.max_tokens + c.chunk - 1) / c.chunk;
+  const int64_t j = n_chunks - c.window / c.chunk - 1;
+  return j > 0 ? j : 0;
+}
+
+// Per absorbed chunk j: sinks created, rows appended, rows before.
+void build_schedule(const kvm_config& c, int64_t n, std::vector<int32_t>& sinks, std::vector<int32_t>& app,
+                    std::vector<int32_t>& before) {
+  sinks.resize(n);
+  app.resize(n);
+  before.resize(n);
+  int64_t rows = 0, nsink = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    before[j] = (int32_t)rows;
+    int64_t cand = c.chunk;
+    const int64_t sk = std::min<int64_t>(c.n_sinks - nsink, cand);
+    nsink += sk;
+    rows += sk;
+    cand -= sk;
+    int64_t m = capacity(c, (j + 1) * (int64_t)c.chunk) - rows;
+    if (m < 0) m = 0;
+    if (m > cand) m = cand;
+    rows += m;
+    sinks[j] = (int32_t)sk;
+    app[j] = (int32_t)m;
+  }
+}
+
+kvm_status validate(const kvm_config* c) {
+  if (!c) return fail(KVM_E_INVALID_ARG, "config is NULL");
+  if (c->batch < 1 || c->heads < 1) return fail(KVM_E_INVALID_ARG, "batch and heads must be >= 1");
+  if ((int64_t)c->batch * c->heads > (1 << 20)) return fail(KVM_E_INVALID_ARG, "batch*heads exceeds 2^20");
+  if (c->head_dim != 64) return fail(KVM_E_INVALID_ARG, "head_dim must be 64");
+  if (c->rope_dims != 32) return fail(KVM_E_INVALID_ARG, "rope_dims must be 32");
+  if (c->chunk != 32 && c->chunk != 64 && c->chunk != 128 && c->chunk != 256)
+    return fail(KVM_E_INVALID_ARG, "chunk must be 32, 64, 128 or 256");
+  if (c->window <= 0 || c->window % c->chunk != 0) return fail(KVM_E_INVALID_ARG, "window must be a positive multiple of chunk");
+  if (c->window > (1 << 20)) return fail(KVM_E_INVALID_ARG, "window exceeds 2^20");
+  if (c->n_sinks < 0 || c->n_sinks > c->chunk) return fail(KVM_E_INVALID_ARG, "n_sinks must be in [0, chunk]");
+  if (c->sched == KVM_SCHED_FIXED) {
+    if (c->max_slots < 1) return fail(KVM_E_INVALID_ARG, "fixed schedule needs max_slots >= 1");
+  } else if (c->sched == KVM_SCHED_SQRT || c->sched == KVM_SCHED_SATURATING) {
+    if (c->alpha < 1 || c->alpha > 4096) return fail(KVM_E_INVALID_ARG, "alpha must be in [1, 4096]");
+    if (c->sched == KVM_SCHED_SATURATING && c->max_slots < 1)
+      return fail(KVM_E_INVALID_ARG, "saturating schedule needs max_slots >= 1");
+  } else {
+    return fail(KVM_E_INVALID_ARG, "unknown schedule");
+  }
+  if (c->max_tokens < 1 || c->max_tokens > ((int64_t)1 << 31) - 1)
+    return fail(KVM_E_INVALID_ARG, "max_tokens must be in [1, 2^31)");
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(KVM_E_INVALID_ARG, "rope_theta must be > 0");
+  if (!(c->ln_eps >= 0.f) || !std::isfinite(c->ln_eps)) return fail(KVM_E_INVALID_ARG, "ln_eps must be >= 0");
+  if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
+    return fail(KVM_E_INVALID_ARG, "softmax_scale must be >= 0");
+  if (c->dtype != KVM_F32 && c->dtype != KVM_BF16) return fail(KVM_E_INVALID_ARG, "dtype must be KVM_F32 or KVM_BF16");
+  if (c->flags & ~KVM_FLAG_TRACE) return fail(KVM_E_INVALID_ARG, "unknown flag bits");
+  // Every merged token needs a candidate row: the first chunk with non-sink
+  // tokens must be allowed to append at least one row.
+  const int64_t J = max_absorbable_chunks(*c);
+  const int64_t jfirst = c->n_sinks == c->chunk ? 1 : 0;
+  if (J > jfirst && capacity(*c, (jfirst + 1) * (int64_t)c->chunk) <= c->n_sinks)
+    return fail(KVM_E_INVALID_ARG, "schedule leaves no non-sink row for the first merged tokens (capacity <= n_sinks)");
+  return KVM_OK;
+}
+
+struct Plan {
+  kvm::Dims m{};
+  std::vector<int32_t> sched;  // 4 per chunk
+  // byte offsets
+  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, rmax, idx, tslot, tkind, ring_k, ring_v,
+      ring_l, rope_cos, rope_sin, sch, nver, part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+kvm_status plan(const kvm_config* c, Plan& p) {
+  kvm_status st = validate(c);
+  if (st != KVM_OK) return st;
+  const int64_t J = max_absorbable_chunks(*c);
+  std::vector<int32_t> sk, app, before;
+  build_schedule(*c, J, sk, app, before);
+  int64_t S_cap = 0, idx_total = 0;
+  p.sched.assign((size_t)J * 4, 0);
+  for (int64_t j = 0; j < J; ++j) {
+    const int64_t after = (int64_t)before[j] + sk[j] + app[j];
+    p.sched[4 * j + 0] = sk[j];
+    p.sched[4 * j + 1] = app[j];
+    p.sched[4 * j + 2] = before[j];
+    p.sched[4 * j + 3] = (int32_t)idx_total;
+    idx_total += after;
+    if (after > S_cap) S_cap = after;
+    if (idx_total >= ((int64_t)1 << 31)) return fail(KVM_E_INVALID_ARG, "index lists exceed 2^31 entries; lower max_tokens");
+  }
+  if (S_cap > (1 << 22)) return fail(KVM_E_INVALID_ARG, "state would exceed 2^22 rows");
+  kvm::Dims& m = p.m;
+  m.BH = c->batch * c->heads;
+  m.C = c->chunk;
+  m.W = c->window;
+  m.R = c->window + c->chunk;
+  m.ns = c->n_sinks;
+  m.S_cap = (int)S_cap;
+  m.J_cap = (int)J;
+  m.V_cap = J * c->chunk;
+  m.idx_total = idx_total;
+  m.max_tokens = c->max_tokens;
+  m.n_seg_max = (int)((S_cap + kvm::kDecSeg - 1) / kvm::kDecSeg + (m.R + kvm::kDecSeg - 1) / kvm::kDecSeg);
+  m.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
+  m.ln_eps = c->ln_eps;
+  m.bf16 = c->dtype == KVM_BF16;
+  m.trace = (c->flags & KVM_FLAG_TRACE) ? 1 : 0;
+  const size_t es = m.bf16 ? 2 : 4;
+  const size_t BH = (size_t)m.BH, S = (size_t)S_cap;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  p.key_sum = take(BH * S * 32 * 4);
+  p.val_sum = take(BH * S * 64 * 4);
+  p.count = take(BH * S * 4);
+  p.rho = take(BH * S * 4);
+  p.unit = take(BH * S * 128);
+  p.kread = take(BH * S * 32 * es);
+  p.vread = take(BH * S * 64 * es);
+  p.pkey = take(BH * (size_t)m.V_cap * 32 * es);
+  p.pval = take(BH * (size_t)m.V_cap * 64 * es);
+  p.prho = take(BH * (size_t)m.V_cap * 4);
+  p.rmax = take(BH * (size_t)J * 4);
+  p.idx = take(BH * (size_t)idx_total * 4);
+  p.tslot = take(m.trace ? BH * (size_t)c->max_tokens * 4 : 0);
+  p.tkind = take(m.trace ? BH * (size_t)c->max_tokens : 0);
+  p.ring_k = take(BH * (size_t)m.R * 64 * es);
+  p.ring_v = take(BH * (size_t)m.R * 64 * es);
+  p.ring_l = take(BH * (size_t)m.R * 4);
+  p.rope_cos = take((size_t)c->max_tokens * 16 * 4);
+  p.rope_sin = take((size_t)c->max_tokens * 16 * 4);
+  p.sch = take((size_t)J * 16);
+  p.nver = take(BH * 4);
+  p.part = take(BH * (size_t)m.n_seg_max * kvm::kPartStride * 4);
+  p.total = off;
+  return KVM_OK;
+}
+
+kvm_status hip_fail(kvm_state* st, hipError_t e, const char* what) {
+  if (st) st->poisoned = true;
+  return fail(KVM_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int rows_after(const kvm_state* st, int64_t j) {
+  if (j < 0) return 0;
+  const int32_t* s = &st->sched[(size_t)j * 4];
+  return s[0] + s[1] + s[2];
+}
+
+}  // namespace
+
+extern "C" {
+
+kvm_status kvm_workspace_bytes(const kvm_config* cfg, size_t* bytes) {
+  try {
+    if (!bytes) return fail(KVM_E_INVALID_ARG, "bytes is NULL");
+    Plan p;
+    kvm_status s = plan(cfg, p);
+    if (s != KVM_OK) return s;
+    *bytes = p.total;
+    return KVM_OK;
+  } catch (...) {
+    return fail(KVM_E_INVALID_ARG, "host allocation failed");
+  }
+}
+
+kvm_status kvm_schedule(const kvm_config* cfg, int64_t n_chunks, int32_t* sinks, int32_t* appends, int32_t* rows) {
+  try {
+    kvm_status s = validate(cfg);
+    if (s != KVM_OK) return s;
+    if (n_chunks < 0 || n_chunks > (1 << 26)) return fail(KVM_E_INVALID_ARG, "n_chunks out of range");
+    std::vector<int32_t> sk, app, before;
+    build_schedule(*cfg, n_chunks, sk, app, before);
+    for (int64_t j = 0; j < n_chunks; ++j) {
+      if (sinks) sinks[j] = sk[j];
+      if (appends) appends[j] = app[j];
+      if (rows) rows[j] = before[j] + sk[j] + app[j];
+    }
+    return KVM_OK;
+  } catch (...) {
+    return fail(KVM_E_INVALID_ARG, "host allocation failed");
+  }
+}
+
+kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t workspace_bytes, void* stream,
+                            kvm_state** out) {
+  try {
+    if (!out) return fail(KVM_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    Plan p;
+    kvm_status s = plan(cfg, p);
+    if (s != KVM_OK) return s;
+    if (!d_workspace) return fail(KVM_E_INVALID_ARG, "workspace is NULL");
+    if (!aligned(d_workspace, 256)) return fail(KVM_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < p.total)
+      return fail(KVM_E_WORKSPACE, "workspace too small: need " + std::to_string(p.total) + " bytes");
+    kvm_state* st = new (std::nothrow) kvm_state();
+    if (!st) return fail(KVM_E_INVALID_ARG, "host allocation failed");
+    st->cfg = *cfg;
+    st->m = p.m;
+    st->sched = std::move(p.sched);
+    char* b = reinterpret_cast<char*>(d_workspace);
+    kvm::Dev& d = st->d;
+    d.key_sum = reinterpret_cast<float*>(b + p.key_sum);
+    d.val_sum = reinterpret_cast<float*>(b + p.val_sum);
+    d.count = reinterpret_cast<int*>(b + p.count);
+    d.rho = reinterpret_cast<float*>(b + p.rho);
+    d.unit = b + p.unit;
+    d.kread = b + p.kread;
+    d.vread = b + p.vread;
+    d.pkey = b + p.pkey;
+    d.pval = b + p.pval;
+    d.prho = reinterpret_cast<float*>(b + p.prho);
+    d.rmax = reinterpret_cast<float*>(b + p.rmax);
+    d.idx = reinterpret_cast<int*>(b + p.idx);
+    d.tslot = reinterpret_cast<int*>(b + p.tslot);
+    d.tkind = reinterpret_cast<uint8_t*>(b + p.tkind);
+    d.ring_k = b + p.ring_k;
+    d.ring_v = b + p.ring_v;
+    d.ring_l = reinterpret_cast<float*>(b + p.ring_l);
+    d.rope_cos = reinterpret_cast<float*>(b + p.rope_cos);
+    d.rope_sin = reinterpret_cast<float*>(b + p.rope_sin);
+    d.sched = reinterpret_cast<int4*>(b + p.sch);
+    d.nver = reinterpret_cast<int*>(b + p.nver);
+    d.part = reinterpret_cast<float*>(b + p.part);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemsetAsync(d.nver, 0, (size_t)st->m.BH * 4, hs);
+    if (e == hipSuccess && st->m.trace) {
+      e = hipMemsetAsync(d.tslot, 0xFF, (size_t)st->m.BH * cfg->max_tokens * 4, hs);
+      if (e == hipSuccess) e = hipMemsetAsync(d.tkind, 0xFF, (size_t)st->m.BH * cfg->max_tokens, hs);
+    }
+    if (e == hipSuccess && !st->sched.empty())
+      e = hipMemcpyAsync(d.sched, st->sched.data(), st->sched.size() * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = kvm::launch_init(st->m, d, (double)cfg->rope_theta, hs);
+    if (e != hipSuccess) {
+      delete st;
+      return fail(KVM_E_HIP, std::string("state initialisation: ") + hipGetErrorString(e));
+    }
+    *out = st;
+    return KVM_OK;
+  } catch (...) {
+    return fail(KVM_E_INVALID_ARG, "host allocation failed");
+  }
+}
+
+kvm_status kvm_state_destroy(kvm_state* st) {
+  delete st;
+  return KVM_OK;
+}
+
+kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* v, const float* gate_logits, void* out,
+                       int64_t n_tokens, void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  if (n_tokens < 0) return fail(KVM_E_INVALID_ARG, "n_tokens < 0");
+  if (n_tokens == 0) return KVM_OK;
+  if (!q || !k || !v || !gate_logits || !out) return fail(KVM_E_INVALID_ARG, "NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
+  const kvm::Dims& m = st->m;
+  if (st->pos % m.C != 0) return fail(KVM_E_STATE, "prefill must start at a multiple of chunk");
+  if (st->pos + n_tokens > m.max_tokens) return fail(KVM_E_CAPACITY, "prefill would pass max_tokens");
+  const size_t bytes = (size_t)m.BH * (size_t)n_tokens * 64 * (m.bf16 ? 2 : 4);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return fail(KVM_E_INVALID_ARG, "out aliases an input");
+  const int64_t p0 = st->pos, e = p0 + n_tokens;
+  const int64_t c_first = p0 / m.C, c_last = (e - 1) / m.C;
+  int64_t need = c_last - m.W / m.C;  // chunks the last query chunk needs absorbed
+  if (need < 0) need = 0;
+  const int64_t a1 = need > st->absorbed ? need : st->absorbed;
+  if (a1 > m.J_cap) return fail(KVM_E_CAPACITY, "absorption would pass the workspace's chunk capacity");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  kvm::Src src{q, k, v, gate_logits, p0, n_tokens};
+  hipError_t err = kvm::launch_scan(m, st->d, src, (int)st->absorbed, (int)a1, hs);
+  if (err != hipSuccess) return hip_fail(st, err, "scan launch");
+  err = kvm::launch_attn(m, st->d, src, c_first, (int)(c_last - c_first + 1), e, out, hs);
+  if (err != hipSuccess) return hip_fail(st, err, "attention launch");
+  const int64_t from = e - m.R > p0 ? e - m.R : p0;
+  err = kvm::launch_ring_fill(m, st->d, src, from, e, hs);
+  if (err != hipSuccess) return hip_fail(st, err, "ring launch");
+  st->pos = e;
+  st->absorbed = a1;
+  return KVM_OK;
+}
+
+kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const void* v, const float* gate_logits,
+                           void* out, void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  if (!q || !k || !v || !gate_logits || !out) return fail(KVM_E_INVALID_ARG, "NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
+  const kvm::Dims& m = st->m;
+  const int64_t t = st->pos;
+  if (t + 1 > m.max_tokens) return fail(KVM_E_CAPACITY, "decode would pass max_tokens");
+  const size_t bytes = (size_t)m.BH * 64 * (m.bf16 ? 2 : 4);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return fail(KVM_E_INVALID_ARG, "out aliases an input");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  int64_t absorbed = st->absorbed;
+  if (t % m.C == 0 && t >= m.W + m.C) {
+    const int64_t j = (t - m.W - m.C) / m.C;
+    if (j != absorbed || j >= m.J_cap) return fail(KVM_E_STATE, "absorbed chunk count out of step with position");
+    kvm::Src src{nullptr, nullptr, nullptr, nullptr, t, 0};  // every position < t comes from the ring
+    hipError_t err = kvm::launch_scan(m, st->d, src, (int)j, (int)j + 1, hs);
+    if (err != hipSuccess) return hip_fail(st, err, "decode absorb launch");
+    absorbed = j + 1;
+  }
+  hipError_t err = kvm::launch_decode_ring(m, st->d, k, v, gate_logits, t, hs);
+  if (err != hipSuccess) return hip_fail(st, err, "decode ring launch");
+  err = kvm::launch_decode_attn(m, st->d, q, t, rows_after(st, absorbed - 1), out, hs);
+  if (err != hipSuccess) return hip_fail(st, err, "decode attention launch");
+  st->pos = t + 1;
+  st->absorbed = absorbed;
+  return KVM_OK;
+}
+
+kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* stream) {
+  if (!st || !dst) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  const kvm::Dims& m = st->m;
+  if ((dst->trace_slot || dst->trace_kind) && !m.trace)
+    return fail(KVM_E_INVALID_ARG, "trace requested but the state was created without KVM_FLAG_TRACE");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const size_t BH = (size_t)m.BH, S = (size_t)m.S_cap, es = m.bf16 ? 2 : 4;
+  struct Copy {
+    void* to;
+    const void* from;
+    size_t bytes;
+  } copies[] = {
+      {dst->key_sum, st->d.key_sum, BH * S * 32 * 4},
+      {dst->val_sum, st->d.val_sum, BH * S * 64 * 4},
+      {dst->count, st->d.count, BH * S * 4},
+      {dst->rho, st->d.rho, BH * S * 4},
+      {dst->key_read, st->d.kread, BH * S * 32 * es},
+      {dst->val_read, st->d.vread, BH * S * 64 * es},
+      {dst->trace_slot, st->d.tslot, BH * (size_t)m.max_tokens * 4},
+      {dst->trace_kind, st->d.tkind, BH * (size_t)m.max_tokens},
+  };
+  for (const Copy& c : copies) {
+    if (!c.to || c.bytes == 0) continue;
+    hipError_t e = hipMemcpyAsync(c.to, c.from, c.bytes, hipMemcpyDefault, hs);
+    if (e != hipSuccess) return hip_fail(const_cast<kvm_state*>(st), e, "state copy");
+  }
+  if (dst->n_rows) {
+    const int32_t r = rows_after(st, st->absorbed - 1);
+    for (size_t s = 0; s < BH; ++s) dst->n_rows[s] = r;  // host memory: the row count is host-side
+  }
+  return KVM_OK;
+}
+
+kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, void* val_read, float* rho_read,
+                             void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  if (j < 0 || j >= st->absorbed) return fail(KVM_E_INVALID_ARG, "chunk j has not been absorbed");
+  const int rows = rows_after(st, j);
+  const int64_t ioff = st->sched[(size_t)j * 4 + 3];
+  hipError_t e = kvm::launch_snapshot_gather(st->m, st->d, rows, ioff, key_read, val_read, rho_read,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(const_cast<kvm_state*>(st), e, "snapshot gather launch");
+  return KVM_OK;
+}
+
+kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info) {
+  if (!st || !info) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  info->position = st->pos;
+  info->absorbed_chunks = st->absorbed;
+  info->rows = rows_after(st, st->absorbed - 1);
+  info->max_rows = st->m.S_cap;
+  info->max_chunks = st->m.J_cap;
+  info->poisoned = st->poisoned ? 1 : 0;
+  return KVM_OK;
+}
+
+const char* kvm_status_str(kvm_status s) {
+  switch (s) {
+    case KVM_OK: return "KVM_OK";
+    case KVM_E_INVALID_ARG: return "KVM_E_INVALID_ARG";
+    case KVM_E_WORKSPACE: return "KVM_E_WORKSPACE";
+    case KVM_E_CAPACITY: return "KVM_E_CAPACITY";
+    case KVM_E_STATE: return "KVM_E_STATE";
+    case KVM_E_HIP: return "KVM_E_HIP";
+  }
+  return "KVM_E_UNKNOWN";
+}
+
+const char* kvm_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

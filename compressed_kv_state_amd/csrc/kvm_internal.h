@@ -1,0 +1,98 @@
+// Internal interface between the C-ABI host library (kvm_api.cpp) and the
+// gfx950 kernels (kvm_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvm {
+
+constexpr int kHeadDim = 64;   // head dimension
+constexpr int kRopeDims = 32;  // rotary dims [0,32)
+constexpr int kLive = 32;      // live state-key dims [32,64)
+constexpr int kDecSeg = 256;   // keys per decode split-K segment
+constexpr int kPartStride = 68;  // floats per decode partial: m, l, pad, pad, o[64]
+
+// Sizes fixed at state creation.
+struct Dims {
+  int BH;             // sequences (batch * heads)
+  int C;              // chunk
+  int W;              // window
+  int R;              // ring slots = W + C
+  int ns;             // sinks
+  int S_cap;          // most rows a state can reach
+  int J_cap;          // most chunks a state can absorb
+  int64_t V_cap;      // row versions per sequence (<= J_cap * C)
+  int64_t idx_total;  // index-list entries per sequence (sum over j of rows after chunk j)
+  int64_t max_tokens;
+  int n_seg_max;      // decode split-K segments per sequence
+  float scale;        // softmax scale
+  float ln_eps;
+  int bf16;           // 1: bf16 storage and MFMA; 0: fp32
+  int trace;          // 1: record per-token assignment
+};
+
+// Device regions carved from the caller's workspace.  Per-sequence arrays are
+// [BH][...] with sequence s = b*H + h outermost.  T (inputs, ring, outputs) is
+// float or bf16 by Dims::bf16.  RT, the read-form storage type, is float on the
+// fp32 path and fp16 on the bf16 path: every read-form quantity is bounded
+// (LayerNorm output |k| <= sqrt(31), unit value direction |u| <= 1), so fp16
+// keeps 3 more mantissa bits than bf16 at no range risk.
+struct Dev {
+  float* key_sum;    // [BH][S_cap][32] raw gated key sums (live dims)
+  float* val_sum;    // [BH][S_cap][64] raw gated value sums
+  int* count;        // [BH][S_cap]
+  float* rho;        // [BH][S_cap] read radius
+  void* unit;        // [BH][S_cap] x 128 B unit key direction: bf16 path [hi 32 | lo 32] bf16, fp32 path 32 f32
+  void* kread;       // [BH][S_cap][32] RT current read-form key (live dims)
+  void* vread;       // [BH][S_cap][64] RT current unit value direction u (read-form value = rho * u)
+  void* pkey;        // [BH][V_cap][32] RT read-form row versions: key
+  void* pval;        // [BH][V_cap][64] RT read-form row versions: unit value direction
+  float* prho;       // [BH][V_cap]       read-form row versions: radius
+  float* rmax;       // [BH][J_cap]       largest radius among the rows after chunk j
+  int* idx;          // [BH][idx_total] per absorbed chunk j: version id of each row after chunk j
+  int* tslot;        // [BH][max_tokens] trace: row created / merged into
+  uint8_t* tkind;    // [BH][max_tokens] trace: 0 sink 1 append 2 merge 255 none
+  void* ring_k;      // [BH][R][64] T  rotated keys of the last R positions (slot = pos % R)
+  void* ring_v;      // [BH][R][64] T
+  float* ring_l;     // [BH][R] gate logits
+  float* rope_cos;   // [max_tokens][16]
+  float* rope_sin;   // [max_tokens][16]
+  int4* sched;       // [J_cap] (sinks_j, appends_j, rows_before_j, idx_off_j)
+  int* nver;         // [BH] versions used
+  float* part;       // [BH][n_seg_max][kPartStride] decode partials
+};
+
+// Token source for a launch: positions >= p0 come from the call's inputs
+// ([BH][n_call][64] rows, gate [BH][n_call]); positions < p0 from the ring.
+struct Src {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* l;
+  int64_t p0;
+  int64_t n_call;
+};
+
+hipError_t launch_init(const Dims& m, const Dev& d, double rope_theta, hipStream_t st);
+// Absorb chunks [j_begin, j_end) for every sequence (sequential over j inside the kernel).
+hipError_t launch_scan(const Dims& m, const Dev& d, const Src& src, int j_begin, int j_end, hipStream_t st);
+// Attention for query chunks [c_begin, c_begin + n_q); queries at positions < end_pos; out rows
+// are [BH][n_call][64] indexed by position - src.p0.
+hipError_t launch_attn(const Dims& m, const Dev& d, const Src& src, int64_t c_begin, int n_q, int64_t end_pos,
+                       void* out, hipStream_t st);
+// Copy positions [from, to) of the call inputs into the ring (keys rotated).
+hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st);
+// Decode query at position t over `rows` state rows and the ring window; out [BH][64].
+hipError_t launch_decode_attn(const Dims& m, const Dev& d, const void* q, int64_t t, int rows, void* out,
+                              hipStream_t st);
+// Write decode token t (rotated key, value, gate logit) into ring slot t % R.
+hipError_t launch_decode_ring(const Dims& m, const Dev& d, const void* k, const void* v, const float* l, int64_t t,
+                              hipStream_t st);
+// Gather the read form of snapshot j (rows_j rows, version list at idx_off) into dense
+// key [BH][rows][32] RT, unit value [BH][rows][64] RT, radius [BH][rows] f32 (any may be null).
+hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t idx_off, void* key_out,
+                                  void* val_out, float* rho_out, hipStream_t st);
+
+}  // namespace kvm

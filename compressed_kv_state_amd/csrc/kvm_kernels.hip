@@ -1,0 +1,1296 @@
+// gfx950 (CDNA4) kernels of the Key-Value Means attention layer.
+//
+// Layer: [KVM abstract]; [KVM summary, Methodology; Core mechanisms 1-5].
+//   scan_kernel     absorbs window-overflow chunks into the state: sinks,
+//                   surprise top-m appends, winner-take-all cosine merge with
+//                   a scalar gate into raw sums and counts, and emits a new
+//                   read-form version of every row it touched.
+//   attn_kernel     one softmax over [state read form || window] per query
+//                   chunk, MFMA for Q.K^T and P.V, online softmax.
+//   dec_*           single-token decode: ring write, split-K attention, combine.
+//
+// Wave64 throughout.  MFMA lane layouts used (checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16: A lane l holds A[l%32][8*(l/32)+e], B lane l holds
+//     B[8*(l/32)+e][l%32] (e = 0..7); D lane l reg r is D[8*(r/4)+4*(l/32)+r%4][l%32].
+//   v_mfma_f32_32x32x2f32: A lane l holds A[l%32][l/32], B lane l holds B[l/32][l%32];
+//     D as above.
+// Any consistent permutation of the contraction index between A and B is
+// free; the kernels pick the one that makes each lane's loads contiguous.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+
+#include "kvm_internal.h"
+
+namespace kvm {
+namespace {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kInf = __builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T> struct Is;
+template <> struct Is<float> { static constexpr bool bf = false; };
+template <> struct Is<bf16> { static constexpr bool bf = true; };
+
+// Read-form storage type: fp16 on the bf16 path (bounded values), float on the fp32 path.
+template <typename T> struct Rd;
+template <> struct Rd<float> { using type = float; };
+template <> struct Rd<bf16> { using type = f16; };
+
+__device__ __forceinline__ float tof(float x) { return x; }
+__device__ __forceinline__ float tof(bf16 x) { return (float)x; }
+__device__ __forceinline__ float tof(f16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T fromf(float x) { return (T)x; }
+
+// Value held by the lane 32 positions away (l ^ 32).
+__device__ __forceinline__ uint32_t partner_u32(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float partner_f(float x) { return __uint_as_float(partner_u32(__float_as_uint(x))); }
+__device__ __forceinline__ int partner_i(int x) { return (int)partner_u32((uint32_t)x); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void copy16(void* dst, const void* src) {
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+__device__ __forceinline__ void zero16(void* dst) { *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0); }
+
+// Total order on floats (NaN included) so that a rank count always selects
+// exactly m items.
+__device__ __forceinline__ uint32_t ordered(float x) {
+  uint32_t b = __float_as_uint(x + 0.0f);  // -0 -> +0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// =====================================================================
+// Initialisation: RoPE table in double precision, rounded to fp32.
+// [KVM summary, Core mechanisms 4]: the window keeps RoPE.  Rotate-half
+// pairing (j, j+16), frequency theta^(-j/16), angle = position * frequency.
+// =====================================================================
+__global__ void rope_table_kernel(float* cosv, float* sinv, int64_t max_tokens, double theta) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= max_tokens * 16) return;
+  const int64_t pos = i >> 4;
+  const int j = (int)(i & 15);
+  const double f = pow(theta, -(double)j / 16.0);
+  const double a = (double)pos * f;
+  cosv[i] = (float)cos(a);
+  sinv[i] = (float)sin(a);
+}
+
+// =====================================================================
+// Scan: absorb overflowed chunks.
+// [KVM summary, Core mechanisms 1]: a chunk that overflows the window updates
+//   the state instead of being dropped.
+// [KVM summary, Core mechanisms 2]: each overflowed key goes to the single
+//   most similar state key (cosine), scaled by a data-dependent gate, into raw
+//   sums and counts ([KVM lay summary, smart merge]).
+// [KVM summary, Core mechanisms 3]: the least redundant overflowed tokens are
+//   appended as new rows; the count m_j comes from the size schedule.
+// [KVM summary, Core mechanisms 5]: the first tokens become protected sinks.
+// One workgroup per sequence, sequential over chunks.  Per chunk:
+//   1. stage keys (live dims), values and gates of the chunk in LDS;
+//   2. surprise: best cosine of every token against the non-sink rows that
+//      existed before the chunk (MFMA, see cos_best);
+//   3. append the m_j tokens of smallest (surprise, position);
+//   4. best cosine against the just-appended rows; assignment = better of the
+//      two (lower row on ties);
+//   5. sort merged tokens by (row, position); each touched or created row is
+//      updated by one thread in position order (deterministic, no atomics),
+//      and gets a new read-form version (LayerNorm key, radius-scaled value).
+// Cosines: argmax over rows of cos(k, K_i) = argmax of dot(k, K_i/|K_i|).  On
+// the bf16 path k is exact in bf16 and the unit direction U_i = K_i/|K_i| is
+// split into bf16 hi + lo (|U - hi - lo| <= 2^-18 |U|), so two bf16 MFMA
+// passes give dot(k, U_i) to ~1e-5 relative.  fp32 path: fp32 MFMA.
+// =====================================================================
+constexpr int kScanThreads = 256;
+constexpr int kSink = 0, kAppend = 1, kMerge = 2;
+
+template <typename T, int C>
+struct ScanSmem {
+  static constexpr int KST = Is<T>::bf ? 40 : 36;  // padded row stride (elements), 16-byte multiple
+  T k[C][KST];        // live key dims of the chunk's tokens
+  T v[C][64];         // values
+  float g[C];         // gate
+  float kn[C];        // |k live|
+  uint32_t mu[C];     // ordered surprise
+  float red_v[4][C];
+  int red_r[4][C];
+  float bE[C];
+  int rE[C];
+  float bA[C];
+  int rA[C];
+  int flag[C];
+  int arow[C];
+  int app_list[C];
+  int srt_tok[C];
+  int srt_row[C];
+  int seg_row[C];
+  int seg_start[C];
+  int seg_len[C];
+  int created_seg[C];
+  int wtot[4];
+  int nold;
+  uint32_t rmax_bits;  // largest radius of the rows created in this chunk (non-negative float bits)
+};
+
+// Best (largest) dot(k_t, U_i) over rows i in [rb, re) for every token t of the
+// chunk; ties to the lowest row.  Writes outv/outr[t] (-inf / INT_MAX if no row).
+// All threads of the block must call it.
+template <typename T, int C>
+__device__ void cos_best(ScanSmem<T, C>& sm, const char* unit, int rb, int re, float* outv, int* outr) {
+  constexpr int CT = C / 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
+  float bv[CT];
+  int br[CT];
+#pragma unroll
+  for (int tt = 0; tt < CT; ++tt) { bv[tt] = -kInf; br[tt] = INT_MAX; }
+  if (re > rb) {
+    const int ntile = (re - rb + 31) >> 5;
+    if constexpr (Is<T>::bf) {
+      // lane half h owns dims [16h, 16h+16) of every 32-dim key
+      bf16x8 bfr[CT][2];
+#pragma unroll
+      for (int tt = 0; tt < CT; ++tt) {
+        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&sm.k[32 * tt + jl][16 * h]);
+        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&sm.k[32 * tt + jl][16 * h + 8]);
+      }
+      const bf16* U = reinterpret_cast<const bf16*>(unit);
+      for (int tile = w; tile < ntile; tile += 4) {
+        const int row0 = rb + (tile << 5);
+        const int ri = min(row0 + jl, re - 1);
+        const bf16* u = U + (size_t)ri * 64;
+        const bf16x8 ah0 = *reinterpret_cast<const bf16x8*>(u + 16 * h);
+        const bf16x8 ah1 = *reinterpret_cast<const bf16x8*>(u + 16 * h + 8);
+        const bf16x8 al0 = *reinterpret_cast<const bf16x8*>(u + 32 + 16 * h);
+        const bf16x8 al1 = *reinterpret_cast<const bf16x8*>(u + 32 + 16 * h + 8);
+#pragma unroll
+        for (int tt = 0; tt < CT; ++tt) {
+          f32x16 acc = {};
+          acc = mfma_bf16(ah0, bfr[tt][0], acc);
+          acc = mfma_bf16(ah1, bfr[tt][1], acc);
+          acc = mfma_bf16(al0, bfr[tt][0], acc);
+          acc = mfma_bf16(al1, bfr[tt][1], acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row < re && acc[r] > bv[tt]) { bv[tt] = acc[r]; br[tt] = row; }
+          }
+        }
+      }
+    } else {
+      // fp32: step kk contracts dims kk and 16+kk (lane half h holds dim 16h+kk)
+      float bfr[CT][16];
+#pragma unroll
+      for (int tt = 0; tt < CT; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(sm.k[32 * tt + jl][16 * h + kk]);
+      const float* U = reinterpret_cast<const float*>(unit);
+      for (int tile = w; tile < ntile; tile += 4) {
+        const int row0 = rb + (tile << 5);
+        const int ri = min(row0 + jl, re - 1);
+        const float* u = U + (size_t)ri * 32 + 16 * h;
+        float a[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) a[kk] = u[kk];
+#pragma unroll
+        for (int tt = 0; tt < CT; ++tt) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int kk = 0; kk < 16; ++kk) acc = mfma_f32(a[kk], bfr[tt][kk], acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row0 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row < re && acc[r] > bv[tt]) { bv[tt] = acc[r]; br[tt] = row; }
+          }
+        }
+      }
+    }
+  }
+  // rows of a lane are visited in increasing order, so '>' kept the lowest row
+  // among equal values; combine the two lane halves and the waves the same way.
+#pragma unroll
+  for (int tt = 0; tt < CT; ++tt) {
+    const float ov = partner_f(bv[tt]);
+    const int orow = partner_i(br[tt]);
+    if (ov > bv[tt] || (ov == bv[tt] && orow < br[tt])) { bv[tt] = ov; br[tt] = orow; }
+    if (h == 0) { sm.red_v[w][32 * tt + jl] = bv[tt]; sm.red_r[w][32 * tt + jl] = br[tt]; }
+  }
+  __syncthreads();
+  for (int t = tid; t < C; t += kScanThreads) {
+    float v = sm.red_v[0][t];
+    int r = sm.red_r[0][t];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      const float ov = sm.red_v[ww][t];
+      const int orow = sm.red_r[ww][t];
+      if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
+    }
+    outv[t] = v;
+    outr[t] = r;
+  }
+  __syncthreads();
+}
+
+// Unit direction of a key sum, stored for the next cosine passes.
+template <typename T>
+__device__ __forceinline__ void store_unit(char* unit_row, const float (&K)[32]) {
+  float n2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) n2 = fmaf(K[i], K[i], n2);
+  const float inv = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
+  if constexpr (Is<T>::bf) {
+    bf16* u = reinterpret_cast<bf16*>(unit_row);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float x = K[i] * inv;
+      const bf16 hi = (bf16)x;
+      u[i] = hi;
+      u[32 + i] = (bf16)(x - (float)hi);
+    }
+  } else {
+    float* u = reinterpret_cast<float*>(unit_row);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) u[i] = K[i] * inv;
+  }
+}
+
+template <typename T, int C>
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src src, int j_begin, int j_end) {
+  using RT = typename Rd<T>::type;
+  constexpr int REL = 16 / sizeof(RT);     // read-form elements per 16-byte piece
+  __shared__ ScanSmem<T, C> sm;
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int EL = 16 / sizeof(T);       // elements per 16-byte piece
+  constexpr int KP = 32 / EL, VP = 64 / EL;
+
+  float* key_sum = d.key_sum + (size_t)s * m.S_cap * 32;
+  float* val_sum = d.val_sum + (size_t)s * m.S_cap * 64;
+  int* count = d.count + (size_t)s * m.S_cap;
+  float* rho = d.rho + (size_t)s * m.S_cap;
+  char* unit = reinterpret_cast<char*>(d.unit) + (size_t)s * m.S_cap * 128;
+  RT* kread = reinterpret_cast<RT*>(d.kread) + (size_t)s * m.S_cap * 32;
+  RT* vread = reinterpret_cast<RT*>(d.vread) + (size_t)s * m.S_cap * 64;
+  RT* pkey = reinterpret_cast<RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  RT* pval = reinterpret_cast<RT*>(d.pval) + (size_t)s * m.V_cap * 64;
+  float* prho = d.prho + (size_t)s * m.V_cap;
+  float* rmaxs = d.rmax + (size_t)s * m.J_cap;
+  float rmax_run = j_begin > 0 ? rmaxs[j_begin - 1] : 0.f;
+  int* idx = d.idx + (size_t)s * m.idx_total;
+  const T* ring_k = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
+  const T* ring_v = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
+  const float* ring_l = d.ring_l + (size_t)s * m.R;
+  int nver = d.nver[s];
+
+  for (int j = j_begin; j < j_end; ++j) {
+    const int4 sc = d.sched[j];
+    const int sinks = sc.x, mj = sc.y, R0 = sc.z;
+    const int64_t ioff = sc.w;
+    const int nc = sinks + mj;
+    const int rows_after = R0 + nc;
+    const int64_t P0 = (int64_t)j * C;
+    const bool from_in = P0 >= src.p0;
+
+    // ---- 1. stage the chunk
+    for (int i = tid; i < C * (KP + VP); i += kScanThreads) {
+      const int t = i / (KP + VP), p = i % (KP + VP);
+      const int64_t pos = P0 + t;
+      const T* krow;
+      const T* vrow;
+      if (from_in) {
+        const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
+        krow = reinterpret_cast<const T*>(src.k) + r * 64;
+        vrow = reinterpret_cast<const T*>(src.v) + r * 64;
+      } else {
+        const size_t r = (size_t)(pos % m.R);
+        krow = ring_k + r * 64;
+        vrow = ring_v + r * 64;
+      }
+      if (p < KP) copy16(&sm.k[t][p * EL], krow + 32 + p * EL);
+      else copy16(&sm.v[t][(p - KP) * EL], vrow + (p - KP) * EL);
+    }
+    for (int t = tid; t < C; t += kScanThreads) {
+      const int64_t pos = P0 + t;
+      const float ell = from_in ? src.l[(size_t)s * src.n_call + (size_t)(pos - src.p0)] : ring_l[pos % m.R];
+      // merge gate = logistic sigmoid of the logit
+      sm.g[t] = 1.0f / (1.0f + expf(-ell));
+    }
+    __syncthreads();
+    for (int t = tid; t < C; t += kScanThreads) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) { const float x = tof(sm.k[t][i]); n2 = fmaf(x, x, n2); }
+      sm.kn[t] = sqrtf(n2);
+    }
+    __syncthreads();
+
+    // ---- 2. surprise against the non-sink rows that existed before the chunk
+    const int eb = m.ns, ee = R0;
+    cos_best<T, C>(sm, unit, eb, ee, sm.bE, sm.rE);
+    for (int t = tid; t < C; t += kScanThreads) {
+      float mu;
+      if (ee > eb) mu = sm.kn[t] > 0.f ? sm.bE[t] / sm.kn[t] : 0.f;
+      else mu = -kInf;
+      sm.mu[t] = ordered(mu);
+    }
+    __syncthreads();
+
+    // ---- 3. append the m_j most surprising candidates (smallest surprise, then position)
+    for (int t = tid; t < C; t += kScanThreads) {
+      if (t < sinks) {
+        sm.flag[t] = kSink;
+      } else {
+        const uint32_t mt = sm.mu[t];
+        int rank = 0;
+        for (int u = sinks; u < C; ++u) {
+          const uint32_t mv = sm.mu[u];
+          rank += (mv < mt) || (mv == mt && u < t);
+        }
+        sm.flag[t] = rank < mj ? kAppend : kMerge;
+      }
+    }
+    __syncthreads();
+    for (int t = tid; t < C; t += kScanThreads) {
+      if (t < sinks) {
+        sm.arow[t] = R0 + t;
+      } else if (sm.flag[t] == kAppend) {
+        int cnt = 0;
+        for (int u = sinks; u < t; ++u) cnt += sm.flag[u] == kAppend;
+        sm.arow[t] = R0 + sinks + cnt;
+        sm.app_list[cnt] = t;
+        float K[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) K[i] = tof(sm.k[t][i]);
+        store_unit<T>(unit + (size_t)(R0 + sinks + cnt) * 128, K);
+      }
+    }
+    __syncthreads();
+
+    // ---- 4. best against the new rows, then the winner-take-all assignment
+    cos_best<T, C>(sm, unit, R0 + sinks, rows_after, sm.bA, sm.rA);
+    const int fallback = ee > eb ? eb : (R0 + sinks);
+    for (int t = tid; t < C; t += kScanThreads) {
+      if (sm.flag[t] == kMerge) {
+        const bool eok = sm.rE[t] != INT_MAX, aok = sm.rA[t] != INT_MAX;
+        int a;
+        if (eok && (!aok || sm.bE[t] >= sm.bA[t])) a = sm.rE[t];
+        else if (aok) a = sm.rA[t];
+        else a = fallback;
+        a = min(max(a, 0), rows_after - 1);
+        sm.arow[t] = a;
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. sort merged tokens by (row, position) and cut them into per-row segments
+    const int nm = C - nc;
+    for (int t = tid; t < C; t += kScanThreads) {
+      if (sm.flag[t] == kMerge) {
+        const int at = sm.arow[t];
+        int rank = 0;
+        for (int u = 0; u < C; ++u) {
+          if (sm.flag[u] != kMerge) continue;
+          const int au = sm.arow[u];
+          rank += (au < at) || (au == at && u < t);
+        }
+        sm.srt_tok[rank] = t;
+        sm.srt_row[rank] = at;
+      }
+    }
+    if (tid == 0) { sm.nold = 0; sm.rmax_bits = 0u; }
+    for (int c2 = tid; c2 < nc; c2 += kScanThreads) sm.created_seg[c2] = -1;
+    __syncthreads();
+    const bool head = tid < nm && (tid == 0 || sm.srt_row[tid] != sm.srt_row[tid - 1]);
+    const unsigned long long bal = __ballot(head);
+    const int within = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) sm.wtot[w] = __popcll(bal);
+    __syncthreads();
+    int off = 0, nseg = 0;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      off += ww < w ? sm.wtot[ww] : 0;
+      nseg += sm.wtot[ww];
+    }
+    if (head) {
+      sm.seg_row[off + within] = sm.srt_row[tid];
+      sm.seg_start[off + within] = tid;
+    }
+    __syncthreads();
+    for (int k = tid; k < nseg; k += kScanThreads) {
+      sm.seg_len[k] = (k + 1 < nseg ? sm.seg_start[k + 1] : nm) - sm.seg_start[k];
+      const int rk = sm.seg_row[k];
+      if (rk < R0 && (k + 1 == nseg || sm.seg_row[k + 1] >= R0)) sm.nold = k + 1;
+      if (rk >= R0 + sinks && rk < rows_after) sm.created_seg[rk - R0] = k;
+    }
+    // the new index list starts as a copy of the previous one
+    if (j > 0) {
+      const int64_t prev = d.sched[j - 1].w;
+      for (int i = tid; i < R0; i += kScanThreads) idx[ioff + i] = idx[prev + i];
+    }
+    __syncthreads();
+
+    // ---- 6. update every touched or created row, in increasing row order
+    const int nold = sm.nold;
+    const int nu = nold + nc;
+    for (int u = tid; u < nu; u += kScanThreads) {
+      int row, seg, creator = -1;
+      if (u < nold) {
+        row = sm.seg_row[u];
+        seg = u;
+      } else {
+        const int c2 = u - nold;
+        row = R0 + c2;
+        seg = sm.created_seg[c2];
+        creator = c2 < sinks ? c2 : sm.app_list[c2 - sinks];
+      }
+      alignas(16) float K[32];
+      alignas(16) float V[64];
+      int n;
+      float rh;
+      if (creator >= 0) {
+        // new row: the creating token, unscaled; its value norm is the read radius
+        float v2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) K[i] = tof(sm.k[creator][i]);
+#pragma unroll
+        for (int i = 0; i < 64; ++i) { V[i] = tof(sm.v[creator][i]); v2 = fmaf(V[i], V[i], v2); }
+        n = 1;
+        rh = sqrtf(v2);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; i += 4) *reinterpret_cast<float4*>(&K[i]) = *reinterpret_cast<const float4*>(key_sum + (size_t)row * 32 + i);
+#pragma unroll
+        for (int i = 0; i < 64; i += 4) *reinterpret_cast<float4*>(&V[i]) = *reinterpret_cast<const float4*>(val_sum + (size_t)row * 64 + i);
+        n = count[row];
+        rh = rho[row];
+      }
+      if (seg >= 0) {
+        const int b = sm.seg_start[seg], e = b + sm.seg_len[seg];
+        for (int r = b; r < e; ++r) {
+          const int t = sm.srt_tok[r];
+          const float gt = sm.g[t];
+#pragma unroll
+          for (int i = 0; i < 32; ++i) K[i] = fmaf(gt, tof(sm.k[t][i]), K[i]);
+#pragma unroll
+          for (int i = 0; i < 64; ++i) V[i] = fmaf(gt, tof(sm.v[t][i]), V[i]);
+          ++n;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) *reinterpret_cast<float4*>(key_sum + (size_t)row * 32 + i) = *reinterpret_cast<const float4*>(&K[i]);
+#pragma unroll
+      for (int i = 0; i < 64; i += 4) *reinterpret_cast<float4*>(val_sum + (size_t)row * 64 + i) = *reinterpret_cast<const float4*>(&V[i]);
+      count[row] = n;
+      rho[row] = rh;
+      store_unit<T>(unit + (size_t)row * 128, K);
+      if (creator >= 0) atomicMax(&sm.rmax_bits, __float_as_uint(rh));
+      // just-in-time read form ([KVM summary, Core mechanisms 2]): LayerNorm of
+      // K/n over the live dims (no affine); the value's direction u = V/|V|,
+      // read as rho * u (the radius fixed at creation).
+      const float invn = 1.0f / (float)n;
+      float mean = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) mean += K[i] * invn;
+      mean *= (1.0f / 32.0f);
+      float var = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
+      var *= (1.0f / 32.0f);
+      const float rs = 1.0f / sqrtf(var + m.ln_eps);
+      float v2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) v2 = fmaf(V[i], V[i], v2);
+      const float vs = v2 > 0.f ? 1.0f / sqrtf(v2) : 0.f;
+      const int ver = nver + u;
+      alignas(16) RT kh[32];
+      alignas(16) RT vh[64];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) kh[i] = fromf<RT>((K[i] * invn - mean) * rs);
+#pragma unroll
+      for (int i = 0; i < 64; ++i) vh[i] = fromf<RT>(V[i] * vs);
+#pragma unroll
+      for (int i = 0; i < 32; i += REL) {
+        copy16(pkey + (size_t)ver * 32 + i, &kh[i]);
+        copy16(kread + (size_t)row * 32 + i, &kh[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 64; i += REL) {
+        copy16(pval + (size_t)ver * 64 + i, &vh[i]);
+        copy16(vread + (size_t)row * 64 + i, &vh[i]);
+      }
+      prho[ver] = rh;
+      idx[ioff + row] = ver;
+    }
+    if (m.trace) {
+      int* tslot = d.tslot + (size_t)s * m.max_tokens;
+      uint8_t* tkind = d.tkind + (size_t)s * m.max_tokens;
+      for (int t = tid; t < C; t += kScanThreads) {
+        tslot[P0 + t] = sm.arow[t];
+        tkind[P0 + t] = (uint8_t)sm.flag[t];
+      }
+    }
+    nver += nu;
+    __syncthreads();
+    rmax_run = fmaxf(rmax_run, __uint_as_float(sm.rmax_bits));
+    if (tid == 0) rmaxs[j] = rmax_run;
+  }
+  if (tid == 0) d.nver[s] = nver;
+}
+
+// =====================================================================
+// Attention over [state read form || window], one workgroup per (sequence,
+// query chunk), one wave per 32 queries.
+// [KVM summary, Methodology]: a single softmax attention layer.
+// [KVM summary, Core mechanisms 4]: state keys have a zero rotary subspace and
+//   meet the unrotated query (only the 32 live dims contract); window keys are
+//   rotated and meet the rotated query.
+// S^T = K . Q^T is computed so that each lane owns one query: the softmax row
+// statistics are lane-local plus one exchange with lane l^32, and P^T comes
+// out of the D layout already in the B-operand layout of O^T = V^T . P^T.
+// =====================================================================
+template <typename T>
+struct AttnCfg {
+  static constexpr int KSTR = Is<T>::bf ? 72 : 68;  // sK row stride (elements)
+  static constexpr int VSTR = Is<T>::bf ? 68 : 65;  // sVt row stride (elements)
+};
+
+// RoPE of a pair (x, y) = (dim j, dim j+16).
+__device__ __forceinline__ void rot(float& x, float& y, float c, float s) {
+  const float a = x * c - y * s;
+  const float b = y * c + x * s;
+  x = a;
+  y = b;
+}
+
+// State tile: rows r0..r0+63 of the snapshot (version ids in idxl).  Stages the
+// read-form key (live dims) into sK, the unit value direction transposed into
+// sVt, and rho_i / rho_max into sRho.  Rows past S are zero.
+template <typename T, int NT>
+__device__ void stage_state(void* sKv, void* sVtv, float* sRho, const int* idxl, const typename Rd<T>::type* pk,
+                            const typename Rd<T>::type* pv, const float* prho, float inv_rmax, int r0, int S) {
+  using RT = typename Rd<T>::type;
+  RT* sK = reinterpret_cast<RT*>(sKv);
+  RT* sVt = reinterpret_cast<RT*>(sVtv);
+  constexpr int KSTR = AttnCfg<T>::KSTR, VSTR = AttnCfg<T>::VSTR;
+  constexpr int EL = 16 / sizeof(RT);
+  constexpr int KPC = 32 / EL;  // pieces per live key row
+  for (int task = threadIdx.x; task < 64 * KPC; task += NT) {
+    const int i = task / KPC, p = task % KPC;
+    const int r = r0 + i;
+    RT* dst = sK + i * KSTR + p * EL;
+    if (r < S) copy16(dst, pk + (size_t)idxl[r] * 32 + p * EL);
+    else zero16(dst);
+  }
+  constexpr int VG = 64 / EL;  // dim groups
+  for (int task = threadIdx.x; task < 32 * VG; task += NT) {
+    const int rp = task / VG, dg = task % VG;
+    const int i0 = 2 * rp;
+    alignas(16) RT a[EL];
+    alignas(16) RT b[EL];
+    const int r = r0 + i0;
+    if (r < S) copy16(a, pv + (size_t)idxl[r] * 64 + dg * EL);
+    else zero16(a);
+    if (r + 1 < S) copy16(b, pv + (size_t)idxl[r + 1] * 64 + dg * EL);
+    else zero16(b);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      RT* dst = sVt + (dg * EL + e) * VSTR + i0;
+      dst[0] = a[e];
+      dst[1] = b[e];
+    }
+  }
+  for (int i = threadIdx.x; i < 64; i += NT) {
+    const int r = r0 + i;
+    sRho[i] = r < S ? prho[idxl[r]] * inv_rmax : 0.f;
+  }
+}
+
+template <typename T, int NT>
+__device__ void stage_window(T* sK, T* sVt, int64_t k0, int64_t hi, const Src& src, int s, const T* ring_k,
+                             const T* ring_v, int R, const float* rc, const float* rsn) {
+  constexpr int KSTR = AttnCfg<T>::KSTR, VSTR = AttnCfg<T>::VSTR;
+  constexpr int EL = 16 / sizeof(T);
+  constexpr int RT_ = 16 / EL;      // rotary tasks per key (each: EL dims + their partners)
+  constexpr int PT = 32 / EL;       // plain pieces per key (dims 32..63)
+  constexpr int KT = RT_ + PT;
+  for (int task = threadIdx.x; task < 64 * KT; task += NT) {
+    const int i = task / KT, p = task % KT;
+    const int64_t pos = k0 + i;
+    T* row = sK + i * KSTR;
+    if (pos >= hi) {
+      if (p < RT_) { zero16(row + p * EL); zero16(row + 16 + p * EL); }
+      else zero16(row + 32 + (p - RT_) * EL);
+      continue;
+    }
+    if (pos >= src.p0) {
+      const T* kr = reinterpret_cast<const T*>(src.k) + ((size_t)s * src.n_call + (size_t)(pos - src.p0)) * 64;
+      if (p < RT_) {
+        alignas(16) T x[EL];
+        alignas(16) T y[EL];
+        copy16(x, kr + p * EL);
+        copy16(y, kr + 16 + p * EL);
+#pragma unroll
+        for (int e = 0; e < EL; ++e) {
+          float a = tof(x[e]), b = tof(y[e]);
+          rot(a, b, rc[pos * 16 + p * EL + e], rsn[pos * 16 + p * EL + e]);
+          x[e] = fromf<T>(a);
+          y[e] = fromf<T>(b);
+        }
+        copy16(row + p * EL, x);
+        copy16(row + 16 + p * EL, y);
+      } else {
+        copy16(row + 32 + (p - RT_) * EL, kr + 32 + (p - RT_) * EL);
+      }
+    } else {
+      const T* kr = ring_k + (size_t)(pos % R) * 64;  // ring keys are already rotated
+      if (p < RT_) { copy16(row + p * EL, kr + p * EL); copy16(row + 16 + p * EL, kr + 16 + p * EL); }
+      else copy16(row + 32 + (p - RT_) * EL, kr + 32 + (p - RT_) * EL);
+    }
+  }
+  constexpr int VG = 64 / EL;
+  for (int task = threadIdx.x; task < 32 * VG; task += NT) {
+    const int rp = task / VG, dg = task % VG;
+    const int i0 = 2 * rp;
+    alignas(16) T a[EL];
+    alignas(16) T b[EL];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t pos = k0 + i0 + q;
+      T* dstv = q ? b : a;
+      if (pos >= hi) { zero16(dstv); continue; }
+      const T* vr = pos >= src.p0
+                        ? reinterpret_cast<const T*>(src.v) + ((size_t)s * src.n_call + (size_t)(pos - src.p0)) * 64
+                        : ring_v + (size_t)(pos % R) * 64;
+      copy16(dstv, vr + dg * EL);
+    }
+#pragma unroll
+    for (int e = 0; e < EL; ++e) {
+      T* dst = sVt + (dg * EL + e) * VSTR + i0;
+      dst[0] = a[e];
+      dst[1] = b[e];
+    }
+  }
+}
+
+// 8 values of a transposed tile row: keys {kb+4h..kb+4h+3, kb+8+4h..kb+8+4h+3} (+16 for the second step).
+template <typename V8, typename V4, typename E>
+__device__ __forceinline__ V8 vfrag(const E* vr, int off) {
+  const V4 a = *reinterpret_cast<const V4*>(vr + off);
+  const V4 b = *reinterpret_cast<const V4*>(vr + off + 8);
+  return V8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <typename T, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, int64_t c_begin, int n_q,
+                                                       int64_t end_pos, T* out) {
+  using RT = typename Rd<T>::type;
+  constexpr bool BF = Is<T>::bf;
+  constexpr int C = NW * 32;
+  constexpr int NT = NW * 64;
+  constexpr int KSTR = AttnCfg<T>::KSTR, VSTR = AttnCfg<T>::VSTR;
+  static_assert(sizeof(RT) == sizeof(T), "read-form and input types share the LDS tile layout");
+  __shared__ __attribute__((aligned(16))) T sK[64 * KSTR];
+  __shared__ __attribute__((aligned(16))) T sVt[64 * VSTR];
+  __shared__ __attribute__((aligned(16))) float sRho[64];
+
+  // Block -> (sequence, chunk).  Consecutive block ids land on consecutive XCDs;
+  // keep every chunk of a sequence on one XCD (its state rows stay in that L2)
+  // and hand out the longest chunks (largest state, full window) first.
+  int s, cl;
+  {
+    const int b = blockIdx.x;
+    if (m.BH % 8 == 0) {
+      const int x = b & 7, k = b >> 3, spx = m.BH >> 3;
+      s = x + 8 * (k % spx);
+      cl = n_q - 1 - k / spx;
+    } else {
+      s = b % m.BH;
+      cl = n_q - 1 - b / m.BH;
+    }
+  }
+  const int64_t c = c_begin + cl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
+  const int64_t cpos = c * C;
+  const int64_t qpos = cpos + 32 * w + jl;
+  const bool qvalid = qpos < end_pos;
+  const int64_t qp = qvalid ? qpos : (end_pos - 1);
+  const float sl2 = m.scale * kLog2e;
+
+  // ---- query fragments (B operand of S^T = K . Q^T)
+  const T* qrow = reinterpret_cast<const T*>(src.q) + ((size_t)s * src.n_call + (size_t)(qp - src.p0)) * 64;
+  const float* rc = d.rope_cos + qp * 16;
+  const float* rsn = d.rope_sin + qp * 16;
+  bf16x8 qf[4];     // bf16 window: k-step kk holds dims 16kk + 8h + e (rotated for kk < 2)
+  f16x8 qs16[2];    // bf16 path, state: dims 32 + 16kk + 8h + e in fp16 (scaled by 2^-qsh)
+  float qw[32];     // fp32 window: dims 32h + kk
+  float qs[16];     // fp32 state: dims 32 + 16h + kk
+  float sl2_state = sl2;
+  if constexpr (BF) {
+    alignas(16) T x[4][8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) copy16(x[kk], qrow + 16 * kk + 8 * h);
+    float qmx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = tof(x[0][e]), b = tof(x[1][e]);
+      rot(a, b, rc[8 * h + e], rsn[8 * h + e]);
+      qf[0][e] = (bf16)a;
+      qf[1][e] = (bf16)b;
+      qf[2][e] = x[2][e];
+      qf[3][e] = x[3][e];
+      qmx = fmaxf(qmx, fmaxf(fabsf(tof(x[2][e])), fabsf(tof(x[3][e]))));
+    }
+    // fp16 range guard: scale the query's live dims by an exact power of two
+    // when they could overflow fp16; the state logits are scaled back.
+    qmx = fmaxf(qmx, partner_f(qmx));
+    int qsh = 0;
+    if (qmx >= 16384.f) {
+      int ex;
+      frexpf(qmx, &ex);
+      qsh = ex - 14;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qs16[0][e] = (f16)ldexpf(tof(x[2][e]), -qsh);
+      qs16[1][e] = (f16)ldexpf(tof(x[3][e]), -qsh);
+    }
+    sl2_state = ldexpf(sl2, qsh);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) qw[kk] = tof(qrow[32 * h + kk]);
+    if (h == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rot(qw[e], qw[16 + e], rc[e], rsn[e]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) qs[kk] = tof(qrow[32 + 16 * h + kk]);
+  }
+
+  float mrun = -kInf, lrun = 0.f;
+  f32x16 O0 = {}, O1 = {};
+
+  // Online softmax over one 32-key subtile: scales acc into log2 units, masks
+  // invalid keys, updates the running max / sum, rescales O, returns p.
+  auto softmax_step = [&](const f32x16& acc, float scl, auto valid, float (&p)[16]) {
+    float sc[16];
+    float mx = -kInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = valid(8 * (r >> 2) + 4 * h + (r & 3)) ? acc[r] * scl : -kInf;
+      mx = fmaxf(mx, sc[r]);
+    }
+    mx = fmaxf(mx, partner_f(mx));
+    const float mnew = fmaxf(mrun, mx);
+    const float muse = mnew == -kInf ? 0.f : mnew;
+    const float alpha = exp2f(mrun - muse);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { p[r] = exp2f(sc[r] - muse); ps += p[r]; }
+    lrun = lrun * alpha + ps;
+    mrun = mnew;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { O0[r] *= alpha; O1[r] *= alpha; }
+  };
+
+  // ---- state part: the state after absorbing chunk c - W/C - 1
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  int64_t ioff = 0;
+  float rmax = 1.f;
+  if (jj >= 0) {
+    const int4 sc4 = d.sched[jj];
+    S = sc4.z + sc4.x + sc4.y;
+    ioff = sc4.w;
+    const float rm = d.rmax[(size_t)s * m.J_cap + jj];
+    rmax = rm > 0.f ? rm : 1.f;
+  }
+  const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
+  const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const RT* pv = reinterpret_cast<const RT*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const float* prho = d.prho + (size_t)s * m.V_cap;
+  const float inv_rmax = 1.0f / rmax;
+  for (int r0 = 0; r0 < S; r0 += 64) {
+    __syncthreads();
+    stage_state<T, NT>(sK, sVt, sRho, idxl, pk, pv, prho, inv_rmax, r0, S);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kb = 32 * sub;
+      if (r0 + kb >= S) continue;
+      const int lim = S - r0 - kb;  // valid rows in this subtile
+      const RT* kr = reinterpret_cast<const RT*>(sK) + (kb + jl) * KSTR;
+      f32x16 acc = {};
+      if constexpr (BF) {
+        acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 8 * h), qs16[0], acc);
+        acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 16 + 8 * h), qs16[1], acc);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) acc = mfma_f32(kr[16 * h + kk], qs[kk], acc);
+      }
+      float p[16];
+      softmax_step(acc, sl2_state, [&](int key) { return key < lim; }, p);
+      // fold rho_i / rho_max into the weights (values are stored as unit directions)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 r4 = *reinterpret_cast<const float4*>(&sRho[kb + 8 * g4 + 4 * h]);
+        p[4 * g4 + 0] *= r4.x;
+        p[4 * g4 + 1] *= r4.y;
+        p[4 * g4 + 2] *= r4.z;
+        p[4 * g4 + 3] *= r4.w;
+      }
+      const RT* vt = reinterpret_cast<const RT*>(sVt);
+      if constexpr (BF) {
+        f16x8 pf0, pf1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pf0[e] = (f16)p[e]; pf1[e] = (f16)p[8 + e]; }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const RT* vr = vt + (32 * dt + jl) * VSTR + kb;
+          f32x16& O = dt ? O1 : O0;
+          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 4 * h), pf0, O);
+          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 16 + 4 * h), pf1, O);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const RT* vr = vt + (32 * dt + jl) * VSTR + kb;
+          f32x16& O = dt ? O1 : O0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O = mfma_f32(vr[8 * (r >> 2) + 4 * h + (r & 3)], p[r], O);
+        }
+      }
+    }
+  }
+  if (S > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { O0[r] *= rmax; O1[r] *= rmax; }
+  }
+
+  // ---- window part: keys [max(0, cC - W), min(cC + C, end)), causal
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < end_pos ? cpos + C : end_pos;
+  const int64_t qlast = min(cpos + 32 * w + 31, end_pos - 1);
+  const T* ring_k = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
+  const T* ring_v = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
+  for (int64_t k0 = lo; k0 < hi; k0 += 64) {
+    __syncthreads();
+    stage_window<T, NT>(sK, sVt, k0, hi, src, s, ring_k, ring_v, m.R, d.rope_cos, d.rope_sin);
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int kb = 32 * sub;
+      const int64_t ks = k0 + kb;
+      if (ks >= hi || ks > qlast) continue;
+      const T* kr = sK + (kb + jl) * KSTR;
+      f32x16 acc = {};
+      if constexpr (BF) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk + 8 * h), qf[kk], acc);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) acc = mfma_f32(kr[32 * h + kk], qw[kk], acc);
+      }
+      float p[16];
+      softmax_step(acc, sl2, [&](int key) { const int64_t kp = ks + key; return kp < hi && kp <= qpos; }, p);
+      if constexpr (BF) {
+        bf16x8 pf0, pf1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pf0[e] = (bf16)p[e]; pf1[e] = (bf16)p[8 + e]; }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const T* vr = sVt + (32 * dt + jl) * VSTR + kb;
+          f32x16& O = dt ? O1 : O0;
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 4 * h), pf0, O);
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 16 + 4 * h), pf1, O);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const T* vr = sVt + (32 * dt + jl) * VSTR + kb;
+          f32x16& O = dt ? O1 : O0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O = mfma_f32(vr[8 * (r >> 2) + 4 * h + (r & 3)], p[r], O);
+        }
+      }
+    }
+  }
+
+  // ---- normalise and store: lane holds dims 8*(r/4) + 4h + r%4 of its query
+  const float lt = lrun + partner_f(lrun);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qvalid) {
+    T* orow = out + ((size_t)s * src.n_call + (size_t)(qpos - src.p0)) * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const f32x16& O = dt ? O1 : O0;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        alignas(16) T vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = fromf<T>(O[4 * g4 + e] * inv);
+        T* dst = orow + 32 * dt + 8 * g4 + 4 * h;
+        if constexpr (BF) {
+          *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(vals);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(vals);
+        }
+      }
+    }
+  }
+}
+
+// =====================================================================
+// Ring maintenance: the last W + C positions (rotated keys, values, gate
+// logits) are kept so that decode steps and later prefill calls can see the
+// window and absorb the chunk that leaves it.
+// =====================================================================
+template <typename T>
+__global__ void ring_fill_kernel(Dims m, Dev d, Src src, int64_t from, int64_t to) {
+  const int s = blockIdx.x;
+  T* rk = reinterpret_cast<T*>(d.ring_k) + (size_t)s * m.R * 64;
+  T* rv = reinterpret_cast<T*>(d.ring_v) + (size_t)s * m.R * 64;
+  float* rl = d.ring_l + (size_t)s * m.R;
+  const int64_t n = (to - from) * 64;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t pos = from + i / 64;
+    const int dd = (int)(i % 64);
+    const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
+    const T* kr = reinterpret_cast<const T*>(src.k) + r * 64;
+    const T* vr = reinterpret_cast<const T*>(src.v) + r * 64;
+    float x = tof(kr[dd]);
+    if (dd < 32) {
+      const int jf = dd & 15;
+      const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+      x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
+    }
+    const size_t slot = (size_t)(pos % m.R);
+    rk[slot * 64 + dd] = fromf<T>(x);
+    rv[slot * 64 + dd] = vr[dd];
+    if (dd == 0) rl[slot] = src.l[r];
+  }
+}
+
+// =====================================================================
+// Decode: split-K over [state rows || window keys] then a combine.
+// Segment sg < nss covers state rows [256 sg, 256 sg + 256); the rest cover
+// window positions.  Each wave takes 64 consecutive keys; a group of lanes
+// shares one key (state: LPR lanes, window: LPK lanes), each lane owning a
+// slice of the dims.  Partials (max, sum, o[64]) go to d.part.
+// =====================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q, int64_t t, int S, int nss,
+                                                       int64_t lo) {
+  constexpr bool BF = Is<T>::bf;
+  __shared__ float sq[64], sqr[64];
+  __shared__ float red[4][kPartStride];
+  const int s = blockIdx.y, sg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float sl2 = m.scale * kLog2e;
+  if (tid < 64) {
+    const T* qr = q + (size_t)s * 64;
+    const float x = tof(qr[tid]);
+    sq[tid] = x;
+    float y = x;
+    if (tid < 32) {
+      const int jf = tid & 15;
+      const float cs = d.rope_cos[t * 16 + jf], sn = d.rope_sin[t * 16 + jf];
+      y = tid < 16 ? x * cs - tof(qr[tid + 16]) * sn : x * cs + tof(qr[tid - 16]) * sn;
+    }
+    sqr[tid] = y;
+  }
+  __syncthreads();
+
+  float mrun = -kInf, lrun = 0.f;
+  float o[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = 0.f;
+  int L;       // lanes per key
+  int vdim0;   // first value dim of this lane
+  int nvd;     // value dims of this lane
+  if (sg < nss) {
+    // state rows: read-form key (RT), unit value direction (RT), radius (f32)
+    using RT = typename Rd<T>::type;
+    constexpr int LPR = BF ? 4 : 8;
+    constexpr int KD = 32 / LPR, VD = 64 / LPR;
+    constexpr int REL = 16 / (int)sizeof(RT);
+    L = LPR;
+    const int e = lane % LPR, grp = lane / LPR;
+    vdim0 = e * VD;
+    nvd = VD;
+    float qk[KD];
+#pragma unroll
+    for (int i = 0; i < KD; ++i) qk[i] = sq[32 + e * KD + i];
+    const RT* kr = reinterpret_cast<const RT*>(d.kread) + (size_t)s * m.S_cap * 32;
+    const RT* vr = reinterpret_cast<const RT*>(d.vread) + (size_t)s * m.S_cap * 64;
+    const float* rr = d.rho + (size_t)s * m.S_cap;
+    const int rb = sg * kDecSeg + w * 64;
+    const int re = min(S, rb + 64);
+    for (int row = rb + grp; row < re; row += 64 / LPR) {
+      alignas(16) RT kk[KD];
+      alignas(16) RT vv[VD];
+#pragma unroll
+      for (int i = 0; i < KD; i += REL) copy16(&kk[i], kr + (size_t)row * 32 + e * KD + i);
+#pragma unroll
+      for (int i = 0; i < VD; i += REL) copy16(&vv[i], vr + (size_t)row * 64 + e * VD + i);
+      const float rho = rr[row];
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < KD; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
+#pragma unroll
+      for (int msk = 1; msk < LPR; msk <<= 1) dot += __shfl_xor(dot, msk);
+      const float lg = dot * sl2;
+      const float mnew = fmaxf(mrun, lg);
+      const float alpha = exp2f(mrun - mnew);
+      const float p = exp2f(lg - mnew);
+      const float pr = p * rho;
+      lrun = lrun * alpha + p;
+      mrun = mnew;
+#pragma unroll
+      for (int i = 0; i < VD; ++i) o[i] = fmaf(pr, tof(vv[i]), o[i] * alpha);
+    }
+  } else {
+    constexpr int LPK = BF ? 8 : 16;
+    constexpr int KD = 64 / LPK;
+    L = LPK;
+    const int e = lane % LPK, grp = lane / LPK;
+    vdim0 = e * KD;
+    nvd = KD;
+    float qk[KD];
+#pragma unroll
+    for (int i = 0; i < KD; ++i) qk[i] = sqr[e * KD + i];
+    const T* rk = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
+    const T* rv = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
+    const int64_t pb = lo + (int64_t)(sg - nss) * kDecSeg + w * 64;
+    const int64_t pe = min(t + 1, pb + 64);
+    for (int64_t pos = pb + grp; pos < pe; pos += 64 / LPK) {
+      const size_t slot = (size_t)(pos % m.R);
+      alignas(16) T kk[KD];
+      alignas(16) T vv[KD];
+#pragma unroll
+      for (int i = 0; i < KD; i += 16 / (int)sizeof(T)) copy16(&kk[i], rk + slot * 64 + e * KD + i);
+#pragma unroll
+      for (int i = 0; i < KD; i += 16 / (int)sizeof(T)) copy16(&vv[i], rv + slot * 64 + e * KD + i);
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < KD; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
+#pragma unroll
+      for (int msk = 1; msk < LPK; msk <<= 1) dot += __shfl_xor(dot, msk);
+      const float lg = dot * sl2;
+      const float mnew = fmaxf(mrun, lg);
+      const float alpha = exp2f(mrun - mnew);
+      const float p = exp2f(lg - mnew);
+      lrun = lrun * alpha + p;
+      mrun = mnew;
+#pragma unroll
+      for (int i = 0; i < KD; ++i) o[i] = fmaf(p, tof(vv[i]), o[i] * alpha);
+    }
+  }
+  // combine the key groups of the wave (lanes with equal lane % L hold the same dims)
+  for (int msk = L; msk < 64; msk <<= 1) {
+    const float mo = __shfl_xor(mrun, msk);
+    const float lo_ = __shfl_xor(lrun, msk);
+    const float mn = fmaxf(mrun, mo);
+    const float a1 = mrun == -kInf ? 0.f : exp2f(mrun - mn);
+    const float a2 = mo == -kInf ? 0.f : exp2f(mo - mn);
+    lrun = lrun * a1 + lo_ * a2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float oo = __shfl_xor(o[i], msk);
+      o[i] = o[i] * a1 + oo * a2;
+    }
+    mrun = mn;
+  }
+  if (lane < L) {
+    if (lane == 0) { red[w][0] = mrun; red[w][1] = lrun; }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i < nvd) red[w][4 + vdim0 + i] = o[i];
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float M = -kInf;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red[ww][0]);
+    float Lsum = 0.f, Ov = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float a = red[ww][0] == -kInf ? 0.f : exp2f(red[ww][0] - M);
+      Lsum += red[ww][1] * a;
+      Ov += red[ww][4 + tid] * a;
+    }
+    float* pp = d.part + ((size_t)s * m.n_seg_max + sg) * kPartStride;
+    pp[4 + tid] = Ov;
+    if (tid == 0) { pp[0] = M; pp[1] = Lsum; }
+  }
+}
+
+template <typename T>
+__global__ void dec_combine_kernel(Dims m, Dev d, int nseg, T* out) {
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const float* pp = d.part + (size_t)s * m.n_seg_max * kPartStride;
+  float M = -kInf;
+  for (int g = 0; g < nseg; ++g) M = fmaxf(M, pp[g * kPartStride]);
+  float L = 0.f, O = 0.f;
+  for (int g = 0; g < nseg; ++g) {
+    const float mg = pp[g * kPartStride];
+    const float a = mg == -kInf ? 0.f : exp2f(mg - M);
+    L += pp[g * kPartStride + 1] * a;
+    O += pp[g * kPartStride + 4 + tid] * a;
+  }
+  out[(size_t)s * 64 + tid] = fromf<T>(L > 0.f ? O / L : 0.f);
+}
+
+// Ring write of one decode token (rotated key, value, gate logit) at slot t % R.
+template <typename T>
+__global__ void dec_ring_kernel(Dims m, Dev d, const T* k, const T* v, const float* l, int64_t t) {
+  const int s = blockIdx.x, dd = threadIdx.x;
+  const T* kr = k + (size_t)s * 64;
+  float x = tof(kr[dd]);
+  if (dd < 32) {
+    const int jf = dd & 15;
+    const float cs = d.rope_cos[t * 16 + jf], sn = d.rope_sin[t * 16 + jf];
+    x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
+  }
+  const size_t slot = (size_t)(t % m.R);
+  reinterpret_cast<T*>(d.ring_k)[((size_t)s * m.R + slot) * 64 + dd] = fromf<T>(x);
+  reinterpret_cast<T*>(d.ring_v)[((size_t)s * m.R + slot) * 64 + dd] = v[(size_t)s * 64 + dd];
+  if (dd == 0) d.ring_l[(size_t)s * m.R + slot] = l[s];
+}
+
+template <typename T>
+__global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, typename Rd<T>::type* key_out,
+                                       typename Rd<T>::type* val_out, float* rho_out) {
+  using RT = typename Rd<T>::type;
+  const int s = blockIdx.x;
+  const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
+  const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const RT* pv = reinterpret_cast<const RT*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const float* pr = d.prho + (size_t)s * m.V_cap;
+  for (int64_t i = threadIdx.x; i < (int64_t)rows * 97; i += blockDim.x) {
+    const int r = (int)(i / 97), dd = (int)(i % 97);
+    const int64_t ver = idxl[r];
+    if (dd < 32) {
+      if (key_out) key_out[((size_t)s * rows + r) * 32 + dd] = pk[ver * 32 + dd];
+    } else if (dd < 96) {
+      if (val_out) val_out[((size_t)s * rows + r) * 64 + dd - 32] = pv[ver * 64 + dd - 32];
+    } else if (rho_out) {
+      rho_out[(size_t)s * rows + r] = pr[ver];
+    }
+  }
+}
+
+template <typename T>
+hipError_t scan_dispatch(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {
+  switch (m.C) {
+    case 32: scan_kernel<T, 32><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
+    case 64: scan_kernel<T, 64><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
+    case 128: scan_kernel<T, 128><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
+    case 256: scan_kernel<T, 256><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t attn_dispatch(const Dims& m, const Dev& d, const Src& src, int64_t cb, int nq, int64_t end, void* out,
+                         hipStream_t st) {
+  const dim3 grid((unsigned)(m.BH * nq));
+  T* o = reinterpret_cast<T*>(out);
+  switch (m.C) {
+    case 32: attn_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, src, cb, nq, end, o); break;
+    case 64: attn_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, src, cb, nq, end, o); break;
+    case 128: attn_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o); break;
+    case 256: attn_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_init(const Dims& m, const Dev& d, double theta, hipStream_t st) {
+  const int64_t n = m.max_tokens * 16;
+  rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(d.rope_cos, d.rope_sin, m.max_tokens, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {
+  if (je <= jb) return hipSuccess;
+  return m.bf16 ? scan_dispatch<bf16>(m, d, src, jb, je, st) : scan_dispatch<float>(m, d, src, jb, je, st);
+}
+
+hipError_t launch_attn(const Dims& m, const Dev& d, const Src& src, int64_t cb, int nq, int64_t end, void* out,
+                       hipStream_t st) {
+  if (nq <= 0) return hipSuccess;
+  return m.bf16 ? attn_dispatch<bf16>(m, d, src, cb, nq, end, out, st)
+                : attn_dispatch<float>(m, d, src, cb, nq, end, out, st);
+}
+
+hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st) {
+  if (to <= from) return hipSuccess;
+  if (m.bf16) ring_fill_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, src, from, to);
+  else ring_fill_kernel<float><<<m.BH, 256, 0, st>>>(m, d, src, from, to);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const Dims& m, const Dev& d, const void* q, int64_t t, int rows, void* out,
+                              hipStream_t st) {
+  const int64_t c = t / m.C;
+  const int64_t lo = c * m.C - m.W > 0 ? c * m.C - m.W : 0;
+  const int nss = (rows + kDecSeg - 1) / kDecSeg;
+  const int nws = (int)((t - lo + 1 + kDecSeg - 1) / kDecSeg);
+  const int nseg = nss + nws;
+  if (nseg > m.n_seg_max) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)nseg, (unsigned)m.BH);
+  if (m.bf16) {
+    dec_attn_kernel<bf16><<<grid, 256, 0, st>>>(m, d, reinterpret_cast<const bf16*>(q), t, rows, nss, lo);
+    dec_combine_kernel<bf16><<<m.BH, 64, 0, st>>>(m, d, nseg, reinterpret_cast<bf16*>(out));
+  } else {
+    dec_attn_kernel<float><<<grid, 256, 0, st>>>(m, d, reinterpret_cast<const float*>(q), t, rows, nss, lo);
+    dec_combine_kernel<float><<<m.BH, 64, 0, st>>>(m, d, nseg, reinterpret_cast<float*>(out));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_ring(const Dims& m, const Dev& d, const void* k, const void* v, const float* l, int64_t t,
+                              hipStream_t st) {
+  if (m.bf16)
+    dec_ring_kernel<bf16><<<m.BH, 64, 0, st>>>(m, d, reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v), l, t);
+  else
+    dec_ring_kernel<float><<<m.BH, 64, 0, st>>>(m, d, reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v), l, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t ioff, void* key_out, void* val_out,
+                                  float* rho_out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (m.bf16)
+    snapshot_gather_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, reinterpret_cast<f16*>(key_out),
+                                                       reinterpret_cast<f16*>(val_out), rho_out);
+  else
+    snapshot_gather_kernel<float><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, reinterpret_cast<float*>(key_out),
+                                                         reinterpret_cast<float*>(val_out), rho_out);
+  return hipGetLastError();
+}
+
+}  // namespace kvm

@@ -1,0 +1,295 @@
+"""Python binding of the C-ABI library libkvm.so (include/kvm.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory (the workspace and the tensors) and
+the current HIP stream.  If libkvm.so is missing, loading fails loudly; there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, fields
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "KvmConfig", "KvmState", "KvmError", "library", "workspace_bytes", "schedule", "SCHED", "DTYPE",
+    "KVM_OK", "KVM_E_INVALID_ARG", "KVM_E_WORKSPACE", "KVM_E_CAPACITY", "KVM_E_STATE", "KVM_E_HIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvm.so")
+
+KVM_OK, KVM_E_INVALID_ARG, KVM_E_WORKSPACE, KVM_E_CAPACITY, KVM_E_STATE, KVM_E_HIP = range(6)
+KVM_FLAG_TRACE = 1
+SCHED = {"fixed": 0, "sqrt": 1, "saturating": 2}
+DTYPE = {"f32": 0, "bf16": 1}
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+_READ_DTYPE = {"f32": torch.float32, "bf16": torch.float16}   # read-form storage type
+
+
+class KvmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("rope_dims", ctypes.c_int32), ("chunk", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("n_sinks", ctypes.c_int32), ("sched", ctypes.c_int32), ("max_slots", ctypes.c_int32),
+        ("alpha", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("rope_theta", ctypes.c_float),
+        ("ln_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class _View(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("n_rows", "key_sum", "val_sum", "count", "rho", "key_read", "val_read", "trace_slot", "trace_kind")]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("position", ctypes.c_int64), ("absorbed_chunks", ctypes.c_int64), ("rows", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("max_chunks", ctypes.c_int64), ("poisoned", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libkvm.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m compressed_kv_state_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.kvm_workspace_bytes.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_size_t)]
+        L.kvm_schedule.argtypes = [ctypes.POINTER(_Config), i64, vp, vp, vp]
+        L.kvm_state_create.argtypes = [ctypes.POINTER(_Config), vp, ctypes.c_size_t, vp, ctypes.POINTER(vp)]
+        L.kvm_state_destroy.argtypes = [vp]
+        L.kvm_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp]
+        L.kvm_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.kvm_state_read.argtypes = [vp, ctypes.POINTER(_View), vp]
+        L.kvm_snapshot_read.argtypes = [vp, i64, vp, vp, vp, vp]
+        L.kvm_state_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
+        L.kvm_status_str.argtypes = [st]
+        L.kvm_status_str.restype = ctypes.c_char_p
+        L.kvm_last_error.argtypes = []
+        L.kvm_last_error.restype = ctypes.c_char_p
+        for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
+                     "kvm_decode_step", "kvm_state_read", "kvm_snapshot_read", "kvm_state_get_info"):
+            getattr(L, name).restype = st
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return library().kvm_status_str(s).decode()
+    except Exception:
+        return f"status {s}"
+
+
+def _check(status: int):
+    if status != KVM_OK:
+        raise KvmError(status, library().kvm_last_error().decode())
+
+
+@dataclass
+class KvmConfig:
+    """Mirror of kvm_config.  sched: 'fixed' | 'sqrt' | 'saturating'; dtype: 'f32' | 'bf16'."""
+
+    batch: int
+    heads: int
+    chunk: int
+    window: int
+    n_sinks: int
+    sched: str
+    max_tokens: int
+    max_slots: int = 0
+    alpha: int = 0
+    dtype: str = "bf16"
+    head_dim: int = 64
+    rope_dims: int = 32
+    rope_theta: float = 10000.0
+    ln_eps: float = 1e-5
+    softmax_scale: float = 0.0
+    trace: bool = False
+
+    @property
+    def seqs(self) -> int:
+        return self.batch * self.heads
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPE[self.dtype]
+
+    @property
+    def read_dtype(self) -> torch.dtype:
+        """Storage type of the state's read form (fp16 on the bf16 path)."""
+        return _READ_DTYPE[self.dtype]
+
+    @staticmethod
+    def of(obj, max_tokens: int, trace: bool = False) -> "KvmConfig":
+        """From any object with the same attribute names (e.g. a workload description)."""
+        names = {f.name for f in fields(KvmConfig)} - {"max_tokens", "trace"}
+        kw = {n: getattr(obj, n) for n in names if hasattr(obj, n)}
+        return KvmConfig(max_tokens=max_tokens, trace=trace, **kw)
+
+    def to_c(self) -> _Config:
+        if self.sched not in SCHED:
+            raise ValueError(f"unknown schedule {self.sched!r}")
+        if self.dtype not in DTYPE:
+            raise ValueError(f"unknown dtype {self.dtype!r}")
+        return _Config(self.batch, self.heads, self.head_dim, self.rope_dims, self.chunk, self.window,
+                       self.n_sinks, SCHED[self.sched], self.max_slots, self.alpha, self.max_tokens,
+                       self.rope_theta, self.ln_eps, self.softmax_scale, DTYPE[self.dtype],
+                       KVM_FLAG_TRACE if self.trace else 0)
+
+
+def workspace_bytes(cfg: KvmConfig) -> int:
+    n = ctypes.c_size_t()
+    c = cfg.to_c()
+    _check(library().kvm_workspace_bytes(ctypes.byref(c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def schedule(cfg: KvmConfig, n_chunks: int):
+    """(sinks, appends, rows_after) per absorbed chunk, as int32 CPU tensors."""
+    out = [torch.zeros(n_chunks, dtype=torch.int32) for _ in range(3)]
+    c = cfg.to_c()
+    _check(library().kvm_schedule(ctypes.byref(c), n_chunks, *(t.data_ptr() for t in out)))
+    return tuple(out)
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class KvmState:
+    """A KVM layer state bound to a torch-allocated device workspace."""
+
+    def __init__(self, cfg: KvmConfig, device: Optional[torch.device] = None):
+        self.cfg = cfg
+        dev = torch.device(device if device is not None else "cuda")
+        if dev.type != "cuda":
+            raise ValueError("KvmState needs a GPU device")
+        self.device = dev if dev.index is not None else torch.device("cuda", torch.cuda.current_device())
+        self._c = cfg.to_c()
+        nbytes = workspace_bytes(cfg)
+        self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        _check(library().kvm_state_create(ctypes.byref(self._c), self.workspace.data_ptr(), nbytes,
+                                          _stream(self.device), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            library().kvm_state_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ checks
+    def _seq_tensor(self, x: torch.Tensor, name: str, tail) -> torch.Tensor:
+        if not isinstance(x, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if x.device != self.device:
+            raise ValueError(f"{name} must be on {self.device}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        S = self.cfg.seqs
+        if x.dim() == len(tail) + 2:
+            if x.shape[0] != self.cfg.batch or x.shape[1] != self.cfg.heads:
+                raise ValueError(f"{name}: leading dims must be (batch, heads)")
+            x = x.reshape(S, *x.shape[2:])
+        if x.dim() != len(tail) + 1 or x.shape[0] != S or any(t is not None and a != t for a, t in zip(x.shape[1:], tail)):
+            raise ValueError(f"{name}: expected shape [B*H, {', '.join(str(t) for t in tail)}], got {tuple(x.shape)}")
+        return x
+
+    def _data(self, x, name, n=None):
+        x = self._seq_tensor(x, name, (n, self.cfg.head_dim) if n is not None else (self.cfg.head_dim,))
+        if x.dtype != self.cfg.torch_dtype:
+            raise TypeError(f"{name} must be {self.cfg.torch_dtype}")
+        return x
+
+    def _gate(self, x, n=None):
+        x = self._seq_tensor(x, "gate_logits", (n,) if n is not None else ())
+        if x.dtype != torch.float32:
+            raise TypeError("gate_logits must be float32")
+        return x
+
+    # ------------------------------------------------------------------ calls
+    def prefill(self, q, k, v, gate_logits, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """kvm_prefill over n tokens: q, k, v [B*H, n, 64] (or [B, H, n, 64]); gate_logits [B*H, n]."""
+        n = q.shape[-2]
+        q2, k2, v2 = (self._data(t, nm, n) for t, nm in ((q, "q"), (k, "k"), (v, "v")))
+        g2 = self._gate(gate_logits, n)
+        if out is None:
+            out = torch.empty_like(q)
+        o2 = self._data(out, "out", n)
+        _check(library().kvm_prefill(self._h, q2.data_ptr(), k2.data_ptr(), v2.data_ptr(), g2.data_ptr(),
+                                     o2.data_ptr(), n, _stream(self.device)))
+        return out
+
+    def decode_step(self, q, k, v, gate_logits, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """kvm_decode_step: q, k, v [B*H, 64]; gate_logits [B*H]."""
+        q2, k2, v2 = (self._data(t, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v")))
+        g2 = self._gate(gate_logits)
+        if out is None:
+            out = torch.empty_like(q)
+        o2 = self._data(out, "out")
+        _check(library().kvm_decode_step(self._h, q2.data_ptr(), k2.data_ptr(), v2.data_ptr(), g2.data_ptr(),
+                                         o2.data_ptr(), _stream(self.device)))
+        return out
+
+    def info(self) -> dict:
+        i = _Info()
+        _check(library().kvm_state_get_info(self._h, ctypes.byref(i)))
+        return {f[0]: getattr(i, f[0]) for f in _Info._fields_}
+
+    def read(self, trace: bool = False) -> dict:
+        """Copy the current state into new device tensors (queued on the current stream)."""
+        inf = self.info()
+        S, Sc, dt = self.cfg.seqs, inf["max_rows"], self.cfg.read_dtype
+        dev = self.device
+        res = {
+            "key_sum": torch.empty(S, Sc, 32, dtype=torch.float32, device=dev),
+            "val_sum": torch.empty(S, Sc, 64, dtype=torch.float32, device=dev),
+            "count": torch.empty(S, Sc, dtype=torch.int32, device=dev),
+            "rho": torch.empty(S, Sc, dtype=torch.float32, device=dev),
+            "key_read": torch.empty(S, Sc, 32, dtype=dt, device=dev),
+            "val_read": torch.empty(S, Sc, 64, dtype=dt, device=dev),
+        }
+        n_rows = torch.zeros(S, dtype=torch.int32)
+        view = _View(n_rows.data_ptr(), *(res[k].data_ptr() for k in
+                                          ("key_sum", "val_sum", "count", "rho", "key_read", "val_read")), None, None)
+        if trace:
+            res["trace_slot"] = torch.empty(S, self.cfg.max_tokens, dtype=torch.int32, device=dev)
+            res["trace_kind"] = torch.empty(S, self.cfg.max_tokens, dtype=torch.uint8, device=dev)
+            view.trace_slot = res["trace_slot"].data_ptr()
+            view.trace_kind = res["trace_kind"].data_ptr()
+        _check(library().kvm_state_read(self._h, ctypes.byref(view), _stream(dev)))
+        res["n_rows"] = n_rows
+        return res
+
+    def snapshot(self, j: int):
+        """Read form of the state after absorbed chunk j: key [B*H, rows_j, 32], unit value
+        direction [B*H, rows_j, 64] (both in read_dtype) and radius [B*H, rows_j] float32;
+        the read-form value is radius * direction."""
+        rows = int(schedule(self.cfg, j + 1)[2][j])
+        dt = self.cfg.read_dtype
+        kr = torch.empty(self.cfg.seqs, rows, 32, dtype=dt, device=self.device)
+        ur = torch.empty(self.cfg.seqs, rows, 64, dtype=dt, device=self.device)
+        rr = torch.empty(self.cfg.seqs, rows, dtype=torch.float32, device=self.device)
+        _check(library().kvm_snapshot_read(self._h, j, kr.data_ptr(), ur.data_ptr(), rr.data_ptr(),
+                                           _stream(self.device)))
+        return kr, ur, rr

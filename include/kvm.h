@@ -1,0 +1,185 @@
+/*
+ * kvm.h -- C ABI of the MI355X (gfx950) Key-Value Means attention layer.
+ *
+ * The layer ([KVM abstract]; [KVM summary, Methodology]) is one softmax
+ * attention over [compressed state || block-sliding window].  Tokens that
+ * overflow the window are merged winner-take-all into a state of raw sums
+ * and counts, or appended as new rows on a size schedule, and the state is
+ * renormalised just in time when read ([KVM summary, Core mechanisms 1-5]).
+ *
+ * Conventions for every entry point
+ *   - Plain C types only.  Device buffers are HIP device pointers; `stream`
+ *     is a hipStream_t passed as void* (NULL = the null stream).
+ *   - The caller owns every buffer, including the device workspace.  The
+ *     library never allocates or frees device memory; it owns only the small
+ *     host-side kvm_state object.  It never writes to its inputs.
+ *   - All device work is queued on `stream`; no call synchronises the host
+ *     with the device.  Results are visible after the caller synchronises.
+ *   - Every call returns a kvm_status and never aborts or throws.  Arguments
+ *     are checked before anything is queued: any status other than KVM_OK
+ *     and KVM_E_HIP means nothing was queued and the state is unchanged.
+ *     KVM_E_HIP (a failed HIP call) poisons the state: later calls on it
+ *     return KVM_E_STATE.  kvm_last_error() gives a thread-local message.
+ *   - One kvm_state must not be used by two calls at the same time.
+ *   - NaN/Inf inputs are not checked; they propagate.
+ *
+ * Tensor layouts (row-major, contiguous):
+ *   prefill  q, k, v, out: [B*H, n, head_dim] in cfg.dtype; gate_logits [B*H, n] float32
+ *   decode   q, k, v, out: [B*H, head_dim]    in cfg.dtype; gate_logits [B*H]    float32
+ *   q and k are passed UNROTATED: the library applies RoPE itself.
+ *   Sequence index s = b*H + h.  All sequences share one position.
+ */
+#ifndef KVM_H
+#define KVM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVM_OK = 0,
+  KVM_E_INVALID_ARG = 1, /* bad config, null pointer, bad size */
+  KVM_E_WORKSPACE = 2,   /* workspace too small or misaligned */
+  KVM_E_CAPACITY = 3,    /* would go past cfg.max_tokens */
+  KVM_E_STATE = 4,       /* call not valid in the state's current position, or state poisoned */
+  KVM_E_HIP = 5          /* a HIP runtime call failed; the state is poisoned */
+} kvm_status;
+
+typedef enum { KVM_F32 = 0, KVM_BF16 = 1 } kvm_dtype;
+
+/* State size schedules ([KVM summary, Core mechanisms 3]; [KVM summary,
+ * Experimental results]: fixed-size state, power-law "sqrt" and saturating).
+ * capacity(T) for T absorbed tokens, sinks included:
+ *   FIXED       max_slots
+ *   SQRT        ceil(alpha * sqrt(T))       (exact integer ceil-sqrt of alpha^2*T)
+ *   SATURATING  min(max_slots, ceil(alpha * sqrt(T)))                     */
+typedef enum { KVM_SCHED_FIXED = 0, KVM_SCHED_SQRT = 1, KVM_SCHED_SATURATING = 2 } kvm_sched;
+
+/* Record, per absorbed token, the row it created or merged into and the kind
+ * (sink / append / merge); read back with kvm_state_read. */
+#define KVM_FLAG_TRACE 1u
+
+typedef struct kvm_config {
+  int32_t batch;          /* B >= 1 */
+  int32_t heads;          /* H >= 1; heads are independent sequences */
+  int32_t head_dim;       /* must be 64 */
+  int32_t rope_dims;      /* must be 32: RoPE on dims [0,32), state keys keep dims [32,64) */
+  int32_t chunk;          /* C in {32, 64, 128, 256} */
+  int32_t window;         /* W: a positive multiple of C */
+  int32_t n_sinks;        /* 0 <= n_sinks <= C: first tokens kept as protected rows */
+  int32_t sched;          /* kvm_sched */
+  int32_t max_slots;      /* FIXED / SATURATING ceiling (>= 1) */
+  int32_t alpha;          /* SQRT / SATURATING integer growth constant (>= 1) */
+  int64_t max_tokens;     /* largest position + 1 the state will ever see (sizes the workspace) */
+  float rope_theta;       /* RoPE base (10000) */
+  float ln_eps;           /* LayerNorm epsilon for state keys (1e-5) */
+  float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
+  int32_t dtype;          /* kvm_dtype of q, k, v, out and of the stored read forms */
+  uint32_t flags;         /* KVM_FLAG_TRACE */
+} kvm_config;
+
+typedef struct kvm_state kvm_state;
+
+/* Copy targets for kvm_state_read.  Any pointer may be NULL (skipped).
+ * n_rows is host memory (filled immediately); every other pointer may be host
+ * or device memory (queued copies, unified addressing).
+ * S_cap = kvm_state_info(...).max_rows.  Rows beyond n_rows[s] are undefined.
+ * rtype, the read-form storage type, is float32 on the KVM_F32 path and IEEE
+ * fp16 on the KVM_BF16 path: every read-form value is bounded (LayerNorm output
+ * |k| <= sqrt(31), unit direction |u| <= 1), so fp16 keeps more precision than
+ * bf16 with no overflow. */
+typedef struct kvm_state_view {
+  int32_t* n_rows;        /* [B*H] host                rows of each sequence's state */
+  float* key_sum;         /* [B*H, S_cap, 32] f32      raw gated key sums (live dims) */
+  float* val_sum;         /* [B*H, S_cap, 64] f32      raw gated value sums */
+  int32_t* count;         /* [B*H, S_cap] i32          tokens absorbed per row */
+  float* rho;             /* [B*H, S_cap] f32          read radius fixed at row creation */
+  void* key_read;         /* [B*H, S_cap, 32] rtype    read-form key, live dims (rotary dims are 0) */
+  void* val_read;         /* [B*H, S_cap, 64] rtype    unit value direction u; read-form value = rho * u */
+  int32_t* trace_slot;    /* [B*H, max_tokens] i32     row created/merged into, -1 if not absorbed */
+  uint8_t* trace_kind;    /* [B*H, max_tokens] u8      0 sink, 1 append, 2 merge, 255 not absorbed */
+} kvm_state_view;
+
+typedef struct kvm_state_info {
+  int64_t position;       /* tokens consumed so far */
+  int64_t absorbed_chunks;/* chunks merged into the state so far */
+  int32_t rows;           /* current rows per sequence (same for all: the schedule is data-independent) */
+  int32_t max_rows;       /* S_cap: rows after the last chunk max_tokens can absorb */
+  int64_t max_chunks;     /* chunks max_tokens can absorb */
+  int32_t poisoned;       /* 1 after KVM_E_HIP */
+} kvm_state_info;
+
+/* Device workspace size for cfg (bytes; the workspace must be 256-byte aligned).
+ * Host only: queues nothing.  Errors: KVM_E_INVALID_ARG. */
+kvm_status kvm_workspace_bytes(const kvm_config* cfg, size_t* bytes);
+
+/* Data-independent schedule ([KVM summary, Core mechanisms 3, 5]): for each of
+ * the first n_chunks absorbed chunks, the sinks created, the rows appended and
+ * the rows after the chunk.  Host only.  Output arrays hold n_chunks entries
+ * (any may be NULL).  Errors: KVM_E_INVALID_ARG. */
+kvm_status kvm_schedule(const kvm_config* cfg, int64_t n_chunks, int32_t* sinks, int32_t* appends,
+                        int32_t* rows_after);
+
+/* Bind a fresh, empty state (position 0) to a caller-owned device workspace
+ * of at least kvm_workspace_bytes(cfg).  Queues the workspace initialisation
+ * (RoPE table, schedule table, counters) on `stream`.
+ * Errors: KVM_E_INVALID_ARG (config; null pointers), KVM_E_WORKSPACE (too
+ * small / misaligned), KVM_E_HIP.  On success *out owns host memory that
+ * kvm_state_destroy frees; the workspace stays the caller's. */
+kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t workspace_bytes,
+                            void* stream, kvm_state** out);
+
+/* Free the host-side state.  Does not touch the workspace.  NULL is allowed. */
+kvm_status kvm_state_destroy(kvm_state* st);
+
+/* Chunk-parallel prefill of n_tokens tokens at the state's current position
+ * ([KVM abstract]: chunk-wise parallelizable prefill; [KVM summary, Core
+ * mechanisms 1-5]).  For each query chunk c, every chunk j <= c - W/C - 1 is
+ * absorbed (sinks, appends, winner-take-all merges) and query t attends with
+ * one softmax over the read form of that state (unrotated q against
+ * LayerNorm-ed state keys whose rotary dims are zero; radius-scaled values)
+ * and the window [max(0, cC - W), t] (rotated q against rotated k).
+ * The position must be a multiple of chunk (else KVM_E_STATE);
+ * position + n_tokens must not exceed max_tokens (else KVM_E_CAPACITY).
+ * n_tokens == 0 is a no-op.  out may not alias q, k, v.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_CAPACITY, KVM_E_HIP. */
+kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* v,
+                       const float* gate_logits, void* out, int64_t n_tokens, void* stream);
+
+/* One decode step at position t = current position ([KVM summary, Problem
+ * statement and Significance]: per-token decoding over a state smaller than
+ * the context).  If t is a multiple of chunk and t >= W + C, chunk
+ * (t - W - C)/C leaves the window and is absorbed first; then the single
+ * query t attends over [state || window [cC - W, t]].  Position advances by 1.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_CAPACITY, KVM_E_STATE, KVM_E_HIP. */
+kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const void* v,
+                           const float* gate_logits, void* out, void* stream);
+
+/* Queue copies of the current state into `dst` (see kvm_state_view).
+ * trace_* need KVM_FLAG_TRACE (else KVM_E_INVALID_ARG if requested).
+ * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
+kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* stream);
+
+/* Queue a gather of the read form of the state right after absorbed chunk j,
+ * i.e. the state that query chunk j + W/C + 1 attends to ([KVM summary, Core
+ * mechanisms 2]: LayerNorm-ed keys, values at the read radius): key
+ * [B*H, rows_j, 32] rtype, unit value direction [B*H, rows_j, 64] rtype, radius
+ * [B*H, rows_j] f32 (device memory; any pointer may be NULL).
+ * j must be < absorbed_chunks.  Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
+kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, void* val_read, float* rho_read,
+                             void* stream);
+
+/* Host-side facts about the state.  Never fails on a valid pointer. */
+kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info);
+
+const char* kvm_status_str(kvm_status s);
+const char* kvm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVM_H */

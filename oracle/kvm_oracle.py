@@ -433,7 +433,8 @@ def _as64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def prefill(q, k, v, ell, p: Params, forced: Optional[dict] = None, keep_snapshots: bool = False) -> SeqResult:
+def prefill(q, k, v, ell, p: Params, forced: Optional[dict] = None, keep_snapshots: bool = False,
+            attend_chunks=None) -> SeqResult:
     """Chunk-by-chunk layer output for one sequence of N tokens.
 
     [KVM abstract]: chunk-wise prefill.  For query chunk c = 0, 1, ...:
@@ -445,6 +446,9 @@ def prefill(q, k, v, ell, p: Params, forced: Optional[dict] = None, keep_snapsho
     tokens before cC - W: the past is split with no overlap.
     q, k, v: [N, head_dim]; ell: [N] gate logits.
     forced: optional {position: (kind, row)} (teacher forcing, see absorb_chunk).
+    attend_chunks: optional set of query chunks whose outputs are computed
+    (sampling for long inputs); other rows of `out` are NaN.  Absorption
+    always runs over every chunk.
     """
     q, k, v, ell = _as64(q), _as64(k), _as64(v), _as64(ell)
     N, d = q.shape
@@ -474,6 +478,9 @@ def prefill(q, k, v, ell, p: Params, forced: Optional[dict] = None, keep_snapsho
             if keep_snapshots:
                 snaps.append(st.copy())
             absorbed += 1
+        if attend_chunks is not None and c not in attend_chunks:
+            out[c * C:min(N, (c + 1) * C)] = np.nan
+            continue
         khat, vhat = read_form(st, p)
         out[c * C:min(N, (c + 1) * C)] = attend_chunk(c, N, q, qr, khat, vhat, kr, v, p)
     return SeqResult(out=out, state=st, kind=kind, slot=slot, logs=logs, rows_after=rows_after,

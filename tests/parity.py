@@ -1,0 +1,202 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, run the oracle under
+the GPU's decisions (teacher forcing), compare.
+
+Decision parity rule: the GPU's append set and merge targets must equal the
+oracle's own choice given the same history, except where the oracle's fp64
+margin is below NEAR_TIE (such cases are counted and reported, not failed).
+Output parity: fp32 path max |diff| <= 1e-4; bf16 path, for every query row t,
+max_d |diff[t, d]| <= 2e-2 * RMS_d(oracle[t, :]).  The bf16 bound is taken per
+row because outputs of early queries (few keys) are ~10x larger than later
+ones, and rounding even the exact output to bf16 exceeds 2e-2 of the global RMS
+there.  The global RMS error is reported beside it.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import oracle.kvm_oracle as O
+from compressed_kv_state_amd import KvmConfig, KvmState
+from kvm_inputs import Inputs, LayerConfig
+
+NEAR_TIE = 1e-4
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL_RMS = 2e-2
+
+
+def to_gpu(inp: Inputs, n0: int = 0, n1: Optional[int] = None):
+    sl = slice(n0, n1)
+    return (inp.q[:, sl].contiguous().cuda(), inp.k[:, sl].contiguous().cuda(), inp.v[:, sl].contiguous().cuda(),
+            inp.gate_logits[:, sl].contiguous().cuda())
+
+
+def run_prefill(w: LayerConfig, inp: Inputs, n_tokens: Optional[int] = None, max_tokens: Optional[int] = None,
+                splits: Optional[List[int]] = None):
+    """Prefill the first n_tokens of `inp` on the GPU (optionally as several calls split at `splits`).
+
+    Returns (out [S, n, 64] float64 CPU, slot [S, n] int64, kind [S, n] int64, state dict, KvmState)."""
+    n = w.n_tokens if n_tokens is None else n_tokens
+    cfg = KvmConfig.of(w, max_tokens=max_tokens or n, trace=True)
+    cfg.batch, cfg.heads = inp.q.shape[0], 1
+    st = KvmState(cfg)
+    bounds = [0] + list(splits or []) + [n]
+    outs = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        q, k, v, g = to_gpu(inp, a, b)
+        outs.append(st.prefill(q, k, v, g))
+    state = st.read(trace=True)
+    torch.cuda.synchronize()
+    out = torch.cat(outs, dim=1).double().cpu().numpy()
+    slot = state["trace_slot"][:, :n].long().cpu().numpy()
+    kind = state["trace_kind"][:, :n].long().cpu().numpy()
+    kind[kind == 255] = O.KIND_NONE
+    return out, slot, kind, state, st
+
+
+def seq_arrays(inp: Inputs, s: int, n: int):
+    return tuple(t[s, :n].double().numpy() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
+
+
+def forced_map(slot_s, kind_s) -> Dict[int, tuple]:
+    return {int(t): (int(kind_s[t]), int(slot_s[t])) for t in np.nonzero(kind_s >= 0)[0]}
+
+
+@dataclass
+class DecisionReport:
+    appends_checked: int = 0
+    append_mismatch: int = 0          # differing append sets with margin >= NEAR_TIE (failures)
+    append_near_tie_diff: int = 0     # differing append sets at a near tie (reported)
+    merges_checked: int = 0
+    merge_mismatch: int = 0           # failures
+    merge_near_tie_diff: int = 0      # reported
+    near_tie_merges: int = 0          # merges whose oracle margin < NEAR_TIE (whatever the GPU chose)
+    details: List[str] = field(default_factory=list)
+
+    @property
+    def ok(self) -> bool:
+        return self.append_mismatch == 0 and self.merge_mismatch == 0
+
+    def merge(self, o: "DecisionReport"):
+        for f in ("appends_checked", "append_mismatch", "append_near_tie_diff", "merges_checked", "merge_mismatch",
+                  "merge_near_tie_diff", "near_tie_merges"):
+            setattr(self, f, getattr(self, f) + getattr(o, f))
+        self.details += o.details[:20]
+
+
+def compare_decisions(res: O.SeqResult, slot_s, kind_s, p: O.Params) -> DecisionReport:
+    """Compare the GPU's per-chunk decisions with the oracle's own (computed under the same history)."""
+    rep = DecisionReport()
+    C = p.chunk
+    for lg in res.logs:
+        toks = range(lg.j * C, (lg.j + 1) * C)
+        gpu_app = sorted(t for t in toks if kind_s[t] == O.KIND_APPEND)
+        rep.appends_checked += 1
+        if gpu_app != lg.appended:
+            if lg.append_margin < NEAR_TIE:
+                rep.append_near_tie_diff += 1
+            else:
+                rep.append_mismatch += 1
+                rep.details.append(f"chunk {lg.j}: append sets differ (margin {lg.append_margin:.3g})")
+        for t, a in lg.assign.items():
+            if kind_s[t] != O.KIND_MERGE:
+                continue
+            rep.merges_checked += 1
+            mg = lg.assign_margin[t]
+            if mg < NEAR_TIE:
+                rep.near_tie_merges += 1
+            if int(slot_s[t]) != a:
+                if mg < NEAR_TIE:
+                    rep.merge_near_tie_diff += 1
+                else:
+                    rep.merge_mismatch += 1
+                    rep.details.append(f"pos {t}: gpu row {int(slot_s[t])} oracle row {a} (margin {mg:.3g})")
+    return rep
+
+
+def check_outputs(dtype: str, got: np.ndarray, want: np.ndarray):
+    """(ok, worst, bound, rms_err_over_rms) over the rows of `want` that are finite.
+
+    fp32: worst = max |diff|, bound = 1e-4.
+    bf16: worst = max over rows of max|diff| / RMS(row of want), bound = 2e-2."""
+    want = want.reshape(-1, want.shape[-1])
+    got = got.reshape(-1, got.shape[-1])
+    rows = np.all(np.isfinite(want), axis=1)
+    w, g = want[rows], got[rows]
+    if w.size == 0:
+        return True, 0.0, 0.0, 0.0
+    err = np.abs(g - w)
+    rel_rms = float(np.sqrt(np.mean(err ** 2)) / max(np.sqrt(np.mean(w ** 2)), 1e-30))
+    if dtype == "f32":
+        worst = float(err.max())
+        return worst <= TOL_F32_ABS, worst, TOL_F32_ABS, rel_rms
+    row_rms = np.sqrt(np.mean(w ** 2, axis=1))
+    worst = float(np.max(err.max(axis=1) / np.maximum(row_rms, 1e-30)))
+    return worst <= TOL_BF16_REL_RMS, worst, TOL_BF16_REL_RMS, rel_rms
+
+
+def check_state(res: O.SeqResult, state: dict, s: int, dtype: str):
+    """Counts exact; fp32 sums and radii against the oracle's fp64 (relative to each row's scale)."""
+    K, V, n, rho, sink = res.state.arrays()
+    S = res.state.rows
+    assert int(state["n_rows"][s]) == S
+    np.testing.assert_array_equal(state["count"][s, :S].cpu().numpy(), n)
+    ks = state["key_sum"][s, :S].double().cpu().numpy()
+    vs = state["val_sum"][s, :S].double().cpu().numpy()
+    rr = state["rho"][s, :S].double().cpu().numpy()
+    kscale = np.maximum(np.abs(K).max(axis=1, keepdims=True), 1e-30)
+    vscale = np.maximum(np.abs(V).max(axis=1, keepdims=True), 1e-30)
+    assert np.max(np.abs(ks - K) / kscale) < 1e-5
+    assert np.max(np.abs(vs - V) / vscale) < 1e-5
+    np.testing.assert_allclose(rr, rho, rtol=1e-6)
+
+
+def run_prefill_decode(w: LayerConfig, inp: Inputs, n0: int, steps: int, cfg_over=None):
+    """Prefill n0 tokens, then `steps` decode steps, on the GPU.  Returns
+    (out [S, n0 + steps, 64] float64, slot, kind, state, KvmState)."""
+    n = n0 + steps
+    cfg = KvmConfig.of(w, max_tokens=n, trace=True)
+    cfg.batch, cfg.heads = inp.q.shape[0], 1
+    if cfg_over:
+        for k_, v_ in cfg_over.items():
+            setattr(cfg, k_, v_)
+    st = KvmState(cfg)
+    outs = []
+    if n0 > 0:
+        q, k, v, g = to_gpu(inp, 0, n0)
+        outs.append(st.prefill(q, k, v, g))
+    q, k, v, g = to_gpu(inp, n0, n)
+    for i in range(steps):
+        outs.append(st.decode_step(q[:, i].contiguous(), k[:, i].contiguous(), v[:, i].contiguous(),
+                                   g[:, i].contiguous())[:, None])
+    state = st.read(trace=True)
+    torch.cuda.synchronize()
+    out = torch.cat(outs, dim=1).double().cpu().numpy()
+    slot = state["trace_slot"][:, :n].long().cpu().numpy()
+    kind = state["trace_kind"][:, :n].long().cpu().numpy()
+    kind[kind == 255] = O.KIND_NONE
+    return out, slot, kind, state, st
+
+
+def oracle_check(w: LayerConfig, inp: Inputs, s: int, n: int, out, slot, kind, state=None, attend_chunks=None,
+                 rows=None, label=""):
+    """Teacher-forced oracle run for sequence s; asserts decision, output and (optionally) state parity.
+    `rows` restricts the output comparison to those positions.  Returns (report, worst, rel_rms)."""
+    p = O.Params.of(w)
+    q, k, v, l = seq_arrays(inp, s, n)
+    res = O.prefill(q, k, v, l, p, forced=forced_map(slot[s], kind[s]), attend_chunks=attend_chunks)
+    rep = compare_decisions(res, slot[s], kind[s], p)
+    want = res.out if rows is None else res.out[rows]
+    got = out[s] if rows is None else out[s][rows]
+    ok, worst, bound, rel = check_outputs(w.dtype, got, want)
+    print(f"   [{label} seq {s}] appends {rep.appends_checked} (near-tie diffs {rep.append_near_tie_diff}), "
+          f"merges {rep.merges_checked} (near-tie diffs {rep.merge_near_tie_diff}, near ties {rep.near_tie_merges}); "
+          f"output worst {worst:.3g} <= {bound:.3g}, rms rel {rel:.3g}", flush=True)
+    assert rep.ok, rep.details[:10]
+    assert ok, f"output parity: worst {worst} > {bound}"
+    if state is not None:
+        check_state(res, state, s, w.dtype)
+    return rep, worst, rel, res
