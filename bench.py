@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the Key-Value Means layer on one MI355X.
+
+A step is one kvm_prefill over the 350M-shaped workload (B=2, H=16, N=32768,
+chunk 128, window 256, sqrt state with ceil(8 sqrt T) rows, 4 sinks, bf16):
+absorption scan, fused attention over [state || window], ring refresh.  Each
+timed step starts from an emptied state (kvm_state_reset, inside the timed
+region).  The line also carries:
+
+  roofline      the attention kernel (dominant): algorithmic MFMA FLOPs per
+                launch / its mean launch time from HIP events recorded by the
+                library around that launch on its stream, against the dense
+                bf16/fp16 MFMA peak.  `traffic` is the HBM bytes per launch
+                from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (scaled by the
+                same counters on a plain copy of known size), taken from
+                profiles/ only when they were measured on this kernel source.
+  decode        the batched-decode workload (64 x 16 sequences, sqrt state
+                prefilled with 16384 tokens): per-step time of the decode
+                kernels and their algorithmic HBM bytes per step.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+
+python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KVM-layer prefill tokens/s (B*H*N) + % bf16 MFMA peak; decode HBM GB/s"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "compressed_kv_state_amd", "csrc", "kvm_kernels.hip")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_kernel_350m_sqrt8_counters.md")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def attn_flops(cfg, n: int) -> int:
+    """Algorithmic MFMA FLOPs of one prefill attention launch over n tokens from position 0.
+
+    Per query t of chunk c: 192 per state row (2*32 for q.k on the 32 live
+    dims, 2*64 for p.v) and 256 per window key (2*64 + 2*64); masked and
+    zero-padded work is not counted."""
+    from compressed_kv_state_amd import schedule
+    C, W = cfg.chunk, cfg.window
+    nq = -(-n // C)
+    rows = schedule(cfg, max(nq, 1))[2].tolist()
+    total = 0
+    for c in range(nq):
+        j = c - W // C - 1
+        S = rows[j] if j >= 0 else 0
+        lo = max(0, c * C - W)
+        for t in range(c * C, min(n, (c + 1) * C)):
+            total += 192 * S + 256 * (t - lo + 1)
+    return total * cfg.seqs
+
+
+def decode_bytes(cfg, rows: int, t: int) -> int:
+    """Algorithmic HBM bytes of one decode step at position t (ring write + attention + combine).
+
+    Per sequence: state rows read once (read-form key 32 x 2 B, unit value
+    direction 64 x 2 B, radius 4 B), window keys/values read once (2 x 64 x 2 B),
+    q/k/v/gate in (3 x 128 + 4 B), ring write (2 x 128 + 4 B), output 128 B."""
+    C, W = cfg.chunk, cfg.window
+    c = t // C
+    w = t - max(0, c * C - W) + 1
+    return cfg.seqs * (196 * rows + 256 * w + 388 + 260 + 128)
+
+
+def read_counters():
+    """Traffic figures from profiles/, if they were measured on the current kernel source."""
+    if not os.path.exists(COUNTERS_MD):
+        return None
+    txt = open(COUNTERS_MD).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_tr or m_sha.group(1) != kernel_sha():
+        return None
+    return float(m_tr.group(1))
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle on a bounded sample: whole sequences of the workload until budget_s has passed."""
+    import oracle.kvm_oracle as O
+    from kvm_inputs import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    p = O.Params.of(w)
+    done, t_used = 0, 0.0
+    while t_used < budget_s and done < w.seqs:
+        inp = make_inputs(w, seqs=[done])
+        arr = [t[0].double().numpy() for t in (inp.q, inp.k, inp.v, inp.gate_logits)]
+        t0 = time.perf_counter()
+        O.prefill(*arr, p)
+        t_used += time.perf_counter() - t0
+        done += 1
+        log(f"cpu oracle: {done} sequence(s), {t_used:.1f}s")
+    return {"value": done * w.n_tokens / t_used, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.seqs} sequences of {w.name} ({w.n_tokens} tokens each), full oracle prefill "
+                      f"(absorption + attention), {t_used:.1f}s"}
+
+
+def bench_prefill(w, steps: int, warmup: int):
+    import torch
+    from compressed_kv_state_amd import KvmConfig, KvmState
+    from kvm_inputs import make_inputs
+    log(f"prefill workload {w.name}: generating inputs")
+    inp = make_inputs(w)
+    q, k, v, g = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
+    del inp
+    cfg = KvmConfig.of(w, max_tokens=w.n_tokens)
+    st = KvmState(cfg)
+    out = torch.empty_like(q)
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
+        st.reset()
+        st.prefill(q, k, v, g, out)
+    torch.cuda.synchronize()
+    st.profile_read()
+    st.profile(True)
+    log(f"timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.reset()
+        st.prefill(q, k, v, g, out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = st.profile_read()
+    st.profile(False)
+    assert torch.isfinite(out.float()).all(), "non-finite output"
+    ms_step = (t1 - t0) * 1e3 / steps
+    prof["final_rows"] = st.info()["rows"]
+    return cfg, ms_step, prof
+
+
+def bench_decode(w, steps: int):
+    import torch
+    from compressed_kv_state_amd import KvmConfig, KvmState
+    from kvm_inputs import make_inputs
+    warm = 8
+    n = w.n_tokens + warm + steps
+    log(f"decode workload {w.name}: generating inputs for {w.seqs} sequences")
+    inp = make_inputs(w, n_total=n)
+    cfg = KvmConfig.of(w, max_tokens=n)
+    st = KvmState(cfg)
+    q, k, v, g = (t[:, :w.n_tokens].contiguous().cuda() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
+    log("decode workload: prefill")
+    st.prefill(q, k, v, g)
+    del q, k, v, g
+    dq, dk, dv, dg = (t[:, w.n_tokens:].contiguous().cuda() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
+    del inp
+    steps_in = [tuple(x[:, i].contiguous() for x in (dq, dk, dv, dg)) for i in range(warm + steps)]
+    out = torch.empty_like(steps_in[0][0])
+    for i in range(warm):
+        st.decode_step(*steps_in[i], out)
+    torch.cuda.synchronize()
+    st.profile(True)
+    t0 = time.perf_counter()
+    for i in range(warm, warm + steps):
+        st.decode_step(*steps_in[i], out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = st.profile_read()
+    st.profile(False)
+    from compressed_kv_state_amd import schedule
+    sched_rows = schedule(cfg, (n - 1) // cfg.chunk + 1)[2].tolist()
+    total_bytes = 0
+    for t in range(w.n_tokens + warm, w.n_tokens + warm + steps):
+        absorbed = max(0, t // cfg.chunk - cfg.window // cfg.chunk)
+        total_bytes += decode_bytes(cfg, sched_rows[absorbed - 1] if absorbed else 0, t)
+    attn_ms = prof["dec_attn_ms"]
+    gbs = total_bytes / (attn_ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "sequences": w.seqs, "prefilled": w.n_tokens, "steps": steps,
+        "ms_per_step": (t1 - t0) * 1e3 / steps,
+        "kernel_ms_per_step": attn_ms / max(prof["dec_attn_launches"], 1),
+        "absorb_ms_per_merge": prof["dec_absorb_ms"] / max(prof["dec_absorb_launches"], 1),
+        "merges": prof["dec_absorb_launches"],
+        "bytes_per_step": total_bytes / steps,
+        "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
+    }
+
+
+def copy_calibration():
+    """A plain device copy of known size, so counter readings can be scaled (profiling runs only)."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {n} bytes")
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str):
+    """Reduce two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) to the summary bench reads."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        hits = {k: v for k, v in d.items() if key in k}
+        return max(hits.items(), key=lambda kv: sum(kv[1]))[1] if hits else []
+
+    copy_f, copy_w = pick(fetch, "copy") or pick(fetch, "elementwise"), pick(write, "copy") or pick(write, "elementwise")
+    attn_f, attn_w = pick(fetch, "attn_kernel"), pick(write, "attn_kernel")
+    copy_kib = (1 << 30) / 1024.0
+    sf = copy_kib / (sum(copy_f) / len(copy_f)) if copy_f else 1.0
+    sw = copy_kib / (sum(copy_w) / len(copy_w)) if copy_w else 1.0
+    f_kib = sum(attn_f) / len(attn_f)
+    w_kib = sum(attn_w) / len(attn_w)
+    traffic = (f_kib * sf + w_kib * sw) * 1024.0
+    with open(out_md, "w") as f:
+        f.write("# attn_kernel HBM traffic, 350M-shaped sqrt workload (B=2, H=16, N=32768), one launch\n\n")
+        f.write(f"Command: `{command}`\n\n")
+        f.write("| counter | attn_kernel KiB/dispatch | copy kernel KiB/dispatch (1 GiB moved) | scale |\n|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {f_kib:.0f} | {sum(copy_f) / max(len(copy_f), 1):.0f} | {sf:.4f} |\n")
+        f.write(f"| WRITE_SIZE | {w_kib:.0f} | {sum(copy_w) / max(len(copy_w), 1):.0f} | {sw:.4f} |\n\n")
+        f.write(f"traffic_bytes_per_launch: {traffic:.6e}\n")
+        f.write(f"kernel_source_sha256_16: {kernel_sha()}\n")
+    print(f"wrote {out_md}: traffic {traffic / 1e9:.3f} GB per launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true", help="add a 1 GiB device copy (counter scaling)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], COUNTERS_MD,
+                           args.summarize_counters[2])
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the KVM layer here is built and measured on a single MI355X "
+              "(no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from kvm_inputs import WORKLOADS
+    wp, wd = WORKLOADS[2], WORKLOADS[4]
+
+    cfg, ms_step, prof = bench_prefill(wp, args.steps, args.warmup)
+    attn_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
+    flops = attn_flops(cfg, wp.n_tokens)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    traffic = read_counters()
+    tokens = wp.seqs * wp.n_tokens
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wp.name, "batch": wp.batch, "heads": wp.heads, "n_tokens": wp.n_tokens,
+                   "chunk": wp.chunk, "window": wp.window, "n_sinks": wp.n_sinks, "sched": "sqrt",
+                   "alpha": wp.alpha, "final_rows": prof["final_rows"]},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": traffic,
+                     "kernel": "attn_kernel", "flops_per_launch": flops, "ms_per_launch": attn_ms},
+        "phases_ms_per_step": {"scan": prof["scan_ms"] / args.steps, "attn": prof["attn_ms"] / args.steps,
+                               "ring": prof["ring_ms"] / args.steps},
+    }
+    if not args.no_decode:
+        res["decode"] = bench_decode(wd, args.decode_steps)
+    if args.copy_calibration:
+        copy_calibration()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

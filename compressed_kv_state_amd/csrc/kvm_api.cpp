@@ -16,6 +16,8 @@
 #include "kvm.h"
 #include "kvm_internal.h"
 
+enum Phase { kScan = 0, kAttn, kRing, kDecAbsorb, kDecAttn, kPhases };
+
 struct kvm_state {
   kvm_config cfg;
   kvm::Dims m;
@@ -24,6 +26,18 @@ struct kvm_state {
   int64_t pos = 0;
   int64_t absorbed = 0;
   bool poisoned = false;
+  // profiling: event pairs recorded around kernel phases
+  bool profiling = false;
+  struct Rec {
+    int phase;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  ~kvm_state() {
+    for (Rec& r : recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+    for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -209,6 +223,30 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+hipEvent_t take_event(kvm_state* st) {
+  if (!st->pool.empty()) {
+    hipEvent_t e = st->pool.back();
+    st->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` on stream hs, bracketed by an event pair when profiling.
+template <typename F>
+hipError_t timed(kvm_state* st, int phase, hipStream_t hs, F launch) {
+  if (!st->profiling) return launch();
+  hipEvent_t a = take_event(st), b = take_event(st);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, hs);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, hs);
+  st->recs.push_back({phase, a, b});
+  return e;
+}
+
 int rows_after(const kvm_state* st, int64_t j) {
   if (j < 0) return 0;
   const int32_t* s = &st->sched[(size_t)j * 4];
@@ -339,12 +377,15 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
   if (a1 > m.J_cap) return fail(KVM_E_CAPACITY, "absorption would pass the workspace's chunk capacity");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   kvm::Src src{q, k, v, gate_logits, p0, n_tokens};
-  hipError_t err = kvm::launch_scan(m, st->d, src, (int)st->absorbed, (int)a1, hs);
+  hipError_t err = hipSuccess;
+  if (a1 > st->absorbed)
+    err = timed(st, kScan, hs, [&] { return kvm::launch_scan(m, st->d, src, (int)st->absorbed, (int)a1, hs); });
   if (err != hipSuccess) return hip_fail(st, err, "scan launch");
-  err = kvm::launch_attn(m, st->d, src, c_first, (int)(c_last - c_first + 1), e, out, hs);
+  err = timed(st, kAttn, hs,
+              [&] { return kvm::launch_attn(m, st->d, src, c_first, (int)(c_last - c_first + 1), e, out, hs); });
   if (err != hipSuccess) return hip_fail(st, err, "attention launch");
   const int64_t from = e - m.R > p0 ? e - m.R : p0;
-  err = kvm::launch_ring_fill(m, st->d, src, from, e, hs);
+  err = timed(st, kRing, hs, [&] { return kvm::launch_ring_fill(m, st->d, src, from, e, hs); });
   if (err != hipSuccess) return hip_fail(st, err, "ring launch");
   st->pos = e;
   st->absorbed = a1;
@@ -370,14 +411,17 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
     const int64_t j = (t - m.W - m.C) / m.C;
     if (j != absorbed || j >= m.J_cap) return fail(KVM_E_STATE, "absorbed chunk count out of step with position");
     kvm::Src src{nullptr, nullptr, nullptr, nullptr, t, 0};  // every position < t comes from the ring
-    hipError_t err = kvm::launch_scan(m, st->d, src, (int)j, (int)j + 1, hs);
+    hipError_t err = timed(st, kDecAbsorb, hs, [&] { return kvm::launch_scan(m, st->d, src, (int)j, (int)j + 1, hs); });
     if (err != hipSuccess) return hip_fail(st, err, "decode absorb launch");
     absorbed = j + 1;
   }
-  hipError_t err = kvm::launch_decode_ring(m, st->d, k, v, gate_logits, t, hs);
-  if (err != hipSuccess) return hip_fail(st, err, "decode ring launch");
-  err = kvm::launch_decode_attn(m, st->d, q, t, rows_after(st, absorbed - 1), out, hs);
-  if (err != hipSuccess) return hip_fail(st, err, "decode attention launch");
+  const int rows = rows_after(st, absorbed - 1);
+  hipError_t err = timed(st, kDecAttn, hs, [&] {
+    hipError_t e2 = kvm::launch_decode_ring(m, st->d, k, v, gate_logits, t, hs);
+    if (e2 == hipSuccess) e2 = kvm::launch_decode_attn(m, st->d, q, t, rows, out, hs);
+    return e2;
+  });
+  if (err != hipSuccess) return hip_fail(st, err, "decode launch");
   st->pos = t + 1;
   st->absorbed = absorbed;
   return KVM_OK;
@@ -438,6 +482,60 @@ kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info) {
   info->max_rows = st->m.S_cap;
   info->max_chunks = st->m.J_cap;
   info->poisoned = st->poisoned ? 1 : 0;
+  return KVM_OK;
+}
+
+kvm_status kvm_state_reset(kvm_state* st, void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemsetAsync(st->d.nver, 0, (size_t)st->m.BH * 4, hs);
+  if (e == hipSuccess && st->m.trace) {
+    e = hipMemsetAsync(st->d.tslot, 0xFF, (size_t)st->m.BH * st->m.max_tokens * 4, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(st->d.tkind, 0xFF, (size_t)st->m.BH * st->m.max_tokens, hs);
+  }
+  if (e != hipSuccess) return hip_fail(st, e, "state reset");
+  st->pos = 0;
+  st->absorbed = 0;
+  st->poisoned = false;
+  return KVM_OK;
+}
+
+kvm_status kvm_profile_enable(kvm_state* st, int enable) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  st->profiling = enable != 0;
+  return KVM_OK;
+}
+
+kvm_status kvm_profile_read(kvm_state* st, kvm_profile_times* out) {
+  if (!st || !out) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  double ms[kPhases] = {0};
+  int64_t n[kPhases] = {0};
+  hipError_t err = hipSuccess;
+  for (kvm_state::Rec& r : st->recs) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e == hipSuccess) {
+      ms[r.phase] += t;
+      n[r.phase] += 1;
+    } else if (err == hipSuccess) {
+      err = e;
+    }
+    st->pool.push_back(r.a);
+    st->pool.push_back(r.b);
+  }
+  st->recs.clear();
+  out->scan_ms = ms[kScan];
+  out->scan_launches = n[kScan];
+  out->attn_ms = ms[kAttn];
+  out->attn_launches = n[kAttn];
+  out->ring_ms = ms[kRing];
+  out->ring_launches = n[kRing];
+  out->dec_absorb_ms = ms[kDecAbsorb];
+  out->dec_absorb_launches = n[kDecAbsorb];
+  out->dec_attn_ms = ms[kDecAttn];
+  out->dec_attn_launches = n[kDecAttn];
+  if (err != hipSuccess) return fail(KVM_E_HIP, std::string("profile events: ") + hipGetErrorString(err));
   return KVM_OK;
 }
 

@@ -56,6 +56,14 @@ class _Info(ctypes.Structure):
                 ("max_rows", ctypes.c_int32), ("max_chunks", ctypes.c_int64), ("poisoned", ctypes.c_int32)]
 
 
+class _Prof(ctypes.Structure):
+    _fields_ = [("scan_ms", ctypes.c_double), ("scan_launches", ctypes.c_int64),
+                ("attn_ms", ctypes.c_double), ("attn_launches", ctypes.c_int64),
+                ("ring_ms", ctypes.c_double), ("ring_launches", ctypes.c_int64),
+                ("dec_absorb_ms", ctypes.c_double), ("dec_absorb_launches", ctypes.c_int64),
+                ("dec_attn_ms", ctypes.c_double), ("dec_attn_launches", ctypes.c_int64)]
+
+
 _lib = None
 
 
@@ -76,12 +84,16 @@ def library() -> ctypes.CDLL:
         L.kvm_state_read.argtypes = [vp, ctypes.POINTER(_View), vp]
         L.kvm_snapshot_read.argtypes = [vp, i64, vp, vp, vp, vp]
         L.kvm_state_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
+        L.kvm_state_reset.argtypes = [vp, vp]
+        L.kvm_profile_enable.argtypes = [vp, st]
+        L.kvm_profile_read.argtypes = [vp, ctypes.POINTER(_Prof)]
         L.kvm_status_str.argtypes = [st]
         L.kvm_status_str.restype = ctypes.c_char_p
         L.kvm_last_error.argtypes = []
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
-                     "kvm_decode_step", "kvm_state_read", "kvm_snapshot_read", "kvm_state_get_info"):
+                     "kvm_decode_step", "kvm_state_read", "kvm_snapshot_read", "kvm_state_get_info",
+                     "kvm_state_reset", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -250,6 +262,20 @@ class KvmState:
         _check(library().kvm_decode_step(self._h, q2.data_ptr(), k2.data_ptr(), v2.data_ptr(), g2.data_ptr(),
                                          o2.data_ptr(), _stream(self.device)))
         return out
+
+    def reset(self):
+        """Back to position 0 with an empty state (queued on the current stream)."""
+        _check(library().kvm_state_reset(self._h, _stream(self.device)))
+
+    def profile(self, enable: bool = True):
+        """Record HIP events around every kernel phase of later calls."""
+        _check(library().kvm_profile_enable(self._h, 1 if enable else 0))
+
+    def profile_read(self) -> dict:
+        """Per-phase device milliseconds and launch counts since the last read (waits for the events)."""
+        p = _Prof()
+        _check(library().kvm_profile_read(self._h, ctypes.byref(p)))
+        return {f[0]: getattr(p, f[0]) for f in _Prof._fields_}
 
     def info(self) -> dict:
         i = _Info()

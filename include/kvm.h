@@ -175,6 +175,29 @@ kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, voi
 /* Host-side facts about the state.  Never fails on a valid pointer. */
 kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info);
 
+/* Return the state to position 0 with an empty compressed state (the RoPE and
+ * schedule tables are kept).  Queues a counter reset on `stream`.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_HIP. */
+kvm_status kvm_state_reset(kvm_state* st, void* stream);
+
+/* Per-phase device times gathered with HIP events while profiling is enabled. */
+typedef struct kvm_profile_times {
+  double scan_ms;          int64_t scan_launches;          /* prefill absorption scan */
+  double attn_ms;          int64_t attn_launches;          /* prefill attention over [state || window] */
+  double ring_ms;          int64_t ring_launches;          /* ring refresh after prefill */
+  double dec_absorb_ms;    int64_t dec_absorb_launches;    /* decode-time absorption */
+  double dec_attn_ms;      int64_t dec_attn_launches;      /* decode ring write + attention + combine */
+} kvm_profile_times;
+
+/* Enable (1) or disable (0) recording of a HIP event pair around every kernel
+ * phase that later calls queue on their stream.  Errors: KVM_E_INVALID_ARG. */
+kvm_status kvm_profile_enable(kvm_state* st, int enable);
+
+/* Wait for the recorded events (this one call synchronises the host with
+ * them), add up the elapsed times per phase into *out, and clear the record.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_HIP. */
+kvm_status kvm_profile_read(kvm_state* st, kvm_profile_times* out);
+
 const char* kvm_status_str(kvm_status s);
 const char* kvm_last_error(void);
 
