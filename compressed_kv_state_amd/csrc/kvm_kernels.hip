@@ -73,6 +73,14 @@ __device__ __forceinline__ void copy16(void* dst, const void* src) {
 }
 __device__ __forceinline__ void zero16(void* dst) { *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0); }
 
+// Barrier that orders LDS only: outstanding global loads stay in flight (a
+// full __syncthreads also waits for every outstanding global access).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Total order on floats (NaN included) so that a rank count always selects
 // exactly m items.
 __device__ __forceinline__ uint32_t ordered(float x) {
@@ -106,34 +114,45 @@ __global__ void rope_table_kernel(float* cosv, float* sinv, int64_t max_tokens, 
 // [KVM summary, Core mechanisms 3]: the least redundant overflowed tokens are
 //   appended as new rows; the count m_j comes from the size schedule.
 // [KVM summary, Core mechanisms 5]: the first tokens become protected sinks.
-// One workgroup per sequence, sequential over chunks.  Per chunk:
-//   1. stage keys (live dims), values and gates of the chunk in LDS;
+// One workgroup (8 waves) per sequence, sequential over chunks.  Per chunk:
+//   1. the chunk's live keys, values and gates go to LDS (loaded from HBM one
+//      chunk ahead, into registers, while the previous chunk is processed);
 //   2. surprise: best cosine of every token against the non-sink rows that
-//      existed before the chunk (MFMA, see cos_best);
-//   3. append the m_j tokens of smallest (surprise, position);
+//      existed before the chunk (MFMA over row tiles, next tile prefetched);
+//   3. append the m_j tokens of smallest (surprise, position) (parallel rank);
 //   4. best cosine against the just-appended rows; assignment = better of the
 //      two (lower row on ties);
-//   5. sort merged tokens by (row, position); each touched or created row is
-//      updated by one thread in position order (deterministic, no atomics),
-//      and gets a new read-form version (LayerNorm key, radius-scaled value).
+//   5. sort merged tokens by (row, position) (parallel rank) and cut them into
+//      per-row segments;
+//   6. four lanes per touched or created row add its segment in position
+//      order (deterministic, no atomics) and write the new read-form version.
 // Cosines: argmax over rows of cos(k, K_i) = argmax of dot(k, K_i/|K_i|).  On
 // the bf16 path k is exact in bf16 and the unit direction U_i = K_i/|K_i| is
 // split into bf16 hi + lo (|U - hi - lo| <= 2^-18 |U|), so two bf16 MFMA
 // passes give dot(k, U_i) to ~1e-5 relative.  fp32 path: fp32 MFMA.
 // =====================================================================
-constexpr int kScanThreads = 256;
+constexpr int kScanWaves = 8;
+constexpr int kScanThreads = 64 * kScanWaves;
 constexpr int kSink = 0, kAppend = 1, kMerge = 2;
+
+// Chunk buffers: NBUF = 2 lets the next chunk stream into LDS (direct
+// global->LDS loads) while the current one is processed.
+template <typename T, int C>
+struct ScanBuf {
+  static constexpr int NBUF = sizeof(T) * C <= 512 ? 2 : 1;
+};
 
 template <typename T, int C>
 struct ScanSmem {
-  static constexpr int KST = Is<T>::bf ? 40 : 36;  // padded row stride (elements), 16-byte multiple
-  T k[C][KST];        // live key dims of the chunk's tokens
-  T v[C][64];         // values
+  static constexpr int NBUF = ScanBuf<T, C>::NBUF;
+  alignas(16) T k[NBUF][C][32];   // live key dims of the chunk's tokens
+  alignas(16) T v[NBUF][C][64];   // values
+  alignas(16) float l[NBUF][C];   // gate logits
   float g[C];         // gate
   float kn[C];        // |k live|
-  uint32_t mu[C];     // ordered surprise
-  float red_v[4][C];
-  int red_r[4][C];
+  alignas(16) uint64_t key[C];    // sort keys
+  float red_v[kScanWaves][C];
+  int red_r[kScanWaves][C];
   float bE[C];
   int rE[C];
   float bA[C];
@@ -147,53 +166,135 @@ struct ScanSmem {
   int seg_start[C];
   int seg_len[C];
   int created_seg[C];
-  int wtot[4];
+  int wtot[kScanWaves];
   int nold;
+  int nseg;
   uint32_t rmax_bits;  // largest radius of the rows created in this chunk (non-negative float bits)
 };
+
+// Queue direct global->LDS loads of chunk P0's live keys, values and gate
+// logits into buffer `buf`.  Each wave instruction moves 64 x 16 bytes (4
+// bytes for the logits) into consecutive LDS; the loads complete in the
+// background (vmcnt), so only a full barrier waits for them.
+template <typename T, int C>
+__device__ __forceinline__ void chunk_load_lds(ScanSmem<T, C>& sm, int buf, const Dims& m, const Src& src, int s,
+                                               int64_t P0, const T* ring_k, const T* ring_v, const float* ring_l) {
+  constexpr int EL = 16 / sizeof(T);
+  constexpr int KP = 32 / EL, VP = 64 / EL;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool from_in = P0 >= src.p0;
+  auto row_of = [&](int t, bool key) -> const T* {
+    const int64_t pos = P0 + t;
+    if (from_in) {
+      const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
+      return (key ? reinterpret_cast<const T*>(src.k) : reinterpret_cast<const T*>(src.v)) + r * 64;
+    }
+    return (key ? ring_k : ring_v) + (size_t)(pos % m.R) * 64;
+  };
+  for (int base = w * 64; base < C * KP; base += kScanThreads) {
+    const int p = base + lane, t = p / KP, q = p % KP;
+    __builtin_amdgcn_global_load_lds(row_of(t, true) + 32 + q * EL, &sm.k[buf][0][0] + base * EL, 16, 0, 0);
+  }
+  for (int base = w * 64; base < C * VP; base += kScanThreads) {
+    const int p = base + lane, t = p / VP, q = p % VP;
+    __builtin_amdgcn_global_load_lds(row_of(t, false) + q * EL, &sm.v[buf][0][0] + base * EL, 16, 0, 0);
+  }
+  // C = 32 fills half a wave: the other lanes stay idle (lane i of the wave
+  // writes LDS word base + i, so an active lane past C would land in the
+  // neighbouring buffer)
+  for (int base = w * 64; base < C; base += kScanThreads) {
+    const int t = base + lane;
+    if (t >= C) break;
+    const int64_t pos = P0 + t;
+    const float* lp = from_in ? src.l + (size_t)s * src.n_call + (size_t)(pos - src.p0) : ring_l + pos % m.R;
+    __builtin_amdgcn_global_load_lds(lp, &sm.l[buf][0] + base, 4, 0, 0);
+  }
+}
+
+// Fold one 32x32 result tile into a lane's running (best value, row): the lane
+// holds rows row0 + 8(r/4) + 4h + r%4 (increasing in r) of its token.  The tile
+// maximum is a max3 tree; the row is looked up only when it beats the running
+// best (strictly, so earlier and lower rows win ties).
+__device__ __forceinline__ void lane_best(f32x16 acc, int row0, int re, int h, float& bv, int& br) {
+  if (row0 + 32 > re) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (row0 + 8 * (r >> 2) + 4 * h + (r & 3) >= re) acc[r] = -kInf;
+  }
+  float mx = acc[0];
+#pragma unroll
+  for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+  mx = fmaxf(mx, acc[15]);
+  if (mx > bv) {
+    int rr = 15;
+#pragma unroll
+    for (int r = 15; r >= 0; --r)
+      if (acc[r] == mx) rr = r;
+    bv = mx;
+    br = row0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+  }
+}
 
 // Best (largest) dot(k_t, U_i) over rows i in [rb, re) for every token t of the
 // chunk; ties to the lowest row.  Writes outv/outr[t] (-inf / INT_MAX if no row).
 // All threads of the block must call it.
 template <typename T, int C>
-__device__ void cos_best(ScanSmem<T, C>& sm, const char* unit, int rb, int re, float* outv, int* outr) {
+__device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, int re, float* outv, int* outr) {
   constexpr int CT = C / 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
   float bv[CT];
   int br[CT];
 #pragma unroll
   for (int tt = 0; tt < CT; ++tt) { bv[tt] = -kInf; br[tt] = INT_MAX; }
-  if (re > rb) {
-    const int ntile = (re - rb + 31) >> 5;
+  const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
+  if (w < ntile) {
     if constexpr (Is<T>::bf) {
       // lane half h owns dims [16h, 16h+16) of every 32-dim key
       bf16x8 bfr[CT][2];
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt) {
-        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&sm.k[32 * tt + jl][16 * h]);
-        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&sm.k[32 * tt + jl][16 * h + 8]);
+        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * tt + jl][16 * h]);
+        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * tt + jl][16 * h + 8]);
       }
       const bf16* U = reinterpret_cast<const bf16*>(unit);
-      for (int tile = w; tile < ntile; tile += 4) {
+      auto load = [&](int tile, bf16x8 (&a)[4]) {
+        const int ri = min(rb + (tile << 5) + jl, re - 1);
+        const bf16* u = U + (size_t)ri * 64 + 16 * h;
+        a[0] = *reinterpret_cast<const bf16x8*>(u);
+        a[1] = *reinterpret_cast<const bf16x8*>(u + 8);
+        a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
+        a[3] = *reinterpret_cast<const bf16x8*>(u + 40);
+      };
+      // two register sets in ping-pong: the loads of tile i+2W are issued right
+      // after the MFMAs of tile i read their set, so they overlap tile i+W
+      auto tile_best = [&](const bf16x8 (&a)[4], int tile) {
         const int row0 = rb + (tile << 5);
-        const int ri = min(row0 + jl, re - 1);
-        const bf16* u = U + (size_t)ri * 64;
-        const bf16x8 ah0 = *reinterpret_cast<const bf16x8*>(u + 16 * h);
-        const bf16x8 ah1 = *reinterpret_cast<const bf16x8*>(u + 16 * h + 8);
-        const bf16x8 al0 = *reinterpret_cast<const bf16x8*>(u + 32 + 16 * h);
-        const bf16x8 al1 = *reinterpret_cast<const bf16x8*>(u + 32 + 16 * h + 8);
+        f32x16 acc[CT];
 #pragma unroll
-        for (int tt = 0; tt < CT; ++tt) {
-          f32x16 acc = {};
-          acc = mfma_bf16(ah0, bfr[tt][0], acc);
-          acc = mfma_bf16(ah1, bfr[tt][1], acc);
-          acc = mfma_bf16(al0, bfr[tt][0], acc);
-          acc = mfma_bf16(al1, bfr[tt][1], acc);
+        for (int tt = 0; tt < CT; ++tt) acc[tt] = f32x16{};
+        // independent accumulators interleaved so dependent MFMAs are CT apart
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (row < re && acc[r] > bv[tt]) { bv[tt] = acc[r]; br[tt] = row; }
-          }
+        for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[0], bfr[tt][0], acc[tt]);
+#pragma unroll
+        for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[1], bfr[tt][1], acc[tt]);
+#pragma unroll
+        for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[2], bfr[tt][0], acc[tt]);
+#pragma unroll
+        for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[3], bfr[tt][1], acc[tt]);
+#pragma unroll
+        for (int tt = 0; tt < CT; ++tt) lane_best(acc[tt], row0, re, h, bv[tt], br[tt]);
+      };
+      // two register sets in ping-pong: the loads of tile i+2W are issued right
+      // after the MFMAs of tile i read their set, so they overlap tile i+W
+      bf16x8 a0[4], a1[4];
+      if (w < ntile) load(w, a0);
+      if (w + kScanWaves < ntile) load(w + kScanWaves, a1);
+      for (int tile = w; tile < ntile; tile += 2 * kScanWaves) {
+        tile_best(a0, tile);
+        if (tile + 2 * kScanWaves < ntile) load(tile + 2 * kScanWaves, a0);
+        if (tile + kScanWaves < ntile) {
+          tile_best(a1, tile + kScanWaves);
+          if (tile + 3 * kScanWaves < ntile) load(tile + 3 * kScanWaves, a1);
         }
       }
     } else {
@@ -202,9 +303,9 @@ __device__ void cos_best(ScanSmem<T, C>& sm, const char* unit, int rb, int re, f
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(sm.k[32 * tt + jl][16 * h + kk]);
+        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(sm.k[buf][32 * tt + jl][16 * h + kk]);
       const float* U = reinterpret_cast<const float*>(unit);
-      for (int tile = w; tile < ntile; tile += 4) {
+      for (int tile = w; tile < ntile; tile += kScanWaves) {
         const int row0 = rb + (tile << 5);
         const int ri = min(row0 + jl, re - 1);
         const float* u = U + (size_t)ri * 32 + 16 * h;
@@ -216,11 +317,7 @@ __device__ void cos_best(ScanSmem<T, C>& sm, const char* unit, int rb, int re, f
           f32x16 acc = {};
 #pragma unroll
           for (int kk = 0; kk < 16; ++kk) acc = mfma_f32(a[kk], bfr[tt][kk], acc);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row0 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (row < re && acc[r] > bv[tt]) { bv[tt] = acc[r]; br[tt] = row; }
-          }
+          lane_best(acc, row0, re, h, bv[tt], br[tt]);
         }
       }
     }
@@ -234,12 +331,12 @@ __device__ void cos_best(ScanSmem<T, C>& sm, const char* unit, int rb, int re, f
     if (ov > bv[tt] || (ov == bv[tt] && orow < br[tt])) { bv[tt] = ov; br[tt] = orow; }
     if (h == 0) { sm.red_v[w][32 * tt + jl] = bv[tt]; sm.red_r[w][32 * tt + jl] = br[tt]; }
   }
-  __syncthreads();
+  lds_barrier();
+  const int nw = min(ntile, kScanWaves);
   for (int t = tid; t < C; t += kScanThreads) {
-    float v = sm.red_v[0][t];
-    int r = sm.red_r[0][t];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
+    float v = -kInf;
+    int r = INT_MAX;
+    for (int ww = 0; ww < nw; ++ww) {
       const float ov = sm.red_v[ww][t];
       const int orow = sm.red_r[ww][t];
       if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
@@ -247,30 +344,33 @@ __device__ void cos_best(ScanSmem<T, C>& sm, const char* unit, int rb, int re, f
     outv[t] = v;
     outr[t] = r;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
-// Unit direction of a key sum, stored for the next cosine passes.
-template <typename T>
-__device__ __forceinline__ void store_unit(char* unit_row, const float (&K)[32]) {
-  float n2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) n2 = fmaf(K[i], K[i], n2);
-  const float inv = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
-  if constexpr (Is<T>::bf) {
-    bf16* u = reinterpret_cast<bf16*>(unit_row);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float x = K[i] * inv;
-      const bf16 hi = (bf16)x;
-      u[i] = hi;
-      u[32 + i] = (bf16)(x - (float)hi);
+// rank[t] = #{s : key[s] < key[t]} for every t < C (tokens to leave out carry
+// the largest key), using all threads: P = threads / C lanes per token, each
+// over C / P keys read two at a time, summed with lane shuffles.  Returns the
+// rank on the lane with part == 0 (else -1) and that lane's token in t_out.
+template <int C>
+__device__ __forceinline__ int parallel_rank(const uint64_t* key, int& t_out) {
+  constexpr int P = kScanThreads / C >= 1 ? kScanThreads / C : 1;
+  constexpr int SPAN = C / P;
+  static_assert(SPAN % 2 == 0, "keys are read in pairs");
+  const int t = threadIdx.x / P, part = threadIdx.x % P;
+  t_out = t;
+  int cnt = 0;
+  if (t < C) {
+    const uint64_t kt = key[t];
+    const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(key + part * SPAN);
+#pragma unroll 8
+    for (int i = 0; i < SPAN / 2; ++i) {
+      const ulonglong2 k2 = kp[i];
+      cnt += (k2.x < kt) + (k2.y < kt);
     }
-  } else {
-    float* u = reinterpret_cast<float*>(unit_row);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) u[i] = K[i] * inv;
   }
+#pragma unroll
+  for (int msk = 1; msk < P; msk <<= 1) cnt += __shfl_xor(cnt, msk);
+  return (t < C && part == 0) ? cnt : -1;
 }
 
 template <typename T, int C>
@@ -280,8 +380,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
   __shared__ ScanSmem<T, C> sm;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  constexpr int EL = 16 / sizeof(T);       // elements per 16-byte piece
-  constexpr int KP = 32 / EL, VP = 64 / EL;
 
   float* key_sum = d.key_sum + (size_t)s * m.S_cap * 32;
   float* val_sum = d.val_sum + (size_t)s * m.S_cap * 64;
@@ -301,92 +399,117 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
   const float* ring_l = d.ring_l + (size_t)s * m.R;
   int nver = d.nver[s];
 
+  constexpr int NBUF = ScanBuf<T, C>::NBUF;
+  if (NBUF == 2 && j_begin < j_end) {
+    chunk_load_lds<T, C>(sm, 0, m, src, s, (int64_t)j_begin * C, ring_k, ring_v, ring_l);
+    __syncthreads();  // waits for the loads (vmcnt) and publishes the buffer
+  }
+
+  // Within a chunk step threads exchange data through LDS only (LDS barriers,
+  // so the next chunk's loads stay in flight); every global write of a step is
+  // read by another thread only in a later step, after the full barrier that
+  // closes the step.
+  int4 sc_next = j_begin < j_end ? d.sched[j_begin] : make_int4(0, 0, 0, 0);
+  int prev_off = j_begin > 0 ? d.sched[j_begin - 1].w : 0;
   for (int j = j_begin; j < j_end; ++j) {
-    const int4 sc = d.sched[j];
+    const int4 sc = sc_next;
     const int sinks = sc.x, mj = sc.y, R0 = sc.z;
     const int64_t ioff = sc.w;
     const int nc = sinks + mj;
     const int rows_after = R0 + nc;
     const int64_t P0 = (int64_t)j * C;
-    const bool from_in = P0 >= src.p0;
 
-    // ---- 1. stage the chunk
-    for (int i = tid; i < C * (KP + VP); i += kScanThreads) {
-      const int t = i / (KP + VP), p = i % (KP + VP);
-      const int64_t pos = P0 + t;
-      const T* krow;
-      const T* vrow;
-      if (from_in) {
-        const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
-        krow = reinterpret_cast<const T*>(src.k) + r * 64;
-        vrow = reinterpret_cast<const T*>(src.v) + r * 64;
-      } else {
-        const size_t r = (size_t)(pos % m.R);
-        krow = ring_k + r * 64;
-        vrow = ring_v + r * 64;
-      }
-      if (p < KP) copy16(&sm.k[t][p * EL], krow + 32 + p * EL);
-      else copy16(&sm.v[t][(p - KP) * EL], vrow + (p - KP) * EL);
+    // ---- 1. the chunk is in LDS buffer `cur`; start streaming the next one into the other
+    const int cur = NBUF == 2 ? (j - j_begin) & 1 : 0;
+    if (NBUF == 2) {
+      if (j + 1 < j_end) chunk_load_lds<T, C>(sm, cur ^ 1, m, src, s, P0 + C, ring_k, ring_v, ring_l);
+    } else {
+      chunk_load_lds<T, C>(sm, 0, m, src, s, P0, ring_k, ring_v, ring_l);
+      __syncthreads();
     }
-    for (int t = tid; t < C; t += kScanThreads) {
-      const int64_t pos = P0 + t;
-      const float ell = from_in ? src.l[(size_t)s * src.n_call + (size_t)(pos - src.p0)] : ring_l[pos % m.R];
-      // merge gate = logistic sigmoid of the logit
-      sm.g[t] = 1.0f / (1.0f + expf(-ell));
-    }
-    __syncthreads();
+    const T (*Kc)[32] = sm.k[cur];
+    const T (*Vc)[64] = sm.v[cur];
     for (int t = tid; t < C; t += kScanThreads) {
       float n2 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) { const float x = tof(sm.k[t][i]); n2 = fmaf(x, x, n2); }
+      for (int i = 0; i < 32; ++i) { const float x = tof(Kc[t][i]); n2 = fmaf(x, x, n2); }
       sm.kn[t] = sqrtf(n2);
+      // merge gate = logistic sigmoid of the logit
+      sm.g[t] = 1.0f / (1.0f + expf(-sm.l[cur][t]));
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 2. surprise against the non-sink rows that existed before the chunk
     const int eb = m.ns, ee = R0;
-    cos_best<T, C>(sm, unit, eb, ee, sm.bE, sm.rE);
+    cos_best<T, C>(sm, cur, unit, eb, ee, sm.bE, sm.rE);
     for (int t = tid; t < C; t += kScanThreads) {
       float mu;
       if (ee > eb) mu = sm.kn[t] > 0.f ? sm.bE[t] / sm.kn[t] : 0.f;
       else mu = -kInf;
-      sm.mu[t] = ordered(mu);
+      // key = (surprise, position): smaller = more surprising; sinks never rank
+      sm.key[t] = t < sinks ? ~0ull : (((uint64_t)ordered(mu) << 32) | (uint32_t)t);
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 3. append the m_j most surprising candidates (smallest surprise, then position)
-    for (int t = tid; t < C; t += kScanThreads) {
-      if (t < sinks) {
-        sm.flag[t] = kSink;
-      } else {
-        const uint32_t mt = sm.mu[t];
-        int rank = 0;
-        for (int u = sinks; u < C; ++u) {
-          const uint32_t mv = sm.mu[u];
-          rank += (mv < mt) || (mv == mt && u < t);
+    // ---- 3. append the m_j most surprising candidates
+    {
+      int t;
+      const int rank = parallel_rank<C>(sm.key, t);
+      if (rank >= 0) sm.flag[t] = t < sinks ? kSink : (rank < mj ? kAppend : kMerge);
+    }
+    lds_barrier();
+    {
+      // position order of the appended tokens: block prefix count over the chunk
+      const bool ap = tid < C && sm.flag[tid] == kAppend;
+      const unsigned long long bal = __ballot(ap);
+      const int within = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) sm.wtot[w] = __popcll(bal);
+      lds_barrier();
+      int off = 0;
+      for (int ww = 0; ww < w; ++ww) off += sm.wtot[ww];
+      if (tid < C) {
+        if (tid < sinks) {
+          sm.arow[tid] = R0 + tid;
+        } else if (ap) {
+          sm.arow[tid] = R0 + sinks + off + within;
+          sm.app_list[off + within] = tid;
         }
-        sm.flag[t] = rank < mj ? kAppend : kMerge;
       }
     }
-    __syncthreads();
-    for (int t = tid; t < C; t += kScanThreads) {
-      if (t < sinks) {
-        sm.arow[t] = R0 + t;
-      } else if (sm.flag[t] == kAppend) {
-        int cnt = 0;
-        for (int u = sinks; u < t; ++u) cnt += sm.flag[u] == kAppend;
-        sm.arow[t] = R0 + sinks + cnt;
-        sm.app_list[cnt] = t;
-        float K[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) K[i] = tof(sm.k[t][i]);
-        store_unit<T>(unit + (size_t)(R0 + sinks + cnt) * 128, K);
-      }
-    }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 4. best against the new rows, then the winner-take-all assignment
-    cos_best<T, C>(sm, unit, R0 + sinks, rows_after, sm.bA, sm.rA);
+    // ---- 4. best against the new rows (their key sums are the creating tokens'
+    // live keys, in LDS: dot(k_t, k_s) / |k_s|), then the winner-take-all assignment
+    for (int t = tid >> 2; t < C; t += kScanThreads / 4) {
+      const int sub = tid & 3;
+      float best = -kInf;
+      int brow = INT_MAX;
+      if (sm.flag[t] == kMerge && mj > 0) {
+        float kt[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
+        for (int e = sub; e < mj; e += 4) {
+          const int s2 = sm.app_list[e];
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) dot = fmaf(kt[i], tof(Kc[s2][i]), dot);
+          const float nk = sm.kn[s2];
+          const float val = nk > 0.f ? dot / nk : 0.f;
+          if (val > best) { best = val; brow = R0 + sinks + e; }
+        }
+      }
+#pragma unroll
+      for (int msk = 1; msk < 4; msk <<= 1) {
+        const float ob = __shfl_xor(best, msk);
+        const int orow = __shfl_xor(brow, msk);
+        if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
+      }
+      if (sub == 0) {
+        sm.bA[t] = best;
+        sm.rA[t] = brow;
+      }
+    }
+    lds_barrier();
     const int fallback = ee > eb ? eb : (R0 + sinks);
     for (int t = tid; t < C; t += kScanThreads) {
       if (sm.flag[t] == kMerge) {
@@ -397,61 +520,80 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
         sm.arow[t] = a;
-      }
-    }
-    __syncthreads();
-
-    // ---- 5. sort merged tokens by (row, position) and cut them into per-row segments
-    const int nm = C - nc;
-    for (int t = tid; t < C; t += kScanThreads) {
-      if (sm.flag[t] == kMerge) {
-        const int at = sm.arow[t];
-        int rank = 0;
-        for (int u = 0; u < C; ++u) {
-          if (sm.flag[u] != kMerge) continue;
-          const int au = sm.arow[u];
-          rank += (au < at) || (au == at && u < t);
-        }
-        sm.srt_tok[rank] = t;
-        sm.srt_row[rank] = at;
+        sm.key[t] = ((uint64_t)(uint32_t)a << 32) | (uint32_t)t;
+      } else {
+        sm.key[t] = ~0ull;  // non-merged tokens sort last
       }
     }
     if (tid == 0) { sm.nold = 0; sm.rmax_bits = 0u; }
     for (int c2 = tid; c2 < nc; c2 += kScanThreads) sm.created_seg[c2] = -1;
-    __syncthreads();
-    const bool head = tid < nm && (tid == 0 || sm.srt_row[tid] != sm.srt_row[tid - 1]);
-    const unsigned long long bal = __ballot(head);
-    const int within = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sm.wtot[w] = __popcll(bal);
-    __syncthreads();
-    int off = 0, nseg = 0;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      off += ww < w ? sm.wtot[ww] : 0;
-      nseg += sm.wtot[ww];
-    }
-    if (head) {
-      sm.seg_row[off + within] = sm.srt_row[tid];
-      sm.seg_start[off + within] = tid;
-    }
-    __syncthreads();
-    for (int k = tid; k < nseg; k += kScanThreads) {
-      sm.seg_len[k] = (k + 1 < nseg ? sm.seg_start[k + 1] : nm) - sm.seg_start[k];
-      const int rk = sm.seg_row[k];
-      if (rk < R0 && (k + 1 == nseg || sm.seg_row[k + 1] >= R0)) sm.nold = k + 1;
-      if (rk >= R0 + sinks && rk < rows_after) sm.created_seg[rk - R0] = k;
-    }
-    // the new index list starts as a copy of the previous one
-    if (j > 0) {
-      const int64_t prev = d.sched[j - 1].w;
-      for (int i = tid; i < R0; i += kScanThreads) idx[ioff + i] = idx[prev + i];
-    }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- 6. update every touched or created row, in increasing row order
+    // ---- 5. sort merged tokens by (row, position); cut into per-row segments
+    const int nm = C - nc;
+    {
+      int t;
+      const int rank = parallel_rank<C>(sm.key, t);
+      if (rank >= 0 && rank < nm) {
+        sm.srt_tok[rank] = t;
+        sm.srt_row[rank] = sm.arow[t];
+      }
+    }
+    lds_barrier();
+    {
+      const bool head = tid < nm && (tid == 0 || sm.srt_row[tid] != sm.srt_row[tid - 1]);
+      const unsigned long long bal = __ballot(head);
+      const int within = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) sm.wtot[w] = __popcll(bal);
+      lds_barrier();
+      int off = 0, nseg = 0;
+#pragma unroll
+      for (int ww = 0; ww < kScanWaves; ++ww) {
+        off += ww < w ? sm.wtot[ww] : 0;
+        nseg += sm.wtot[ww];
+      }
+      if (head) {
+        sm.seg_row[off + within] = sm.srt_row[tid];
+        sm.seg_start[off + within] = tid;
+      }
+      if (tid == 0) sm.nseg = nseg;
+    }
+    lds_barrier();
+    {
+      const int nseg = sm.nseg;
+      for (int k2 = tid; k2 < nseg; k2 += kScanThreads) {
+        sm.seg_len[k2] = (k2 + 1 < nseg ? sm.seg_start[k2 + 1] : nm) - sm.seg_start[k2];
+        const int rk = sm.seg_row[k2];
+        if (rk < R0 && (k2 + 1 == nseg || sm.seg_row[k2 + 1] >= R0)) sm.nold = k2 + 1;
+        if (rk >= R0 + sinks && rk < rows_after) sm.created_seg[rk - R0] = k2;
+      }
+    }
+    lds_barrier();
     const int nold = sm.nold;
     const int nu = nold + nc;
-    for (int u = tid; u < nu; u += kScanThreads) {
+
+    // schedule entry of the next step: a scalar load, issued here so that it is
+    // covered by this step's closing barrier rather than stalling an LDS barrier
+    if (j + 1 < j_end) sc_next = d.sched[j + 1];
+
+    // ---- 6a. the new index list: rows before the chunk that this chunk does not
+    // touch keep their version (touched rows are the first nold segments, sorted)
+    if (j > 0) {
+      const int64_t prev = prev_off;
+      for (int i = tid; i < R0; i += kScanThreads) {
+        int lo = 0, hi = nold;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (sm.seg_row[mid] < i) lo = mid + 1;
+          else hi = mid;
+        }
+        if (lo == nold || sm.seg_row[lo] != i) idx[ioff + i] = idx[prev + i];
+      }
+    }
+
+    // ---- 6b. update every touched or created row (four lanes per row, in increasing row order)
+    for (int u = tid >> 2; u < nu; u += kScanThreads / 4) {
+      const int sub = tid & 3;  // lane owns key dims [8 sub, 8 sub + 8) and value dims [16 sub, 16 sub + 16)
       int row, seg, creator = -1;
       if (u < nold) {
         row = sm.seg_row[u];
@@ -462,24 +604,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
         seg = sm.created_seg[c2];
         creator = c2 < sinks ? c2 : sm.app_list[c2 - sinks];
       }
-      alignas(16) float K[32];
-      alignas(16) float V[64];
+      alignas(16) float K[8];
+      alignas(16) float V[16];
       int n;
       float rh;
       if (creator >= 0) {
         // new row: the creating token, unscaled; its value norm is the read radius
         float v2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) K[i] = tof(sm.k[creator][i]);
+        for (int i = 0; i < 8; ++i) K[i] = tof(Kc[creator][8 * sub + i]);
 #pragma unroll
-        for (int i = 0; i < 64; ++i) { V[i] = tof(sm.v[creator][i]); v2 = fmaf(V[i], V[i], v2); }
+        for (int i = 0; i < 16; ++i) { V[i] = tof(Vc[creator][16 * sub + i]); v2 = fmaf(V[i], V[i], v2); }
+        v2 += __shfl_xor(v2, 1);
+        v2 += __shfl_xor(v2, 2);
         n = 1;
         rh = sqrtf(v2);
       } else {
+        const float* ks = key_sum + (size_t)row * 32 + 8 * sub;
+        const float* vs = val_sum + (size_t)row * 64 + 16 * sub;
 #pragma unroll
-        for (int i = 0; i < 32; i += 4) *reinterpret_cast<float4*>(&K[i]) = *reinterpret_cast<const float4*>(key_sum + (size_t)row * 32 + i);
+        for (int i = 0; i < 8; i += 4) *reinterpret_cast<float4*>(&K[i]) = *reinterpret_cast<const float4*>(ks + i);
 #pragma unroll
-        for (int i = 0; i < 64; i += 4) *reinterpret_cast<float4*>(&V[i]) = *reinterpret_cast<const float4*>(val_sum + (size_t)row * 64 + i);
+        for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4*>(&V[i]) = *reinterpret_cast<const float4*>(vs + i);
         n = count[row];
         rh = rho[row];
       }
@@ -489,56 +635,93 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
           const int t = sm.srt_tok[r];
           const float gt = sm.g[t];
 #pragma unroll
-          for (int i = 0; i < 32; ++i) K[i] = fmaf(gt, tof(sm.k[t][i]), K[i]);
+          for (int i = 0; i < 8; ++i) K[i] = fmaf(gt, tof(Kc[t][8 * sub + i]), K[i]);
 #pragma unroll
-          for (int i = 0; i < 64; ++i) V[i] = fmaf(gt, tof(sm.v[t][i]), V[i]);
-          ++n;
+          for (int i = 0; i < 16; ++i) V[i] = fmaf(gt, tof(Vc[t][16 * sub + i]), V[i]);
+        }
+        n += e - b;
+      }
+      {
+        float* ks = key_sum + (size_t)row * 32 + 8 * sub;
+        float* vs = val_sum + (size_t)row * 64 + 16 * sub;
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) *reinterpret_cast<float4*>(ks + i) = *reinterpret_cast<const float4*>(&K[i]);
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4*>(vs + i) = *reinterpret_cast<const float4*>(&V[i]);
+      }
+      if (sub == 0) {
+        count[row] = n;
+        rho[row] = rh;
+        if (creator >= 0) atomicMax(&sm.rmax_bits, __float_as_uint(rh));
+      }
+      // row sums of squares and moments over the four lanes
+      float k2 = 0.f, ksum = 0.f, v2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { k2 = fmaf(K[i], K[i], k2); ksum += K[i]; }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v2 = fmaf(V[i], V[i], v2);
+      k2 += __shfl_xor(k2, 1);
+      k2 += __shfl_xor(k2, 2);
+      ksum += __shfl_xor(ksum, 1);
+      ksum += __shfl_xor(ksum, 2);
+      v2 += __shfl_xor(v2, 1);
+      v2 += __shfl_xor(v2, 2);
+      // unit key direction for the next cosine passes
+      {
+        const float inv = k2 > 0.f ? 1.0f / sqrtf(k2) : 0.f;
+        char* ur = unit + (size_t)row * 128;
+        if constexpr (Is<T>::bf) {
+          alignas(16) bf16 hi[8], lo[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float y = K[i] * inv;
+            hi[i] = (bf16)y;
+            lo[i] = (bf16)(y - (float)hi[i]);
+          }
+          copy16(ur + 16 * sub, hi);
+          copy16(ur + 64 + 16 * sub, lo);
+        } else {
+          alignas(16) float uu[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) uu[i] = K[i] * inv;
+          copy16(ur + 32 * sub, uu);
+          copy16(ur + 32 * sub + 16, uu + 4);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 32; i += 4) *reinterpret_cast<float4*>(key_sum + (size_t)row * 32 + i) = *reinterpret_cast<const float4*>(&K[i]);
-#pragma unroll
-      for (int i = 0; i < 64; i += 4) *reinterpret_cast<float4*>(val_sum + (size_t)row * 64 + i) = *reinterpret_cast<const float4*>(&V[i]);
-      count[row] = n;
-      rho[row] = rh;
-      store_unit<T>(unit + (size_t)row * 128, K);
-      if (creator >= 0) atomicMax(&sm.rmax_bits, __float_as_uint(rh));
       // just-in-time read form ([KVM summary, Core mechanisms 2]): LayerNorm of
       // K/n over the live dims (no affine); the value's direction u = V/|V|,
       // read as rho * u (the radius fixed at creation).
       const float invn = 1.0f / (float)n;
-      float mean = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) mean += K[i] * invn;
-      mean *= (1.0f / 32.0f);
+      const float mean = ksum * invn * (1.0f / 32.0f);
       float var = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
+      for (int i = 0; i < 8; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
+      var += __shfl_xor(var, 1);
+      var += __shfl_xor(var, 2);
       var *= (1.0f / 32.0f);
       const float rs = 1.0f / sqrtf(var + m.ln_eps);
-      float v2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 64; ++i) v2 = fmaf(V[i], V[i], v2);
-      const float vs = v2 > 0.f ? 1.0f / sqrtf(v2) : 0.f;
+      const float vsc = v2 > 0.f ? 1.0f / sqrtf(v2) : 0.f;
       const int ver = nver + u;
-      alignas(16) RT kh[32];
-      alignas(16) RT vh[64];
+      alignas(16) RT kh[8];
+      alignas(16) RT vh[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) kh[i] = fromf<RT>((K[i] * invn - mean) * rs);
+      for (int i = 0; i < 8; ++i) kh[i] = fromf<RT>((K[i] * invn - mean) * rs);
 #pragma unroll
-      for (int i = 0; i < 64; ++i) vh[i] = fromf<RT>(V[i] * vs);
+      for (int i = 0; i < 16; ++i) vh[i] = fromf<RT>(V[i] * vsc);
 #pragma unroll
-      for (int i = 0; i < 32; i += REL) {
-        copy16(pkey + (size_t)ver * 32 + i, &kh[i]);
-        copy16(kread + (size_t)row * 32 + i, &kh[i]);
+      for (int i = 0; i < 8; i += REL) {
+        copy16(pkey + (size_t)ver * 32 + 8 * sub + i, &kh[i]);
+        copy16(kread + (size_t)row * 32 + 8 * sub + i, &kh[i]);
       }
 #pragma unroll
-      for (int i = 0; i < 64; i += REL) {
-        copy16(pval + (size_t)ver * 64 + i, &vh[i]);
-        copy16(vread + (size_t)row * 64 + i, &vh[i]);
+      for (int i = 0; i < 16; i += REL) {
+        copy16(pval + (size_t)ver * 64 + 16 * sub + i, &vh[i]);
+        copy16(vread + (size_t)row * 64 + 16 * sub + i, &vh[i]);
       }
-      prho[ver] = rh;
-      idx[ioff + row] = ver;
+      if (sub == 0) {
+        prho[ver] = rh;
+        idx[ioff + row] = ver;
+      }
     }
     if (m.trace) {
       int* tslot = d.tslot + (size_t)s * m.max_tokens;
@@ -549,7 +732,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
       }
     }
     nver += nu;
-    __syncthreads();
+    prev_off = (int)ioff;
+    __syncthreads();  // the step's global writes are visible to every thread of the next step
     rmax_run = fmaxf(rmax_run, __uint_as_float(sm.rmax_bits));
     if (tid == 0) rmaxs[j] = rmax_run;
   }
@@ -960,6 +1144,384 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, i
 }
 
 // =====================================================================
+// Pipelined bf16 attention (chunks of 128 or 256 queries).
+// Same contraction layout as attn_kernel; what changes is the schedule:
+//   * the snapshot's version list is preloaded into LDS;
+//   * 64-key tiles are double-buffered: the global loads of tile T+1 are
+//     issued into registers before tile T is computed and written to the
+//     other LDS buffer after it, with one LDS-only barrier per tile;
+//   * softmax in log2 units with scale*log2(e) folded into the query, the
+//     running max fed to the MFMA as its C operand (the accumulator comes out
+//     as logit - max), and a lazy rescale: the reference max moves only when
+//     a tile exceeds it by more than 2^kTau;
+//   * rho_i / rho_max is folded into the staged state values.
+// =====================================================================
+constexpr int kIdxCap = 4096;   // snapshot version ids kept in LDS
+constexpr float kTau = 8.0f;    // lazy-rescale threshold (log2 units): p <= 2^8 in bf16/fp16
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Src src, int64_t c_begin, int n_q,
+                                                            int64_t end_pos, bf16* out) {
+  constexpr int C = NW * 32;
+  constexpr int NT = NW * 64;
+  constexpr int KSTR = 72, VSTR = 68;   // padded LDS strides (2-byte elements)
+  static_assert(NT >= 256, "one staging task per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][64 * VSTR];
+  __shared__ int sIdx[kIdxCap];
+
+  int s, cl;
+  {
+    const int b = blockIdx.x;
+    if (m.BH % 8 == 0) {
+      const int x = b & 7, k = b >> 3, spx = m.BH >> 3;
+      s = x + 8 * (k % spx);
+      cl = n_q - 1 - k / spx;
+    } else {
+      s = b % m.BH;
+      cl = n_q - 1 - b / m.BH;
+    }
+  }
+  const int64_t c = c_begin + cl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
+  const int64_t cpos = c * C;
+  const int64_t qpos = cpos + 32 * w + jl;
+  const bool qvalid = qpos < end_pos;
+  const int64_t qp = qvalid ? qpos : (end_pos - 1);
+  const float c2 = m.scale * kLog2e;
+
+  // ---- snapshot of chunk c - W/C - 1
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  int64_t ioff = 0;
+  float rmax = 1.f;
+  if (jj >= 0) {
+    const int4 sc4 = d.sched[jj];
+    S = sc4.z + sc4.x + sc4.y;
+    ioff = sc4.w;
+    const float rm = d.rmax[(size_t)s * m.J_cap + jj];
+    rmax = rm > 0.f ? rm : 1.f;
+  }
+  const int* idxg = d.idx + (size_t)s * m.idx_total + ioff;
+  const bool idx_lds = S <= kIdxCap;
+  if (idx_lds)
+    for (int i = tid; i < S; i += NT) sIdx[i] = idxg[i];
+  const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const f16* pv = reinterpret_cast<const f16*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const float* prho = d.prho + (size_t)s * m.V_cap;
+  const float inv_rmax = 1.0f / rmax;
+
+  // ---- query fragments (B operand of S^T = K . Q^T), pre-scaled by scale*log2(e)
+  const bf16* qrow = reinterpret_cast<const bf16*>(src.q) + ((size_t)s * src.n_call + (size_t)(qp - src.p0)) * 64;
+  bf16x8 qf[4];    // window: k-step kk holds dims 16kk + 8h + e (rotated for kk < 2)
+  f16x8 qs16[2];   // state: dims 32 + 16kk + 8h + e, fp16, scaled by 2^-qsh
+  int qsh = 0;
+  {
+    alignas(16) bf16 x[4][8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) copy16(x[kk], qrow + 16 * kk + 8 * h);
+    const float* rc = d.rope_cos + qp * 16;
+    const float* rsn = d.rope_sin + qp * 16;
+    float qmx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = tof(x[0][e]), b = tof(x[1][e]);
+      rot(a, b, rc[8 * h + e], rsn[8 * h + e]);
+      qf[0][e] = (bf16)(a * c2);
+      qf[1][e] = (bf16)(b * c2);
+      qf[2][e] = (bf16)(tof(x[2][e]) * c2);
+      qf[3][e] = (bf16)(tof(x[3][e]) * c2);
+      qmx = fmaxf(qmx, fmaxf(fabsf(tof(x[2][e])), fabsf(tof(x[3][e]))) * c2);
+    }
+    // fp16 range guard for the state query: exact power-of-two pre-scale
+    qmx = fmaxf(qmx, partner_f(qmx));
+    if (qmx >= 16384.f) {
+      int ex;
+      frexpf(qmx, &ex);
+      qsh = ex - 14;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qs16[0][e] = (f16)ldexpf(tof(x[2][e]) * c2, -qsh);
+      qs16[1][e] = (f16)ldexpf(tof(x[3][e]) * c2, -qsh);
+    }
+  }
+  const bool wave_qsh = __ballot(qsh != 0) != 0ull;
+
+  // ---- running softmax state: acc comes out of the MFMA as logit*c - mref
+  float mref = 0.f, lrun = 0.f;
+  bool started = false;
+  f32x16 negm = {};
+  f32x16 O0 = {}, O1 = {};
+
+  // tile geometry: state tiles first, then window tiles
+  const int n_st = (S + 63) >> 6;
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < end_pos ? cpos + C : end_pos;
+  const int n_wt = (int)((hi - lo + 63) >> 6);
+  const int n_tiles = n_st + n_wt;
+  const int64_t qlast = min(cpos + 32 * w + 31, end_pos - 1);
+  const int64_t qfirst = cpos + 32 * w;
+  const bf16* ring_k = reinterpret_cast<const bf16*>(d.ring_k) + (size_t)s * m.R * 64;
+  const bf16* ring_v = reinterpret_cast<const bf16*>(d.ring_v) + (size_t)s * m.R * 64;
+
+  // ---- staging: one K task and one V task per thread (threads >= 256 idle)
+  const bool stager = tid < 256;
+  const int ki = tid >> 2, kp = tid & 3;     // K task: key/row ki, part kp
+  const int vrp = tid >> 3, vdg = tid & 7;   // V task: rows 2vrp, 2vrp+1; dims 8vdg..8vdg+7
+  uint4 kr0, kr1, vr0, vr1;
+  float rho_a = 0.f, rho_b = 0.f;
+  int64_t k_pos = 0;   // window key position to rotate at commit (-1: no rotation)
+  bool k_zero = false;
+
+  auto row_version = [&](int r) -> int { return idx_lds ? sIdx[r] : idxg[r]; };
+  auto issue = [&](int T) {
+    if (!stager) return;
+    if (T < n_st) {
+      const int r0 = T << 6;
+      const int r = r0 + ki;
+      k_zero = r >= S;
+      k_pos = -1;
+      if (!k_zero) kr0 = *reinterpret_cast<const uint4*>(pk + (size_t)row_version(r) * 32 + 8 * kp);
+      const int ra = r0 + 2 * vrp;
+      if (ra < S) {
+        const int va = row_version(ra);
+        vr0 = *reinterpret_cast<const uint4*>(pv + (size_t)va * 64 + 8 * vdg);
+        rho_a = prho[va];
+      } else {
+        rho_a = 0.f;
+      }
+      if (ra + 1 < S) {
+        const int vb = row_version(ra + 1);
+        vr1 = *reinterpret_cast<const uint4*>(pv + (size_t)vb * 64 + 8 * vdg);
+        rho_b = prho[vb];
+      } else {
+        rho_b = 0.f;
+      }
+    } else {
+      const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
+      const int64_t pos = k0 + ki;
+      k_zero = pos >= hi;
+      k_pos = -1;
+      if (!k_zero) {
+        const bool in = pos >= src.p0;
+        const bf16* row = in ? reinterpret_cast<const bf16*>(src.k) + ((size_t)s * src.n_call + (size_t)(pos - src.p0)) * 64
+                             : ring_k + (size_t)(pos % m.R) * 64;
+        if (kp < 2) {
+          kr0 = *reinterpret_cast<const uint4*>(row + 8 * kp);
+          kr1 = *reinterpret_cast<const uint4*>(row + 16 + 8 * kp);
+          if (in) k_pos = pos;   // ring keys are stored rotated
+        } else {
+          kr0 = *reinterpret_cast<const uint4*>(row + 32 + 16 * (kp - 2));
+          kr1 = *reinterpret_cast<const uint4*>(row + 40 + 16 * (kp - 2));
+        }
+      }
+      const int64_t pa = k0 + 2 * vrp;
+      rho_a = pa < hi ? 1.f : 0.f;
+      rho_b = pa + 1 < hi ? 1.f : 0.f;
+      if (pa < hi) {
+        const bf16* row = pa >= src.p0 ? reinterpret_cast<const bf16*>(src.v) + ((size_t)s * src.n_call + (size_t)(pa - src.p0)) * 64
+                                       : ring_v + (size_t)(pa % m.R) * 64;
+        vr0 = *reinterpret_cast<const uint4*>(row + 8 * vdg);
+      }
+      if (pa + 1 < hi) {
+        const bf16* row = pa + 1 >= src.p0 ? reinterpret_cast<const bf16*>(src.v) + ((size_t)s * src.n_call + (size_t)(pa + 1 - src.p0)) * 64
+                                           : ring_v + (size_t)((pa + 1) % m.R) * 64;
+        vr1 = *reinterpret_cast<const uint4*>(row + 8 * vdg);
+      }
+    }
+  };
+  auto commit = [&](int T, int buf) {
+    if (!stager) return;
+    uint16_t* K = sK[buf] + ki * KSTR;
+    uint16_t* Vt = sVt[buf];
+    if (T < n_st) {
+      *reinterpret_cast<uint4*>(K + 8 * kp) = k_zero ? make_uint4(0, 0, 0, 0) : kr0;
+      // values: unit direction * rho / rho_max, fp16, transposed (dim-major)
+      const float fa = rho_a * inv_rmax, fb = rho_b * inv_rmax;
+      const f16* a = reinterpret_cast<const f16*>(&vr0);
+      const f16* b = reinterpret_cast<const f16*>(&vr1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const f16 x = (f16)(fa > 0.f ? (float)a[e] * fa : 0.f);
+        const f16 y = (f16)(fb > 0.f ? (float)b[e] * fb : 0.f);
+        const uint32_t pr = (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+        *reinterpret_cast<uint32_t*>(Vt + (8 * vdg + e) * VSTR + 2 * vrp) = pr;
+      }
+    } else {
+      uint4 x = kr0, y = kr1;
+      if (k_zero) {
+        x = make_uint4(0, 0, 0, 0);
+        y = x;
+      } else if (k_pos >= 0) {
+        bf16* xa = reinterpret_cast<bf16*>(&x);
+        bf16* ya = reinterpret_cast<bf16*>(&y);
+        const float* rc = d.rope_cos + k_pos * 16 + 8 * kp;
+        const float* rs = d.rope_sin + k_pos * 16 + 8 * kp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float a = (float)xa[e], b = (float)ya[e];
+          rot(a, b, rc[e], rs[e]);
+          xa[e] = (bf16)a;
+          ya[e] = (bf16)b;
+        }
+      }
+      if (kp < 2) {
+        *reinterpret_cast<uint4*>(K + 8 * kp) = x;
+        *reinterpret_cast<uint4*>(K + 16 + 8 * kp) = y;
+      } else {
+        *reinterpret_cast<uint4*>(K + 32 + 16 * (kp - 2)) = x;
+        *reinterpret_cast<uint4*>(K + 40 + 16 * (kp - 2)) = y;
+      }
+      const uint16_t* a = reinterpret_cast<const uint16_t*>(&vr0);
+      const uint16_t* b = reinterpret_cast<const uint16_t*>(&vr1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pr = (rho_a > 0.f ? (uint32_t)a[e] : 0u) | ((rho_b > 0.f ? (uint32_t)b[e] : 0u) << 16);
+        *reinterpret_cast<uint32_t*>(Vt + (8 * vdg + e) * VSTR + 2 * vrp) = pr;
+      }
+    }
+  };
+
+  // ---- online softmax over one 32-key subtile (acc = logit*c - mref; invalid keys already -inf)
+  auto softmax_p = [&](f32x16& acc, float (&p)[16]) {
+    float mx = acc[0];
+#pragma unroll
+    for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+    mx = fmaxf(mx, acc[15]);
+    mx = fmaxf(mx, partner_f(mx));
+    if ((!started && mx != -kInf) || mx > kTau) {
+      if (started) {
+        const float alpha = exp2f(-mx);
+        lrun *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { O0[r] *= alpha; O1[r] *= alpha; }
+      }
+      mref += mx;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { acc[r] -= mx; negm[r] = -mref; }
+      started = true;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { p[r] = exp2f(acc[r]); ps += p[r]; }
+    lrun += ps;
+  };
+
+  auto compute = [&](int T, int buf) {
+    const uint16_t* K = sK[buf];
+    const uint16_t* Vt = sVt[buf];
+    if (T < n_st) {
+      const int r0 = T << 6;
+#pragma unroll 1
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kb = 32 * sub;
+        if (r0 + kb >= S) continue;
+        const int lim = S - r0 - kb;
+        const f16* kr = reinterpret_cast<const f16*>(K) + (kb + jl) * KSTR;
+        f32x16 acc;
+        if (!wave_qsh) {
+          acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 8 * h), qs16[0], negm);
+          acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 16 + 8 * h), qs16[1], acc);
+        } else {
+          acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 8 * h), qs16[0], f32x16{});
+          acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 16 + 8 * h), qs16[1], acc);
+          const float sc = ldexpf(1.f, qsh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = acc[r] * sc - mref;
+        }
+        if (lim < 32) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
+        }
+        float p[16];
+        softmax_p(acc, p);
+        f16x8 pf0, pf1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pf0[e] = (f16)p[e]; pf1[e] = (f16)p[8 + e]; }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const f16* vr = reinterpret_cast<const f16*>(Vt) + (32 * dt + jl) * VSTR + kb;
+          f32x16& O = dt ? O1 : O0;
+          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 4 * h), pf0, O);
+          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 16 + 4 * h), pf1, O);
+        }
+      }
+      if (T == n_st - 1) {
+        // state values were staged at rho_i / rho_max: restore the scale once
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { O0[r] *= rmax; O1[r] *= rmax; }
+      }
+    } else {
+      const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
+#pragma unroll 1
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kb = 32 * sub;
+        const int64_t ks = k0 + kb;
+        if (ks >= hi || ks > qlast) continue;
+        const bf16* kr = reinterpret_cast<const bf16*>(K) + (kb + jl) * KSTR;
+        f32x16 acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 8 * h), qf[0], negm);
+#pragma unroll
+        for (int kk = 1; kk < 4; ++kk)
+          acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk + 8 * h), qf[kk], acc);
+        if (ks + 31 >= hi || ks + 31 > qfirst) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t kpos = ks + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kpos >= hi || kpos > qpos) acc[r] = -kInf;
+          }
+        }
+        float p[16];
+        softmax_p(acc, p);
+        bf16x8 pf0, pf1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pf0[e] = (bf16)p[e]; pf1[e] = (bf16)p[8 + e]; }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const bf16* vr = reinterpret_cast<const bf16*>(Vt) + (32 * dt + jl) * VSTR + kb;
+          f32x16& O = dt ? O1 : O0;
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 4 * h), pf0, O);
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 16 + 4 * h), pf1, O);
+        }
+      }
+    }
+  };
+
+  // ---- pipeline: prologue stages tile 0; each iteration loads T+1, computes T, stages T+1
+  __syncthreads();   // version ids in LDS
+  if (n_tiles > 0) {
+    issue(0);
+    commit(0, 0);
+  }
+  lds_barrier();
+  for (int T = 0; T < n_tiles; ++T) {
+    if (T + 1 < n_tiles) issue(T + 1);
+    compute(T, T & 1);
+    if (T + 1 < n_tiles) commit(T + 1, (T + 1) & 1);
+    lds_barrier();
+  }
+
+  // ---- normalise and store: lane holds dims 8*(r/4) + 4h + r%4 of its query
+  const float lt = lrun + partner_f(lrun);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qvalid) {
+    bf16* orow = out + ((size_t)s * src.n_call + (size_t)(qpos - src.p0)) * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const f32x16& O = dt ? O1 : O0;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        alignas(8) bf16 vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = (bf16)(O[4 * g4 + e] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * g4 + 4 * h) = *reinterpret_cast<const uint2*>(vals);
+      }
+    }
+  }
+}
+
+// =====================================================================
 // Ring maintenance: the last W + C positions (rotated keys, values, gate
 // logits) are kept so that decode steps and later prefill calls can see the
 // window and absorb the chunk that leaves it.
@@ -1219,8 +1781,14 @@ hipError_t attn_dispatch(const Dims& m, const Dev& d, const Src& src, int64_t cb
   switch (m.C) {
     case 32: attn_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, src, cb, nq, end, o); break;
     case 64: attn_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, src, cb, nq, end, o); break;
-    case 128: attn_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o); break;
-    case 256: attn_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o); break;
+    case 128:
+      if constexpr (Is<T>::bf) attn_bf16_kernel<4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o);
+      else attn_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o);
+      break;
+    case 256:
+      if constexpr (Is<T>::bf) attn_bf16_kernel<8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o);
+      else attn_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
