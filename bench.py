@@ -7,10 +7,13 @@ absorption scan, fused attention over [state || window], ring refresh.  Each
 timed step starts from an emptied state (kvm_state_reset, inside the timed
 region).  The line also carries:
 
-  roofline      the attention kernel (dominant): algorithmic MFMA FLOPs per
-                launch / its mean launch time from HIP events recorded by the
-                library around that launch on its stream, against the dense
-                bf16/fp16 MFMA peak.  `traffic` is the HBM bytes per launch
+  roofline      the attention kernel (dominant flops): algorithmic MFMA FLOPs
+                per launch / its mean launch time from HIP events recorded by
+                the library around each launch on the stream it runs on,
+                against the dense bf16/fp16 MFMA peak.  A prefill launches the
+                attention in several pieces beside the absorption scan, so the
+                per-launch figures are means over the pieces (total FLOPs /
+                total kernel time).  `traffic` is the HBM bytes per launch
                 from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (scaled by the
                 same counters on a plain copy of known size), taken from
                 profiles/ only when they were measured on this kernel source.
@@ -38,7 +41,8 @@ METRIC = "KVM-layer prefill tokens/s (B*H*N) + % bf16 MFMA peak; decode HBM GB/s
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "compressed_kv_state_amd", "csrc", "kvm_kernels.hip")
-COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_kernel_350m_sqrt8_counters.md")
+ATTN_KERNEL = "attn_bf16_kernel"   # the bf16 attention kernel for chunks of 128 / 256
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_bf16_kernel_350m_sqrt8_counters.md")
 
 
 def log(msg):
@@ -213,7 +217,10 @@ def copy_calibration():
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str):
-    """Reduce two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) to the summary bench reads."""
+    """Reduce two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) to the summary bench reads.
+
+    The scale of each counter is 1 GiB over its mean reading on the 1 GiB device copies of
+    --copy-calibration (the copy's dispatches are the large ones of the copy kernel)."""
     import csv
 
     def per_kernel(path, counter):
@@ -222,34 +229,71 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str
             for row in csv.DictReader(f):
                 if row.get("Counter_Name") != counter:
                     continue
-                name = row.get("Kernel_Name", "")
-                vals.setdefault(name, []).append(float(row["Counter_Value"]))
+                vals.setdefault(row.get("Kernel_Name", ""), []).append(float(row["Counter_Value"]))
         return vals
+
+    def copies(d):
+        v = [x for k, xs in d.items() if "copyBuffer" in k or "copy" in k.lower() for x in xs]
+        if not v:
+            raise SystemExit("no copy-kernel dispatches in the counter CSV (run with --copy-calibration)")
+        big = max(v)
+        v = [x for x in v if x >= 0.5 * big]
+        return sum(v) / len(v)
+
+    def kernel(d):
+        v = [x for k, xs in d.items() if ATTN_KERNEL in k for x in xs]
+        if not v:
+            raise SystemExit(f"no {ATTN_KERNEL} dispatches in the counter CSV")
+        return sum(v) / len(v), len(v)
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
-
-    def pick(d, key):
-        hits = {k: v for k, v in d.items() if key in k}
-        return max(hits.items(), key=lambda kv: sum(kv[1]))[1] if hits else []
-
-    copy_f, copy_w = pick(fetch, "copy") or pick(fetch, "elementwise"), pick(write, "copy") or pick(write, "elementwise")
-    attn_f, attn_w = pick(fetch, "attn_kernel"), pick(write, "attn_kernel")
     copy_kib = (1 << 30) / 1024.0
-    sf = copy_kib / (sum(copy_f) / len(copy_f)) if copy_f else 1.0
-    sw = copy_kib / (sum(copy_w) / len(copy_w)) if copy_w else 1.0
-    f_kib = sum(attn_f) / len(attn_f)
-    w_kib = sum(attn_w) / len(attn_w)
+    cf, cw = copies(fetch), copies(write)
+    sf, sw = copy_kib / cf, copy_kib / cw
+    (f_kib, nf), (w_kib, nw) = kernel(fetch), kernel(write)
     traffic = (f_kib * sf + w_kib * sw) * 1024.0
     with open(out_md, "w") as f:
-        f.write("# attn_kernel HBM traffic, 350M-shaped sqrt workload (B=2, H=16, N=32768), one launch\n\n")
-        f.write(f"Command: `{command}`\n\n")
-        f.write("| counter | attn_kernel KiB/dispatch | copy kernel KiB/dispatch (1 GiB moved) | scale |\n|---|---|---|---|\n")
-        f.write(f"| FETCH_SIZE | {f_kib:.0f} | {sum(copy_f) / max(len(copy_f), 1):.0f} | {sf:.4f} |\n")
-        f.write(f"| WRITE_SIZE | {w_kib:.0f} | {sum(copy_w) / max(len(copy_w), 1):.0f} | {sw:.4f} |\n\n")
+        f.write(f"# {ATTN_KERNEL} HBM traffic, 350M-shaped sqrt workload (B=2, H=16, N=32768), per launch\n\n")
+        f.write(f"Command (one pass per counter): `{command}`\n\n")
+        f.write(f"| counter | {ATTN_KERNEL} KiB/dispatch (mean of {nf}/{nw}) | copy kernel KiB/dispatch "
+                f"(1 GiB moved) | scale |\n|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {f_kib:.0f} | {cf:.0f} | {sf:.4f} |\n")
+        f.write(f"| WRITE_SIZE | {w_kib:.0f} | {cw:.0f} | {sw:.4f} |\n\n")
+        f.write("A prefill launches the attention in pieces beside the scan; the figures are means over\n"
+                "the pieces of the profiled prefills, like bench.py's per-launch FLOPs and time.\n\n")
         f.write(f"traffic_bytes_per_launch: {traffic:.6e}\n")
         f.write(f"kernel_source_sha256_16: {kernel_sha()}\n")
     print(f"wrote {out_md}: traffic {traffic / 1e9:.3f} GB per launch")
+
+
+def summarize_trace(db: str, out_md: str, command: str, title: str):
+    """Per-kernel dispatch statistics from a rocprofv3 --kernel-trace database (rocpd sqlite)."""
+    import sqlite3
+    import statistics
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, grid_x, workgroup_x, start, end from kernels order by start").fetchall()
+    dec0 = min([t0 for name, _, _, t0, _ in rows if "dec_attn_kernel" in name] or [float("inf")])
+    prefill_attn = [(t1 - t0) / 1e3 for name, _, _, t0, t1 in rows if ATTN_KERNEL in name and t0 < dec0]
+    sel = {}
+    for name, gx, wx, t0, t1 in rows:
+        if "kvm" not in name:
+            continue
+        short = re.sub(r"^.*?(\w+_kernel)", r"\1", name.replace("(anonymous namespace)::", ""))
+        short = re.sub(r"_ZN3kvm12_GLOBAL__N_1\d+", "", short)
+        sel.setdefault((short[:60], gx, wx), []).append((t1 - t0) / 1e3)
+    with open(out_md, "w") as f:
+        f.write(f"# {title}\n\nCommand: `{command}`\n\n")
+        f.write("| kernel | grid (threads) | block | calls | total us | avg us | min us | max us |\n"
+                "|---|---|---|---|---|---|---|---|\n")
+        for (short, gx, wx), d in sorted(sel.items(), key=lambda kv: -sum(kv[1])):
+            f.write(f"| {short} | {gx} | {wx} | {len(d)} | {sum(d):.1f} | {statistics.mean(d):.1f} | "
+                    f"{min(d):.1f} | {max(d):.1f} |\n")
+        if prefill_attn:
+            f.write(f"\n{ATTN_KERNEL} in the prefill workload (dispatches before the first decode kernel): "
+                    f"{len(prefill_attn)} dispatches, mean {statistics.mean(prefill_attn):.1f} us, "
+                    f"total {sum(prefill_attn):.1f} us\n")
+    print(open(out_md).read())
 
 
 def main():
@@ -263,8 +307,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true", help="add a 1 GiB device copy (counter scaling)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("DB", "OUT_MD", "COMMAND", "TITLE"))
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], COUNTERS_MD,
                            args.summarize_counters[2])
@@ -283,8 +331,9 @@ def main():
     wp, wd = WORKLOADS[2], WORKLOADS[4]
 
     cfg, ms_step, prof = bench_prefill(wp, args.steps, args.warmup)
-    attn_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
-    flops = attn_flops(cfg, wp.n_tokens)
+    launches = max(prof["attn_launches"], 1)
+    attn_ms = prof["attn_ms"] / launches
+    flops = attn_flops(cfg, wp.n_tokens) * args.steps / launches   # mean per launch
     achieved = flops / (attn_ms * 1e-3) / 1e12
     traffic = read_counters()
     tokens = wp.seqs * wp.n_tokens
@@ -306,9 +355,11 @@ def main():
                    "alpha": wp.alpha, "final_rows": prof["final_rows"]},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_MFMA_TFLOPS, "traffic": traffic,
-                     "kernel": "attn_kernel", "flops_per_launch": flops, "ms_per_launch": attn_ms},
+                     "kernel": ATTN_KERNEL, "flops_per_launch": flops, "ms_per_launch": attn_ms,
+                     "launches_per_step": launches / args.steps},
         "phases_ms_per_step": {"scan": prof["scan_ms"] / args.steps, "attn": prof["attn_ms"] / args.steps,
-                               "ring": prof["ring_ms"] / args.steps},
+                               "ring": prof["ring_ms"] / args.steps,
+                               "note": "scan and attention overlap on two streams; phases sum past the step"},
     }
     if not args.no_decode:
         res["decode"] = bench_decode(wd, args.decode_steps)

@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -34,9 +35,15 @@ struct kvm_state {
   };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
+  // prefill overlap: attention of ready query chunks runs on `side` while the
+  // scan continues on the caller's stream (fork/join through `sync_ev`)
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> sync_ev;
   ~kvm_state() {
     for (Rec& r : recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
     for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+    for (hipEvent_t e : sync_ev) (void)hipEventDestroy(e);
+    if (side) (void)hipStreamDestroy(side);
   }
 };
 
@@ -247,6 +254,31 @@ hipError_t timed(kvm_state* st, int phase, hipStream_t hs, F launch) {
   return e;
 }
 
+// The i-th fork/join event of a prefill call (created on first use, reused by later calls:
+// a wait binds to the record that precedes it in host order).
+hipEvent_t sync_event(kvm_state* st, size_t i) {
+  while (st->sync_ev.size() <= i) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    st->sync_ev.push_back(e);
+  }
+  return st->sync_ev[i];
+}
+
+// Absorption [a0, a1) in pieces that shrink by a third each time (at least
+// kMinPiece chunks): attention of the chunks a piece makes ready overlaps the
+// next piece, and only the last, small piece's dependants run after the scan.
+constexpr int64_t kMinPiece = 4;
+std::vector<int64_t> scan_pieces(int64_t a0, int64_t a1) {
+  std::vector<int64_t> b{a0};
+  while (b.back() < a1) {
+    const int64_t rem = a1 - b.back();
+    const int64_t p = std::max<int64_t>(kMinPiece, (rem + 2) / 3);
+    b.push_back(std::min(a1, b.back() + p));
+  }
+  return b;
+}
+
 int rows_after(const kvm_state* st, int64_t j) {
   if (j < 0) return 0;
   const int32_t* s = &st->sched[(size_t)j * 4];
@@ -378,12 +410,52 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   kvm::Src src{q, k, v, gate_logits, p0, n_tokens};
   hipError_t err = hipSuccess;
-  if (a1 > st->absorbed)
-    err = timed(st, kScan, hs, [&] { return kvm::launch_scan(m, st->d, src, (int)st->absorbed, (int)a1, hs); });
-  if (err != hipSuccess) return hip_fail(st, err, "scan launch");
-  err = timed(st, kAttn, hs,
-              [&] { return kvm::launch_attn(m, st->d, src, c_first, (int)(c_last - c_first + 1), e, out, hs); });
-  if (err != hipSuccess) return hip_fail(st, err, "attention launch");
+  auto attn = [&](hipStream_t sx, int64_t cb, int64_t ce) {  // query chunks [cb, ce]
+    return timed(st, kAttn, sx,
+                 [&] { return kvm::launch_attn(m, st->d, src, cb, (int)(ce - cb + 1), e, out, sx); });
+  };
+  if (a1 > st->absorbed) {
+    // Query chunk c reads the state after chunks [0, c - W/C) are absorbed.
+    // Fork: the side stream starts after everything queued on hs so far.
+    const int64_t wc = m.W / m.C;
+    const std::vector<int64_t> pieces = scan_pieces(st->absorbed, a1);
+    if (!st->side) err = hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking);
+    size_t ev = 0;
+    hipEvent_t fork = err == hipSuccess ? sync_event(st, ev++) : nullptr;
+    if (err == hipSuccess && !fork) err = hipErrorOutOfMemory;
+    if (err == hipSuccess) err = hipEventRecord(fork, hs);
+    if (err == hipSuccess) err = hipStreamWaitEvent(st->side, fork, 0);
+    int64_t done = c_first - 1;  // attention queued through this chunk
+    auto release = [&](int64_t absorbed) {
+      const int64_t hi = std::min(c_last, absorbed + wc);
+      if (err == hipSuccess && hi > done) {
+        err = attn(st->side, done + 1, hi);
+        done = hi;
+      }
+    };
+    release(pieces.front());
+    for (size_t i = 0; i + 1 < pieces.size() && err == hipSuccess; ++i) {
+      const int64_t jb = pieces[i], je = pieces[i + 1];
+      err = timed(st, kScan, hs, [&] { return kvm::launch_scan(m, st->d, src, (int)jb, (int)je, hs); });
+      if (err == hipSuccess && done < c_last) {
+        hipEvent_t ready = sync_event(st, ev++);
+        if (!ready) err = hipErrorOutOfMemory;
+        if (err == hipSuccess) err = hipEventRecord(ready, hs);
+        if (err == hipSuccess) err = hipStreamWaitEvent(st->side, ready, 0);
+        release(je);
+      }
+    }
+    // Join: hs continues only after the side stream's attention.
+    hipEvent_t join = err == hipSuccess ? sync_event(st, ev++) : nullptr;
+    if (err == hipSuccess && !join) err = hipErrorOutOfMemory;
+    if (err == hipSuccess) err = hipEventRecord(join, st->side);
+    if (err == hipSuccess) err = hipStreamWaitEvent(hs, join, 0);
+    if (err == hipSuccess && done != c_last) err = hipErrorInvalidValue;
+    if (err != hipSuccess) return hip_fail(st, err, "scan/attention launch");
+  } else {
+    err = attn(hs, c_first, c_last);
+    if (err != hipSuccess) return hip_fail(st, err, "attention launch");
+  }
   const int64_t from = e - m.R > p0 ? e - m.R : p0;
   err = timed(st, kRing, hs, [&] { return kvm::launch_ring_fill(m, st->d, src, from, e, hs); });
   if (err != hipSuccess) return hip_fail(st, err, "ring launch");

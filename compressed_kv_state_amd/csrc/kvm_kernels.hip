@@ -36,6 +36,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr float kInf = __builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
 
+// 2^x with the hardware instruction alone (no denormal-range fix-up): softmax
+// arguments are <= 8 here, and a result that would be denormal (x < -126)
+// contributes nothing next to the running maximum's weight 1.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 template <typename T> struct Is;
 template <> struct Is<float> { static constexpr bool bf = false; };
 template <> struct Is<bf16> { static constexpr bool bf = true; };
@@ -985,10 +990,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, i
     mx = fmaxf(mx, partner_f(mx));
     const float mnew = fmaxf(mrun, mx);
     const float muse = mnew == -kInf ? 0.f : mnew;
-    const float alpha = exp2f(mrun - muse);
+    const float alpha = exp2_fast(mrun - muse);
     float ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { p[r] = exp2f(sc[r] - muse); ps += p[r]; }
+    for (int r = 0; r < 16; ++r) { p[r] = exp2_fast(sc[r] - muse); ps += p[r]; }
     lrun = lrun * alpha + ps;
     mrun = mnew;
 #pragma unroll
@@ -1392,7 +1397,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
     mx = fmaxf(mx, partner_f(mx));
     if ((!started && mx != -kInf) || mx > kTau) {
       if (started) {
-        const float alpha = exp2f(-mx);
+        const float alpha = exp2_fast(-mx);
         lrun *= alpha;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { O0[r] *= alpha; O1[r] *= alpha; }
@@ -1404,7 +1409,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
     }
     float ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { p[r] = exp2f(acc[r]); ps += p[r]; }
+    for (int r = 0; r < 16; ++r) { p[r] = exp2_fast(acc[r]); ps += p[r]; }
     lrun += ps;
   };
 
@@ -1466,11 +1471,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
         for (int kk = 1; kk < 4; ++kk)
           acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk + 8 * h), qf[kk], acc);
         if (ks + 31 >= hi || ks + 31 > qfirst) {
+          // key ks + off is valid for this lane's query iff off < lim
+          const int lim = (int)min(hi - ks, qpos - ks + 1);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t kpos = ks + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (kpos >= hi || kpos > qpos) acc[r] = -kInf;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
         }
         float p[16];
         softmax_p(acc, p);
@@ -1622,8 +1627,8 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q
       for (int msk = 1; msk < LPR; msk <<= 1) dot += __shfl_xor(dot, msk);
       const float lg = dot * sl2;
       const float mnew = fmaxf(mrun, lg);
-      const float alpha = exp2f(mrun - mnew);
-      const float p = exp2f(lg - mnew);
+      const float alpha = exp2_fast(mrun - mnew);
+      const float p = exp2_fast(lg - mnew);
       const float pr = p * rho;
       lrun = lrun * alpha + p;
       mrun = mnew;
@@ -1659,8 +1664,8 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q
       for (int msk = 1; msk < LPK; msk <<= 1) dot += __shfl_xor(dot, msk);
       const float lg = dot * sl2;
       const float mnew = fmaxf(mrun, lg);
-      const float alpha = exp2f(mrun - mnew);
-      const float p = exp2f(lg - mnew);
+      const float alpha = exp2_fast(mrun - mnew);
+      const float p = exp2_fast(lg - mnew);
       lrun = lrun * alpha + p;
       mrun = mnew;
 #pragma unroll
@@ -1672,8 +1677,8 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q
     const float mo = __shfl_xor(mrun, msk);
     const float lo_ = __shfl_xor(lrun, msk);
     const float mn = fmaxf(mrun, mo);
-    const float a1 = mrun == -kInf ? 0.f : exp2f(mrun - mn);
-    const float a2 = mo == -kInf ? 0.f : exp2f(mo - mn);
+    const float a1 = mrun == -kInf ? 0.f : exp2_fast(mrun - mn);
+    const float a2 = mo == -kInf ? 0.f : exp2_fast(mo - mn);
     lrun = lrun * a1 + lo_ * a2;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1696,7 +1701,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q
     float Lsum = 0.f, Ov = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float a = red[ww][0] == -kInf ? 0.f : exp2f(red[ww][0] - M);
+      const float a = red[ww][0] == -kInf ? 0.f : exp2_fast(red[ww][0] - M);
       Lsum += red[ww][1] * a;
       Ov += red[ww][4 + tid] * a;
     }
@@ -1715,7 +1720,7 @@ __global__ void dec_combine_kernel(Dims m, Dev d, int nseg, T* out) {
   float L = 0.f, O = 0.f;
   for (int g = 0; g < nseg; ++g) {
     const float mg = pp[g * kPartStride];
-    const float a = mg == -kInf ? 0.f : exp2f(mg - M);
+    const float a = mg == -kInf ? 0.f : exp2_fast(mg - M);
     L += pp[g * kPartStride + 1] * a;
     O += pp[g * kPartStride + 4 + tid] * a;
   }

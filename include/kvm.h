@@ -132,7 +132,8 @@ kvm_status kvm_schedule(const kvm_config* cfg, int64_t n_chunks, int32_t* sinks,
 kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t workspace_bytes,
                             void* stream, kvm_state** out);
 
-/* Free the host-side state.  Does not touch the workspace.  NULL is allowed. */
+/* Free the host-side state (and its internal stream and events).  Does not
+ * touch the workspace.  NULL is allowed. */
 kvm_status kvm_state_destroy(kvm_state* st);
 
 /* Chunk-parallel prefill of n_tokens tokens at the state's current position
@@ -145,6 +146,11 @@ kvm_status kvm_state_destroy(kvm_state* st);
  * The position must be a multiple of chunk (else KVM_E_STATE);
  * position + n_tokens must not exceed max_tokens (else KVM_E_CAPACITY).
  * n_tokens == 0 is a no-op.  out may not alias q, k, v.
+ * Stream order: the call's work starts after everything queued on `stream`
+ * before it and everything queued after it starts after the call's work.
+ * Inside, attention of query chunks whose state is ready runs on a second,
+ * library-owned stream (created on first use, default priority) beside the
+ * remaining absorption, joined back to `stream` with events.
  * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_CAPACITY, KVM_E_HIP. */
 kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* v,
                        const float* gate_logits, void* out, int64_t n_tokens, void* stream);
