@@ -144,7 +144,7 @@ struct Plan {
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
   size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, rmax, idx, tslot, tkind, ring_k, ring_v,
-      ring_l, rope_cos, rope_sin, sch, nver, part, total;
+      ring_l, rope_cos, rope_sin, sch, nver, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -179,7 +179,6 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   m.V_cap = J * c->chunk;
   m.idx_total = idx_total;
   m.max_tokens = c->max_tokens;
-  m.n_seg_max = (int)((S_cap + kvm::kDecSeg - 1) / kvm::kDecSeg + (m.R + kvm::kDecSeg - 1) / kvm::kDecSeg);
   m.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
   m.ln_eps = c->ln_eps;
   m.bf16 = c->dtype == KVM_BF16;
@@ -213,7 +212,6 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   p.rope_sin = take((size_t)c->max_tokens * 16 * 4);
   p.sch = take((size_t)J * 16);
   p.nver = take(BH * 4);
-  p.part = take(BH * (size_t)m.n_seg_max * kvm::kPartStride * 4);
   p.total = off;
   return KVM_OK;
 }
@@ -360,7 +358,6 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     d.rope_sin = reinterpret_cast<float*>(b + p.rope_sin);
     d.sched = reinterpret_cast<int4*>(b + p.sch);
     d.nver = reinterpret_cast<int*>(b + p.nver);
-    d.part = reinterpret_cast<float*>(b + p.part);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipMemsetAsync(d.nver, 0, (size_t)st->m.BH * 4, hs);
     if (e == hipSuccess && st->m.trace) {
@@ -489,9 +486,7 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
   }
   const int rows = rows_after(st, absorbed - 1);
   hipError_t err = timed(st, kDecAttn, hs, [&] {
-    hipError_t e2 = kvm::launch_decode_ring(m, st->d, k, v, gate_logits, t, hs);
-    if (e2 == hipSuccess) e2 = kvm::launch_decode_attn(m, st->d, q, t, rows, out, hs);
-    return e2;
+    return kvm::launch_decode(m, st->d, q, k, v, gate_logits, t, rows, out, hs);
   });
   if (err != hipSuccess) return hip_fail(st, err, "decode launch");
   st->pos = t + 1;

@@ -11,8 +11,6 @@ namespace kvm {
 constexpr int kHeadDim = 64;   // head dimension
 constexpr int kRopeDims = 32;  // rotary dims [0,32)
 constexpr int kLive = 32;      // live state-key dims [32,64)
-constexpr int kDecSeg = 256;   // keys per decode split-K segment
-constexpr int kPartStride = 68;  // floats per decode partial: m, l, pad, pad, o[64]
 
 // Sizes fixed at state creation.
 struct Dims {
@@ -26,7 +24,6 @@ struct Dims {
   int64_t V_cap;      // row versions per sequence (<= J_cap * C)
   int64_t idx_total;  // index-list entries per sequence (sum over j of rows after chunk j)
   int64_t max_tokens;
-  int n_seg_max;      // decode split-K segments per sequence
   float scale;        // softmax scale
   float ln_eps;
   int bf16;           // 1: bf16 storage and MFMA; 0: fp32
@@ -61,7 +58,6 @@ struct Dev {
   float* rope_sin;   // [max_tokens][16]
   int4* sched;       // [J_cap] (sinks_j, appends_j, rows_before_j, idx_off_j)
   int* nver;         // [BH] versions used
-  float* part;       // [BH][n_seg_max][kPartStride] decode partials
 };
 
 // Token source for a launch: positions >= p0 come from the call's inputs
@@ -84,12 +80,10 @@ hipError_t launch_attn(const Dims& m, const Dev& d, const Src& src, int64_t c_be
                        void* out, hipStream_t st);
 // Copy positions [from, to) of the call inputs into the ring (keys rotated).
 hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st);
-// Decode query at position t over `rows` state rows and the ring window; out [BH][64].
-hipError_t launch_decode_attn(const Dims& m, const Dev& d, const void* q, int64_t t, int rows, void* out,
-                              hipStream_t st);
-// Write decode token t (rotated key, value, gate logit) into ring slot t % R.
-hipError_t launch_decode_ring(const Dims& m, const Dev& d, const void* k, const void* v, const float* l, int64_t t,
-                              hipStream_t st);
+// Decode step at position t: write token t (rotated key, value, gate logit) into ring
+// slot t % R, then attend over `rows` state rows and the window; out [BH][64].
+hipError_t launch_decode(const Dims& m, const Dev& d, const void* q, const void* k, const void* v, const float* l,
+                         int64_t t, int rows, void* out, hipStream_t st);
 // Gather the read form of snapshot j (rows_j rows, version list at idx_off) into dense
 // key [BH][rows][32] RT, unit value [BH][rows][64] RT, radius [BH][rows] f32 (any may be null).
 hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t idx_off, void* key_out,

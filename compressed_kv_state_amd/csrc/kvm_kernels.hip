@@ -1558,121 +1558,144 @@ __global__ void ring_fill_kernel(Dims m, Dev d, Src src, int64_t from, int64_t t
 }
 
 // =====================================================================
-// Decode: split-K over [state rows || window keys] then a combine.
-// Segment sg < nss covers state rows [256 sg, 256 sg + 256); the rest cover
-// window positions.  Each wave takes 64 consecutive keys; a group of lanes
-// shares one key (state: LPR lanes, window: LPK lanes), each lane owning a
-// slice of the dims.  Partials (max, sum, o[64]) go to d.part.
+// Decode ([KVM abstract]: per-token cost independent of the context length;
+// [KVM summary, Core mechanisms 4]): one workgroup per sequence, eight waves.
+// The new token's rotated key, value and gate logit go to ring slot t % R;
+// query t attends over the state rows (unrotated q against the read-form
+// keys, values rho * u) and the window [lo, t] (rotated q against rotated
+// keys) with one softmax.  Eight lanes share a key, lane e owning value dims
+// [8e, 8e + 8) and a slice of the key dims; every sequence has the same row
+// count, so the workgroups are balanced.  Waves split the state rows and the
+// window keys evenly, then combine in LDS.
 // =====================================================================
+constexpr int kDecWaves = 8;
+
 template <typename T>
-__global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q, int64_t t, int S, int nss,
-                                                       int64_t lo) {
-  constexpr bool BF = Is<T>::bf;
-  __shared__ float sq[64], sqr[64];
-  __shared__ float red[4][kPartStride];
-  const int s = blockIdx.y, sg = blockIdx.x;
+__global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, const T* q, const T* kin, const T* vin,
+                                                            const float* lin, T* out, int64_t t, int S,
+                                                            int64_t lo) {
+  using RT = typename Rd<T>::type;
+  constexpr int L = 8;
+  __shared__ float sq[64], sqr[64], skt[64], svt[64];
+  __shared__ float red_m[kDecWaves], red_l[kDecWaves];
+  __shared__ float red_o[kDecWaves][64];
+  const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float sl2 = m.scale * kLog2e;
   if (tid < 64) {
+    // query (scaled into log2 units) and the new token; RoPE on dims [0, 32)
     const T* qr = q + (size_t)s * 64;
-    const float x = tof(qr[tid]);
-    sq[tid] = x;
-    float y = x;
+    const T* kr = kin + (size_t)s * 64;
+    float x = tof(qr[tid]), y = x, kx = tof(kr[tid]);
     if (tid < 32) {
       const int jf = tid & 15;
       const float cs = d.rope_cos[t * 16 + jf], sn = d.rope_sin[t * 16 + jf];
       y = tid < 16 ? x * cs - tof(qr[tid + 16]) * sn : x * cs + tof(qr[tid - 16]) * sn;
+      kx = tid < 16 ? kx * cs - tof(kr[tid + 16]) * sn : kx * cs + tof(kr[tid - 16]) * sn;
     }
-    sqr[tid] = y;
+    const T kq = fromf<T>(kx);
+    const T vv = vin[(size_t)s * 64 + tid];
+    sq[tid] = x * sl2;
+    sqr[tid] = y * sl2;
+    skt[tid] = tof(kq);
+    svt[tid] = tof(vv);
+    const size_t slot = (size_t)s * m.R + (size_t)(t % m.R);
+    reinterpret_cast<T*>(d.ring_k)[slot * 64 + tid] = kq;
+    reinterpret_cast<T*>(d.ring_v)[slot * 64 + tid] = vv;
+    if (tid == 0) d.ring_l[slot] = lin[s];
   }
   __syncthreads();
 
+  const int e = lane & (L - 1), grp = lane >> 3;
   float mrun = -kInf, lrun = 0.f;
-  float o[16];
+  float o[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = 0.f;
-  int L;       // lanes per key
-  int vdim0;   // first value dim of this lane
-  int nvd;     // value dims of this lane
-  if (sg < nss) {
-    // state rows: read-form key (RT), unit value direction (RT), radius (f32)
-    using RT = typename Rd<T>::type;
-    constexpr int LPR = BF ? 4 : 8;
-    constexpr int KD = 32 / LPR, VD = 64 / LPR;
-    constexpr int REL = 16 / (int)sizeof(RT);
-    L = LPR;
-    const int e = lane % LPR, grp = lane / LPR;
-    vdim0 = e * VD;
-    nvd = VD;
-    float qk[KD];
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  auto update = [&](float lg, float pscale, const float (&vv)[8]) {
+    const float mnew = fmaxf(mrun, lg);
+    const float alpha = exp2_fast(mrun - mnew);
+    const float p = exp2_fast(lg - mnew);
+    lrun = lrun * alpha + p;
+    mrun = mnew;
+    const float pv = p * pscale;
 #pragma unroll
-    for (int i = 0; i < KD; ++i) qk[i] = sq[32 + e * KD + i];
+    for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vv[i], o[i] * alpha);
+  };
+
+  // ---- state rows: read-form key dims [32 + 4e, 32 + 4e + 4), unit value direction, radius
+  {
+    float qk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qk[i] = sq[32 + 4 * e + i];
     const RT* kr = reinterpret_cast<const RT*>(d.kread) + (size_t)s * m.S_cap * 32;
     const RT* vr = reinterpret_cast<const RT*>(d.vread) + (size_t)s * m.S_cap * 64;
     const float* rr = d.rho + (size_t)s * m.S_cap;
-    const int rb = sg * kDecSeg + w * 64;
-    const int re = min(S, rb + 64);
-    for (int row = rb + grp; row < re; row += 64 / LPR) {
-      alignas(16) RT kk[KD];
-      alignas(16) RT vv[VD];
+    const int per = (S + kDecWaves - 1) / kDecWaves;
+    const int rb = w * per, re = min(S, rb + per);
+#pragma unroll 2
+    for (int row = rb + grp; row < re; row += 64 / L) {
+      alignas(16) RT kk[4];
+      alignas(16) RT vh[8];
+      if constexpr (sizeof(RT) == 2) {
+        *reinterpret_cast<uint2*>(kk) = *reinterpret_cast<const uint2*>(kr + (size_t)row * 32 + 4 * e);
+      } else {
+        copy16(kk, kr + (size_t)row * 32 + 4 * e);
+      }
 #pragma unroll
-      for (int i = 0; i < KD; i += REL) copy16(&kk[i], kr + (size_t)row * 32 + e * KD + i);
-#pragma unroll
-      for (int i = 0; i < VD; i += REL) copy16(&vv[i], vr + (size_t)row * 64 + e * VD + i);
+      for (int i = 0; i < 8; i += 16 / (int)sizeof(RT)) copy16(&vh[i], vr + (size_t)row * 64 + 8 * e + i);
       const float rho = rr[row];
       float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < KD; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
+      for (int i = 0; i < 4; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      dot += __shfl_xor(dot, 4);
+      float vv[8];
 #pragma unroll
-      for (int msk = 1; msk < LPR; msk <<= 1) dot += __shfl_xor(dot, msk);
-      const float lg = dot * sl2;
-      const float mnew = fmaxf(mrun, lg);
-      const float alpha = exp2_fast(mrun - mnew);
-      const float p = exp2_fast(lg - mnew);
-      const float pr = p * rho;
-      lrun = lrun * alpha + p;
-      mrun = mnew;
-#pragma unroll
-      for (int i = 0; i < VD; ++i) o[i] = fmaf(pr, tof(vv[i]), o[i] * alpha);
-    }
-  } else {
-    constexpr int LPK = BF ? 8 : 16;
-    constexpr int KD = 64 / LPK;
-    L = LPK;
-    const int e = lane % LPK, grp = lane / LPK;
-    vdim0 = e * KD;
-    nvd = KD;
-    float qk[KD];
-#pragma unroll
-    for (int i = 0; i < KD; ++i) qk[i] = sqr[e * KD + i];
-    const T* rk = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
-    const T* rv = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
-    const int64_t pb = lo + (int64_t)(sg - nss) * kDecSeg + w * 64;
-    const int64_t pe = min(t + 1, pb + 64);
-    for (int64_t pos = pb + grp; pos < pe; pos += 64 / LPK) {
-      const size_t slot = (size_t)(pos % m.R);
-      alignas(16) T kk[KD];
-      alignas(16) T vv[KD];
-#pragma unroll
-      for (int i = 0; i < KD; i += 16 / (int)sizeof(T)) copy16(&kk[i], rk + slot * 64 + e * KD + i);
-#pragma unroll
-      for (int i = 0; i < KD; i += 16 / (int)sizeof(T)) copy16(&vv[i], rv + slot * 64 + e * KD + i);
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < KD; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
-#pragma unroll
-      for (int msk = 1; msk < LPK; msk <<= 1) dot += __shfl_xor(dot, msk);
-      const float lg = dot * sl2;
-      const float mnew = fmaxf(mrun, lg);
-      const float alpha = exp2_fast(mrun - mnew);
-      const float p = exp2_fast(lg - mnew);
-      lrun = lrun * alpha + p;
-      mrun = mnew;
-#pragma unroll
-      for (int i = 0; i < KD; ++i) o[i] = fmaf(p, tof(vv[i]), o[i] * alpha);
+      for (int i = 0; i < 8; ++i) vv[i] = tof(vh[i]);
+      update(dot, rho, vv);
     }
   }
-  // combine the key groups of the wave (lanes with equal lane % L hold the same dims)
+  // ---- window keys [lo, t] (ring slots; position t from LDS)
+  {
+    float qk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qk[i] = sqr[8 * e + i];
+    const T* rk = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
+    const T* rv = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
+    const int nwk = (int)(t - lo + 1);
+    const int per = (nwk + kDecWaves - 1) / kDecWaves;
+    const int kb = w * per, ke = min(nwk, kb + per);
+#pragma unroll 2
+    for (int i0 = kb + grp; i0 < ke; i0 += 64 / L) {
+      const int64_t pos = lo + i0;
+      float kf[8], vv[8];
+      if (pos == t) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { kf[i] = skt[8 * e + i]; vv[i] = svt[8 * e + i]; }
+      } else {
+        const size_t slot = (size_t)(pos % m.R);
+        alignas(16) T kh[8];
+        alignas(16) T vh[8];
+#pragma unroll
+        for (int i = 0; i < 8; i += 16 / (int)sizeof(T)) {
+          copy16(&kh[i], rk + slot * 64 + 8 * e + i);
+          copy16(&vh[i], rv + slot * 64 + 8 * e + i);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { kf[i] = tof(kh[i]); vv[i] = tof(vh[i]); }
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot = fmaf(qk[i], kf[i], dot);
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      dot += __shfl_xor(dot, 4);
+      update(dot, 1.f, vv);
+    }
+  }
+  // ---- combine the eight key groups of the wave, then the waves
+#pragma unroll
   for (int msk = L; msk < 64; msk <<= 1) {
     const float mo = __shfl_xor(mrun, msk);
     const float lo_ = __shfl_xor(lrun, msk);
@@ -1681,67 +1704,31 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(Dims m, Dev d, const T* q
     const float a2 = mo == -kInf ? 0.f : exp2_fast(mo - mn);
     lrun = lrun * a1 + lo_ * a2;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const float oo = __shfl_xor(o[i], msk);
       o[i] = o[i] * a1 + oo * a2;
     }
     mrun = mn;
   }
   if (lane < L) {
-    if (lane == 0) { red[w][0] = mrun; red[w][1] = lrun; }
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i < nvd) red[w][4 + vdim0 + i] = o[i];
+    for (int i = 0; i < 8; ++i) red_o[w][8 * e + i] = o[i];
+    if (lane == 0) { red_m[w] = mrun; red_l[w] = lrun; }
   }
   __syncthreads();
   if (tid < 64) {
     float M = -kInf;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, red[ww][0]);
-    float Lsum = 0.f, Ov = 0.f;
+    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, red_m[ww]);
+    float Ls = 0.f, Ov = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float a = red[ww][0] == -kInf ? 0.f : exp2_fast(red[ww][0] - M);
-      Lsum += red[ww][1] * a;
-      Ov += red[ww][4 + tid] * a;
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      const float a = red_m[ww] == -kInf ? 0.f : exp2_fast(red_m[ww] - M);
+      Ls += red_l[ww] * a;
+      Ov += red_o[ww][tid] * a;
     }
-    float* pp = d.part + ((size_t)s * m.n_seg_max + sg) * kPartStride;
-    pp[4 + tid] = Ov;
-    if (tid == 0) { pp[0] = M; pp[1] = Lsum; }
+    out[(size_t)s * 64 + tid] = fromf<T>(Ls > 0.f ? Ov / Ls : 0.f);
   }
-}
-
-template <typename T>
-__global__ void dec_combine_kernel(Dims m, Dev d, int nseg, T* out) {
-  const int s = blockIdx.x, tid = threadIdx.x;
-  const float* pp = d.part + (size_t)s * m.n_seg_max * kPartStride;
-  float M = -kInf;
-  for (int g = 0; g < nseg; ++g) M = fmaxf(M, pp[g * kPartStride]);
-  float L = 0.f, O = 0.f;
-  for (int g = 0; g < nseg; ++g) {
-    const float mg = pp[g * kPartStride];
-    const float a = mg == -kInf ? 0.f : exp2_fast(mg - M);
-    L += pp[g * kPartStride + 1] * a;
-    O += pp[g * kPartStride + 4 + tid] * a;
-  }
-  out[(size_t)s * 64 + tid] = fromf<T>(L > 0.f ? O / L : 0.f);
-}
-
-// Ring write of one decode token (rotated key, value, gate logit) at slot t % R.
-template <typename T>
-__global__ void dec_ring_kernel(Dims m, Dev d, const T* k, const T* v, const float* l, int64_t t) {
-  const int s = blockIdx.x, dd = threadIdx.x;
-  const T* kr = k + (size_t)s * 64;
-  float x = tof(kr[dd]);
-  if (dd < 32) {
-    const int jf = dd & 15;
-    const float cs = d.rope_cos[t * 16 + jf], sn = d.rope_sin[t * 16 + jf];
-    x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
-  }
-  const size_t slot = (size_t)(t % m.R);
-  reinterpret_cast<T*>(d.ring_k)[((size_t)s * m.R + slot) * 64 + dd] = fromf<T>(x);
-  reinterpret_cast<T*>(d.ring_v)[((size_t)s * m.R + slot) * 64 + dd] = v[(size_t)s * 64 + dd];
-  if (dd == 0) d.ring_l[(size_t)s * m.R + slot] = l[s];
 }
 
 template <typename T>
@@ -1826,31 +1813,18 @@ hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_decode_attn(const Dims& m, const Dev& d, const void* q, int64_t t, int rows, void* out,
-                              hipStream_t st) {
+hipError_t launch_decode(const Dims& m, const Dev& d, const void* q, const void* k, const void* v, const float* l,
+                         int64_t t, int rows, void* out, hipStream_t st) {
   const int64_t c = t / m.C;
   const int64_t lo = c * m.C - m.W > 0 ? c * m.C - m.W : 0;
-  const int nss = (rows + kDecSeg - 1) / kDecSeg;
-  const int nws = (int)((t - lo + 1 + kDecSeg - 1) / kDecSeg);
-  const int nseg = nss + nws;
-  if (nseg > m.n_seg_max) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)nseg, (unsigned)m.BH);
-  if (m.bf16) {
-    dec_attn_kernel<bf16><<<grid, 256, 0, st>>>(m, d, reinterpret_cast<const bf16*>(q), t, rows, nss, lo);
-    dec_combine_kernel<bf16><<<m.BH, 64, 0, st>>>(m, d, nseg, reinterpret_cast<bf16*>(out));
-  } else {
-    dec_attn_kernel<float><<<grid, 256, 0, st>>>(m, d, reinterpret_cast<const float*>(q), t, rows, nss, lo);
-    dec_combine_kernel<float><<<m.BH, 64, 0, st>>>(m, d, nseg, reinterpret_cast<float*>(out));
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_ring(const Dims& m, const Dev& d, const void* k, const void* v, const float* l, int64_t t,
-                              hipStream_t st) {
   if (m.bf16)
-    dec_ring_kernel<bf16><<<m.BH, 64, 0, st>>>(m, d, reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v), l, t);
+    dec_kernel<bf16><<<m.BH, 64 * kDecWaves, 0, st>>>(m, d, reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
+                                                     reinterpret_cast<const bf16*>(v), l, reinterpret_cast<bf16*>(out), t,
+                                                     rows, lo);
   else
-    dec_ring_kernel<float><<<m.BH, 64, 0, st>>>(m, d, reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v), l, t);
+    dec_kernel<float><<<m.BH, 64 * kDecWaves, 0, st>>>(m, d, reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
+                                                      reinterpret_cast<const float*>(v), l, reinterpret_cast<float*>(out), t,
+                                                      rows, lo);
   return hipGetLastError();
 }
 

@@ -192,7 +192,7 @@ typedef struct kvm_profile_times {
   double attn_ms;          int64_t attn_launches;          /* prefill attention over [state || window] */
   double ring_ms;          int64_t ring_launches;          /* ring refresh after prefill */
   double dec_absorb_ms;    int64_t dec_absorb_launches;    /* decode-time absorption */
-  double dec_attn_ms;      int64_t dec_attn_launches;      /* decode ring write + attention + combine */
+  double dec_attn_ms;      int64_t dec_attn_launches;      /* decode step kernel: ring write + attention */
 } kvm_profile_times;
 
 /* Enable (1) or disable (0) recording of a HIP event pair around every kernel
