@@ -143,7 +143,7 @@ struct Plan {
   kvm::Dims m{};
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
-  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, rmax, idx, tslot, tkind, ring_k, ring_v,
+  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, idx, tslot, tkind, ring_k, ring_v,
       ring_l, rope_cos, rope_sin, sch, nver, total;
 };
 
@@ -201,7 +201,6 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   p.pkey = take(BH * (size_t)m.V_cap * 32 * es);
   p.pval = take(BH * (size_t)m.V_cap * 64 * es);
   p.prho = take(BH * (size_t)m.V_cap * 4);
-  p.rmax = take(BH * (size_t)J * 4);
   p.idx = take(BH * (size_t)idx_total * 4);
   p.tslot = take(m.trace ? BH * (size_t)c->max_tokens * 4 : 0);
   p.tkind = take(m.trace ? BH * (size_t)c->max_tokens : 0);
@@ -347,7 +346,6 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     d.pkey = b + p.pkey;
     d.pval = b + p.pval;
     d.prho = reinterpret_cast<float*>(b + p.prho);
-    d.rmax = reinterpret_cast<float*>(b + p.rmax);
     d.idx = reinterpret_cast<int*>(b + p.idx);
     d.tslot = reinterpret_cast<int*>(b + p.tslot);
     d.tkind = reinterpret_cast<uint8_t*>(b + p.tkind);

@@ -43,11 +43,10 @@ struct Dev {
   float* rho;        // [BH][S_cap] read radius
   void* unit;        // [BH][S_cap] x 128 B unit key direction: bf16 path [hi 32 | lo 32] bf16, fp32 path 32 f32
   void* kread;       // [BH][S_cap][32] RT current read-form key (live dims)
-  void* vread;       // [BH][S_cap][64] RT current unit value direction u (read-form value = rho * u)
+  void* vread;       // [BH][S_cap][64] T  current read-form value rho * u
   void* pkey;        // [BH][V_cap][32] RT read-form row versions: key
-  void* pval;        // [BH][V_cap][64] RT read-form row versions: unit value direction
+  void* pval;        // [BH][V_cap][64] T  read-form row versions: value rho * u
   float* prho;       // [BH][V_cap]       read-form row versions: radius
-  float* rmax;       // [BH][J_cap]       largest radius among the rows after chunk j
   int* idx;          // [BH][idx_total] per absorbed chunk j: version id of each row after chunk j
   int* tslot;        // [BH][max_tokens] trace: row created / merged into
   uint8_t* tkind;    // [BH][max_tokens] trace: 0 sink 1 append 2 merge 255 none

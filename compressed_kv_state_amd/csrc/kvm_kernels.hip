@@ -45,7 +45,8 @@ template <typename T> struct Is;
 template <> struct Is<float> { static constexpr bool bf = false; };
 template <> struct Is<bf16> { static constexpr bool bf = true; };
 
-// Read-form storage type: fp16 on the bf16 path (bounded values), float on the fp32 path.
+// Read-form key storage type: fp16 on the bf16 path (LayerNorm output, bounded), float on
+// the fp32 path.  Read-form values (rho * u, unbounded) are stored in the input type.
 template <typename T> struct Rd;
 template <> struct Rd<float> { using type = float; };
 template <> struct Rd<bf16> { using type = f16; };
@@ -174,7 +175,6 @@ struct ScanSmem {
   int wtot[kScanWaves];
   int nold;
   int nseg;
-  uint32_t rmax_bits;  // largest radius of the rows created in this chunk (non-negative float bits)
 };
 
 // Queue direct global->LDS loads of chunk P0's live keys, values and gate
@@ -392,12 +392,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
   float* rho = d.rho + (size_t)s * m.S_cap;
   char* unit = reinterpret_cast<char*>(d.unit) + (size_t)s * m.S_cap * 128;
   RT* kread = reinterpret_cast<RT*>(d.kread) + (size_t)s * m.S_cap * 32;
-  RT* vread = reinterpret_cast<RT*>(d.vread) + (size_t)s * m.S_cap * 64;
+  T* vread = reinterpret_cast<T*>(d.vread) + (size_t)s * m.S_cap * 64;
   RT* pkey = reinterpret_cast<RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
-  RT* pval = reinterpret_cast<RT*>(d.pval) + (size_t)s * m.V_cap * 64;
+  T* pval = reinterpret_cast<T*>(d.pval) + (size_t)s * m.V_cap * 64;
   float* prho = d.prho + (size_t)s * m.V_cap;
-  float* rmaxs = d.rmax + (size_t)s * m.J_cap;
-  float rmax_run = j_begin > 0 ? rmaxs[j_begin - 1] : 0.f;
   int* idx = d.idx + (size_t)s * m.idx_total;
   const T* ring_k = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
   const T* ring_v = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
@@ -530,7 +528,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
         sm.key[t] = ~0ull;  // non-merged tokens sort last
       }
     }
-    if (tid == 0) { sm.nold = 0; sm.rmax_bits = 0u; }
+    if (tid == 0) sm.nold = 0;
     for (int c2 = tid; c2 < nc; c2 += kScanThreads) sm.created_seg[c2] = -1;
     lds_barrier();
 
@@ -657,7 +655,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
       if (sub == 0) {
         count[row] = n;
         rho[row] = rh;
-        if (creator >= 0) atomicMax(&sm.rmax_bits, __float_as_uint(rh));
       }
       // row sums of squares and moments over the four lanes
       float k2 = 0.f, ksum = 0.f, v2 = 0.f;
@@ -694,8 +691,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
         }
       }
       // just-in-time read form ([KVM summary, Core mechanisms 2]): LayerNorm of
-      // K/n over the live dims (no affine); the value's direction u = V/|V|,
-      // read as rho * u (the radius fixed at creation).
+      // K/n over the live dims (no affine); the value rho * V/|V| (direction of
+      // the sum at the radius fixed at creation).
       const float invn = 1.0f / (float)n;
       const float mean = ksum * invn * (1.0f / 32.0f);
       float var = 0.f;
@@ -705,14 +702,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
       var += __shfl_xor(var, 2);
       var *= (1.0f / 32.0f);
       const float rs = 1.0f / sqrtf(var + m.ln_eps);
-      const float vsc = v2 > 0.f ? 1.0f / sqrtf(v2) : 0.f;
+      const float vsc = v2 > 0.f ? rh / sqrtf(v2) : 0.f;
       const int ver = nver + u;
       alignas(16) RT kh[8];
-      alignas(16) RT vh[16];
+      alignas(16) T vh[16];
 #pragma unroll
       for (int i = 0; i < 8; ++i) kh[i] = fromf<RT>((K[i] * invn - mean) * rs);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vh[i] = fromf<RT>(V[i] * vsc);
+      for (int i = 0; i < 16; ++i) vh[i] = fromf<T>(V[i] * vsc);
 #pragma unroll
       for (int i = 0; i < 8; i += REL) {
         copy16(pkey + (size_t)ver * 32 + 8 * sub + i, &kh[i]);
@@ -739,8 +736,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
     nver += nu;
     prev_off = (int)ioff;
     __syncthreads();  // the step's global writes are visible to every thread of the next step
-    rmax_run = fmaxf(rmax_run, __uint_as_float(sm.rmax_bits));
-    if (tid == 0) rmaxs[j] = rmax_run;
   }
   if (tid == 0) d.nver[s] = nver;
 }
@@ -771,14 +766,13 @@ __device__ __forceinline__ void rot(float& x, float& y, float c, float s) {
 }
 
 // State tile: rows r0..r0+63 of the snapshot (version ids in idxl).  Stages the
-// read-form key (live dims) into sK, the unit value direction transposed into
-// sVt, and rho_i / rho_max into sRho.  Rows past S are zero.
+// read-form key (live dims) into sK and the read-form value rho * u transposed
+// into sVt.  Rows past S are zero.
 template <typename T, int NT>
-__device__ void stage_state(void* sKv, void* sVtv, float* sRho, const int* idxl, const typename Rd<T>::type* pk,
-                            const typename Rd<T>::type* pv, const float* prho, float inv_rmax, int r0, int S) {
+__device__ void stage_state(void* sKv, T* sVt, const int* idxl, const typename Rd<T>::type* pk, const T* pv, int r0,
+                            int S) {
   using RT = typename Rd<T>::type;
   RT* sK = reinterpret_cast<RT*>(sKv);
-  RT* sVt = reinterpret_cast<RT*>(sVtv);
   constexpr int KSTR = AttnCfg<T>::KSTR, VSTR = AttnCfg<T>::VSTR;
   constexpr int EL = 16 / sizeof(RT);
   constexpr int KPC = 32 / EL;  // pieces per live key row
@@ -793,8 +787,8 @@ __device__ void stage_state(void* sKv, void* sVtv, float* sRho, const int* idxl,
   for (int task = threadIdx.x; task < 32 * VG; task += NT) {
     const int rp = task / VG, dg = task % VG;
     const int i0 = 2 * rp;
-    alignas(16) RT a[EL];
-    alignas(16) RT b[EL];
+    alignas(16) T a[EL];
+    alignas(16) T b[EL];
     const int r = r0 + i0;
     if (r < S) copy16(a, pv + (size_t)idxl[r] * 64 + dg * EL);
     else zero16(a);
@@ -802,14 +796,10 @@ __device__ void stage_state(void* sKv, void* sVtv, float* sRho, const int* idxl,
     else zero16(b);
 #pragma unroll
     for (int e = 0; e < EL; ++e) {
-      RT* dst = sVt + (dg * EL + e) * VSTR + i0;
+      T* dst = sVt + (dg * EL + e) * VSTR + i0;
       dst[0] = a[e];
       dst[1] = b[e];
     }
-  }
-  for (int i = threadIdx.x; i < 64; i += NT) {
-    const int r = r0 + i;
-    sRho[i] = r < S ? prho[idxl[r]] * inv_rmax : 0.f;
   }
 }
 
@@ -899,7 +889,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, i
   static_assert(sizeof(RT) == sizeof(T), "read-form and input types share the LDS tile layout");
   __shared__ __attribute__((aligned(16))) T sK[64 * KSTR];
   __shared__ __attribute__((aligned(16))) T sVt[64 * VSTR];
-  __shared__ __attribute__((aligned(16))) float sRho[64];
 
   // Block -> (sequence, chunk).  Consecutive block ids land on consecutive XCDs;
   // keep every chunk of a sequence on one XCD (its state rows stay in that L2)
@@ -1004,22 +993,17 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, i
   const int64_t jj = c - m.W / C - 1;
   int S = 0;
   int64_t ioff = 0;
-  float rmax = 1.f;
   if (jj >= 0) {
     const int4 sc4 = d.sched[jj];
     S = sc4.z + sc4.x + sc4.y;
     ioff = sc4.w;
-    const float rm = d.rmax[(size_t)s * m.J_cap + jj];
-    rmax = rm > 0.f ? rm : 1.f;
   }
   const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
-  const RT* pv = reinterpret_cast<const RT*>(d.pval) + (size_t)s * m.V_cap * 64;
-  const float* prho = d.prho + (size_t)s * m.V_cap;
-  const float inv_rmax = 1.0f / rmax;
+  const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
   for (int r0 = 0; r0 < S; r0 += 64) {
     __syncthreads();
-    stage_state<T, NT>(sK, sVt, sRho, idxl, pk, pv, prho, inv_rmax, r0, S);
+    stage_state<T, NT>(sK, sVt, idxl, pk, pv, r0, S);
     __syncthreads();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -1037,41 +1021,27 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, i
       }
       float p[16];
       softmax_step(acc, sl2_state, [&](int key) { return key < lim; }, p);
-      // fold rho_i / rho_max into the weights (values are stored as unit directions)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const float4 r4 = *reinterpret_cast<const float4*>(&sRho[kb + 8 * g4 + 4 * h]);
-        p[4 * g4 + 0] *= r4.x;
-        p[4 * g4 + 1] *= r4.y;
-        p[4 * g4 + 2] *= r4.z;
-        p[4 * g4 + 3] *= r4.w;
-      }
-      const RT* vt = reinterpret_cast<const RT*>(sVt);
       if constexpr (BF) {
-        f16x8 pf0, pf1;
+        bf16x8 pf0, pf1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pf0[e] = (f16)p[e]; pf1[e] = (f16)p[8 + e]; }
+        for (int e = 0; e < 8; ++e) { pf0[e] = (bf16)p[e]; pf1[e] = (bf16)p[8 + e]; }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const RT* vr = vt + (32 * dt + jl) * VSTR + kb;
+          const T* vr = sVt + (32 * dt + jl) * VSTR + kb;
           f32x16& O = dt ? O1 : O0;
-          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 4 * h), pf0, O);
-          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 16 + 4 * h), pf1, O);
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 4 * h), pf0, O);
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 16 + 4 * h), pf1, O);
         }
       } else {
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const RT* vr = vt + (32 * dt + jl) * VSTR + kb;
+          const T* vr = sVt + (32 * dt + jl) * VSTR + kb;
           f32x16& O = dt ? O1 : O0;
 #pragma unroll
           for (int r = 0; r < 16; ++r) O = mfma_f32(vr[8 * (r >> 2) + 4 * h + (r & 3)], p[r], O);
         }
       }
     }
-  }
-  if (S > 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { O0[r] *= rmax; O1[r] *= rmax; }
   }
 
   // ---- window part: keys [max(0, cC - W), min(cC + C, end)), causal
@@ -1199,22 +1169,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
   const int64_t jj = c - m.W / C - 1;
   int S = 0;
   int64_t ioff = 0;
-  float rmax = 1.f;
   if (jj >= 0) {
     const int4 sc4 = d.sched[jj];
     S = sc4.z + sc4.x + sc4.y;
     ioff = sc4.w;
-    const float rm = d.rmax[(size_t)s * m.J_cap + jj];
-    rmax = rm > 0.f ? rm : 1.f;
   }
   const int* idxg = d.idx + (size_t)s * m.idx_total + ioff;
   const bool idx_lds = S <= kIdxCap;
   if (idx_lds)
     for (int i = tid; i < S; i += NT) sIdx[i] = idxg[i];
   const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
-  const f16* pv = reinterpret_cast<const f16*>(d.pval) + (size_t)s * m.V_cap * 64;
-  const float* prho = d.prho + (size_t)s * m.V_cap;
-  const float inv_rmax = 1.0f / rmax;
+  const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
 
   // ---- query fragments (B operand of S^T = K . Q^T), pre-scaled by scale*log2(e)
   const bf16* qrow = reinterpret_cast<const bf16*>(src.q) + ((size_t)s * src.n_call + (size_t)(qp - src.p0)) * 64;
@@ -1275,7 +1240,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
   const int ki = tid >> 2, kp = tid & 3;     // K task: key/row ki, part kp
   const int vrp = tid >> 3, vdg = tid & 7;   // V task: rows 2vrp, 2vrp+1; dims 8vdg..8vdg+7
   uint4 kr0, kr1, vr0, vr1;
-  float rho_a = 0.f, rho_b = 0.f;
+  bool va_ok = false, vb_ok = false;
   int64_t k_pos = 0;   // window key position to rotate at commit (-1: no rotation)
   bool k_zero = false;
 
@@ -1289,20 +1254,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
       k_pos = -1;
       if (!k_zero) kr0 = *reinterpret_cast<const uint4*>(pk + (size_t)row_version(r) * 32 + 8 * kp);
       const int ra = r0 + 2 * vrp;
-      if (ra < S) {
-        const int va = row_version(ra);
-        vr0 = *reinterpret_cast<const uint4*>(pv + (size_t)va * 64 + 8 * vdg);
-        rho_a = prho[va];
-      } else {
-        rho_a = 0.f;
-      }
-      if (ra + 1 < S) {
-        const int vb = row_version(ra + 1);
-        vr1 = *reinterpret_cast<const uint4*>(pv + (size_t)vb * 64 + 8 * vdg);
-        rho_b = prho[vb];
-      } else {
-        rho_b = 0.f;
-      }
+      va_ok = ra < S;
+      vb_ok = ra + 1 < S;
+      if (va_ok) vr0 = *reinterpret_cast<const uint4*>(pv + (size_t)row_version(ra) * 64 + 8 * vdg);
+      if (vb_ok) vr1 = *reinterpret_cast<const uint4*>(pv + (size_t)row_version(ra + 1) * 64 + 8 * vdg);
     } else {
       const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
       const int64_t pos = k0 + ki;
@@ -1322,8 +1277,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
         }
       }
       const int64_t pa = k0 + 2 * vrp;
-      rho_a = pa < hi ? 1.f : 0.f;
-      rho_b = pa + 1 < hi ? 1.f : 0.f;
+      va_ok = pa < hi;
+      vb_ok = pa + 1 < hi;
       if (pa < hi) {
         const bf16* row = pa >= src.p0 ? reinterpret_cast<const bf16*>(src.v) + ((size_t)s * src.n_call + (size_t)(pa - src.p0)) * 64
                                        : ring_v + (size_t)(pa % m.R) * 64;
@@ -1342,17 +1297,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
     uint16_t* Vt = sVt[buf];
     if (T < n_st) {
       *reinterpret_cast<uint4*>(K + 8 * kp) = k_zero ? make_uint4(0, 0, 0, 0) : kr0;
-      // values: unit direction * rho / rho_max, fp16, transposed (dim-major)
-      const float fa = rho_a * inv_rmax, fb = rho_b * inv_rmax;
-      const f16* a = reinterpret_cast<const f16*>(&vr0);
-      const f16* b = reinterpret_cast<const f16*>(&vr1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const f16 x = (f16)(fa > 0.f ? (float)a[e] * fa : 0.f);
-        const f16 y = (f16)(fb > 0.f ? (float)b[e] * fb : 0.f);
-        const uint32_t pr = (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-        *reinterpret_cast<uint32_t*>(Vt + (8 * vdg + e) * VSTR + 2 * vrp) = pr;
-      }
     } else {
       uint4 x = kr0, y = kr1;
       if (k_zero) {
@@ -1378,13 +1322,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
         *reinterpret_cast<uint4*>(K + 32 + 16 * (kp - 2)) = x;
         *reinterpret_cast<uint4*>(K + 40 + 16 * (kp - 2)) = y;
       }
-      const uint16_t* a = reinterpret_cast<const uint16_t*>(&vr0);
-      const uint16_t* b = reinterpret_cast<const uint16_t*>(&vr1);
+    }
+    // values (state rho * u or window v, bf16), transposed (dim-major)
+    const uint16_t* a = reinterpret_cast<const uint16_t*>(&vr0);
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(&vr1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t pr = (rho_a > 0.f ? (uint32_t)a[e] : 0u) | ((rho_b > 0.f ? (uint32_t)b[e] : 0u) << 16);
-        *reinterpret_cast<uint32_t*>(Vt + (8 * vdg + e) * VSTR + 2 * vrp) = pr;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t pr = (va_ok ? (uint32_t)a[e] : 0u) | ((vb_ok ? (uint32_t)b[e] : 0u) << 16);
+      *reinterpret_cast<uint32_t*>(Vt + (8 * vdg + e) * VSTR + 2 * vrp) = pr;
     }
   };
 
@@ -1442,21 +1387,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
         }
         float p[16];
         softmax_p(acc, p);
-        f16x8 pf0, pf1;
+        bf16x8 pf0, pf1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pf0[e] = (f16)p[e]; pf1[e] = (f16)p[8 + e]; }
+        for (int e = 0; e < 8; ++e) { pf0[e] = (bf16)p[e]; pf1[e] = (bf16)p[8 + e]; }
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
-          const f16* vr = reinterpret_cast<const f16*>(Vt) + (32 * dt + jl) * VSTR + kb;
+          const bf16* vr = reinterpret_cast<const bf16*>(Vt) + (32 * dt + jl) * VSTR + kb;
           f32x16& O = dt ? O1 : O0;
-          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 4 * h), pf0, O);
-          O = mfma_f16(vfrag<f16x8, f16x4>(vr, 16 + 4 * h), pf1, O);
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 4 * h), pf0, O);
+          O = mfma_bf16(vfrag<bf16x8, bf16x4>(vr, 16 + 4 * h), pf1, O);
         }
-      }
-      if (T == n_st - 1) {
-        // state values were staged at rho_i / rho_max: restore the scale once
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { O0[r] *= rmax; O1[r] *= rmax; }
       }
     } else {
       const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
@@ -1611,39 +1551,36 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
   float o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  auto update = [&](float lg, float pscale, const float (&vv)[8]) {
+  auto update = [&](float lg, const float (&vv)[8]) {
     const float mnew = fmaxf(mrun, lg);
     const float alpha = exp2_fast(mrun - mnew);
     const float p = exp2_fast(lg - mnew);
     lrun = lrun * alpha + p;
     mrun = mnew;
-    const float pv = p * pscale;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = fmaf(pv, vv[i], o[i] * alpha);
+    for (int i = 0; i < 8; ++i) o[i] = fmaf(p, vv[i], o[i] * alpha);
   };
 
-  // ---- state rows: read-form key dims [32 + 4e, 32 + 4e + 4), unit value direction, radius
+  // ---- state rows: read-form key dims [32 + 4e, 32 + 4e + 4) and value rho * u
   {
     float qk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) qk[i] = sq[32 + 4 * e + i];
     const RT* kr = reinterpret_cast<const RT*>(d.kread) + (size_t)s * m.S_cap * 32;
-    const RT* vr = reinterpret_cast<const RT*>(d.vread) + (size_t)s * m.S_cap * 64;
-    const float* rr = d.rho + (size_t)s * m.S_cap;
+    const T* vr = reinterpret_cast<const T*>(d.vread) + (size_t)s * m.S_cap * 64;
     const int per = (S + kDecWaves - 1) / kDecWaves;
     const int rb = w * per, re = min(S, rb + per);
 #pragma unroll 2
     for (int row = rb + grp; row < re; row += 64 / L) {
       alignas(16) RT kk[4];
-      alignas(16) RT vh[8];
+      alignas(16) T vh[8];
       if constexpr (sizeof(RT) == 2) {
         *reinterpret_cast<uint2*>(kk) = *reinterpret_cast<const uint2*>(kr + (size_t)row * 32 + 4 * e);
       } else {
         copy16(kk, kr + (size_t)row * 32 + 4 * e);
       }
 #pragma unroll
-      for (int i = 0; i < 8; i += 16 / (int)sizeof(RT)) copy16(&vh[i], vr + (size_t)row * 64 + 8 * e + i);
-      const float rho = rr[row];
+      for (int i = 0; i < 8; i += 16 / (int)sizeof(T)) copy16(&vh[i], vr + (size_t)row * 64 + 8 * e + i);
       float dot = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
@@ -1653,7 +1590,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
       float vv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) vv[i] = tof(vh[i]);
-      update(dot, rho, vv);
+      update(dot, vv);
     }
   }
   // ---- window keys [lo, t] (ring slots; position t from LDS)
@@ -1691,7 +1628,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
       dot += __shfl_xor(dot, 1);
       dot += __shfl_xor(dot, 2);
       dot += __shfl_xor(dot, 4);
-      update(dot, 1.f, vv);
+      update(dot, vv);
     }
   }
   // ---- combine the eight key groups of the wave, then the waves
@@ -1733,12 +1670,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
 
 template <typename T>
 __global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, typename Rd<T>::type* key_out,
-                                       typename Rd<T>::type* val_out, float* rho_out) {
+                                       T* val_out, float* rho_out) {
   using RT = typename Rd<T>::type;
   const int s = blockIdx.x;
   const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
-  const RT* pv = reinterpret_cast<const RT*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
   const float* pr = d.prho + (size_t)s * m.V_cap;
   for (int64_t i = threadIdx.x; i < (int64_t)rows * 97; i += blockDim.x) {
     const int r = (int)(i / 97), dd = (int)(i % 97);
@@ -1833,7 +1770,7 @@ hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t
   if (rows <= 0) return hipSuccess;
   if (m.bf16)
     snapshot_gather_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, reinterpret_cast<f16*>(key_out),
-                                                       reinterpret_cast<f16*>(val_out), rho_out);
+                                                       reinterpret_cast<bf16*>(val_out), rho_out);
   else
     snapshot_gather_kernel<float><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, reinterpret_cast<float*>(key_out),
                                                          reinterpret_cast<float*>(val_out), rho_out);

@@ -142,7 +142,8 @@ class KvmConfig:
 
     @property
     def read_dtype(self) -> torch.dtype:
-        """Storage type of the state's read form (fp16 on the bf16 path)."""
+        """Storage type of the state's read-form keys (fp16 on the bf16 path); read-form
+        values use the input dtype."""
         return _READ_DTYPE[self.dtype]
 
     @staticmethod
@@ -293,7 +294,7 @@ class KvmState:
             "count": torch.empty(S, Sc, dtype=torch.int32, device=dev),
             "rho": torch.empty(S, Sc, dtype=torch.float32, device=dev),
             "key_read": torch.empty(S, Sc, 32, dtype=dt, device=dev),
-            "val_read": torch.empty(S, Sc, 64, dtype=dt, device=dev),
+            "val_read": torch.empty(S, Sc, 64, dtype=self.cfg.torch_dtype, device=dev),
         }
         n_rows = torch.zeros(S, dtype=torch.int32)
         view = _View(n_rows.data_ptr(), *(res[k].data_ptr() for k in
@@ -308,13 +309,12 @@ class KvmState:
         return res
 
     def snapshot(self, j: int):
-        """Read form of the state after absorbed chunk j: key [B*H, rows_j, 32], unit value
-        direction [B*H, rows_j, 64] (both in read_dtype) and radius [B*H, rows_j] float32;
-        the read-form value is radius * direction."""
+        """Read form of the state after absorbed chunk j: key [B*H, rows_j, 32] (read_dtype),
+        value rho * u [B*H, rows_j, 64] (input dtype) and radius [B*H, rows_j] float32."""
         rows = int(schedule(self.cfg, j + 1)[2][j])
         dt = self.cfg.read_dtype
         kr = torch.empty(self.cfg.seqs, rows, 32, dtype=dt, device=self.device)
-        ur = torch.empty(self.cfg.seqs, rows, 64, dtype=dt, device=self.device)
+        ur = torch.empty(self.cfg.seqs, rows, 64, dtype=self.cfg.torch_dtype, device=self.device)
         rr = torch.empty(self.cfg.seqs, rows, dtype=torch.float32, device=self.device)
         _check(library().kvm_snapshot_read(self._h, j, kr.data_ptr(), ur.data_ptr(), rr.data_ptr(),
                                            _stream(self.device)))

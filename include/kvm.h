@@ -87,18 +87,19 @@ typedef struct kvm_state kvm_state;
  * n_rows is host memory (filled immediately); every other pointer may be host
  * or device memory (queued copies, unified addressing).
  * S_cap = kvm_state_info(...).max_rows.  Rows beyond n_rows[s] are undefined.
- * rtype, the read-form storage type, is float32 on the KVM_F32 path and IEEE
- * fp16 on the KVM_BF16 path: every read-form value is bounded (LayerNorm output
- * |k| <= sqrt(31), unit direction |u| <= 1), so fp16 keeps more precision than
- * bf16 with no overflow. */
+ * ktype, the read-form key storage type, is float32 on the KVM_F32 path and
+ * IEEE fp16 on the KVM_BF16 path: a LayerNorm output over 32 dims has
+ * |k| <= sqrt(31), so fp16 keeps more precision than bf16 with no overflow.
+ * Read-form values rho * u are stored in cfg.dtype (bf16 or f32): their range
+ * is that of the input values. */
 typedef struct kvm_state_view {
   int32_t* n_rows;        /* [B*H] host                rows of each sequence's state */
   float* key_sum;         /* [B*H, S_cap, 32] f32      raw gated key sums (live dims) */
   float* val_sum;         /* [B*H, S_cap, 64] f32      raw gated value sums */
   int32_t* count;         /* [B*H, S_cap] i32          tokens absorbed per row */
   float* rho;             /* [B*H, S_cap] f32          read radius fixed at row creation */
-  void* key_read;         /* [B*H, S_cap, 32] rtype    read-form key, live dims (rotary dims are 0) */
-  void* val_read;         /* [B*H, S_cap, 64] rtype    unit value direction u; read-form value = rho * u */
+  void* key_read;         /* [B*H, S_cap, 32] ktype    read-form key, live dims (rotary dims are 0) */
+  void* val_read;         /* [B*H, S_cap, 64] dtype    read-form value rho * u, u = V / |V| */
   int32_t* trace_slot;    /* [B*H, max_tokens] i32     row created/merged into, -1 if not absorbed */
   uint8_t* trace_kind;    /* [B*H, max_tokens] u8      0 sink, 1 append, 2 merge, 255 not absorbed */
 } kvm_state_view;
@@ -172,7 +173,7 @@ kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* 
 /* Queue a gather of the read form of the state right after absorbed chunk j,
  * i.e. the state that query chunk j + W/C + 1 attends to ([KVM summary, Core
  * mechanisms 2]: LayerNorm-ed keys, values at the read radius): key
- * [B*H, rows_j, 32] rtype, unit value direction [B*H, rows_j, 64] rtype, radius
+ * [B*H, rows_j, 32] ktype, value rho * u [B*H, rows_j, 64] in cfg.dtype, radius
  * [B*H, rows_j] f32 (device memory; any pointer may be NULL).
  * j must be < absorbed_chunks.  Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
 kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, void* val_read, float* rho_read,
