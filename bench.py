@@ -41,7 +41,7 @@ METRIC = "KVM-layer prefill tokens/s (B*H*N) + % bf16 MFMA peak; decode HBM GB/s
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "compressed_kv_state_amd", "csrc", "kvm_kernels.hip")
-ATTN_KERNEL = "attn_bf16_kernel"   # the bf16 attention kernel for chunks of 128 / 256
+ATTN_KERNEL = "attn_dma_kernel"   # the bf16 attention kernel for chunks of 128 / 256
 COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_bf16_kernel_350m_sqrt8_counters.md")
 
 
@@ -358,7 +358,7 @@ def main():
                      "kernel": ATTN_KERNEL, "flops_per_launch": flops, "ms_per_launch": attn_ms,
                      "launches_per_step": launches / args.steps},
         "phases_ms_per_step": {"scan": prof["scan_ms"] / args.steps, "attn": prof["attn_ms"] / args.steps,
-                               "ring": prof["ring_ms"] / args.steps,
+                               "ring": prof["ring_ms"] / args.steps, "rope_prep": prof["prep_ms"] / args.steps,
                                "note": "scan and attention overlap on two streams; phases sum past the step"},
     }
     if not args.no_decode:

@@ -17,7 +17,7 @@
 #include "kvm.h"
 #include "kvm_internal.h"
 
-enum Phase { kScan = 0, kAttn, kRing, kDecAbsorb, kDecAttn, kPhases };
+enum Phase { kScan = 0, kAttn, kRing, kDecAbsorb, kDecAttn, kPrep, kPhases };
 
 struct kvm_state {
   kvm_config cfg;
@@ -143,7 +143,7 @@ struct Plan {
   kvm::Dims m{};
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
-  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, idx, tslot, tkind, ring_k, ring_v,
+  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, idx, krot, tslot, tkind, ring_k, ring_v,
       ring_l, rope_cos, rope_sin, sch, nver, total;
 };
 
@@ -207,6 +207,7 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   p.ring_k = take(BH * (size_t)m.R * 64 * es);
   p.ring_v = take(BH * (size_t)m.R * 64 * es);
   p.ring_l = take(BH * (size_t)m.R * 4);
+  p.krot = take(m.bf16 && m.C >= 128 ? BH * (size_t)c->max_tokens * 32 * 2 : 0);
   p.rope_cos = take((size_t)c->max_tokens * 16 * 4);
   p.rope_sin = take((size_t)c->max_tokens * 16 * 4);
   p.sch = take((size_t)J * 16);
@@ -353,6 +354,7 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     d.ring_v = b + p.ring_v;
     d.ring_l = reinterpret_cast<float*>(b + p.ring_l);
     d.rope_cos = reinterpret_cast<float*>(b + p.rope_cos);
+    d.krot = p.m.bf16 && p.m.C >= 128 ? b + p.krot : nullptr;
     d.rope_sin = reinterpret_cast<float*>(b + p.rope_sin);
     d.sched = reinterpret_cast<int4*>(b + p.sch);
     d.nver = reinterpret_cast<int*>(b + p.nver);
@@ -406,8 +408,13 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
   kvm::Src src{q, k, v, gate_logits, p0, n_tokens};
   hipError_t err = hipSuccess;
   auto attn = [&](hipStream_t sx, int64_t cb, int64_t ce) {  // query chunks [cb, ce]
+    const int s_max = rows_after(st, ce - m.W / m.C - 1);
     return timed(st, kAttn, sx,
-                 [&] { return kvm::launch_attn(m, st->d, src, cb, (int)(ce - cb + 1), e, out, sx); });
+                 [&] { return kvm::launch_attn(m, st->d, src, cb, (int)(ce - cb + 1), e, out, s_max, sx); });
+  };
+  auto rope = [&](hipStream_t sx) {
+    if (!st->d.krot) return hipSuccess;
+    return timed(st, kPrep, sx, [&] { return kvm::launch_rope_keys(m, st->d, src, sx); });
   };
   if (a1 > st->absorbed) {
     // Query chunk c reads the state after chunks [0, c - W/C) are absorbed.
@@ -420,6 +427,7 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
     if (err == hipSuccess && !fork) err = hipErrorOutOfMemory;
     if (err == hipSuccess) err = hipEventRecord(fork, hs);
     if (err == hipSuccess) err = hipStreamWaitEvent(st->side, fork, 0);
+    if (err == hipSuccess) err = rope(st->side);
     int64_t done = c_first - 1;  // attention queued through this chunk
     auto release = [&](int64_t absorbed) {
       const int64_t hi = std::min(c_last, absorbed + wc);
@@ -448,7 +456,8 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
     if (err == hipSuccess && done != c_last) err = hipErrorInvalidValue;
     if (err != hipSuccess) return hip_fail(st, err, "scan/attention launch");
   } else {
-    err = attn(hs, c_first, c_last);
+    err = rope(hs);
+    if (err == hipSuccess) err = attn(hs, c_first, c_last);
     if (err != hipSuccess) return hip_fail(st, err, "attention launch");
   }
   const int64_t from = e - m.R > p0 ? e - m.R : p0;
@@ -600,6 +609,8 @@ kvm_status kvm_profile_read(kvm_state* st, kvm_profile_times* out) {
   out->dec_absorb_launches = n[kDecAbsorb];
   out->dec_attn_ms = ms[kDecAttn];
   out->dec_attn_launches = n[kDecAttn];
+  out->prep_ms = ms[kPrep];
+  out->prep_launches = n[kPrep];
   if (err != hipSuccess) return fail(KVM_E_HIP, std::string("profile events: ") + hipGetErrorString(err));
   return KVM_OK;
 }

@@ -53,6 +53,7 @@ struct Dev {
   void* ring_k;      // [BH][R][64] T  rotated keys of the last R positions (slot = pos % R)
   void* ring_v;      // [BH][R][64] T
   float* ring_l;     // [BH][R] gate logits
+  void* krot;        // [BH][max_tokens][32] bf16 rotated key dims [0, 32) (bf16, C >= 128; else null)
   float* rope_cos;   // [max_tokens][16]
   float* rope_sin;   // [max_tokens][16]
   int4* sched;       // [J_cap] (sinks_j, appends_j, rows_before_j, idx_off_j)
@@ -74,9 +75,12 @@ hipError_t launch_init(const Dims& m, const Dev& d, double rope_theta, hipStream
 // Absorb chunks [j_begin, j_end) for every sequence (sequential over j inside the kernel).
 hipError_t launch_scan(const Dims& m, const Dev& d, const Src& src, int j_begin, int j_end, hipStream_t st);
 // Attention for query chunks [c_begin, c_begin + n_q); queries at positions < end_pos; out rows
-// are [BH][n_call][64] indexed by position - src.p0.
+// are [BH][n_call][64] indexed by position - src.p0.  s_max: rows of the largest snapshot the
+// chunks read.  With d.krot set, the rotated keys of the call must be in krot (launch_rope_keys).
 hipError_t launch_attn(const Dims& m, const Dev& d, const Src& src, int64_t c_begin, int n_q, int64_t end_pos,
-                       void* out, hipStream_t st);
+                       void* out, int s_max, hipStream_t st);
+// Rotated key dims [0, 32) of the call's tokens into d.krot (no-op when d.krot is null).
+hipError_t launch_rope_keys(const Dims& m, const Dev& d, const Src& src, hipStream_t st);
 // Copy positions [from, to) of the call inputs into the ring (keys rotated).
 hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st);
 // Decode step at position t: write token t (rotated key, value, gate logit) into ring

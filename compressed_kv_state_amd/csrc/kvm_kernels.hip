@@ -1467,6 +1467,350 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
 }
 
 // =====================================================================
+// Prefill attention, bf16, chunks of 128 / 256 (NW = C/32 waves of 32 queries).
+// Every 64-key tile is staged by direct global->LDS transfers (no registers,
+// no VALU): state rows are gathered from the row-version pool through the
+// snapshot's index list (keys fp16, values rho * u bf16), window keys come
+// pre-rotated (rotary dims from the RoPE prep buffer, live dims from k, or the
+// ring for positions before this call).  LDS tiles are row-major with the
+// 16-byte units of each row XOR-swizzled by the row index (applied through the
+// source addresses), and the value operand of O^T = V^T . P^T is read with
+// ds_read_b64_tr_b16, which returns 4 consecutive keys of one dim per lane.
+// Two stages: the transfer of tile T+1 overlaps the MFMAs and softmax of T.
+// [KVM summary, Core mechanisms 2, 4]; [KVM summary, Methodology].
+// =====================================================================
+constexpr int kDmaIdxCap = 8192;   // snapshot rows whose version ids fit the LDS list
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x4 ds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_dma_kernel(Dims m, Dev d, Src src, int64_t c_begin, int n_q,
+                                                              int64_t end_pos, bf16* out) {
+  constexpr int C = NW * 32;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t sK0[8192];
+  __shared__ __attribute__((aligned(16))) uint8_t sK1[8192];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[8192];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[8192];
+  extern __shared__ int sIdx[];
+
+  int s, cl;
+  {
+    const int b = blockIdx.x;
+    if (m.BH % 8 == 0) {
+      const int x = b & 7, k = b >> 3, spx = m.BH >> 3;
+      s = x + 8 * (k % spx);
+      cl = n_q - 1 - k / spx;
+    } else {
+      s = b % m.BH;
+      cl = n_q - 1 - b / m.BH;
+    }
+  }
+  const int64_t c = c_begin + cl;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
+  const int64_t cpos = c * C;
+  const int64_t qpos = cpos + 32 * w + jl;
+  const bool qvalid = qpos < end_pos;
+  const int64_t qp = qvalid ? qpos : (end_pos - 1);
+  const float c2 = m.scale * kLog2e;
+
+  // ---- snapshot of chunk c - W/C - 1: its version ids into LDS
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  int64_t ioff = 0;
+  if (jj >= 0) {
+    const int4 sc4 = d.sched[jj];
+    S = sc4.z + sc4.x + sc4.y;
+    ioff = sc4.w;
+  }
+  {
+    const int* idxg = d.idx + (size_t)s * m.idx_total + ioff;
+    for (int i = tid; i < S; i += NT) sIdx[i] = idxg[i];
+  }
+  const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
+
+  // ---- query fragments (B operand of S^T = K . Q^T), pre-scaled by scale*log2(e)
+  const bf16* qrow = reinterpret_cast<const bf16*>(src.q) + ((size_t)s * src.n_call + (size_t)(qp - src.p0)) * 64;
+  bf16x8 qf[4];    // window: k-step kk holds dims 16kk + 8h + e (rotated for kk < 2)
+  f16x8 qs16[2];   // state: dims 32 + 16kk + 8h + e, fp16, scaled by 2^-qsh
+  int qsh = 0;
+  {
+    alignas(16) bf16 x[4][8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) copy16(x[kk], qrow + 16 * kk + 8 * h);
+    const float* rc = d.rope_cos + qp * 16;
+    const float* rsn = d.rope_sin + qp * 16;
+    float qmx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = tof(x[0][e]), b = tof(x[1][e]);
+      rot(a, b, rc[8 * h + e], rsn[8 * h + e]);
+      qf[0][e] = (bf16)(a * c2);
+      qf[1][e] = (bf16)(b * c2);
+      qf[2][e] = (bf16)(tof(x[2][e]) * c2);
+      qf[3][e] = (bf16)(tof(x[3][e]) * c2);
+      qmx = fmaxf(qmx, fmaxf(fabsf(tof(x[2][e])), fabsf(tof(x[3][e]))) * c2);
+    }
+    // fp16 range guard for the state query: exact power-of-two pre-scale
+    qmx = fmaxf(qmx, partner_f(qmx));
+    if (qmx >= 16384.f) {
+      int ex;
+      frexpf(qmx, &ex);
+      qsh = ex - 14;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qs16[0][e] = (f16)ldexpf(tof(x[2][e]) * c2, -qsh);
+      qs16[1][e] = (f16)ldexpf(tof(x[3][e]) * c2, -qsh);
+    }
+  }
+  const bool wave_qsh = __ballot(qsh != 0) != 0ull;
+
+  // ---- running softmax state: acc comes out of the MFMA as logit*c - mref
+  float mref = 0.f, lrun = 0.f;
+  bool started = false;
+  f32x16 negm = {};
+  f32x16 O0 = {}, O1 = {};
+
+  // ---- tile geometry: state tiles first, then window tiles
+  const int n_st = (S + 63) >> 6;
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < end_pos ? cpos + C : end_pos;
+  const int n_wt = (int)((hi - lo + 63) >> 6);
+  const int n_tiles = n_st + n_wt;
+  const int64_t qlast = min(cpos + 32 * w + 31, end_pos - 1);
+  const int64_t qfirst = cpos + 32 * w;
+  const bf16* krot = reinterpret_cast<const bf16*>(d.krot) + (size_t)s * m.max_tokens * 32;
+  const bf16* kin = reinterpret_cast<const bf16*>(src.k) + (size_t)s * src.n_call * 64;
+  const bf16* vin = reinterpret_cast<const bf16*>(src.v) + (size_t)s * src.n_call * 64;
+  const bf16* ring_k = reinterpret_cast<const bf16*>(d.ring_k) + (size_t)s * m.R * 64;
+  const bf16* ring_v = reinterpret_cast<const bf16*>(d.ring_v) + (size_t)s * m.R * 64;
+
+  // ---- lane-constant LDS offsets
+  // K operand: key kb + jl, 16-byte unit 2kk + h, swizzled by the key's low bits
+  const int kswz_w = jl & 7, kswz_s = jl & 3;
+  // V operand (transposed read): group g = lane/16 supplies keys 4h + (lane%16)/4 and
+  // dims 32dt + 16(g%2) + 4(lane%4); unit index swizzled by the key's low bits
+  int voff[2];
+  {
+    const int g = lane >> 4, p = lane & 15;
+    const int kl = 4 * h + (p >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const int d0 = 32 * dt + 16 * (g & 1) + 4 * (p & 3);
+      voff[dt] = kl * 128 + 16 * ((d0 >> 3) ^ kl) + 8 * ((d0 >> 2) & 1);
+    }
+  }
+
+  // ---- direct global->LDS staging of tile T (each wave a share of the 1 KB transfers)
+  auto issue = [&](int T, uint8_t* K, uint8_t* V) {
+    if (T < n_st) {
+      const int r0 = T << 6;
+      for (int i = w; i < 4; i += NW) {           // keys: 16 rows x 64 B per transfer
+        const int row = 16 * i + (lane >> 2);
+        const int unit = (lane & 3) ^ (row & 3);
+        const int r = min(r0 + row, S - 1);
+        __builtin_amdgcn_global_load_lds(pk + (size_t)sIdx[r] * 32 + 8 * unit, K + 1024 * i, 16, 0, 0);
+      }
+      for (int i = w; i < 8; i += NW) {           // values: 8 rows x 128 B per transfer
+        const int row = 8 * i + (lane >> 3);
+        const int unit = (lane & 7) ^ (row & 7);
+        const int r = min(r0 + row, S - 1);
+        __builtin_amdgcn_global_load_lds(pv + (size_t)sIdx[r] * 64 + 8 * unit, V + 1024 * i, 16, 0, 0);
+      }
+    } else {
+      const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
+      for (int i = w; i < 8; i += NW) {           // keys and values: 8 keys x 128 B per transfer
+        const int key = 8 * i + (lane >> 3);
+        const int unit = (lane & 7) ^ (key & 7);
+        const int64_t pos = min(k0 + key, hi - 1);
+        const bf16* ks;
+        const bf16* vs;
+        if (pos >= src.p0) {
+          const size_t r = (size_t)(pos - src.p0) * 64;
+          ks = unit < 4 ? krot + pos * 32 + 8 * unit : kin + r + 8 * unit;
+          vs = vin + r + 8 * unit;
+        } else {
+          const size_t r = (size_t)(pos % m.R) * 64;   // ring keys are stored rotated
+          ks = ring_k + r + 8 * unit;
+          vs = ring_v + r + 8 * unit;
+        }
+        __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
+      }
+    }
+  };
+
+  // ---- online softmax of one 32-key subtile; p packed to bf16, row sum from the packed p
+  auto softmax = [&](f32x16& acc, bf16x8& pf0, bf16x8& pf1) {
+    float mx = fmaxf(acc[0], acc[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+    mx = fmaxf(mx, partner_f(mx));
+    if ((!started && mx != -kInf) || mx > kTau) {
+      if (started) {
+        const float alpha = exp2_fast(-mx);
+        lrun *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { O0[r] *= alpha; O1[r] *= alpha; }
+      }
+      mref += mx;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { acc[r] -= mx; negm[r] = -mref; }
+      started = true;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pf0[e] = (bf16)exp2_fast(acc[e]);
+      pf1[e] = (bf16)exp2_fast(acc[8 + e]);
+    }
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+    float ls = lrun;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf0[e], pf0[e + 1]}, one, ls, false);
+      ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf1[e], pf1[e + 1]}, one, ls, false);
+    }
+    lrun = ls;
+  };
+  // O^T += V^T . P^T over the 32 keys [kb, kb + 32) of the staged tile
+  auto pv_acc = [&](const uint8_t* V, int kb, const bf16x8& pf0, const bf16x8& pf1) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      f32x16& O = dt ? O1 : O0;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint8_t* base = V + (kb + 16 * b) * 128 + voff[dt];
+        const bf16x4 lo4 = ds_read_tr(base);
+        const bf16x4 hi4 = ds_read_tr(base + 8 * 128);
+        const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        O = mfma_bf16(a, b ? pf1 : pf0, O);
+      }
+    }
+  };
+  auto compute = [&](int T, const uint8_t* K, const uint8_t* V) {
+    if (T < n_st) {
+      const int r0 = T << 6;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kb = 32 * sub;
+        if (r0 + kb >= S) break;
+        const int lim = S - r0 - kb;
+        const uint8_t* kr = K + (kb + jl) * 64;
+        const f16x8 a0 = *reinterpret_cast<const f16x8*>(kr + 16 * (h ^ kswz_s));
+        const f16x8 a1 = *reinterpret_cast<const f16x8*>(kr + 16 * ((2 + h) ^ kswz_s));
+        f32x16 acc;
+        if (!wave_qsh) {
+          acc = mfma_f16(a0, qs16[0], negm);
+          acc = mfma_f16(a1, qs16[1], acc);
+        } else {
+          acc = mfma_f16(a0, qs16[0], f32x16{});
+          acc = mfma_f16(a1, qs16[1], acc);
+          const float sc = ldexpf(1.f, qsh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = acc[r] * sc - mref;
+        }
+        if (lim < 32) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
+        }
+        bf16x8 pf0, pf1;
+        softmax(acc, pf0, pf1);
+        pv_acc(V, kb, pf0, pf1);
+      }
+    } else {
+      const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int kb = 32 * sub;
+        const int64_t ks = k0 + kb;
+        if (ks >= hi || ks > qlast) break;
+        const uint8_t* kr = K + (kb + jl) * 128;
+        f32x16 acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * (h ^ kswz_w)), qf[0], negm);
+#pragma unroll
+        for (int kk = 1; kk < 4; ++kk)
+          acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * kk + h) ^ kswz_w)), qf[kk], acc);
+        if (ks + 31 >= hi || ks + 31 > qfirst) {
+          // key ks + off is valid for this lane's query iff off < lim
+          const int lim = (int)min(hi - ks, qpos - ks + 1);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
+        }
+        bf16x8 pf0, pf1;
+        softmax(acc, pf0, pf1);
+        pv_acc(V, kb, pf0, pf1);
+      }
+    }
+  };
+
+  // ---- two-stage pipeline; each barrier also waits for the wave's own transfers
+  __syncthreads();   // version ids in LDS
+  if (n_tiles > 0) issue(0, sK0, sV0);
+  for (int T = 0; T < n_tiles; T += 2) {
+    __syncthreads();   // tile T in stage 0; stage 1 free
+    if (T + 1 < n_tiles) issue(T + 1, sK1, sV1);
+    compute(T, sK0, sV0);
+    if (T + 1 >= n_tiles) break;
+    __syncthreads();   // tile T+1 in stage 1; stage 0 free
+    if (T + 2 < n_tiles) issue(T + 2, sK0, sV0);
+    compute(T + 1, sK1, sV1);
+  }
+
+  // ---- normalise and store: lane holds dims 8*(r/4) + 4h + r%4 of its query
+  const float lt = lrun + partner_f(lrun);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qvalid) {
+    bf16* orow = out + ((size_t)s * src.n_call + (size_t)(qpos - src.p0)) * 64;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const f32x16& O = dt ? O1 : O0;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        alignas(8) bf16 vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vals[e] = (bf16)(O[4 * g4 + e] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * g4 + 4 * h) = *reinterpret_cast<const uint2*>(vals);
+      }
+    }
+  }
+}
+
+// RoPE prep for the DMA attention: rotary dims [0, 32) of every key of the call,
+// rotated at its absolute position, into krot[BH][max_tokens][32] (bf16).
+__global__ void rope_keys_kernel(Dims m, Dev d, Src src) {
+  const int64_t n = (int64_t)m.BH * src.n_call * 2;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int hh = (int)(i & 1);
+    const int64_t tok = i >> 1;
+    const int s = (int)(tok / src.n_call);
+    const int64_t pos = src.p0 + tok % src.n_call;
+    const bf16* kr = reinterpret_cast<const bf16*>(src.k) + (size_t)tok * 64;
+    alignas(16) bf16 x[8], y[8];
+    copy16(x, kr + 8 * hh);
+    copy16(y, kr + 16 + 8 * hh);
+    const float* rc = d.rope_cos + pos * 16 + 8 * hh;
+    const float* rs = d.rope_sin + pos * 16 + 8 * hh;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = tof(x[e]), b = tof(y[e]);
+      rot(a, b, rc[e], rs[e]);
+      x[e] = (bf16)a;
+      y[e] = (bf16)b;
+    }
+    bf16* dst = reinterpret_cast<bf16*>(d.krot) + ((size_t)s * m.max_tokens + (size_t)pos) * 32;
+    copy16(dst + 8 * hh, x);
+    copy16(dst + 16 + 8 * hh, y);
+  }
+}
+
+// =====================================================================
 // Ring maintenance: the last W + C positions (rotated keys, values, gate
 // logits) are kept so that decode steps and later prefill calls can see the
 // window and absorb the chunk that leaves it.
@@ -1704,19 +2048,29 @@ hipError_t scan_dispatch(const Dims& m, const Dev& d, const Src& src, int jb, in
 
 template <typename T>
 hipError_t attn_dispatch(const Dims& m, const Dev& d, const Src& src, int64_t cb, int nq, int64_t end, void* out,
-                         hipStream_t st) {
+                         int s_max, hipStream_t st) {
   const dim3 grid((unsigned)(m.BH * nq));
   T* o = reinterpret_cast<T*>(out);
+  const bool dma = Is<T>::bf && d.krot != nullptr && s_max <= kDmaIdxCap;
+  const size_t idx_bytes = (size_t)(s_max > 0 ? s_max : 1) * 4;
   switch (m.C) {
     case 32: attn_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, src, cb, nq, end, o); break;
     case 64: attn_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, src, cb, nq, end, o); break;
     case 128:
-      if constexpr (Is<T>::bf) attn_bf16_kernel<4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o);
-      else attn_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o);
+      if constexpr (Is<T>::bf) {
+        if (dma) attn_dma_kernel<4><<<grid, 256, idx_bytes, st>>>(m, d, src, cb, nq, end, o);
+        else attn_bf16_kernel<4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o);
+      } else {
+        attn_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, src, cb, nq, end, o);
+      }
       break;
     case 256:
-      if constexpr (Is<T>::bf) attn_bf16_kernel<8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o);
-      else attn_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o);
+      if constexpr (Is<T>::bf) {
+        if (dma) attn_dma_kernel<8><<<grid, 512, idx_bytes, st>>>(m, d, src, cb, nq, end, o);
+        else attn_bf16_kernel<8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o);
+      } else {
+        attn_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, src, cb, nq, end, o);
+      }
       break;
     default: return hipErrorInvalidValue;
   }
@@ -1737,10 +2091,18 @@ hipError_t launch_scan(const Dims& m, const Dev& d, const Src& src, int jb, int 
 }
 
 hipError_t launch_attn(const Dims& m, const Dev& d, const Src& src, int64_t cb, int nq, int64_t end, void* out,
-                       hipStream_t st) {
+                       int s_max, hipStream_t st) {
   if (nq <= 0) return hipSuccess;
-  return m.bf16 ? attn_dispatch<bf16>(m, d, src, cb, nq, end, out, st)
-                : attn_dispatch<float>(m, d, src, cb, nq, end, out, st);
+  return m.bf16 ? attn_dispatch<bf16>(m, d, src, cb, nq, end, out, s_max, st)
+                : attn_dispatch<float>(m, d, src, cb, nq, end, out, s_max, st);
+}
+
+hipError_t launch_rope_keys(const Dims& m, const Dev& d, const Src& src, hipStream_t st) {
+  if (!d.krot || src.n_call <= 0) return hipSuccess;
+  const int64_t n = (int64_t)m.BH * src.n_call * 2;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+  rope_keys_kernel<<<(unsigned)blocks, 256, 0, st>>>(m, d, src);
+  return hipGetLastError();
 }
 
 hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st) {

@@ -61,7 +61,8 @@ class _Prof(ctypes.Structure):
                 ("attn_ms", ctypes.c_double), ("attn_launches", ctypes.c_int64),
                 ("ring_ms", ctypes.c_double), ("ring_launches", ctypes.c_int64),
                 ("dec_absorb_ms", ctypes.c_double), ("dec_absorb_launches", ctypes.c_int64),
-                ("dec_attn_ms", ctypes.c_double), ("dec_attn_launches", ctypes.c_int64)]
+                ("dec_attn_ms", ctypes.c_double), ("dec_attn_launches", ctypes.c_int64),
+                ("prep_ms", ctypes.c_double), ("prep_launches", ctypes.c_int64)]
 
 
 _lib = None

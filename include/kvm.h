@@ -194,6 +194,7 @@ typedef struct kvm_profile_times {
   double ring_ms;          int64_t ring_launches;          /* ring refresh after prefill */
   double dec_absorb_ms;    int64_t dec_absorb_launches;    /* decode-time absorption */
   double dec_attn_ms;      int64_t dec_attn_launches;      /* decode step kernel: ring write + attention */
+  double prep_ms;          int64_t prep_launches;          /* prefill RoPE prep of the call's keys */
 } kvm_profile_times;
 
 /* Enable (1) or disable (0) recording of a HIP event pair around every kernel
