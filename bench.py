@@ -42,7 +42,7 @@ PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "compressed_kv_state_amd", "csrc", "kvm_kernels.hip")
 ATTN_KERNEL = "attn_dma_kernel"   # the bf16 attention kernel for chunks of 128 / 256
-COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_bf16_kernel_350m_sqrt8_counters.md")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_dma_kernel_350m_sqrt8_counters.md")
 
 
 def log(msg):
@@ -50,8 +50,11 @@ def log(msg):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel's own source text (the counters describe that kernel only)."""
+    src = open(KERNEL_SRC).read()
+    a = src.index(f"void {ATTN_KERNEL}(")
+    b = src.index("\n}\n", a)
+    return hashlib.sha256(src[a:b].encode()).hexdigest()[:16]
 
 
 def attn_flops(cfg, n: int) -> int:
@@ -263,7 +266,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str
         f.write("A prefill launches the attention in pieces beside the scan; the figures are means over\n"
                 "the pieces of the profiled prefills, like bench.py's per-launch FLOPs and time.\n\n")
         f.write(f"traffic_bytes_per_launch: {traffic:.6e}\n")
-        f.write(f"kernel_source_sha256_16: {kernel_sha()}\n")
+        f.write(f"kernel_source_sha256_16: {kernel_sha()}  (source text of {ATTN_KERNEL})\n")
     print(f"wrote {out_md}: traffic {traffic / 1e9:.3f} GB per launch")
 
 
@@ -273,7 +276,7 @@ def summarize_trace(db: str, out_md: str, command: str, title: str):
     import statistics
     con = sqlite3.connect(db)
     rows = con.execute("select name, grid_x, workgroup_x, start, end from kernels order by start").fetchall()
-    dec0 = min([t0 for name, _, _, t0, _ in rows if "dec_attn_kernel" in name] or [float("inf")])
+    dec0 = min([t0 for name, _, _, t0, _ in rows if "dec_kernel" in name] or [float("inf")])
     prefill_attn = [(t1 - t0) / 1e3 for name, _, _, t0, t1 in rows if ATTN_KERNEL in name and t0 < dec0]
     sel = {}
     for name, gx, wx, t0, t1 in rows:
@@ -289,6 +292,10 @@ def summarize_trace(db: str, out_md: str, command: str, title: str):
         for (short, gx, wx), d in sorted(sel.items(), key=lambda kv: -sum(kv[1])):
             f.write(f"| {short} | {gx} | {wx} | {len(d)} | {sum(d):.1f} | {statistics.mean(d):.1f} | "
                     f"{min(d):.1f} | {max(d):.1f} |\n")
+        dec = [x for (k, _, _), d in sel.items() if k.startswith("dec_kernel") for x in d]
+        if dec:
+            f.write(f"\ndec_kernel (one fused decode step, all sequences): {len(dec)} dispatches, "
+                    f"mean {statistics.mean(dec):.1f} us\n")
         if prefill_attn:
             f.write(f"\n{ATTN_KERNEL} in the prefill workload (dispatches before the first decode kernel): "
                     f"{len(prefill_attn)} dispatches, mean {statistics.mean(prefill_attn):.1f} us, "
