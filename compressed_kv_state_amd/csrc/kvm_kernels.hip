@@ -137,8 +137,22 @@ __global__ void rope_table_kernel(float* cosv, float* sinv, int64_t max_tokens, 
 // split into bf16 hi + lo (|U - hi - lo| <= 2^-18 |U|), so two bf16 MFMA
 // passes give dot(k, U_i) to ~1e-5 relative.  fp32 path: fp32 MFMA.
 // =====================================================================
-constexpr int kScanWaves = 8;
-constexpr int kScanThreads = 64 * kScanWaves;
+// Workgroup geometry per chunk size.  Eight waves: each holds CTW token blocks
+// of 32 in the cosine pass (at most 4, for registers); TS wave groups split the
+// chunk's tokens and the WG waves of a group stride over the state rows.  (12
+// or 16 waves with the tokens split further measured slower: the cosine pass
+// is MFMA/VALU-bound per SIMD, and splitting lengthens each wave's tile chain.)
+template <int C>
+struct ScanGeom {
+  static constexpr int NW = 8;                        // waves
+  static constexpr int NT = 64 * NW;                  // threads
+  static constexpr int CT = C / 32;                   // token blocks of 32
+  static constexpr int CTW = CT < 4 ? CT : 4;         // token blocks per wave
+  static constexpr int TS = CT / CTW;                 // token groups
+  static constexpr int WG = NW / TS;                  // waves sharing one token group (tile stride)
+};
+
+constexpr int pow2_floor(int x) { return x >= 2 ? 2 * pow2_floor(x / 2) : 1; }
 constexpr int kSink = 0, kAppend = 1, kMerge = 2;
 
 // Chunk buffers: NBUF = 2 lets the next chunk stream into LDS (direct
@@ -148,17 +162,22 @@ struct ScanBuf {
   static constexpr int NBUF = sizeof(T) * C <= 512 ? 2 : 1;
 };
 
+constexpr int kVerCap = 4096;   // rows whose current version ids the scan keeps in LDS
+
 template <typename T, int C>
 struct ScanSmem {
   static constexpr int NBUF = ScanBuf<T, C>::NBUF;
+  // the touched rows' raw sums are prefetched into LDS where it fits
+  static constexpr bool PREF = sizeof(T) == 2 ? C <= 128 : C <= 64;
+  static constexpr int PC = PREF ? C : 1;
   alignas(16) T k[NBUF][C][32];   // live key dims of the chunk's tokens
   alignas(16) T v[NBUF][C][64];   // values
   alignas(16) float l[NBUF][C];   // gate logits
   float g[C];         // gate
   float kn[C];        // |k live|
   alignas(16) uint64_t key[C];    // sort keys
-  float red_v[kScanWaves][C];
-  int red_r[kScanWaves][C];
+  float red_v[ScanGeom<C>::NW][C];
+  int red_r[ScanGeom<C>::NW][C];
   float bE[C];
   int rE[C];
   float bA[C];
@@ -172,7 +191,12 @@ struct ScanSmem {
   int seg_start[C];
   int seg_len[C];
   int created_seg[C];
-  int wtot[kScanWaves];
+  int wtot[ScanGeom<C>::NW];
+  alignas(16) float mk[PC][32];   // key sum of the row merged-into by token t (prefetch)
+  alignas(16) float mv[PC][64];   // value sum of that row
+  int mc[PC];                     // its count
+  float mr[PC];                   // its radius
+  int ver_cur[kVerCap];           // current version id of every row
   int nold;
   int nseg;
 };
@@ -196,23 +220,51 @@ __device__ __forceinline__ void chunk_load_lds(ScanSmem<T, C>& sm, int buf, cons
     }
     return (key ? ring_k : ring_v) + (size_t)(pos % m.R) * 64;
   };
-  for (int base = w * 64; base < C * KP; base += kScanThreads) {
+  constexpr int NT = ScanGeom<C>::NT;
+  for (int base = w * 64; base < C * KP; base += NT) {
     const int p = base + lane, t = p / KP, q = p % KP;
     __builtin_amdgcn_global_load_lds(row_of(t, true) + 32 + q * EL, &sm.k[buf][0][0] + base * EL, 16, 0, 0);
   }
-  for (int base = w * 64; base < C * VP; base += kScanThreads) {
+  for (int base = w * 64; base < C * VP; base += NT) {
     const int p = base + lane, t = p / VP, q = p % VP;
     __builtin_amdgcn_global_load_lds(row_of(t, false) + q * EL, &sm.v[buf][0][0] + base * EL, 16, 0, 0);
   }
   // C = 32 fills half a wave: the other lanes stay idle (lane i of the wave
   // writes LDS word base + i, so an active lane past C would land in the
   // neighbouring buffer)
-  for (int base = w * 64; base < C; base += kScanThreads) {
+  for (int base = w * 64; base < C; base += NT) {
     const int t = base + lane;
     if (t >= C) break;
     const int64_t pos = P0 + t;
     const float* lp = from_in ? src.l + (size_t)s * src.n_call + (size_t)(pos - src.p0) : ring_l + pos % m.R;
     __builtin_amdgcn_global_load_lds(lp, &sm.l[buf][0] + base, 4, 0, 0);
+  }
+}
+
+// Queue direct global->LDS transfers of the row each merged token of the chunk
+// goes to (raw key and value sums, count, radius) into the token's slot of
+// sm.mk / mv / mc / mr; a full barrier (vmcnt) completes them.
+template <typename T, int C>
+__device__ __forceinline__ void prefetch_rows(ScanSmem<T, C>& sm, const float* key_sum, const float* val_sum,
+                                              const int* count, const float* rho) {
+  constexpr int NW = ScanGeom<C>::NW;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int i = w; i < C / 8; i += NW) {        // key sums: 8 tokens x 128 B per transfer
+    const int t = 8 * i + (lane >> 3);
+    if (sm.flag[t] == kMerge)
+      __builtin_amdgcn_global_load_lds(key_sum + (size_t)sm.arow[t] * 32 + 4 * (lane & 7), &sm.mk[8 * i][0], 16, 0, 0);
+  }
+  for (int i = w; i < C / 4; i += NW) {        // value sums: 4 tokens x 256 B per transfer
+    const int t = 4 * i + (lane >> 4);
+    if (sm.flag[t] == kMerge)
+      __builtin_amdgcn_global_load_lds(val_sum + (size_t)sm.arow[t] * 64 + 4 * (lane & 15), &sm.mv[4 * i][0], 16, 0, 0);
+  }
+  for (int i = w; i < (C + 63) / 64; i += NW) {  // count and radius: 64 tokens x 4 B per transfer
+    const int t = 64 * i + lane;
+    if (t < C && sm.flag[t] == kMerge) {
+      __builtin_amdgcn_global_load_lds(count + sm.arow[t], &sm.mc[64 * i], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(rho + sm.arow[t], &sm.mr[64 * i], 4, 0, 0);
+    }
   }
 }
 
@@ -245,21 +297,24 @@ __device__ __forceinline__ void lane_best(f32x16 acc, int row0, int re, int h, f
 // All threads of the block must call it.
 template <typename T, int C>
 __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, int re, float* outv, int* outr) {
-  constexpr int CT = C / 32;
+  using G = ScanGeom<C>;
+  constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
+  const int tg = w % G::TS, wt = w / G::TS;   // token group, tile lane
+  const int tok0 = 32 * CT * tg;              // first token of the group
   float bv[CT];
   int br[CT];
 #pragma unroll
   for (int tt = 0; tt < CT; ++tt) { bv[tt] = -kInf; br[tt] = INT_MAX; }
   const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
-  if (w < ntile) {
+  if (wt < ntile) {
     if constexpr (Is<T>::bf) {
       // lane half h owns dims [16h, 16h+16) of every 32-dim key
       bf16x8 bfr[CT][2];
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt) {
-        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * tt + jl][16 * h]);
-        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][32 * tt + jl][16 * h + 8]);
+        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][tok0 + 32 * tt + jl][16 * h]);
+        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][tok0 + 32 * tt + jl][16 * h + 8]);
       }
       const bf16* U = reinterpret_cast<const bf16*>(unit);
       auto load = [&](int tile, bf16x8 (&a)[4]) {
@@ -291,15 +346,16 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
       };
       // two register sets in ping-pong: the loads of tile i+2W are issued right
       // after the MFMAs of tile i read their set, so they overlap tile i+W
+      constexpr int WG = G::WG;
       bf16x8 a0[4], a1[4];
-      if (w < ntile) load(w, a0);
-      if (w + kScanWaves < ntile) load(w + kScanWaves, a1);
-      for (int tile = w; tile < ntile; tile += 2 * kScanWaves) {
+      load(wt, a0);
+      if (wt + WG < ntile) load(wt + WG, a1);
+      for (int tile = wt; tile < ntile; tile += 2 * WG) {
         tile_best(a0, tile);
-        if (tile + 2 * kScanWaves < ntile) load(tile + 2 * kScanWaves, a0);
-        if (tile + kScanWaves < ntile) {
-          tile_best(a1, tile + kScanWaves);
-          if (tile + 3 * kScanWaves < ntile) load(tile + 3 * kScanWaves, a1);
+        if (tile + 2 * WG < ntile) load(tile + 2 * WG, a0);
+        if (tile + WG < ntile) {
+          tile_best(a1, tile + WG);
+          if (tile + 3 * WG < ntile) load(tile + 3 * WG, a1);
         }
       }
     } else {
@@ -308,9 +364,9 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(sm.k[buf][32 * tt + jl][16 * h + kk]);
+        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(sm.k[buf][tok0 + 32 * tt + jl][16 * h + kk]);
       const float* U = reinterpret_cast<const float*>(unit);
-      for (int tile = w; tile < ntile; tile += kScanWaves) {
+      for (int tile = wt; tile < ntile; tile += G::WG) {
         const int row0 = rb + (tile << 5);
         const int ri = min(row0 + jl, re - 1);
         const float* u = U + (size_t)ri * 32 + 16 * h;
@@ -334,11 +390,11 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
     const float ov = partner_f(bv[tt]);
     const int orow = partner_i(br[tt]);
     if (ov > bv[tt] || (ov == bv[tt] && orow < br[tt])) { bv[tt] = ov; br[tt] = orow; }
-    if (h == 0) { sm.red_v[w][32 * tt + jl] = bv[tt]; sm.red_r[w][32 * tt + jl] = br[tt]; }
+    if (h == 0 && wt < ntile) { sm.red_v[wt][tok0 + 32 * tt + jl] = bv[tt]; sm.red_r[wt][tok0 + 32 * tt + jl] = br[tt]; }
   }
   lds_barrier();
-  const int nw = min(ntile, kScanWaves);
-  for (int t = tid; t < C; t += kScanThreads) {
+  const int nw = min(ntile, G::WG);
+  for (int t = tid; t < C; t += G::NT) {
     float v = -kInf;
     int r = INT_MAX;
     for (int ww = 0; ww < nw; ++ww) {
@@ -353,12 +409,13 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
 }
 
 // rank[t] = #{s : key[s] < key[t]} for every t < C (tokens to leave out carry
-// the largest key), using all threads: P = threads / C lanes per token, each
-// over C / P keys read two at a time, summed with lane shuffles.  Returns the
+// the largest key), using up to all threads: P = min(threads / C, C / 2) lanes
+// per token, each over C / P keys read two at a time, summed with lane shuffles.  Returns the
 // rank on the lane with part == 0 (else -1) and that lane's token in t_out.
 template <int C>
 __device__ __forceinline__ int parallel_rank(const uint64_t* key, int& t_out) {
-  constexpr int P = kScanThreads / C >= 1 ? kScanThreads / C : 1;
+  constexpr int NT = ScanGeom<C>::NT;
+  constexpr int P = pow2_floor(NT / C < C / 2 ? NT / C : C / 2);
   constexpr int SPAN = C / P;
   static_assert(SPAN % 2 == 0, "keys are read in pairs");
   const int t = threadIdx.x / P, part = threadIdx.x % P;
@@ -379,7 +436,9 @@ __device__ __forceinline__ int parallel_rank(const uint64_t* key, int& t_out) {
 }
 
 template <typename T, int C>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src src, int j_begin, int j_end) {
+__global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Src src, int j_begin, int j_end) {
+  constexpr int kScanThreads = ScanGeom<C>::NT;
+  constexpr int kScanWaves = ScanGeom<C>::NW;
   using RT = typename Rd<T>::type;
   constexpr int REL = 16 / sizeof(RT);     // read-form elements per 16-byte piece
   __shared__ ScanSmem<T, C> sm;
@@ -401,6 +460,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
   const T* ring_v = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
   const float* ring_l = d.ring_l + (size_t)s * m.R;
   int nver = d.nver[s];
+  constexpr bool PREF = ScanSmem<T, C>::PREF;
+  // the current version of every row lives in LDS; each chunk's index list is
+  // written out from it at the start of the next step (stores only)
+  const bool ver_lds = m.S_cap <= kVerCap;
+  if (ver_lds && j_begin > 0 && j_begin < j_end) {
+    const int r0 = d.sched[j_begin].z;
+    const int* prev = idx + d.sched[j_begin - 1].w;
+    for (int i = tid; i < r0; i += kScanThreads) sm.ver_cur[i] = prev[i];
+  }
 
   constexpr int NBUF = ScanBuf<T, C>::NBUF;
   if (NBUF == 2 && j_begin < j_end) {
@@ -414,6 +482,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
   // closes the step.
   int4 sc_next = j_begin < j_end ? d.sched[j_begin] : make_int4(0, 0, 0, 0);
   int prev_off = j_begin > 0 ? d.sched[j_begin - 1].w : 0;
+  int last_rows = 0;
   for (int j = j_begin; j < j_end; ++j) {
     const int4 sc = sc_next;
     const int sinks = sc.x, mj = sc.y, R0 = sc.z;
@@ -421,6 +490,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
     const int nc = sinks + mj;
     const int rows_after = R0 + nc;
     const int64_t P0 = (int64_t)j * C;
+
+    // index list of the previous step (its rows are the R0 rows before this chunk)
+    if (ver_lds && j > j_begin)
+      for (int i = tid; i < R0; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
 
     // ---- 1. the chunk is in LDS buffer `cur`; start streaming the next one into the other
     const int cur = NBUF == 2 ? (j - j_begin) & 1 : 0;
@@ -532,6 +605,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
     for (int c2 = tid; c2 < nc; c2 += kScanThreads) sm.created_seg[c2] = -1;
     lds_barrier();
 
+    // start fetching each merged token's target row (sums, count, radius) into LDS;
+    // the update below reads them after the sort (direct global->LDS transfers)
+    if constexpr (PREF) prefetch_rows<T, C>(sm, key_sum, val_sum, count, rho);
+
     // ---- 5. sort merged tokens by (row, position); cut into per-row segments
     const int nm = C - nc;
     {
@@ -581,7 +658,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
 
     // ---- 6a. the new index list: rows before the chunk that this chunk does not
     // touch keep their version (touched rows are the first nold segments, sorted)
-    if (j > 0) {
+    if (!ver_lds && j > 0) {
       const int64_t prev = prev_off;
       for (int i = tid; i < R0; i += kScanThreads) {
         int lo = 0, hi = nold;
@@ -593,6 +670,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
         if (lo == nold || sm.seg_row[lo] != i) idx[ioff + i] = idx[prev + i];
       }
     }
+
+    if constexpr (PREF) __syncthreads();   // the prefetched rows have landed (each wave waits for its own)
 
     // ---- 6b. update every touched or created row (four lanes per row, in increasing row order)
     for (int u = tid >> 2; u < nu; u += kScanThreads / 4) {
@@ -622,6 +701,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
         v2 += __shfl_xor(v2, 2);
         n = 1;
         rh = sqrtf(v2);
+      } else if (PREF) {
+        // prefetched by the segment's first token
+        const int t0 = sm.srt_tok[sm.seg_start[seg]];
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) *reinterpret_cast<float4*>(&K[i]) = *reinterpret_cast<const float4*>(&sm.mk[t0][8 * sub + i]);
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4*>(&V[i]) = *reinterpret_cast<const float4*>(&sm.mv[t0][16 * sub + i]);
+        n = sm.mc[t0];
+        rh = sm.mr[t0];
       } else {
         const float* ks = key_sum + (size_t)row * 32 + 8 * sub;
         const float* vs = val_sum + (size_t)row * 64 + 16 * sub;
@@ -722,7 +810,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
       }
       if (sub == 0) {
         prho[ver] = rh;
-        idx[ioff + row] = ver;
+        if (ver_lds) sm.ver_cur[row] = ver;
+        else idx[ioff + row] = ver;
       }
     }
     if (m.trace) {
@@ -735,8 +824,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(Dims m, Dev d, Src s
     }
     nver += nu;
     prev_off = (int)ioff;
+    last_rows = rows_after;
     __syncthreads();  // the step's global writes are visible to every thread of the next step
   }
+  if (ver_lds && j_end > j_begin)
+    for (int i = tid; i < last_rows; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
   if (tid == 0) d.nver[s] = nver;
 }
 
@@ -2037,10 +2129,10 @@ __global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, ty
 template <typename T>
 hipError_t scan_dispatch(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {
   switch (m.C) {
-    case 32: scan_kernel<T, 32><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
-    case 64: scan_kernel<T, 64><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
-    case 128: scan_kernel<T, 128><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
-    case 256: scan_kernel<T, 256><<<m.BH, kScanThreads, 0, st>>>(m, d, src, jb, je); break;
+    case 32: scan_kernel<T, 32><<<m.BH, ScanGeom<32>::NT, 0, st>>>(m, d, src, jb, je); break;
+    case 64: scan_kernel<T, 64><<<m.BH, ScanGeom<64>::NT, 0, st>>>(m, d, src, jb, je); break;
+    case 128: scan_kernel<T, 128><<<m.BH, ScanGeom<128>::NT, 0, st>>>(m, d, src, jb, je); break;
+    case 256: scan_kernel<T, 256><<<m.BH, ScanGeom<256>::NT, 0, st>>>(m, d, src, jb, je); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
