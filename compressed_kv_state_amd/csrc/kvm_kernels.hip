@@ -87,6 +87,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier that publishes data brought in by global->LDS transfers.  Such a
+// transfer writes LDS when its vector-memory counter retires, and a
+// workgroup-scope barrier does not wait for vector memory on this target, so
+// each wave first waits for all of its own transfers (vmcnt(0); the immediate
+// leaves expcnt and lgkmcnt at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void dma_barrier() {
+  wait_vmem();
+  __syncthreads();
+}
+
 // Total order on floats (NaN included) so that a rank count always selects
 // exactly m items.
 __device__ __forceinline__ uint32_t ordered(float x) {
@@ -204,7 +215,7 @@ struct ScanSmem {
 // Queue direct global->LDS loads of chunk P0's live keys, values and gate
 // logits into buffer `buf`.  Each wave instruction moves 64 x 16 bytes (4
 // bytes for the logits) into consecutive LDS; the loads complete in the
-// background (vmcnt), so only a full barrier waits for them.
+// background (vmcnt); dma_barrier() waits for them.
 template <typename T, int C>
 __device__ __forceinline__ void chunk_load_lds(ScanSmem<T, C>& sm, int buf, const Dims& m, const Src& src, int s,
                                                int64_t P0, const T* ring_k, const T* ring_v, const float* ring_l) {
@@ -243,7 +254,7 @@ __device__ __forceinline__ void chunk_load_lds(ScanSmem<T, C>& sm, int buf, cons
 
 // Queue direct global->LDS transfers of the row each merged token of the chunk
 // goes to (raw key and value sums, count, radius) into the token's slot of
-// sm.mk / mv / mc / mr; a full barrier (vmcnt) completes them.
+// sm.mk / mv / mc / mr; dma_barrier() completes them.
 template <typename T, int C>
 __device__ __forceinline__ void prefetch_rows(ScanSmem<T, C>& sm, const float* key_sum, const float* val_sum,
                                               const int* count, const float* rho) {
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   constexpr int NBUF = ScanBuf<T, C>::NBUF;
   if (NBUF == 2 && j_begin < j_end) {
     chunk_load_lds<T, C>(sm, 0, m, src, s, (int64_t)j_begin * C, ring_k, ring_v, ring_l);
-    __syncthreads();  // waits for the loads (vmcnt) and publishes the buffer
+    dma_barrier();
   }
 
   // Within a chunk step threads exchange data through LDS only (LDS barriers,
@@ -501,7 +512,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       if (j + 1 < j_end) chunk_load_lds<T, C>(sm, cur ^ 1, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     } else {
       chunk_load_lds<T, C>(sm, 0, m, src, s, P0, ring_k, ring_v, ring_l);
-      __syncthreads();
+      dma_barrier();
     }
     const T (*Kc)[32] = sm.k[cur];
     const T (*Vc)[64] = sm.v[cur];
@@ -671,7 +682,11 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       }
     }
 
-    if constexpr (PREF) __syncthreads();   // the prefetched rows have landed (each wave waits for its own)
+    // every wave waits for its own transfers (the next chunk's, issued at the
+    // start of the step, and the prefetched rows) before its stores of the
+    // update enter the same counter; the prefetched rows are then published
+    if constexpr (PREF) dma_barrier();
+    else wait_vmem();
 
     // ---- 6b. update every touched or created row (four lanes per row, in increasing row order)
     for (int u = tid >> 2; u < nu; u += kScanThreads / 4) {
@@ -825,7 +840,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     nver += nu;
     prev_off = (int)ioff;
     last_rows = rows_after;
-    __syncthreads();  // the step's global writes are visible to every thread of the next step
+    __syncthreads();  // publishes the next chunk's buffer (each wave waited above) and the step's writes
   }
   if (ver_lds && j_end > j_begin)
     for (int i = tid; i < last_rows; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
@@ -1846,11 +1861,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_dma_kernel(Dims m, Dev d, Src
   __syncthreads();   // version ids in LDS
   if (n_tiles > 0) issue(0, sK0, sV0);
   for (int T = 0; T < n_tiles; T += 2) {
-    __syncthreads();   // tile T in stage 0; stage 1 free
+    dma_barrier();   // tile T in stage 0; stage 1 free
     if (T + 1 < n_tiles) issue(T + 1, sK1, sV1);
     compute(T, sK0, sV0);
     if (T + 1 >= n_tiles) break;
-    __syncthreads();   // tile T+1 in stage 1; stage 0 free
+    dma_barrier();   // tile T+1 in stage 1; stage 0 free
     if (T + 2 < n_tiles) issue(T + 2, sK0, sV0);
     compute(T + 1, sK1, sV1);
   }
