@@ -1595,7 +1595,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const uint8_t* p) {
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_dma_kernel(Dims m, Dev d, Src src, int64_t c_begin, int n_q,
+__global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src src, int64_t c_begin, int n_q,
                                                               int64_t end_pos, bf16* out) {
   constexpr int C = NW * 32;
   constexpr int NT = NW * 64;
@@ -1753,11 +1753,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_dma_kernel(Dims m, Dev d, Src
     }
   };
 
-  // ---- online softmax of one 32-key subtile; p packed to bf16, row sum from the packed p
-  auto softmax = [&](f32x16& acc, bf16x8& pf0, bf16x8& pf1) {
-    float mx = fmaxf(acc[0], acc[1]);
+  // ---- online softmax of one 64-key tile (two 32-key subtiles, the second
+  // optional): one maximum, one rescale decision, p packed to bf16 and the row
+  // sum taken from the packed p
+  auto softmax = [&](f32x16& a0, f32x16& a1, bool two, bf16x8 (&pf)[4]) {
+    float mx = fmaxf(a0[0], a0[1]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, a0[r]), a0[r + 1]);
+    if (two) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, a1[r]), a1[r + 1]);
+    }
     mx = fmaxf(mx, partner_f(mx));
     if ((!started && mx != -kInf) || mx > kTau) {
       if (started) {
@@ -1768,20 +1774,32 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_dma_kernel(Dims m, Dev d, Src
       }
       mref += mx;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { acc[r] -= mx; negm[r] = -mref; }
+      for (int r = 0; r < 16; ++r) { a0[r] -= mx; a1[r] -= mx; negm[r] = -mref; }
       started = true;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pf0[e] = (bf16)exp2_fast(acc[e]);
-      pf1[e] = (bf16)exp2_fast(acc[8 + e]);
     }
     const bf16x2 one = {(bf16)1.f, (bf16)1.f};
     float ls = lrun;
 #pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pf[0][e] = (bf16)exp2_fast(a0[e]);
+      pf[1][e] = (bf16)exp2_fast(a0[8 + e]);
+    }
+#pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf0[e], pf0[e + 1]}, one, ls, false);
-      ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf1[e], pf1[e + 1]}, one, ls, false);
+      ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[0][e], pf[0][e + 1]}, one, ls, false);
+      ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[1][e], pf[1][e + 1]}, one, ls, false);
+    }
+    if (two) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf[2][e] = (bf16)exp2_fast(a1[e]);
+        pf[3][e] = (bf16)exp2_fast(a1[8 + e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[2][e], pf[2][e + 1]}, one, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[3][e], pf[3][e + 1]}, one, ls, false);
+      }
     }
     lrun = ls;
   };
@@ -1800,61 +1818,62 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_dma_kernel(Dims m, Dev d, Src
       }
     }
   };
+  // masks keys at offsets >= lim of a 32-key subtile (this lane's rows 8(r/4) + 4h + r%4)
+  auto mask = [&](f32x16& acc, int lim) {
+    if (lim < 32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
+    }
+  };
   auto compute = [&](int T, const uint8_t* K, const uint8_t* V) {
+    f32x16 a0, a1;
+    bool two;
     if (T < n_st) {
       const int r0 = T << 6;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int kb = 32 * sub;
-        if (r0 + kb >= S) break;
-        const int lim = S - r0 - kb;
+      two = r0 + 32 < S;
+      auto qk = [&](int kb, f32x16& acc) {
         const uint8_t* kr = K + (kb + jl) * 64;
-        const f16x8 a0 = *reinterpret_cast<const f16x8*>(kr + 16 * (h ^ kswz_s));
-        const f16x8 a1 = *reinterpret_cast<const f16x8*>(kr + 16 * ((2 + h) ^ kswz_s));
-        f32x16 acc;
+        const f16x8 k0v = *reinterpret_cast<const f16x8*>(kr + 16 * (h ^ kswz_s));
+        const f16x8 k1v = *reinterpret_cast<const f16x8*>(kr + 16 * ((2 + h) ^ kswz_s));
         if (!wave_qsh) {
-          acc = mfma_f16(a0, qs16[0], negm);
-          acc = mfma_f16(a1, qs16[1], acc);
+          acc = mfma_f16(k0v, qs16[0], negm);
+          acc = mfma_f16(k1v, qs16[1], acc);
         } else {
-          acc = mfma_f16(a0, qs16[0], f32x16{});
-          acc = mfma_f16(a1, qs16[1], acc);
+          acc = mfma_f16(k0v, qs16[0], f32x16{});
+          acc = mfma_f16(k1v, qs16[1], acc);
           const float sc = ldexpf(1.f, qsh);
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] = acc[r] * sc - mref;
         }
-        if (lim < 32) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
-        }
-        bf16x8 pf0, pf1;
-        softmax(acc, pf0, pf1);
-        pv_acc(V, kb, pf0, pf1);
+      };
+      qk(0, a0);
+      mask(a0, S - r0);
+      if (two) {
+        qk(32, a1);
+        mask(a1, S - r0 - 32);
       }
     } else {
       const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int kb = 32 * sub;
-        const int64_t ks = k0 + kb;
-        if (ks >= hi || ks > qlast) break;
+      if (k0 > qlast) return;   // every key of the tile is after this wave's queries
+      two = k0 + 32 < hi && k0 + 32 <= qlast;
+      auto qk = [&](int kb, f32x16& acc) {
         const uint8_t* kr = K + (kb + jl) * 128;
-        f32x16 acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * (h ^ kswz_w)), qf[0], negm);
+        acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * (h ^ kswz_w)), qf[0], negm);
 #pragma unroll
         for (int kk = 1; kk < 4; ++kk)
           acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * kk + h) ^ kswz_w)), qf[kk], acc);
-        if (ks + 31 >= hi || ks + 31 > qfirst) {
-          // key ks + off is valid for this lane's query iff off < lim
-          const int lim = (int)min(hi - ks, qpos - ks + 1);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (8 * (r >> 2) + 4 * h + (r & 3) >= lim) acc[r] = -kInf;
-        }
-        bf16x8 pf0, pf1;
-        softmax(acc, pf0, pf1);
-        pv_acc(V, kb, pf0, pf1);
-      }
+        const int64_t ks = k0 + kb;
+        // key ks + off is valid for this lane's query iff off < lim
+        if (ks + 31 >= hi || ks + 31 > qfirst) mask(acc, (int)min(hi - ks, qpos - ks + 1));
+      };
+      qk(0, a0);
+      if (two) qk(32, a1);
     }
+    bf16x8 pf[4];
+    softmax(a0, a1, two, pf);
+    pv_acc(V, 0, pf[0], pf[1]);
+    if (two) pv_acc(V, 32, pf[2], pf[3]);
   };
 
   // ---- two-stage pipeline; each barrier also waits for the wave's own transfers
