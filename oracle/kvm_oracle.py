@@ -48,7 +48,12 @@ KIND_MERGE = 2
 
 @dataclass(frozen=True)
 class Params:
-    """Layer constants.  sched: 'fixed' | 'sqrt' | 'saturating'."""
+    """Layer constants.  sched: 'fixed' | 'sqrt' | 'saturating' | 'power'.
+
+    The last four fields select the variants of [KVM summary, Experimental
+    results] (power-law schedules) and of its ablation study (value-length
+    normalisation, sink protection and the merge gate, each removable).
+    """
 
     chunk: int
     window: int
@@ -60,18 +65,33 @@ class Params:
     rope_dims: int = 32
     rope_theta: float = 10000.0
     ln_eps: float = 1e-5
+    exponent: float = 0.5          # 'power' schedule: capacity ceil(alpha * T**exponent)
+    value_norm: bool = True        # read values at the row's radius (else the plain mean V/n)
+    sink_protect: bool = True      # sink rows are never merge targets nor surprise references
+    merge_gate: bool = True        # merged tokens are scaled by sigmoid(l) (else by 1)
 
     @staticmethod
     def of(cfg) -> "Params":
         """Build from any object with the same attribute names (e.g. a workload config)."""
         return Params(chunk=cfg.chunk, window=cfg.window, n_sinks=cfg.n_sinks, sched=cfg.sched,
                       max_slots=cfg.max_slots, alpha=cfg.alpha, head_dim=cfg.head_dim,
-                      rope_dims=cfg.rope_dims, rope_theta=cfg.rope_theta, ln_eps=cfg.ln_eps)
+                      rope_dims=cfg.rope_dims, rope_theta=cfg.rope_theta, ln_eps=cfg.ln_eps,
+                      exponent=getattr(cfg, "exponent", 0.5), value_norm=getattr(cfg, "value_norm", True),
+                      sink_protect=getattr(cfg, "sink_protect", True),
+                      merge_gate=getattr(cfg, "merge_gate", True))
 
 
 # --------------------------------------------------------------------------
 # Elementary pieces
 # --------------------------------------------------------------------------
+
+def merge_weights(ell, p: Params):
+    """The per-token merge weight: the gate, or 1 without it ([KVM summary,
+    Experimental results, ablations]: the merge gate can be removed)."""
+    if p.merge_gate:
+        return gate(ell)
+    return np.ones_like(np.asarray(ell, dtype=np.float64))
+
 
 def gate(ell):
     """Merge gate g = sigmoid(l).
@@ -121,10 +141,14 @@ def capacity(T: int, p: Params) -> int:
     and saturating schedules.
     (reading) fixed: max_slots; sqrt: ceil(alpha*sqrt(T)); saturating:
     min(max_slots, ceil(alpha*sqrt(T))).  ceil(alpha*sqrt(T)) is taken as the
-    exact integer ceiling of sqrt(alpha^2 * T) (alpha an integer).
+    exact integer ceiling of sqrt(alpha^2 * T) (alpha an integer).  power:
+    ceil(alpha * T**exponent) in IEEE double (the power-law family the sqrt
+    variant belongs to; the exact integer form above is kept for sqrt).
     """
     if p.sched == "fixed":
         return p.max_slots
+    if p.sched == "power":
+        return int(math.ceil(float(p.alpha) * float(T) ** float(p.exponent)))
     c = _ceil_sqrt_int(p.alpha * p.alpha * int(T))
     if p.sched == "sqrt":
         return c
@@ -257,6 +281,12 @@ def absorb_chunk(st: State, j: int, ktil, v, g, p: Params, forced: Optional[dict
     """
     C = p.chunk
     P = list(range(j * C, (j + 1) * C))
+    first_row = st.rows
+    # rows that take part as references and merge targets: all of them, except
+    # protected sinks ([KVM summary, Experimental results, ablations]: removing
+    # sink protection makes the sink rows ordinary rows)
+    def eligible(i):
+        return not (st.sink[i] and p.sink_protect)
 
     # (a) sinks [KVM summary, Core mechanisms 5]: (reading) the earliest tokens
     # of the sequence become protected rows, created unscaled, never merge targets.
@@ -272,7 +302,7 @@ def absorb_chunk(st: State, j: int, ktil, v, g, p: Params, forced: Optional[dict
 
     # (c) surprise: the best cosine against the non-sink rows that existed
     # before this chunk (reading: -inf when there are none).
-    E = [i for i in range(st.rows) if not st.sink[i]]
+    E = [i for i in range(first_row) if eligible(i)]
     mu = {}
     if E and P:
         KE = np.array([st.K[i] for i in E])
@@ -298,10 +328,9 @@ def absorb_chunk(st: State, j: int, ktil, v, g, p: Params, forced: Optional[dict
             raise ValueError(f"chunk {j}: forced append count {len(A)} != schedule {m}")
     else:
         A = A_own
-    first_new = st.rows
     for t in A:
         st.add_row(ktil[t], v[t], sink=False)
-    cand = E + list(range(first_new, st.rows))
+    cand = E + [i for i in range(first_row, st.rows) if eligible(i)]
 
     # (e) winner-take-all assignment [KVM summary, Core mechanisms 2]: each
     # remaining token goes to the single candidate row of highest cosine,
@@ -355,7 +384,9 @@ def read_form(st: State, p: Params):
     [KVM lay summary]: division by the count happens only now.
     (reading) LayerNorm over the live dims of K_i / n_i, biased variance,
     eps = ln_eps, no affine parameters; the rotary dims of the key are zero.
-    v_hat = rho_i * V_i / |V_i| (0 if |V_i| = 0).
+    v_hat = rho_i * V_i / |V_i| (0 if |V_i| = 0).  Without value-length
+    normalisation ([KVM summary, Experimental results, ablations]) the value
+    is read as the plain mean V_i / n_i.
     Returns k_hat [S, head_dim], v_hat [S, head_dim].
     """
     d, dr = p.head_dim, p.rope_dims
@@ -369,6 +400,8 @@ def read_form(st: State, p: Params):
     mean = x.mean(axis=1, keepdims=True)
     var = ((x - mean) ** 2).mean(axis=1, keepdims=True)
     khat[:, dr:] = (x - mean) / np.sqrt(var + p.ln_eps)
+    if not p.value_norm:
+        return khat, V / n[:, None]
     nv = np.linalg.norm(V, axis=1)
     ok = nv > 0
     vhat[ok] = rho[ok, None] * V[ok] / nv[ok, None]
@@ -459,7 +492,7 @@ def prefill(q, k, v, ell, p: Params, forced: Optional[dict] = None, keep_snapsho
     qr = rope(q, pos, dr, p.rope_theta)
     kr = rope(k, pos, dr, p.rope_theta)
     ktil = k[:, dr:]                      # the live (non-rotary) key dims
-    g = gate(ell)
+    g = merge_weights(ell, p)
     st = State(dk=d - dr, dv=v.shape[1])
     kind = np.full(N, KIND_NONE, dtype=np.int64)
     slot = np.full(N, -1, dtype=np.int64)
@@ -551,7 +584,7 @@ class Decoder:
             assert j == self.absorbed
             K = np.array(self.k)
             V = np.array(self.v)
-            lg = absorb_chunk(self.st, j, K[:, dr:], V, gate(np.array(self.ell)), p, forced)
+            lg = absorb_chunk(self.st, j, K[:, dr:], V, merge_weights(np.array(self.ell), p), p, forced)
             self.logs.append(lg)
             self.absorbed += 1
         khat, vhat = read_form(self.st, p)
@@ -594,7 +627,11 @@ def brute_force(q, k, v, ell, p: Params) -> np.ndarray:
     summary, Core mechanisms 2: similarity metric]; then every query of the
     chunk attends over [read-form state || all N tokens] with a dense N-wide
     mask that keeps only [max(0, cC - W), t].  Shares no helper with the
-    incremental form above except `gate`, `rope` and `capacity`.
+    incremental form above except `gate`, `rope` and `capacity`.  The ablation
+    variants of Params are written out here on their own: merge weight 1
+    without the gate; unprotected sinks are ordinary rows (surprise references
+    and merge targets); without value-length normalisation a row reads its
+    mean value.
     """
     q, k, v, ell = _as64(q), _as64(k), _as64(v), _as64(ell)
     N, d = q.shape
@@ -603,7 +640,7 @@ def brute_force(q, k, v, ell, p: Params) -> np.ndarray:
     qr = rope(q, pos, dr, p.rope_theta)
     kr = rope(k, pos, dr, p.rope_theta)
     kt = k[:, dr:]
-    g = gate(ell)
+    g = gate(ell) if p.merge_gate else np.ones(N)
     scale = 1.0 / math.sqrt(d)
     out = np.zeros((N, v.shape[1]))
     for c in range(-(-N // C)):
@@ -623,7 +660,9 @@ def brute_force(q, k, v, ell, p: Params) -> np.ndarray:
             rad = np.concatenate([rad, np.linalg.norm(v[sk], axis=1)])
             is_sink = np.concatenate([is_sink, np.ones(len(sk), dtype=bool)])
             m = min(max(capacity((j + 1) * C, p) - len(Ks), 0), len(rest))
-            old = np.where(~is_sink)[0]
+            protected = is_sink if p.sink_protect else np.zeros(len(Ks), dtype=bool)
+            n_before = len(Ks) - len(sk)               # rows that existed before this chunk
+            old = np.where(~protected[:n_before])[0]
 
             def unit(X):
                 nr = np.linalg.norm(X, axis=1, keepdims=True)
@@ -642,7 +681,7 @@ def brute_force(q, k, v, ell, p: Params) -> np.ndarray:
             cnt = np.concatenate([cnt, np.ones(len(app))])
             rad = np.concatenate([rad, np.linalg.norm(v[app], axis=1)])
             is_sink = np.concatenate([is_sink, np.zeros(len(app), dtype=bool)])
-            cands = np.where(~is_sink)[0]
+            cands = np.where(~is_sink)[0] if p.sink_protect else np.arange(len(Ks))
             if len(mer):
                 sims = unit(kt[mer]) @ unit(Ks[cands]).T
                 win = cands[np.argmax(sims, axis=1)]
@@ -656,8 +695,11 @@ def brute_force(q, k, v, ell, p: Params) -> np.ndarray:
             mu = x.mean(axis=1, keepdims=True)
             sd = np.sqrt(((x - mu) ** 2).mean(axis=1, keepdims=True) + p.ln_eps)
             kh = np.hstack([np.zeros((len(Ks), dr)), (x - mu) / sd])
-            vn = np.linalg.norm(Vs, axis=1, keepdims=True)
-            vh = np.where(vn > 0, rad[:, None] * Vs / np.where(vn > 0, vn, 1.0), 0.0)
+            if p.value_norm:
+                vn = np.linalg.norm(Vs, axis=1, keepdims=True)
+                vh = np.where(vn > 0, rad[:, None] * Vs / np.where(vn > 0, vn, 1.0), 0.0)
+            else:
+                vh = Vs / cnt[:, None]
         else:
             kh = np.zeros((0, d))
             vh = np.zeros((0, v.shape[1]))

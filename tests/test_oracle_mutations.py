@@ -68,6 +68,8 @@ ALL = [
     pins.check_gate, pins.check_rope, pins.check_window_covers_all, pins.check_append_everything,
     pins.check_read_form, lambda m: pins.check_sums_and_counts(m, "random"), pins.check_assignment_rules,
     pins.check_attention_with_state, i9, i13, i11,
+    pins.check_no_gate_is_saturated_gate, pins.check_mean_read_without_value_norm, pins.check_unprotected_sinks,
+    pins.check_power_schedule,
 ]
 
 MUTANTS = {
@@ -88,8 +90,14 @@ MUTANTS = {
                                    "ranked = sorted(P, key=lambda t: (mu[t], -t))"),
     "ties to the highest row": ("best = np.argmax(cs, axis=1)",
                                 "best = cs.shape[1] - 1 - np.argmax(cs[:, ::-1], axis=1)"),
-    "sinks are merge candidates": ("E = [i for i in range(st.rows) if not st.sink[i]]", "E = list(range(st.rows))"),
-    "merge candidates exclude this chunk's new rows": ("cand = E + list(range(first_new, st.rows))", "cand = E"),
+    "sinks are merge candidates": ("return not (st.sink[i] and p.sink_protect)", "return True"),
+    "merge candidates exclude this chunk's new rows": ("cand = E + [i for i in range(first_row, st.rows) if eligible(i)]",
+                                                       "cand = E"),
+    "unprotected sinks still excluded": ("return not (st.sink[i] and p.sink_protect)", "return not st.sink[i]"),
+    "gate kept when removed": ("    if p.merge_gate:\n        return gate(ell)", "    if True:\n        return gate(ell)"),
+    "radius kept when value normalisation is removed": ("    if not p.value_norm:\n        return khat, V / n[:, None]",
+                                                        "    if False:\n        return khat, V / n[:, None]"),
+    "power exponent ignored": ("float(T) ** float(p.exponent)", "float(T) ** 0.5"),
     "window one token short": ("lo = max(0, c * C - p.window)\n    keys", "lo = max(0, c * C - p.window + 1)\n    keys"),
     "absorb one chunk late": ("while absorbed <= c - W // C - 1:", "while absorbed <= c - W // C - 2:"),
     "softmax scale squared": ("s = 1.0 / math.sqrt(p.head_dim)\n    C = p.chunk", "s = 1.0 / p.head_dim\n    C = p.chunk"),

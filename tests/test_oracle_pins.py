@@ -348,6 +348,11 @@ CASES = [
     dict(chunk=8, window=8, n_sinks=1, sched="fixed", max_slots=6),
     dict(chunk=4, window=12, n_sinks=0, sched="saturating", alpha=3, max_slots=10),
     dict(chunk=16, window=32, n_sinks=16, sched="sqrt", alpha=3),
+    # ablation variants and a power-law schedule: the matrix form states each on its own
+    dict(chunk=8, window=16, n_sinks=2, sched="sqrt", alpha=2, merge_gate=False),
+    dict(chunk=8, window=16, n_sinks=2, sched="sqrt", alpha=2, value_norm=False),
+    dict(chunk=8, window=16, n_sinks=3, sched="sqrt", alpha=2, sink_protect=False),
+    dict(chunk=8, window=16, n_sinks=2, sched="power", alpha=2, exponent=0.6),
 ]
 
 
@@ -406,3 +411,104 @@ def test_generator_is_seeded_and_rounded():
     assert torch.equal(a.k[1], b.k[0])
     kn = a.k[0].float().numpy()
     assert 0.9 < np.median(np.linalg.norm(kn, axis=1)) < 1.15
+
+
+# ------------------------------------------------------------------ ablation variants and power-law schedules
+
+def check_no_gate_is_saturated_gate(mod):
+    """Removing the merge gate = a gate of exactly 1: sigmoid(60) rounds to 1.0 in fp64."""
+    assert expit(60.0) == 1.0
+    p = mod.Params(chunk=8, window=16, n_sinks=2, sched="sqrt", alpha=2)
+    q, k, v, ell = rand_seq(200, 31, clustered=5)
+    a = mod.prefill(q, k, v, ell, mod.Params(**{**p.__dict__, "merge_gate": False}))
+    b = mod.prefill(q, k, v, np.full(len(ell), 60.0), p)
+    c = mod.prefill(q, k, v, ell, p)
+    np.testing.assert_array_equal(a.out, b.out)
+    np.testing.assert_array_equal(a.slot, b.slot)
+    assert np.max(np.abs(a.out - c.out)) > 1e-3      # the gate matters on this input
+
+
+def test_no_merge_gate_is_a_gate_of_one():
+    check_no_gate_is_saturated_gate(O)
+
+
+def check_mean_read_without_value_norm(mod):
+    """Without value-length normalisation a row reads the mean of what it absorbed:
+    rebuilt here from the per-position log (creator + gated merged tokens) / count."""
+    N, C = 300, 8
+    p = mod.Params(chunk=C, window=16, n_sinks=2, sched="sqrt", alpha=2, value_norm=False)
+    q, k, v, ell = rand_seq(N, 32, clustered=5)
+    res = mod.prefill(q, k, v, ell, p, keep_snapshots=True)
+    g = expit(ell)
+    snap = res.snapshots[-1]
+    absorbed = len(res.snapshots) * C
+    _, vhat = mod.read_form(snap, p)
+    for i in range(snap.rows):
+        members = np.where((np.arange(N) < absorbed) & (res.slot == i))[0]
+        creators = [t for t in members if res.kind[t] != mod.KIND_MERGE]
+        merged = [t for t in members if res.kind[t] == mod.KIND_MERGE]
+        want = (v[creators[0]] + (g[merged, None] * v[merged]).sum(axis=0)) / len(members)
+        np.testing.assert_allclose(vhat[i], want, rtol=1e-12, atol=1e-12)
+    # and it differs from the radius read
+    _, vrad = mod.read_form(snap, mod.Params(**{**p.__dict__, "value_norm": True}))
+    assert np.max(np.abs(vrad - vhat)) > 1e-3
+
+
+def test_mean_read_without_value_length_normalisation():
+    check_mean_read_without_value_norm(O)
+
+
+def check_unprotected_sinks(mod):
+    """Without sink protection the sink rows are ordinary rows: surprise references
+    from the next chunk on and merge targets (also in the chunk that creates them).
+    Surprise, appends and assignments are re-derived with scipy over all rows."""
+    N, C, ns = 480, 16, 3
+    p = mod.Params(chunk=C, window=32, n_sinks=ns, sched="sqrt", alpha=3, sink_protect=False)
+    q, k, v, ell = rand_seq(N, 33, clustered=6)
+    res = mod.prefill(q, k, v, ell, p, keep_snapshots=True)
+    kt = k[:, 32:]
+    sched = mod.schedule(len(res.snapshots), p)
+    merged_into_sinks = 0
+    for j in range(len(res.snapshots)):
+        prev_rows = res.snapshots[j - 1].rows if j else 0
+        Kp = res.snapshots[j - 1].arrays()[0] if j else np.zeros((0, 32))
+        toks = np.arange(j * C, (j + 1) * C)
+        s_new, m, _ = sched[j]
+        sk, rest = toks[:s_new], toks[s_new:]
+        if prev_rows:
+            mu = (1.0 - cdist(kt[rest], Kp, metric="cosine")).max(axis=1)
+        else:
+            mu = np.full(len(rest), -np.inf)
+        order = np.lexsort((rest, mu))
+        app = np.sort(rest[order[:m]])
+        assert set(toks[res.kind[toks] == mod.KIND_APPEND]) == set(app)
+        cand_keys = np.vstack([Kp, kt[sk], kt[app]]) if prev_rows else np.vstack([kt[sk], kt[app]])
+        mer = toks[res.kind[toks] == mod.KIND_MERGE]
+        sims = 1.0 - cdist(kt[mer], cand_keys, metric="cosine")
+        for a, t in enumerate(mer):
+            best = np.flatnonzero(sims[a] >= sims[a].max() - 1e-12)
+            assert res.slot[t] == best[0]
+            merged_into_sinks += int(best[0] < ns)
+    assert merged_into_sinks > 0
+
+
+def test_unprotected_sinks_are_ordinary_rows():
+    check_unprotected_sinks(O)
+
+
+def check_power_schedule(mod):
+    """power: ceil(alpha * T**p) as a float formula; p = 1/2 agrees with the exact
+    integer sqrt schedule wherever alpha^2 T is not a perfect square."""
+    for alpha, ex in [(2, 0.6), (8, 0.5), (16, 0.33)]:
+        p = mod.Params(chunk=64, window=128, n_sinks=4, sched="power", alpha=alpha, exponent=ex)
+        for T in range(64, 64 * 200, 64):
+            assert mod.capacity(T, p) == math.ceil(alpha * T ** ex)
+    ps = mod.Params(chunk=64, window=128, n_sinks=4, sched="sqrt", alpha=8)
+    pp = mod.Params(chunk=64, window=128, n_sinks=4, sched="power", alpha=8, exponent=0.5)
+    for T in range(64, 64 * 500, 64):
+        if math.isqrt(64 * T) ** 2 != 64 * T:
+            assert mod.capacity(T, ps) == mod.capacity(T, pp)
+
+
+def test_power_law_schedule():
+    check_power_schedule(O)
