@@ -67,6 +67,7 @@ uint64_t ceil_sqrt_u64(uint64_t x) {
 // Rows the schedule wants (sinks included) once T tokens have been absorbed.
 int64_t capacity(const kvm_config& c, int64_t T) {
   if (c.sched == KVM_SCHED_FIXED) return c.max_slots;
+  if (c.sched == KVM_SCHED_POWER) return (int64_t)std::ceil((double)c.alpha * std::pow((double)T, c.exponent));
   const uint64_t a = (uint64_t)c.alpha;
   const int64_t s = (int64_t)ceil_sqrt_u64(a * a * (uint64_t)T);
   if (c.sched == KVM_SCHED_SQRT) return s;
@@ -115,6 +116,9 @@ kvm_status validate(const kvm_config* c) {
   if (c->n_sinks < 0 || c->n_sinks > c->chunk) return fail(KVM_E_INVALID_ARG, "n_sinks must be in [0, chunk]");
   if (c->sched == KVM_SCHED_FIXED) {
     if (c->max_slots < 1) return fail(KVM_E_INVALID_ARG, "fixed schedule needs max_slots >= 1");
+  } else if (c->sched == KVM_SCHED_POWER) {
+    if (c->alpha < 1 || c->alpha > 4096) return fail(KVM_E_INVALID_ARG, "alpha must be in [1, 4096]");
+    if (!(c->exponent > 0.0 && c->exponent <= 1.0)) return fail(KVM_E_INVALID_ARG, "exponent must be in (0, 1]");
   } else if (c->sched == KVM_SCHED_SQRT || c->sched == KVM_SCHED_SATURATING) {
     if (c->alpha < 1 || c->alpha > 4096) return fail(KVM_E_INVALID_ARG, "alpha must be in [1, 4096]");
     if (c->sched == KVM_SCHED_SATURATING && c->max_slots < 1)
@@ -129,12 +133,15 @@ kvm_status validate(const kvm_config* c) {
   if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
     return fail(KVM_E_INVALID_ARG, "softmax_scale must be >= 0");
   if (c->dtype != KVM_F32 && c->dtype != KVM_BF16) return fail(KVM_E_INVALID_ARG, "dtype must be KVM_F32 or KVM_BF16");
-  if (c->flags & ~KVM_FLAG_TRACE) return fail(KVM_E_INVALID_ARG, "unknown flag bits");
+  const uint32_t known = KVM_FLAG_TRACE | KVM_FLAG_NO_VALUE_NORM | KVM_FLAG_NO_SINK_PROTECT | KVM_FLAG_NO_MERGE_GATE;
+  if (c->flags & ~known) return fail(KVM_E_INVALID_ARG, "unknown flag bits");
   // Every merged token needs a candidate row: the first chunk with non-sink
-  // tokens must be allowed to append at least one row.
+  // tokens must be allowed to append at least one row (unprotected sinks are
+  // candidates themselves).
   const int64_t J = max_absorbable_chunks(*c);
   const int64_t jfirst = c->n_sinks == c->chunk ? 1 : 0;
-  if (J > jfirst && capacity(*c, (jfirst + 1) * (int64_t)c->chunk) <= c->n_sinks)
+  const bool sinks_take_merges = (c->flags & KVM_FLAG_NO_SINK_PROTECT) && c->n_sinks > 0;
+  if (!sinks_take_merges && J > jfirst && capacity(*c, (jfirst + 1) * (int64_t)c->chunk) <= c->n_sinks)
     return fail(KVM_E_INVALID_ARG, "schedule leaves no non-sink row for the first merged tokens (capacity <= n_sinks)");
   return KVM_OK;
 }
@@ -183,6 +190,9 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   m.ln_eps = c->ln_eps;
   m.bf16 = c->dtype == KVM_BF16;
   m.trace = (c->flags & KVM_FLAG_TRACE) ? 1 : 0;
+  m.no_vnorm = (c->flags & KVM_FLAG_NO_VALUE_NORM) ? 1 : 0;
+  m.unprot = (c->flags & KVM_FLAG_NO_SINK_PROTECT) ? 1 : 0;
+  m.no_gate = (c->flags & KVM_FLAG_NO_MERGE_GATE) ? 1 : 0;
   const size_t es = m.bf16 ? 2 : 4;
   const size_t BH = (size_t)m.BH, S = (size_t)S_cap;
   size_t off = 0;

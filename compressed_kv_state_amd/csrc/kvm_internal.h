@@ -28,6 +28,9 @@ struct Dims {
   float ln_eps;
   int bf16;           // 1: bf16 storage and MFMA; 0: fp32
   int trace;          // 1: record per-token assignment
+  int no_vnorm;       // 1: read values as the mean V/n (ablation)
+  int unprot;         // 1: sink rows are ordinary rows (ablation)
+  int no_gate;        // 1: merge weight 1 (ablation)
 };
 
 // Device regions carved from the caller's workspace.  Per-sequence arrays are

@@ -521,13 +521,14 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
 #pragma unroll
       for (int i = 0; i < 32; ++i) { const float x = tof(Kc[t][i]); n2 = fmaf(x, x, n2); }
       sm.kn[t] = sqrtf(n2);
-      // merge gate = logistic sigmoid of the logit
-      sm.g[t] = 1.0f / (1.0f + expf(-sm.l[cur][t]));
+      // merge gate = logistic sigmoid of the logit (1 when the gate is removed)
+      sm.g[t] = m.no_gate ? 1.0f : 1.0f / (1.0f + expf(-sm.l[cur][t]));
     }
     lds_barrier();
 
     // ---- 2. surprise against the non-sink rows that existed before the chunk
-    const int eb = m.ns, ee = R0;
+    // (every row before the chunk when sinks are unprotected)
+    const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
     cos_best<T, C>(sm, cur, unit, eb, ee, sm.bE, sm.rE);
     for (int t = tid; t < C; t += kScanThreads) {
       float mu;
@@ -566,23 +567,26 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     lds_barrier();
 
     // ---- 4. best against the new rows (their key sums are the creating tokens'
-    // live keys, in LDS: dot(k_t, k_s) / |k_s|), then the winner-take-all assignment
+    // live keys, in LDS: dot(k_t, k_s) / |k_s|), then the winner-take-all assignment.
+    // New row R0 + e was created by token e (a sink, e < sinks) or by the
+    // (e - sinks)-th appended token; sink rows are candidates only unprotected.
+    const int e0 = m.unprot ? 0 : sinks;
     for (int t = tid >> 2; t < C; t += kScanThreads / 4) {
       const int sub = tid & 3;
       float best = -kInf;
       int brow = INT_MAX;
-      if (sm.flag[t] == kMerge && mj > 0) {
+      if (sm.flag[t] == kMerge && nc > e0) {
         float kt[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
-        for (int e = sub; e < mj; e += 4) {
-          const int s2 = sm.app_list[e];
+        for (int e = e0 + sub; e < nc; e += 4) {
+          const int s2 = e < sinks ? e : sm.app_list[e - sinks];
           float dot = 0.f;
 #pragma unroll
           for (int i = 0; i < 32; ++i) dot = fmaf(kt[i], tof(Kc[s2][i]), dot);
           const float nk = sm.kn[s2];
           const float val = nk > 0.f ? dot / nk : 0.f;
-          if (val > best) { best = val; brow = R0 + sinks + e; }
+          if (val > best) { best = val; brow = R0 + e; }
         }
       }
 #pragma unroll
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         sm.seg_len[k2] = (k2 + 1 < nseg ? sm.seg_start[k2 + 1] : nm) - sm.seg_start[k2];
         const int rk = sm.seg_row[k2];
         if (rk < R0 && (k2 + 1 == nseg || sm.seg_row[k2 + 1] >= R0)) sm.nold = k2 + 1;
-        if (rk >= R0 + sinks && rk < rows_after) sm.created_seg[rk - R0] = k2;
+        if (rk >= R0 && rk < rows_after) sm.created_seg[rk - R0] = k2;
       }
     }
     lds_barrier();
@@ -805,7 +809,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       var += __shfl_xor(var, 2);
       var *= (1.0f / 32.0f);
       const float rs = 1.0f / sqrtf(var + m.ln_eps);
-      const float vsc = v2 > 0.f ? rh / sqrtf(v2) : 0.f;
+      // the value at the row's radius, or (ablation) the plain mean
+      const float vsc = m.no_vnorm ? invn : (v2 > 0.f ? rh / sqrtf(v2) : 0.f);
       const int ver = nver + u;
       alignas(16) RT kh[8];
       alignas(16) T vh[16];

@@ -23,7 +23,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvm.so")
 
 KVM_OK, KVM_E_INVALID_ARG, KVM_E_WORKSPACE, KVM_E_CAPACITY, KVM_E_STATE, KVM_E_HIP = range(6)
 KVM_FLAG_TRACE = 1
-SCHED = {"fixed": 0, "sqrt": 1, "saturating": 2}
+KVM_FLAG_NO_VALUE_NORM = 2
+KVM_FLAG_NO_SINK_PROTECT = 4
+KVM_FLAG_NO_MERGE_GATE = 8
+SCHED = {"fixed": 0, "sqrt": 1, "saturating": 2, "power": 3}
 DTYPE = {"f32": 0, "bf16": 1}
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _READ_DTYPE = {"f32": torch.float32, "bf16": torch.float16}   # read-form storage type
@@ -42,7 +45,7 @@ class _Config(ctypes.Structure):
         ("n_sinks", ctypes.c_int32), ("sched", ctypes.c_int32), ("max_slots", ctypes.c_int32),
         ("alpha", ctypes.c_int32), ("max_tokens", ctypes.c_int64), ("rope_theta", ctypes.c_float),
         ("ln_eps", ctypes.c_float), ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("flags", ctypes.c_uint32),
+        ("flags", ctypes.c_uint32), ("exponent", ctypes.c_double),
     ]
 
 
@@ -114,7 +117,8 @@ def _check(status: int):
 
 @dataclass
 class KvmConfig:
-    """Mirror of kvm_config.  sched: 'fixed' | 'sqrt' | 'saturating'; dtype: 'f32' | 'bf16'."""
+    """Mirror of kvm_config.  sched: 'fixed' | 'sqrt' | 'saturating' | 'power'; dtype: 'f32' | 'bf16'.
+    value_norm / sink_protect / merge_gate False select the ablation variants (flag bits)."""
 
     batch: int
     heads: int
@@ -132,6 +136,10 @@ class KvmConfig:
     ln_eps: float = 1e-5
     softmax_scale: float = 0.0
     trace: bool = False
+    exponent: float = 0.5
+    value_norm: bool = True
+    sink_protect: bool = True
+    merge_gate: bool = True
 
     @property
     def seqs(self) -> int:
@@ -159,10 +167,13 @@ class KvmConfig:
             raise ValueError(f"unknown schedule {self.sched!r}")
         if self.dtype not in DTYPE:
             raise ValueError(f"unknown dtype {self.dtype!r}")
+        flags = ((KVM_FLAG_TRACE if self.trace else 0) | (0 if self.value_norm else KVM_FLAG_NO_VALUE_NORM)
+                 | (0 if self.sink_protect else KVM_FLAG_NO_SINK_PROTECT)
+                 | (0 if self.merge_gate else KVM_FLAG_NO_MERGE_GATE))
         return _Config(self.batch, self.heads, self.head_dim, self.rope_dims, self.chunk, self.window,
                        self.n_sinks, SCHED[self.sched], self.max_slots, self.alpha, self.max_tokens,
-                       self.rope_theta, self.ln_eps, self.softmax_scale, DTYPE[self.dtype],
-                       KVM_FLAG_TRACE if self.trace else 0)
+                       self.rope_theta, self.ln_eps, self.softmax_scale, DTYPE[self.dtype], flags,
+                       float(self.exponent))
 
 
 def workspace_bytes(cfg: KvmConfig) -> int:

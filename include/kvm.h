@@ -55,12 +55,19 @@ typedef enum { KVM_F32 = 0, KVM_BF16 = 1 } kvm_dtype;
  * capacity(T) for T absorbed tokens, sinks included:
  *   FIXED       max_slots
  *   SQRT        ceil(alpha * sqrt(T))       (exact integer ceil-sqrt of alpha^2*T)
- *   SATURATING  min(max_slots, ceil(alpha * sqrt(T)))                     */
-typedef enum { KVM_SCHED_FIXED = 0, KVM_SCHED_SQRT = 1, KVM_SCHED_SATURATING = 2 } kvm_sched;
+ *   SATURATING  min(max_slots, ceil(alpha * sqrt(T)))
+ *   POWER       ceil(alpha * T^exponent)    (IEEE double pow; 0 < exponent <= 1) */
+typedef enum { KVM_SCHED_FIXED = 0, KVM_SCHED_SQRT = 1, KVM_SCHED_SATURATING = 2, KVM_SCHED_POWER = 3 } kvm_sched;
 
 /* Record, per absorbed token, the row it created or merged into and the kind
  * (sink / append / merge); read back with kvm_state_read. */
 #define KVM_FLAG_TRACE 1u
+
+/* Ablation variants ([KVM summary, Experimental results]: the ablation study
+ * removes value-length normalisation, sink protection and the merge gate). */
+#define KVM_FLAG_NO_VALUE_NORM 2u    /* read a row's value as its mean V/n instead of rho * V/|V| */
+#define KVM_FLAG_NO_SINK_PROTECT 4u  /* sink rows are ordinary rows: surprise references and merge targets */
+#define KVM_FLAG_NO_MERGE_GATE 8u    /* merged tokens are added with weight 1 (gate logits ignored) */
 
 typedef struct kvm_config {
   int32_t batch;          /* B >= 1 */
@@ -78,7 +85,8 @@ typedef struct kvm_config {
   float ln_eps;           /* LayerNorm epsilon for state keys (1e-5) */
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
   int32_t dtype;          /* kvm_dtype of q, k, v, out and of the stored read forms */
-  uint32_t flags;         /* KVM_FLAG_TRACE */
+  uint32_t flags;         /* KVM_FLAG_TRACE | KVM_FLAG_NO_VALUE_NORM | KVM_FLAG_NO_SINK_PROTECT | KVM_FLAG_NO_MERGE_GATE */
+  double exponent;        /* POWER: growth exponent in (0, 1]; ignored by the other schedules */
 } kvm_config;
 
 typedef struct kvm_state kvm_state;
@@ -99,7 +107,7 @@ typedef struct kvm_state_view {
   int32_t* count;         /* [B*H, S_cap] i32          tokens absorbed per row */
   float* rho;             /* [B*H, S_cap] f32          read radius fixed at row creation */
   void* key_read;         /* [B*H, S_cap, 32] ktype    read-form key, live dims (rotary dims are 0) */
-  void* val_read;         /* [B*H, S_cap, 64] dtype    read-form value rho * u, u = V / |V| */
+  void* val_read;         /* [B*H, S_cap, 64] dtype    read-form value rho * u, u = V / |V| (V/n with KVM_FLAG_NO_VALUE_NORM) */
   int32_t* trace_slot;    /* [B*H, max_tokens] i32     row created/merged into, -1 if not absorbed */
   uint8_t* trace_kind;    /* [B*H, max_tokens] u8      0 sink, 1 append, 2 merge, 255 not absorbed */
 } kvm_state_view;

@@ -34,7 +34,7 @@ class LayerConfig:
     chunk: int
     window: int
     n_sinks: int
-    sched: str                 # "fixed" | "sqrt" | "saturating"
+    sched: str                 # "fixed" | "sqrt" | "saturating" | "power"
     max_slots: int = 0         # fixed / saturating ceiling
     alpha: int = 0             # sqrt / saturating: capacity = ceil(alpha * sqrt(T))
     dtype: str = "bf16"        # "f32" | "bf16"
@@ -42,6 +42,10 @@ class LayerConfig:
     rope_dims: int = 32
     rope_theta: float = 10000.0
     ln_eps: float = 1e-5
+    exponent: float = 0.5      # power: capacity = ceil(alpha * T**exponent)
+    value_norm: bool = True    # layer variants (False = the ablation without it)
+    sink_protect: bool = True
+    merge_gate: bool = True
     # generator recipe
     key_gen: str = "normal"    # "normal" | "clustered"
     n_clusters: int = 0

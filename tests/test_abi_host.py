@@ -44,6 +44,8 @@ def base(**kw):
     dict(sched="fixed", max_slots=0), dict(sched="saturating", alpha=8, max_slots=0), dict(max_tokens=0),
     dict(rope_theta=0.0), dict(ln_eps=-1.0), dict(softmax_scale=-1.0),
     dict(sched="fixed", max_slots=4, n_sinks=4),   # no non-sink row for merged tokens
+    dict(sched="power", alpha=2, exponent=0.0), dict(sched="power", alpha=2, exponent=1.5),
+    dict(sched="power", alpha=0, exponent=0.5),
 ])
 def test_invalid_configs_are_rejected(bad):
     with pytest.raises(K.KvmError) as e:
@@ -61,7 +63,7 @@ def test_all_sinks_first_chunk_needs_room_in_second():
 def test_unknown_flags_and_dtype_rejected():
     lib = K.library()
     c = base().to_c()
-    c.flags = 6
+    c.flags = 16
     n = ctypes.c_size_t()
     assert lib.kvm_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == K.KVM_E_INVALID_ARG
     c = base().to_c()
@@ -117,3 +119,20 @@ def test_workload_workspace_sizes_fit_one_gpu():
     for w in WORKLOADS:
         cfg = K.KvmConfig.of(w, max_tokens=w.n_tokens + w.decode_steps)
         assert K.workspace_bytes(cfg) < 64 * 2**30
+
+
+@pytest.mark.parametrize("alpha,ex", [(2, 0.6), (8, 0.5), (16, 0.33), (3, 1.0)])
+def test_power_schedule_matches_oracle(alpha, ex):
+    cfg = base(sched="power", alpha=alpha, exponent=ex, max_tokens=64 * 700)
+    n = 600
+    sk, app, rows = K.schedule(cfg, n)
+    want = oracle_schedule(n, Params(chunk=64, window=128, n_sinks=4, sched="power", alpha=alpha, exponent=ex))
+    np.testing.assert_array_equal(app.numpy(), [x[1] for x in want])
+    np.testing.assert_array_equal(rows.numpy(), [x[2] for x in want])
+
+
+def test_unprotected_sinks_can_be_the_only_merge_targets():
+    # with protection a fixed state of n_sinks rows leaves merged tokens no row; unprotected sinks take them
+    with pytest.raises(K.KvmError):
+        K.workspace_bytes(base(sched="fixed", max_slots=4, n_sinks=4))
+    K.workspace_bytes(base(sched="fixed", max_slots=4, n_sinks=4, sink_protect=False))
