@@ -142,7 +142,9 @@ def bench_prefill(w, steps: int, warmup: int):
         st.prefill(q, k, v, g, out)
     torch.cuda.synchronize()
     st.profile_read()
-    st.profile(True)
+    # inside the timed region only the attention launches carry event pairs
+    # (the roofline kernel); the other phases are timed in two extra steps after it
+    st.profile(2)
     log(f"timing {steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -152,11 +154,49 @@ def bench_prefill(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     prof = st.profile_read()
-    st.profile(False)
     assert torch.isfinite(out.float()).all(), "non-finite output"
     ms_step = (t1 - t0) * 1e3 / steps
+    st.profile(True)
+    for _ in range(2):
+        st.reset()
+        st.prefill(q, k, v, g, out)
+    other = st.profile_read()
+    st.profile(False)
+    for key in ("scan", "ring", "prep"):
+        prof[key + "_ms"] = other[key + "_ms"] * steps / 2   # per timed step, like attn_ms
     prof["final_rows"] = st.info()["rows"]
-    return cfg, ms_step, prof
+    return cfg, ms_step, prof, (q, k, v, g)
+
+
+VARIANTS = {"no_value_norm": dict(value_norm=False), "no_sink_protect": dict(sink_protect=False),
+            "no_merge_gate": dict(merge_gate=False), "power_0.6_alpha3": dict(sched="power", alpha=3, exponent=0.6)}
+
+
+def bench_variants(w, tensors, steps: int):
+    """The layer variants (the pages' ablations, a power-law schedule) on the same workload and inputs:
+    time per prefill step, as for the main line (reported beside it, not in `value`)."""
+    import torch
+    from compressed_kv_state_amd import KvmConfig, KvmState
+    q, k, v, g = tensors
+    res = {}
+    for name, over in VARIANTS.items():
+        cfg = KvmConfig.of(w.replace(**over), max_tokens=w.n_tokens)
+        st = KvmState(cfg)
+        out = torch.empty_like(q)
+        st.reset()
+        st.prefill(q, k, v, g, out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.reset()
+            st.prefill(q, k, v, g, out)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        res[name] = {"ms_per_step": ms, "tokens_per_s": w.seqs * w.n_tokens / (ms * 1e-3),
+                     "final_rows": st.info()["rows"]}
+        log(f"variant {name}: {ms:.3f} ms/step")
+        del st, out
+    return res
 
 
 def bench_decode(w, steps: int):
@@ -310,6 +350,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true", help="add a 1 GiB device copy (counter scaling)")
@@ -337,7 +378,7 @@ def main():
     from kvm_inputs import WORKLOADS
     wp, wd = WORKLOADS[2], WORKLOADS[4]
 
-    cfg, ms_step, prof = bench_prefill(wp, args.steps, args.warmup)
+    cfg, ms_step, prof, tensors = bench_prefill(wp, args.steps, args.warmup)
     launches = max(prof["attn_launches"], 1)
     attn_ms = prof["attn_ms"] / launches
     flops = attn_flops(cfg, wp.n_tokens) * args.steps / launches   # mean per launch
@@ -366,8 +407,12 @@ def main():
                      "launches_per_step": launches / args.steps},
         "phases_ms_per_step": {"scan": prof["scan_ms"] / args.steps, "attn": prof["attn_ms"] / args.steps,
                                "ring": prof["ring_ms"] / args.steps, "rope_prep": prof["prep_ms"] / args.steps,
-                               "note": "scan and attention overlap on two streams; phases sum past the step"},
+                               "note": "scan and attention overlap on two streams; phases sum past the step; "
+                                       "attn from the timed steps, the others from 2 profiled steps after them"},
     }
+    if not args.no_variants:
+        res["variants"] = bench_variants(wp, tensors, 5)
+    del tensors
     if not args.no_decode:
         res["decode"] = bench_decode(wd, args.decode_steps)
     if args.copy_calibration:

@@ -18,6 +18,10 @@
 #include "kvm_internal.h"
 
 enum Phase { kScan = 0, kAttn, kRing, kDecAbsorb, kDecAttn, kPrep, kPhases };
+static_assert(KVM_PROFILE_SCAN == 1 << kScan && KVM_PROFILE_ATTN == 1 << kAttn && KVM_PROFILE_RING == 1 << kRing &&
+                  KVM_PROFILE_DEC_ABSORB == 1 << kDecAbsorb && KVM_PROFILE_DEC_ATTN == 1 << kDecAttn &&
+                  KVM_PROFILE_PREP == 1 << kPrep && KVM_PROFILE_ALL == (1 << kPhases) - 1,
+              "profile masks follow the phase order");
 
 struct kvm_state {
   kvm_config cfg;
@@ -28,7 +32,7 @@ struct kvm_state {
   int64_t absorbed = 0;
   bool poisoned = false;
   // profiling: event pairs recorded around kernel phases
-  bool profiling = false;
+  int profiling = 0;     // mask of phases (bit = 1 << Phase) that record events
   struct Rec {
     int phase;
     hipEvent_t a, b;
@@ -252,7 +256,7 @@ hipEvent_t take_event(kvm_state* st) {
 // Runs `launch` on stream hs, bracketed by an event pair when profiling.
 template <typename F>
 hipError_t timed(kvm_state* st, int phase, hipStream_t hs, F launch) {
-  if (!st->profiling) return launch();
+  if (!(st->profiling & (1 << phase))) return launch();
   hipEvent_t a = take_event(st), b = take_event(st);
   if (!a || !b) return hipErrorOutOfMemory;
   hipError_t e = hipEventRecord(a, hs);
@@ -584,9 +588,10 @@ kvm_status kvm_state_reset(kvm_state* st, void* stream) {
   return KVM_OK;
 }
 
-kvm_status kvm_profile_enable(kvm_state* st, int enable) {
+kvm_status kvm_profile_enable(kvm_state* st, int phases) {
   if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
-  st->profiling = enable != 0;
+  if (phases & ~KVM_PROFILE_ALL) return fail(KVM_E_INVALID_ARG, "unknown profile phase bits");
+  st->profiling = phases;
   return KVM_OK;
 }
 

@@ -280,9 +280,11 @@ class KvmState:
         """Back to position 0 with an empty state (queued on the current stream)."""
         _check(library().kvm_state_reset(self._h, _stream(self.device)))
 
-    def profile(self, enable: bool = True):
-        """Record HIP events around every kernel phase of later calls."""
-        _check(library().kvm_profile_enable(self._h, 1 if enable else 0))
+    def profile(self, enable=True):
+        """Record HIP events around later kernel launches: True = every phase, False = none,
+        or a mask of KVM_PROFILE_* phase bits."""
+        mask = enable if isinstance(enable, int) and not isinstance(enable, bool) else (63 if enable else 0)
+        _check(library().kvm_profile_enable(self._h, mask))
 
     def profile_read(self) -> dict:
         """Per-phase device milliseconds and launch counts since the last read (waits for the events)."""

@@ -205,9 +205,19 @@ typedef struct kvm_profile_times {
   double prep_ms;          int64_t prep_launches;          /* prefill RoPE prep of the call's keys */
 } kvm_profile_times;
 
-/* Enable (1) or disable (0) recording of a HIP event pair around every kernel
- * phase that later calls queue on their stream.  Errors: KVM_E_INVALID_ARG. */
-kvm_status kvm_profile_enable(kvm_state* st, int enable);
+/* Phases for kvm_profile_enable's mask (fields of kvm_profile_times). */
+#define KVM_PROFILE_SCAN 1
+#define KVM_PROFILE_ATTN 2
+#define KVM_PROFILE_RING 4
+#define KVM_PROFILE_DEC_ABSORB 8
+#define KVM_PROFILE_DEC_ATTN 16
+#define KVM_PROFILE_PREP 32
+#define KVM_PROFILE_ALL 63
+
+/* Record a HIP event pair, on the stream the launch uses, around every later
+ * kernel launch of the phases in `phases` (a KVM_PROFILE_* mask; 0 stops
+ * recording).  Errors: KVM_E_INVALID_ARG (NULL state, bits outside ALL). */
+kvm_status kvm_profile_enable(kvm_state* st, int phases);
 
 /* Wait for the recorded events (this one call synchronises the host with
  * them), add up the elapsed times per phase into *out, and clear the record.

@@ -136,3 +136,13 @@ def test_unprotected_sinks_can_be_the_only_merge_targets():
     with pytest.raises(K.KvmError):
         K.workspace_bytes(base(sched="fixed", max_slots=4, n_sinks=4))
     K.workspace_bytes(base(sched="fixed", max_slots=4, n_sinks=4, sink_protect=False))
+
+
+def test_profile_mask_bits_are_checked():
+    lib = K.library()
+    assert lib.kvm_profile_enable(None, 1) == K.KVM_E_INVALID_ARG
+    # every defined phase bit is named in the header and the mask covers exactly them
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "kvm.h")).read()
+    bits = [int(v) for v in re.findall(r"#define KVM_PROFILE_(?!ALL)\w+ (\d+)", hdr)]
+    assert sorted(bits) == [1, 2, 4, 8, 16, 32]
+    assert int(re.search(r"#define KVM_PROFILE_ALL (\d+)", hdr).group(1)) == sum(bits)

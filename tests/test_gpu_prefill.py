@@ -262,3 +262,20 @@ def test_error_paths_leave_state_usable():
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     assert st.info()["position"] == 130 and st.info()["poisoned"] == 0
+
+
+def test_profile_mask_records_selected_phases():
+    w = small("bf16", chunk=128, window=256, n_tokens=2000, heads=2)
+    print("case: profile mask", flush=True)
+    inp = make_inputs(w)
+    cfg = KvmConfig.of(w, max_tokens=2000)
+    cfg.batch, cfg.heads = 2, 1
+    st = KvmState(cfg)
+    q, k, v, g = to_gpu(inp)
+    st.profile(2)                       # attention launches only
+    st.prefill(q, k, v, g)
+    p = st.profile_read()
+    assert p["attn_launches"] >= 1 and p["attn_ms"] > 0
+    assert p["scan_launches"] == 0 and p["ring_launches"] == 0 and p["prep_launches"] == 0
+    with pytest.raises(KvmError):
+        st.profile(64)
