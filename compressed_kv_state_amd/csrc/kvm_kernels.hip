@@ -18,6 +18,7 @@
 // free; the kernels pick the one that makes each lane's loads contiguous.
 #include <hip/hip_runtime.h>
 #include <limits.h>
+#include <type_traits>
 #include <math.h>
 
 #include "kvm_internal.h"
@@ -32,6 +33,8 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kInf = __builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -79,12 +82,17 @@ __device__ __forceinline__ void copy16(void* dst, const void* src) {
 }
 __device__ __forceinline__ void zero16(void* dst) { *reinterpret_cast<uint4*>(dst) = make_uint4(0, 0, 0, 0); }
 
-// Barrier that orders LDS only: outstanding global loads stay in flight (a
-// full __syncthreads also waits for every outstanding global access).
+// Barrier that orders LDS only: each wave waits for its own LDS accesses
+// (lgkmcnt(0); vmcnt and expcnt left at their maxima) and meets the others.
+// Outstanding global loads and global->LDS transfers stay in flight.  (A
+// release fence on LDS would make the compiler wait for every transfer in
+// flight into any LDS variable; the empty asm statements keep the compiler
+// from moving memory accesses across the barrier instead.)
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
 
 // Barrier that publishes data brought in by global->LDS transfers.  Such a
@@ -132,8 +140,8 @@ __global__ void rope_table_kernel(float* cosv, float* sinv, int64_t max_tokens, 
 //   appended as new rows; the count m_j comes from the size schedule.
 // [KVM summary, Core mechanisms 5]: the first tokens become protected sinks.
 // One workgroup (8 waves) per sequence, sequential over chunks.  Per chunk:
-//   1. the chunk's live keys, values and gates go to LDS (loaded from HBM one
-//      chunk ahead, into registers, while the previous chunk is processed);
+//   1. the chunk's live keys, values and gates are in LDS (loaded into
+//      registers during the previous step, stored at its end);
 //   2. surprise: best cosine of every token against the non-sink rows that
 //      existed before the chunk (MFMA over row tiles, next tile prefetched);
 //   3. append the m_j tokens of smallest (surprise, position) (parallel rank);
@@ -166,8 +174,8 @@ struct ScanGeom {
 constexpr int pow2_floor(int x) { return x >= 2 ? 2 * pow2_floor(x / 2) : 1; }
 constexpr int kSink = 0, kAppend = 1, kMerge = 2;
 
-// Chunk buffers: NBUF = 2 lets the next chunk stream into LDS (direct
-// global->LDS loads) while the current one is processed.
+// Chunk buffers: with NBUF = 2 the next chunk is stored into the spare buffer
+// at the end of a step; with one buffer it is stored at the top of its own step.
 template <typename T, int C>
 struct ScanBuf {
   static constexpr int NBUF = sizeof(T) * C <= 512 ? 2 : 1;
@@ -176,14 +184,15 @@ struct ScanBuf {
 constexpr int kVerCap = 4096;   // rows whose current version ids the scan keeps in LDS
 
 template <typename T, int C>
+struct ScanChunk {
+  alignas(16) T k[C][32];   // live key dims of the chunk's tokens
+  alignas(16) T v[C][64];   // values
+  float l[C];               // gate logits
+};
+
+template <typename T, int C>
 struct ScanSmem {
-  static constexpr int NBUF = ScanBuf<T, C>::NBUF;
-  // the touched rows' raw sums are prefetched into LDS where it fits
-  static constexpr bool PREF = sizeof(T) == 2 ? C <= 128 : C <= 64;
-  static constexpr int PC = PREF ? C : 1;
-  alignas(16) T k[NBUF][C][32];   // live key dims of the chunk's tokens
-  alignas(16) T v[NBUF][C][64];   // values
-  alignas(16) float l[NBUF][C];   // gate logits
+  ScanChunk<T, C> ch[ScanBuf<T, C>::NBUF];
   float g[C];         // gate
   float kn[C];        // |k live|
   alignas(16) uint64_t key[C];    // sort keys
@@ -202,81 +211,93 @@ struct ScanSmem {
   int seg_start[C];
   int seg_len[C];
   int created_seg[C];
+  int useg[C];        // segment a merged token heads (position order), else -1
   int wtot[ScanGeom<C>::NW];
-  alignas(16) float mk[PC][32];   // key sum of the row merged-into by token t (prefetch)
-  alignas(16) float mv[PC][64];   // value sum of that row
-  int mc[PC];                     // its count
-  float mr[PC];                   // its radius
   int ver_cur[kVerCap];           // current version id of every row
   int nold;
   int nseg;
 };
 
-// Queue direct global->LDS loads of chunk P0's live keys, values and gate
-// logits into buffer `buf`.  Each wave instruction moves 64 x 16 bytes (4
-// bytes for the logits) into consecutive LDS; the loads complete in the
-// background (vmcnt); dma_barrier() waits for them.
+// A chunk's live keys, values and gate logits in registers, between loads
+// issued one chunk step ahead and the stores into an LDS buffer: thread tid
+// holds the 16-byte pieces tid, tid + NT, ... of the keys and of the values
+// (piece p = token p / KP (VP), part p % KP (VP)) and token tid's logit.
 template <typename T, int C>
-__device__ __forceinline__ void chunk_load_lds(ScanSmem<T, C>& sm, int buf, const Dims& m, const Src& src, int s,
-                                               int64_t P0, const T* ring_k, const T* ring_v, const float* ring_l) {
-  constexpr int EL = 16 / sizeof(T);
-  constexpr int KP = 32 / EL, VP = 64 / EL;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+struct ChunkRegs {
+  static constexpr int EL = 16 / sizeof(T);
+  static constexpr int KP = 32 / EL, VP = 64 / EL;
+  static constexpr int NT = ScanGeom<C>::NT;
+  static constexpr int NK = (C * KP + NT - 1) / NT, NV = (C * VP + NT - 1) / NT;
+  u32x4 k[NK], v[NV];
+  float l;
+};
+
+template <typename T, int C>
+__device__ __forceinline__ void chunk_load(ChunkRegs<T, C>& r, const Dims& m, const Src& src, int s, int64_t P0,
+                                           const T* ring_k, const T* ring_v, const float* ring_l) {
+  using R = ChunkRegs<T, C>;
+  const int tid = threadIdx.x;
   const bool from_in = P0 >= src.p0;
   auto row_of = [&](int t, bool key) -> const T* {
     const int64_t pos = P0 + t;
     if (from_in) {
-      const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
-      return (key ? reinterpret_cast<const T*>(src.k) : reinterpret_cast<const T*>(src.v)) + r * 64;
+      const size_t rr = (size_t)s * src.n_call + (size_t)(pos - src.p0);
+      return (key ? reinterpret_cast<const T*>(src.k) : reinterpret_cast<const T*>(src.v)) + rr * 64;
     }
     return (key ? ring_k : ring_v) + (size_t)(pos % m.R) * 64;
   };
-  constexpr int NT = ScanGeom<C>::NT;
-  for (int base = w * 64; base < C * KP; base += NT) {
-    const int p = base + lane, t = p / KP, q = p % KP;
-    __builtin_amdgcn_global_load_lds(row_of(t, true) + 32 + q * EL, &sm.k[buf][0][0] + base * EL, 16, 0, 0);
+  // unconditional loads (indexes past the chunk repeat its last piece; the
+  // stores skip them), so that no wait is needed until the stores
+#pragma unroll
+  for (int i = 0; i < R::NK; ++i) {
+    const int p = min(tid + i * R::NT, C * R::KP - 1);
+    r.k[i] = *reinterpret_cast<const u32x4*>(row_of(p / R::KP, true) + 32 + (p % R::KP) * R::EL);
   }
-  for (int base = w * 64; base < C * VP; base += NT) {
-    const int p = base + lane, t = p / VP, q = p % VP;
-    __builtin_amdgcn_global_load_lds(row_of(t, false) + q * EL, &sm.v[buf][0][0] + base * EL, 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < R::NV; ++i) {
+    const int p = min(tid + i * R::NT, C * R::VP - 1);
+    r.v[i] = *reinterpret_cast<const u32x4*>(row_of(p / R::VP, false) + (p % R::VP) * R::EL);
   }
-  // C = 32 fills half a wave: the other lanes stay idle (lane i of the wave
-  // writes LDS word base + i, so an active lane past C would land in the
-  // neighbouring buffer)
-  for (int base = w * 64; base < C; base += NT) {
-    const int t = base + lane;
-    if (t >= C) break;
-    const int64_t pos = P0 + t;
-    const float* lp = from_in ? src.l + (size_t)s * src.n_call + (size_t)(pos - src.p0) : ring_l + pos % m.R;
-    __builtin_amdgcn_global_load_lds(lp, &sm.l[buf][0] + base, 4, 0, 0);
-  }
+  const int64_t pos = P0 + min(tid, C - 1);
+  r.l = from_in ? src.l[(size_t)s * src.n_call + (size_t)(pos - src.p0)] : ring_l[pos % m.R];
 }
 
-// Queue direct global->LDS transfers of the row each merged token of the chunk
-// goes to (raw key and value sums, count, radius) into the token's slot of
-// sm.mk / mv / mc / mr; dma_barrier() completes them.
 template <typename T, int C>
-__device__ __forceinline__ void prefetch_rows(ScanSmem<T, C>& sm, const float* key_sum, const float* val_sum,
-                                              const int* count, const float* rho) {
-  constexpr int NW = ScanGeom<C>::NW;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int i = w; i < C / 8; i += NW) {        // key sums: 8 tokens x 128 B per transfer
-    const int t = 8 * i + (lane >> 3);
-    if (sm.flag[t] == kMerge)
-      __builtin_amdgcn_global_load_lds(key_sum + (size_t)sm.arow[t] * 32 + 4 * (lane & 7), &sm.mk[8 * i][0], 16, 0, 0);
+__device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<T, C>& dst) {
+  using R = ChunkRegs<T, C>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < R::NK; ++i) {
+    const int p = tid + i * R::NT;
+    if (p < C * R::KP) *reinterpret_cast<u32x4*>(&dst.k[0][0] + p * R::EL) = r.k[i];
   }
-  for (int i = w; i < C / 4; i += NW) {        // value sums: 4 tokens x 256 B per transfer
-    const int t = 4 * i + (lane >> 4);
-    if (sm.flag[t] == kMerge)
-      __builtin_amdgcn_global_load_lds(val_sum + (size_t)sm.arow[t] * 64 + 4 * (lane & 15), &sm.mv[4 * i][0], 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < R::NV; ++i) {
+    const int p = tid + i * R::NT;
+    if (p < C * R::VP) *reinterpret_cast<u32x4*>(&dst.v[0][0] + p * R::EL) = r.v[i];
   }
-  for (int i = w; i < (C + 63) / 64; i += NW) {  // count and radius: 64 tokens x 4 B per transfer
-    const int t = 64 * i + lane;
-    if (t < C && sm.flag[t] == kMerge) {
-      __builtin_amdgcn_global_load_lds(count + sm.arow[t], &sm.mc[64 * i], 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(rho + sm.arow[t], &sm.mr[64 * i], 4, 0, 0);
-    }
-  }
+  if (tid < C) dst.l[tid] = r.l;
+}
+
+// One lane's quarter of the row a merged token goes to: key dims [8 sub,
+// 8 sub + 8), value dims [16 sub, 16 sub + 16), count and radius.  Loaded once
+// the chunk's assignment is known, consumed by the update.
+struct RowRegs {
+  f32x4 k[2], v[4];
+  int n;
+  float rh;
+};
+
+__device__ __forceinline__ void row_load(RowRegs& r, const float* key_sum, const float* val_sum, const int* count,
+                                         const float* rho, int row, int sub) {
+  const f32x4* ks = reinterpret_cast<const f32x4*>(key_sum + (size_t)row * 32 + 8 * sub);
+  const f32x4* vs = reinterpret_cast<const f32x4*>(val_sum + (size_t)row * 64 + 16 * sub);
+  r.k[0] = ks[0];
+  r.k[1] = ks[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = vs[i];
+  r.n = count[row];
+  r.rh = rho[row];
 }
 
 // Fold one 32x32 result tile into a lane's running (best value, row): the lane
@@ -303,11 +324,39 @@ __device__ __forceinline__ void lane_best(f32x16 acc, int row0, int re, int h, f
   }
 }
 
+// bf16 path: one 32-row tile of unit directions (hi and lo halves) as the MFMA
+// A operand: lane (jl, h) holds dims [16h, 16h+16) of row rb + 32 tile + jl
+// (rows past re - 1 repeat the last row; lane_best masks them).
+struct UnitTiles {
+  bf16x8 a0[4], a1[4];
+};
+__device__ __forceinline__ void unit_tile_load(const char* unit, int rb, int re, int tile, bf16x8 (&a)[4]) {
+  const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
+  const int ri = min(rb + (tile << 5) + jl, re - 1);
+  const bf16* u = reinterpret_cast<const bf16*>(unit) + (size_t)ri * 64 + 16 * h;
+  a[0] = *reinterpret_cast<const bf16x8*>(u);
+  a[1] = *reinterpret_cast<const bf16x8*>(u + 8);
+  a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
+  a[3] = *reinterpret_cast<const bf16x8*>(u + 40);
+}
+// The first two tiles of this wave's share of rows [rb, re) for cos_best,
+// loaded ahead so that their latency overlaps the work before the pass.
+template <int C>
+__device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, UnitTiles& pre) {
+  using G = ScanGeom<C>;
+  const int wt = (threadIdx.x >> 6) / G::TS;
+  const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
+  if (wt < ntile) unit_tile_load(unit, rb, re, wt, pre.a0);
+  if (wt + G::WG < ntile) unit_tile_load(unit, rb, re, wt + G::WG, pre.a1);
+}
+
 // Best (largest) dot(k_t, U_i) over rows i in [rb, re) for every token t of the
 // chunk; ties to the lowest row.  Writes outv/outr[t] (-inf / INT_MAX if no row).
-// All threads of the block must call it.
+// All threads of the block must call it; on the bf16 path `pre` holds the
+// tiles cos_preload fetched for the same rows.
 template <typename T, int C>
-__device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, int re, float* outv, int* outr) {
+__device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, C>& ch, const char* unit, int rb,
+                                         int re, float* outv, int* outr, UnitTiles& pre) {
   using G = ScanGeom<C>;
   constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
@@ -324,20 +373,10 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
       bf16x8 bfr[CT][2];
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt) {
-        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][tok0 + 32 * tt + jl][16 * h]);
-        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&sm.k[buf][tok0 + 32 * tt + jl][16 * h + 8]);
+        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&ch.k[tok0 + 32 * tt + jl][16 * h]);
+        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&ch.k[tok0 + 32 * tt + jl][16 * h + 8]);
       }
-      const bf16* U = reinterpret_cast<const bf16*>(unit);
-      auto load = [&](int tile, bf16x8 (&a)[4]) {
-        const int ri = min(rb + (tile << 5) + jl, re - 1);
-        const bf16* u = U + (size_t)ri * 64 + 16 * h;
-        a[0] = *reinterpret_cast<const bf16x8*>(u);
-        a[1] = *reinterpret_cast<const bf16x8*>(u + 8);
-        a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
-        a[3] = *reinterpret_cast<const bf16x8*>(u + 40);
-      };
-      // two register sets in ping-pong: the loads of tile i+2W are issued right
-      // after the MFMAs of tile i read their set, so they overlap tile i+W
+      auto load = [&](int tile, bf16x8 (&a)[4]) { unit_tile_load(unit, rb, re, tile, a); };
       auto tile_best = [&](const bf16x8 (&a)[4], int tile) {
         const int row0 = rb + (tile << 5);
         f32x16 acc[CT];
@@ -358,9 +397,8 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
       // two register sets in ping-pong: the loads of tile i+2W are issued right
       // after the MFMAs of tile i read their set, so they overlap tile i+W
       constexpr int WG = G::WG;
-      bf16x8 a0[4], a1[4];
-      load(wt, a0);
-      if (wt + WG < ntile) load(wt + WG, a1);
+      bf16x8(&a0)[4] = pre.a0;
+      bf16x8(&a1)[4] = pre.a1;
       for (int tile = wt; tile < ntile; tile += 2 * WG) {
         tile_best(a0, tile);
         if (tile + 2 * WG < ntile) load(tile + 2 * WG, a0);
@@ -375,7 +413,7 @@ __device__ void cos_best(ScanSmem<T, C>& sm, int buf, const char* unit, int rb, 
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(sm.k[buf][tok0 + 32 * tt + jl][16 * h + kk]);
+        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(ch.k[tok0 + 32 * tt + jl][16 * h + kk]);
       const float* U = reinterpret_cast<const float*>(unit);
       for (int tile = wt; tile < ntile; tile += G::WG) {
         const int row0 = rb + (tile << 5);
@@ -447,11 +485,14 @@ __device__ __forceinline__ int parallel_rank(const uint64_t* key, int& t_out) {
 }
 
 template <typename T, int C>
-__global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Src src, int j_begin, int j_end) {
+__global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Src src, const int4* __restrict__ sched,
+                                                                 int j_begin, int j_end) {
   constexpr int kScanThreads = ScanGeom<C>::NT;
   constexpr int kScanWaves = ScanGeom<C>::NW;
   using RT = typename Rd<T>::type;
   constexpr int REL = 16 / sizeof(RT);     // read-form elements per 16-byte piece
+  constexpr int NBUF = ScanBuf<T, C>::NBUF;
+  constexpr int TP = (4 * C + kScanThreads - 1) / kScanThreads;   // token groups of four lanes per thread
   __shared__ ScanSmem<T, C> sm;
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -471,30 +512,35 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   const T* ring_v = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
   const float* ring_l = d.ring_l + (size_t)s * m.R;
   int nver = d.nver[s];
-  constexpr bool PREF = ScanSmem<T, C>::PREF;
   // the current version of every row lives in LDS; each chunk's index list is
   // written out from it at the start of the next step (stores only)
   const bool ver_lds = m.S_cap <= kVerCap;
   if (ver_lds && j_begin > 0 && j_begin < j_end) {
-    const int r0 = d.sched[j_begin].z;
-    const int* prev = idx + d.sched[j_begin - 1].w;
+    const int r0 = sched[j_begin].z;
+    const int* prev = idx + sched[j_begin - 1].w;
     for (int i = tid; i < r0; i += kScanThreads) sm.ver_cur[i] = prev[i];
   }
 
-  constexpr int NBUF = ScanBuf<T, C>::NBUF;
-  if (NBUF == 2 && j_begin < j_end) {
-    chunk_load_lds<T, C>(sm, 0, m, src, s, (int64_t)j_begin * C, ring_k, ring_v, ring_l);
-    dma_barrier();
+  // the chunk in flight: loaded one step ahead, stored into LDS at the end of
+  // the step before its own (two buffers) or at the top of its own step (one)
+  ChunkRegs<T, C> cr;
+  if (j_begin < j_end) {
+    chunk_load<T, C>(cr, m, src, s, (int64_t)j_begin * C, ring_k, ring_v, ring_l);
+    if constexpr (NBUF == 2) {
+      chunk_store<T, C>(cr, sm.ch[0]);
+      __syncthreads();
+    }
   }
 
   // Within a chunk step threads exchange data through LDS only (LDS barriers,
-  // so the next chunk's loads stay in flight); every global write of a step is
-  // read by another thread only in a later step, after the full barrier that
-  // closes the step.
-  int4 sc_next = j_begin < j_end ? d.sched[j_begin] : make_int4(0, 0, 0, 0);
-  int prev_off = j_begin > 0 ? d.sched[j_begin - 1].w : 0;
+  // so loads stay in flight); every global write of a step is read by another
+  // thread only in a later step, after the barrier that closes the step.
+  int4 sc_next = j_begin < j_end ? sched[j_begin] : make_int4(0, 0, 0, 0);
+  int prev_off = j_begin > 0 ? sched[j_begin - 1].w : 0;
   int last_rows = 0;
   for (int j = j_begin; j < j_end; ++j) {
+    const int cur = NBUF == 2 ? (j - j_begin) & 1 : 0;
+    ScanChunk<T, C>& chc = sm.ch[cur];
     const int4 sc = sc_next;
     const int sinks = sc.x, mj = sc.y, R0 = sc.z;
     const int64_t ioff = sc.w;
@@ -506,30 +552,35 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if (ver_lds && j > j_begin)
       for (int i = tid; i < R0; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
 
-    // ---- 1. the chunk is in LDS buffer `cur`; start streaming the next one into the other
-    const int cur = NBUF == 2 ? (j - j_begin) & 1 : 0;
-    if (NBUF == 2) {
-      if (j + 1 < j_end) chunk_load_lds<T, C>(sm, cur ^ 1, m, src, s, P0 + C, ring_k, ring_v, ring_l);
-    } else {
-      chunk_load_lds<T, C>(sm, 0, m, src, s, P0, ring_k, ring_v, ring_l);
-      dma_barrier();
+    // ---- 1. the chunk is in LDS buffer `cur` (one buffer: store it now); the
+    // first unit-direction tiles of the surprise pass start loading
+    if constexpr (NBUF == 1) {
+      chunk_store<T, C>(cr, chc);
+      lds_barrier();
     }
-    const T (*Kc)[32] = sm.k[cur];
-    const T (*Vc)[64] = sm.v[cur];
+    // surprise is measured against the non-sink rows that existed before the
+    // chunk (every row before the chunk when sinks are unprotected)
+    const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
+    UnitTiles pre;
+    if constexpr (Is<T>::bf) cos_preload<C>(unit, eb, ee, pre);
+    const T (*Kc)[32] = chc.k;
+    const T (*Vc)[64] = chc.v;
     for (int t = tid; t < C; t += kScanThreads) {
       float n2 = 0.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) { const float x = tof(Kc[t][i]); n2 = fmaf(x, x, n2); }
       sm.kn[t] = sqrtf(n2);
       // merge gate = logistic sigmoid of the logit (1 when the gate is removed)
-      sm.g[t] = m.no_gate ? 1.0f : 1.0f / (1.0f + expf(-sm.l[cur][t]));
+      sm.g[t] = m.no_gate ? 1.0f : 1.0f / (1.0f + expf(-chc.l[t]));
     }
     lds_barrier();
 
-    // ---- 2. surprise against the non-sink rows that existed before the chunk
-    // (every row before the chunk when sinks are unprotected)
-    const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
-    cos_best<T, C>(sm, cur, unit, eb, ee, sm.bE, sm.rE);
+    // ---- 2. surprise against the rows before the chunk
+    cos_best<T, C>(sm, chc, unit, eb, ee, sm.bE, sm.rE, pre);
+    // The next chunk loads from here to the end of the step (issued after the
+    // pass: loads complete in order, so a wait for the pass's tiles would also
+    // wait for these).
+    if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     for (int t = tid; t < C; t += kScanThreads) {
       float mu;
       if (ee > eb) mu = sm.kn[t] > 0.f ? sm.bE[t] / sm.kn[t] : 0.f;
@@ -615,14 +666,21 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       } else {
         sm.key[t] = ~0ull;  // non-merged tokens sort last
       }
+      sm.useg[t] = -1;
     }
     if (tid == 0) sm.nold = 0;
     for (int c2 = tid; c2 < nc; c2 += kScanThreads) sm.created_seg[c2] = -1;
     lds_barrier();
 
-    // start fetching each merged token's target row (sums, count, radius) into LDS;
-    // the update below reads them after the sort (direct global->LDS transfers)
-    if constexpr (PREF) prefetch_rows<T, C>(sm, key_sum, val_sum, count, rho);
+    // start loading each merged token's target row (sums, count, radius) into
+    // the registers of the token's lane group, which updates that row below if
+    // the token comes first on it (the row's values from the previous steps)
+    RowRegs rr[TP];
+#pragma unroll
+    for (int ps = 0; ps < TP; ++ps) {
+      const int t = (tid >> 2) + ps * (kScanThreads / 4);
+      if (t < C && sm.flag[t] == kMerge) row_load(rr[ps], key_sum, val_sum, count, rho, sm.arow[t], tid & 3);
+    }
 
     // ---- 5. sort merged tokens by (row, position); cut into per-row segments
     const int nm = C - nc;
@@ -650,6 +708,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       if (head) {
         sm.seg_row[off + within] = sm.srt_row[tid];
         sm.seg_start[off + within] = tid;
+        sm.useg[sm.srt_tok[tid]] = off + within;
       }
       if (tid == 0) sm.nseg = nseg;
     }
@@ -669,7 +728,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
 
     // schedule entry of the next step: a scalar load, issued here so that it is
     // covered by this step's closing barrier rather than stalling an LDS barrier
-    if (j + 1 < j_end) sc_next = d.sched[j + 1];
+    if (j + 1 < j_end) sc_next = sched[j + 1];
 
     // ---- 6a. the new index list: rows before the chunk that this chunk does not
     // touch keep their version (touched rows are the first nold segments, sorted)
@@ -686,25 +745,33 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       }
     }
 
-    // every wave waits for its own transfers (the next chunk's, issued at the
-    // start of the step, and the prefetched rows) before its stores of the
-    // update enter the same counter; the prefetched rows are then published
-    if constexpr (PREF) dma_barrier();
-    else wait_vmem();
-
-    // ---- 6b. update every touched or created row (four lanes per row, in increasing row order)
-    for (int u = tid >> 2; u < nu; u += kScanThreads / 4) {
-      const int sub = tid & 3;  // lane owns key dims [8 sub, 8 sub + 8) and value dims [16 sub, 16 sub + 16)
-      int row, seg, creator = -1;
-      if (u < nold) {
-        row = sm.seg_row[u];
-        seg = u;
-      } else {
-        const int c2 = u - nold;
-        row = R0 + c2;
-        seg = sm.created_seg[c2];
-        creator = c2 < sinks ? c2 : sm.app_list[c2 - sinks];
+    // ---- 6b. update every touched or created row.  Entry u of the step's row
+    // list (the nold touched rows in increasing order, then the nc new ones)
+    // gets version nver + u.  The four lanes of token t's group (lane sub owns
+    // key dims [8 sub, 8 sub + 8) and value dims [16 sub, 16 sub + 16)) update
+    // the row t comes first on (position order), or fill the row t creates.
+#pragma unroll
+    for (int ps = 0; ps < TP; ++ps) {
+      const int t = (tid >> 2) + ps * (kScanThreads / 4);
+      const int sub = tid & 3;
+      int u = -1, row = 0, seg = -1, creator = -1;
+      if (t < C) {
+        if (sm.flag[t] == kMerge) {
+          const int sg = sm.useg[t];
+          if (sg >= 0 && sg < nold) {
+            u = sg;
+            row = sm.seg_row[sg];
+            seg = sg;
+          }
+        } else {
+          const int c2 = sm.arow[t] - R0;
+          u = nold + c2;
+          row = R0 + c2;
+          seg = sm.created_seg[c2];
+          creator = t;
+        }
       }
+      if (u < 0) continue;
       alignas(16) float K[8];
       alignas(16) float V[16];
       int n;
@@ -720,24 +787,16 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         v2 += __shfl_xor(v2, 2);
         n = 1;
         rh = sqrtf(v2);
-      } else if (PREF) {
-        // prefetched by the segment's first token
-        const int t0 = sm.srt_tok[sm.seg_start[seg]];
-#pragma unroll
-        for (int i = 0; i < 8; i += 4) *reinterpret_cast<float4*>(&K[i]) = *reinterpret_cast<const float4*>(&sm.mk[t0][8 * sub + i]);
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4*>(&V[i]) = *reinterpret_cast<const float4*>(&sm.mv[t0][16 * sub + i]);
-        n = sm.mc[t0];
-        rh = sm.mr[t0];
       } else {
-        const float* ks = key_sum + (size_t)row * 32 + 8 * sub;
-        const float* vs = val_sum + (size_t)row * 64 + 16 * sub;
 #pragma unroll
-        for (int i = 0; i < 8; i += 4) *reinterpret_cast<float4*>(&K[i]) = *reinterpret_cast<const float4*>(ks + i);
+        for (int i = 0; i < 4; ++i) {
+          K[i] = rr[ps].k[0][i];
+          K[4 + i] = rr[ps].k[1][i];
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4*>(&V[i]) = *reinterpret_cast<const float4*>(vs + i);
-        n = count[row];
-        rh = rho[row];
+          for (int q = 0; q < 4; ++q) V[4 * q + i] = rr[ps].v[q][i];
+        }
+        n = rr[ps].n;
+        rh = rr[ps].rh;
       }
       if (seg >= 0) {
         const int b = sm.seg_start[seg], e = b + sm.seg_len[seg];
@@ -842,10 +901,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         tkind[P0 + t] = (uint8_t)sm.flag[t];
       }
     }
+    // the next chunk into the spare buffer (chunk j - 1's, no longer read)
+    if constexpr (NBUF == 2)
+      if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1]);
     nver += nu;
     prev_off = (int)ioff;
     last_rows = rows_after;
-    __syncthreads();  // publishes the next chunk's buffer (each wave waited above) and the step's writes
+    __syncthreads();  // publishes the next chunk's buffer and the step's writes
   }
   if (ver_lds && j_end > j_begin)
     for (int i = tid; i < last_rows; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
@@ -2168,10 +2230,10 @@ __global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, ty
 template <typename T>
 hipError_t scan_dispatch(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {
   switch (m.C) {
-    case 32: scan_kernel<T, 32><<<m.BH, ScanGeom<32>::NT, 0, st>>>(m, d, src, jb, je); break;
-    case 64: scan_kernel<T, 64><<<m.BH, ScanGeom<64>::NT, 0, st>>>(m, d, src, jb, je); break;
-    case 128: scan_kernel<T, 128><<<m.BH, ScanGeom<128>::NT, 0, st>>>(m, d, src, jb, je); break;
-    case 256: scan_kernel<T, 256><<<m.BH, ScanGeom<256>::NT, 0, st>>>(m, d, src, jb, je); break;
+    case 32: scan_kernel<T, 32><<<m.BH, ScanGeom<32>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
+    case 64: scan_kernel<T, 64><<<m.BH, ScanGeom<64>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
+    case 128: scan_kernel<T, 128><<<m.BH, ScanGeom<128>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
+    case 256: scan_kernel<T, 256><<<m.BH, ScanGeom<256>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
