@@ -300,33 +300,45 @@ __device__ __forceinline__ void row_load(RowRegs& r, const float* key_sum, const
   r.rh = rho[row];
 }
 
-// Fold one 32x32 result tile into a lane's running (best value, row): the lane
-// holds rows row0 + 8(r/4) + 4h + r%4 (increasing in r) of its token.  The tile
-// maximum is a max3 tree; the row is looked up only when it beats the running
-// best (strictly, so earlier and lower rows win ties).
-__device__ __forceinline__ void lane_best(f32x16 acc, int row0, int re, int h, float& bv, int& br) {
-  if (row0 + 32 > re) {
+// Argmax keys.  The surprise pass scales each token's live key by a power of
+// two, 2^-e with |k| = m 2^e, m in [0.5, 1) (an exact scaling that does not
+// change which row is most similar), and starts every accumulator at 2, so a
+// tile holds 2 + dot(k', U_i) in (1, 3): positive floats, ordered like their
+// bit patterns.  A value's key is its bit pattern with the 4 low mantissa bits
+// replaced by 15 - r, r the lane's slot of the row (increasing with the row):
+// one unsigned max over a lane's 16 slots gives the largest value to 2^-18
+// (the split of U into bf16 halves is good to 2^-18 as well) and, among
+// values equal at that precision, the lowest row.
+constexpr float kKeyBase = 2.0f;
+
+__device__ __forceinline__ float key_scale(float kn, int& e) {
+  (void)frexpf(kn, &e);
+  return ldexpf(1.0f, -e);
+}
+
+// Fold one 32x32 result tile into a lane's running best (truncated key bk, row
+// br): the lane holds rows row0h + 8(r/4) + r%4 of its token (row0h = first
+// row of the tile + 4h).  Tiles come in increasing row order and only a
+// strictly larger truncated key replaces the best, so ties keep the lower row.
+__device__ __forceinline__ void lane_best(const f32x16& acc, int row0h, uint32_t& bk, int& br) {
+  uint32_t k[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (row0 + 8 * (r >> 2) + 4 * h + (r & 3) >= re) acc[r] = -kInf;
-  }
-  float mx = acc[0];
+  for (int r = 0; r < 16; ++r) k[r] = (__float_as_uint(acc[r]) & ~0xFu) | (uint32_t)(15 - r);
+  uint32_t m = max(max(k[0], k[1]), k[2]);
 #pragma unroll
-  for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, acc[r]), acc[r + 1]);
-  mx = fmaxf(mx, acc[15]);
-  if (mx > bv) {
-    int rr = 15;
-#pragma unroll
-    for (int r = 15; r >= 0; --r)
-      if (acc[r] == mx) rr = r;
-    bv = mx;
-    br = row0 + 8 * (rr >> 2) + 4 * h + (rr & 3);
-  }
+  for (int r = 3; r < 15; r += 2) m = max(max(m, k[r]), k[r + 1]);
+  m = max(m, k[15]);
+  const int r = 15 - (int)(m & 15u);
+  const uint32_t mt = m & ~0xFu;
+  const bool imp = mt > bk;
+  br = imp ? row0h + r + (r & 12) : br;
+  bk = imp ? mt : bk;
 }
 
 // bf16 path: one 32-row tile of unit directions (hi and lo halves) as the MFMA
-// A operand: lane (jl, h) holds dims [16h, 16h+16) of row rb + 32 tile + jl
-// (rows past re - 1 repeat the last row; lane_best masks them).
+// A operand: lane (jl, h) holds dims [16h, 16h+16) of row rb + 32 tile + jl.
+// Rows past re - 1 repeat row re - 1: equal values at higher rows, which never
+// win a tie, so they need no mask.
 struct UnitTiles {
   bf16x8 a0[4], a1[4];
 };
@@ -351,7 +363,8 @@ __device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, Un
 }
 
 // Best (largest) dot(k_t, U_i) over rows i in [rb, re) for every token t of the
-// chunk; ties to the lowest row.  Writes outv/outr[t] (-inf / INT_MAX if no row).
+// chunk, compared on the argmax keys (to 2^-17 |k_t|); ties to the lowest row.
+// Writes outv/outr[t] (-inf / INT_MAX if no row).
 // All threads of the block must call it; on the bf16 path `pre` holds the
 // tiles cos_preload fetched for the same rows.
 template <typename T, int C>
@@ -362,29 +375,39 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
   const int tg = w % G::TS, wt = w / G::TS;   // token group, tile lane
   const int tok0 = 32 * CT * tg;              // first token of the group
-  float bv[CT];
+  uint32_t bk[CT];
   int br[CT];
 #pragma unroll
-  for (int tt = 0; tt < CT; ++tt) { bv[tt] = -kInf; br[tt] = INT_MAX; }
+  for (int tt = 0; tt < CT; ++tt) { bk[tt] = 0u; br[tt] = INT_MAX; }
   const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
   if (wt < ntile) {
+    f32x16 base;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) base[r] = kKeyBase;
+    float sc[CT];
+#pragma unroll
+    for (int tt = 0; tt < CT; ++tt) {
+      int e;
+      sc[tt] = key_scale(sm.kn[tok0 + 32 * tt + jl], e);
+    }
     if constexpr (Is<T>::bf) {
-      // lane half h owns dims [16h, 16h+16) of every 32-dim key
+      // lane half h owns dims [16h, 16h+16) of every 32-dim key (scaled, exact)
       bf16x8 bfr[CT][2];
 #pragma unroll
-      for (int tt = 0; tt < CT; ++tt) {
-        bfr[tt][0] = *reinterpret_cast<const bf16x8*>(&ch.k[tok0 + 32 * tt + jl][16 * h]);
-        bfr[tt][1] = *reinterpret_cast<const bf16x8*>(&ch.k[tok0 + 32 * tt + jl][16 * h + 8]);
-      }
+      for (int tt = 0; tt < CT; ++tt)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&ch.k[tok0 + 32 * tt + jl][16 * h + 8 * q]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bfr[tt][q][i] = (bf16)((float)x[i] * sc[tt]);
+        }
       auto load = [&](int tile, bf16x8 (&a)[4]) { unit_tile_load(unit, rb, re, tile, a); };
       auto tile_best = [&](const bf16x8 (&a)[4], int tile) {
-        const int row0 = rb + (tile << 5);
+        const int row0h = rb + (tile << 5) + 4 * h;
         f32x16 acc[CT];
-#pragma unroll
-        for (int tt = 0; tt < CT; ++tt) acc[tt] = f32x16{};
         // independent accumulators interleaved so dependent MFMAs are CT apart
 #pragma unroll
-        for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[0], bfr[tt][0], acc[tt]);
+        for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[0], bfr[tt][0], base);
 #pragma unroll
         for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[1], bfr[tt][1], acc[tt]);
 #pragma unroll
@@ -392,7 +415,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
 #pragma unroll
         for (int tt = 0; tt < CT; ++tt) acc[tt] = mfma_bf16(a[3], bfr[tt][1], acc[tt]);
 #pragma unroll
-        for (int tt = 0; tt < CT; ++tt) lane_best(acc[tt], row0, re, h, bv[tt], br[tt]);
+        for (int tt = 0; tt < CT; ++tt) lane_best(acc[tt], row0h, bk[tt], br[tt]);
       };
       // two register sets in ping-pong: the loads of tile i+2W are issued right
       // after the MFMAs of tile i read their set, so they overlap tile i+W
@@ -413,7 +436,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(ch.k[tok0 + 32 * tt + jl][16 * h + kk]);
+        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(ch.k[tok0 + 32 * tt + jl][16 * h + kk]) * sc[tt];
       const float* U = reinterpret_cast<const float*>(unit);
       for (int tile = wt; tile < ntile; tile += G::WG) {
         const int row0 = rb + (tile << 5);
@@ -424,34 +447,40 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
         for (int kk = 0; kk < 16; ++kk) a[kk] = u[kk];
 #pragma unroll
         for (int tt = 0; tt < CT; ++tt) {
-          f32x16 acc = {};
+          f32x16 acc = base;
 #pragma unroll
           for (int kk = 0; kk < 16; ++kk) acc = mfma_f32(a[kk], bfr[tt][kk], acc);
-          lane_best(acc, row0, re, h, bv[tt], br[tt]);
+          lane_best(acc, row0 + 4 * h, bk[tt], br[tt]);
         }
       }
     }
   }
-  // rows of a lane are visited in increasing order, so '>' kept the lowest row
-  // among equal values; combine the two lane halves and the waves the same way.
+  // combine the two lane halves and the waves on (truncated key, row): the
+  // larger key, or the lower row on equal keys
 #pragma unroll
   for (int tt = 0; tt < CT; ++tt) {
-    const float ov = partner_f(bv[tt]);
+    const uint32_t ok = partner_u32(bk[tt]);
     const int orow = partner_i(br[tt]);
-    if (ov > bv[tt] || (ov == bv[tt] && orow < br[tt])) { bv[tt] = ov; br[tt] = orow; }
-    if (h == 0 && wt < ntile) { sm.red_v[wt][tok0 + 32 * tt + jl] = bv[tt]; sm.red_r[wt][tok0 + 32 * tt + jl] = br[tt]; }
+    if (ok > bk[tt] || (ok == bk[tt] && orow < br[tt])) { bk[tt] = ok; br[tt] = orow; }
+    if (h == 0 && wt < ntile) {
+      sm.red_v[wt][tok0 + 32 * tt + jl] = __uint_as_float(bk[tt]);
+      sm.red_r[wt][tok0 + 32 * tt + jl] = br[tt];
+    }
   }
   lds_barrier();
   const int nw = min(ntile, G::WG);
   for (int t = tid; t < C; t += G::NT) {
-    float v = -kInf;
+    float v = 0.f;
     int r = INT_MAX;
     for (int ww = 0; ww < nw; ++ww) {
       const float ov = sm.red_v[ww][t];
       const int orow = sm.red_r[ww][t];
       if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
     }
-    outv[t] = v;
+    // back to the dot product: subtract the base (exact on (1, 3)) and undo the scaling
+    int e;
+    (void)key_scale(sm.kn[t], e);
+    outv[t] = r == INT_MAX ? -kInf : ldexpf(v - kKeyBase, e);
     outr[t] = r;
   }
   lds_barrier();
