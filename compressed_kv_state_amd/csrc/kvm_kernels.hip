@@ -67,6 +67,35 @@ __device__ __forceinline__ uint32_t partner_u32(uint32_t x) {
 __device__ __forceinline__ float partner_f(float x) { return __uint_as_float(partner_u32(__float_as_uint(x))); }
 __device__ __forceinline__ int partner_i(int x) { return (int)partner_u32((uint32_t)x); }
 
+// Value held by lane l ^ M (M < 32): DPP within groups of four lanes for M = 1
+// and 2, a swizzle (XOR mode, no memory access) otherwise.  Every lane of the
+// group of 2M lanes must be active.
+template <int M>
+__device__ __forceinline__ int xor_lane(int x) {
+  static_assert(M > 0 && M < 32, "lane mask");
+  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  else return __builtin_amdgcn_ds_swizzle(x, 0x1F | (M << 10));
+}
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) { return __int_as_float(xor_lane<M>(__float_as_int(x))); }
+// sum over the four lanes of a group
+__device__ __forceinline__ float quad_sum(float x) {
+  x += xor_lane<1>(x);
+  return x + xor_lane<2>(x);
+}
+// sum over each aligned group of P consecutive lanes (P a power of two <= 32)
+template <int P, typename V>
+__device__ __forceinline__ V group_sum(V x) {
+  static_assert(P >= 1 && P <= 32 && (P & (P - 1)) == 0, "lanes per group");
+  if constexpr (P >= 2) x += xor_lane<1>(x);
+  if constexpr (P >= 4) x += xor_lane<2>(x);
+  if constexpr (P >= 8) x += xor_lane<4>(x);
+  if constexpr (P >= 16) x += xor_lane<8>(x);
+  if constexpr (P >= 32) x += xor_lane<16>(x);
+  return x;
+}
+
 __device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -187,15 +216,14 @@ template <typename T, int C>
 struct ScanChunk {
   alignas(16) T k[C][32];   // live key dims of the chunk's tokens
   alignas(16) T v[C][64];   // values
-  float l[C];               // gate logits
+  float g[C];               // merge gates
+  float kn[C];              // |k live|
 };
 
 template <typename T, int C>
 struct ScanSmem {
   ScanChunk<T, C> ch[ScanBuf<T, C>::NBUF];
-  float g[C];         // gate
-  float kn[C];        // |k live|
-  alignas(16) uint64_t key[C];    // sort keys
+  alignas(16) uint32_t key[C];    // sort keys
   float red_v[ScanGeom<C>::NW][C];
   int red_r[ScanGeom<C>::NW][C];
   float bE[C];
@@ -237,46 +265,61 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<T, C>& r, const Dims& m, co
                                            const T* ring_k, const T* ring_v, const float* ring_l) {
   using R = ChunkRegs<T, C>;
   const int tid = threadIdx.x;
-  const bool from_in = P0 >= src.p0;
-  auto row_of = [&](int t, bool key) -> const T* {
-    const int64_t pos = P0 + t;
-    if (from_in) {
-      const size_t rr = (size_t)s * src.n_call + (size_t)(pos - src.p0);
-      return (key ? reinterpret_cast<const T*>(src.k) : reinterpret_cast<const T*>(src.v)) + rr * 64;
-    }
-    return (key ? ring_k : ring_v) + (size_t)(pos % m.R) * 64;
-  };
+  // the chunk's first token: a row of the call's input, or a ring slot (the
+  // chunk size divides the ring size, so a chunk never wraps the ring)
+  const T *kb, *vb;
+  const float* lb;
+  if (P0 >= src.p0) {
+    const size_t r0 = (size_t)s * src.n_call + (size_t)(P0 - src.p0);
+    kb = reinterpret_cast<const T*>(src.k) + r0 * 64;
+    vb = reinterpret_cast<const T*>(src.v) + r0 * 64;
+    lb = src.l + r0;
+  } else {
+    const size_t r0 = (size_t)(P0 % m.R);
+    kb = ring_k + r0 * 64;
+    vb = ring_v + r0 * 64;
+    lb = ring_l + r0;
+  }
   // unconditional loads (indexes past the chunk repeat its last piece; the
   // stores skip them), so that no wait is needed until the stores
 #pragma unroll
   for (int i = 0; i < R::NK; ++i) {
     const int p = min(tid + i * R::NT, C * R::KP - 1);
-    r.k[i] = *reinterpret_cast<const u32x4*>(row_of(p / R::KP, true) + 32 + (p % R::KP) * R::EL);
+    r.k[i] = *reinterpret_cast<const u32x4*>(kb + (p / R::KP) * 64 + 32 + (p % R::KP) * R::EL);
   }
 #pragma unroll
   for (int i = 0; i < R::NV; ++i) {
     const int p = min(tid + i * R::NT, C * R::VP - 1);
-    r.v[i] = *reinterpret_cast<const u32x4*>(row_of(p / R::VP, false) + (p % R::VP) * R::EL);
+    r.v[i] = *reinterpret_cast<const u32x4*>(vb + (p / R::VP) * 64 + (p % R::VP) * R::EL);
   }
-  const int64_t pos = P0 + min(tid, C - 1);
-  r.l = from_in ? src.l[(size_t)s * src.n_call + (size_t)(pos - src.p0)] : ring_l[pos % m.R];
+  r.l = lb[min(tid, C - 1)];
 }
 
+// Store a chunk held in registers into an LDS buffer, with each token's live
+// key norm (sum of squares over the KP lanes holding its pieces) and merge
+// gate (logistic sigmoid of the logit; 1 when the gate is removed).
+
 template <typename T, int C>
-__device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<T, C>& dst) {
+__device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<T, C>& dst, bool no_gate) {
   using R = ChunkRegs<T, C>;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < R::NK; ++i) {
     const int p = tid + i * R::NT;
     if (p < C * R::KP) *reinterpret_cast<u32x4*>(&dst.k[0][0] + p * R::EL) = r.k[i];
+    const T* x = reinterpret_cast<const T*>(&r.k[i]);
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < R::EL; ++e) n2 = fmaf(tof(x[e]), tof(x[e]), n2);
+    n2 = group_sum<R::KP>(n2);
+    if (p < C * R::KP && p % R::KP == 0) dst.kn[p / R::KP] = sqrtf(n2);
   }
 #pragma unroll
   for (int i = 0; i < R::NV; ++i) {
     const int p = tid + i * R::NT;
     if (p < C * R::VP) *reinterpret_cast<u32x4*>(&dst.v[0][0] + p * R::EL) = r.v[i];
   }
-  if (tid < C) dst.l[tid] = r.l;
+  if (tid < C) dst.g[tid] = no_gate ? 1.0f : 1.0f / (1.0f + expf(-r.l));
 }
 
 // One lane's quarter of the row a merged token goes to: key dims [8 sub,
@@ -388,7 +431,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
 #pragma unroll
     for (int tt = 0; tt < CT; ++tt) {
       int e;
-      sc[tt] = key_scale(sm.kn[tok0 + 32 * tt + jl], e);
+      sc[tt] = key_scale(ch.kn[tok0 + 32 * tt + jl], e);
     }
     if constexpr (Is<T>::bf) {
       // lane half h owns dims [16h, 16h+16) of every 32-dim key (scaled, exact)
@@ -479,7 +522,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
     }
     // back to the dot product: subtract the base (exact on (1, 3)) and undo the scaling
     int e;
-    (void)key_scale(sm.kn[t], e);
+    (void)key_scale(ch.kn[t], e);
     outv[t] = r == INT_MAX ? -kInf : ldexpf(v - kKeyBase, e);
     outr[t] = r;
   }
@@ -487,29 +530,29 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
 }
 
 // rank[t] = #{s : key[s] < key[t]} for every t < C (tokens to leave out carry
-// the largest key), using up to all threads: P = min(threads / C, C / 2) lanes
-// per token, each over C / P keys read two at a time, summed with lane shuffles.  Returns the
-// rank on the lane with part == 0 (else -1) and that lane's token in t_out.
+// the largest key), using up to all threads: P = min(threads / C, C / 4) lanes
+// per token, each over C / P keys read four at a time, summed across the P
+// lanes.  Returns the rank on the lane with part == 0 (else -1) and that
+// lane's token in t_out.
 template <int C>
-__device__ __forceinline__ int parallel_rank(const uint64_t* key, int& t_out) {
+__device__ __forceinline__ int parallel_rank(const uint32_t* key, int& t_out) {
   constexpr int NT = ScanGeom<C>::NT;
-  constexpr int P = pow2_floor(NT / C < C / 2 ? NT / C : C / 2);
+  constexpr int P = pow2_floor(NT / C < C / 4 ? NT / C : C / 4);
   constexpr int SPAN = C / P;
-  static_assert(SPAN % 2 == 0, "keys are read in pairs");
+  static_assert(SPAN % 4 == 0, "keys are read in fours");
   const int t = threadIdx.x / P, part = threadIdx.x % P;
   t_out = t;
   int cnt = 0;
   if (t < C) {
-    const uint64_t kt = key[t];
-    const ulonglong2* kp = reinterpret_cast<const ulonglong2*>(key + part * SPAN);
-#pragma unroll 8
-    for (int i = 0; i < SPAN / 2; ++i) {
-      const ulonglong2 k2 = kp[i];
-      cnt += (k2.x < kt) + (k2.y < kt);
+    const uint32_t kt = key[t];
+    const u32x4* kp = reinterpret_cast<const u32x4*>(key + part * SPAN);
+#pragma unroll
+    for (int i = 0; i < SPAN / 4; ++i) {
+      const u32x4 k4 = kp[i];
+      cnt += (k4[0] < kt) + (k4[1] < kt) + (k4[2] < kt) + (k4[3] < kt);
     }
   }
-#pragma unroll
-  for (int msk = 1; msk < P; msk <<= 1) cnt += __shfl_xor(cnt, msk);
+  cnt = group_sum<P>(cnt);
   return (t < C && part == 0) ? cnt : -1;
 }
 
@@ -556,7 +599,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   if (j_begin < j_end) {
     chunk_load<T, C>(cr, m, src, s, (int64_t)j_begin * C, ring_k, ring_v, ring_l);
     if constexpr (NBUF == 2) {
-      chunk_store<T, C>(cr, sm.ch[0]);
+      chunk_store<T, C>(cr, sm.ch[0], m.no_gate);
       __syncthreads();
     }
   }
@@ -581,10 +624,11 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if (ver_lds && j > j_begin)
       for (int i = tid; i < R0; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
 
-    // ---- 1. the chunk is in LDS buffer `cur` (one buffer: store it now); the
-    // first unit-direction tiles of the surprise pass start loading
+    // ---- 1. the chunk, its key norms and gates are in LDS buffer `cur` (one
+    // buffer: store it now); the first unit-direction tiles of the surprise
+    // pass start loading
     if constexpr (NBUF == 1) {
-      chunk_store<T, C>(cr, chc);
+      chunk_store<T, C>(cr, chc, m.no_gate);
       lds_barrier();
     }
     // surprise is measured against the non-sink rows that existed before the
@@ -594,15 +638,6 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if constexpr (Is<T>::bf) cos_preload<C>(unit, eb, ee, pre);
     const T (*Kc)[32] = chc.k;
     const T (*Vc)[64] = chc.v;
-    for (int t = tid; t < C; t += kScanThreads) {
-      float n2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) { const float x = tof(Kc[t][i]); n2 = fmaf(x, x, n2); }
-      sm.kn[t] = sqrtf(n2);
-      // merge gate = logistic sigmoid of the logit (1 when the gate is removed)
-      sm.g[t] = m.no_gate ? 1.0f : 1.0f / (1.0f + expf(-chc.l[t]));
-    }
-    lds_barrier();
 
     // ---- 2. surprise against the rows before the chunk
     cos_best<T, C>(sm, chc, unit, eb, ee, sm.bE, sm.rE, pre);
@@ -612,10 +647,12 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     for (int t = tid; t < C; t += kScanThreads) {
       float mu;
-      if (ee > eb) mu = sm.kn[t] > 0.f ? sm.bE[t] / sm.kn[t] : 0.f;
+      if (ee > eb) mu = chc.kn[t] > 0.f ? sm.bE[t] / chc.kn[t] : 0.f;
       else mu = -kInf;
-      // key = (surprise, position): smaller = more surprising; sinks never rank
-      sm.key[t] = t < sinks ? ~0ull : (((uint64_t)ordered(mu) << 32) | (uint32_t)t);
+      // key = (surprise to 2^-15, position): smaller = more surprising; sinks
+      // never rank.  (The low 8 bits of the ordered surprise give way to the
+      // position, C <= 256; surprises that close are a near tie.)
+      sm.key[t] = t < sinks ? ~0u : ((ordered(mu) & ~0xFFu) | (uint32_t)t);
     }
     lds_barrier();
 
@@ -664,15 +701,17 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           float dot = 0.f;
 #pragma unroll
           for (int i = 0; i < 32; ++i) dot = fmaf(kt[i], tof(Kc[s2][i]), dot);
-          const float nk = sm.kn[s2];
+          const float nk = chc.kn[s2];
           const float val = nk > 0.f ? dot / nk : 0.f;
           if (val > best) { best = val; brow = R0 + e; }
         }
       }
-#pragma unroll
-      for (int msk = 1; msk < 4; msk <<= 1) {
-        const float ob = __shfl_xor(best, msk);
-        const int orow = __shfl_xor(brow, msk);
+      {
+        float ob = xor_lane<1>(best);
+        int orow = xor_lane<1>(brow);
+        if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
+        ob = xor_lane<2>(best);
+        orow = xor_lane<2>(brow);
         if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
       }
       if (sub == 0) {
@@ -691,9 +730,9 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
         sm.arow[t] = a;
-        sm.key[t] = ((uint64_t)(uint32_t)a << 32) | (uint32_t)t;
+        sm.key[t] = ((uint32_t)a << 8) | (uint32_t)t;   // rows < 2^24
       } else {
-        sm.key[t] = ~0ull;  // non-merged tokens sort last
+        sm.key[t] = ~0u;  // non-merged tokens sort last
       }
       sm.useg[t] = -1;
     }
@@ -812,8 +851,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         for (int i = 0; i < 8; ++i) K[i] = tof(Kc[creator][8 * sub + i]);
 #pragma unroll
         for (int i = 0; i < 16; ++i) { V[i] = tof(Vc[creator][16 * sub + i]); v2 = fmaf(V[i], V[i], v2); }
-        v2 += __shfl_xor(v2, 1);
-        v2 += __shfl_xor(v2, 2);
+        v2 = quad_sum(v2);
         n = 1;
         rh = sqrtf(v2);
       } else {
@@ -831,7 +869,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         const int b = sm.seg_start[seg], e = b + sm.seg_len[seg];
         for (int r = b; r < e; ++r) {
           const int t = sm.srt_tok[r];
-          const float gt = sm.g[t];
+          const float gt = chc.g[t];
 #pragma unroll
           for (int i = 0; i < 8; ++i) K[i] = fmaf(gt, tof(Kc[t][8 * sub + i]), K[i]);
 #pragma unroll
@@ -857,12 +895,9 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       for (int i = 0; i < 8; ++i) { k2 = fmaf(K[i], K[i], k2); ksum += K[i]; }
 #pragma unroll
       for (int i = 0; i < 16; ++i) v2 = fmaf(V[i], V[i], v2);
-      k2 += __shfl_xor(k2, 1);
-      k2 += __shfl_xor(k2, 2);
-      ksum += __shfl_xor(ksum, 1);
-      ksum += __shfl_xor(ksum, 2);
-      v2 += __shfl_xor(v2, 1);
-      v2 += __shfl_xor(v2, 2);
+      k2 = quad_sum(k2);
+      ksum = quad_sum(ksum);
+      v2 = quad_sum(v2);
       // unit key direction for the next cosine passes
       {
         const float inv = k2 > 0.f ? 1.0f / sqrtf(k2) : 0.f;
@@ -893,8 +928,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       float var = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
-      var += __shfl_xor(var, 1);
-      var += __shfl_xor(var, 2);
+      var = quad_sum(var);
       var *= (1.0f / 32.0f);
       const float rs = 1.0f / sqrtf(var + m.ln_eps);
       // the value at the row's radius, or (ablation) the plain mean
@@ -932,7 +966,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     }
     // the next chunk into the spare buffer (chunk j - 1's, no longer read)
     if constexpr (NBUF == 2)
-      if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1]);
+      if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
     nver += nu;
     prev_off = (int)ioff;
     last_rows = rows_after;
