@@ -231,19 +231,11 @@ struct ScanSmem {
   float bA[C];
   int rA[C];
   int flag[C];
-  int arow[C];
+  int arow[C];        // row each token merges into or creates
+  alignas(16) int mrow[C];   // row of each merged token, -1 for the others
   int app_list[C];
-  int srt_tok[C];
-  int srt_row[C];
-  int seg_row[C];
-  int seg_start[C];
-  int seg_len[C];
-  int created_seg[C];
-  int useg[C];        // segment a merged token heads (position order), else -1
   int wtot[ScanGeom<C>::NW];
   int ver_cur[kVerCap];           // current version id of every row
-  int nold;
-  int nseg;
 };
 
 // A chunk's live keys, values and gate logits in registers, between loads
@@ -641,6 +633,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
 
     // ---- 2. surprise against the rows before the chunk
     cos_best<T, C>(sm, chc, unit, eb, ee, sm.bE, sm.rE, pre);
+    // With the index lists in global memory, the new list starts as a copy of
+    // the previous one; the update overwrites the rows it touches.  (Each wave
+    // waits for its copies to complete, so the overwrites come after them.)
+    if (!ver_lds && j > 0) {
+      for (int i = tid; i < R0; i += kScanThreads) idx[ioff + i] = idx[prev_off + i];
+      wait_vmem();
+    }
     // The next chunk loads from here to the end of the step (issued after the
     // pass: loads complete in order, so a wait for the pass's tiles would also
     // wait for these).
@@ -730,14 +729,11 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
         sm.arow[t] = a;
-        sm.key[t] = ((uint32_t)a << 8) | (uint32_t)t;   // rows < 2^24
+        sm.mrow[t] = a;
       } else {
-        sm.key[t] = ~0u;  // non-merged tokens sort last
+        sm.mrow[t] = -1;
       }
-      sm.useg[t] = -1;
     }
-    if (tid == 0) sm.nold = 0;
-    for (int c2 = tid; c2 < nc; c2 += kScanThreads) sm.created_seg[c2] = -1;
     lds_barrier();
 
     // start loading each merged token's target row (sums, count, radius) into
@@ -750,107 +746,74 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       if (t < C && sm.flag[t] == kMerge) row_load(rr[ps], key_sum, val_sum, count, rho, sm.arow[t], tid & 3);
     }
 
-    // ---- 5. sort merged tokens by (row, position); cut into per-row segments
-    const int nm = C - nc;
-    {
-      int t;
-      const int rank = parallel_rank<C>(sm.key, t);
-      if (rank >= 0 && rank < nm) {
-        sm.srt_tok[rank] = t;
-        sm.srt_row[rank] = sm.arow[t];
-      }
-    }
-    lds_barrier();
-    {
-      const bool head = tid < nm && (tid == 0 || sm.srt_row[tid] != sm.srt_row[tid - 1]);
-      const unsigned long long bal = __ballot(head);
-      const int within = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) sm.wtot[w] = __popcll(bal);
-      lds_barrier();
-      int off = 0, nseg = 0;
-#pragma unroll
-      for (int ww = 0; ww < kScanWaves; ++ww) {
-        off += ww < w ? sm.wtot[ww] : 0;
-        nseg += sm.wtot[ww];
-      }
-      if (head) {
-        sm.seg_row[off + within] = sm.srt_row[tid];
-        sm.seg_start[off + within] = tid;
-        sm.useg[sm.srt_tok[tid]] = off + within;
-      }
-      if (tid == 0) sm.nseg = nseg;
-    }
-    lds_barrier();
-    {
-      const int nseg = sm.nseg;
-      for (int k2 = tid; k2 < nseg; k2 += kScanThreads) {
-        sm.seg_len[k2] = (k2 + 1 < nseg ? sm.seg_start[k2 + 1] : nm) - sm.seg_start[k2];
-        const int rk = sm.seg_row[k2];
-        if (rk < R0 && (k2 + 1 == nseg || sm.seg_row[k2 + 1] >= R0)) sm.nold = k2 + 1;
-        if (rk >= R0 && rk < rows_after) sm.created_seg[rk - R0] = k2;
-      }
-    }
-    lds_barrier();
-    const int nold = sm.nold;
-    const int nu = nold + nc;
-
     // schedule entry of the next step: a scalar load, issued here so that it is
     // covered by this step's closing barrier rather than stalling an LDS barrier
     if (j + 1 < j_end) sc_next = sched[j + 1];
 
-    // ---- 6a. the new index list: rows before the chunk that this chunk does not
-    // touch keep their version (touched rows are the first nold segments, sorted)
-    if (!ver_lds && j > 0) {
-      const int64_t prev = prev_off;
-      for (int i = tid; i < R0; i += kScanThreads) {
-        int lo = 0, hi = nold;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (sm.seg_row[mid] < i) lo = mid + 1;
-          else hi = mid;
-        }
-        if (lo == nold || sm.seg_row[lo] != i) idx[ioff + i] = idx[prev + i];
-      }
-    }
-
-    // ---- 6b. update every touched or created row.  Entry u of the step's row
-    // list (the nold touched rows in increasing order, then the nc new ones)
-    // gets version nver + u.  The four lanes of token t's group (lane sub owns
-    // key dims [8 sub, 8 sub + 8) and value dims [16 sub, 16 sub + 16)) update
-    // the row t comes first on (position order), or fill the row t creates.
+    // ---- 5. update every touched or created row.  The lane group of token t
+    // (four lanes; lane sub owns key dims [8 sub, 8 sub + 8) and value dims
+    // [16 sub, 16 sub + 16)) fills the row t creates, or updates the row t
+    // merges into when t comes first on it in position order.  The row's
+    // merged tokens are found by a scan of the chunk's targets (lane sub scans
+    // positions [sub Q, sub Q + Q)) and added in position order; the row's new
+    // read form becomes version nver + t.
+    constexpr int Q = C / 4, QW = (Q + 31) / 32;
 #pragma unroll
     for (int ps = 0; ps < TP; ++ps) {
       const int t = (tid >> 2) + ps * (kScanThreads / 4);
       const int sub = tid & 3;
-      int u = -1, row = 0, seg = -1, creator = -1;
-      if (t < C) {
-        if (sm.flag[t] == kMerge) {
-          const int sg = sm.useg[t];
-          if (sg >= 0 && sg < nold) {
-            u = sg;
-            row = sm.seg_row[sg];
-            seg = sg;
-          }
-        } else {
-          const int c2 = sm.arow[t] - R0;
-          u = nold + c2;
-          row = R0 + c2;
-          seg = sm.created_seg[c2];
-          creator = t;
+      const int tc = min(t, C - 1);
+      const bool merged = sm.flag[tc] == kMerge;
+      const int target = sm.arow[tc];
+      uint32_t mk[QW];
+#pragma unroll
+      for (int q = 0; q < QW; ++q) mk[q] = 0u;
+      {
+        const u32x4* m4 = reinterpret_cast<const u32x4*>(sm.mrow + sub * Q);
+#pragma unroll
+        for (int i = 0; i < Q / 4; ++i) {
+          const u32x4 x = m4[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (x[e] == (uint32_t)target) mk[(4 * i + e) >> 5] |= 1u << ((4 * i + e) & 31);
         }
       }
-      if (u < 0) continue;
+      // a merged token heads its row unless a lower position merges into it too
+      uint32_t low = 0u;
+      {
+        const int qt = tc / Q, bt = tc % Q;
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+          const int lo = bt - 32 * q;   // bits of this word below position t
+          const uint32_t below = lo >= 32 ? ~0u : (lo > 0 ? (1u << lo) - 1u : 0u);
+          low |= sub < qt ? mk[q] : (sub == qt ? (mk[q] & below) : 0u);
+        }
+        low |= (uint32_t)xor_lane<1>((int)low);
+        low |= (uint32_t)xor_lane<2>((int)low);
+      }
+      // every lane of the group takes all four quarters' masks
+      uint32_t all[4][QW];
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        all[0][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0x00, 0xF, 0xF, false);
+        all[1][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0x55, 0xF, 0xF, false);
+        all[2][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0xAA, 0xF, 0xF, false);
+        all[3][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0xFF, 0xF, 0xF, false);
+      }
+      const bool creates = !merged;
+      if (t >= C || (merged && (low != 0u || target >= R0))) continue;   // the same for the whole group
+      const int row = target;
       alignas(16) float K[8];
       alignas(16) float V[16];
       int n;
       float rh;
-      if (creator >= 0) {
+      if (creates) {
         // new row: the creating token, unscaled; its value norm is the read radius
         float v2 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) K[i] = tof(Kc[creator][8 * sub + i]);
+        for (int i = 0; i < 8; ++i) K[i] = tof(Kc[t][8 * sub + i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { V[i] = tof(Vc[creator][16 * sub + i]); v2 = fmaf(V[i], V[i], v2); }
+        for (int i = 0; i < 16; ++i) { V[i] = tof(Vc[t][16 * sub + i]); v2 = fmaf(V[i], V[i], v2); }
         v2 = quad_sum(v2);
         n = 1;
         rh = sqrtf(v2);
@@ -865,18 +828,22 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         n = rr[ps].n;
         rh = rr[ps].rh;
       }
-      if (seg >= 0) {
-        const int b = sm.seg_start[seg], e = b + sm.seg_len[seg];
-        for (int r = b; r < e; ++r) {
-          const int t = sm.srt_tok[r];
-          const float gt = chc.g[t];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) K[i] = fmaf(gt, tof(Kc[t][8 * sub + i]), K[i]);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) V[i] = fmaf(gt, tof(Vc[t][16 * sub + i]), V[i]);
+        for (int qw = 0; qw < QW; ++qw) {
+          uint32_t mm = all[q][qw];
+          while (mm) {
+            const int tm = q * Q + 32 * qw + __builtin_ctz(mm);
+            mm &= mm - 1u;
+            const float gt = chc.g[tm];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) K[i] = fmaf(gt, tof(Kc[tm][8 * sub + i]), K[i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) V[i] = fmaf(gt, tof(Vc[tm][16 * sub + i]), V[i]);
+            ++n;
+          }
         }
-        n += e - b;
-      }
       {
         float* ks = key_sum + (size_t)row * 32 + 8 * sub;
         float* vs = val_sum + (size_t)row * 64 + 16 * sub;
@@ -933,7 +900,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       const float rs = 1.0f / sqrtf(var + m.ln_eps);
       // the value at the row's radius, or (ablation) the plain mean
       const float vsc = m.no_vnorm ? invn : (v2 > 0.f ? rh / sqrtf(v2) : 0.f);
-      const int ver = nver + u;
+      const int ver = nver + t;
       alignas(16) RT kh[8];
       alignas(16) T vh[16];
 #pragma unroll
@@ -967,7 +934,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // the next chunk into the spare buffer (chunk j - 1's, no longer read)
     if constexpr (NBUF == 2)
       if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
-    nver += nu;
+    nver += C;
     prev_off = (int)ioff;
     last_rows = rows_after;
     __syncthreads();  // publishes the next chunk's buffer and the step's writes
