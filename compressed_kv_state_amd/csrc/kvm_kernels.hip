@@ -207,7 +207,7 @@ constexpr int kSink = 0, kAppend = 1, kMerge = 2;
 // at the end of a step; with one buffer it is stored at the top of its own step.
 template <typename T, int C>
 struct ScanBuf {
-  static constexpr int NBUF = sizeof(T) * C <= 512 ? 2 : 1;
+  static constexpr int NBUF = C <= 128 ? 2 : 1;
 };
 
 constexpr int kVerCap = 4096;   // rows whose current version ids the scan keeps in LDS
@@ -215,6 +215,8 @@ constexpr int kVerCap = 4096;   // rows whose current version ids the scan keeps
 template <typename T, int C>
 struct ScanChunk {
   alignas(16) T k[C][32];   // live key dims of the chunk's tokens
+  // bf16: the same scaled for the argmax keys (k 2^-e, |k| = m 2^e, m in [0.5, 1))
+  alignas(16) T ks[Is<T>::bf ? C : 1][32];
   alignas(16) T v[C][64];   // values
   float g[C];               // merge gates
   float kn[C];              // |k live|
@@ -304,7 +306,23 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<
 #pragma unroll
     for (int e = 0; e < R::EL; ++e) n2 = fmaf(tof(x[e]), tof(x[e]), n2);
     n2 = group_sum<R::KP>(n2);
-    if (p < C * R::KP && p % R::KP == 0) dst.kn[p / R::KP] = sqrtf(n2);
+    const float kn = sqrtf(n2);
+    if constexpr (Is<T>::bf) {
+      // k 2^-e, exact: each bf16 widened to fp32 (its bits in the upper half),
+      // scaled, and narrowed back by taking the upper half
+      int e;
+      (void)frexpf(kn, &e);
+      u32x4 ys;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t xw = r.k[i][q];
+        const uint32_t lo = __float_as_uint(ldexpf(__uint_as_float(xw << 16), -e));
+        const uint32_t hi = __float_as_uint(ldexpf(__uint_as_float(xw & 0xFFFF0000u), -e));
+        ys[q] = (lo >> 16) | (hi & 0xFFFF0000u);
+      }
+      if (p < C * R::KP) *reinterpret_cast<u32x4*>(&dst.ks[0][0] + p * R::EL) = ys;
+    }
+    if (p < C * R::KP && p % R::KP == 0) dst.kn[p / R::KP] = kn;
   }
 #pragma unroll
   for (int i = 0; i < R::NV; ++i) {
@@ -372,11 +390,37 @@ __device__ __forceinline__ void lane_best(const f32x16& acc, int row0h, uint32_t
 
 // bf16 path: one 32-row tile of unit directions (hi and lo halves) as the MFMA
 // A operand: lane (jl, h) holds dims [16h, 16h+16) of row rb + 32 tile + jl.
+// The first NL rows the pass reads (from row LB: 0, or the first row after the
+// protected sinks) are also kept in LDS, hi and lo halves in a row of UL_PITCH
+// elements (padded so that 16 lanes reading 16 rows hit distinct banks); the
+// update writes both copies.
 // Rows past re - 1 repeat row re - 1: equal values at higher rows, which never
 // win a tie, so they need no mask.
 struct UnitTiles {
   bf16x8 a0[4], a1[4];
 };
+constexpr int UL_PITCH = 72;
+template <typename T, int C>
+struct ScanUnitLds {
+  static constexpr int avail = 163840 - (int)sizeof(ScanSmem<T, C>) - 512;
+  static constexpr int fit = avail / (UL_PITCH * 2);
+  static constexpr int NL = !Is<T>::bf ? 0 : (fit >= 512 ? 512 : (fit > 0 ? fit & ~31 : 0));   // rows
+};
+// LDS-resident tiles of rows [rb, re) (rb == LB): all of them when the rows
+// end within the NL kept, else the first NL / 32.
+__device__ __forceinline__ int lds_tiles(int rb, int re, int LB, int NL) {
+  if (rb != LB || re <= rb) return 0;
+  return re <= LB + NL ? (re - rb + 31) >> 5 : NL >> 5;
+}
+__device__ __forceinline__ void unit_tile_lds(const bf16* ul, int rb, int re, int LB, int tile, bf16x8 (&a)[4]) {
+  const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
+  const int ri = min(rb + (tile << 5) + jl, re - 1) - LB;
+  const bf16* u = ul + ri * UL_PITCH + 16 * h;
+  a[0] = *reinterpret_cast<const bf16x8*>(u);
+  a[1] = *reinterpret_cast<const bf16x8*>(u + 8);
+  a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
+  a[3] = *reinterpret_cast<const bf16x8*>(u + 40);
+}
 __device__ __forceinline__ void unit_tile_load(const char* unit, int rb, int re, int tile, bf16x8 (&a)[4]) {
   const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
   const int ri = min(rb + (tile << 5) + jl, re - 1);
@@ -386,15 +430,22 @@ __device__ __forceinline__ void unit_tile_load(const char* unit, int rb, int re,
   a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
   a[3] = *reinterpret_cast<const bf16x8*>(u + 40);
 }
-// The first two tiles of this wave's share of rows [rb, re) for cos_best,
-// loaded ahead so that their latency overlaps the work before the pass.
+// First tile of this wave's share (wt, wt + WG, ...) that is not LDS-resident.
 template <int C>
-__device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, UnitTiles& pre) {
+__device__ __forceinline__ int first_global_tile(int wt, int ntl) {
+  constexpr int WG = ScanGeom<C>::WG;
+  return wt >= ntl ? wt : wt + WG * ((ntl - wt + WG - 1) / WG);
+}
+// The first two global-memory tiles of this wave's share of rows [rb, re) for
+// cos_best, loaded ahead so that their latency overlaps the work before them.
+template <int C>
+__device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, int ntl, UnitTiles& pre) {
   using G = ScanGeom<C>;
   const int wt = (threadIdx.x >> 6) / G::TS;
   const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
-  if (wt < ntile) unit_tile_load(unit, rb, re, wt, pre.a0);
-  if (wt + G::WG < ntile) unit_tile_load(unit, rb, re, wt + G::WG, pre.a1);
+  const int g0 = first_global_tile<C>(wt, ntl);
+  if (g0 < ntile) unit_tile_load(unit, rb, re, g0, pre.a0);
+  if (g0 + G::WG < ntile) unit_tile_load(unit, rb, re, g0 + G::WG, pre.a1);
 }
 
 // Best (largest) dot(k_t, U_i) over rows i in [rb, re) for every token t of the
@@ -403,8 +454,9 @@ __device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, Un
 // All threads of the block must call it; on the bf16 path `pre` holds the
 // tiles cos_preload fetched for the same rows.
 template <typename T, int C>
-__device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, C>& ch, const char* unit, int rb,
-                                         int re, float* outv, int* outr, UnitTiles& pre) {
+__device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, C>& ch, const char* unit,
+                                         const bf16* ul, int LB, int ntl, int rb, int re, float* outv, int* outr,
+                                         UnitTiles& pre) {
   using G = ScanGeom<C>;
   constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
@@ -419,23 +471,14 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
     f32x16 base;
 #pragma unroll
     for (int r = 0; r < 16; ++r) base[r] = kKeyBase;
-    float sc[CT];
-#pragma unroll
-    for (int tt = 0; tt < CT; ++tt) {
-      int e;
-      sc[tt] = key_scale(ch.kn[tok0 + 32 * tt + jl], e);
-    }
     if constexpr (Is<T>::bf) {
-      // lane half h owns dims [16h, 16h+16) of every 32-dim key (scaled, exact)
+      // lane half h owns dims [16h, 16h+16) of every 32-dim (scaled) key
       bf16x8 bfr[CT][2];
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt)
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&ch.k[tok0 + 32 * tt + jl][16 * h + 8 * q]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bfr[tt][q][i] = (bf16)((float)x[i] * sc[tt]);
-        }
+        for (int q = 0; q < 2; ++q)
+          bfr[tt][q] = *reinterpret_cast<const bf16x8*>(&ch.ks[tok0 + 32 * tt + jl][16 * h + 8 * q]);
       auto load = [&](int tile, bf16x8 (&a)[4]) { unit_tile_load(unit, rb, re, tile, a); };
       auto tile_best = [&](const bf16x8 (&a)[4], int tile) {
         const int row0h = rb + (tile << 5) + 4 * h;
@@ -455,9 +498,15 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
       // two register sets in ping-pong: the loads of tile i+2W are issued right
       // after the MFMAs of tile i read their set, so they overlap tile i+W
       constexpr int WG = G::WG;
+      // LDS-resident tiles first (lowest rows), then the global ones
+      for (int tile = wt; tile < ntl; tile += WG) {
+        bf16x8 b[4];
+        unit_tile_lds(ul, rb, re, LB, tile, b);
+        tile_best(b, tile);
+      }
       bf16x8(&a0)[4] = pre.a0;
       bf16x8(&a1)[4] = pre.a1;
-      for (int tile = wt; tile < ntile; tile += 2 * WG) {
+      for (int tile = first_global_tile<C>(wt, ntl); tile < ntile; tile += 2 * WG) {
         tile_best(a0, tile);
         if (tile + 2 * WG < ntile) load(tile + 2 * WG, a0);
         if (tile + WG < ntile) {
@@ -471,7 +520,10 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
 #pragma unroll
       for (int tt = 0; tt < CT; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) bfr[tt][kk] = tof(ch.k[tok0 + 32 * tt + jl][16 * h + kk]) * sc[tt];
+        for (int kk = 0; kk < 16; ++kk) {
+          int e;
+          bfr[tt][kk] = tof(ch.k[tok0 + 32 * tt + jl][16 * h + kk]) * key_scale(ch.kn[tok0 + 32 * tt + jl], e);
+        }
       const float* U = reinterpret_cast<const float*>(unit);
       for (int tile = wt; tile < ntile; tile += G::WG) {
         const int row0 = rb + (tile << 5);
@@ -558,6 +610,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   constexpr int NBUF = ScanBuf<T, C>::NBUF;
   constexpr int TP = (4 * C + kScanThreads - 1) / kScanThreads;   // token groups of four lanes per thread
   __shared__ ScanSmem<T, C> sm;
+  constexpr int NL = ScanUnitLds<T, C>::NL;
+  __shared__ alignas(16) bf16 ul[NL > 0 ? NL : 1][UL_PITCH];
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
@@ -583,6 +637,14 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     const int r0 = sched[j_begin].z;
     const int* prev = idx + sched[j_begin - 1].w;
     for (int i = tid; i < r0; i += kScanThreads) sm.ver_cur[i] = prev[i];
+  }
+
+  // unit directions kept in LDS: rows [LB, LB + NL) that exist at the start
+  const int LB = m.unprot ? 0 : m.ns;
+  if (NL > 0 && j_begin < j_end) {
+    const int nfill = min(max(sched[j_begin].z - LB, 0), NL);
+    for (int p = tid; p < nfill * 8; p += kScanThreads)
+      copy16(&ul[p >> 3][(p & 3) * 8 + ((p >> 2) & 1) * 32], unit + (size_t)(LB + (p >> 3)) * 128 + 16 * (p & 7));
   }
 
   // the chunk in flight: loaded one step ahead, stored into LDS at the end of
@@ -627,12 +689,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // chunk (every row before the chunk when sinks are unprotected)
     const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
     UnitTiles pre;
-    if constexpr (Is<T>::bf) cos_preload<C>(unit, eb, ee, pre);
+    const int ntl = NL > 0 ? lds_tiles(eb, ee, LB, NL) : 0;
+    if constexpr (Is<T>::bf) cos_preload<C>(unit, eb, ee, ntl, pre);
     const T (*Kc)[32] = chc.k;
     const T (*Vc)[64] = chc.v;
 
     // ---- 2. surprise against the rows before the chunk
-    cos_best<T, C>(sm, chc, unit, eb, ee, sm.bE, sm.rE, pre);
+    cos_best<T, C>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, sm.bE, sm.rE, pre);
     // With the index lists in global memory, the new list starts as a copy of
     // the previous one; the update overwrites the rows it touches.  (Each wave
     // waits for its copies to complete, so the overwrites come after them.)
@@ -867,7 +930,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       v2 = quad_sum(v2);
       // unit key direction for the next cosine passes
       {
-        const float inv = k2 > 0.f ? 1.0f / sqrtf(k2) : 0.f;
+        const float inv = k2 > 0.f ? __builtin_amdgcn_rsqf(k2) : 0.f;   // 1 ulp
         char* ur = unit + (size_t)row * 128;
         if constexpr (Is<T>::bf) {
           alignas(16) bf16 hi[8], lo[8];
@@ -879,6 +942,10 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           }
           copy16(ur + 16 * sub, hi);
           copy16(ur + 64 + 16 * sub, lo);
+          if (NL > 0 && row >= LB && row < LB + NL) {
+            copy16(&ul[row - LB][8 * sub], hi);
+            copy16(&ul[row - LB][32 + 8 * sub], lo);
+          }
         } else {
           alignas(16) float uu[8];
 #pragma unroll
@@ -890,16 +957,16 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       // just-in-time read form ([KVM summary, Core mechanisms 2]): LayerNorm of
       // K/n over the live dims (no affine); the value rho * V/|V| (direction of
       // the sum at the radius fixed at creation).
-      const float invn = 1.0f / (float)n;
+      const float invn = __builtin_amdgcn_rcpf((float)n);   // 1 ulp
       const float mean = ksum * invn * (1.0f / 32.0f);
       float var = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
       var = quad_sum(var);
       var *= (1.0f / 32.0f);
-      const float rs = 1.0f / sqrtf(var + m.ln_eps);
+      const float rs = __builtin_amdgcn_rsqf(var + m.ln_eps);
       // the value at the row's radius, or (ablation) the plain mean
-      const float vsc = m.no_vnorm ? invn : (v2 > 0.f ? rh / sqrtf(v2) : 0.f);
+      const float vsc = m.no_vnorm ? invn : (v2 > 0.f ? rh * __builtin_amdgcn_rsqf(v2) : 0.f);
       const int ver = nver + t;
       alignas(16) RT kh[8];
       alignas(16) T vh[16];
