@@ -760,11 +760,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
         for (int e = e0 + sub; e < nc; e += 4) {
           const int s2 = e < sinks ? e : sm.app_list[e - sinks];
-          float dot = 0.f;
+          // four partial sums (dims i mod 4) keep the dependent chains short
+          float dp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 32; ++i) dot = fmaf(kt[i], tof(Kc[s2][i]), dot);
+          for (int i = 0; i < 32; ++i) dp[i & 3] = fmaf(kt[i], tof(Kc[s2][i]), dp[i & 3]);
+          const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
           const float nk = chc.kn[s2];
-          const float val = nk > 0.f ? dot / nk : 0.f;
+          const float val = nk > 0.f ? dot * __builtin_amdgcn_rcpf(nk) : 0.f;   // 1 ulp
           if (val > best) { best = val; brow = R0 + e; }
         }
       }
