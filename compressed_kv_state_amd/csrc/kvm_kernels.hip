@@ -2108,29 +2108,28 @@ __global__ void rope_keys_kernel(Dims m, Dev d, Src src) {
 // window and absorb the chunk that leaves it.
 // =====================================================================
 template <typename T>
-__global__ void ring_fill_kernel(Dims m, Dev d, Src src, int64_t from, int64_t to) {
-  const int s = blockIdx.x;
+__global__ __launch_bounds__(256) void ring_fill_kernel(Dims m, Dev d, Src src, int64_t from, int64_t to) {
+  // four tokens per workgroup, one lane per dimension
+  const int s = blockIdx.y;
+  const int64_t pos = from + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pos >= to) return;
+  const int dd = threadIdx.x & 63;
   T* rk = reinterpret_cast<T*>(d.ring_k) + (size_t)s * m.R * 64;
   T* rv = reinterpret_cast<T*>(d.ring_v) + (size_t)s * m.R * 64;
   float* rl = d.ring_l + (size_t)s * m.R;
-  const int64_t n = (to - from) * 64;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const int64_t pos = from + i / 64;
-    const int dd = (int)(i % 64);
-    const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
-    const T* kr = reinterpret_cast<const T*>(src.k) + r * 64;
-    const T* vr = reinterpret_cast<const T*>(src.v) + r * 64;
-    float x = tof(kr[dd]);
-    if (dd < 32) {
-      const int jf = dd & 15;
-      const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
-      x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
-    }
-    const size_t slot = (size_t)(pos % m.R);
-    rk[slot * 64 + dd] = fromf<T>(x);
-    rv[slot * 64 + dd] = vr[dd];
-    if (dd == 0) rl[slot] = src.l[r];
+  const size_t r = (size_t)s * src.n_call + (size_t)(pos - src.p0);
+  const T* kr = reinterpret_cast<const T*>(src.k) + r * 64;
+  const T* vr = reinterpret_cast<const T*>(src.v) + r * 64;
+  float x = tof(kr[dd]);
+  if (dd < 32) {
+    const int jf = dd & 15;
+    const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+    x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
   }
+  const size_t slot = (size_t)(pos % m.R);
+  rk[slot * 64 + dd] = fromf<T>(x);
+  rv[slot * 64 + dd] = vr[dd];
+  if (dd == 0) rl[slot] = src.l[r];
 }
 
 // =====================================================================
@@ -2399,8 +2398,9 @@ hipError_t launch_rope_keys(const Dims& m, const Dev& d, const Src& src, hipStre
 
 hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st) {
   if (to <= from) return hipSuccess;
-  if (m.bf16) ring_fill_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, src, from, to);
-  else ring_fill_kernel<float><<<m.BH, 256, 0, st>>>(m, d, src, from, to);
+  const dim3 grid((unsigned)((to - from + 3) / 4), (unsigned)m.BH);
+  if (m.bf16) ring_fill_kernel<bf16><<<grid, 256, 0, st>>>(m, d, src, from, to);
+  else ring_fill_kernel<float><<<grid, 256, 0, st>>>(m, d, src, from, to);
   return hipGetLastError();
 }
 
