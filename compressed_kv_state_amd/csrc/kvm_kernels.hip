@@ -176,10 +176,10 @@ __global__ void rope_table_kernel(float* cosv, float* sinv, int64_t max_tokens, 
 //   3. append the m_j tokens of smallest (surprise, position) (parallel rank);
 //   4. best cosine against the just-appended rows; assignment = better of the
 //      two (lower row on ties);
-//   5. sort merged tokens by (row, position) (parallel rank) and cut them into
-//      per-row segments;
-//   6. four lanes per touched or created row add its segment in position
-//      order (deterministic, no atomics) and write the new read-form version.
+//   5. the four lanes of the first token on each touched row (the creating
+//      token for a new row) find the row's tokens by scanning the chunk's
+//      targets, add them in position order (deterministic, no atomics) and
+//      write the row's new read-form version.
 // Cosines: argmax over rows of cos(k, K_i) = argmax of dot(k, K_i/|K_i|).  On
 // the bf16 path k is exact in bf16 and the unit direction U_i = K_i/|K_i| is
 // split into bf16 hi + lo (|U - hi - lo| <= 2^-18 |U|), so two bf16 MFMA
