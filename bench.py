@@ -154,6 +154,7 @@ def bench_prefill(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     prof = st.profile_read()
+    st.check()
     assert torch.isfinite(out.float()).all(), "non-finite output"
     ms_step = (t1 - t0) * 1e3 / steps
     st.profile(True)
@@ -192,6 +193,7 @@ def bench_variants(w, tensors, steps: int):
             st.prefill(q, k, v, g, out)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        st.check()
         res[name] = {"ms_per_step": ms, "tokens_per_s": w.seqs * w.n_tokens / (ms * 1e-3),
                      "final_rows": st.info()["rows"]}
         log(f"variant {name}: {ms:.3f} ms/step")
@@ -228,6 +230,7 @@ def bench_decode(w, steps: int):
     t1 = time.perf_counter()
     prof = st.profile_read()
     st.profile(False)
+    st.check()
     from compressed_kv_state_amd import schedule
     sched_rows = schedule(cfg, (n - 1) // cfg.chunk + 1)[2].tolist()
     total_bytes = 0

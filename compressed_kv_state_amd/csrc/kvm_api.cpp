@@ -155,7 +155,7 @@ struct Plan {
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
   size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, idx, krot, tslot, tkind, ring_k, ring_v,
-      ring_l, rope_cos, rope_sin, sch, nver, total;
+      ring_l, rope_cos, rope_sin, sch, nver, xbuf, xerr, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -197,6 +197,19 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   m.no_vnorm = (c->flags & KVM_FLAG_NO_VALUE_NORM) ? 1 : 0;
   m.unprot = (c->flags & KVM_FLAG_NO_SINK_PROTECT) ? 1 : 0;
   m.no_gate = (c->flags & KVM_FLAG_NO_MERGE_GATE) ? 1 : 0;
+  // Scan workgroups per sequence: enough for about 128 workgroups in all (the
+  // rest of the chip runs the attention beside the scan), at most 8, and only
+  // if each workgroup's share of the rows (every P-th 32-row tile) fits its
+  // LDS cache of unit directions; else one workgroup per sequence.
+  {
+    int want = 0;
+    while (want < 3 && (int64_t)m.BH << (want + 1) <= 128) ++want;
+    const int64_t lb = m.unprot ? 0 : m.ns;
+    const int64_t ntile = S_cap > lb ? (S_cap - lb + 31) / 32 : 0;
+    const int64_t own_rows = ((ntile + (1 << want) - 1) >> want) * 32;
+    m.Psh = want > 0 && own_rows <= kvm::scan_lds_rows(m.C, m.bf16) ? want : 0;
+    m.P = 1 << m.Psh;
+  }
   const size_t es = m.bf16 ? 2 : 4;
   const size_t BH = (size_t)m.BH, S = (size_t)S_cap;
   size_t off = 0;
@@ -226,6 +239,8 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   p.rope_sin = take((size_t)c->max_tokens * 16 * 4);
   p.sch = take((size_t)J * 16);
   p.nver = take(BH * 4);
+  p.xbuf = take(BH * 2 * (size_t)m.P * m.C * 8);
+  p.xerr = take(4);
   p.total = off;
   return KVM_OK;
 }
@@ -372,8 +387,12 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     d.rope_sin = reinterpret_cast<float*>(b + p.rope_sin);
     d.sched = reinterpret_cast<int4*>(b + p.sch);
     d.nver = reinterpret_cast<int*>(b + p.nver);
+    d.xbuf = reinterpret_cast<uint2*>(b + p.xbuf);
+    d.xerr = reinterpret_cast<int*>(b + p.xerr);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipMemsetAsync(d.nver, 0, (size_t)st->m.BH * 4, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(d.xerr, 0, 4, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(d.xbuf, 0, (size_t)st->m.BH * 2 * st->m.P * st->m.C * 8, hs);
     if (e == hipSuccess && st->m.trace) {
       e = hipMemsetAsync(d.tslot, 0xFF, (size_t)st->m.BH * cfg->max_tokens * 4, hs);
       if (e == hipSuccess) e = hipMemsetAsync(d.tkind, 0xFF, (size_t)st->m.BH * cfg->max_tokens, hs);
@@ -573,10 +592,27 @@ kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info) {
   return KVM_OK;
 }
 
+kvm_status kvm_state_check(kvm_state* st, void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  int flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, st->d.xerr, 4, hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_fail(st, e, "state check");
+  if (flag != 0) {
+    st->poisoned = true;
+    return fail(KVM_E_HIP, "an absorption scan workgroup gave up waiting at a cross-workgroup exchange");
+  }
+  return KVM_OK;
+}
+
 kvm_status kvm_state_reset(kvm_state* st, void* stream) {
   if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemsetAsync(st->d.nver, 0, (size_t)st->m.BH * 4, hs);
+  if (e == hipSuccess) e = hipMemsetAsync(st->d.xerr, 0, 4, hs);
+  if (e == hipSuccess) e = hipMemsetAsync(st->d.xbuf, 0, (size_t)st->m.BH * 2 * st->m.P * st->m.C * 8, hs);
   if (e == hipSuccess && st->m.trace) {
     e = hipMemsetAsync(st->d.tslot, 0xFF, (size_t)st->m.BH * st->m.max_tokens * 4, hs);
     if (e == hipSuccess) e = hipMemsetAsync(st->d.tkind, 0xFF, (size_t)st->m.BH * st->m.max_tokens, hs);

@@ -31,6 +31,9 @@ struct Dims {
   int no_vnorm;       // 1: read values as the mean V/n (ablation)
   int unprot;         // 1: sink rows are ordinary rows (ablation)
   int no_gate;        // 1: merge weight 1 (ablation)
+  int P;              // scan workgroups per sequence (1, 2, 4 or 8); each owns every P-th 32-row tile
+                      // and, when P > 1, keeps all of its rows' unit directions in LDS
+  int Psh;            // log2(P)
 };
 
 // Device regions carved from the caller's workspace.  Per-sequence arrays are
@@ -61,6 +64,8 @@ struct Dev {
   float* rope_sin;   // [max_tokens][16]
   int4* sched;       // [J_cap] (sinks_j, appends_j, rows_before_j, idx_off_j)
   int* nver;         // [BH] versions used
+  uint2* xbuf;       // [BH][2][P][C] scan exchange: each workgroup's best per token (key bits, row | step tag)
+  int* xerr;         // [1] set when a scan workgroup gave up waiting at an exchange
 };
 
 // Token source for a launch: positions >= p0 come from the call's inputs
@@ -74,6 +79,8 @@ struct Src {
   int64_t n_call;
 };
 
+// Rows of unit directions a scan workgroup keeps in LDS (bf16 path; 0 on the fp32 path).
+int scan_lds_rows(int C, bool is_bf16);
 hipError_t launch_init(const Dims& m, const Dev& d, double rope_theta, hipStream_t st);
 // Absorb chunks [j_begin, j_end) for every sequence (sequential over j inside the kernel).
 hipError_t launch_scan(const Dims& m, const Dev& d, const Src& src, int j_begin, int j_end, hipStream_t st);

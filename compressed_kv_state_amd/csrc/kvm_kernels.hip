@@ -237,8 +237,14 @@ struct ScanSmem {
   alignas(16) int mrow[C];   // row of each merged token, -1 for the others
   int app_list[C];
   int wtot[ScanGeom<C>::NW];
-  int ver_cur[kVerCap];           // current version id of every row
+  int xok;                        // 0 after a wait at the exchange timed out
+  int ver_cur[kVerCap];           // current version id of every row (own rows kept current)
 };
+
+// Polls of an exchange record before a scan workgroup gives up (~1 s): the
+// workgroups of a sequence are all resident unless other kernels hold the
+// CUs, which they release; the limit only guarantees that every wave ends.
+constexpr int kSpinLimit = 1 << 22;
 
 // A chunk's live keys, values and gate logits in registers, between loads
 // issued one chunk step ahead and the stores into an LDS buffer: thread tid
@@ -406,15 +412,29 @@ struct ScanUnitLds {
   static constexpr int fit = avail / (UL_PITCH * 2);
   static constexpr int NL = !Is<T>::bf ? 0 : (fit >= 512 ? 512 : (fit > 0 ? fit & ~31 : 0));   // rows
 };
-// LDS-resident tiles of rows [rb, re) (rb == LB): all of them when the rows
-// end within the NL kept, else the first NL / 32.
-__device__ __forceinline__ int lds_tiles(int rb, int re, int LB, int NL) {
-  if (rb != LB || re <= rb) return 0;
-  return re <= LB + NL ? (re - rb + 31) >> 5 : NL >> 5;
+// Row partition: a sequence's rows from LB on are split into 32-row tiles,
+// and of P = 2^psh workgroups, workgroup p owns tiles p, p + P, ... (rows
+// below LB, the protected sinks, belong to workgroup 0).  A workgroup numbers
+// its own tiles locally (k = 0, 1, ...: global tile p + k P).
+__device__ __forceinline__ int own_tiles(int ntile, int p, int psh) {
+  return ntile > p ? ((ntile - 1 - p) >> psh) + 1 : 0;
 }
-__device__ __forceinline__ void unit_tile_lds(const bf16* ul, int rb, int re, int LB, int tile, bf16x8 (&a)[4]) {
+// LDS slot of own row r >= LB: local tile * 32 + offset in the tile
+__device__ __forceinline__ int own_slot(int r, int LB, int psh) {
+  return ((((r - LB) >> 5) >> psh) << 5) + ((r - LB) & 31);
+}
+// LDS-resident local tiles of rows [rb, re) (rb == LB): the first NL / 32 of
+// the workgroup's own tiles.
+__device__ __forceinline__ int lds_tiles(int rb, int re, int LB, int NL, int p, int psh) {
+  if (rb != LB || re <= rb) return 0;
+  return min(own_tiles((re - rb + 31) >> 5, p, psh), NL >> 5);
+}
+// Global tile gt (own, local tile kt) from LDS; rows past re - 1 repeat row
+// re - 1, which lies in the same (last) tile.
+__device__ __forceinline__ void unit_tile_lds(const bf16* ul, int rb, int re, int LB, int gt, int psh,
+                                              bf16x8 (&a)[4]) {
   const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
-  const int ri = min(rb + (tile << 5) + jl, re - 1) - LB;
+  const int ri = own_slot(min(rb + (gt << 5) + jl, re - 1), LB, psh);
   const bf16* u = ul + ri * UL_PITCH + 16 * h;
   a[0] = *reinterpret_cast<const bf16x8*>(u);
   a[1] = *reinterpret_cast<const bf16x8*>(u + 8);
@@ -430,33 +450,37 @@ __device__ __forceinline__ void unit_tile_load(const char* unit, int rb, int re,
   a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
   a[3] = *reinterpret_cast<const bf16x8*>(u + 40);
 }
-// First tile of this wave's share (wt, wt + WG, ...) that is not LDS-resident.
+// First local tile of this wave's share (wt, wt + WG, ...) that is not LDS-resident.
 template <int C>
 __device__ __forceinline__ int first_global_tile(int wt, int ntl) {
   constexpr int WG = ScanGeom<C>::WG;
   return wt >= ntl ? wt : wt + WG * ((ntl - wt + WG - 1) / WG);
 }
-// The first two global-memory tiles of this wave's share of rows [rb, re) for
-// cos_best, loaded ahead so that their latency overlaps the work before them.
+// The first two global-memory tiles of this wave's share of the workgroup's
+// rows in [rb, re) for cos_best, loaded ahead so that their latency overlaps
+// the work before them.
 template <int C>
-__device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, int ntl, UnitTiles& pre) {
+__device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, int ntl, int p, int psh,
+                                            UnitTiles& pre) {
   using G = ScanGeom<C>;
   const int wt = (threadIdx.x >> 6) / G::TS;
-  const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
+  const int nown = own_tiles(re > rb ? (re - rb + 31) >> 5 : 0, p, psh);
   const int g0 = first_global_tile<C>(wt, ntl);
-  if (g0 < ntile) unit_tile_load(unit, rb, re, g0, pre.a0);
-  if (g0 + G::WG < ntile) unit_tile_load(unit, rb, re, g0 + G::WG, pre.a1);
+  if (g0 < nown) unit_tile_load(unit, rb, re, p + (g0 << psh), pre.a0);
+  if (g0 + G::WG < nown) unit_tile_load(unit, rb, re, p + ((g0 + G::WG) << psh), pre.a1);
 }
 
-// Best (largest) dot(k_t, U_i) over rows i in [rb, re) for every token t of the
-// chunk, compared on the argmax keys (to 2^-17 |k_t|); ties to the lowest row.
-// Writes outv/outr[t] (-inf / INT_MAX if no row).
+// Best (largest) dot(k_t, U_i) over this workgroup's rows i in [rb, re) for
+// every token t of the chunk, compared on the argmax keys (to 2^-17 |k_t|);
+// ties to the lowest row.  Writes the best key (as a float in (1, 3), 0 if
+// the workgroup has no row) and its row (INT_MAX if none) to outv / outr.
 // All threads of the block must call it; on the bf16 path `pre` holds the
-// tiles cos_preload fetched for the same rows.
-template <typename T, int C>
+// tiles cos_preload fetched for the same rows.  PART: the rows are split over
+// several workgroups and every own row is LDS-resident (ntl == own tiles).
+template <typename T, int C, bool PART>
 __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, C>& ch, const char* unit,
-                                         const bf16* ul, int LB, int ntl, int rb, int re, float* outv, int* outr,
-                                         UnitTiles& pre) {
+                                         const bf16* ul, int LB, int ntl, int rb, int re, int p, int psh,
+                                         float* outv, int* outr, UnitTiles& pre) {
   using G = ScanGeom<C>;
   constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
@@ -466,8 +490,8 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
   int br[CT];
 #pragma unroll
   for (int tt = 0; tt < CT; ++tt) { bk[tt] = 0u; br[tt] = INT_MAX; }
-  const int ntile = re > rb ? (re - rb + 31) >> 5 : 0;
-  if (wt < ntile) {
+  const int nown = own_tiles(re > rb ? (re - rb + 31) >> 5 : 0, p, psh);   // own tiles (local k < nown)
+  if (wt < nown) {
     f32x16 base;
 #pragma unroll
     for (int r = 0; r < 16; ++r) base[r] = kKeyBase;
@@ -479,9 +503,9 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           bfr[tt][q] = *reinterpret_cast<const bf16x8*>(&ch.ks[tok0 + 32 * tt + jl][16 * h + 8 * q]);
-      auto load = [&](int tile, bf16x8 (&a)[4]) { unit_tile_load(unit, rb, re, tile, a); };
-      auto tile_best = [&](const bf16x8 (&a)[4], int tile) {
-        const int row0h = rb + (tile << 5) + 4 * h;
+      auto load = [&](int kt, bf16x8 (&a)[4]) { unit_tile_load(unit, rb, re, p + (kt << psh), a); };
+      auto tile_best = [&](const bf16x8 (&a)[4], int kt) {
+        const int row0h = rb + ((p + (kt << psh)) << 5) + 4 * h;
         f32x16 acc[CT];
         // independent accumulators interleaved so dependent MFMAs are CT apart
 #pragma unroll
@@ -499,19 +523,21 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
       // after the MFMAs of tile i read their set, so they overlap tile i+W
       constexpr int WG = G::WG;
       // LDS-resident tiles first (lowest rows), then the global ones
-      for (int tile = wt; tile < ntl; tile += WG) {
+      for (int kt = wt; kt < ntl; kt += WG) {
         bf16x8 b[4];
-        unit_tile_lds(ul, rb, re, LB, tile, b);
-        tile_best(b, tile);
+        unit_tile_lds(ul, rb, re, LB, p + (kt << psh), psh, b);
+        tile_best(b, kt);
       }
-      bf16x8(&a0)[4] = pre.a0;
-      bf16x8(&a1)[4] = pre.a1;
-      for (int tile = first_global_tile<C>(wt, ntl); tile < ntile; tile += 2 * WG) {
-        tile_best(a0, tile);
-        if (tile + 2 * WG < ntile) load(tile + 2 * WG, a0);
-        if (tile + WG < ntile) {
-          tile_best(a1, tile + WG);
-          if (tile + 3 * WG < ntile) load(tile + 3 * WG, a1);
+      if constexpr (!PART) {
+        bf16x8(&a0)[4] = pre.a0;
+        bf16x8(&a1)[4] = pre.a1;
+        for (int kt = first_global_tile<C>(wt, ntl); kt < nown; kt += 2 * WG) {
+          tile_best(a0, kt);
+          if (kt + 2 * WG < nown) load(kt + 2 * WG, a0);
+          if (kt + WG < nown) {
+            tile_best(a1, kt + WG);
+            if (kt + 3 * WG < nown) load(kt + 3 * WG, a1);
+          }
         }
       }
     } else {
@@ -525,8 +551,8 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
           bfr[tt][kk] = tof(ch.k[tok0 + 32 * tt + jl][16 * h + kk]) * key_scale(ch.kn[tok0 + 32 * tt + jl], e);
         }
       const float* U = reinterpret_cast<const float*>(unit);
-      for (int tile = wt; tile < ntile; tile += G::WG) {
-        const int row0 = rb + (tile << 5);
+      for (int kt = wt; kt < nown; kt += G::WG) {
+        const int row0 = rb + ((p + (kt << psh)) << 5);
         const int ri = min(row0 + jl, re - 1);
         const float* u = U + (size_t)ri * 32 + 16 * h;
         float a[16];
@@ -549,13 +575,13 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
     const uint32_t ok = partner_u32(bk[tt]);
     const int orow = partner_i(br[tt]);
     if (ok > bk[tt] || (ok == bk[tt] && orow < br[tt])) { bk[tt] = ok; br[tt] = orow; }
-    if (h == 0 && wt < ntile) {
+    if (h == 0 && wt < nown) {
       sm.red_v[wt][tok0 + 32 * tt + jl] = __uint_as_float(bk[tt]);
       sm.red_r[wt][tok0 + 32 * tt + jl] = br[tt];
     }
   }
   lds_barrier();
-  const int nw = min(ntile, G::WG);
+  const int nw = min(nown, G::WG);
   for (int t = tid; t < C; t += G::NT) {
     float v = 0.f;
     int r = INT_MAX;
@@ -564,10 +590,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, 
       const int orow = sm.red_r[ww][t];
       if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
     }
-    // back to the dot product: subtract the base (exact on (1, 3)) and undo the scaling
-    int e;
-    (void)key_scale(ch.kn[t], e);
-    outv[t] = r == INT_MAX ? -kInf : ldexpf(v - kKeyBase, e);
+    outv[t] = v;
     outr[t] = r;
   }
   lds_barrier();
@@ -600,7 +623,12 @@ __device__ __forceinline__ int parallel_rank(const uint32_t* key, int& t_out) {
   return (t < C && part == 0) ? cnt : -1;
 }
 
-template <typename T, int C>
+// PART: the sequence's rows are split over P = 2^Psh > 1 workgroups, each
+// holding all of its own rows' unit directions in LDS (the host picks P so
+// that they fit), with one exchange of per-token bests per chunk; otherwise
+// one workgroup per sequence, rows past the LDS-resident ones streamed from
+// global memory.
+template <typename T, int C, bool PART>
 __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Src src, const int4* __restrict__ sched,
                                                                  int j_begin, int j_end) {
   constexpr int kScanThreads = ScanGeom<C>::NT;
@@ -612,8 +640,32 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   __shared__ ScanSmem<T, C> sm;
   constexpr int NL = ScanUnitLds<T, C>::NL;
   __shared__ alignas(16) bf16 ul[NL > 0 ? NL : 1][UL_PITCH];
-  const int s = blockIdx.x;
+  // Workgroup p of the P = 2^psh that share sequence s (each owns every P-th
+  // 32-row tile of the rows from LB on).  With the sequence count a multiple
+  // of 8, a sequence's workgroups are P consecutive dispatches on one XCD
+  // (dispatch b goes to XCD b mod 8), so their exchanges stay in one L2.
+  const int psh = PART ? m.Psh : 0;
+  int s, p;
+  if constexpr (PART) {
+    const int b = blockIdx.x;
+    if (m.BH % 8 == 0) {
+      const int k = b >> 3;
+      s = ((k >> psh) << 3) + (b & 7);
+      p = k & (m.P - 1);
+    } else {
+      s = b >> psh;
+      p = b & (m.P - 1);
+    }
+  } else {
+    s = blockIdx.x;
+    p = 0;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int LB = m.unprot ? 0 : m.ns;   // first row of the tile partition
+  auto own = [&](int r) {
+    if constexpr (PART) return r < LB ? p == 0 : (((r - LB) >> 5) & (m.P - 1)) == p;
+    else return true;
+  };
 
   float* key_sum = d.key_sum + (size_t)s * m.S_cap * 32;
   float* val_sum = d.val_sum + (size_t)s * m.S_cap * 64;
@@ -639,12 +691,16 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     for (int i = tid; i < r0; i += kScanThreads) sm.ver_cur[i] = prev[i];
   }
 
-  // unit directions kept in LDS: rows [LB, LB + NL) that exist at the start
-  const int LB = m.unprot ? 0 : m.ns;
+  // unit directions kept in LDS: the first NL rows of the workgroup's own
+  // tiles (local slot = local tile * 32 + offset) that exist at the start
   if (NL > 0 && j_begin < j_end) {
-    const int nfill = min(max(sched[j_begin].z - LB, 0), NL);
-    for (int p = tid; p < nfill * 8; p += kScanThreads)
-      copy16(&ul[p >> 3][(p & 3) * 8 + ((p >> 2) & 1) * 32], unit + (size_t)(LB + (p >> 3)) * 128 + 16 * (p & 7));
+    const int R0s = sched[j_begin].z;
+    const int nfill = min(own_tiles(R0s > LB ? (R0s - LB + 31) >> 5 : 0, p, psh) * 32, NL);
+    for (int q = tid; q < nfill * 8; q += kScanThreads) {
+      const int ls = q >> 3;
+      const int r = LB + ((p + ((ls >> 5) << psh)) << 5) + (ls & 31);
+      if (r < R0s) copy16(&ul[ls][(q & 3) * 8 + ((q >> 2) & 1) * 32], unit + (size_t)r * 128 + 16 * (q & 7));
+    }
   }
 
   // the chunk in flight: loaded one step ahead, stored into LDS at the end of
@@ -676,7 +732,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
 
     // index list of the previous step (its rows are the R0 rows before this chunk)
     if (ver_lds && j > j_begin)
-      for (int i = tid; i < R0; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
+      for (int i = tid; i < R0; i += kScanThreads)
+        if (own(i)) idx[prev_off + i] = sm.ver_cur[i];
 
     // ---- 1. the chunk, its key norms and gates are in LDS buffer `cur` (one
     // buffer: store it now); the first unit-direction tiles of the surprise
@@ -689,18 +746,95 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // chunk (every row before the chunk when sinks are unprotected)
     const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
     UnitTiles pre;
-    const int ntl = NL > 0 ? lds_tiles(eb, ee, LB, NL) : 0;
-    if constexpr (Is<T>::bf) cos_preload<C>(unit, eb, ee, ntl, pre);
+    const int ntl = NL > 0 ? lds_tiles(eb, ee, LB, NL, p, psh) : 0;
+    if constexpr (Is<T>::bf && !PART) cos_preload<C>(unit, eb, ee, ntl, p, psh, pre);
     const T (*Kc)[32] = chc.k;
     const T (*Vc)[64] = chc.v;
 
-    // ---- 2. surprise against the rows before the chunk
-    cos_best<T, C>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, sm.bE, sm.rE, pre);
+    // ---- 2. surprise against the rows before the chunk: each workgroup's
+    // best over its own rows, then (P > 1) the exchange of those bests
+    if (tid == 0) sm.xok = 1;
+    cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, sm.bE, sm.rE, pre);
+    if constexpr (PART) {
+      // Exchange of the P workgroups' bests.  Each token's best is published
+      // as one 64-bit record: key bits | (row (24 bits, all ones for none) |
+      // step tag << 24) << 32, in the buffer of this step's parity; the tag
+      // is 0x80 | (j mod 128), never 0, the value the buffer is cleared to at
+      // state creation and reset.  Readers poll the records themselves until
+      // all carry this step's tag, so the exchange is one store and one load
+      // round trip; a record is written and read whole (relaxed agent-scope
+      // atomics, coherent across the chip), and the tag tells it from the one
+      // of two steps back.  (A
+      // workgroup overwrites a slot two steps later only after it has read
+      // every other workgroup's records of the step between, which they
+      // publish after reading this one.)  The combine order does not matter:
+      // (larger key, then lower row) is a total order.
+      uint64_t* xb = reinterpret_cast<uint64_t*>(d.xbuf) + ((size_t)s * 2 + (j & 1)) * ((size_t)m.P * C);
+      const uint32_t tag = 0x80u | (uint32_t)(j & 0x7F);
+      for (int t = tid; t < C; t += kScanThreads) {
+        const uint32_t r = sm.rE[t] == INT_MAX ? 0xFFFFFFu : (uint32_t)sm.rE[t];
+        const uint64_t x = (uint64_t)__float_as_uint(sm.bE[t]) | ((uint64_t)(r | (tag << 24)) << 32);
+        __hip_atomic_store(xb + (size_t)p * C + t, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // XL lanes per token (a power of two, at most 8): lane sub polls the
+      // records of workgroups sub, sub + XL, ...; the group then combines.
+      constexpr int XL = kScanThreads / C < 8 ? kScanThreads / C : 8;
+      constexpr int XR = (8 + XL - 1) / XL;   // records per lane at most
+      const int xt = tid / XL, xs = tid % XL;
+      if (xt < C) {
+        float v = 0.f;
+        int r = INT_MAX;
+        uint32_t pending = 0u;
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+          const int q = xs + XL * i;
+          if (q < m.P) pending |= 1u << i;
+        }
+        for (int spin = 0; pending != 0u;) {
+          uint64_t x[XR];
+#pragma unroll
+          for (int i = 0; i < XR; ++i)
+            if (pending & (1u << i))
+              x[i] = __hip_atomic_load(xb + (size_t)(xs + XL * i) * C + xt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int i = 0; i < XR; ++i) {
+            if ((pending & (1u << i)) && (uint32_t)(x[i] >> 56) == tag) {
+              pending &= ~(1u << i);
+              const float ov = __uint_as_float((uint32_t)x[i]);
+              const uint32_t rr = (uint32_t)(x[i] >> 32) & 0xFFFFFFu;
+              const int orow = rr == 0xFFFFFFu ? INT_MAX : (int)rr;
+              if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
+            }
+          }
+          if (pending != 0u) {
+            if (++spin >= kSpinLimit) {
+              sm.xok = 0;
+              __hip_atomic_store(d.xerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < XL; o <<= 1) {
+          const float ov = __shfl_xor(v, o);
+          const int orow = __shfl_xor(r, o);
+          if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
+        }
+        if (xs == 0) {
+          sm.bE[xt] = v;
+          sm.rE[xt] = r;
+        }
+      }
+      lds_barrier();
+      if (!sm.xok) break;   // the whole workgroup leaves the chunk loop
+    }
     // With the index lists in global memory, the new list starts as a copy of
     // the previous one; the update overwrites the rows it touches.  (Each wave
     // waits for its copies to complete, so the overwrites come after them.)
     if (!ver_lds && j > 0) {
-      for (int i = tid; i < R0; i += kScanThreads) idx[ioff + i] = idx[prev_off + i];
+      for (int i = tid; i < R0; i += kScanThreads)
+        if (own(i)) idx[ioff + i] = idx[prev_off + i];
       wait_vmem();
     }
     // The next chunk loads from here to the end of the step (issued after the
@@ -708,6 +842,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // wait for these).
     if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     for (int t = tid; t < C; t += kScanThreads) {
+      // back to the dot product: subtract the key base (exact on (1, 3)) and
+      // undo the token's power-of-two scaling
+      {
+        int e;
+        (void)key_scale(chc.kn[t], e);
+        sm.bE[t] = sm.rE[t] == INT_MAX ? -kInf : ldexpf(sm.bE[t] - kKeyBase, e);
+      }
       float mu;
       if (ee > eb) mu = chc.kn[t] > 0.f ? sm.bE[t] / chc.kn[t] : 0.f;
       else mu = -kInf;
@@ -808,7 +949,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
 #pragma unroll
     for (int ps = 0; ps < TP; ++ps) {
       const int t = (tid >> 2) + ps * (kScanThreads / 4);
-      if (t < C && sm.flag[t] == kMerge) row_load(rr[ps], key_sum, val_sum, count, rho, sm.arow[t], tid & 3);
+      if (t < C && sm.flag[t] == kMerge && own(sm.arow[t]))
+        row_load(rr[ps], key_sum, val_sum, count, rho, sm.arow[t], tid & 3);
     }
 
     // schedule entry of the next step: a scalar load, issued here so that it is
@@ -830,6 +972,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       const int tc = min(t, C - 1);
       const bool merged = sm.flag[tc] == kMerge;
       const int target = sm.arow[tc];
+      if (t >= C || !own(target)) continue;   // another workgroup's row (the same for the lane group)
       uint32_t mk[QW];
 #pragma unroll
       for (int q = 0; q < QW; ++q) mk[q] = 0u;
@@ -944,9 +1087,12 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           }
           copy16(ur + 16 * sub, hi);
           copy16(ur + 64 + 16 * sub, lo);
-          if (NL > 0 && row >= LB && row < LB + NL) {
-            copy16(&ul[row - LB][8 * sub], hi);
-            copy16(&ul[row - LB][32 + 8 * sub], lo);
+          if (NL > 0 && row >= LB) {
+            const int ls = own_slot(row, LB, psh);
+            if (ls < NL) {
+              copy16(&ul[ls][8 * sub], hi);
+              copy16(&ul[ls][32 + 8 * sub], lo);
+            }
           }
         } else {
           alignas(16) float uu[8];
@@ -992,7 +1138,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         else idx[ioff + row] = ver;
       }
     }
-    if (m.trace) {
+    if (m.trace && p == 0) {
       int* tslot = d.tslot + (size_t)s * m.max_tokens;
       uint8_t* tkind = d.tkind + (size_t)s * m.max_tokens;
       for (int t = tid; t < C; t += kScanThreads) {
@@ -1009,8 +1155,9 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     __syncthreads();  // publishes the next chunk's buffer and the step's writes
   }
   if (ver_lds && j_end > j_begin)
-    for (int i = tid; i < last_rows; i += kScanThreads) idx[prev_off + i] = sm.ver_cur[i];
-  if (tid == 0) d.nver[s] = nver;
+    for (int i = tid; i < last_rows; i += kScanThreads)
+      if (own(i)) idx[prev_off + i] = sm.ver_cur[i];
+  if (tid == 0 && p == 0) d.nver[s] = nver;
 }
 
 // =====================================================================
@@ -2327,11 +2474,24 @@ __global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, ty
 
 template <typename T>
 hipError_t scan_dispatch(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {
+  const bool part = m.P > 1;
   switch (m.C) {
-    case 32: scan_kernel<T, 32><<<m.BH, ScanGeom<32>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
-    case 64: scan_kernel<T, 64><<<m.BH, ScanGeom<64>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
-    case 128: scan_kernel<T, 128><<<m.BH, ScanGeom<128>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
-    case 256: scan_kernel<T, 256><<<m.BH, ScanGeom<256>::NT, 0, st>>>(m, d, src, d.sched, jb, je); break;
+    case 32:
+      if (part) scan_kernel<T, 32, true><<<m.BH * m.P, ScanGeom<32>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      else scan_kernel<T, 32, false><<<m.BH, ScanGeom<32>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      break;
+    case 64:
+      if (part) scan_kernel<T, 64, true><<<m.BH * m.P, ScanGeom<64>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      else scan_kernel<T, 64, false><<<m.BH, ScanGeom<64>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      break;
+    case 128:
+      if (part) scan_kernel<T, 128, true><<<m.BH * m.P, ScanGeom<128>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      else scan_kernel<T, 128, false><<<m.BH, ScanGeom<128>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      break;
+    case 256:
+      if (part) scan_kernel<T, 256, true><<<m.BH * m.P, ScanGeom<256>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      else scan_kernel<T, 256, false><<<m.BH, ScanGeom<256>::NT, 0, st>>>(m, d, src, d.sched, jb, je);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2374,6 +2534,17 @@ hipError_t launch_init(const Dims& m, const Dev& d, double theta, hipStream_t st
   const int64_t n = m.max_tokens * 16;
   rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(d.rope_cos, d.rope_sin, m.max_tokens, theta);
   return hipGetLastError();
+}
+
+int scan_lds_rows(int C, bool is_bf16) {
+  if (!is_bf16) return 0;
+  switch (C) {
+    case 32: return ScanUnitLds<bf16, 32>::NL;
+    case 64: return ScanUnitLds<bf16, 64>::NL;
+    case 128: return ScanUnitLds<bf16, 128>::NL;
+    case 256: return ScanUnitLds<bf16, 256>::NL;
+    default: return 0;
+  }
 }
 
 hipError_t launch_scan(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {

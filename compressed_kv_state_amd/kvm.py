@@ -89,6 +89,7 @@ def library() -> ctypes.CDLL:
         L.kvm_snapshot_read.argtypes = [vp, i64, vp, vp, vp, vp]
         L.kvm_state_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
         L.kvm_state_reset.argtypes = [vp, vp]
+        L.kvm_state_check.argtypes = [vp, vp]
         L.kvm_profile_enable.argtypes = [vp, st]
         L.kvm_profile_read.argtypes = [vp, ctypes.POINTER(_Prof)]
         L.kvm_status_str.argtypes = [st]
@@ -97,7 +98,7 @@ def library() -> ctypes.CDLL:
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
                      "kvm_decode_step", "kvm_state_read", "kvm_snapshot_read", "kvm_state_get_info",
-                     "kvm_state_reset", "kvm_profile_enable", "kvm_profile_read"):
+                     "kvm_state_reset", "kvm_state_check", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -279,6 +280,11 @@ class KvmState:
     def reset(self):
         """Back to position 0 with an empty state (queued on the current stream)."""
         _check(library().kvm_state_reset(self._h, _stream(self.device)))
+
+    def check(self):
+        """Raise KvmError if an absorption scan gave up at a cross-workgroup exchange
+        (synchronises the current stream)."""
+        _check(library().kvm_state_check(self._h, _stream(self.device)))
 
     def profile(self, enable=True):
         """Record HIP events around later kernel launches: True = every phase, False = none,

@@ -190,6 +190,16 @@ kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, voi
 /* Host-side facts about the state.  Never fails on a valid pointer. */
 kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info);
 
+/* Check that every absorption scan queued so far on this state finished its
+ * work.  When a sequence's state rows are split over several workgroups (a
+ * state with few sequences), the workgroups meet once per absorbed chunk to
+ * combine their best-matching rows; a workgroup that waits there for about a
+ * second gives up, so that no kernel can hang, and marks the state.  This
+ * call copies that mark to the host and synchronises `stream`.
+ * Errors: KVM_E_INVALID_ARG; KVM_E_HIP if a scan gave up (the state is then
+ * poisoned) or on a HIP failure. */
+kvm_status kvm_state_check(kvm_state* st, void* stream);
+
 /* Return the state to position 0 with an empty compressed state (the RoPE and
  * schedule tables are kept).  Queues a counter reset on `stream`.
  * Errors: KVM_E_INVALID_ARG, KVM_E_HIP. */

@@ -50,6 +50,7 @@ def run_prefill(w: LayerConfig, inp: Inputs, n_tokens: Optional[int] = None, max
         outs.append(st.prefill(q, k, v, g))
     state = st.read(trace=True)
     torch.cuda.synchronize()
+    st.check()
     out = torch.cat(outs, dim=1).double().cpu().numpy()
     slot = state["trace_slot"][:, :n].long().cpu().numpy()
     kind = state["trace_kind"][:, :n].long().cpu().numpy()
@@ -174,6 +175,7 @@ def run_prefill_decode(w: LayerConfig, inp: Inputs, n0: int, steps: int, cfg_ove
                                    g[:, i].contiguous())[:, None])
     state = st.read(trace=True)
     torch.cuda.synchronize()
+    st.check()
     out = torch.cat(outs, dim=1).double().cpu().numpy()
     slot = state["trace_slot"][:, :n].long().cpu().numpy()
     kind = state["trace_kind"][:, :n].long().cpu().numpy()
