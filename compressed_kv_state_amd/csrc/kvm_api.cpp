@@ -589,6 +589,7 @@ kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info) {
   info->max_rows = st->m.S_cap;
   info->max_chunks = st->m.J_cap;
   info->poisoned = st->poisoned ? 1 : 0;
+  info->scan_groups = st->m.P;
   return KVM_OK;
 }
 

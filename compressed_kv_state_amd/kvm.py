@@ -56,7 +56,8 @@ class _View(ctypes.Structure):
 
 class _Info(ctypes.Structure):
     _fields_ = [("position", ctypes.c_int64), ("absorbed_chunks", ctypes.c_int64), ("rows", ctypes.c_int32),
-                ("max_rows", ctypes.c_int32), ("max_chunks", ctypes.c_int64), ("poisoned", ctypes.c_int32)]
+                ("max_rows", ctypes.c_int32), ("max_chunks", ctypes.c_int64), ("poisoned", ctypes.c_int32),
+                ("scan_groups", ctypes.c_int32)]
 
 
 class _Prof(ctypes.Structure):

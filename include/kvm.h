@@ -119,6 +119,7 @@ typedef struct kvm_state_info {
   int32_t max_rows;       /* S_cap: rows after the last chunk max_tokens can absorb */
   int64_t max_chunks;     /* chunks max_tokens can absorb */
   int32_t poisoned;       /* 1 after KVM_E_HIP */
+  int32_t scan_groups;    /* workgroups that share one sequence's absorption scan (1, 2, 4 or 8) */
 } kvm_state_info;
 
 /* Device workspace size for cfg (bytes; the workspace must be 256-byte aligned).

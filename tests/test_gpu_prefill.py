@@ -279,3 +279,27 @@ def test_profile_mask_records_selected_phases():
     assert p["scan_launches"] == 0 and p["ring_launches"] == 0 and p["prep_launches"] == 0
     with pytest.raises(KvmError):
         st.profile(64)
+
+
+def test_scan_row_partition_is_invisible():
+    """The absorption scan splits a sequence's rows over 1, 2, 4 or 8 workgroups by how many
+    sequences share the GPU; the state and outputs of a sequence must not depend on it."""
+    w = small("bf16", chunk=128, window=256, n_tokens=2048 + 77, heads=1, alpha=8, n_clusters=64)
+    ref = None
+    seen = set()
+    for nseq in (4, 32, 64, 128):
+        print(f"case: partition invariance, {nseq} sequences", flush=True)
+        inp = make_inputs(w, seqs=range(nseq))
+        out, slot, kind, state, st = run_prefill(w, inp)
+        groups = st.info()["scan_groups"]
+        seen.add(groups)
+        got = (out[:4], slot[:4], kind[:4], {k: state[k][:4].cpu() for k in ("key_sum", "val_sum", "count", "rho",
+                                                                           "key_read", "val_read")})
+        if ref is None:
+            ref = got
+            continue
+        assert np.array_equal(ref[0], got[0]), f"outputs differ ({groups} vs first)"
+        assert np.array_equal(ref[1], got[1]) and np.array_equal(ref[2], got[2]), "decisions differ"
+        for key in ref[3]:
+            assert torch.equal(ref[3][key], got[3][key]), key
+    assert seen == {8, 4, 2, 1}, seen
