@@ -20,6 +20,8 @@ region).  The line also carries:
   decode        the batched-decode workload (64 x 16 sequences, sqrt state
                 prefilled with 16384 tokens): per-step time of the decode
                 kernels and their algorithmic HBM bytes per step.
+  attn_alone    the attention kernel alone on the chip (serial prefill, outside the
+                timed steps): context for the roofline, whose launches share the chip.
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -167,6 +169,42 @@ def bench_prefill(w, steps: int, warmup: int):
         prof[key + "_ms"] = other[key + "_ms"] * steps / 2   # per timed step, like attn_ms
     prof["final_rows"] = st.info()["rows"]
     return cfg, ms_step, prof, (q, k, v, g)
+
+
+def bench_attn_alone(w, tensors, steps: int):
+    """The attention kernel with the chip to itself: the same prefill with KVM_FLAG_SERIAL_PREFILL
+    (every absorption first, then the attention of all query chunks in one launch on the same
+    stream).  Context for the main roofline, whose launches share the chip with the scan."""
+    import torch
+    from compressed_kv_state_amd import KvmConfig, KvmState
+    q, k, v, g = tensors
+    cfg = KvmConfig.of(w, max_tokens=w.n_tokens)
+    cfg.serial_prefill = True
+    st = KvmState(cfg)
+    out = torch.empty_like(q)
+    st.reset()
+    st.prefill(q, k, v, g, out)
+    torch.cuda.synchronize()
+    st.profile(2)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.reset()
+        st.prefill(q, k, v, g, out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = st.profile_read()
+    st.profile(False)
+    st.check()
+    launches = max(prof["attn_launches"], 1)
+    ms = prof["attn_ms"] / launches
+    flops = attn_flops(cfg, w.n_tokens) * steps / launches
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"attention alone: {ms:.3f} ms per launch, {achieved:.0f} TFLOP/s")
+    return {"kernel": ATTN_KERNEL, "ms_per_step": (t1 - t0) * 1e3 / steps, "ms_per_launch": ms,
+            "launches_per_step": launches / steps, "flops_per_launch": flops, "achieved": achieved,
+            "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
+            "note": "serial prefill (KVM_FLAG_SERIAL_PREFILL): the attention runs after the absorption, "
+                    "alone on the chip; not the timed line"}
 
 
 VARIANTS = {"no_value_norm": dict(value_norm=False), "no_sink_protect": dict(sink_protect=False),
@@ -413,6 +451,7 @@ def main():
                                "note": "scan and attention overlap on two streams; phases sum past the step; "
                                        "attn from the timed steps, the others from 2 profiled steps after them"},
     }
+    res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
     if not args.no_variants:
         res["variants"] = bench_variants(wp, tensors, 5)
     del tensors

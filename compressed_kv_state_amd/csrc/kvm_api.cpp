@@ -137,7 +137,8 @@ kvm_status validate(const kvm_config* c) {
   if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale))
     return fail(KVM_E_INVALID_ARG, "softmax_scale must be >= 0");
   if (c->dtype != KVM_F32 && c->dtype != KVM_BF16) return fail(KVM_E_INVALID_ARG, "dtype must be KVM_F32 or KVM_BF16");
-  const uint32_t known = KVM_FLAG_TRACE | KVM_FLAG_NO_VALUE_NORM | KVM_FLAG_NO_SINK_PROTECT | KVM_FLAG_NO_MERGE_GATE;
+  const uint32_t known = KVM_FLAG_TRACE | KVM_FLAG_NO_VALUE_NORM | KVM_FLAG_NO_SINK_PROTECT | KVM_FLAG_NO_MERGE_GATE |
+                         KVM_FLAG_SERIAL_PREFILL;
   if (c->flags & ~known) return fail(KVM_E_INVALID_ARG, "unknown flag bits");
   // Every merged token needs a candidate row: the first chunk with non-sink
   // tokens must be allowed to append at least one row (unprotected sinks are
@@ -449,7 +450,14 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
     if (!st->d.krot) return hipSuccess;
     return timed(st, kPrep, sx, [&] { return kvm::launch_rope_keys(m, st->d, src, sx); });
   };
-  if (a1 > st->absorbed) {
+  if (a1 > st->absorbed && (st->cfg.flags & KVM_FLAG_SERIAL_PREFILL)) {
+    // every absorption first, then all the attention, on the caller's stream
+    err = rope(hs);
+    if (err == hipSuccess)
+      err = timed(st, kScan, hs, [&] { return kvm::launch_scan(m, st->d, src, (int)st->absorbed, (int)a1, hs); });
+    if (err == hipSuccess) err = attn(hs, c_first, c_last);
+    if (err != hipSuccess) return hip_fail(st, err, "scan/attention launch");
+  } else if (a1 > st->absorbed) {
     // Query chunk c reads the state after chunks [0, c - W/C) are absorbed.
     // Fork: the side stream starts after everything queued on hs so far.
     const int64_t wc = m.W / m.C;

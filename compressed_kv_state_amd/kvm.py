@@ -26,6 +26,7 @@ KVM_FLAG_TRACE = 1
 KVM_FLAG_NO_VALUE_NORM = 2
 KVM_FLAG_NO_SINK_PROTECT = 4
 KVM_FLAG_NO_MERGE_GATE = 8
+KVM_FLAG_SERIAL_PREFILL = 16
 SCHED = {"fixed": 0, "sqrt": 1, "saturating": 2, "power": 3}
 DTYPE = {"f32": 0, "bf16": 1}
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -142,6 +143,7 @@ class KvmConfig:
     value_norm: bool = True
     sink_protect: bool = True
     merge_gate: bool = True
+    serial_prefill: bool = False
 
     @property
     def seqs(self) -> int:
@@ -171,7 +173,8 @@ class KvmConfig:
             raise ValueError(f"unknown dtype {self.dtype!r}")
         flags = ((KVM_FLAG_TRACE if self.trace else 0) | (0 if self.value_norm else KVM_FLAG_NO_VALUE_NORM)
                  | (0 if self.sink_protect else KVM_FLAG_NO_SINK_PROTECT)
-                 | (0 if self.merge_gate else KVM_FLAG_NO_MERGE_GATE))
+                 | (0 if self.merge_gate else KVM_FLAG_NO_MERGE_GATE)
+                 | (KVM_FLAG_SERIAL_PREFILL if self.serial_prefill else 0))
         return _Config(self.batch, self.heads, self.head_dim, self.rope_dims, self.chunk, self.window,
                        self.n_sinks, SCHED[self.sched], self.max_slots, self.alpha, self.max_tokens,
                        self.rope_theta, self.ln_eps, self.softmax_scale, DTYPE[self.dtype], flags,

@@ -69,6 +69,13 @@ typedef enum { KVM_SCHED_FIXED = 0, KVM_SCHED_SQRT = 1, KVM_SCHED_SATURATING = 2
 #define KVM_FLAG_NO_SINK_PROTECT 4u  /* sink rows are ordinary rows: surprise references and merge targets */
 #define KVM_FLAG_NO_MERGE_GATE 8u    /* merged tokens are added with weight 1 (gate logits ignored) */
 
+/* Serial prefill: kvm_prefill absorbs every chunk it needs before any
+ * attention, then runs the attention of all its query chunks in one launch,
+ * everything on the caller's stream (no library-owned stream).  Same results
+ * bit for bit; by default the attention of chunks whose state is ready runs
+ * on a second stream beside the rest of the absorption. */
+#define KVM_FLAG_SERIAL_PREFILL 16u
+
 typedef struct kvm_config {
   int32_t batch;          /* B >= 1 */
   int32_t heads;          /* H >= 1; heads are independent sequences */
@@ -85,7 +92,8 @@ typedef struct kvm_config {
   float ln_eps;           /* LayerNorm epsilon for state keys (1e-5) */
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
   int32_t dtype;          /* kvm_dtype of q, k, v, out and of the stored read forms */
-  uint32_t flags;         /* KVM_FLAG_TRACE | KVM_FLAG_NO_VALUE_NORM | KVM_FLAG_NO_SINK_PROTECT | KVM_FLAG_NO_MERGE_GATE */
+  uint32_t flags;         /* KVM_FLAG_TRACE | KVM_FLAG_NO_VALUE_NORM | KVM_FLAG_NO_SINK_PROTECT | KVM_FLAG_NO_MERGE_GATE
+                             | KVM_FLAG_SERIAL_PREFILL */
   double exponent;        /* POWER: growth exponent in (0, 1]; ignored by the other schedules */
 } kvm_config;
 

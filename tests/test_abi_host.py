@@ -63,9 +63,11 @@ def test_all_sinks_first_chunk_needs_room_in_second():
 def test_unknown_flags_and_dtype_rejected():
     lib = K.library()
     c = base().to_c()
-    c.flags = 16
+    c.flags = 32
     n = ctypes.c_size_t()
     assert lib.kvm_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == K.KVM_E_INVALID_ARG
+    c.flags = B.KVM_FLAG_SERIAL_PREFILL | B.KVM_FLAG_TRACE   # known bits pass
+    assert lib.kvm_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == K.KVM_OK
     c = base().to_c()
     c.dtype = 7
     assert lib.kvm_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == K.KVM_E_INVALID_ARG

@@ -303,3 +303,27 @@ def test_scan_row_partition_is_invisible():
         for key in ref[3]:
             assert torch.equal(ref[3][key], got[3][key]), key
     assert seen == {8, 4, 2, 1}, seen
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_serial_prefill_matches_overlapped(dtype):
+    """KVM_FLAG_SERIAL_PREFILL (every absorption, then all the attention, on one stream) gives the
+    default overlapped prefill's results bit for bit."""
+    w = small(dtype, chunk=128, window=256, n_tokens=3000 + 11, heads=4)
+    print(f"case: serial vs overlapped prefill, {dtype}", flush=True)
+    inp = make_inputs(w)
+    res = []
+    for serial in (False, True):
+        cfg = KvmConfig.of(w, max_tokens=w.n_tokens, trace=True)
+        cfg.batch, cfg.heads = w.seqs, 1
+        cfg.serial_prefill = serial
+        st = KvmState(cfg)
+        q, k, v, g = to_gpu(inp, 0, w.n_tokens)
+        out = st.prefill(q, k, v, g)
+        state = st.read(trace=True)
+        torch.cuda.synchronize()
+        st.check()
+        res.append((out.cpu(), {k_: t.cpu() for k_, t in state.items() if torch.is_tensor(t)}))
+    assert torch.equal(res[0][0], res[1][0])
+    for key in ("key_sum", "val_sum", "count", "rho", "key_read", "val_read", "trace_slot", "trace_kind"):
+        assert torch.equal(res[0][1][key], res[1][1][key]), key
