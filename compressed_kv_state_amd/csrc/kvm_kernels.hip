@@ -200,6 +200,18 @@ struct ScanGeom {
   static constexpr int WG = NW / TS;                  // waves sharing one token group (tile stride)
 };
 
+// Cosine-pass geometry of the row-split scan: a workgroup holds about a
+// quarter of the rows or less, so waves take at most 2 token blocks and more
+// waves share each token group's tiles (better balance over few tiles).
+template <int C, bool PART>
+struct CosGeom : ScanGeom<C> {};
+template <int C>
+struct CosGeom<C, true> : ScanGeom<C> {
+  static constexpr int CTW = ScanGeom<C>::CT < 2 ? ScanGeom<C>::CT : 2;
+  static constexpr int TS = ScanGeom<C>::CT / CTW;
+  static constexpr int WG = ScanGeom<C>::NW / TS;
+};
+
 constexpr int pow2_floor(int x) { return x >= 2 ? 2 * pow2_floor(x / 2) : 1; }
 constexpr int kSink = 0, kAppend = 1, kMerge = 2;
 
@@ -481,7 +493,7 @@ template <typename T, int C, bool PART>
 __device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, C>& ch, const char* unit,
                                          const bf16* ul, int LB, int ntl, int rb, int re, int p, int psh,
                                          float* outv, int* outr, UnitTiles& pre) {
-  using G = ScanGeom<C>;
+  using G = CosGeom<C, PART>;
   constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
   const int tg = w % G::TS, wt = w / G::TS;   // token group, tile lane
@@ -826,6 +838,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           sm.rE[xt] = r;
         }
       }
+      wait_vmem();   // this workgroup's global writes of the previous step, before the row loads below
       lds_barrier();
       if (!sm.xok) break;   // the whole workgroup leaves the chunk loop
     }
@@ -1152,7 +1165,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     nver += C;
     prev_off = (int)ioff;
     last_rows = rows_after;
-    __syncthreads();  // publishes the next chunk's buffer and the step's writes
+    // Publish the next chunk's buffer and the step's writes.  The row-split
+    // kernel reads none of this step's global writes before the next step's
+    // exchange (its unit directions come from LDS), so it needs only an LDS
+    // barrier here; each thread waits for its stores before the barrier that
+    // closes the exchange, by when they have long completed.
+    if constexpr (PART) lds_barrier();
+    else __syncthreads();
   }
   if (ver_lds && j_end > j_begin)
     for (int i = tid; i < last_rows; i += kScanThreads)
