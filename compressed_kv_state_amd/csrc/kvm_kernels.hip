@@ -872,28 +872,28 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     }
     lds_barrier();
 
-    // ---- 3. append the m_j most surprising candidates
+    // ---- 3. append the m_j most surprising candidates.  The lane that
+    // reports a token's rank also places it: a wave's reporting lanes hold
+    // consecutive tokens in lane order, so a ballot and the per-wave counts
+    // give each appended token its place in position order.
     {
       int t;
       const int rank = parallel_rank<C>(sm.key, t);
-      if (rank >= 0) sm.flag[t] = t < sinks ? kSink : (rank < mj ? kAppend : kMerge);
-    }
-    lds_barrier();
-    {
-      // position order of the appended tokens: block prefix count over the chunk
-      const bool ap = tid < C && sm.flag[tid] == kAppend;
+      const bool lead = rank >= 0;
+      const bool ap = lead && t >= sinks && rank < mj;
       const unsigned long long bal = __ballot(ap);
       const int within = __popcll(bal & ((1ull << lane) - 1ull));
       if (lane == 0) sm.wtot[w] = __popcll(bal);
       lds_barrier();
       int off = 0;
       for (int ww = 0; ww < w; ++ww) off += sm.wtot[ww];
-      if (tid < C) {
-        if (tid < sinks) {
-          sm.arow[tid] = R0 + tid;
+      if (lead) {
+        sm.flag[t] = t < sinks ? kSink : (ap ? kAppend : kMerge);
+        if (t < sinks) {
+          sm.arow[t] = R0 + t;
         } else if (ap) {
-          sm.arow[tid] = R0 + sinks + off + within;
-          sm.app_list[off + within] = tid;
+          sm.arow[t] = R0 + sinks + off + within;
+          sm.app_list[off + within] = t;
         }
       }
     }
