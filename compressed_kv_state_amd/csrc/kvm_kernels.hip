@@ -2046,41 +2046,65 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
     }
   }
 
-  // ---- direct global->LDS staging of tile T (each wave a share of the 1 KB transfers)
+  // ---- direct global->LDS staging of tile T (each wave a share of the 1 KB
+  // transfers).  Addresses are a tile-uniform base plus a small per-lane byte
+  // offset (version ids zero-extended), which keeps the per-transfer vector
+  // arithmetic to a few 32-bit operations.
   auto issue = [&](int T, uint8_t* K, uint8_t* V) {
     if (T < n_st) {
       const int r0 = T << 6;
+      const char* pkb = reinterpret_cast<const char*>(pk);
+      const char* pvb = reinterpret_cast<const char*>(pv);
       for (int i = w; i < 4; i += NW) {           // keys: 16 rows x 64 B per transfer
         const int row = 16 * i + (lane >> 2);
-        const int unit = (lane & 3) ^ (row & 3);
+        const uint32_t unit = (uint32_t)((lane & 3) ^ (row & 3));
         const int r = min(r0 + row, S - 1);
-        __builtin_amdgcn_global_load_lds(pk + (size_t)sIdx[r] * 32 + 8 * unit, K + 1024 * i, 16, 0, 0);
+        const char* ks = pkb + ((uint64_t)(uint32_t)sIdx[r] << 6) + 16u * unit;
+        __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
       }
       for (int i = w; i < 8; i += NW) {           // values: 8 rows x 128 B per transfer
         const int row = 8 * i + (lane >> 3);
-        const int unit = (lane & 7) ^ (row & 7);
+        const uint32_t unit = (uint32_t)((lane & 7) ^ (row & 7));
         const int r = min(r0 + row, S - 1);
-        __builtin_amdgcn_global_load_lds(pv + (size_t)sIdx[r] * 64 + 8 * unit, V + 1024 * i, 16, 0, 0);
+        const char* vs = pvb + ((uint64_t)(uint32_t)sIdx[r] << 7) + 16u * unit;
+        __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
       }
     } else {
       const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
-      for (int i = w; i < 8; i += NW) {           // keys and values: 8 keys x 128 B per transfer
-        const int key = 8 * i + (lane >> 3);
-        const int unit = (lane & 7) ^ (key & 7);
-        const int64_t pos = min(k0 + key, hi - 1);
-        const bf16* ks;
-        const bf16* vs;
-        if (pos >= src.p0) {
-          const size_t r = (size_t)(pos - src.p0) * 64;
-          ks = unit < 4 ? krot + pos * 32 + 8 * unit : kin + r + 8 * unit;
-          vs = vin + r + 8 * unit;
-        } else {
-          const size_t r = (size_t)(pos % m.R) * 64;   // ring keys are stored rotated
-          ks = ring_k + r + 8 * unit;
-          vs = ring_v + r + 8 * unit;
+      if (k0 >= src.p0) {
+        // every key of the tile is an input of this call (the usual case)
+        const int last = (int)min((int64_t)63, hi - 1 - k0);
+        const char* kr0 = reinterpret_cast<const char*>(krot + k0 * 32);
+        const char* ki0 = reinterpret_cast<const char*>(kin + (k0 - src.p0) * 64);
+        const char* vi0 = reinterpret_cast<const char*>(vin + (k0 - src.p0) * 64);
+        for (int i = w; i < 8; i += NW) {         // keys and values: 8 keys x 128 B per transfer
+          const int key = 8 * i + (lane >> 3);
+          const uint32_t unit = (uint32_t)((lane & 7) ^ (key & 7));
+          const uint32_t kc = (uint32_t)min(key, last);
+          const char* ks = unit < 4 ? kr0 + (kc * 64u + 16u * unit) : ki0 + (kc * 128u + 16u * unit);
+          const char* vs = vi0 + (kc * 128u + 16u * unit);
+          __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
+      } else {
+        for (int i = w; i < 8; i += NW) {
+          const int key = 8 * i + (lane >> 3);
+          const int unit = (lane & 7) ^ (key & 7);
+          const int64_t pos = min(k0 + key, hi - 1);
+          const bf16* ks;
+          const bf16* vs;
+          if (pos >= src.p0) {
+            const size_t r = (size_t)(pos - src.p0) * 64;
+            ks = unit < 4 ? krot + pos * 32 + 8 * unit : kin + r + 8 * unit;
+            vs = vin + r + 8 * unit;
+          } else {
+            const size_t r = (size_t)(pos % m.R) * 64;   // ring keys are stored rotated
+            ks = ring_k + r + 8 * unit;
+            vs = ring_v + r + 8 * unit;
+          }
+          __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
+        }
       }
     }
   };
@@ -2197,7 +2221,9 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
           acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * ((2 * kk + h) ^ kswz_w)), qf[kk], acc);
         const int64_t ks = k0 + kb;
         // key ks + off is valid for this lane's query iff off < lim
-        if (ks + 31 >= hi || ks + 31 > qfirst) mask(acc, (int)min(hi - ks, qpos - ks + 1));
+        // (32-bit per lane: the query's offset 32 w + jl in the chunk plus the
+        // uniform distance from the key tile to the chunk start)
+        if (ks + 31 >= hi || ks + 31 > qfirst) mask(acc, min((int)(hi - ks), (int)(cpos - ks) + 32 * w + jl + 1));
       };
       qk(0, a0);
       if (two) qk(32, a1);
