@@ -393,6 +393,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attn-alone", action="store_true",
+                    help="skip the serial-prefill attention measurement (e.g. for counter runs of the timed launches)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true", help="add a 1 GiB device copy (counter scaling)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
@@ -451,7 +453,8 @@ def main():
                                "note": "scan and attention overlap on two streams; phases sum past the step; "
                                        "attn from the timed steps, the others from 2 profiled steps after them"},
     }
-    res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
+    if not args.no_attn_alone:
+        res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
     if not args.no_variants:
         res["variants"] = bench_variants(wp, tensors, 5)
     del tensors
