@@ -2159,19 +2159,21 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
     }
     lrun = ls;
   };
-  // O^T += V^T . P^T over the 32 keys [kb, kb + 32) of the staged tile
-  auto pv_acc = [&](const uint8_t* V, int kb, const bf16x8& pf0, const bf16x8& pf1) {
+  // O^T += V^T . P^T over the 32 keys [kb, kb + 32) of the staged tile.  The
+  // V^T fragment of (dt, b) = (0, 0) can be read ahead (vfrag) so that its
+  // LDS latency passes during the softmax.
+  auto vfrag = [&](const uint8_t* V, int kb, int dt, int b) {
+    const uint8_t* base = V + (kb + 16 * b) * 128 + voff[dt];
+    const bf16x4 lo4 = ds_read_tr(base);
+    const bf16x4 hi4 = ds_read_tr(base + 8 * 128);
+    return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  };
+  auto pv_acc = [&](const uint8_t* V, int kb, const bf16x8& pf0, const bf16x8& pf1, const bf16x8& v00) {
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       f32x16& O = dt ? O1 : O0;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint8_t* base = V + (kb + 16 * b) * 128 + voff[dt];
-        const bf16x4 lo4 = ds_read_tr(base);
-        const bf16x4 hi4 = ds_read_tr(base + 8 * 128);
-        const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        O = mfma_bf16(a, b ? pf1 : pf0, O);
-      }
+      for (int b = 0; b < 2; ++b) O = mfma_bf16(dt == 0 && b == 0 ? v00 : vfrag(V, kb, dt, b), b ? pf1 : pf0, O);
     }
   };
   // masks keys at offsets >= lim of a 32-key subtile (this lane's rows 8(r/4) + 4h + r%4)
@@ -2228,10 +2230,11 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
       qk(0, a0);
       if (two) qk(32, a1);
     }
+    const bf16x8 v00 = vfrag(V, 0, 0, 0);   // in flight during the softmax
     bf16x8 pf[4];
     softmax(a0, a1, two, pf);
-    pv_acc(V, 0, pf[0], pf[1]);
-    if (two) pv_acc(V, 32, pf[2], pf[3]);
+    pv_acc(V, 0, pf[0], pf[1], v00);
+    if (two) pv_acc(V, 32, pf[2], pf[3], vfrag(V, 32, 0, 0));
   };
 
   // ---- two-stage pipeline; each barrier also waits for the wave's own transfers
