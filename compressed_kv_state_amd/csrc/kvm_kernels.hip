@@ -253,7 +253,8 @@ struct ScanSmem {
   int ver_cur[kVerCap];           // current version id of every row (own rows kept current)
 };
 
-// Polls of an exchange record before a scan workgroup gives up (~1 s): the
+// Polls of an exchange record before a scan workgroup gives up (each poll is a
+// memory round trip, so a few seconds): the
 // workgroups of a sequence are all resident unless other kernels hold the
 // CUs, which they release; the limit only guarantees that every wave ends.
 constexpr int kSpinLimit = 1 << 22;

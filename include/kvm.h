@@ -202,8 +202,8 @@ kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info);
 /* Check that every absorption scan queued so far on this state finished its
  * work.  When a sequence's state rows are split over several workgroups (a
  * state with few sequences), the workgroups meet once per absorbed chunk to
- * combine their best-matching rows; a workgroup that waits there for about a
- * second gives up, so that no kernel can hang, and marks the state.  This
+ * combine their best-matching rows; a workgroup that waits there for a few
+ * seconds gives up, so that no kernel can hang, and marks the state.  This
  * call copies that mark to the host and synchronises `stream`.
  * Errors: KVM_E_INVALID_ARG; KVM_E_HIP if a scan gave up (the state is then
  * poisoned) or on a HIP failure. */
