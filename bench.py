@@ -20,6 +20,7 @@ region).  The line also carries:
   decode        the batched-decode workload (64 x 16 sequences, sqrt state
                 prefilled with 16384 tokens): per-step time of the decode
                 kernels and their algorithmic HBM bytes per step.
+  other_workloads  prefill time of the 120M-shaped and the long workloads (context).
   attn_alone    the attention kernel alone on the chip (serial prefill, outside the
                 timed steps): context for the roofline, whose launches share the chip.
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
@@ -205,6 +206,38 @@ def bench_attn_alone(w, tensors, steps: int):
             "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
             "note": "serial prefill (KVM_FLAG_SERIAL_PREFILL): the attention runs after the absorption, "
                     "alone on the chip; not the timed line"}
+
+
+def bench_other_workloads(steps: int):
+    """Prefill time of the other prefill workloads (the 120M-shaped fixed state and the long
+    saturating one): context beside the main line, not part of it."""
+    import torch
+    from compressed_kv_state_amd import KvmConfig, KvmState
+    from kvm_inputs import WORKLOADS, make_inputs
+    res = {}
+    for w in (WORKLOADS[1], WORKLOADS[3]):
+        inp = make_inputs(w)
+        q, k, v, g = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
+        del inp
+        st = KvmState(KvmConfig.of(w, max_tokens=w.n_tokens))
+        out = torch.empty_like(q)
+        st.reset()
+        st.prefill(q, k, v, g, out)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.reset()
+            st.prefill(q, k, v, g, out)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        st.check()
+        info = st.info()
+        res[w.name] = {"ms_per_step": ms, "tokens_per_s": w.seqs * w.n_tokens / (ms * 1e-3),
+                       "sequences": w.seqs, "n_tokens": w.n_tokens, "final_rows": info["rows"],
+                       "scan_groups": info["scan_groups"]}
+        log(f"{w.name}: {ms:.3f} ms per prefill")
+        del st, out, q, k, v, g
+    return res
 
 
 VARIANTS = {"no_value_norm": dict(value_norm=False), "no_sink_protect": dict(sink_protect=False),
@@ -393,6 +426,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-attn-alone", action="store_true",
                     help="skip the serial-prefill attention measurement (e.g. for counter runs of the timed launches)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -457,6 +491,8 @@ def main():
         res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
     if not args.no_variants:
         res["variants"] = bench_variants(wp, tensors, 5)
+    if not args.no_other:
+        res["other_workloads"] = bench_other_workloads(3)
     del tensors
     if not args.no_decode:
         res["decode"] = bench_decode(wd, args.decode_steps)

@@ -79,7 +79,7 @@ struct Src {
   int64_t n_call;
 };
 
-// Rows of unit directions a scan workgroup keeps in LDS (bf16 path; 0 on the fp32 path).
+// Rows of unit directions a row-split scan workgroup keeps in LDS (bf16 path; 0 on the fp32 path).
 int scan_lds_rows(int C, bool is_bf16);
 hipError_t launch_init(const Dims& m, const Dev& d, double rope_theta, hipStream_t st);
 // Absorb chunks [j_begin, j_end) for every sequence (sequential over j inside the kernel).

@@ -234,12 +234,17 @@ struct ScanChunk {
   float kn[C];              // |k live|
 };
 
-template <typename T, int C>
+// PART: the row-split kernel, which keeps the version ids of its sink and own
+// rows only (at most C + 512: the host splits only when a workgroup's rows
+// fit its LDS cache of at most 512 rows), indexed by vslot.
+template <typename T, int C, bool PART = false>
 struct ScanSmem {
+  static constexpr int RW = CosGeom<C, PART>::WG;   // waves whose bests the cosine pass combines
+  static constexpr int VC = PART ? C + 512 : kVerCap;
   ScanChunk<T, C> ch[ScanBuf<T, C>::NBUF];
   alignas(16) uint32_t key[C];    // sort keys
-  float red_v[ScanGeom<C>::NW][C];
-  int red_r[ScanGeom<C>::NW][C];
+  float red_v[RW][C];
+  int red_r[RW][C];
   float bE[C];
   int rE[C];
   float bA[C];
@@ -250,7 +255,7 @@ struct ScanSmem {
   int app_list[C];
   int wtot[ScanGeom<C>::NW];
   int xok;                        // 0 after a wait at the exchange timed out
-  int ver_cur[kVerCap];           // current version id of every row (own rows kept current)
+  int ver_cur[VC];                // current version id of every (own) row
 };
 
 // Polls of an exchange record before a scan workgroup gives up (each poll is a
@@ -419,9 +424,9 @@ struct UnitTiles {
   bf16x8 a0[4], a1[4];
 };
 constexpr int UL_PITCH = 72;
-template <typename T, int C>
+template <typename T, int C, bool PART = false>
 struct ScanUnitLds {
-  static constexpr int avail = 163840 - (int)sizeof(ScanSmem<T, C>) - 512;
+  static constexpr int avail = 163840 - (int)sizeof(ScanSmem<T, C, PART>) - 512;
   static constexpr int fit = avail / (UL_PITCH * 2);
   static constexpr int NL = !Is<T>::bf ? 0 : (fit >= 512 ? 512 : (fit > 0 ? fit & ~31 : 0));   // rows
 };
@@ -491,7 +496,7 @@ __device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, in
 // tiles cos_preload fetched for the same rows.  PART: the rows are split over
 // several workgroups and every own row is LDS-resident (ntl == own tiles).
 template <typename T, int C, bool PART>
-__device__ __forceinline__ void cos_best(ScanSmem<T, C>& sm, const ScanChunk<T, C>& ch, const char* unit,
+__device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChunk<T, C>& ch, const char* unit,
                                          const bf16* ul, int LB, int ntl, int rb, int re, int p, int psh,
                                          float* outv, int* outr, UnitTiles& pre) {
   using G = CosGeom<C, PART>;
@@ -650,8 +655,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   constexpr int REL = 16 / sizeof(RT);     // read-form elements per 16-byte piece
   constexpr int NBUF = ScanBuf<T, C>::NBUF;
   constexpr int TP = (4 * C + kScanThreads - 1) / kScanThreads;   // token groups of four lanes per thread
-  __shared__ ScanSmem<T, C> sm;
-  constexpr int NL = ScanUnitLds<T, C>::NL;
+  __shared__ ScanSmem<T, C, PART> sm;
+  constexpr int NL = ScanUnitLds<T, C, PART>::NL;
   __shared__ alignas(16) bf16 ul[NL > 0 ? NL : 1][UL_PITCH];
   // Workgroup p of the P = 2^psh that share sequence s (each owns every P-th
   // 32-row tile of the rows from LB on).  With the sequence count a multiple
@@ -679,6 +684,11 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if constexpr (PART) return r < LB ? p == 0 : (((r - LB) >> 5) & (m.P - 1)) == p;
     else return true;
   };
+  // slot of an own row's current version id in LDS
+  auto vslot = [&](int r) {
+    if constexpr (PART) return r < LB ? r : LB + own_slot(r, LB, psh);
+    else return r;
+  };
 
   float* key_sum = d.key_sum + (size_t)s * m.S_cap * 32;
   float* val_sum = d.val_sum + (size_t)s * m.S_cap * 64;
@@ -697,11 +707,12 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   int nver = d.nver[s];
   // the current version of every row lives in LDS; each chunk's index list is
   // written out from it at the start of the next step (stores only)
-  const bool ver_lds = m.S_cap <= kVerCap;
+  const bool ver_lds = PART || m.S_cap <= kVerCap;
   if (ver_lds && j_begin > 0 && j_begin < j_end) {
     const int r0 = sched[j_begin].z;
     const int* prev = idx + sched[j_begin - 1].w;
-    for (int i = tid; i < r0; i += kScanThreads) sm.ver_cur[i] = prev[i];
+    for (int i = tid; i < r0; i += kScanThreads)
+      if (own(i)) sm.ver_cur[vslot(i)] = prev[i];
   }
 
   // unit directions kept in LDS: the first NL rows of the workgroup's own
@@ -746,7 +757,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // index list of the previous step (its rows are the R0 rows before this chunk)
     if (ver_lds && j > j_begin)
       for (int i = tid; i < R0; i += kScanThreads)
-        if (own(i)) idx[prev_off + i] = sm.ver_cur[i];
+        if (own(i)) idx[prev_off + i] = sm.ver_cur[vslot(i)];
 
     // ---- 1. the chunk, its key norms and gates are in LDS buffer `cur` (one
     // buffer: store it now); the first unit-direction tiles of the surprise
@@ -1148,7 +1159,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       }
       if (sub == 0) {
         prho[ver] = rh;
-        if (ver_lds) sm.ver_cur[row] = ver;
+        if (ver_lds) sm.ver_cur[vslot(row)] = ver;
         else idx[ioff + row] = ver;
       }
     }
@@ -1176,7 +1187,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   }
   if (ver_lds && j_end > j_begin)
     for (int i = tid; i < last_rows; i += kScanThreads)
-      if (own(i)) idx[prev_off + i] = sm.ver_cur[i];
+      if (own(i)) idx[prev_off + i] = sm.ver_cur[vslot(i)];
   if (tid == 0 && p == 0) d.nver[s] = nver;
 }
 
@@ -2588,10 +2599,10 @@ hipError_t launch_init(const Dims& m, const Dev& d, double theta, hipStream_t st
 int scan_lds_rows(int C, bool is_bf16) {
   if (!is_bf16) return 0;
   switch (C) {
-    case 32: return ScanUnitLds<bf16, 32>::NL;
-    case 64: return ScanUnitLds<bf16, 64>::NL;
-    case 128: return ScanUnitLds<bf16, 128>::NL;
-    case 256: return ScanUnitLds<bf16, 256>::NL;
+    case 32: return ScanUnitLds<bf16, 32, true>::NL;
+    case 64: return ScanUnitLds<bf16, 64, true>::NL;
+    case 128: return ScanUnitLds<bf16, 128, true>::NL;
+    case 256: return ScanUnitLds<bf16, 256, true>::NL;
     default: return 0;
   }
 }

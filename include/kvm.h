@@ -205,8 +205,8 @@ kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info);
  * combine their best-matching rows; a workgroup that waits there for a few
  * seconds gives up, so that no kernel can hang, and marks the state.  This
  * call copies that mark to the host and synchronises `stream`.
- * Errors: KVM_E_INVALID_ARG; KVM_E_HIP if a scan gave up (the state is then
- * poisoned) or on a HIP failure. */
+ * Errors: KVM_E_INVALID_ARG; KVM_E_STATE if the state is already poisoned;
+ * KVM_E_HIP if a scan gave up (the state is then poisoned) or on a HIP failure. */
 kvm_status kvm_state_check(kvm_state* st, void* stream);
 
 /* Return the state to position 0 with an empty compressed state (the RoPE and
