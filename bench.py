@@ -20,6 +20,8 @@ region).  The line also carries:
   decode        the batched-decode workload (64 x 16 sequences, sqrt state
                 prefilled with 16384 tokens): per-step time of the decode
                 kernels and their algorithmic HBM bytes per step.
+  scan          the absorption scan's time per chunk step and its input bytes against
+                HBM (it is latency-bound: sequential over chunks).
   other_workloads  prefill time of the 120M-shaped and the long workloads (context).
   attn_alone    the attention kernel alone on the chip (serial prefill, outside the
                 timed steps): context for the roofline, whose launches share the chip.
@@ -169,6 +171,7 @@ def bench_prefill(w, steps: int, warmup: int):
     for key in ("scan", "ring", "prep"):
         prof[key + "_ms"] = other[key + "_ms"] * steps / 2   # per timed step, like attn_ms
     prof["final_rows"] = st.info()["rows"]
+    prof["scan_groups"] = st.info()["scan_groups"]
     return cfg, ms_step, prof, (q, k, v, g)
 
 
@@ -487,6 +490,17 @@ def main():
                                "note": "scan and attention overlap on two streams; phases sum past the step; "
                                        "attn from the timed steps, the others from 2 profiled steps after them"},
     }
+    # the absorption scan: sequential over chunks, so latency-bound; its input bytes per
+    # absorbed token (live key 64 B + value 128 B + gate logit 4 B, bf16) against HBM
+    absorbed = max(0, (wp.n_tokens - 1) // wp.chunk - wp.window // wp.chunk)   # chunks the prefill absorbs
+    scan_ms = prof["scan_ms"] / args.steps
+    in_bytes = wp.seqs * absorbed * wp.chunk * (64 + 128 + 4)
+    res["scan"] = {"kernel": "scan_kernel", "bound": "latency (sequential over chunks)",
+                   "ms_per_step": scan_ms, "chunk_steps": absorbed,
+                   "us_per_chunk_step": scan_ms * 1e3 / max(absorbed, 1),
+                   "workgroups_per_sequence": prof.get("scan_groups"),
+                   "input_bytes_per_step": in_bytes, "achieved_GBs": in_bytes / (scan_ms * 1e-3) / 1e9,
+                   "peak_GBs": PEAK_HBM_GBS, "frac": in_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if not args.no_attn_alone:
         res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
     if not args.no_variants:
