@@ -168,18 +168,23 @@ __global__ void rope_table_kernel(float* cosv, float* sinv, int64_t max_tokens, 
 // [KVM summary, Core mechanisms 3]: the least redundant overflowed tokens are
 //   appended as new rows; the count m_j comes from the size schedule.
 // [KVM summary, Core mechanisms 5]: the first tokens become protected sinks.
-// One workgroup (8 waves) per sequence, sequential over chunks.  Per chunk:
+// One workgroup (8 waves) per sequence, or P of them sharing a sequence's
+// rows (every P-th 32-row tile each; see scan_kernel), sequential over chunks.
+// Per chunk:
 //   1. the chunk's live keys, values and gates are in LDS (loaded into
 //      registers during the previous step, stored at its end);
 //   2. surprise: best cosine of every token against the non-sink rows that
 //      existed before the chunk (MFMA over row tiles, next tile prefetched);
+//      with P > 1 each workgroup takes its own rows and the P bests per token
+//      are exchanged through memory;
 //   3. append the m_j tokens of smallest (surprise, position) (parallel rank);
 //   4. best cosine against the just-appended rows; assignment = better of the
 //      two (lower row on ties);
 //   5. the four lanes of the first token on each touched row (the creating
 //      token for a new row) find the row's tokens by scanning the chunk's
 //      targets, add them in position order (deterministic, no atomics) and
-//      write the row's new read-form version.
+//      write the row's new read-form version (with P > 1, only for the rows
+//      the workgroup owns; steps 3 and 4 run identically in every workgroup).
 // Cosines: argmax over rows of cos(k, K_i) = argmax of dot(k, K_i/|K_i|).  On
 // the bf16 path k is exact in bf16 and the unit direction U_i = K_i/|K_i| is
 // split into bf16 hi + lo (|U - hi - lo| <= 2^-18 |U|), so two bf16 MFMA
