@@ -606,13 +606,32 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
   lds_barrier();
   const int nw = min(nown, G::WG);
   for (int t = tid; t < C; t += G::NT) {
+    if constexpr (G::WG < 4) {   // two waves: a short loop (and fewer live registers)
+      float v = 0.f;
+      int r = INT_MAX;
+      for (int ww = 0; ww < nw; ++ww) {
+        const float ov = sm.red_v[ww][t];
+        const int orow = sm.red_r[ww][t];
+        if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
+      }
+      outv[t] = v;
+      outr[t] = r;
+      continue;
+    }
+    // every wave's partial is read first (independent LDS reads in flight
+    // together), then combined; slots of waves without tiles are skipped
+    float pv[G::WG];
+    int pr[G::WG];
+#pragma unroll
+    for (int ww = 0; ww < G::WG; ++ww) {
+      pv[ww] = sm.red_v[ww][t];
+      pr[ww] = sm.red_r[ww][t];
+    }
     float v = 0.f;
     int r = INT_MAX;
-    for (int ww = 0; ww < nw; ++ww) {
-      const float ov = sm.red_v[ww][t];
-      const int orow = sm.red_r[ww][t];
-      if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
-    }
+#pragma unroll
+    for (int ww = 0; ww < G::WG; ++ww)
+      if (ww < nw && (pv[ww] > v || (pv[ww] == v && pr[ww] < r))) { v = pv[ww]; r = pr[ww]; }
     outv[t] = v;
     outr[t] = r;
   }
