@@ -1962,6 +1962,22 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
 }
 
+// LDS swizzles of the staged attention tiles: a row's 16-byte unit u is
+// stored at u XOR swz(row).  Each is chosen so that the lanes served in one
+// LDS cycle hit distinct banks, whether a cycle serves 128 or 256 bytes:
+//  - state keys (64-byte rows, ds_read_b128 by key row): the 8 or 16
+//    consecutive rows of a cycle get distinct (row mod 2 or 4, unit) pairs;
+//  - window keys (128-byte rows, ds_read_b128 by key row): likewise for
+//    (row mod 1 or 2, unit) over 8 or 16 consecutive rows;
+//  - values (128-byte rows, ds_read_b64_tr_b16): the 16 lanes of a cycle
+//    read four rows two units each, so rows 0..3 (and 4..7) must land on
+//    disjoint unit pairs.
+// The previous row & mask swizzles measured ~50 M conflict cycles per
+// 350M-workload launch; these measure none.
+__device__ __forceinline__ int swz_sk(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+__device__ __forceinline__ int swz_wk(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src src, int64_t c_begin, int n_q,
                                                               int64_t end_pos, bf16* out) {
@@ -2067,10 +2083,10 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
   const bf16* ring_v = reinterpret_cast<const bf16*>(d.ring_v) + (size_t)s * m.R * 64;
 
   // ---- lane-constant LDS offsets
-  // K operand: key kb + jl, 16-byte unit 2kk + h, swizzled by the key's low bits
-  const int kswz_w = jl & 7, kswz_s = jl & 3;
+  // K operand: key kb + jl, 16-byte unit 2kk + h, swizzled (swz_wk / swz_sk)
+  const int kswz_w = swz_wk(jl), kswz_s = swz_sk(jl);
   // V operand (transposed read): group g = lane/16 supplies keys 4h + (lane%16)/4 and
-  // dims 32dt + 16(g%2) + 4(lane%4); unit index swizzled by the key's low bits
+  // dims 32dt + 16(g%2) + 4(lane%4); unit index swizzled (swz_v)
   int voff[2];
   {
     const int g = lane >> 4, p = lane & 15;
@@ -2078,7 +2094,7 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       const int d0 = 32 * dt + 16 * (g & 1) + 4 * (p & 3);
-      voff[dt] = kl * 128 + 16 * ((d0 >> 3) ^ kl) + 8 * ((d0 >> 2) & 1);
+      voff[dt] = kl * 128 + 16 * ((d0 >> 3) ^ swz_v(kl)) + 8 * ((d0 >> 2) & 1);
     }
   }
 
@@ -2093,14 +2109,14 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
       const char* pvb = reinterpret_cast<const char*>(pv);
       for (int i = w; i < 4; i += NW) {           // keys: 16 rows x 64 B per transfer
         const int row = 16 * i + (lane >> 2);
-        const uint32_t unit = (uint32_t)((lane & 3) ^ (row & 3));
+        const uint32_t unit = (uint32_t)((lane & 3) ^ swz_sk(row));
         const int r = min(r0 + row, S - 1);
         const char* ks = pkb + ((uint64_t)(uint32_t)sIdx[r] << 6) + 16u * unit;
         __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
       }
       for (int i = w; i < 8; i += NW) {           // values: 8 rows x 128 B per transfer
         const int row = 8 * i + (lane >> 3);
-        const uint32_t unit = (uint32_t)((lane & 7) ^ (row & 7));
+        const uint32_t unit = (uint32_t)((lane & 7) ^ swz_v(row));
         const int r = min(r0 + row, S - 1);
         const char* vs = pvb + ((uint64_t)(uint32_t)sIdx[r] << 7) + 16u * unit;
         __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
@@ -2115,28 +2131,30 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
         const char* vi0 = reinterpret_cast<const char*>(vin + (k0 - src.p0) * 64);
         for (int i = w; i < 8; i += NW) {         // keys and values: 8 keys x 128 B per transfer
           const int key = 8 * i + (lane >> 3);
-          const uint32_t unit = (uint32_t)((lane & 7) ^ (key & 7));
+          const uint32_t unit = (uint32_t)((lane & 7) ^ swz_wk(key));
+          const uint32_t vunit = (uint32_t)((lane & 7) ^ swz_v(key));
           const uint32_t kc = (uint32_t)min(key, last);
           const char* ks = unit < 4 ? kr0 + (kc * 64u + 16u * unit) : ki0 + (kc * 128u + 16u * unit);
-          const char* vs = vi0 + (kc * 128u + 16u * unit);
+          const char* vs = vi0 + (kc * 128u + 16u * vunit);
           __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
           __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
         }
       } else {
         for (int i = w; i < 8; i += NW) {
           const int key = 8 * i + (lane >> 3);
-          const int unit = (lane & 7) ^ (key & 7);
+          const int unit = (lane & 7) ^ swz_wk(key);
+          const int vunit = (lane & 7) ^ swz_v(key);
           const int64_t pos = min(k0 + key, hi - 1);
           const bf16* ks;
           const bf16* vs;
           if (pos >= src.p0) {
             const size_t r = (size_t)(pos - src.p0) * 64;
             ks = unit < 4 ? krot + pos * 32 + 8 * unit : kin + r + 8 * unit;
-            vs = vin + r + 8 * unit;
+            vs = vin + r + 8 * vunit;
           } else {
             const size_t r = (size_t)(pos % m.R) * 64;   // ring keys are stored rotated
             ks = ring_k + r + 8 * unit;
-            vs = ring_v + r + 8 * unit;
+            vs = ring_v + r + 8 * vunit;
           }
           __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
           __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
