@@ -911,8 +911,15 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // ---- 3. append the m_j most surprising candidates.  The lane that
     // reports a token's rank also places it: a wave's reporting lanes hold
     // consecutive tokens in lane order, so a ballot and the per-wave counts
-    // give each appended token its place in position order.
-    {
+    // give each appended token its place in position order.  Without appends
+    // (a full fixed or saturated state) every non-sink token merges and no
+    // rank is needed (m_j is the same for the whole workgroup).
+    if (mj == 0) {
+      for (int t = tid; t < C; t += kScanThreads) {
+        sm.flag[t] = t < sinks ? kSink : kMerge;
+        if (t < sinks) sm.arow[t] = R0 + t;
+      }
+    } else {
       int t;
       const int rank = parallel_rank<C>(sm.key, t);
       const bool lead = rank >= 0;
