@@ -947,44 +947,47 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // New row R0 + e was created by token e (a sink, e < sinks) or by the
     // (e - sinks)-th appended token; sink rows are candidates only unprotected.
     const int e0 = m.unprot ? 0 : sinks;
-    for (int t = tid >> 2; t < C; t += kScanThreads / 4) {
-      const int sub = tid & 3;
-      float best = -kInf;
-      int brow = INT_MAX;
-      if (sm.flag[t] == kMerge && nc > e0) {
-        float kt[32];
+    const bool new_rows = nc > e0;   // candidates among this step's new rows (uniform)
+    if (new_rows) {
+      for (int t = tid >> 2; t < C; t += kScanThreads / 4) {
+        const int sub = tid & 3;
+        float best = -kInf;
+        int brow = INT_MAX;
+        if (sm.flag[t] == kMerge) {
+          float kt[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
-        for (int e = e0 + sub; e < nc; e += 4) {
-          const int s2 = e < sinks ? e : sm.app_list[e - sinks];
-          // four partial sums (dims i mod 4) keep the dependent chains short
-          float dp[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
+          for (int e = e0 + sub; e < nc; e += 4) {
+            const int s2 = e < sinks ? e : sm.app_list[e - sinks];
+            // four partial sums (dims i mod 4) keep the dependent chains short
+            float dp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 32; ++i) dp[i & 3] = fmaf(kt[i], tof(Kc[s2][i]), dp[i & 3]);
-          const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
-          const float nk = chc.kn[s2];
-          const float val = nk > 0.f ? dot * __builtin_amdgcn_rcpf(nk) : 0.f;   // 1 ulp
-          if (val > best) { best = val; brow = R0 + e; }
+            for (int i = 0; i < 32; ++i) dp[i & 3] = fmaf(kt[i], tof(Kc[s2][i]), dp[i & 3]);
+            const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
+            const float nk = chc.kn[s2];
+            const float val = nk > 0.f ? dot * __builtin_amdgcn_rcpf(nk) : 0.f;   // 1 ulp
+            if (val > best) { best = val; brow = R0 + e; }
+          }
+        }
+        {
+          float ob = xor_lane<1>(best);
+          int orow = xor_lane<1>(brow);
+          if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
+          ob = xor_lane<2>(best);
+          orow = xor_lane<2>(brow);
+          if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
+        }
+        if (sub == 0) {
+          sm.bA[t] = best;
+          sm.rA[t] = brow;
         }
       }
-      {
-        float ob = xor_lane<1>(best);
-        int orow = xor_lane<1>(brow);
-        if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
-        ob = xor_lane<2>(best);
-        orow = xor_lane<2>(brow);
-        if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
-      }
-      if (sub == 0) {
-        sm.bA[t] = best;
-        sm.rA[t] = brow;
-      }
+      lds_barrier();
     }
-    lds_barrier();
     const int fallback = ee > eb ? eb : (R0 + sinks);
     for (int t = tid; t < C; t += kScanThreads) {
       if (sm.flag[t] == kMerge) {
-        const bool eok = sm.rE[t] != INT_MAX, aok = sm.rA[t] != INT_MAX;
+        const bool eok = sm.rE[t] != INT_MAX, aok = new_rows && sm.rA[t] != INT_MAX;
         int a;
         if (eok && (!aok || sm.bE[t] >= sm.bA[t])) a = sm.rE[t];
         else if (aok) a = sm.rA[t];
