@@ -220,6 +220,20 @@ struct CosGeom<C, true> : ScanGeom<C> {
 constexpr int pow2_floor(int x) { return x >= 2 ? 2 * pow2_floor(x / 2) : 1; }
 constexpr int kSink = 0, kAppend = 1, kMerge = 2;
 
+// Ranking geometry: P threads per token, each counting the smaller keys in
+// one span of SPAN tokens.  Spans are stored SPAN + 4 words apart so that the
+// P addresses one LDS cycle serves (one per span) fall in different banks.
+template <int C>
+struct RankGeom {
+  static constexpr int NT = ScanGeom<C>::NT;
+  static constexpr int P = pow2_floor(NT / C < C / 4 ? NT / C : C / 4);
+  static constexpr int SPAN = C / P;
+};
+template <int C>
+__device__ __forceinline__ int rank_slot(int t) {
+  return t + 4 * (t / RankGeom<C>::SPAN);
+}
+
 // Chunk buffers: with NBUF = 2 the next chunk is stored into the spare buffer
 // at the end of a step; with one buffer it is stored at the top of its own step.
 template <typename T, int C>
@@ -247,7 +261,7 @@ struct ScanSmem {
   static constexpr int RW = CosGeom<C, PART>::WG;   // waves whose bests the cosine pass combines
   static constexpr int VC = PART ? C + 512 : kVerCap;
   ScanChunk<T, C> ch[ScanBuf<T, C>::NBUF];
-  alignas(16) uint32_t key[C];    // sort keys
+  alignas(16) uint32_t key[C + 4 * RankGeom<C>::P];   // sort keys (padded spans: rank_slot)
   float red_v[RW][C];
   int red_r[RW][C];
   float bE[C];
@@ -256,7 +270,10 @@ struct ScanSmem {
   int rA[C];
   int flag[C];
   int arow[C];        // row each token merges into or creates
-  alignas(16) int mrow[C];   // row of each merged token, -1 for the others
+  // row of each merged token (-1 for the others); the update scans the tokens
+  // in four quarters, stored C/4 + 4 words apart so that the four quarters'
+  // reads of one LDS cycle fall in different banks
+  alignas(16) int mrow[C + 16];
   int app_list[C];
   int wtot[ScanGeom<C>::NW];
   int xok;                        // 0 after a wait at the exchange timed out
@@ -645,16 +662,15 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
 // lane's token in t_out.
 template <int C>
 __device__ __forceinline__ int parallel_rank(const uint32_t* key, int& t_out) {
-  constexpr int NT = ScanGeom<C>::NT;
-  constexpr int P = pow2_floor(NT / C < C / 4 ? NT / C : C / 4);
-  constexpr int SPAN = C / P;
+  using G = RankGeom<C>;
+  constexpr int P = G::P, SPAN = G::SPAN;
   static_assert(SPAN % 4 == 0, "keys are read in fours");
   const int t = threadIdx.x / P, part = threadIdx.x % P;
   t_out = t;
   int cnt = 0;
   if (t < C) {
-    const uint32_t kt = key[t];
-    const u32x4* kp = reinterpret_cast<const u32x4*>(key + part * SPAN);
+    const uint32_t kt = key[rank_slot<C>(t)];
+    const u32x4* kp = reinterpret_cast<const u32x4*>(key + part * (SPAN + 4));
 #pragma unroll
     for (int i = 0; i < SPAN / 4; ++i) {
       const u32x4 k4 = kp[i];
@@ -904,7 +920,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       // key = (surprise to 2^-15, position): smaller = more surprising; sinks
       // never rank.  (The low 8 bits of the ordered surprise give way to the
       // position, C <= 256; surprises that close are a near tie.)
-      sm.key[t] = t < sinks ? ~0u : ((ordered(mu) & ~0xFFu) | (uint32_t)t);
+      sm.key[rank_slot<C>(t)] = t < sinks ? ~0u : ((ordered(mu) & ~0xFFu) | (uint32_t)t);
     }
     lds_barrier();
 
@@ -994,9 +1010,9 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
         sm.arow[t] = a;
-        sm.mrow[t] = a;
+        sm.mrow[t + 4 * (t / (C / 4))] = a;
       } else {
-        sm.mrow[t] = -1;
+        sm.mrow[t + 4 * (t / (C / 4))] = -1;
       }
     }
     lds_barrier();
@@ -1036,7 +1052,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
 #pragma unroll
       for (int q = 0; q < QW; ++q) mk[q] = 0u;
       {
-        const u32x4* m4 = reinterpret_cast<const u32x4*>(sm.mrow + sub * Q);
+        const u32x4* m4 = reinterpret_cast<const u32x4*>(sm.mrow + sub * (Q + 4));
 #pragma unroll
         for (int i = 0; i < Q / 4; ++i) {
           const u32x4 x = m4[i];
