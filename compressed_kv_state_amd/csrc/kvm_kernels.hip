@@ -781,6 +781,10 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   // Within a chunk step threads exchange data through LDS only (LDS barriers,
   // so loads stay in flight); every global write of a step is read by another
   // thread only in a later step, after the barrier that closes the step.
+  // Row-split kernel with two chunk buffers: the next chunk loads during the
+  // surprise pass (which reads LDS only) and is stored into the spare buffer
+  // while the exchange records travel, off the step's critical path.
+  constexpr bool kEarly = PART && NBUF == 2;
   int4 sc_next = j_begin < j_end ? sched[j_begin] : make_int4(0, 0, 0, 0);
   int prev_off = j_begin > 0 ? sched[j_begin - 1].w : 0;
   int last_rows = 0;
@@ -809,6 +813,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // surprise is measured against the non-sink rows that existed before the
     // chunk (every row before the chunk when sinks are unprotected)
     const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
+    if constexpr (kEarly)
+      if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     UnitTiles pre;
     const int ntl = NL > 0 ? lds_tiles(eb, ee, LB, NL, p, psh) : 0;
     if constexpr (Is<T>::bf && !PART) cos_preload<C>(unit, eb, ee, ntl, p, psh, pre);
@@ -840,6 +846,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         const uint64_t x = (uint64_t)__float_as_uint(sm.bE[t]) | ((uint64_t)(r | (tag << 24)) << 32);
         __hip_atomic_store(xb + (size_t)p * C + t, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      if constexpr (kEarly)
+        if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
       // XL lanes per token (a power of two, at most 8): lane sub polls the
       // records of workgroups sub, sub + XL, ...; the group then combines.
       constexpr int XL = kScanThreads / C < 8 ? kScanThreads / C : 8;
@@ -902,10 +910,11 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         if (own(i)) idx[ioff + i] = idx[prev_off + i];
       wait_vmem();
     }
-    // The next chunk loads from here to the end of the step (issued after the
-    // pass: loads complete in order, so a wait for the pass's tiles would also
-    // wait for these).
-    if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
+    // Otherwise the next chunk loads from here to the end of the step (issued
+    // after the pass: loads complete in order, so a wait for the pass's tiles
+    // would also wait for these).
+    if constexpr (!kEarly)
+      if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     for (int t = tid; t < C; t += kScanThreads) {
       // back to the dot product: subtract the key base (exact on (1, 3)) and
       // undo the token's power-of-two scaling
@@ -1222,7 +1231,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       }
     }
     // the next chunk into the spare buffer (chunk j - 1's, no longer read)
-    if constexpr (NBUF == 2)
+    if constexpr (NBUF == 2 && !kEarly)
       if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
     nver += C;
     prev_off = (int)ioff;
