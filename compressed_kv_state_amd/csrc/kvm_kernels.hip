@@ -2522,7 +2522,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
     const int nwk = (int)(t - lo + 1);
     const int per = (nwk + kDecWaves - 1) / kDecWaves;
     const int kb = w * per, ke = min(nwk, kb + per);
-#pragma unroll 2
+    // ring slot of position lo + i0, stepped along with i0 (no 64-bit modulo per key)
+    int slot = (int)((lo + kb + grp) % m.R);
     for (int i0 = kb + grp; i0 < ke; i0 += 64 / L) {
       const int64_t pos = lo + i0;
       float kf[8], vv[8];
@@ -2530,17 +2531,26 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
 #pragma unroll
         for (int i = 0; i < 8; ++i) { kf[i] = skt[8 * e + i]; vv[i] = svt[8 * e + i]; }
       } else {
-        const size_t slot = (size_t)(pos % m.R);
-        alignas(16) T kh[8];
-        alignas(16) T vh[8];
+        // both rows' loads are issued before either is used (one memory
+        // round trip per key batch, not two)
+        constexpr int NQ = 8 * (int)sizeof(T) / 16;
+        uint4 kq[NQ], vq[NQ];
 #pragma unroll
-        for (int i = 0; i < 8; i += 16 / (int)sizeof(T)) {
-          copy16(&kh[i], rk + slot * 64 + 8 * e + i);
-          copy16(&vh[i], rv + slot * 64 + 8 * e + i);
+        for (int i = 0; i < NQ; ++i) {
+          kq[i] = *reinterpret_cast<const uint4*>(rk + (size_t)slot * 64 + 8 * e + i * (16 / (int)sizeof(T)));
+          vq[i] = *reinterpret_cast<const uint4*>(rv + (size_t)slot * 64 + 8 * e + i * (16 / (int)sizeof(T)));
         }
+        const T* kh = reinterpret_cast<const T*>(kq);
+        const T* vh = reinterpret_cast<const T*>(vq);
 #pragma unroll
         for (int i = 0; i < 8; ++i) { kf[i] = tof(kh[i]); vv[i] = tof(vh[i]); }
+        // scheduling order for this block: address arithmetic, the loads, the rest
+        __builtin_amdgcn_sched_group_barrier(0x0002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0020, 2 * NQ, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0002, 64, 0);
       }
+      slot += 64 / L;
+      if (slot >= m.R) slot -= m.R;
       float dot = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) dot = fmaf(qk[i], kf[i], dot);
