@@ -127,6 +127,23 @@ def test_append_everything(dtype):
         oracle_check(w, inp, s, 900, out, slot, kind, state, label="append-all")
 
 
+@pytest.mark.parametrize("chunk,window", [(128, 256), (256, 512)])
+def test_state_past_the_lds_version_list(chunk, window):
+    """Largest states: every absorbed token appended until a snapshot holds more
+    than 8192 rows, past what the staged attention keeps in LDS (those chunks
+    take the register-staged bf16 kernel) and past the scan's LDS version list
+    (index lists in global memory, one scan workgroup per sequence)."""
+    w = small("bf16", heads=2, sched="fixed", max_slots=100000, n_tokens=9472, chunk=chunk, window=window)
+    print(f"case: append everything to > 8192 rows, C {chunk}", flush=True)
+    inp = make_inputs(w)
+    out, slot, kind, state, _ = run_prefill(w, inp)
+    absorbed = w.n_tokens - window - chunk
+    assert np.all(kind[:, :4] == O.KIND_SINK) and np.all(kind[:, 4:absorbed] == O.KIND_APPEND)
+    assert int(state["n_rows"].min()) == absorbed > 8192
+    for s in range(w.seqs):
+        oracle_check(w, inp, s, w.n_tokens, out, slot, kind, state, label="rows>8192")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("logit", [-1e4, 1e4])
 def test_gate_extremes(dtype, logit):
