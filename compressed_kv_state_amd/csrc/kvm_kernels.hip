@@ -2037,7 +2037,11 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
     }
   }
   const int64_t c = c_begin + cl;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, jl = lane & 31, h = lane >> 5;
+  // wave index, made uniform for the compiler: the LDS targets of the
+  // global->LDS transfers (in M0) then come from scalar registers, with no
+  // per-transfer loop over lanes
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t cpos = c * C;
   const int64_t qpos = cpos + 32 * w + jl;
   const bool qvalid = qpos < end_pos;
