@@ -30,7 +30,7 @@ Where the pages leave a step open the plainest reading is taken; each is
 stated at the function that uses it.  "(reading)" marks those places.
 
 Public entry points: gate, rope, capacity, schedule, prefill, decode,
-brute_force, prefill_batch.
+brute_force.
 """
 from __future__ import annotations
 
@@ -69,6 +69,7 @@ class Params:
     value_norm: bool = True        # read values at the row's radius (else the plain mean V/n)
     sink_protect: bool = True      # sink rows are never merge targets nor surprise references
     merge_gate: bool = True        # merged tokens are scaled by sigmoid(l) (else by 1)
+    softmax_scale: float = 0.0     # logit scale; 0 means 1/sqrt(head_dim)
 
     @staticmethod
     def of(cfg) -> "Params":
@@ -78,12 +79,22 @@ class Params:
                       rope_dims=cfg.rope_dims, rope_theta=cfg.rope_theta, ln_eps=cfg.ln_eps,
                       exponent=getattr(cfg, "exponent", 0.5), value_norm=getattr(cfg, "value_norm", True),
                       sink_protect=getattr(cfg, "sink_protect", True),
-                      merge_gate=getattr(cfg, "merge_gate", True))
+                      merge_gate=getattr(cfg, "merge_gate", True),
+                      softmax_scale=getattr(cfg, "softmax_scale", 0.0))
 
 
 # --------------------------------------------------------------------------
 # Elementary pieces
 # --------------------------------------------------------------------------
+
+def logit_scale(p: Params) -> float:
+    """The one softmax scale shared by state and window logits.
+
+    [KVM summary, Methodology]: one softmax attention layer over state and
+    window.  (reading) The usual 1/sqrt(head_dim) unless a scale is given.
+    """
+    return float(p.softmax_scale) if p.softmax_scale > 0 else 1.0 / math.sqrt(p.head_dim)
+
 
 def merge_weights(ell, p: Params):
     """The per-token merge weight: the gate, or 1 without it ([KVM summary,
@@ -175,19 +186,6 @@ def schedule(n_absorbed_chunks: int, p: Params):
         m = min(max(capacity(T, p) - rows, 0), cand)
         rows += m
         out.append((s, m, rows))
-    return out
-
-
-def cosine_rows(x, Y):
-    """cos(x, y_i) for each row y_i of Y; 0 where a norm is 0."""
-    x = np.asarray(x, dtype=np.float64)
-    Y = np.asarray(Y, dtype=np.float64)
-    nx = np.linalg.norm(x)
-    ny = np.linalg.norm(Y, axis=-1)
-    dots = Y @ x
-    out = np.zeros(Y.shape[0], dtype=np.float64)
-    ok = (ny > 0) & (nx > 0)
-    out[ok] = dots[ok] / (ny[ok] * nx)
     return out
 
 
@@ -413,10 +411,10 @@ def attend_one(t: int, q_t, qr_t, khat, vhat, kr, v, p: Params, c: int):
 
     [KVM summary, Methodology; Core mechanisms 4]: a single softmax attention
     layer; the unrotated query scores the state keys, the rotated query scores
-    the window keys.  (reading) Scale 1/sqrt(head_dim) for both parts; the
+    the window keys.  (reading) One scale, logit_scale(p), for both parts; the
     window is [max(0, cC - W), t].
     """
-    s = 1.0 / math.sqrt(p.head_dim)
+    s = logit_scale(p)
     lo = max(0, c * p.chunk - p.window)
     logits_state = s * (khat @ q_t) if khat.shape[0] else np.zeros(0)
     logits_win = s * (kr[lo:t + 1] @ qr_t)
@@ -431,7 +429,7 @@ def attend_one(t: int, q_t, qr_t, khat, vhat, kr, v, p: Params, c: int):
 
 def attend_chunk(c: int, N: int, q, qr, khat, vhat, kr, v, p: Params):
     """attend_one for every query of chunk c at once (same arithmetic, array form)."""
-    s = 1.0 / math.sqrt(p.head_dim)
+    s = logit_scale(p)
     C = p.chunk
     rows = np.arange(c * C, min(N, (c + 1) * C))
     lo = max(0, c * C - p.window)
@@ -605,15 +603,6 @@ def decode(q, k, v, ell, p: Params) -> np.ndarray:
     return np.array([dec.step(q[t], k[t], v[t], ell[t]) for t in range(len(q))])
 
 
-def prefill_batch(q, k, v, ell, p: Params, forced_list=None, keep_snapshots: bool = False):
-    """prefill over independent sequences: q, k, v [S, N, d], ell [S, N]."""
-    res = []
-    for s in range(np.shape(q)[0]):
-        f = forced_list[s] if forced_list is not None else None
-        res.append(prefill(q[s], k[s], v[s], ell[s], p, forced=f, keep_snapshots=keep_snapshots))
-    return res
-
-
 # --------------------------------------------------------------------------
 # Second formulation, for tiny inputs only
 # --------------------------------------------------------------------------
@@ -641,7 +630,7 @@ def brute_force(q, k, v, ell, p: Params) -> np.ndarray:
     kr = rope(k, pos, dr, p.rope_theta)
     kt = k[:, dr:]
     g = gate(ell) if p.merge_gate else np.ones(N)
-    scale = 1.0 / math.sqrt(d)
+    scale = p.softmax_scale if p.softmax_scale > 0 else d ** -0.5
     out = np.zeros((N, v.shape[1]))
     for c in range(-(-N // C)):
         Ks = np.zeros((0, d - dr))

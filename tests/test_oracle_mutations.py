@@ -69,7 +69,7 @@ ALL = [
     pins.check_read_form, lambda m: pins.check_sums_and_counts(m, "random"), pins.check_assignment_rules,
     pins.check_attention_with_state, i9, i13, i11,
     pins.check_no_gate_is_saturated_gate, pins.check_mean_read_without_value_norm, pins.check_unprotected_sinks,
-    pins.check_power_schedule,
+    pins.check_power_schedule, pins.check_softmax_scale,
 ]
 
 MUTANTS = {
@@ -100,7 +100,9 @@ MUTANTS = {
     "power exponent ignored": ("float(T) ** float(p.exponent)", "float(T) ** 0.5"),
     "window one token short": ("lo = max(0, c * C - p.window)\n    keys", "lo = max(0, c * C - p.window + 1)\n    keys"),
     "absorb one chunk late": ("while absorbed <= c - W // C - 1:", "while absorbed <= c - W // C - 2:"),
-    "softmax scale squared": ("s = 1.0 / math.sqrt(p.head_dim)\n    C = p.chunk", "s = 1.0 / p.head_dim\n    C = p.chunk"),
+    "softmax scale squared": ("else 1.0 / math.sqrt(p.head_dim)", "else 1.0 / p.head_dim"),
+    "given softmax scale ignored": ("return float(p.softmax_scale) if p.softmax_scale > 0",
+                                    "return 1.0 / math.sqrt(p.head_dim) if p.softmax_scale > 0"),
     "rotary dims of state keys not zeroed": ("khat = np.zeros((S, d))\n    vhat", "khat = np.ones((S, d))\n    vhat"),
     "capacity floor instead of ceil": ("return r if r * r == x else r + 1", "return r"),
     "radius of the current sum": ("self.rho.append(float(np.linalg.norm(v)))", "self.rho.append(1.0)"),

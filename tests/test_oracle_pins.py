@@ -50,11 +50,11 @@ def rope_complex(x, pos, rope_dims=32, theta=10000.0):
     return out
 
 
-def sdpa(qm, km, vm, mask):
+def sdpa(qm, km, vm, mask, scale=None):
     """torch scaled_dot_product_attention in float64 on the CPU."""
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
     m = torch.from_numpy(mask)[None, None]
-    return F.scaled_dot_product_attention(t(qm), t(km), t(vm), attn_mask=m)[0, 0].numpy()
+    return F.scaled_dot_product_attention(t(qm), t(km), t(vm), attn_mask=m, scale=scale)[0, 0].numpy()
 
 
 # ---------------------------------------------------------------- gate
@@ -174,6 +174,32 @@ def check_append_everything(mod):
 
 def test_I2_append_everything_is_dense_attention_on_normalised_keys():
     check_append_everything(O)
+
+
+def check_softmax_scale(mod):
+    """A given logit scale replaces 1/sqrt(head_dim) for state and window logits alike:
+    the append-everything layer equals torch SDPA with that scale."""
+    N, C, W, ns, sc = 60, 8, 16, 2, 0.37
+    p = mod.Params(chunk=C, window=W, n_sinks=ns, sched="fixed", max_slots=10_000, softmax_scale=sc)
+    q, k, v, ell = rand_seq(N, 13)
+    res = mod.prefill(q, k, v, ell, p)
+    pos = np.arange(N)
+    qr, kr = rope_complex(q, pos), rope_complex(k, pos)
+    kt = torch.from_numpy(k[:, 32:])
+    khat = np.hstack([np.zeros((N, 32)), F.layer_norm(kt, (32,), eps=1e-5).numpy()])
+    mask = np.zeros((N, 2 * N), dtype=bool)
+    for t in range(N):
+        lo = max(0, (t // C) * C - W)
+        mask[t, :lo] = True
+        mask[t, N + lo:N + t + 1] = True
+    want = sdpa(qr, np.vstack([khat, kr]), np.vstack([v, v]), mask, scale=sc)
+    np.testing.assert_allclose(res.out, want, rtol=0, atol=1e-12)
+    # the second formulation honours the scale too
+    np.testing.assert_allclose(mod.brute_force(q, k, v, ell, p), want, rtol=0, atol=1e-12)
+
+
+def test_given_softmax_scale_is_used_for_state_and_window():
+    check_softmax_scale(O)
 
 
 # ---------------------------------------------------------------- I3 / read form
