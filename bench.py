@@ -85,13 +85,14 @@ def attn_flops(cfg, n: int) -> int:
 def decode_bytes(cfg, rows: int, t: int) -> int:
     """Algorithmic HBM bytes of one decode step at position t (ring write + attention + combine).
 
-    Per sequence: state rows read once (read-form key 32 x 2 B, unit value
-    direction 64 x 2 B, radius 4 B), window keys/values read once (2 x 64 x 2 B),
-    q/k/v/gate in (3 x 128 + 4 B), ring write (2 x 128 + 4 B), output 128 B."""
+    Per sequence: state rows read once (read-form key, 32 live dims x 2 B fp16,
+    and read-form value rho * u, 64 x 2 B bf16: 192 B), window keys/values read
+    once (2 x 64 x 2 B), q/k/v/gate in (3 x 128 + 4 B), ring write (2 x 128 + 4 B),
+    output 128 B."""
     C, W = cfg.chunk, cfg.window
     c = t // C
     w = t - max(0, c * C - W) + 1
-    return cfg.seqs * (196 * rows + 256 * w + 388 + 260 + 128)
+    return cfg.seqs * (192 * rows + 256 * w + 388 + 260 + 128)
 
 
 def read_counters():
@@ -107,27 +108,40 @@ def read_counters():
 
 
 def cpu_baseline(w, budget_s: float):
-    """The oracle on a bounded sample: whole sequences of the workload until budget_s has passed."""
+    """The oracle on a bounded sample: whole sequences of the workload until budget_s has passed,
+    once with the BLAS library's default thread count and once with one thread."""
     import oracle.kvm_oracle as O
     from kvm_inputs import make_inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    def blas_threads():
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
     p = O.Params.of(w)
-    done, t_used = 0, 0.0
-    while t_used < budget_s and done < w.seqs:
-        inp = make_inputs(w, seqs=[done])
-        arr = [t[0].double().numpy() for t in (inp.q, inp.k, inp.v, inp.gate_logits)]
-        t0 = time.perf_counter()
-        O.prefill(*arr, p)
-        t_used += time.perf_counter() - t0
-        done += 1
-        log(f"cpu oracle: {done} sequence(s), {t_used:.1f}s")
+
+    def run(label):
+        done, t_used = 0, 0.0
+        while t_used < budget_s and done < w.seqs:
+            inp = make_inputs(w, seqs=[done])
+            arr = [t[0].double().numpy() for t in (inp.q, inp.k, inp.v, inp.gate_logits)]
+            t0 = time.perf_counter()
+            O.prefill(*arr, p)
+            t_used += time.perf_counter() - t0
+            done += 1
+            log(f"cpu oracle ({label}): {done} sequence(s), {t_used:.1f}s")
+        return done, t_used
+
+    threads = blas_threads()
+    done, t_used = run(f"{threads} BLAS threads")
+    with threadpool_limits(limits=1):
+        done1, t1 = run("1 thread")
     return {"value": done * w.n_tokens / t_used, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": os.cpu_count(),
             "sample": f"{done} of {w.seqs} sequences of {w.name} ({w.n_tokens} tokens each), full oracle prefill "
-                      f"(absorption + attention), {t_used:.1f}s"}
+                      f"(absorption + attention), {t_used:.1f}s, NumPy fp64 with {threads} BLAS threads "
+                      f"on a host with {os.cpu_count()} CPUs",
+            "one_thread": {"value": done1 * w.n_tokens / t1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"{done1} sequences, {t1:.1f}s"}}
 
 
 def bench_prefill(w, steps: int, warmup: int):
@@ -276,44 +290,53 @@ def bench_variants(w, tensors, steps: int):
 
 
 def bench_decode(w, steps: int):
+    """Decode steps of the batched-decode workload.  `steps` steps of one state (its ~285 MB of
+    state rows and window fit the 256 MB last-level cache of the chip only in part), then the
+    same number of steps alternating between that state and a second one prefilled with the same
+    tokens (two working sets at different addresses, ~570 MB in all: each step's rows come from
+    HBM, not from the cache).  Kernel time from HIP events around each decode kernel."""
     import torch
-    from compressed_kv_state_amd import KvmConfig, KvmState
+    from compressed_kv_state_amd import KvmConfig, KvmState, schedule
     from kvm_inputs import make_inputs
     warm = 8
-    n = w.n_tokens + warm + steps
+    n = w.n_tokens + warm + 2 * steps
     log(f"decode workload {w.name}: generating inputs for {w.seqs} sequences")
     inp = make_inputs(w, n_total=n)
     cfg = KvmConfig.of(w, max_tokens=n)
-    st = KvmState(cfg)
+    states = [KvmState(cfg), KvmState(cfg)]
     q, k, v, g = (t[:, :w.n_tokens].contiguous().cuda() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
-    log("decode workload: prefill")
-    st.prefill(q, k, v, g)
+    log("decode workload: prefill of two states")
+    for st in states:
+        st.prefill(q, k, v, g)
     del q, k, v, g
     dq, dk, dv, dg = (t[:, w.n_tokens:].contiguous().cuda() for t in (inp.q, inp.k, inp.v, inp.gate_logits))
     del inp
-    steps_in = [tuple(x[:, i].contiguous() for x in (dq, dk, dv, dg)) for i in range(warm + steps)]
+    steps_in = [tuple(x[:, i].contiguous() for x in (dq, dk, dv, dg)) for i in range(warm + 2 * steps)]
     out = torch.empty_like(steps_in[0][0])
     for i in range(warm):
-        st.decode_step(*steps_in[i], out)
+        for st in states:
+            st.decode_step(*steps_in[i], out)
     torch.cuda.synchronize()
-    st.profile(True)
+    sched_rows = schedule(cfg, (n - 1) // cfg.chunk + 1)[2].tolist()
+
+    def step_bytes(t):
+        absorbed = max(0, t // cfg.chunk - cfg.window // cfg.chunk)
+        return decode_bytes(cfg, sched_rows[absorbed - 1] if absorbed else 0, t)
+
+    # one state: positions [n0 + warm, n0 + warm + steps) of state 0
+    a = states[0]
+    a.profile(True)
     t0 = time.perf_counter()
     for i in range(warm, warm + steps):
-        st.decode_step(*steps_in[i], out)
+        a.decode_step(*steps_in[i], out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = st.profile_read()
-    st.profile(False)
-    st.check()
-    from compressed_kv_state_amd import schedule
-    sched_rows = schedule(cfg, (n - 1) // cfg.chunk + 1)[2].tolist()
-    total_bytes = 0
-    for t in range(w.n_tokens + warm, w.n_tokens + warm + steps):
-        absorbed = max(0, t // cfg.chunk - cfg.window // cfg.chunk)
-        total_bytes += decode_bytes(cfg, sched_rows[absorbed - 1] if absorbed else 0, t)
+    prof = a.profile_read()
+    a.profile(False)
+    total_bytes = sum(step_bytes(w.n_tokens + i) for i in range(warm, warm + steps))
     attn_ms = prof["dec_attn_ms"]
     gbs = total_bytes / (attn_ms * 1e-3) / 1e9
-    return {
+    res = {
         "workload": w.name, "sequences": w.seqs, "prefilled": w.n_tokens, "steps": steps,
         "ms_per_step": (t1 - t0) * 1e3 / steps,
         "kernel_ms_per_step": attn_ms / max(prof["dec_attn_launches"], 1),
@@ -321,7 +344,39 @@ def bench_decode(w, steps: int):
         "merges": prof["dec_absorb_launches"],
         "bytes_per_step": total_bytes / steps,
         "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS,
+        "note": "one state; its per-step working set (~285 MB) is re-read every step and partly cache-resident",
     }
+    # two states alternating: state 0 continues at n0 + warm + steps, state 1 at n0 + warm
+    b = states[1]
+    for st in states:
+        st.profile(16)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        a.decode_step(*steps_in[warm + steps + i], out)
+        b.decode_step(*steps_in[warm + i], out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pa, pb = a.profile_read(), b.profile_read()
+    for st in states:
+        st.profile(False)
+        st.check()
+    two_bytes = sum(step_bytes(w.n_tokens + warm + steps + i) + step_bytes(w.n_tokens + warm + i)
+                    for i in range(steps))
+    two_ms = pa["dec_attn_ms"] + pb["dec_attn_ms"]
+    launches = pa["dec_attn_launches"] + pb["dec_attn_launches"]
+    gbs2 = two_bytes / (two_ms * 1e-3) / 1e9
+    res["hbm_resident"] = {
+        "states": 2, "steps_each": steps, "kernel_ms_per_step": two_ms / max(launches, 1),
+        "ms_per_step": (t1 - t0) * 1e3 / (2 * steps), "bytes_per_step": two_bytes / (2 * steps),
+        "achieved_GBs": gbs2, "peak_GBs": PEAK_HBM_GBS, "frac": gbs2 / PEAK_HBM_GBS,
+        "note": "decode steps alternate between two states prefilled with the same tokens (~570 MB of rows "
+                "and window read per pair of steps, twice the 256 MB last-level cache)",
+    }
+    log(f"decode: one state {res['kernel_ms_per_step'] * 1e3:.1f} us/step ({res['frac']:.3f} of HBM), "
+        f"two states {res['hbm_resident']['kernel_ms_per_step'] * 1e3:.1f} us/step "
+        f"({res['hbm_resident']['frac']:.3f})")
+    del states, steps_in, dq, dk, dv, dg
+    return res
 
 
 def copy_calibration():

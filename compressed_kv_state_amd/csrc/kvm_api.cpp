@@ -155,8 +155,8 @@ struct Plan {
   kvm::Dims m{};
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
-  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, idx, krot, tslot, tkind, ring_k, ring_v,
-      ring_l, rope_cos, rope_sin, sch, nver, xbuf, xerr, total;
+  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, pcount, idx, krot, tslot, tkind, ring_k,
+      ring_v, ring_l, rope_cos, rope_sin, sch, nver, xbuf, xerr, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -229,6 +229,7 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   p.pkey = take(BH * (size_t)m.V_cap * 32 * es);
   p.pval = take(BH * (size_t)m.V_cap * 64 * es);
   p.prho = take(BH * (size_t)m.V_cap * 4);
+  p.pcount = take(BH * (size_t)m.V_cap * 4);
   p.idx = take(BH * (size_t)idx_total * 4);
   p.tslot = take(m.trace ? BH * (size_t)c->max_tokens * 4 : 0);
   p.tkind = take(m.trace ? BH * (size_t)c->max_tokens : 0);
@@ -318,6 +319,27 @@ int rows_after(const kvm_state* st, int64_t j) {
   return s[0] + s[1] + s[2];
 }
 
+// Chunks absorbed once `pos` tokens have been consumed (by prefill calls or
+// decode steps alike): query chunk ceil(pos/C) - 1 has needed every chunk up
+// to its own index - W/C - 1.
+int64_t absorbed_at(const kvm::Dims& m, int64_t pos) {
+  const int64_t a = (pos + m.C - 1) / m.C - m.W / m.C - 1;
+  return a > 0 ? a : 0;
+}
+
+// Queue the clearing of the counters and exchange buffers the kernels rely on
+// (state creation, reset, load).
+hipError_t clear_counters(kvm_state* st, bool trace_too, hipStream_t hs) {
+  hipError_t e = hipMemsetAsync(st->d.nver, 0, (size_t)st->m.BH * 4, hs);
+  if (e == hipSuccess) e = hipMemsetAsync(st->d.xerr, 0, 4, hs);
+  if (e == hipSuccess) e = hipMemsetAsync(st->d.xbuf, 0, (size_t)st->m.BH * 2 * st->m.P * st->m.C * 8, hs);
+  if (e == hipSuccess && st->m.trace && trace_too) {
+    e = hipMemsetAsync(st->d.tslot, 0xFF, (size_t)st->m.BH * st->m.max_tokens * 4, hs);
+    if (e == hipSuccess) e = hipMemsetAsync(st->d.tkind, 0xFF, (size_t)st->m.BH * st->m.max_tokens, hs);
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,6 +404,7 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     d.pkey = b + p.pkey;
     d.pval = b + p.pval;
     d.prho = reinterpret_cast<float*>(b + p.prho);
+    d.pcount = reinterpret_cast<int*>(b + p.pcount);
     d.idx = reinterpret_cast<int*>(b + p.idx);
     d.tslot = reinterpret_cast<int*>(b + p.tslot);
     d.tkind = reinterpret_cast<uint8_t*>(b + p.tkind);
@@ -396,13 +419,7 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     d.xbuf = reinterpret_cast<uint2*>(b + p.xbuf);
     d.xerr = reinterpret_cast<int*>(b + p.xerr);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = hipMemsetAsync(d.nver, 0, (size_t)st->m.BH * 4, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(d.xerr, 0, 4, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(d.xbuf, 0, (size_t)st->m.BH * 2 * st->m.P * st->m.C * 8, hs);
-    if (e == hipSuccess && st->m.trace) {
-      e = hipMemsetAsync(d.tslot, 0xFF, (size_t)st->m.BH * cfg->max_tokens * 4, hs);
-      if (e == hipSuccess) e = hipMemsetAsync(d.tkind, 0xFF, (size_t)st->m.BH * cfg->max_tokens, hs);
-    }
+    hipError_t e = clear_counters(st, true, hs);
     if (e == hipSuccess && !st->sched.empty())
       e = hipMemcpyAsync(d.sched, st->sched.data(), st->sched.size() * 4, hipMemcpyHostToDevice, hs);
     if (e == hipSuccess) e = kvm::launch_init(st->m, d, (double)cfg->rope_theta, hs);
@@ -547,14 +564,31 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
   return KVM_OK;
 }
 
-kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* stream) {
+kvm_status kvm_state_read(const kvm_state* st, int64_t chunk, kvm_state_view* dst, void* stream) {
   if (!st || !dst) return fail(KVM_E_INVALID_ARG, "NULL argument");
   if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
   const kvm::Dims& m = st->m;
-  if ((dst->trace_slot || dst->trace_kind) && !m.trace)
-    return fail(KVM_E_INVALID_ARG, "trace requested but the state was created without KVM_FLAG_TRACE");
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const size_t BH = (size_t)m.BH, S = (size_t)m.S_cap, es = m.bf16 ? 2 : 4;
+  if (chunk < -1 || chunk >= st->absorbed)
+    return fail(KVM_E_INVALID_ARG, "chunk must be -1 (current state) or an absorbed chunk");
+  if (chunk >= 0) {
+    // a past snapshot: read-form row versions only
+    if (dst->key_sum || dst->val_sum || dst->ring_k || dst->ring_v || dst->ring_l || dst->trace_slot ||
+        dst->trace_kind)
+      return fail(KVM_E_INVALID_ARG,
+                  "a past snapshot keeps only read-form row versions: raw sums, ring and trace are current-state only");
+    const int rows = rows_after(st, chunk);
+    const int64_t ioff = st->sched[(size_t)chunk * 4 + 3];
+    hipError_t e = kvm::launch_snapshot_gather(m, st->d, rows, ioff, m.S_cap, dst->key_read, dst->val_read, dst->rho,
+                                               dst->count, hs);
+    if (e != hipSuccess) return hip_fail(const_cast<kvm_state*>(st), e, "snapshot gather launch");
+    if (dst->n_rows)
+      for (size_t s = 0; s < BH; ++s) dst->n_rows[s] = rows;
+    return KVM_OK;
+  }
+  if ((dst->trace_slot || dst->trace_kind) && !m.trace)
+    return fail(KVM_E_INVALID_ARG, "trace requested but the state was created without KVM_FLAG_TRACE");
   struct Copy {
     void* to;
     const void* from;
@@ -568,6 +602,9 @@ kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* 
       {dst->val_read, st->d.vread, BH * S * 64 * es},
       {dst->trace_slot, st->d.tslot, BH * (size_t)m.max_tokens * 4},
       {dst->trace_kind, st->d.tkind, BH * (size_t)m.max_tokens},
+      {dst->ring_k, st->d.ring_k, BH * (size_t)m.R * 64 * es},
+      {dst->ring_v, st->d.ring_v, BH * (size_t)m.R * 64 * es},
+      {dst->ring_l, st->d.ring_l, BH * (size_t)m.R * 4},
   };
   for (const Copy& c : copies) {
     if (!c.to || c.bytes == 0) continue;
@@ -578,6 +615,60 @@ kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* 
     const int32_t r = rows_after(st, st->absorbed - 1);
     for (size_t s = 0; s < BH; ++s) dst->n_rows[s] = r;  // host memory: the row count is host-side
   }
+  dst->position = st->pos;
+  return KVM_OK;
+}
+
+kvm_status kvm_state_load(kvm_state* st, const kvm_state_view* src, void* stream) {
+  if (!st || !src) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  const kvm::Dims& m = st->m;
+  const int64_t pos = src->position;
+  if (pos < 0 || pos > m.max_tokens) return fail(KVM_E_INVALID_ARG, "position outside [0, max_tokens]");
+  const int64_t absorbed = absorbed_at(m, pos);
+  if (absorbed > m.J_cap) return fail(KVM_E_INVALID_ARG, "position needs more absorbed chunks than the workspace holds");
+  const int rows = rows_after(st, absorbed - 1);
+  const size_t BH = (size_t)m.BH, S = (size_t)m.S_cap, es = m.bf16 ? 2 : 4;
+  if (src->n_rows)
+    for (size_t s = 0; s < BH; ++s)
+      if (src->n_rows[s] != rows)
+        return fail(KVM_E_INVALID_ARG, "n_rows[" + std::to_string(s) + "] = " + std::to_string(src->n_rows[s]) +
+                                           " but the schedule has " + std::to_string(rows) + " rows at this position");
+  if (rows > 0 && (!src->key_sum || !src->val_sum || !src->count || !src->rho))
+    return fail(KVM_E_INVALID_ARG, "key_sum, val_sum, count and rho are required when the state has rows");
+  if (pos > 0 && (!src->ring_k || !src->ring_v || !src->ring_l))
+    return fail(KVM_E_INVALID_ARG, "ring_k, ring_v and ring_l are required when position > 0");
+  if ((src->trace_slot || src->trace_kind) && !m.trace)
+    return fail(KVM_E_INVALID_ARG, "trace given but the state was created without KVM_FLAG_TRACE");
+  if (m.trace && (!src->trace_slot != !src->trace_kind))
+    return fail(KVM_E_INVALID_ARG, "give both trace arrays or neither");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = clear_counters(st, !src->trace_slot, hs);
+  struct Copy {
+    void* to;
+    const void* from;
+    size_t bytes;
+  } copies[] = {
+      {st->d.key_sum, src->key_sum, BH * S * 32 * 4},
+      {st->d.val_sum, src->val_sum, BH * S * 64 * 4},
+      {st->d.count, src->count, BH * S * 4},
+      {st->d.rho, src->rho, BH * S * 4},
+      {st->d.ring_k, src->ring_k, BH * (size_t)m.R * 64 * es},
+      {st->d.ring_v, src->ring_v, BH * (size_t)m.R * 64 * es},
+      {st->d.ring_l, src->ring_l, BH * (size_t)m.R * 4},
+      {st->d.tslot, src->trace_slot, BH * (size_t)m.max_tokens * 4},
+      {st->d.tkind, src->trace_kind, BH * (size_t)m.max_tokens},
+  };
+  for (const Copy& c : copies) {
+    if (e != hipSuccess) break;
+    if (!c.from || c.bytes == 0) continue;
+    e = hipMemcpyAsync(c.to, c.from, c.bytes, hipMemcpyDefault, hs);
+  }
+  if (e == hipSuccess && rows > 0)
+    e = kvm::launch_state_load(m, st->d, rows, absorbed > 0 ? st->sched[(size_t)(absorbed - 1) * 4 + 3] : -1, hs);
+  if (e != hipSuccess) return hip_fail(st, e, "state load");
+  st->pos = pos;
+  st->absorbed = absorbed;
   return KVM_OK;
 }
 
@@ -588,7 +679,7 @@ kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, voi
   if (j < 0 || j >= st->absorbed) return fail(KVM_E_INVALID_ARG, "chunk j has not been absorbed");
   const int rows = rows_after(st, j);
   const int64_t ioff = st->sched[(size_t)j * 4 + 3];
-  hipError_t e = kvm::launch_snapshot_gather(st->m, st->d, rows, ioff, key_read, val_read, rho_read,
+  hipError_t e = kvm::launch_snapshot_gather(st->m, st->d, rows, ioff, rows, key_read, val_read, rho_read, nullptr,
                                              reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(const_cast<kvm_state*>(st), e, "snapshot gather launch");
   return KVM_OK;
@@ -623,14 +714,7 @@ kvm_status kvm_state_check(kvm_state* st, void* stream) {
 
 kvm_status kvm_state_reset(kvm_state* st, void* stream) {
   if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipMemsetAsync(st->d.nver, 0, (size_t)st->m.BH * 4, hs);
-  if (e == hipSuccess) e = hipMemsetAsync(st->d.xerr, 0, 4, hs);
-  if (e == hipSuccess) e = hipMemsetAsync(st->d.xbuf, 0, (size_t)st->m.BH * 2 * st->m.P * st->m.C * 8, hs);
-  if (e == hipSuccess && st->m.trace) {
-    e = hipMemsetAsync(st->d.tslot, 0xFF, (size_t)st->m.BH * st->m.max_tokens * 4, hs);
-    if (e == hipSuccess) e = hipMemsetAsync(st->d.tkind, 0xFF, (size_t)st->m.BH * st->m.max_tokens, hs);
-  }
+  hipError_t e = clear_counters(st, true, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e, "state reset");
   st->pos = 0;
   st->absorbed = 0;

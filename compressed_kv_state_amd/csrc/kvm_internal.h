@@ -53,6 +53,7 @@ struct Dev {
   void* pkey;        // [BH][V_cap][32] RT read-form row versions: key
   void* pval;        // [BH][V_cap][64] T  read-form row versions: value rho * u
   float* prho;       // [BH][V_cap]       read-form row versions: radius
+  int* pcount;       // [BH][V_cap]       read-form row versions: count
   int* idx;          // [BH][idx_total] per absorbed chunk j: version id of each row after chunk j
   int* tslot;        // [BH][max_tokens] trace: row created / merged into
   uint8_t* tkind;    // [BH][max_tokens] trace: 0 sink 1 append 2 merge 255 none
@@ -97,9 +98,15 @@ hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t
 // slot t % R, then attend over `rows` state rows and the window; out [BH][64].
 hipError_t launch_decode(const Dims& m, const Dev& d, const void* q, const void* k, const void* v, const float* l,
                          int64_t t, int rows, void* out, hipStream_t st);
-// Gather the read form of snapshot j (rows_j rows, version list at idx_off) into dense
-// key [BH][rows][32] RT, unit value [BH][rows][64] RT, radius [BH][rows] f32 (any may be null).
-hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t idx_off, void* key_out,
-                                  void* val_out, float* rho_out, hipStream_t st);
+// Gather the read form of snapshot j (rows_j rows, version list at idx_off) into
+// key [BH][stride][32] RT, value rho * u [BH][stride][64] T, radius and count [BH][stride]
+// (rows [0, rows) of each sequence; any output may be null; stride >= rows).
+hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t idx_off, int stride, void* key_out,
+                                  void* val_out, float* rho_out, int* count_out, hipStream_t st);
+// After the raw state (key_sum, val_sum, count, rho: `rows` rows per sequence) has been
+// written into the workspace: derive every row's unit direction, current read form and a
+// row version (version id = row, nver = rows), and the index list at idx_off of the last
+// absorbed chunk (idx_off < 0: none).
+hipError_t launch_state_load(const Dims& m, const Dev& d, int rows, int64_t idx_off, hipStream_t st);
 
 }  // namespace kvm

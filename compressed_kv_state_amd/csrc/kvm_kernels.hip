@@ -434,6 +434,83 @@ __device__ __forceinline__ void lane_best(const f32x16& acc, int row0h, uint32_t
   bk = imp ? mt : bk;
 }
 
+// Everything derived from one state row's raw sums, computed by the row's
+// group of four lanes (lane sub owns key dims [8 sub, 8 sub + 8) and value
+// dims [16 sub, 16 sub + 16)): the unit key direction K/|K| for the cosine
+// passes (bf16 path: bf16 hi + lo halves; also into the LDS copy `ulrow` when
+// not null) and the just-in-time read form ([KVM summary, Core mechanisms 2]):
+// LayerNorm of K/n over the live dims (no affine) and the value rho * V/|V|
+// (direction of the sum at the radius fixed at creation; the plain mean V/n
+// without value-length normalisation), written as the current read form and
+// as a row version.  The absorption scan and the state load share this code,
+// so a loaded state reads back bit for bit like the one it was exported from.
+template <typename T>
+__device__ __forceinline__ void row_derive(const float (&K)[8], const float (&V)[16], int n, float rh, int sub,
+                                           const Dims& m, char* unit_row, bf16* ulrow,
+                                           typename Rd<T>::type* kread_row, T* vread_row,
+                                           typename Rd<T>::type* pkey_ver, T* pval_ver) {
+  using RT = typename Rd<T>::type;
+  constexpr int REL = 16 / sizeof(RT);
+  // row sums of squares and moments over the four lanes
+  float k2 = 0.f, ksum = 0.f, v2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { k2 = fmaf(K[i], K[i], k2); ksum += K[i]; }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v2 = fmaf(V[i], V[i], v2);
+  k2 = quad_sum(k2);
+  ksum = quad_sum(ksum);
+  v2 = quad_sum(v2);
+  {
+    const float inv = k2 > 0.f ? __builtin_amdgcn_rsqf(k2) : 0.f;   // 1 ulp
+    if constexpr (Is<T>::bf) {
+      alignas(16) bf16 hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float y = K[i] * inv;
+        hi[i] = (bf16)y;
+        lo[i] = (bf16)(y - (float)hi[i]);
+      }
+      copy16(unit_row + 16 * sub, hi);
+      copy16(unit_row + 64 + 16 * sub, lo);
+      if (ulrow) {
+        copy16(ulrow + 8 * sub, hi);
+        copy16(ulrow + 32 + 8 * sub, lo);
+      }
+    } else {
+      alignas(16) float uu[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) uu[i] = K[i] * inv;
+      copy16(unit_row + 32 * sub, uu);
+      copy16(unit_row + 32 * sub + 16, uu + 4);
+    }
+  }
+  const float invn = __builtin_amdgcn_rcpf((float)n);   // 1 ulp
+  const float mean = ksum * invn * (1.0f / 32.0f);
+  float var = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
+  var = quad_sum(var);
+  var *= (1.0f / 32.0f);
+  const float rs = __builtin_amdgcn_rsqf(var + m.ln_eps);
+  const float vsc = m.no_vnorm ? invn : (v2 > 0.f ? rh * __builtin_amdgcn_rsqf(v2) : 0.f);
+  alignas(16) RT kh[8];
+  alignas(16) T vh[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kh[i] = fromf<RT>((K[i] * invn - mean) * rs);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) vh[i] = fromf<T>(V[i] * vsc);
+#pragma unroll
+  for (int i = 0; i < 8; i += REL) {
+    copy16(pkey_ver + 8 * sub + i, &kh[i]);
+    copy16(kread_row + 8 * sub + i, &kh[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i += REL) {
+    copy16(pval_ver + 16 * sub + i, &vh[i]);
+    copy16(vread_row + 16 * sub + i, &vh[i]);
+  }
+}
+
 // bf16 path: one 32-row tile of unit directions (hi and lo halves) as the MFMA
 // A operand: lane (jl, h) holds dims [16h, 16h+16) of row rb + 32 tile + jl.
 // The first NL rows the pass reads (from row LB: 0, or the first row after the
@@ -740,6 +817,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   RT* pkey = reinterpret_cast<RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
   T* pval = reinterpret_cast<T*>(d.pval) + (size_t)s * m.V_cap * 64;
   float* prho = d.prho + (size_t)s * m.V_cap;
+  int* pcount = d.pcount + (size_t)s * m.V_cap;
   int* idx = d.idx + (size_t)s * m.idx_total;
   const T* ring_k = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
   const T* ring_v = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
@@ -1148,76 +1226,20 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         count[row] = n;
         rho[row] = rh;
       }
-      // row sums of squares and moments over the four lanes
-      float k2 = 0.f, ksum = 0.f, v2 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { k2 = fmaf(K[i], K[i], k2); ksum += K[i]; }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v2 = fmaf(V[i], V[i], v2);
-      k2 = quad_sum(k2);
-      ksum = quad_sum(ksum);
-      v2 = quad_sum(v2);
-      // unit key direction for the next cosine passes
-      {
-        const float inv = k2 > 0.f ? __builtin_amdgcn_rsqf(k2) : 0.f;   // 1 ulp
-        char* ur = unit + (size_t)row * 128;
-        if constexpr (Is<T>::bf) {
-          alignas(16) bf16 hi[8], lo[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float y = K[i] * inv;
-            hi[i] = (bf16)y;
-            lo[i] = (bf16)(y - (float)hi[i]);
-          }
-          copy16(ur + 16 * sub, hi);
-          copy16(ur + 64 + 16 * sub, lo);
-          if (NL > 0 && row >= LB) {
-            const int ls = own_slot(row, LB, psh);
-            if (ls < NL) {
-              copy16(&ul[ls][8 * sub], hi);
-              copy16(&ul[ls][32 + 8 * sub], lo);
-            }
-          }
-        } else {
-          alignas(16) float uu[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) uu[i] = K[i] * inv;
-          copy16(ur + 32 * sub, uu);
-          copy16(ur + 32 * sub + 16, uu + 4);
+      // the row's unit key direction (both copies) and its read form, version nver + t
+      const int ver = nver + t;
+      bf16* ulrow = nullptr;
+      if constexpr (Is<T>::bf && NL > 0) {
+        if (row >= LB) {
+          const int ls = own_slot(row, LB, psh);
+          if (ls < NL) ulrow = &ul[ls][0];
         }
       }
-      // just-in-time read form ([KVM summary, Core mechanisms 2]): LayerNorm of
-      // K/n over the live dims (no affine); the value rho * V/|V| (direction of
-      // the sum at the radius fixed at creation).
-      const float invn = __builtin_amdgcn_rcpf((float)n);   // 1 ulp
-      const float mean = ksum * invn * (1.0f / 32.0f);
-      float var = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { const float dx = K[i] * invn - mean; var = fmaf(dx, dx, var); }
-      var = quad_sum(var);
-      var *= (1.0f / 32.0f);
-      const float rs = __builtin_amdgcn_rsqf(var + m.ln_eps);
-      // the value at the row's radius, or (ablation) the plain mean
-      const float vsc = m.no_vnorm ? invn : (v2 > 0.f ? rh * __builtin_amdgcn_rsqf(v2) : 0.f);
-      const int ver = nver + t;
-      alignas(16) RT kh[8];
-      alignas(16) T vh[16];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kh[i] = fromf<RT>((K[i] * invn - mean) * rs);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) vh[i] = fromf<T>(V[i] * vsc);
-#pragma unroll
-      for (int i = 0; i < 8; i += REL) {
-        copy16(pkey + (size_t)ver * 32 + 8 * sub + i, &kh[i]);
-        copy16(kread + (size_t)row * 32 + 8 * sub + i, &kh[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; i += REL) {
-        copy16(pval + (size_t)ver * 64 + 16 * sub + i, &vh[i]);
-        copy16(vread + (size_t)row * 64 + 16 * sub + i, &vh[i]);
-      }
+      row_derive<T>(K, V, n, rh, sub, m, unit + (size_t)row * 128, ulrow, kread + (size_t)row * 32,
+                    vread + (size_t)row * 64, pkey + (size_t)ver * 32, pval + (size_t)ver * 64);
       if (sub == 0) {
         prho[ver] = rh;
+        pcount[ver] = n;
         if (ver_lds) sm.ver_cur[vslot(row)] = ver;
         else idx[ioff + row] = ver;
       }
@@ -2493,7 +2515,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
     const T* vr = reinterpret_cast<const T*>(d.vread) + (size_t)s * m.S_cap * 64;
     const int per = (S + kDecWaves - 1) / kDecWaves;
     const int rb = w * per, re = min(S, rb + per);
-#pragma unroll 2
     for (int row = rb + grp; row < re; row += 64 / L) {
       alignas(16) RT kk[4];
       alignas(16) T vh[8];
@@ -2602,25 +2623,70 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
 }
 
 template <typename T>
-__global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, typename Rd<T>::type* key_out,
-                                       T* val_out, float* rho_out) {
+__global__ void snapshot_gather_kernel(Dims m, Dev d, int rows, int64_t ioff, int stride,
+                                       typename Rd<T>::type* key_out, T* val_out, float* rho_out, int* count_out) {
   using RT = typename Rd<T>::type;
   const int s = blockIdx.x;
   const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
   const float* pr = d.prho + (size_t)s * m.V_cap;
-  for (int64_t i = threadIdx.x; i < (int64_t)rows * 97; i += blockDim.x) {
-    const int r = (int)(i / 97), dd = (int)(i % 97);
+  const int* pc = d.pcount + (size_t)s * m.V_cap;
+  for (int64_t i = threadIdx.x; i < (int64_t)rows * 98; i += blockDim.x) {
+    const int r = (int)(i / 98), dd = (int)(i % 98);
     const int64_t ver = idxl[r];
+    const size_t o = (size_t)s * stride + r;
     if (dd < 32) {
-      if (key_out) key_out[((size_t)s * rows + r) * 32 + dd] = pk[ver * 32 + dd];
+      if (key_out) key_out[o * 32 + dd] = pk[ver * 32 + dd];
     } else if (dd < 96) {
-      if (val_out) val_out[((size_t)s * rows + r) * 64 + dd - 32] = pv[ver * 64 + dd - 32];
-    } else if (rho_out) {
-      rho_out[(size_t)s * rows + r] = pr[ver];
+      if (val_out) val_out[o * 64 + dd - 32] = pv[ver * 64 + dd - 32];
+    } else if (dd == 96) {
+      if (rho_out) rho_out[o] = pr[ver];
+    } else if (count_out) {
+      count_out[o] = pc[ver];
     }
   }
+}
+
+// State load: one workgroup per sequence, four lanes per row (the lane layout of
+// the scan's row update, so that row_derive gives the same bits).  Version id of
+// row r = r; the index list of the last absorbed chunk names them.
+template <typename T>
+__global__ __launch_bounds__(256) void state_load_kernel(Dims m, Dev d, int rows, int64_t ioff) {
+  using RT = typename Rd<T>::type;
+  const int s = blockIdx.x;
+  const int sub = threadIdx.x & 3;
+  const float* key_sum = d.key_sum + (size_t)s * m.S_cap * 32;
+  const float* val_sum = d.val_sum + (size_t)s * m.S_cap * 64;
+  const int* count = d.count + (size_t)s * m.S_cap;
+  const float* rho = d.rho + (size_t)s * m.S_cap;
+  char* unit = reinterpret_cast<char*>(d.unit) + (size_t)s * m.S_cap * 128;
+  RT* kread = reinterpret_cast<RT*>(d.kread) + (size_t)s * m.S_cap * 32;
+  T* vread = reinterpret_cast<T*>(d.vread) + (size_t)s * m.S_cap * 64;
+  RT* pkey = reinterpret_cast<RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  T* pval = reinterpret_cast<T*>(d.pval) + (size_t)s * m.V_cap * 64;
+  float* prho = d.prho + (size_t)s * m.V_cap;
+  int* pcount = d.pcount + (size_t)s * m.V_cap;
+  for (int r = threadIdx.x >> 2; r < rows; r += blockDim.x >> 2) {
+    RowRegs rr;
+    row_load(rr, key_sum, val_sum, count, rho, r, sub);
+    float K[8], V[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      K[i] = rr.k[0][i];
+      K[4 + i] = rr.k[1][i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) V[4 * q + i] = rr.v[q][i];
+    }
+    row_derive<T>(K, V, rr.n, rr.rh, sub, m, unit + (size_t)r * 128, nullptr, kread + (size_t)r * 32,
+                  vread + (size_t)r * 64, pkey + (size_t)r * 32, pval + (size_t)r * 64);
+    if (sub == 0) {
+      prho[r] = rr.rh;
+      pcount[r] = rr.n;
+      if (ioff >= 0) d.idx[(size_t)s * m.idx_total + ioff + r] = r;
+    }
+  }
+  if (threadIdx.x == 0) d.nver[s] = rows;
 }
 
 template <typename T>
@@ -2741,15 +2807,21 @@ hipError_t launch_decode(const Dims& m, const Dev& d, const void* q, const void*
   return hipGetLastError();
 }
 
-hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t ioff, void* key_out, void* val_out,
-                                  float* rho_out, hipStream_t st) {
+hipError_t launch_snapshot_gather(const Dims& m, const Dev& d, int rows, int64_t ioff, int stride, void* key_out,
+                                  void* val_out, float* rho_out, int* count_out, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (m.bf16)
-    snapshot_gather_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, reinterpret_cast<f16*>(key_out),
-                                                       reinterpret_cast<bf16*>(val_out), rho_out);
+    snapshot_gather_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, stride, reinterpret_cast<f16*>(key_out),
+                                                       reinterpret_cast<bf16*>(val_out), rho_out, count_out);
   else
-    snapshot_gather_kernel<float><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, reinterpret_cast<float*>(key_out),
-                                                         reinterpret_cast<float*>(val_out), rho_out);
+    snapshot_gather_kernel<float><<<m.BH, 256, 0, st>>>(m, d, rows, ioff, stride, reinterpret_cast<float*>(key_out),
+                                                         reinterpret_cast<float*>(val_out), rho_out, count_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_load(const Dims& m, const Dev& d, int rows, int64_t ioff, hipStream_t st) {
+  if (m.bf16) state_load_kernel<bf16><<<m.BH, 256, 0, st>>>(m, d, rows, ioff);
+  else state_load_kernel<float><<<m.BH, 256, 0, st>>>(m, d, rows, ioff);
   return hipGetLastError();
 }
 

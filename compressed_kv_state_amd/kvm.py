@@ -51,8 +51,10 @@ class _Config(ctypes.Structure):
 
 
 class _View(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("n_rows", "key_sum", "val_sum", "count", "rho", "key_read", "val_read", "trace_slot", "trace_kind")]
+    _fields_ = ([(n, ctypes.c_void_p) for n in
+                 ("n_rows", "key_sum", "val_sum", "count", "rho", "key_read", "val_read", "trace_slot", "trace_kind")]
+                + [("position", ctypes.c_int64)]
+                + [(n, ctypes.c_void_p) for n in ("ring_k", "ring_v", "ring_l")])
 
 
 class _Info(ctypes.Structure):
@@ -87,7 +89,8 @@ def library() -> ctypes.CDLL:
         L.kvm_state_destroy.argtypes = [vp]
         L.kvm_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp]
         L.kvm_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
-        L.kvm_state_read.argtypes = [vp, ctypes.POINTER(_View), vp]
+        L.kvm_state_read.argtypes = [vp, i64, ctypes.POINTER(_View), vp]
+        L.kvm_state_load.argtypes = [vp, ctypes.POINTER(_View), vp]
         L.kvm_snapshot_read.argtypes = [vp, i64, vp, vp, vp, vp]
         L.kvm_state_get_info.argtypes = [vp, ctypes.POINTER(_Info)]
         L.kvm_state_reset.argtypes = [vp, vp]
@@ -99,7 +102,7 @@ def library() -> ctypes.CDLL:
         L.kvm_last_error.argtypes = []
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
-                     "kvm_decode_step", "kvm_state_read", "kvm_snapshot_read", "kvm_state_get_info",
+                     "kvm_decode_step", "kvm_state_read", "kvm_state_load", "kvm_snapshot_read", "kvm_state_get_info",
                      "kvm_state_reset", "kvm_state_check", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
         _lib = L
@@ -307,30 +310,68 @@ class KvmState:
         _check(library().kvm_state_get_info(self._h, ctypes.byref(i)))
         return {f[0]: getattr(i, f[0]) for f in _Info._fields_}
 
-    def read(self, trace: bool = False) -> dict:
-        """Copy the current state into new device tensors (queued on the current stream)."""
+    def read(self, trace: bool = False, chunk: int = -1, ring: bool = False, sums: Optional[bool] = None) -> dict:
+        """Copy the state into new device tensors (queued on the current stream).
+
+        chunk -1: the current state (raw sums, counts, radii, read form; the window ring
+        with ring=True; the per-token trace with trace=True).  chunk j >= 0: the state
+        right after absorbed chunk j (counts, radii and read form; the library refuses
+        the raw sums of a past chunk, sums=True asks for them anyway)."""
         inf = self.info()
         S, Sc, dt = self.cfg.seqs, inf["max_rows"], self.cfg.read_dtype
         dev = self.device
         res = {
-            "key_sum": torch.empty(S, Sc, 32, dtype=torch.float32, device=dev),
-            "val_sum": torch.empty(S, Sc, 64, dtype=torch.float32, device=dev),
             "count": torch.empty(S, Sc, dtype=torch.int32, device=dev),
             "rho": torch.empty(S, Sc, dtype=torch.float32, device=dev),
             "key_read": torch.empty(S, Sc, 32, dtype=dt, device=dev),
             "val_read": torch.empty(S, Sc, 64, dtype=self.cfg.torch_dtype, device=dev),
         }
+        if sums if sums is not None else chunk < 0:
+            res["key_sum"] = torch.empty(S, Sc, 32, dtype=torch.float32, device=dev)
+            res["val_sum"] = torch.empty(S, Sc, 64, dtype=torch.float32, device=dev)
         n_rows = torch.zeros(S, dtype=torch.int32)
-        view = _View(n_rows.data_ptr(), *(res[k].data_ptr() for k in
-                                          ("key_sum", "val_sum", "count", "rho", "key_read", "val_read")), None, None)
+        view = _View()
+        view.n_rows = n_rows.data_ptr()
+        for k_, t in res.items():
+            setattr(view, k_, t.data_ptr())
         if trace:
             res["trace_slot"] = torch.empty(S, self.cfg.max_tokens, dtype=torch.int32, device=dev)
             res["trace_kind"] = torch.empty(S, self.cfg.max_tokens, dtype=torch.uint8, device=dev)
             view.trace_slot = res["trace_slot"].data_ptr()
             view.trace_kind = res["trace_kind"].data_ptr()
-        _check(library().kvm_state_read(self._h, ctypes.byref(view), _stream(dev)))
+        if ring:
+            R = self.cfg.window + self.cfg.chunk
+            res["ring_k"] = torch.empty(S, R, 64, dtype=self.cfg.torch_dtype, device=dev)
+            res["ring_v"] = torch.empty(S, R, 64, dtype=self.cfg.torch_dtype, device=dev)
+            res["ring_l"] = torch.empty(S, R, dtype=torch.float32, device=dev)
+            for k_ in ("ring_k", "ring_v", "ring_l"):
+                setattr(view, k_, res[k_].data_ptr())
+        _check(library().kvm_state_read(self._h, chunk, ctypes.byref(view), _stream(dev)))
         res["n_rows"] = n_rows
+        if chunk < 0:
+            res["position"] = int(view.position)
         return res
+
+    def load(self, saved: dict):
+        """kvm_state_load from a dict made by read(ring=True) (and trace=True for a traced state)
+        of a state with the same configuration.  The tensors must stay alive until the current
+        stream has run the load."""
+        view = _View()
+        view.position = int(saved["position"])
+        keep = []
+        for k_ in ("key_sum", "val_sum", "count", "rho", "ring_k", "ring_v", "ring_l", "trace_slot", "trace_kind"):
+            t = saved.get(k_)
+            if t is not None:
+                t = t.contiguous()
+                keep.append(t)
+                setattr(view, k_, t.data_ptr())
+        n_rows = saved.get("n_rows")
+        if n_rows is not None:
+            n_rows = n_rows.to(torch.int32).cpu().contiguous()
+            keep.append(n_rows)
+            view.n_rows = n_rows.data_ptr()
+        _check(library().kvm_state_load(self._h, ctypes.byref(view), _stream(self.device)))
+        self._load_keep = keep
 
     def snapshot(self, j: int):
         """Read form of the state after absorbed chunk j: key [B*H, rows_j, 32] (read_dtype),

@@ -99,10 +99,14 @@ typedef struct kvm_config {
 
 typedef struct kvm_state kvm_state;
 
-/* Copy targets for kvm_state_read.  Any pointer may be NULL (skipped).
- * n_rows is host memory (filled immediately); every other pointer may be host
- * or device memory (queued copies, unified addressing).
- * S_cap = kvm_state_info(...).max_rows.  Rows beyond n_rows[s] are undefined.
+/* A state in plain arrays: what kvm_state_read fills and kvm_state_load takes.
+ * [KVM lay summary, "smart merge"]: the state is kept as raw (gated) sums and
+ * counts per row, divided only when read; [KVM summary, Core mechanisms 1]: it
+ * is a separate state beside the exact window, so a state plus the window's
+ * tokens is everything a later call needs.
+ * Any pointer may be NULL (skipped).  S_cap = kvm_state_info.max_rows,
+ * R = window + chunk.  Row-indexed arrays hold S_cap rows per sequence; rows
+ * beyond n_rows[s] are undefined.
  * ktype, the read-form key storage type, is float32 on the KVM_F32 path and
  * IEEE fp16 on the KVM_BF16 path: a LayerNorm output over 32 dims has
  * |k| <= sqrt(31), so fp16 keeps more precision than bf16 with no overflow.
@@ -118,6 +122,10 @@ typedef struct kvm_state_view {
   void* val_read;         /* [B*H, S_cap, 64] dtype    read-form value rho * u, u = V / |V| (V/n with KVM_FLAG_NO_VALUE_NORM) */
   int32_t* trace_slot;    /* [B*H, max_tokens] i32     row created/merged into, -1 if not absorbed */
   uint8_t* trace_kind;    /* [B*H, max_tokens] u8      0 sink, 1 append, 2 merge, 255 not absorbed */
+  int64_t position;       /* tokens consumed (kvm_state_read with chunk -1 writes it; kvm_state_load reads it) */
+  void* ring_k;           /* [B*H, R, 64] dtype        window keys, RoPE-rotated at their positions: position p in slot p mod R */
+  void* ring_v;           /* [B*H, R, 64] dtype        window values, same slots */
+  float* ring_l;          /* [B*H, R] f32              window gate logits, same slots */
 } kvm_state_view;
 
 typedef struct kvm_state_info {
@@ -131,7 +139,12 @@ typedef struct kvm_state_info {
 } kvm_state_info;
 
 /* Device workspace size for cfg (bytes; the workspace must be 256-byte aligned).
- * Host only: queues nothing.  Errors: KVM_E_INVALID_ARG. */
+ * The workspace holds the state of [KVM summary, Core mechanisms 1] (raw sums,
+ * counts and radii per row [KVM lay summary, "smart merge"], sized by the
+ * schedule of Core mechanisms 3 at max_tokens), its read-form row versions
+ * (Core mechanisms 2), the last W + C tokens of the window, and RoPE tables
+ * (Core mechanisms 4).  Host only: queues nothing.
+ * Errors: KVM_E_INVALID_ARG. */
 kvm_status kvm_workspace_bytes(const kvm_config* cfg, size_t* bytes);
 
 /* Data-independent schedule ([KVM summary, Core mechanisms 3, 5]): for each of
@@ -141,17 +154,20 @@ kvm_status kvm_workspace_bytes(const kvm_config* cfg, size_t* bytes);
 kvm_status kvm_schedule(const kvm_config* cfg, int64_t n_chunks, int32_t* sinks, int32_t* appends,
                         int32_t* rows_after);
 
-/* Bind a fresh, empty state (position 0) to a caller-owned device workspace
- * of at least kvm_workspace_bytes(cfg).  Queues the workspace initialisation
- * (RoPE table, schedule table, counters) on `stream`.
+/* Bind a fresh, empty state (position 0: no tokens seen, no state rows, the
+ * starting point of the chunk recurrence of [KVM summary, Core mechanisms 1])
+ * to a caller-owned device workspace of at least kvm_workspace_bytes(cfg).
+ * Queues the workspace initialisation (RoPE table, schedule table, counters)
+ * on `stream`.
  * Errors: KVM_E_INVALID_ARG (config; null pointers), KVM_E_WORKSPACE (too
  * small / misaligned), KVM_E_HIP.  On success *out owns host memory that
  * kvm_state_destroy frees; the workspace stays the caller's. */
 kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t workspace_bytes,
                             void* stream, kvm_state** out);
 
-/* Free the host-side state (and its internal stream and events).  Does not
- * touch the workspace.  NULL is allowed. */
+/* Free the host side of a state made by kvm_state_create (the host record of
+ * the state of [KVM summary, Core mechanisms 1], its internal stream and
+ * events).  Does not touch the workspace.  NULL is allowed.  Never fails. */
 kvm_status kvm_state_destroy(kvm_state* st);
 
 /* Chunk-parallel prefill of n_tokens tokens at the state's current position
@@ -182,35 +198,72 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
 kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const void* v,
                            const float* gate_logits, void* out, void* stream);
 
-/* Queue copies of the current state into `dst` (see kvm_state_view).
- * trace_* need KVM_FLAG_TRACE (else KVM_E_INVALID_ARG if requested).
+/* Export the state ([KVM lay summary, "smart merge"]: raw sums and counts,
+ * divided only at read; [KVM summary, Core mechanisms 2]: the read form).
+ *   chunk == -1: the current state.  Every field of `dst` may be requested;
+ *     n_rows and position are host fields written at once; the other arrays
+ *     may be host or device memory (copies queued on `stream`, unified
+ *     addressing).  trace_* need KVM_FLAG_TRACE.  What this fills is what
+ *     kvm_state_load takes to resume.
+ *   0 <= chunk < absorbed_chunks: the state right after absorbed chunk
+ *     `chunk`, i.e. the one query chunk chunk + W/C + 1 attends to.  The
+ *     state keeps past snapshots only as read-form row versions, so only
+ *     n_rows, count, rho, key_read and val_read can be given (device memory:
+ *     a gather kernel writes them); requesting key_sum, val_sum, ring_* or
+ *     trace_* for a past chunk is KVM_E_INVALID_ARG (position is untouched).
  * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
-kvm_status kvm_state_read(const kvm_state* st, const kvm_state_view* dst, void* stream);
+kvm_status kvm_state_read(const kvm_state* st, int64_t chunk, kvm_state_view* dst, void* stream);
+
+/* Resume from an exported state ([KVM summary, Core mechanisms 1]: the state
+ * and the window are the whole carry of the chunk recurrence, so continuing
+ * from them is the same as never having stopped).  `src` holds what
+ * kvm_state_read(chunk -1) wrote for a state with the same configuration:
+ * position; key_sum, val_sum, count, rho (required when the position has
+ * absorbed chunks); ring_k, ring_v, ring_l (required when position > 0);
+ * n_rows (host; optional, checked against the schedule when given);
+ * trace_slot and trace_kind (optional; with KVM_FLAG_TRACE a NULL trace is
+ * cleared to "not absorbed").  key_read and val_read are ignored: the read
+ * form, the unit directions and the row versions are rebuilt from the raw
+ * sums with the same arithmetic the absorption uses, so later calls give the
+ * bits an uninterrupted state would.  Source arrays may be host or device
+ * memory (copies queued on `stream`; the caller keeps them alive until the
+ * stream reaches this call).  The state's previous contents are discarded.
+ * Errors: KVM_E_INVALID_ARG (position outside [0, max_tokens], row counts
+ * that differ from the schedule, a required array missing), KVM_E_STATE
+ * (poisoned state), KVM_E_HIP. */
+kvm_status kvm_state_load(kvm_state* st, const kvm_state_view* src, void* stream);
 
 /* Queue a gather of the read form of the state right after absorbed chunk j,
  * i.e. the state that query chunk j + W/C + 1 attends to ([KVM summary, Core
  * mechanisms 2]: LayerNorm-ed keys, values at the read radius): key
  * [B*H, rows_j, 32] ktype, value rho * u [B*H, rows_j, 64] in cfg.dtype, radius
- * [B*H, rows_j] f32 (device memory; any pointer may be NULL).
+ * [B*H, rows_j] f32 (device memory; any pointer may be NULL).  The dense form
+ * of kvm_state_read(j) without the S_cap row stride.
  * j must be < absorbed_chunks.  Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
 kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, void* val_read, float* rho_read,
                              void* stream);
 
-/* Host-side facts about the state.  Never fails on a valid pointer. */
+/* Host-side facts about the state: position, absorbed chunks and rows of the
+ * chunk recurrence ([KVM summary, Core mechanisms 1, 3]).  Never fails on a
+ * valid pointer. */
 kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info);
 
 /* Check that every absorption scan queued so far on this state finished its
- * work.  When a sequence's state rows are split over several workgroups (a
- * state with few sequences), the workgroups meet once per absorbed chunk to
- * combine their best-matching rows; a workgroup that waits there for a few
- * seconds gives up, so that no kernel can hang, and marks the state.  This
- * call copies that mark to the host and synchronises `stream`.
+ * work ([KVM summary, Core mechanisms 2-3]: every overflowed token is merged
+ * or appended).  When a sequence's state rows are split over several
+ * workgroups (a state with few sequences), the workgroups meet once per
+ * absorbed chunk to combine their best-matching rows; a workgroup that waits
+ * there for a few seconds gives up, so that no kernel can hang, and marks the
+ * state.  This call copies that mark to the host and synchronises `stream`.
  * Errors: KVM_E_INVALID_ARG; KVM_E_STATE if the state is already poisoned;
  * KVM_E_HIP if a scan gave up (the state is then poisoned) or on a HIP failure. */
 kvm_status kvm_state_check(kvm_state* st, void* stream);
 
-/* Return the state to position 0 with an empty compressed state (the RoPE and
- * schedule tables are kept).  Queues a counter reset on `stream`.
+/* Return the state to position 0 with an empty compressed state, the start of
+ * the chunk recurrence ([KVM summary, Core mechanisms 1]); the RoPE and
+ * schedule tables are kept.  Queues a counter reset on `stream`.  Reset also
+ * clears the poison of an earlier KVM_E_HIP: it rewrites every counter and
+ * exchange buffer the kernels read, and later calls rewrite the rest.
  * Errors: KVM_E_INVALID_ARG, KVM_E_HIP. */
 kvm_status kvm_state_reset(kvm_state* st, void* stream);
 
@@ -235,14 +288,19 @@ typedef struct kvm_profile_times {
 
 /* Record a HIP event pair, on the stream the launch uses, around every later
  * kernel launch of the phases in `phases` (a KVM_PROFILE_* mask; 0 stops
- * recording).  Errors: KVM_E_INVALID_ARG (NULL state, bits outside ALL). */
+ * recording).  Measurement only: the phases are the steps of [KVM summary,
+ * Core mechanisms 1-5] (absorption, attention, window upkeep).
+ * Errors: KVM_E_INVALID_ARG (NULL state, bits outside ALL). */
 kvm_status kvm_profile_enable(kvm_state* st, int phases);
 
 /* Wait for the recorded events (this one call synchronises the host with
  * them), add up the elapsed times per phase into *out, and clear the record.
+ * Measurement only (phases as for kvm_profile_enable).
  * Errors: KVM_E_INVALID_ARG, KVM_E_HIP. */
 kvm_status kvm_profile_read(kvm_state* st, kvm_profile_times* out);
 
+/* Name of a status code, and the calling thread's message for the last failed
+ * call.  Error reporting of this library; no passage of the method defines it. */
 const char* kvm_status_str(kvm_status s);
 const char* kvm_last_error(void);
 

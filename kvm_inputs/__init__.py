@@ -42,6 +42,7 @@ class LayerConfig:
     rope_dims: int = 32
     rope_theta: float = 10000.0
     ln_eps: float = 1e-5
+    softmax_scale: float = 0.0  # logit scale, 0 = 1/sqrt(head_dim)
     exponent: float = 0.5      # power: capacity = ceil(alpha * T**exponent)
     value_norm: bool = True    # layer variants (False = the ablation without it)
     sink_protect: bool = True

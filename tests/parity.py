@@ -4,15 +4,22 @@ the GPU's decisions (teacher forcing), compare.
 Decision parity rule: the GPU's append set and merge targets must equal the
 oracle's own choice given the same history, except where the oracle's fp64
 margin is below NEAR_TIE (such cases are counted and reported, not failed).
-Output parity: fp32 path max |diff| <= 1e-4; bf16 path, for every query row t,
-max_d |diff[t, d]| <= 2e-2 * RMS_d(oracle[t, :]).  The bf16 bound is taken per
-row because outputs of early queries (few keys) are ~10x larger than later
-ones, and rounding even the exact output to bf16 exceeds 2e-2 of the global RMS
-there.  The global RMS error is reported beside it.
+Output parity: fp32 path max |diff| <= 1e-4.  bf16 path, per sequence: for
+every query row t, max_d |diff[t, d]| <= 2e-2 * max(RMS(oracle), RMS_d(oracle[t, :])),
+and the RMS of the error over all rows <= 2e-2 * RMS(oracle).  The reference is
+the sequence's output RMS, except on rows whose own RMS is larger: outputs of
+early queries (few keys) are up to ~10x the sequence's RMS, and rounding even
+the exact output to bf16 there exceeds 2e-2 of the sequence's RMS, so those
+rows are held to 2e-2 of their own RMS.
+
+When the environment variable KVM_PARITY_RECORD names a file, the decision
+and output figures of every check are gathered per label and written there as
+JSON at the end of the session (tests/conftest.py).
 """
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional
 
@@ -75,6 +82,9 @@ class DecisionReport:
     merge_mismatch: int = 0           # failures
     merge_near_tie_diff: int = 0      # reported
     near_tie_merges: int = 0          # merges whose oracle margin < NEAR_TIE (whatever the GPU chose)
+    near_tie_appends: int = 0         # append choices whose oracle margin < NEAR_TIE
+    min_merge_margin: float = math.inf    # smallest oracle top-1 minus top-2 cosine among checked merges
+    min_append_margin: float = math.inf   # smallest oracle surprise gap across an append boundary
     details: List[str] = field(default_factory=list)
 
     @property
@@ -83,8 +93,10 @@ class DecisionReport:
 
     def merge(self, o: "DecisionReport"):
         for f in ("appends_checked", "append_mismatch", "append_near_tie_diff", "merges_checked", "merge_mismatch",
-                  "merge_near_tie_diff", "near_tie_merges"):
+                  "merge_near_tie_diff", "near_tie_merges", "near_tie_appends"):
             setattr(self, f, getattr(self, f) + getattr(o, f))
+        self.min_merge_margin = min(self.min_merge_margin, o.min_merge_margin)
+        self.min_append_margin = min(self.min_append_margin, o.min_append_margin)
         self.details += o.details[:20]
 
 
@@ -96,6 +108,9 @@ def compare_decisions(res: O.SeqResult, slot_s, kind_s, p: O.Params) -> Decision
         toks = range(lg.j * C, (lg.j + 1) * C)
         gpu_app = sorted(t for t in toks if kind_s[t] == O.KIND_APPEND)
         rep.appends_checked += 1
+        rep.min_append_margin = min(rep.min_append_margin, lg.append_margin)
+        if lg.append_margin < NEAR_TIE:
+            rep.near_tie_appends += 1
         if gpu_app != lg.appended:
             if lg.append_margin < NEAR_TIE:
                 rep.append_near_tie_diff += 1
@@ -107,6 +122,7 @@ def compare_decisions(res: O.SeqResult, slot_s, kind_s, p: O.Params) -> Decision
                 continue
             rep.merges_checked += 1
             mg = lg.assign_margin[t]
+            rep.min_merge_margin = min(rep.min_merge_margin, mg)
             if mg < NEAR_TIE:
                 rep.near_tie_merges += 1
             if int(slot_s[t]) != a:
@@ -122,7 +138,8 @@ def check_outputs(dtype: str, got: np.ndarray, want: np.ndarray):
     """(ok, worst, bound, rms_err_over_rms) over the rows of `want` that are finite.
 
     fp32: worst = max |diff|, bound = 1e-4.
-    bf16: worst = max over rows of max|diff| / RMS(row of want), bound = 2e-2."""
+    bf16: worst = max over rows of max|diff| / max(RMS(want), RMS(row of want)),
+    bound = 2e-2; the RMS error over all rows must also be <= 2e-2 of RMS(want)."""
     want = want.reshape(-1, want.shape[-1])
     got = got.reshape(-1, got.shape[-1])
     rows = np.all(np.isfinite(want), axis=1)
@@ -135,8 +152,54 @@ def check_outputs(dtype: str, got: np.ndarray, want: np.ndarray):
         worst = float(err.max())
         return worst <= TOL_F32_ABS, worst, TOL_F32_ABS, rel_rms
     row_rms = np.sqrt(np.mean(w ** 2, axis=1))
-    worst = float(np.max(err.max(axis=1) / np.maximum(row_rms, 1e-30)))
-    return worst <= TOL_BF16_REL_RMS, worst, TOL_BF16_REL_RMS, rel_rms
+    ref = np.maximum(row_rms, np.sqrt(np.mean(w ** 2)))
+    worst = float(np.max(err.max(axis=1) / np.maximum(ref, 1e-30)))
+    return worst <= TOL_BF16_REL_RMS and rel_rms <= TOL_BF16_REL_RMS, worst, TOL_BF16_REL_RMS, rel_rms
+
+
+# ------------------------------------------------------------------ record of the checks
+
+RECORD: Dict[str, dict] = {}
+
+
+def record(label: str, rep: Optional[DecisionReport] = None, worst: Optional[float] = None,
+           rel_rms: Optional[float] = None, **extra):
+    """Add one sequence's figures to the per-label totals (written out when KVM_PARITY_RECORD is set)."""
+    r = RECORD.setdefault(label, {"sequences": 0, "appends_checked": 0, "append_near_tie_diff": 0,
+                                  "near_tie_appends": 0, "merges_checked": 0, "merge_near_tie_diff": 0,
+                                  "near_tie_merges": 0, "decision_failures": 0, "min_merge_margin": None,
+                                  "min_append_margin": None, "worst_output": None, "max_rel_rms": None})
+    r["sequences"] += 1
+    if rep is not None:
+        for f in ("appends_checked", "append_near_tie_diff", "near_tie_appends", "merges_checked",
+                  "merge_near_tie_diff", "near_tie_merges"):
+            r[f] += getattr(rep, f)
+        r["decision_failures"] += rep.append_mismatch + rep.merge_mismatch
+        for f in ("min_merge_margin", "min_append_margin"):
+            v = getattr(rep, f)
+            if math.isfinite(v):
+                r[f] = v if r[f] is None else min(r[f], v)
+    if worst is not None:
+        r["worst_output"] = worst if r["worst_output"] is None else max(r["worst_output"], worst)
+    if rel_rms is not None:
+        r["max_rel_rms"] = rel_rms if r["max_rel_rms"] is None else max(r["max_rel_rms"], rel_rms)
+    for k, v in extra.items():
+        if isinstance(v, (int, float)) and not isinstance(v, bool) and isinstance(r.get(k), (int, float)):
+            r[k] += v
+        elif isinstance(v, list):
+            r.setdefault(k, []).extend(v)
+        else:
+            r.setdefault(k, v)
+
+
+def write_record():
+    path = os.environ.get("KVM_PARITY_RECORD")
+    if not path or not RECORD:
+        return
+    import json
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump({"near_tie_bar": NEAR_TIE, "checks": RECORD}, f, indent=1, sort_keys=True)
 
 
 def check_state(res: O.SeqResult, state: dict, s: int, dtype: str):
@@ -197,8 +260,35 @@ def oracle_check(w: LayerConfig, inp: Inputs, s: int, n: int, out, slot, kind, s
     print(f"   [{label} seq {s}] appends {rep.appends_checked} (near-tie diffs {rep.append_near_tie_diff}), "
           f"merges {rep.merges_checked} (near-tie diffs {rep.merge_near_tie_diff}, near ties {rep.near_tie_merges}); "
           f"output worst {worst:.3g} <= {bound:.3g}, rms rel {rel:.3g}", flush=True)
+    record(label, rep, worst, rel)
     assert rep.ok, rep.details[:10]
-    assert ok, f"output parity: worst {worst} > {bound}"
+    assert ok, f"output parity: worst {worst} (bound {bound}), rms rel {rel}"
     if state is not None:
         check_state(res, state, s, w.dtype)
     return rep, worst, rel, res
+
+
+def free_running_check(w: LayerConfig, inp: Inputs, s: int, n: int, slot, kind, forced_rep: Optional[DecisionReport],
+                       label: str):
+    """The oracle on its own (no teacher forcing, absorption only) against the GPU's decisions
+    for sequence s.  Returns the first chunk whose decisions differ (None if none).
+
+    With no near-tie flip in the teacher-forced comparison (the GPU took the oracle's own
+    decision at every chunk), both run the same history, so every decision must agree; a
+    divergence is then a failure.  forced_rep None: the teacher-forced report is computed here."""
+    p = O.Params.of(w)
+    arr = seq_arrays(inp, s, n)
+    if forced_rep is None:
+        res_f = O.prefill(*arr, p, forced=forced_map(slot[s], kind[s]), attend_chunks=set())
+        forced_rep = compare_decisions(res_f, slot[s], kind[s], p)
+    res = O.prefill(*arr, p, attend_chunks=set())
+    diff = np.nonzero((res.kind != kind[s]) | (res.slot != slot[s]))[0]
+    first = int(diff[0]) // p.chunk if len(diff) else None
+    flips = forced_rep.append_near_tie_diff + forced_rep.merge_near_tie_diff
+    record(label, None, identical=int(first is None), near_tie_flips=flips,
+           first_divergence=[] if first is None else [[s, first]])
+    print(f"   [{label} seq {s}] free-running: first differing chunk {first}, near-tie flips {flips}", flush=True)
+    assert forced_rep.ok, forced_rep.details[:10]
+    if flips == 0:
+        assert first is None, f"seq {s}: free-running oracle diverges at chunk {first} without a near-tie flip"
+    return first

@@ -12,8 +12,8 @@ import torch
 import oracle.kvm_oracle as O
 from compressed_kv_state_amd import KVM_E_CAPACITY, KVM_E_STATE, KvmConfig, KvmError, KvmState
 from kvm_inputs import WORKLOADS, LayerConfig, make_inputs
-from tests.parity import (check_outputs, forced_map, oracle_check, run_prefill, run_prefill_decode, seq_arrays,
-                          to_gpu)
+from tests.parity import (check_outputs, forced_map, free_running_check, oracle_check, run_prefill,
+                          run_prefill_decode, seq_arrays, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,35 +39,66 @@ def test_tiny_f32_workload_exact():
     assert check_outputs("f32", out[0], free.out)[0]
 
 
-def test_120m_fixed256_workload():
-    print("case: 120M-shaped fixed-256 workload, 4x12x8192, oracle on 4 sequences", flush=True)
-    inp = make_inputs(W1)
-    out, slot, kind, state, _ = run_prefill(W1, inp)
-    for s in (0, 13, 30, 47):
-        oracle_check(W1, inp, s, W1.n_tokens, out, slot, kind, state, label="120m")
+_RUNS = {}
+_FORCED = {}
 
 
-def test_350m_sqrt_workload_and_planted_keys():
-    print("case: 350M-shaped sqrt workload, 2x16x32768, oracle on 2 sequences", flush=True)
-    inp = make_inputs(W2)
-    out, slot, kind, state, _ = run_prefill(W2, inp)
+def workload_run(w):
+    """One GPU prefill of a whole workload, shared by the tests of this module."""
+    if w.name not in _RUNS:
+        inp = make_inputs(w)
+        out, slot, kind, state, st = run_prefill(w, inp)
+        st.close()
+        _RUNS[w.name] = (inp, out, slot, kind, state)
+    return _RUNS[w.name]
+
+
+def test_120m_fixed256_workload_all_sequences():
+    print("case: 120M-shaped fixed-256 workload, 4x12x8192, oracle on all 48 sequences", flush=True)
+    inp, out, slot, kind, state = workload_run(W1)
+    for s in range(W1.seqs):
+        rep, _, _, _ = oracle_check(W1, inp, s, W1.n_tokens, out, slot, kind, state, label=W1.name)
+        _FORCED[(W1.name, s)] = rep
+
+
+def test_120m_fixed256_free_running_decisions():
+    print("case: 120M-shaped workload, free-running oracle decisions on all 48 sequences", flush=True)
+    inp, out, slot, kind, state = workload_run(W1)
+    for s in range(W1.seqs):
+        free_running_check(W1, inp, s, W1.n_tokens, slot, kind, _FORCED.get((W1.name, s)), W1.name + " free-running")
+
+
+def test_350m_sqrt_workload_all_sequences_and_planted_keys():
+    print("case: 350M-shaped sqrt workload, 2x16x32768, oracle on all 32 sequences", flush=True)
+    inp, out, slot, kind, state = workload_run(W2)
     # I12: every planted isolated key is appended, in every sequence
     for s in range(W2.seqs):
         assert np.all(kind[s][inp.planted_pos[s]] == O.KIND_APPEND), s
     assert int(state["n_rows"][0]) == 1440
-    for s in (0, 21):
-        oracle_check(W2, inp, s, W2.n_tokens, out, slot, kind, state, label="350m")
+    for s in range(W2.seqs):
+        rep, _, _, _ = oracle_check(W2, inp, s, W2.n_tokens, out, slot, kind, state, label=W2.name)
+        _FORCED[(W2.name, s)] = rep
+
+
+def test_350m_sqrt_free_running_decisions():
+    print("case: 350M-shaped workload, free-running oracle decisions on all 32 sequences", flush=True)
+    inp, out, slot, kind, state = workload_run(W2)
+    for s in range(W2.seqs):
+        free_running_check(W2, inp, s, W2.n_tokens, slot, kind, _FORCED.get((W2.name, s)), W2.name + " free-running")
+    _RUNS.pop(W2.name, None)
 
 
 def test_long_saturating_workload_sampled():
-    print("case: long saturating workload, 1x16x131072, oracle on 1 sequence, sampled chunks", flush=True)
+    print("case: long saturating workload, 1x16x131072, oracle on 2 sequences, sampled chunks", flush=True)
     inp = make_inputs(W3)
     out, slot, kind, state, _ = run_prefill(W3, inp)
     assert int(state["n_rows"][0]) == 4096
     C = W3.chunk
-    chunks = {0, 1, 2, 3, 4, 200, 258, 259, 511}
+    chunks = {0, 1, 2, 3, 4, 200, 257, 258, 259, 300, 400, 511}
     rows = np.concatenate([np.arange(c * C, (c + 1) * C) for c in sorted(chunks)])
-    oracle_check(W3, inp, 9, W3.n_tokens, out, slot, kind, state, attend_chunks=chunks, rows=rows, label="long")
+    for s in (3, 9):
+        oracle_check(W3, inp, s, W3.n_tokens, out, slot, kind, state, attend_chunks=chunks, rows=rows,
+                     label=W3.name + " (sampled chunks)")
 
 
 def test_deterministic_repeat():
@@ -114,6 +145,17 @@ def test_window_covers_sequence_is_plain_causal_attention():
     assert np.all(kind == O.KIND_NONE)
     for s in range(2):
         oracle_check(w, inp, s, 300, out, slot, kind, None, label="W>=N")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk,window", [(64, 128), (128, 256)])
+def test_given_softmax_scale(dtype, chunk, window):
+    w = small(dtype, chunk=chunk, window=window, n_tokens=3 * window + chunk + 9, softmax_scale=0.21)
+    print(f"case: softmax scale 0.21 {dtype} C={chunk}", flush=True)
+    inp = make_inputs(w)
+    out, slot, kind, state, _ = run_prefill(w, inp)
+    for s in range(w.seqs):
+        oracle_check(w, inp, s, w.n_tokens, out, slot, kind, state, label="softmax scale")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
