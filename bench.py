@@ -391,55 +391,66 @@ def copy_calibration():
     log(f"copy calibration: 3 copies of {n} bytes")
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str):
-    """Reduce two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) to the summary bench reads.
-
-    The scale of each counter is 1 GiB over its mean reading on the 1 GiB device copies of
-    --copy-calibration (the copy's dispatches are the large ones of the copy kernel)."""
+def _counter_rows(path, counter):
+    """{kernel name: [values in dispatch order]} for one counter of a rocprofv3 --pmc CSV."""
     import csv
+    vals = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            vals.setdefault(row.get("Kernel_Name", ""), []).append(float(row["Counter_Value"]))
+    return vals
 
-    def per_kernel(path, counter):
-        vals = {}
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter:
-                    continue
-                vals.setdefault(row.get("Kernel_Name", ""), []).append(float(row["Counter_Value"]))
-        return vals
 
-    def copies(d):
-        v = [x for k, xs in d.items() if "copyBuffer" in k or "copy" in k.lower() for x in xs]
+def _copy_scale(d):
+    """KiB moved per KiB counted, from the 1 GiB device copies of --copy-calibration."""
+    v = [x for k, xs in d.items() if "copyBuffer" in k or "copy" in k.lower() for x in xs]
+    if not v:
+        raise SystemExit("no copy-kernel dispatches in the counter CSV (run with --copy-calibration)")
+    big = max(v)
+    v = [x for x in v if x >= 0.5 * big]
+    mean = sum(v) / len(v)
+    return (1 << 30) / 1024.0 / mean, mean
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str, kernel: str = ATTN_KERNEL,
+                       title: str = ""):
+    """Reduce two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) to a summary of `kernel`.
+
+    Each counter is scaled by 1 GiB over its mean reading on the 1 GiB device copies of
+    --copy-calibration (the copy's dispatches are the large ones of the copy kernel).  For the
+    attention kernel the summary also carries the traffic figure bench.py reads, tied to a hash
+    of the kernel's source text."""
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
+    write = _counter_rows(write_csv, "WRITE_SIZE")
+    sf, cf = _copy_scale(fetch)
+    sw, cw = _copy_scale(write)
+
+    def pick(d):
+        v = [x for k, xs in d.items() if kernel in k for x in xs]
         if not v:
-            raise SystemExit("no copy-kernel dispatches in the counter CSV (run with --copy-calibration)")
-        big = max(v)
-        v = [x for x in v if x >= 0.5 * big]
-        return sum(v) / len(v)
+            raise SystemExit(f"no {kernel} dispatches in the counter CSV")
+        return v
 
-    def kernel(d):
-        v = [x for k, xs in d.items() if ATTN_KERNEL in k for x in xs]
-        if not v:
-            raise SystemExit(f"no {ATTN_KERNEL} dispatches in the counter CSV")
-        return sum(v) / len(v), len(v)
-
-    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
-    write = per_kernel(write_csv, "WRITE_SIZE")
-    copy_kib = (1 << 30) / 1024.0
-    cf, cw = copies(fetch), copies(write)
-    sf, sw = copy_kib / cf, copy_kib / cw
-    (f_kib, nf), (w_kib, nw) = kernel(fetch), kernel(write)
+    fv, wv = pick(fetch), pick(write)
+    f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
     traffic = (f_kib * sf + w_kib * sw) * 1024.0
     with open(out_md, "w") as f:
-        f.write(f"# {ATTN_KERNEL} HBM traffic, 350M-shaped sqrt workload (B=2, H=16, N=32768), per launch\n\n")
+        f.write(f"# {kernel} HBM traffic per dispatch{': ' + title if title else ''}\n\n")
         f.write(f"Command (one pass per counter): `{command}`\n\n")
-        f.write(f"| counter | {ATTN_KERNEL} KiB/dispatch (mean of {nf}/{nw}) | copy kernel KiB/dispatch "
-                f"(1 GiB moved) | scale |\n|---|---|---|---|\n")
-        f.write(f"| FETCH_SIZE | {f_kib:.0f} | {cf:.0f} | {sf:.4f} |\n")
-        f.write(f"| WRITE_SIZE | {w_kib:.0f} | {cw:.0f} | {sw:.4f} |\n\n")
-        f.write("A prefill launches the attention in pieces beside the scan; the figures are means over\n"
-                "the pieces of the profiled prefills, like bench.py's per-launch FLOPs and time.\n\n")
-        f.write(f"traffic_bytes_per_launch: {traffic:.6e}\n")
-        f.write(f"kernel_source_sha256_16: {kernel_sha()}  (source text of {ATTN_KERNEL})\n")
-    print(f"wrote {out_md}: traffic {traffic / 1e9:.3f} GB per launch")
+        f.write(f"| counter | {kernel} KiB/dispatch (mean of {len(fv)}/{len(wv)}) | total KiB | copy kernel "
+                f"KiB/dispatch (1 GiB moved) | scale |\n|---|---|---|---|---|\n")
+        f.write(f"| FETCH_SIZE | {f_kib:.0f} | {sum(fv):.0f} | {cf:.0f} | {sf:.4f} |\n")
+        f.write(f"| WRITE_SIZE | {w_kib:.0f} | {sum(wv):.0f} | {cw:.0f} | {sw:.4f} |\n\n")
+        f.write(f"bytes per dispatch (scaled fetch + write): {traffic:.6e}\n")
+        f.write(f"bytes over all dispatches: {(sum(fv) * sf + sum(wv) * sw) * 1024.0:.6e}\n")
+        if kernel == ATTN_KERNEL:
+            f.write("\nA prefill launches the attention in pieces beside the scan; the figures are means over\n"
+                    "the pieces of the profiled prefills, like bench.py's per-launch FLOPs and time.\n\n")
+            f.write(f"traffic_bytes_per_launch: {traffic:.6e}\n")
+            f.write(f"kernel_source_sha256_16: {kernel_sha()}  (source text of {ATTN_KERNEL})\n")
+    print(open(out_md).read())
 
 
 def summarize_trace(db: str, out_md: str, command: str, title: str):
@@ -490,6 +501,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true", help="add a 1 GiB device copy (counter scaling)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
+    ap.add_argument("--counter-kernel", default=ATTN_KERNEL, help="kernel the counter summary describes")
+    ap.add_argument("--counter-out", default=COUNTERS_MD, help="where the counter summary goes")
+    ap.add_argument("--counter-title", default="", help="workload line of the counter summary")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("DB", "OUT_MD", "COMMAND", "TITLE"))
     args = ap.parse_args()
 
@@ -497,8 +511,8 @@ def main():
         summarize_trace(*args.summarize_trace)
         return 0
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], COUNTERS_MD,
-                           args.summarize_counters[2])
+        summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.counter_out,
+                           args.summarize_counters[2], args.counter_kernel, args.counter_title)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
