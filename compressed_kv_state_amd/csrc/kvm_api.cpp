@@ -84,15 +84,12 @@ int64_t max_absorbable_chunks(const kvm_config& c) {
   return j > 0 ? j : 0;
 }
 
-// Per absorbed chunk j: sinks created, rows appended, rows before.
-void build_schedule(const kvm_config& c, int64_t n, std::vector<int32_t>& sinks, std::vector<int32_t>& app,
-                    std::vector<int32_t>& before) {
-  sinks.resize(n);
-  app.resize(n);
-  before.resize(n);
+// Per absorbed chunk j < n: f(j, sinks created, rows appended, rows before).
+template <typename F>
+void for_each_chunk(const kvm_config& c, int64_t n, F f) {
   int64_t rows = 0, nsink = 0;
   for (int64_t j = 0; j < n; ++j) {
-    before[j] = (int32_t)rows;
+    const int64_t before = rows;
     int64_t cand = c.chunk;
     const int64_t sk = std::min<int64_t>(c.n_sinks - nsink, cand);
     nsink += sk;
@@ -102,9 +99,20 @@ void build_schedule(const kvm_config& c, int64_t n, std::vector<int32_t>& sinks,
     if (m < 0) m = 0;
     if (m > cand) m = cand;
     rows += m;
-    sinks[j] = (int32_t)sk;
-    app[j] = (int32_t)m;
+    f(j, (int32_t)sk, (int32_t)m, (int32_t)before);
   }
+}
+
+void build_schedule(const kvm_config& c, int64_t n, std::vector<int32_t>& sinks, std::vector<int32_t>& app,
+                    std::vector<int32_t>& before) {
+  sinks.resize(n);
+  app.resize(n);
+  before.resize(n);
+  for_each_chunk(c, n, [&](int64_t j, int32_t sk, int32_t m, int32_t b) {
+    sinks[j] = sk;
+    app[j] = m;
+    before[j] = b;
+  });
 }
 
 kvm_status validate(const kvm_config* c) {
@@ -161,24 +169,28 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-kvm_status plan(const kvm_config* c, Plan& p) {
+// Sizes and workspace offsets for cfg.  keep_sched: also fill p.sched (host memory);
+// without it nothing is allocated.
+kvm_status plan(const kvm_config* c, Plan& p, bool keep_sched = true) {
   kvm_status st = validate(c);
   if (st != KVM_OK) return st;
   const int64_t J = max_absorbable_chunks(*c);
-  std::vector<int32_t> sk, app, before;
-  build_schedule(*c, J, sk, app, before);
   int64_t S_cap = 0, idx_total = 0;
-  p.sched.assign((size_t)J * 4, 0);
-  for (int64_t j = 0; j < J; ++j) {
-    const int64_t after = (int64_t)before[j] + sk[j] + app[j];
-    p.sched[4 * j + 0] = sk[j];
-    p.sched[4 * j + 1] = app[j];
-    p.sched[4 * j + 2] = before[j];
-    p.sched[4 * j + 3] = (int32_t)idx_total;
+  bool too_many = false;
+  if (keep_sched) p.sched.assign((size_t)J * 4, 0);
+  for_each_chunk(*c, J, [&](int64_t j, int32_t sk, int32_t app, int32_t before) {
+    const int64_t after = (int64_t)before + sk + app;
+    if (keep_sched) {
+      p.sched[4 * j + 0] = sk;
+      p.sched[4 * j + 1] = app;
+      p.sched[4 * j + 2] = before;
+      p.sched[4 * j + 3] = (int32_t)idx_total;
+    }
     idx_total += after;
     if (after > S_cap) S_cap = after;
-    if (idx_total >= ((int64_t)1 << 31)) return fail(KVM_E_INVALID_ARG, "index lists exceed 2^31 entries; lower max_tokens");
-  }
+    if (idx_total >= ((int64_t)1 << 31)) too_many = true;
+  });
+  if (too_many) return fail(KVM_E_INVALID_ARG, "index lists exceed 2^31 entries; lower max_tokens");
   if (S_cap > (1 << 22)) return fail(KVM_E_INVALID_ARG, "state would exceed 2^22 rows");
   kvm::Dims& m = p.m;
   m.BH = c->batch * c->heads;
@@ -245,6 +257,34 @@ kvm_status plan(const kvm_config* c, Plan& p) {
   p.xerr = take(4);
   p.total = off;
   return KVM_OK;
+}
+
+// Device regions of a workspace at `b` laid out by plan `p`.
+void carve(const Plan& p, char* b, kvm::Dev& d) {
+  d.key_sum = reinterpret_cast<float*>(b + p.key_sum);
+  d.val_sum = reinterpret_cast<float*>(b + p.val_sum);
+  d.count = reinterpret_cast<int*>(b + p.count);
+  d.rho = reinterpret_cast<float*>(b + p.rho);
+  d.unit = b + p.unit;
+  d.kread = b + p.kread;
+  d.vread = b + p.vread;
+  d.pkey = b + p.pkey;
+  d.pval = b + p.pval;
+  d.prho = reinterpret_cast<float*>(b + p.prho);
+  d.pcount = reinterpret_cast<int*>(b + p.pcount);
+  d.idx = reinterpret_cast<int*>(b + p.idx);
+  d.tslot = reinterpret_cast<int*>(b + p.tslot);
+  d.tkind = reinterpret_cast<uint8_t*>(b + p.tkind);
+  d.ring_k = b + p.ring_k;
+  d.ring_v = b + p.ring_v;
+  d.ring_l = reinterpret_cast<float*>(b + p.ring_l);
+  d.rope_cos = reinterpret_cast<float*>(b + p.rope_cos);
+  d.krot = p.m.bf16 && p.m.C >= 128 ? b + p.krot : nullptr;
+  d.rope_sin = reinterpret_cast<float*>(b + p.rope_sin);
+  d.sched = reinterpret_cast<int4*>(b + p.sch);
+  d.nver = reinterpret_cast<int*>(b + p.nver);
+  d.xbuf = reinterpret_cast<uint2*>(b + p.xbuf);
+  d.xerr = reinterpret_cast<int*>(b + p.xerr);
 }
 
 kvm_status hip_fail(kvm_state* st, hipError_t e, const char* what) {
@@ -392,37 +432,12 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     st->cfg = *cfg;
     st->m = p.m;
     st->sched = std::move(p.sched);
-    char* b = reinterpret_cast<char*>(d_workspace);
-    kvm::Dev& d = st->d;
-    d.key_sum = reinterpret_cast<float*>(b + p.key_sum);
-    d.val_sum = reinterpret_cast<float*>(b + p.val_sum);
-    d.count = reinterpret_cast<int*>(b + p.count);
-    d.rho = reinterpret_cast<float*>(b + p.rho);
-    d.unit = b + p.unit;
-    d.kread = b + p.kread;
-    d.vread = b + p.vread;
-    d.pkey = b + p.pkey;
-    d.pval = b + p.pval;
-    d.prho = reinterpret_cast<float*>(b + p.prho);
-    d.pcount = reinterpret_cast<int*>(b + p.pcount);
-    d.idx = reinterpret_cast<int*>(b + p.idx);
-    d.tslot = reinterpret_cast<int*>(b + p.tslot);
-    d.tkind = reinterpret_cast<uint8_t*>(b + p.tkind);
-    d.ring_k = b + p.ring_k;
-    d.ring_v = b + p.ring_v;
-    d.ring_l = reinterpret_cast<float*>(b + p.ring_l);
-    d.rope_cos = reinterpret_cast<float*>(b + p.rope_cos);
-    d.krot = p.m.bf16 && p.m.C >= 128 ? b + p.krot : nullptr;
-    d.rope_sin = reinterpret_cast<float*>(b + p.rope_sin);
-    d.sched = reinterpret_cast<int4*>(b + p.sch);
-    d.nver = reinterpret_cast<int*>(b + p.nver);
-    d.xbuf = reinterpret_cast<uint2*>(b + p.xbuf);
-    d.xerr = reinterpret_cast<int*>(b + p.xerr);
+    carve(p, reinterpret_cast<char*>(d_workspace), st->d);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = clear_counters(st, true, hs);
     if (e == hipSuccess && !st->sched.empty())
-      e = hipMemcpyAsync(d.sched, st->sched.data(), st->sched.size() * 4, hipMemcpyHostToDevice, hs);
-    if (e == hipSuccess) e = kvm::launch_init(st->m, d, (double)cfg->rope_theta, hs);
+      e = hipMemcpyAsync(st->d.sched, st->sched.data(), st->sched.size() * 4, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = kvm::launch_init(st->m, st->d, (double)cfg->rope_theta, hs);
     if (e != hipSuccess) {
       delete st;
       return fail(KVM_E_HIP, std::string("state initialisation: ") + hipGetErrorString(e));
@@ -528,6 +543,49 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
   if (err != hipSuccess) return hip_fail(st, err, "ring launch");
   st->pos = e;
   st->absorbed = a1;
+  return KVM_OK;
+}
+
+kvm_status kvm_prefill_noalloc(const kvm_config* cfg, const void* q, const void* k, const void* v,
+                               const float* gate_logits, void* out, int64_t n_tokens, void* stream) {
+  // No device or host allocation on the success path: the plan keeps no
+  // schedule vector, the schedule table is computed on the device, counters are
+  // cleared by a fill kernel, and the workspace is the static scratch.
+  Plan p;
+  kvm_status s = plan(cfg, p, false);
+  if (s != KVM_OK) return s;
+  if (cfg->flags & KVM_FLAG_TRACE) return fail(KVM_E_INVALID_ARG, "KVM_FLAG_TRACE needs a state to read the trace from");
+  if (cfg->sched == KVM_SCHED_POWER)
+    return fail(KVM_E_INVALID_ARG, "the power schedule is not available here (the device builds integer schedules only)");
+  if (p.total > kvm::kScratchBytes)
+    return fail(KVM_E_WORKSPACE, "the configuration needs " + std::to_string(p.total) +
+                                     " bytes of workspace; the static scratch holds " + std::to_string(kvm::kScratchBytes));
+  if (n_tokens < 0 || n_tokens > cfg->max_tokens) return fail(KVM_E_INVALID_ARG, "n_tokens must be in [0, max_tokens]");
+  if (n_tokens == 0) return KVM_OK;
+  if (!q || !k || !v || !gate_logits || !out) return fail(KVM_E_INVALID_ARG, "NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
+  const kvm::Dims& m = p.m;
+  const size_t bytes = (size_t)m.BH * (size_t)n_tokens * 64 * (m.bf16 ? 2 : 4);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return fail(KVM_E_INVALID_ARG, "out aliases an input");
+  void* base = nullptr;
+  hipError_t err = kvm::scratch_address(&base);
+  if (err != hipSuccess) return fail(KVM_E_HIP, std::string("scratch address: ") + hipGetErrorString(err));
+  kvm::Dev d{};
+  carve(p, reinterpret_cast<char*>(base), d);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int64_t c_last = (n_tokens - 1) / m.C;
+  const int64_t a1 = std::max<int64_t>(0, c_last - m.W / m.C);   // chunks the last query chunk needs
+  int s_max = 0;                                                 // rows of the last snapshot read
+  for_each_chunk(*cfg, a1, [&](int64_t, int32_t sk, int32_t app, int32_t before) { s_max = before + sk + app; });
+  const kvm::SchedParams sp{m.C, m.ns, cfg->sched, cfg->max_slots, cfg->alpha, m.J_cap};
+  kvm::Src src{q, k, v, gate_logits, 0, n_tokens};
+  err = kvm::launch_noalloc_init(m, d, sp, (double)cfg->rope_theta, hs);
+  if (err == hipSuccess && d.krot) err = kvm::launch_rope_keys(m, d, src, hs);
+  if (err == hipSuccess) err = kvm::launch_scan(m, d, src, 0, (int)a1, hs);
+  if (err == hipSuccess) err = kvm::launch_attn(m, d, src, 0, (int)(c_last + 1), n_tokens, out, s_max, hs);
+  if (err != hipSuccess) return fail(KVM_E_HIP, std::string("prefill launch: ") + hipGetErrorString(err));
   return KVM_OK;
 }
 

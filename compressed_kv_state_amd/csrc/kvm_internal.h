@@ -80,6 +80,26 @@ struct Src {
   int64_t n_call;
 };
 
+// The data-independent size schedule as the device computes it (integer schedules only:
+// fixed, sqrt and saturating; the same rules as the host's).
+struct SchedParams {
+  int C;          // chunk
+  int ns;         // sinks
+  int sched;      // kvm_sched (FIXED, SQRT or SATURATING)
+  int max_slots;
+  int alpha;
+  int J;          // chunks to describe
+};
+
+// Bytes of the library's static device scratch (one per GPU, for kvm_prefill_noalloc).
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+// Device address of the static scratch on the current device (looked up once per device).
+hipError_t scratch_address(void** out);
+// Initialise a workspace carved from the scratch for one call: RoPE table, schedule table
+// (computed on the device), and zeroed counters and exchange buffers (fill kernels, no memset).
+hipError_t launch_noalloc_init(const Dims& m, const Dev& d, const SchedParams& sp, double rope_theta,
+                               hipStream_t st);
+
 // Rows of unit directions a row-split scan workgroup keeps in LDS (bf16 path; 0 on the fp32 path).
 int scan_lds_rows(int C, bool is_bf16);
 hipError_t launch_init(const Dims& m, const Dev& d, double rope_theta, hipStream_t st);

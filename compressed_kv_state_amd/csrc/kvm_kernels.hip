@@ -21,7 +21,18 @@
 #include <type_traits>
 #include <math.h>
 
+#include "kvm.h"
 #include "kvm_internal.h"
+
+#include <algorithm>
+#include <mutex>
+
+// Device scratch for kvm_prefill_noalloc, the entry point for callers that
+// cannot allocate device memory: the whole workspace of one call lives here
+// (each GPU holds its own copy until the process ends).  Host code reaches it
+// only through the address hipGetSymbolAddress gives (kvm::scratch_address).
+static __device__ __align__(256) uint8_t scratch[kvm::kScratchBytes];
+static_assert(kvm::kScratchBytes == KVM_NOALLOC_SCRATCH_BYTES, "scratch size as declared in kvm.h");
 
 namespace kvm {
 namespace {
@@ -2689,6 +2700,47 @@ __global__ __launch_bounds__(256) void state_load_kernel(Dims m, Dev d, int rows
   if (threadIdx.x == 0) d.nver[s] = rows;
 }
 
+// Schedule table of a workspace in the static scratch (one thread: at most a few
+// thousand chunks), with the host's rules: sinks first, then
+// m_j = min(max(capacity((j + 1) C) - rows, 0), candidates), capacity =
+// max_slots (fixed), ceil(alpha sqrt(T)) (sqrt, as the integer ceil-sqrt of
+// alpha^2 T) or the smaller of the two (saturating).  Every other thread
+// zeroes the version counters and the scan's exchange buffers.
+__global__ void noalloc_init_kernel(SchedParams sp, int4* sched, int* nver, int bh, uint2* xbuf, int64_t xwords,
+                                    int* xerr) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t k = i; k < xwords; k += n) xbuf[k] = make_uint2(0u, 0u);
+  for (int64_t k = i; k < bh; k += n) nver[k] = 0;
+  if (i != 0) return;
+  *xerr = 0;
+  int64_t rows = 0, nsink = 0, idx_off = 0;
+  for (int j = 0; j < sp.J; ++j) {
+    int64_t cand = sp.C;
+    const int64_t sk = min((int64_t)sp.ns - nsink, cand);
+    const int64_t before = rows;
+    nsink += sk;
+    rows += sk;
+    cand -= sk;
+    const uint64_t T = (uint64_t)(j + 1) * (uint64_t)sp.C;
+    int64_t cap = sp.max_slots;
+    if (sp.sched != 0) {
+      const uint64_t x = (uint64_t)sp.alpha * (uint64_t)sp.alpha * T;
+      uint64_t r = (uint64_t)sqrt((double)x);
+      while (r > 0 && r * r > x) --r;
+      while ((r + 1) * (r + 1) <= x) ++r;
+      const int64_t cs = (int64_t)(r * r == x ? r : r + 1);
+      cap = sp.sched == 1 ? cs : min(cs, (int64_t)sp.max_slots);
+    }
+    int64_t m = cap - rows;
+    if (m < 0) m = 0;
+    if (m > cand) m = cand;
+    rows += m;
+    sched[j] = make_int4((int)sk, (int)m, (int)before, (int)idx_off);
+    idx_off += rows;
+  }
+}
+
 template <typename T>
 hipError_t scan_dispatch(const Dims& m, const Dev& d, const Src& src, int jb, int je, hipStream_t st) {
   const bool part = m.P > 1;
@@ -2751,6 +2803,38 @@ hipError_t launch_init(const Dims& m, const Dev& d, double theta, hipStream_t st
   const int64_t n = m.max_tokens * 16;
   rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(d.rope_cos, d.rope_sin, m.max_tokens, theta);
   return hipGetLastError();
+}
+
+hipError_t launch_noalloc_init(const Dims& m, const Dev& d, const SchedParams& sp, double theta, hipStream_t st) {
+  hipError_t e = launch_init(m, d, theta, st);
+  if (e != hipSuccess) return e;
+  const int64_t xwords = (int64_t)m.BH * 2 * m.P * m.C;
+  const int64_t work = xwords > m.BH ? xwords : m.BH;
+  const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 1024);
+  noalloc_init_kernel<<<blocks, 256, 0, st>>>(sp, d.sched, d.nver, m.BH, d.xbuf, xwords, d.xerr);
+  return hipGetLastError();
+}
+
+hipError_t scratch_address(void** out) {
+  // One lookup per device, with that device current: each GPU holds its own
+  // copy of the array at its own address.  The name of the array is a host-side
+  // stand-in and is never passed to a kernel or a copy.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 int scan_lds_rows(int C, bool is_bf16) {

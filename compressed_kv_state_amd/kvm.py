@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KvmConfig", "KvmState", "KvmError", "library", "workspace_bytes", "schedule", "SCHED", "DTYPE",
+    "KvmConfig", "KvmState", "KvmError", "library", "workspace_bytes", "schedule", "prefill_noalloc", "SCHED", "DTYPE",
     "KVM_OK", "KVM_E_INVALID_ARG", "KVM_E_WORKSPACE", "KVM_E_CAPACITY", "KVM_E_STATE", "KVM_E_HIP",
 ]
 
@@ -89,6 +89,7 @@ def library() -> ctypes.CDLL:
         L.kvm_state_destroy.argtypes = [vp]
         L.kvm_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp]
         L.kvm_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        L.kvm_prefill_noalloc.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, vp, vp, i64, vp]
         L.kvm_state_read.argtypes = [vp, i64, ctypes.POINTER(_View), vp]
         L.kvm_state_load.argtypes = [vp, ctypes.POINTER(_View), vp]
         L.kvm_snapshot_read.argtypes = [vp, i64, vp, vp, vp, vp]
@@ -102,6 +103,7 @@ def library() -> ctypes.CDLL:
         L.kvm_last_error.argtypes = []
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
+                     "kvm_prefill_noalloc",
                      "kvm_decode_step", "kvm_state_read", "kvm_state_load", "kvm_snapshot_read", "kvm_state_get_info",
                      "kvm_state_reset", "kvm_state_check", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
@@ -201,6 +203,26 @@ def schedule(cfg: KvmConfig, n_chunks: int):
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def prefill_noalloc(cfg: KvmConfig, q, k, v, gate_logits, out) -> torch.Tensor:
+    """kvm_prefill_noalloc: one prefill from an empty state with the workspace in the library's
+    static device scratch (no allocation by the library).  q, k, v, out [B*H, n, 64] in cfg.dtype,
+    gate_logits [B*H, n] float32, all contiguous on one GPU; `out` is written in place."""
+    n = q.shape[-2]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.device != dev or not t.is_contiguous() or t.dtype != cfg.torch_dtype or t.shape[-1] != cfg.head_dim:
+            raise ValueError(f"{name}: contiguous {cfg.torch_dtype} [B*H, n, {cfg.head_dim}] on {dev} expected")
+        if t.numel() != cfg.seqs * n * cfg.head_dim:
+            raise ValueError(f"{name}: expected {cfg.seqs} x {n} x {cfg.head_dim} elements")
+    if (gate_logits.device != dev or not gate_logits.is_contiguous() or gate_logits.dtype != torch.float32
+            or gate_logits.numel() != cfg.seqs * n):
+        raise ValueError("gate_logits: contiguous float32 [B*H, n] expected")
+    c = cfg.to_c()
+    _check(library().kvm_prefill_noalloc(ctypes.byref(c), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         gate_logits.data_ptr(), out.data_ptr(), n, _stream(dev)))
+    return out
 
 
 class KvmState:

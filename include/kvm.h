@@ -189,6 +189,28 @@ kvm_status kvm_state_destroy(kvm_state* st);
 kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* v,
                        const float* gate_logits, void* out, int64_t n_tokens, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one
+ * prefill of n_tokens tokens from an empty state at position 0, the same
+ * computation and results as kvm_state_create + kvm_prefill on a state with
+ * this configuration (bit for bit), with the workspace in the library's static
+ * device scratch instead of a caller buffer.  Nothing is allocated: no
+ * hipMalloc/hipFree, no library stream or event, no host memory on success;
+ * the scratch (KVM_NOALLOC_SCRATCH_BYTES, 128 MiB) is held by each GPU the
+ * library runs on until the process ends.  Everything runs on `stream`.
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller.  The call clears what must start at
+ * zero itself.  q, k, v, out [B*H, n_tokens, 64] in cfg.dtype, gate_logits
+ * [B*H, n_tokens] f32, as for kvm_prefill; n_tokens <= cfg.max_tokens.
+ * Errors: KVM_E_INVALID_ARG (config; KVM_FLAG_TRACE, which needs a state;
+ * KVM_SCHED_POWER; tensors), KVM_E_WORKSPACE (the configuration's workspace,
+ * kvm_workspace_bytes, exceeds the scratch), KVM_E_HIP.  Nothing is queued on
+ * any error but KVM_E_HIP. */
+#define KVM_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+kvm_status kvm_prefill_noalloc(const kvm_config* cfg, const void* q, const void* k, const void* v,
+                               const float* gate_logits, void* out, int64_t n_tokens, void* stream);
+
 /* One decode step at position t = current position ([KVM summary, Problem
  * statement and Significance]: per-token decoding over a state smaller than
  * the context).  If t is a multiple of chunk and t >= W + C, chunk
