@@ -2455,25 +2455,75 @@ __global__ __launch_bounds__(256) void ring_fill_kernel(Dims m, Dev d, Src src, 
 
 // =====================================================================
 // Decode ([KVM abstract]: per-token cost independent of the context length;
-// [KVM summary, Core mechanisms 4]): one workgroup per sequence, eight waves.
-// The new token's rotated key, value and gate logit go to ring slot t % R;
-// query t attends over the state rows (unrotated q against the read-form
-// keys, values rho * u) and the window [lo, t] (rotated q against rotated
-// keys) with one softmax.  Eight lanes share a key, lane e owning value dims
-// [8e, 8e + 8) and a slice of the key dims; every sequence has the same row
-// count, so the workgroups are balanced.  Waves split the state rows and the
-// window keys evenly, then combine in LDS.
+// [KVM summary, Core mechanisms 4]): one workgroup of eight waves per
+// sequence.  The new token's rotated key, value and gate logit go to ring slot
+// t % R; query t attends over the state rows (unrotated q against the
+// read-form keys, values rho * u) and the window [lo, t] (rotated q against
+// rotated keys) with one softmax.
+// The step is bound by reading the state rows and the window once, so the
+// kernel is laid out for bytes in flight: the keys and values are read in two
+// separate passes over blocks of up to kDecBlock logits.  Pass 1 computes the
+// block's logits into LDS (a few lanes per key, 16 bytes each, several keys
+// per lane in flight, no dependence between keys); the block's maximum then
+// gives exact weights; pass 2 streams the values and accumulates
+// p * v (again several rows per lane in flight, no running-maximum chain).
+// A state larger than one block rescales the accumulators between blocks.
+// State rows are read with non-temporal loads: each is used once per step.
 // =====================================================================
-constexpr int kDecWaves = 8;
+constexpr int kDecWaves = 4;
+constexpr int kDecBlock = 2048;   // logits per block (8 KB of LDS)
+constexpr int kDecUnroll = 2;     // keys or value rows per lane in each batch (two batches in flight)
+
+__device__ __forceinline__ u32x4 ld_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// 16 bytes as floats: 8 bf16, 8 fp16 or 4 f32 (the first 16 / sizeof(E) entries of f)
+template <typename E>
+__device__ __forceinline__ void unpack16(const u32x4& x, float* f) {
+  if constexpr (sizeof(E) == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(x[i]);
+  } else if constexpr (std::is_same<E, bf16>::value) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(x[i] << 16);
+      f[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = (float)__builtin_bit_cast(f16, (uint16_t)(x[i] & 0xFFFFu));
+      f[2 * i + 1] = (float)__builtin_bit_cast(f16, (uint16_t)(x[i] >> 16));
+    }
+  }
+}
+
+// sum over aligned groups of G lanes (G a power of two <= 16)
+template <int G>
+__device__ __forceinline__ float dec_group_sum(float x) {
+  if constexpr (G >= 2) x += xor_lane<1>(x);
+  if constexpr (G >= 4) x += xor_lane<2>(x);
+  if constexpr (G >= 8) x += xor_lane<4>(x);
+  if constexpr (G >= 16) x += xor_lane<8>(x);
+  return x;
+}
 
 template <typename T>
 __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, const T* q, const T* kin, const T* vin,
                                                             const float* lin, T* out, int64_t t, int S,
                                                             int64_t lo) {
   using RT = typename Rd<T>::type;
-  constexpr int L = 8;
+  constexpr int NT = 64 * kDecWaves;
+  constexpr int KE = 16 / (int)sizeof(RT);   // state-key dims per lane (of 32)
+  constexpr int KL = 32 / KE;                // lanes per state key
+  constexpr int VE = 16 / (int)sizeof(T);    // value (and window-key) dims per lane (of 64)
+  constexpr int VL = 64 / VE;                // lanes per value row / window key
+  constexpr int U = kDecUnroll;
   __shared__ float sq[64], sqr[64], skt[64], svt[64];
-  __shared__ float red_m[kDecWaves], red_l[kDecWaves];
+  __shared__ float sL[kDecBlock];
+  __shared__ float red[kDecWaves];
   __shared__ float red_o[kDecWaves][64];
   const int s = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -2502,132 +2552,190 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
   }
   __syncthreads();
 
-  const int e = lane & (L - 1), grp = lane >> 3;
-  float mrun = -kInf, lrun = 0.f;
-  float o[8];
+  const char* kr = reinterpret_cast<const char*>(d.kread) + (size_t)s * m.S_cap * 32 * sizeof(RT);
+  const char* vr = reinterpret_cast<const char*>(d.vread) + (size_t)s * m.S_cap * 64 * sizeof(T);
+  const char* rk = reinterpret_cast<const char*>(d.ring_k) + (size_t)s * m.R * 64 * sizeof(T);
+  const char* rv = reinterpret_cast<const char*>(d.ring_v) + (size_t)s * m.R * 64 * sizeof(T);
+  const int nw = (int)(t - lo + 1);          // window keys, position t last
+  const int total = S + nw;
+  const int ksub = lane % KL, kgrp = lane / KL;   // pass 1, state keys
+  const int vsub = lane % VL, vgrp = lane / VL;   // pass 1 window keys and pass 2
+  float qs[KE], qw[VE];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  auto update = [&](float lg, const float (&vv)[8]) {
-    const float mnew = fmaxf(mrun, lg);
-    const float alpha = exp2_fast(mrun - mnew);
-    const float p = exp2_fast(lg - mnew);
-    lrun = lrun * alpha + p;
-    mrun = mnew;
+  for (int i = 0; i < KE; ++i) qs[i] = sq[32 + KE * ksub + i];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = fmaf(p, vv[i], o[i] * alpha);
-  };
+  for (int i = 0; i < VE; ++i) qw[i] = sqr[VE * vsub + i];
 
-  // ---- state rows: read-form key dims [32 + 4e, 32 + 4e + 4) and value rho * u
-  {
-    float qk[4];
+  float M = -kInf, lsum = 0.f;
+  float o[VE];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qk[i] = sq[32 + 4 * e + i];
-    const RT* kr = reinterpret_cast<const RT*>(d.kread) + (size_t)s * m.S_cap * 32;
-    const T* vr = reinterpret_cast<const T*>(d.vread) + (size_t)s * m.S_cap * 64;
-    const int per = (S + kDecWaves - 1) / kDecWaves;
-    const int rb = w * per, re = min(S, rb + per);
-    for (int row = rb + grp; row < re; row += 64 / L) {
-      alignas(16) RT kk[4];
-      alignas(16) T vh[8];
-      if constexpr (sizeof(RT) == 2) {
-        *reinterpret_cast<uint2*>(kk) = *reinterpret_cast<const uint2*>(kr + (size_t)row * 32 + 4 * e);
-      } else {
-        copy16(kk, kr + (size_t)row * 32 + 4 * e);
-      }
+  for (int i = 0; i < VE; ++i) o[i] = 0.f;
+
+  for (int b0 = 0; b0 < total; b0 += kDecBlock) {
+    const int b1 = min(total, b0 + kDecBlock);
+    // ---- pass 1: logits of [b0, b1) into sL
+    {
+      // software-pipelined: the next batch of keys is requested before this one is used
+      const int e1 = min(b1, S);
+      constexpr int PER = 64 / KL * kDecWaves;   // state keys per round of the workgroup
+      auto load = [&](u32x4 (&x)[U], int r0) {
 #pragma unroll
-      for (int i = 0; i < 8; i += 16 / (int)sizeof(T)) copy16(&vh[i], vr + (size_t)row * 64 + 8 * e + i);
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dot = fmaf(qk[i], tof(kk[i]), dot);
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      dot += __shfl_xor(dot, 4);
-      float vv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) vv[i] = tof(vh[i]);
-      update(dot, vv);
-    }
-  }
-  // ---- window keys [lo, t] (ring slots; position t from LDS)
-  {
-    float qk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qk[i] = sqr[8 * e + i];
-    const T* rk = reinterpret_cast<const T*>(d.ring_k) + (size_t)s * m.R * 64;
-    const T* rv = reinterpret_cast<const T*>(d.ring_v) + (size_t)s * m.R * 64;
-    const int nwk = (int)(t - lo + 1);
-    const int per = (nwk + kDecWaves - 1) / kDecWaves;
-    const int kb = w * per, ke = min(nwk, kb + per);
-    // ring slot of position lo + i0, stepped along with i0 (no 64-bit modulo per key)
-    int slot = (int)((lo + kb + grp) % m.R);
-    for (int i0 = kb + grp; i0 < ke; i0 += 64 / L) {
-      const int64_t pos = lo + i0;
-      float kf[8], vv[8];
-      if (pos == t) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { kf[i] = skt[8 * e + i]; vv[i] = svt[8 * e + i]; }
-      } else {
-        // both rows' loads are issued before either is used (one memory
-        // round trip per key batch, not two)
-        constexpr int NQ = 8 * (int)sizeof(T) / 16;
-        uint4 kq[NQ], vq[NQ];
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-          kq[i] = *reinterpret_cast<const uint4*>(rk + (size_t)slot * 64 + 8 * e + i * (16 / (int)sizeof(T)));
-          vq[i] = *reinterpret_cast<const uint4*>(rv + (size_t)slot * 64 + 8 * e + i * (16 / (int)sizeof(T)));
+        for (int u = 0; u < U; ++u) {
+          const int r = max(min(r0 + u * PER, e1 - 1), 0);
+          x[u] = ld_nt(kr + (size_t)r * 32 * sizeof(RT) + 16 * ksub);
         }
-        const T* kh = reinterpret_cast<const T*>(kq);
-        const T* vh = reinterpret_cast<const T*>(vq);
+      };
+      int r0 = b0 + w * (64 / KL) + kgrp;
+      u32x4 x[U];
+      if (r0 < e1) load(x, r0);
+      for (; r0 < e1; r0 += PER * U) {
+        u32x4 xn[U];
+        if (r0 + PER * U < e1) load(xn, r0 + PER * U);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { kf[i] = tof(kh[i]); vv[i] = tof(vh[i]); }
-        // scheduling order for this block: address arithmetic, the loads, the rest
-        __builtin_amdgcn_sched_group_barrier(0x0002, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(0x0020, 2 * NQ, 0);
-        __builtin_amdgcn_sched_group_barrier(0x0002, 64, 0);
+        for (int u = 0; u < U; ++u) {
+          float f[8];
+          unpack16<RT>(x[u], f);
+          float dot = 0.f;
+#pragma unroll
+          for (int i = 0; i < KE; ++i) dot = fmaf(qs[i], f[i], dot);
+          dot = dec_group_sum<KL>(dot);
+          const int r = r0 + u * PER;
+          if (ksub == 0 && r < e1) sL[r - b0] = dot;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = xn[u];
       }
-      slot += 64 / L;
-      if (slot >= m.R) slot -= m.R;
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dot = fmaf(qk[i], kf[i], dot);
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      dot += __shfl_xor(dot, 4);
-      update(dot, vv);
     }
-  }
-  // ---- combine the eight key groups of the wave, then the waves
+    {
+      const int e0 = max(b0, S);
+      constexpr int PER = 64 / VL * kDecWaves;   // window keys per round
+      for (int i0 = e0 - S + w * (64 / VL) + vgrp; i0 + S < b1; i0 += PER * U) {
+        u32x4 x[U];
 #pragma unroll
-  for (int msk = L; msk < 64; msk <<= 1) {
-    const float mo = __shfl_xor(mrun, msk);
-    const float lo_ = __shfl_xor(lrun, msk);
-    const float mn = fmaxf(mrun, mo);
-    const float a1 = mrun == -kInf ? 0.f : exp2_fast(mrun - mn);
-    const float a2 = mo == -kInf ? 0.f : exp2_fast(mo - mn);
-    lrun = lrun * a1 + lo_ * a2;
+        for (int u = 0; u < U; ++u) {
+          const int i = min(i0 + u * PER, b1 - S - 1);
+          const int64_t pos = lo + i;
+          x[u] = pos == t ? u32x4{0u, 0u, 0u, 0u}
+                          : ld16(rk + ((size_t)(pos % m.R) * 64 + VE * vsub) * sizeof(T));
+        }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float oo = __shfl_xor(o[i], msk);
-      o[i] = o[i] * a1 + oo * a2;
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * PER;
+          float f[8];
+          unpack16<T>(x[u], f);
+          if (lo + i == t) {
+#pragma unroll
+            for (int k = 0; k < VE; ++k) f[k] = skt[VE * vsub + k];
+          }
+          float dot = 0.f;
+#pragma unroll
+          for (int k = 0; k < VE; ++k) dot = fmaf(qw[k], f[k], dot);
+          dot = dec_group_sum<VL>(dot);
+          if (vsub == 0 && i + S < b1) sL[i + S - b0] = dot;
+        }
+      }
     }
-    mrun = mn;
-  }
-  if (lane < L) {
+    // the first batch of pass 2's values is requested now, so that it is in
+    // flight while the block's maximum and weights are formed
+    const int ve1 = min(b1, S);
+    constexpr int VPER = 64 / VL * kDecWaves;   // value rows per round of the workgroup
+    auto vload = [&](u32x4 (&x)[U], int r0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) red_o[w][8 * e + i] = o[i];
-    if (lane == 0) { red_m[w] = mrun; red_l[w] = lrun; }
+      for (int u = 0; u < U; ++u) {
+        const int r = max(min(r0 + u * VPER, ve1 - 1), 0);
+        x[u] = ld_nt(vr + ((size_t)r * 64 + VE * vsub) * sizeof(T));
+      }
+    };
+    int vr0 = b0 + w * (64 / VL) + vgrp;
+    u32x4 vx[U];
+    if (vr0 < ve1) vload(vx, vr0);
+    __syncthreads();
+    // ---- the block's maximum, then exact weights in place
+    float mx = -kInf;
+    for (int i = tid; i < b1 - b0; i += NT) mx = fmaxf(mx, sL[i]);
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+    if (lane == 0) red[w] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int ww = 1; ww < kDecWaves; ++ww) mx = fmaxf(mx, red[ww]);
+    const float Mn = fmaxf(M, mx);
+    const float sc = M == -kInf ? 0.f : exp2_fast(M - Mn);
+    M = Mn;
+    lsum *= sc;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) o[i] *= sc;
+    for (int i = tid; i < b1 - b0; i += NT) {
+      const float p = exp2_fast(sL[i] - M);
+      sL[i] = p;
+      lsum += p;
+    }
+    __syncthreads();
+    // ---- pass 2: values of [b0, b1)
+    for (; vr0 < ve1; vr0 += VPER * U) {
+      u32x4 xn[U];
+      if (vr0 + VPER * U < ve1) vload(xn, vr0 + VPER * U);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = vr0 + u * VPER;
+        const float p = r < ve1 ? sL[r - b0] : 0.f;
+        float f[8];
+        unpack16<T>(vx[u], f);
+#pragma unroll
+        for (int k = 0; k < VE; ++k) o[k] = fmaf(p, f[k], o[k]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) vx[u] = xn[u];
+    }
+    {
+      const int e0 = max(b0, S);
+      constexpr int PER = 64 / VL * kDecWaves;
+      for (int i0 = e0 - S + w * (64 / VL) + vgrp; i0 + S < b1; i0 += PER * U) {
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = min(i0 + u * PER, b1 - S - 1);
+          const int64_t pos = lo + i;
+          x[u] = pos == t ? u32x4{0u, 0u, 0u, 0u}
+                          : ld16(rv + ((size_t)(pos % m.R) * 64 + VE * vsub) * sizeof(T));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * PER;
+          const float p = i + S < b1 ? sL[i + S - b0] : 0.f;
+          float f[8];
+          unpack16<T>(x[u], f);
+          if (lo + i == t) {
+#pragma unroll
+            for (int k = 0; k < VE; ++k) f[k] = svt[VE * vsub + k];
+          }
+#pragma unroll
+          for (int k = 0; k < VE; ++k) o[k] = fmaf(p, f[k], o[k]);
+        }
+      }
+    }
+    __syncthreads();   // sL is rewritten by the next block
   }
+  // ---- combine: lane groups of the wave (same dims), then the waves; the row sum over all threads
+#pragma unroll
+  for (int msk = VL; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int k = 0; k < VE; ++k) o[k] += __shfl_xor(o[k], msk);
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) lsum += __shfl_xor(lsum, msk);
+  if (lane < VL) {
+#pragma unroll
+    for (int k = 0; k < VE; ++k) red_o[w][VE * lane + k] = o[k];
+  }
+  if (lane == 0) red[w] = lsum;
   __syncthreads();
   if (tid < 64) {
-    float M = -kInf;
-#pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, red_m[ww]);
     float Ls = 0.f, Ov = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
-      const float a = red_m[ww] == -kInf ? 0.f : exp2_fast(red_m[ww] - M);
-      Ls += red_l[ww] * a;
-      Ov += red_o[ww][tid] * a;
+      Ls += red[ww];
+      Ov += red_o[ww][tid];
     }
     out[(size_t)s * 64 + tid] = fromf<T>(Ls > 0.f ? Ov / Ls : 0.f);
   }
