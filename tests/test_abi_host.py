@@ -148,3 +148,29 @@ def test_profile_mask_bits_are_checked():
     bits = [int(v) for v in re.findall(r"#define KVM_PROFILE_(?!ALL)\w+ (\d+)", hdr)]
     assert sorted(bits) == [1, 2, 4, 8, 16, 32]
     assert int(re.search(r"#define KVM_PROFILE_ALL (\d+)", hdr).group(1)) == sum(bits)
+
+
+def test_host_library_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """kvm_api.cpp built for the host only with g++ -fsanitize=address,undefined (the kernel
+    launchers replaced by do-nothing stand-ins, tests/sanitize/stub_launch.cpp), driven through
+    every host-side path that needs no GPU (tests/sanitize/driver.cpp), with leak detection."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    exe = tmp_path / "kvm_sanitized"
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+           "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "compressed_kv_state_amd", "csrc"),
+           os.path.join(ROOT, "compressed_kv_state_amd", "csrc", "kvm_api.cpp"),
+           os.path.join(ROOT, "tests", "sanitize", "stub_launch.cpp"),
+           os.path.join(ROOT, "tests", "sanitize", "driver.cpp"),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "sanitized host checks: ok" in r.stdout
+    assert "runtime error" not in r.stderr and "ERROR: AddressSanitizer" not in r.stderr
