@@ -163,7 +163,7 @@ struct Plan {
   kvm::Dims m{};
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
-  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, pcount, idx, krot, tslot, tkind, ring_k,
+  size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, pcount, pnorm, idx, krot, tslot, tkind, ring_k,
       ring_v, ring_l, rope_cos, rope_sin, sch, nver, xbuf, xerr, total;
 };
 
@@ -242,6 +242,7 @@ kvm_status plan(const kvm_config* c, Plan& p, bool keep_sched = true) {
   p.pval = take(BH * (size_t)m.V_cap * 64 * es);
   p.prho = take(BH * (size_t)m.V_cap * 4);
   p.pcount = take(BH * (size_t)m.V_cap * 4);
+  p.pnorm = take(BH * (size_t)m.V_cap * 8);
   p.idx = take(BH * (size_t)idx_total * 4);
   p.tslot = take(m.trace ? BH * (size_t)c->max_tokens * 4 : 0);
   p.tkind = take(m.trace ? BH * (size_t)c->max_tokens : 0);
@@ -272,6 +273,7 @@ void carve(const Plan& p, char* b, kvm::Dev& d) {
   d.pval = b + p.pval;
   d.prho = reinterpret_cast<float*>(b + p.prho);
   d.pcount = reinterpret_cast<int*>(b + p.pcount);
+  d.pnorm = reinterpret_cast<float2*>(b + p.pnorm);
   d.idx = reinterpret_cast<int*>(b + p.idx);
   d.tslot = reinterpret_cast<int*>(b + p.tslot);
   d.tkind = reinterpret_cast<uint8_t*>(b + p.tkind);
@@ -619,6 +621,79 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
   if (err != hipSuccess) return hip_fail(st, err, "decode launch");
   st->pos = t + 1;
   st->absorbed = absorbed;
+  return KVM_OK;
+}
+
+namespace {
+struct BwdPlan {
+  size_t part_win, part_state, tot_rho, lse_d, total;
+};
+BwdPlan bwd_plan(const kvm::Dims& m, int64_t n_tokens) {
+  BwdPlan b{};
+  const size_t BH = (size_t)m.BH;
+  const size_t nq = (size_t)((n_tokens + m.C - 1) / m.C);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  b.part_win = take(BH * nq * (size_t)m.R * 128 * 4);
+  b.part_state = take(BH * (size_t)m.idx_total * 96 * 4);
+  b.tot_rho = take(BH * (size_t)m.idx_total * 4);
+  b.lse_d = take(BH * (size_t)n_tokens * 8);
+  b.total = off;
+  return b;
+}
+}  // namespace
+
+kvm_status kvm_backward_workspace_bytes(const kvm_config* cfg, size_t* bytes) {
+  try {
+    if (!bytes) return fail(KVM_E_INVALID_ARG, "bytes is NULL");
+    Plan p;
+    kvm_status s = plan(cfg, p, false);
+    if (s != KVM_OK) return s;
+    *bytes = bwd_plan(p.m, cfg->max_tokens).total;
+    return KVM_OK;
+  } catch (...) {
+    return fail(KVM_E_INVALID_ARG, "host allocation failed");
+  }
+}
+
+kvm_status kvm_prefill_backward(kvm_state* st, const void* q, const void* k, const void* v, const float* gate_logits,
+                                const void* d_out, float* d_q, float* d_k, float* d_v, float* d_gate,
+                                int64_t n_tokens, void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  const kvm::Dims& m = st->m;
+  if (!m.trace) return fail(KVM_E_INVALID_ARG, "the backward reads the forward's decisions: create the state with KVM_FLAG_TRACE");
+  if (n_tokens <= 0) return fail(KVM_E_INVALID_ARG, "n_tokens must be > 0");
+  if (n_tokens != st->pos) return fail(KVM_E_STATE, "the state's position must equal n_tokens");
+  if (!q || !k || !v || !gate_logits || !d_out || !d_q || !d_k || !d_v || !d_gate || !d_workspace)
+    return fail(KVM_E_INVALID_ARG, "NULL pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_out, 16) || !aligned(d_q, 16) ||
+      !aligned(d_k, 16) || !aligned(d_v, 16) || !aligned(gate_logits, 4) || !aligned(d_gate, 4))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
+  if (!aligned(d_workspace, 256)) return fail(KVM_E_WORKSPACE, "workspace must be 256-byte aligned");
+  const BwdPlan bp = bwd_plan(m, n_tokens);
+  if (workspace_bytes < bp.total)
+    return fail(KVM_E_WORKSPACE, "backward workspace too small: need " + std::to_string(bp.total) + " bytes");
+  char* w = reinterpret_cast<char*>(d_workspace);
+  kvm::Bwd b{};
+  b.part_win = reinterpret_cast<float*>(w + bp.part_win);
+  b.part_state = reinterpret_cast<float*>(w + bp.part_state);
+  b.tot_rho = reinterpret_cast<float*>(w + bp.tot_rho);
+  b.lse_d = reinterpret_cast<float2*>(w + bp.lse_d);
+  b.dq = d_q;
+  b.dk = d_k;
+  b.dv = d_v;
+  b.dl = d_gate;
+  b.nq = (int)((n_tokens + m.C - 1) / m.C);
+  b.absorbed = (int)st->absorbed;
+  const kvm::BwdIn in{q, k, v, gate_logits, d_out, n_tokens};
+  const int rows_last = rows_after(st, st->absorbed - 1);
+  hipError_t e = kvm::launch_backward(m, st->d, in, b, rows_last, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(st, e, "backward launch");
   return KVM_OK;
 }
 

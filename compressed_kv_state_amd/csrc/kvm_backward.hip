@@ -1,0 +1,599 @@
+// gfx950 kernels of the Key-Value Means layer's backward pass.
+//
+// [KVM abstract]: the layer supports chunk-wise parallelizable training.  The
+// gradient of a loss with respect to q, k, v and the gate logits is taken
+// through the forward that kvm_prefill computed, with its discrete choices
+// (the winner-take-all row of every merged token, the appended tokens, read
+// back from the trace) held fixed:
+//   bwd_q_kernel      per (sequence, query chunk): the joint softmax over
+//                     [snapshot read form || window] recomputed (row maximum,
+//                     then the row sum and D = sum_j P_j dP_j), then dq;
+//   bwd_kv_kernel     per (sequence, query chunk): each wave owns key tiles and
+//                     accumulates their dk and dv over the chunk's queries;
+//                     the result is one partial per (chunk, key);
+//   bwd_win_kernel    per token: the window keys' partials of the chunks that
+//                     saw the key, RoPE transposed ([KVM summary, Core
+//                     mechanisms 4]);
+//   bwd_state_kernel  per state row: back through the read form of every
+//                     snapshot (LayerNorm of K/n, the value at its radius;
+//                     [KVM summary, Core mechanisms 2]) and the running sums of
+//                     the chunk recurrence, last chunk first ([KVM lay summary,
+//                     "smart merge"]: the sums only grow);
+//   bwd_token_kernel  per absorbed token: merged tokens took g * (k, v) into
+//                     their row, creators set it (and its radius |v|); the gate
+//                     g = sigmoid(l) ([KVM summary, Core mechanisms 2]).
+// Everything in fp32; contractions on v_mfma_f32_32x32x2f32.  Every gradient
+// element is written by one thread in a fixed order: no float atomics, so the
+// backward is bitwise repeatable.
+//
+// v_mfma_f32_32x32x2f32: lane l gives A[l%32][k_l] and B[k_l][l%32] with
+// k_l = l/32 (or any bijection of the contraction index, used consistently by
+// A and B); D lane l register r is D[row(r, l/32)][l%32], row(r, h) =
+// 8(r/4) + 4h + r%4.  A score tile computed with keys as rows thus holds, in
+// register r of lane l, exactly the A operand that a product contracting over
+// those keys needs at step r (contraction index row(r, l/32)): dS and P feed
+// the next products from registers, with no transpose through LDS.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <type_traits>
+
+#include "kvm_device.h"
+#include "kvm_internal.h"
+
+namespace kvm {
+namespace {
+
+__device__ __forceinline__ int mrow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+constexpr int kPitch = 65;   // fp32 tile rows in LDS: 64 dims + 1 (rows land on distinct banks)
+
+// Tile T of query chunk c's keys: state tiles (32 snapshot rows each) first,
+// then window tiles (32 positions of [lo, hi) each).  Stages the keys (state:
+// read-form key in columns 32..63, columns 0..31 zero; window: the input key
+// rotated by RoPE at its position, fp32) and the values (state: read-form
+// value; window: the input value) into LDS as fp32, zero past the end.
+template <typename T>
+__device__ void bwd_stage(float* Kt, float* Vt, int Tile, int n_st, int S, const int* idxl, const Dims& m,
+                          const Dev& d, const BwdIn& in, int s, int64_t lo, int64_t hi, int tid, int nt) {
+  using RT = typename Rd<T>::type;
+  const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const T* kin = reinterpret_cast<const T*>(in.k) + (size_t)s * in.N * 64;
+  const T* vin = reinterpret_cast<const T*>(in.v) + (size_t)s * in.N * 64;
+  for (int e = tid; e < 32 * 64; e += nt) {
+    const int key = e >> 6, dd = e & 63;
+    float kv = 0.f, vv = 0.f;
+    if (Tile < n_st) {
+      const int r = Tile * 32 + key;
+      if (r < S) {
+        const int64_t ver = idxl[r];
+        if (dd >= 32) kv = tof(pk[ver * 32 + dd - 32]);
+        vv = tof(pv[ver * 64 + dd]);
+      }
+    } else {
+      const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
+      if (pos < hi) {
+        const T* kr = kin + pos * 64;
+        kv = tof(kr[dd]);
+        if (dd < 32) {
+          const int jf = dd & 15;
+          const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+          kv = dd < 16 ? kv * cs - tof(kr[dd + 16]) * sn : kv * cs + tof(kr[dd - 16]) * sn;
+        }
+        vv = tof(vin[pos * 64 + dd]);
+      }
+    }
+    Kt[key * kPitch + dd] = kv;
+    Vt[key * kPitch + dd] = vv;
+  }
+}
+
+// Tile validity of score element (key row kr of the tile, query at position qp).
+__device__ __forceinline__ bool bwd_valid(int Tile, int n_st, int S, int64_t lo, int64_t hi, int key, int64_t qp,
+                                          bool qvalid) {
+  if (!qvalid) return false;
+  if (Tile < n_st) return Tile * 32 + key < S;
+  const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
+  return pos < hi && pos <= qp;
+}
+
+// ---------------------------------------------------------------------------
+// dq.  One wave per 32 queries, lane l%32 = query; scores S^T = K . Q^T with the
+// keys as rows.  Three sweeps over the key tiles: the row maximum, then the row
+// sum and D = sum_j P_j dP_j (dP = dO . v_j), then dq += dS . K.
+// ---------------------------------------------------------------------------
+template <typename T, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_q_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  constexpr int C = NW * 32;
+  constexpr int NT = NW * 64;
+  __shared__ float Kt[32 * kPitch], Vt[32 * kPitch];
+  const int s = blockIdx.x % m.BH;
+  const int c = blockIdx.x / m.BH;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, ql = lane & 31;
+  const int64_t cpos = (int64_t)c * C;
+  const int64_t qp = cpos + 32 * w + ql;
+  const bool qvalid = qp < in.N;
+  const int64_t qq = qvalid ? qp : in.N - 1;
+  const float c2 = m.scale * kLog2e;
+  // snapshot read by this chunk and its tiles
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  const int* idxl = d.idx + (size_t)s * m.idx_total;
+  if (jj >= 0) {
+    const int4 sc = d.sched[jj];
+    S = sc.x + sc.y + sc.z;
+    idxl += sc.w;
+  }
+  const int n_st = (S + 31) >> 5;
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
+  const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
+  // query (rotated, scaled into log2 units) and dO, as B operands: step k takes dims 2k + h
+  float qf[32], df[32];
+  {
+    const T* qr = reinterpret_cast<const T*>(in.q) + ((size_t)s * in.N + qq) * 64;
+    const T* dor = reinterpret_cast<const T*>(in.dout) + ((size_t)s * in.N + qq) * 64;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int dd = 2 * k + h;
+      float x = tof(qr[dd]);
+      if (dd < 32) {
+        const int jf = dd & 15;
+        const float cs = d.rope_cos[qq * 16 + jf], sn = d.rope_sin[qq * 16 + jf];
+        x = dd < 16 ? x * cs - tof(qr[dd + 16]) * sn : x * cs + tof(qr[dd - 16]) * sn;
+      }
+      qf[k] = x * c2;
+      df[k] = qvalid ? tof(dor[dd]) : 0.f;
+    }
+  }
+  auto scores = [&](int Tile) {
+    f32x16 acc = {};
+    const bool st = Tile < n_st;   // state keys live on dims 32..63 only
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (k >= 16 || !st) acc = mfma_f32(Kt[ql * kPitch + 2 * k + h], qf[k], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!bwd_valid(Tile, n_st, S, lo, hi, mrow(r, h), qp, qvalid)) acc[r] = -kInf;
+    return acc;
+  };
+  auto dscores = [&]() {
+    f32x16 acc = {};
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc = mfma_f32(Vt[ql * kPitch + 2 * k + h], df[k], acc);
+    return acc;
+  };
+  // sweep 1: row maximum
+  float mx = -kInf;
+  for (int Tile = 0; Tile < n_tiles; ++Tile) {
+    __syncthreads();
+    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, s, lo, hi, tid, NT);
+    __syncthreads();
+    const f32x16 a = scores(Tile);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, a[r]);
+  }
+  mx = fmaxf(mx, partner_f(mx));
+  // sweep 2: row sum and D
+  float ls = 0.f, ds = 0.f;
+  for (int Tile = 0; Tile < n_tiles; ++Tile) {
+    __syncthreads();
+    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, s, lo, hi, tid, NT);
+    __syncthreads();
+    const f32x16 a = scores(Tile);
+    const f32x16 dp = dscores();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = a[r] == -kInf ? 0.f : exp2f(a[r] - mx);
+      ls += p;
+      ds = fmaf(p, dp[r], ds);
+    }
+  }
+  ls += partner_f(ls);
+  ds += partner_f(ds);
+  const float lse = mx + log2f(ls);
+  const float Dq = ds / ls;
+  if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
+  // sweep 3: dq += dS . K (contraction over the tile's keys in register order)
+  f32x16 dq0 = {}, dq1 = {};
+  for (int Tile = 0; Tile < n_tiles; ++Tile) {
+    __syncthreads();
+    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, s, lo, hi, tid, NT);
+    __syncthreads();
+    const f32x16 a = scores(Tile);
+    const f32x16 dp = dscores();
+    f32x16 dsc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = a[r] == -kInf ? 0.f : exp2f(a[r] - lse);
+      dsc[r] = p * (dp[r] - Dq);
+    }
+    if (Tile >= n_st) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dq0 = mfma_f32(dsc[k], Kt[mrow(k, h) * kPitch + ql], dq0);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dq1 = mfma_f32(dsc[k], Kt[mrow(k, h) * kPitch + 32 + ql], dq1);
+  }
+  // dq rows are queries (register r: query row(r, h)), lane column = dim; RoPE transposed
+  // on dims 0..31 (pair (j, j + 16): the partner is lane l ^ 16), natural-logit scale
+  float* dqo = b.dq + (size_t)s * in.N * 64;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t qpos = cpos + 32 * w + mrow(r, h);
+    const float y = dq0[r];
+    const float yp = __shfl_xor(y, 16);
+    if (qpos < in.N) {
+      const int jf = ql & 15;
+      const float cs = d.rope_cos[qpos * 16 + jf], sn = d.rope_sin[qpos * 16 + jf];
+      const float x = ql < 16 ? y * cs + yp * sn : y * cs - yp * sn;
+      dqo[qpos * 64 + ql] = m.scale * x;
+      dqo[qpos * 64 + 32 + ql] = m.scale * dq1[r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv partials of one query chunk.  The chunk's queries (rotated), dO, and
+// their (lse, D) sit in LDS, in blocks of up to 128 queries; each wave owns key
+// tiles (tile w, w + NW, ...) and contracts over the queries, so a key's
+// partial is complete in one wave's registers.  S = Q . K^T with the queries as
+// rows.
+// ---------------------------------------------------------------------------
+constexpr int kQB = 128;   // queries per LDS block
+
+template <typename T, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  using RT = typename Rd<T>::type;
+  constexpr int C = NW * 32;
+  constexpr int QB = C < kQB ? C : kQB;
+  __shared__ float Qs[QB * kPitch], Ds[QB * kPitch];
+  __shared__ float2 LD[QB];
+  const int s = blockIdx.x % m.BH;
+  const int c = blockIdx.x / m.BH;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, kl = lane & 31;
+  const int64_t cpos = (int64_t)c * C;
+  const float c2 = m.scale * kLog2e;
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  int64_t ioff = 0;
+  if (jj >= 0) {
+    const int4 sc = d.sched[jj];
+    S = sc.x + sc.y + sc.z;
+    ioff = sc.w;
+  }
+  const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
+  const int n_st = (S + 31) >> 5;
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
+  const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
+  const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const T* kin = reinterpret_cast<const T*>(in.k) + (size_t)s * in.N * 64;
+  const T* vin = reinterpret_cast<const T*>(in.v) + (size_t)s * in.N * 64;
+  const T* qin = reinterpret_cast<const T*>(in.q) + (size_t)s * in.N * 64;
+  const T* doin = reinterpret_cast<const T*>(in.dout) + (size_t)s * in.N * 64;
+  for (int q0 = 0; q0 < C; q0 += QB) {
+    // the block's queries, rotated (unscaled), their dO and (lse, D); zero past the end
+    __syncthreads();
+    for (int e = tid; e < QB * 64; e += NW * 64) {
+      const int qi = e >> 6, dd = e & 63;
+      const int64_t pos = cpos + q0 + qi;
+      float x = 0.f, g = 0.f;
+      if (pos < in.N) {
+        const T* qr = qin + pos * 64;
+        x = tof(qr[dd]);
+        if (dd < 32) {
+          const int jf = dd & 15;
+          const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+          x = dd < 16 ? x * cs - tof(qr[dd + 16]) * sn : x * cs + tof(qr[dd - 16]) * sn;
+        }
+        g = tof(doin[pos * 64 + dd]);
+      }
+      Qs[qi * kPitch + dd] = x;
+      Ds[qi * kPitch + dd] = g;
+    }
+    for (int qi = tid; qi < QB; qi += NW * 64) {
+      const int64_t pos = cpos + q0 + qi;
+      LD[qi] = pos < in.N ? b.lse_d[(size_t)s * in.N + pos] : make_float2(kInf, 0.f);
+    }
+    __syncthreads();
+    for (int Tile = w; Tile < n_tiles; Tile += NW) {
+      const bool st = Tile < n_st;
+      // this wave's keys as B operands (step k: dims 2k + h) and their positions
+      float kf[32], vf[32];
+      int64_t kpos = 0;
+      bool kvalid;
+      if (st) {
+        const int r = Tile * 32 + kl;
+        kvalid = r < S;
+        const int64_t ver = kvalid ? idxl[r] : 0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const int dd = 2 * k + h;
+          kf[k] = kvalid && dd >= 32 ? tof(pk[ver * 32 + dd - 32]) : 0.f;
+          vf[k] = kvalid ? tof(pv[ver * 64 + dd]) : 0.f;
+        }
+      } else {
+        kpos = lo + (int64_t)(Tile - n_st) * 32 + kl;
+        kvalid = kpos < hi;
+        const int64_t pp = kvalid ? kpos : lo;
+        const T* kr = kin + pp * 64;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const int dd = 2 * k + h;
+          float x = tof(kr[dd]);
+          if (dd < 32) {
+            const int jf = dd & 15;
+            const float cs = d.rope_cos[pp * 16 + jf], sn = d.rope_sin[pp * 16 + jf];
+            x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
+          }
+          kf[k] = kvalid ? x : 0.f;
+          vf[k] = kvalid ? tof(vin[pp * 64 + dd]) : 0.f;
+        }
+      }
+      f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
+      for (int qs = 0; qs < QB; qs += 32) {
+        f32x16 sc = {}, dp = {};
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          if (k >= 16 || !st) sc = mfma_f32(Qs[(qs + kl) * kPitch + 2 * k + h], kf[k], sc);
+#pragma unroll
+        for (int k = 0; k < 32; ++k) dp = mfma_f32(Ds[(qs + kl) * kPitch + 2 * k + h], vf[k], dp);
+        f32x16 p, dsc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qs + mrow(r, h);
+          const int64_t qpos = cpos + q0 + qi;
+          const float2 ld = LD[qi];
+          const bool ok = kvalid && qpos < in.N && (st || kpos <= qpos);
+          const float pr = ok ? exp2f(sc[r] * c2 - ld.x) : 0.f;
+          p[r] = pr;
+          dsc[r] = pr * (dp[r] - ld.y);
+        }
+        // dk[key][d] += dS^T . Q, dv[key][e] += P^T . dO: contraction over the sub-block's
+        // queries in register order (query row(k, h) at step k)
+        if (!st) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) dk0 = mfma_f32(dsc[k], Qs[(qs + mrow(k, h)) * kPitch + kl], dk0);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int qrow = (qs + mrow(k, h)) * kPitch;
+          dk1 = mfma_f32(dsc[k], Qs[qrow + 32 + kl], dk1);
+          dv0 = mfma_f32(p[k], Ds[qrow + kl], dv0);
+          dv1 = mfma_f32(p[k], Ds[qrow + 32 + kl], dv1);
+        }
+      }
+      // rows of the results are keys (register r: key row(r, h)), lane column = dim.  The
+      // first query block writes the partial, later blocks add to it (same wave, in order).
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = mrow(r, h);
+        float* dst;
+        if (st) {
+          const int row = Tile * 32 + key;
+          if (row >= S) continue;
+          dst = b.part_state + ((size_t)s * m.idx_total + ioff + row) * 96;
+          const float a0 = m.scale * dk1[r], a1 = dv0[r], a2 = dv1[r];
+          if (q0 == 0) {
+            dst[kl] = a0;
+            dst[32 + kl] = a1;
+            dst[64 + kl] = a2;
+          } else {
+            dst[kl] += a0;
+            dst[32 + kl] += a1;
+            dst[64 + kl] += a2;
+          }
+        } else {
+          const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
+          if (pos >= hi) continue;
+          const int64_t off = pos - (cpos - m.W);   // in [0, W + C)
+          dst = b.part_win + (((size_t)s * b.nq + c) * m.R + off) * 128;
+          const float a0 = m.scale * dk0[r], a1 = m.scale * dk1[r], a2 = dv0[r], a3 = dv1[r];
+          if (q0 == 0) {
+            dst[kl] = a0;
+            dst[32 + kl] = a1;
+            dst[64 + kl] = a2;
+            dst[96 + kl] = a3;
+          } else {
+            dst[kl] += a0;
+            dst[32 + kl] += a1;
+            dst[64 + kl] += a2;
+            dst[96 + kl] += a3;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Window keys: the partials of every chunk whose window holds position p (in
+// chunk order), RoPE transposed on dims 0..31.  Writes dk and dv of every
+// position (the state path adds to them later).  One wave per position, lane =
+// dim.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_win_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  const int s = blockIdx.y;
+  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int dd = threadIdx.x & 63;
+  if (pos >= in.N) return;
+  const int64_t c0 = pos / m.C;
+  int64_t c1 = (pos + m.W) / m.C;
+  if (c1 > b.nq - 1) c1 = b.nq - 1;
+  float gk = 0.f, gv = 0.f;
+  for (int64_t c = c0; c <= c1; ++c) {
+    const int64_t off = pos - (c * m.C - m.W);
+    const float* src = b.part_win + (((size_t)s * b.nq + c) * m.R + off) * 128;
+    gk += src[dd];
+    gv += src[64 + dd];
+  }
+  const float gp = __shfl_xor(gk, 16);
+  float x = gk;
+  if (dd < 32) {
+    const int jf = dd & 15;
+    const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+    x = dd < 16 ? gk * cs + gp * sn : gk * cs - gp * sn;
+  }
+  b.dk[((size_t)s * in.N + pos) * 64 + dd] = x;
+  b.dv[((size_t)s * in.N + pos) * 64 + dd] = gv;
+}
+
+// ---------------------------------------------------------------------------
+// State rows: for row i, from the last snapshot that holds it down to its
+// creation, the read-form gradient of that snapshot's version is taken back to
+// the raw sums (LayerNorm of K/n: dK = rs (g - mean g - x mean(g x)) / n; value
+// rho u, u = V/|V|: dV = (rho/|V|) (g - u (u.g)), d rho = u.g; the plain mean
+// V/n without value-length normalisation) and added to the running totals, which
+// replace the partial in place: afterwards entry (j, i) holds the gradient of
+// row i's sums as they stood after chunk j.  One wave per row; lane = dim.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, int rows_last) {
+  using RT = typename Rd<T>::type;
+  const int s = blockIdx.y;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (i >= rows_last) return;
+  const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const float* prho = d.prho + (size_t)s * m.V_cap;
+  const int* pcnt = d.pcount + (size_t)s * m.V_cap;
+  const float2* pnm = d.pnorm + (size_t)s * m.V_cap;
+  const int* idx = d.idx + (size_t)s * m.idx_total;
+  float* part = b.part_state + (size_t)s * m.idx_total * 96;
+  float* trho = b.tot_rho + (size_t)s * m.idx_total;
+  float tk = 0.f, tv = 0.f, tr = 0.f;
+  for (int j = b.absorbed - 1; j >= 0; --j) {
+    const int4 sc = d.sched[j];
+    if (i >= sc.x + sc.y + sc.z) break;   // the row does not exist yet after chunk j
+    const int64_t off = (int64_t)sc.w + i;
+    const int64_t ver = idx[off];
+    float* e = part + off * 96;
+    const float gk = l < 32 ? e[l] : 0.f;
+    const float gv = e[32 + l];
+    const float xh = l < 32 ? tof(pk[ver * 32 + l]) : 0.f;
+    const float2 nm = pnm[ver];
+    const float invn = 1.0f / (float)pcnt[ver];
+    // LayerNorm backward over the 32 live dims (lanes 0..31; lanes 32..63 carry zeros)
+    float sg = gk, sgx = gk * xh;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      sg += __shfl_xor(sg, o);
+      sgx += __shfl_xor(sgx, o);
+    }
+    const float dK = l < 32 ? nm.x * (gk - sg * (1.0f / 32.0f) - xh * sgx * (1.0f / 32.0f)) * invn : 0.f;
+    float dV, dR = 0.f;
+    if (m.no_vnorm) {
+      dV = gv * invn;
+    } else {
+      const float rho = prho[ver];
+      const float u = rho > 0.f ? tof(pv[ver * 64 + l]) / rho : 0.f;
+      float ug = u * gv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) ug += __shfl_xor(ug, o);
+      dV = nm.y * (gv - u * ug);
+      dR = ug;
+    }
+    tk += dK;
+    tv += dV;
+    tr += dR;
+    if (l < 32) e[l] = tk;
+    e[32 + l] = tv;
+    if (l == 0) trho[off] = tr;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Absorbed tokens: a merged token added g * (k_live, v) to its row after its
+// chunk; a sink or appended token created the row (k_live, v unscaled, radius
+// |v|).  Adds to dk (live dims) and dv, writes the gate-logit gradient
+// (sigmoid'), and zero for tokens never absorbed.  One wave per token.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_token_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  const int s = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (t >= in.N) return;
+  float* dl = b.dl + (size_t)s * in.N;
+  if (t >= (int64_t)b.absorbed * m.C) {
+    if (l == 0) dl[t] = 0.f;
+    return;
+  }
+  const int j = (int)(t / m.C);
+  const int kind = d.tkind[(size_t)s * m.max_tokens + t];
+  const int row = d.tslot[(size_t)s * m.max_tokens + t];
+  const int4 sc = d.sched[j];
+  const int64_t off = (int64_t)s * m.idx_total + sc.w + row;
+  const float* e = b.part_state + off * 96;
+  const float tk = l < 32 ? e[l] : 0.f;
+  const float tv = e[32 + l];
+  const size_t ti = (size_t)s * in.N + (size_t)t;
+  const float kt = l < 32 ? tof(reinterpret_cast<const T*>(in.k)[ti * 64 + 32 + l]) : 0.f;
+  const float vt = tof(reinterpret_cast<const T*>(in.v)[ti * 64 + l]);
+  float* dk = b.dk + ti * 64;
+  float* dv = b.dv + ti * 64;
+  if (kind == 2) {   // merge
+    const float lg = in.l[ti];
+    const float g = m.no_gate ? 1.f : 1.f / (1.f + __expf(-lg));
+    float dg = kt * tk + vt * tv;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) dg += __shfl_xor(dg, o);
+    if (l < 32) dk[32 + l] += g * tk;
+    dv[l] += g * tv;
+    if (l == 0) dl[t] = m.no_gate ? 0.f : dg * g * (1.f - g);
+  } else {           // sink or append: the row's creator
+    float v2 = vt * vt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v2 += __shfl_xor(v2, o);
+    const float tr = b.tot_rho[off];
+    const float nv = sqrtf(v2);
+    if (l < 32) dk[32 + l] += tk;
+    dv[l] += tv + (nv > 0.f ? tr * vt / nv : 0.f);
+    if (l == 0) dl[t] = 0.f;
+  }
+}
+
+template <typename T>
+hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last, hipStream_t st) {
+  const dim3 grid((unsigned)(m.BH * b.nq));
+  switch (m.C) {
+    case 32:
+      bwd_q_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, in, b);
+      bwd_kv_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, in, b);
+      break;
+    case 64:
+      bwd_q_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, in, b);
+      bwd_kv_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, in, b);
+      break;
+    case 128:
+      bwd_q_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, in, b);
+      bwd_kv_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, in, b);
+      break;
+    case 256:
+      bwd_q_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, in, b);
+      bwd_kv_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, in, b);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bwd_win_kernel<<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  if (rows_last > 0)
+    bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
+  bwd_token_kernel<T><<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last,
+                           hipStream_t st) {
+  if (in.N <= 0) return hipSuccess;
+  return m.bf16 ? bwd_dispatch<bf16>(m, d, in, b, rows_last, st) : bwd_dispatch<float>(m, d, in, b, rows_last, st);
+}
+
+}  // namespace kvm

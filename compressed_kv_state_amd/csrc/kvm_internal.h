@@ -54,6 +54,7 @@ struct Dev {
   void* pval;        // [BH][V_cap][64] T  read-form row versions: value rho * u
   float* prho;       // [BH][V_cap]       read-form row versions: radius
   int* pcount;       // [BH][V_cap]       read-form row versions: count
+  float2* pnorm;     // [BH][V_cap]       read-form row versions: (LayerNorm 1/sqrt(var + eps), value scale)
   int* idx;          // [BH][idx_total] per absorbed chunk j: version id of each row after chunk j
   int* tslot;        // [BH][max_tokens] trace: row created / merged into
   uint8_t* tkind;    // [BH][max_tokens] trace: 0 sink 1 append 2 merge 255 none
@@ -99,6 +100,33 @@ hipError_t scratch_address(void** out);
 // (computed on the device), and zeroed counters and exchange buffers (fill kernels, no memset).
 hipError_t launch_noalloc_init(const Dims& m, const Dev& d, const SchedParams& sp, double rope_theta,
                                hipStream_t st);
+
+// Backward pass: the forward's inputs, the output gradient, and where the input
+// gradients go (all [BH][N][64] / [BH][N]; gradients float32).
+struct BwdIn {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* l;
+  const void* dout;
+  int64_t N;         // tokens of the prefill being differentiated (positions [0, N))
+};
+// Backward buffers (carved from the caller's backward workspace) and outputs.
+struct Bwd {
+  float* part_win;     // [BH][nq][R][128]     per (query chunk, window key): dk (rotated) 64 | dv 64
+  float* part_state;   // [BH][idx_total][96]  per (snapshot j, row): read-form gradient (key 32 | value 64),
+                       //                      then the running totals of the row's sums after chunk j
+  float* tot_rho;      // [BH][idx_total]      running total of the radius gradient
+  float2* lse_d;       // [BH][N]              per query: log2 of the softmax denominator, D = sum P dP
+  float* dq;           // [BH][N][64]
+  float* dk;           // [BH][N][64]
+  float* dv;           // [BH][N][64]
+  float* dl;           // [BH][N]
+  int nq;              // query chunks ceil(N / C)
+  int absorbed;        // snapshots (absorbed chunks)
+};
+hipError_t launch_backward(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last,
+                           hipStream_t st);
 
 // Rows of unit directions a row-split scan workgroup keeps in LDS (bf16 path; 0 on the fp32 path).
 int scan_lds_rows(int C, bool is_bf16);

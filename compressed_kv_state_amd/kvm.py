@@ -90,6 +90,8 @@ def library() -> ctypes.CDLL:
         L.kvm_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp]
         L.kvm_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.kvm_prefill_noalloc.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, vp, vp, i64, vp]
+        L.kvm_backward_workspace_bytes.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_size_t)]
+        L.kvm_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.kvm_state_read.argtypes = [vp, i64, ctypes.POINTER(_View), vp]
         L.kvm_state_load.argtypes = [vp, ctypes.POINTER(_View), vp]
         L.kvm_snapshot_read.argtypes = [vp, i64, vp, vp, vp, vp]
@@ -103,7 +105,7 @@ def library() -> ctypes.CDLL:
         L.kvm_last_error.argtypes = []
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
-                     "kvm_prefill_noalloc",
+                     "kvm_prefill_noalloc", "kvm_backward_workspace_bytes", "kvm_prefill_backward",
                      "kvm_decode_step", "kvm_state_read", "kvm_state_load", "kvm_snapshot_read", "kvm_state_get_info",
                      "kvm_state_reset", "kvm_state_check", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
@@ -305,6 +307,27 @@ class KvmState:
         _check(library().kvm_decode_step(self._h, q2.data_ptr(), k2.data_ptr(), v2.data_ptr(), g2.data_ptr(),
                                          o2.data_ptr(), _stream(self.device)))
         return out
+
+    def backward(self, q, k, v, gate_logits, d_out, workspace: Optional[torch.Tensor] = None):
+        """kvm_prefill_backward: gradients of sum(d_out * out) for the prefill this state ran over
+        positions [0, n) with these inputs (the state needs trace=True).  Returns float32
+        (d_q, d_k, d_v [B*H, n, 64], d_gate [B*H, n]).  `workspace` (uint8, at least
+        kvm_backward_workspace_bytes) is allocated here when not given."""
+        n = q.shape[-2]
+        q2, k2, v2, o2 = (self._data(t, nm, n) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (d_out, "d_out")))
+        g2 = self._gate(gate_logits, n)
+        S = self.cfg.seqs
+        dq, dk, dv = (torch.empty(S, n, self.cfg.head_dim, dtype=torch.float32, device=self.device) for _ in range(3))
+        dg = torch.empty(S, n, dtype=torch.float32, device=self.device)
+        need = ctypes.c_size_t()
+        _check(library().kvm_backward_workspace_bytes(ctypes.byref(self._c), ctypes.byref(need)))
+        if workspace is None:
+            workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=self.device)
+        _check(library().kvm_prefill_backward(self._h, q2.data_ptr(), k2.data_ptr(), v2.data_ptr(), g2.data_ptr(),
+                                              o2.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                              dg.data_ptr(), n, workspace.data_ptr(), workspace.numel(),
+                                              _stream(self.device)))
+        return dq, dk, dv, dg
 
     def reset(self):
         """Back to position 0 with an empty state (queued on the current stream)."""

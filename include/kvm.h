@@ -220,6 +220,34 @@ kvm_status kvm_prefill_noalloc(const kvm_config* cfg, const void* q, const void*
 kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const void* v,
                            const float* gate_logits, void* out, void* stream);
 
+/* Device workspace for kvm_prefill_backward over up to cfg.max_tokens tokens
+ * (bytes; 256-byte aligned): per-(query chunk, key) partial gradients, the
+ * running gradients of every snapshot row's sums, per-query softmax
+ * statistics.  Host only.  Errors: KVM_E_INVALID_ARG. */
+kvm_status kvm_backward_workspace_bytes(const kvm_config* cfg, size_t* bytes);
+
+/* Backward pass of the prefill ([KVM abstract]: the layer supports chunk-wise
+ * parallelizable training): the gradient of sum(d_out * out) with respect to
+ * q, k, v and the gate logits, where out is what kvm_prefill computed on this
+ * state for positions [0, n_tokens) with these inputs.  The discrete choices
+ * of the forward (the winner-take-all row of each merged token and the
+ * appended tokens, [KVM summary, Core mechanisms 2-3]) are held fixed; the
+ * gradient flows through the joint softmax, RoPE, the just-in-time read form
+ * (LayerNorm of K/n, values at the read radius), the gated sums of the chunk
+ * recurrence and the gate sigmoid.  Counts carry no gradient.
+ * The state must have been created with KVM_FLAG_TRACE (the decisions are read
+ * from the trace) and be at position n_tokens (prefill calls and decode steps
+ * from position 0; q, k, v and gate_logits are the inputs of all of them).
+ * q, k, v, d_out: [B*H, n_tokens, 64] in cfg.dtype; gate_logits [B*H, n_tokens]
+ * f32; outputs d_q, d_k, d_v [B*H, n_tokens, 64] f32 and d_gate [B*H, n_tokens]
+ * f32 (written, not accumulated).  The state is not modified.  Deterministic:
+ * no float atomics; the same call gives the same bits.
+ * Errors: KVM_E_INVALID_ARG (pointers, sizes, no trace), KVM_E_STATE (position
+ * differs from n_tokens, poisoned state), KVM_E_WORKSPACE, KVM_E_HIP. */
+kvm_status kvm_prefill_backward(kvm_state* st, const void* q, const void* k, const void* v, const float* gate_logits,
+                                const void* d_out, float* d_q, float* d_k, float* d_v, float* d_gate,
+                                int64_t n_tokens, void* d_workspace, size_t workspace_bytes, void* stream);
+
 /* Export the state ([KVM lay summary, "smart merge"]: raw sums and counts,
  * divided only at read; [KVM summary, Core mechanisms 2]: the read form).
  *   chunk == -1: the current state.  Every field of `dst` may be requested;

@@ -128,6 +128,10 @@ int main() {
   kvm_profile_times pt;
   EXPECT(kvm_profile_read(nullptr, &pt) == KVM_E_INVALID_ARG);
   EXPECT(kvm_state_destroy(nullptr) == KVM_OK);
+  EXPECT(kvm_backward_workspace_bytes(&c, &bytes) == KVM_OK && bytes > 0);
+  EXPECT(kvm_backward_workspace_bytes(nullptr, &bytes) == KVM_E_INVALID_ARG);
+  EXPECT(kvm_prefill_backward(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              1, nullptr, 0, nullptr) == KVM_E_INVALID_ARG);
   // the entry point that allocates nothing: argument checks come before any device call
   alignas(16) static uint16_t buf[4][2 * 3 * 64 * 64];
   alignas(16) static float gl[2 * 3 * 64];
