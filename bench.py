@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "KVM-layer prefill tokens/s (B*H*N) + % bf16 MFMA peak; decode HBM GB/s"
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 (the backward contracts in fp32)
 KERNEL_SRC = os.path.join(ROOT, "compressed_kv_state_amd", "csrc", "kvm_kernels.hip")
 ATTN_KERNEL = "attn_dma_kernel"   # the bf16 attention kernel for chunks of 128 / 256
 COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_dma_kernel_350m_sqrt8_counters.md")
@@ -79,6 +80,25 @@ def attn_flops(cfg, n: int) -> int:
         lo = max(0, c * C - W)
         for t in range(c * C, min(n, (c + 1) * C)):
             total += 192 * S + 256 * (t - lo + 1)
+    return total * cfg.seqs
+
+
+def backward_flops(cfg, n: int) -> int:
+    """Algorithmic FLOPs of the attention part of one backward over n tokens from position 0: the
+    five products of an attention backward (scores, dP, dq, dk, dv).  Per query t of chunk c:
+    448 per state row (2*32 scores + 2*64 dP + 2*32 dq + 2*32 dk + 2*64 dv on the 32 live key
+    dims) and 640 per window key (5 * 2*64); masked and zero-padded work is not counted."""
+    from compressed_kv_state_amd import schedule
+    C, W = cfg.chunk, cfg.window
+    nq = -(-n // C)
+    rows = schedule(cfg, max(nq, 1))[2].tolist()
+    total = 0
+    for c in range(nq):
+        j = c - W // C - 1
+        S = rows[j] if j >= 0 else 0
+        lo = max(0, c * C - W)
+        for t in range(c * C, min(n, (c + 1) * C)):
+            total += 448 * S + 640 * (t - lo + 1)
     return total * cfg.seqs
 
 
@@ -257,6 +277,43 @@ def bench_other_workloads(steps: int):
     return res
 
 
+def bench_backward(w, tensors, steps: int):
+    """kvm_prefill_backward over the whole workload after one traced prefill: time per backward
+    (HIP events on the stream it runs on) and its algorithmic fp32 contraction rate."""
+    import torch
+    from compressed_kv_state_amd import KvmConfig, KvmState
+    q, k, v, g = tensors
+    cfg = KvmConfig.of(w, max_tokens=w.n_tokens, trace=True)
+    st = KvmState(cfg)
+    out = st.prefill(q, k, v, g)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    d_out = torch.randn(out.shape, device="cuda", generator=gen).to(out.dtype)
+    st.backward(q, k, v, g, d_out)      # warm-up (allocates the backward workspace once)
+    torch.cuda.synchronize()
+    import ctypes
+    from compressed_kv_state_amd.kvm import library
+    need = ctypes.c_size_t()
+    library().kvm_backward_workspace_bytes(ctypes.byref(st._c), ctypes.byref(need))
+    ws = torch.empty(int(need.value), dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        grads = st.backward(q, k, v, g, d_out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert all(torch.isfinite(t).all() for t in grads), "non-finite gradient"
+    flops = backward_flops(cfg, w.n_tokens)
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"backward: {ms:.3f} ms, {achieved:.1f} TFLOP/s algorithmic (fp32)")
+    del st, grads, ws
+    return {"ms_per_step": ms, "tokens_per_s": w.seqs * w.n_tokens / (ms * 1e-3), "flops": flops,
+            "achieved": achieved, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_MFMA_TFLOPS, "workspace_bytes": int(need.value),
+            "note": "gradients of q, k, v and gate logits, fp32 contractions; time of the whole backward "
+                    "(five kernels) per prefill of the workload"}
+
+
 VARIANTS = {"no_value_norm": dict(value_norm=False), "no_sink_protect": dict(sink_protect=False),
             "no_merge_gate": dict(merge_gate=False), "power_0.6_alpha3": dict(sched="power", alpha=3, exponent=0.6)}
 
@@ -391,13 +448,16 @@ def copy_calibration():
     log(f"copy calibration: 3 copies of {n} bytes")
 
 
-def _counter_rows(path, counter):
-    """{kernel name: [values in dispatch order]} for one counter of a rocprofv3 --pmc CSV."""
+def _counter_rows(path, counter, grid=None):
+    """{kernel name: [values in dispatch order]} for one counter of a rocprofv3 --pmc CSV
+    (only dispatches of `grid` threads when given; copy kernels always)."""
     import csv
     vals = {}
     with open(path) as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter:
+                continue
+            if grid and "copy" not in row.get("Kernel_Name", "").lower() and row.get("Grid_Size") != str(grid):
                 continue
             vals.setdefault(row.get("Kernel_Name", ""), []).append(float(row["Counter_Value"]))
     return vals
@@ -415,15 +475,15 @@ def _copy_scale(d):
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str, kernel: str = ATTN_KERNEL,
-                       title: str = ""):
+                       title: str = "", grid=None):
     """Reduce two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) to a summary of `kernel`.
 
     Each counter is scaled by 1 GiB over its mean reading on the 1 GiB device copies of
     --copy-calibration (the copy's dispatches are the large ones of the copy kernel).  For the
     attention kernel the summary also carries the traffic figure bench.py reads, tied to a hash
     of the kernel's source text."""
-    fetch = _counter_rows(fetch_csv, "FETCH_SIZE")
-    write = _counter_rows(write_csv, "WRITE_SIZE")
+    fetch = _counter_rows(fetch_csv, "FETCH_SIZE", grid)
+    write = _counter_rows(write_csv, "WRITE_SIZE", grid)
     sf, cf = _copy_scale(fetch)
     sw, cw = _copy_scale(write)
 
@@ -438,6 +498,8 @@ def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str
     traffic = (f_kib * sf + w_kib * sw) * 1024.0
     with open(out_md, "w") as f:
         f.write(f"# {kernel} HBM traffic per dispatch{': ' + title if title else ''}\n\n")
+        if grid:
+            f.write(f"Dispatches of {grid} threads only.\n\n")
         f.write(f"Command (one pass per counter): `{command}`\n\n")
         f.write(f"| counter | {kernel} KiB/dispatch (mean of {len(fv)}/{len(wv)}) | total KiB | copy kernel "
                 f"KiB/dispatch (1 GiB moved) | scale |\n|---|---|---|---|---|\n")
@@ -494,6 +556,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-attn-alone", action="store_true",
@@ -504,6 +567,7 @@ def main():
     ap.add_argument("--counter-kernel", default=ATTN_KERNEL, help="kernel the counter summary describes")
     ap.add_argument("--counter-out", default=COUNTERS_MD, help="where the counter summary goes")
     ap.add_argument("--counter-title", default="", help="workload line of the counter summary")
+    ap.add_argument("--counter-grid", type=int, default=0, help="only dispatches of this many threads")
     ap.add_argument("--summarize-trace", nargs=4, metavar=("DB", "OUT_MD", "COMMAND", "TITLE"))
     args = ap.parse_args()
 
@@ -512,7 +576,8 @@ def main():
         return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters[0], args.summarize_counters[1], args.counter_out,
-                           args.summarize_counters[2], args.counter_kernel, args.counter_title)
+                           args.summarize_counters[2], args.counter_kernel, args.counter_title,
+                           args.counter_grid or None)
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -572,6 +637,8 @@ def main():
                    "peak_GBs": PEAK_HBM_GBS, "frac": in_bytes / (scan_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if not args.no_attn_alone:
         res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
+    if not args.no_backward:
+        res["backward"] = bench_backward(wp, tensors, 3)
     if not args.no_variants:
         res["variants"] = bench_variants(wp, tensors, 5)
     if not args.no_other:

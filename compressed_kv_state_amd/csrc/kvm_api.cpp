@@ -626,7 +626,7 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
 
 namespace {
 struct BwdPlan {
-  size_t part_win, part_state, tot_rho, lse_d, total;
+  size_t part_win, part_state, tot_rho, lse_d, qr32, kr32, total;
 };
 BwdPlan bwd_plan(const kvm::Dims& m, int64_t n_tokens) {
   BwdPlan b{};
@@ -642,6 +642,8 @@ BwdPlan bwd_plan(const kvm::Dims& m, int64_t n_tokens) {
   b.part_state = take(BH * (size_t)m.idx_total * 96 * 4);
   b.tot_rho = take(BH * (size_t)m.idx_total * 4);
   b.lse_d = take(BH * (size_t)n_tokens * 8);
+  b.qr32 = take(BH * (size_t)n_tokens * 64 * 4);
+  b.kr32 = take(BH * (size_t)n_tokens * 64 * 4);
   b.total = off;
   return b;
 }
@@ -684,6 +686,8 @@ kvm_status kvm_prefill_backward(kvm_state* st, const void* q, const void* k, con
   b.part_state = reinterpret_cast<float*>(w + bp.part_state);
   b.tot_rho = reinterpret_cast<float*>(w + bp.tot_rho);
   b.lse_d = reinterpret_cast<float2*>(w + bp.lse_d);
+  b.qr32 = reinterpret_cast<float*>(w + bp.qr32);
+  b.kr32 = reinterpret_cast<float*>(w + bp.kr32);
   b.dq = d_q;
   b.dk = d_k;
   b.dv = d_v;

@@ -50,43 +50,75 @@ constexpr int kPitch = 65;   // fp32 tile rows in LDS: 64 dims + 1 (rows land on
 
 // Tile T of query chunk c's keys: state tiles (32 snapshot rows each) first,
 // then window tiles (32 positions of [lo, hi) each).  Stages the keys (state:
-// read-form key in columns 32..63, columns 0..31 zero; window: the input key
-// rotated by RoPE at its position, fp32) and the values (state: read-form
-// value; window: the input value) into LDS as fp32, zero past the end.
+// read-form key in columns 32..63, columns 0..31 zero; window: the rotated key
+// kept by bwd_rot_kernel) and the values (state: read-form value; window: the
+// input value) into LDS as fp32, zero past the end; 16-byte loads (4 dims per
+// thread and row).
+template <typename E>
+__device__ __forceinline__ float4 load4(const E* p) {
+  if constexpr (sizeof(E) == 4) {
+    return *reinterpret_cast<const float4*>(p);
+  } else {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    const E* e = reinterpret_cast<const E*>(&x);
+    return make_float4(tof(e[0]), tof(e[1]), tof(e[2]), tof(e[3]));
+  }
+}
+
 template <typename T>
 __device__ void bwd_stage(float* Kt, float* Vt, int Tile, int n_st, int S, const int* idxl, const Dims& m,
-                          const Dev& d, const BwdIn& in, int s, int64_t lo, int64_t hi, int tid, int nt) {
+                          const Dev& d, const BwdIn& in, const Bwd& b, int s, int64_t lo, int64_t hi, int tid,
+                          int nt) {
   using RT = typename Rd<T>::type;
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
-  const T* kin = reinterpret_cast<const T*>(in.k) + (size_t)s * in.N * 64;
+  const float* kr32 = b.kr32 + (size_t)s * in.N * 64;
   const T* vin = reinterpret_cast<const T*>(in.v) + (size_t)s * in.N * 64;
-  for (int e = tid; e < 32 * 64; e += nt) {
-    const int key = e >> 6, dd = e & 63;
-    float kv = 0.f, vv = 0.f;
+  for (int e = tid; e < 32 * 16; e += nt) {
+    const int key = e >> 4, c4 = e & 15;
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
     if (Tile < n_st) {
       const int r = Tile * 32 + key;
       if (r < S) {
         const int64_t ver = idxl[r];
-        if (dd >= 32) kv = tof(pk[ver * 32 + dd - 32]);
-        vv = tof(pv[ver * 64 + dd]);
+        if (c4 >= 8) kv = load4(pk + ver * 32 + 4 * c4 - 32);
+        vv = load4(pv + ver * 64 + 4 * c4);
       }
     } else {
       const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
       if (pos < hi) {
-        const T* kr = kin + pos * 64;
-        kv = tof(kr[dd]);
-        if (dd < 32) {
-          const int jf = dd & 15;
-          const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
-          kv = dd < 16 ? kv * cs - tof(kr[dd + 16]) * sn : kv * cs + tof(kr[dd - 16]) * sn;
-        }
-        vv = tof(vin[pos * 64 + dd]);
+        kv = *reinterpret_cast<const float4*>(kr32 + pos * 64 + 4 * c4);
+        vv = load4(vin + pos * 64 + 4 * c4);
       }
     }
-    Kt[key * kPitch + dd] = kv;
-    Vt[key * kPitch + dd] = vv;
+    float* kd = Kt + key * kPitch + 4 * c4;
+    float* vd = Vt + key * kPitch + 4 * c4;
+    kd[0] = kv.x; kd[1] = kv.y; kd[2] = kv.z; kd[3] = kv.w;
+    vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
   }
+}
+
+// Rotated queries and keys of every position, fp32 (RoPE at the position,
+// [KVM summary, Core mechanisms 4]): read by the tiles of several query
+// chunks, so rotated once.  One wave per position, lane = dim.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_rot_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  const int s = blockIdx.y;
+  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int dd = threadIdx.x & 63;
+  if (pos >= in.N) return;
+  const size_t r = ((size_t)s * in.N + pos) * 64;
+  const T* qr = reinterpret_cast<const T*>(in.q) + r;
+  const T* kr = reinterpret_cast<const T*>(in.k) + r;
+  float x = tof(qr[dd]), y = tof(kr[dd]);
+  if (dd < 32) {
+    const int jf = dd & 15;
+    const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+    x = dd < 16 ? x * cs - tof(qr[dd + 16]) * sn : x * cs + tof(qr[dd - 16]) * sn;
+    y = dd < 16 ? y * cs - tof(kr[dd + 16]) * sn : y * cs + tof(kr[dd - 16]) * sn;
+  }
+  b.qr32[r + dd] = x;
+  b.kr32[r + dd] = y;
 }
 
 // Tile validity of score element (key row kr of the tile, query at position qp).
@@ -100,8 +132,8 @@ __device__ __forceinline__ bool bwd_valid(int Tile, int n_st, int S, int64_t lo,
 
 // ---------------------------------------------------------------------------
 // dq.  One wave per 32 queries, lane l%32 = query; scores S^T = K . Q^T with the
-// keys as rows.  Three sweeps over the key tiles: the row maximum, then the row
-// sum and D = sum_j P_j dP_j (dP = dO . v_j), then dq += dS . K.
+// keys as rows.  Two sweeps over the key tiles: the row maximum, row sum and
+// D = sum_j P_j dP_j (dP = dO . v_j) online, then dq += dS . K.
 // ---------------------------------------------------------------------------
 template <typename T, int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
@@ -132,18 +164,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(Dims m, Dev d, BwdIn in,
   // query (rotated, scaled into log2 units) and dO, as B operands: step k takes dims 2k + h
   float qf[32], df[32];
   {
-    const T* qr = reinterpret_cast<const T*>(in.q) + ((size_t)s * in.N + qq) * 64;
+    const float* qr = b.qr32 + ((size_t)s * in.N + qq) * 64;
     const T* dor = reinterpret_cast<const T*>(in.dout) + ((size_t)s * in.N + qq) * 64;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const int dd = 2 * k + h;
-      float x = tof(qr[dd]);
-      if (dd < 32) {
-        const int jf = dd & 15;
-        const float cs = d.rope_cos[qq * 16 + jf], sn = d.rope_sin[qq * 16 + jf];
-        x = dd < 16 ? x * cs - tof(qr[dd + 16]) * sn : x * cs + tof(qr[dd - 16]) * sn;
-      }
-      qf[k] = x * c2;
+      qf[k] = qr[dd] * c2;
       df[k] = qvalid ? tof(dor[dd]) : 0.f;
     }
   }
@@ -164,30 +190,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(Dims m, Dev d, BwdIn in,
     for (int k = 0; k < 32; ++k) acc = mfma_f32(Vt[ql * kPitch + 2 * k + h], df[k], acc);
     return acc;
   };
-  // sweep 1: row maximum
-  float mx = -kInf;
+  // sweep 1: the row maximum, row sum and D = sum_j P_j dP_j, online (the two
+  // halves of a lane pair hold the same query and move their reference together)
+  float mx = -kInf, ls = 0.f, ds = 0.f;
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
-    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, s, lo, hi, tid, NT);
-    __syncthreads();
-    const f32x16 a = scores(Tile);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, a[r]);
-  }
-  mx = fmaxf(mx, partner_f(mx));
-  // sweep 2: row sum and D
-  float ls = 0.f, ds = 0.f;
-  for (int Tile = 0; Tile < n_tiles; ++Tile) {
-    __syncthreads();
-    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, s, lo, hi, tid, NT);
+    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, b, s, lo, hi, tid, NT);
     __syncthreads();
     const f32x16 a = scores(Tile);
     const f32x16 dp = dscores();
+    float mt = -kInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = a[r] == -kInf ? 0.f : exp2f(a[r] - mx);
-      ls += p;
-      ds = fmaf(p, dp[r], ds);
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, a[r]);
+    mt = fmaxf(mt, partner_f(mt));
+    const float mn = fmaxf(mx, mt);
+    if (mn != -kInf) {
+      const float al = mx == -kInf ? 0.f : exp2f(mx - mn);
+      ls *= al;
+      ds *= al;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = a[r] == -kInf ? 0.f : exp2f(a[r] - mn);
+        ls += p;
+        ds = fmaf(p, dp[r], ds);
+      }
+      mx = mn;
     }
   }
   ls += partner_f(ls);
@@ -195,11 +222,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(Dims m, Dev d, BwdIn in,
   const float lse = mx + log2f(ls);
   const float Dq = ds / ls;
   if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
-  // sweep 3: dq += dS . K (contraction over the tile's keys in register order)
+  // sweep 2: dq += dS . K (contraction over the tile's keys in register order)
   f32x16 dq0 = {}, dq1 = {};
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
-    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, s, lo, hi, tid, NT);
+    bwd_stage<T>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, b, s, lo, hi, tid, NT);
     __syncthreads();
     const f32x16 a = scores(Tile);
     const f32x16 dp = dscores();
@@ -270,29 +297,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in
   const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
-  const T* kin = reinterpret_cast<const T*>(in.k) + (size_t)s * in.N * 64;
   const T* vin = reinterpret_cast<const T*>(in.v) + (size_t)s * in.N * 64;
-  const T* qin = reinterpret_cast<const T*>(in.q) + (size_t)s * in.N * 64;
   const T* doin = reinterpret_cast<const T*>(in.dout) + (size_t)s * in.N * 64;
   for (int q0 = 0; q0 < C; q0 += QB) {
     // the block's queries, rotated (unscaled), their dO and (lse, D); zero past the end
     __syncthreads();
-    for (int e = tid; e < QB * 64; e += NW * 64) {
-      const int qi = e >> 6, dd = e & 63;
+    for (int e = tid; e < QB * 16; e += NW * 64) {
+      const int qi = e >> 4, c4 = e & 15;
       const int64_t pos = cpos + q0 + qi;
-      float x = 0.f, g = 0.f;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), g = x;
       if (pos < in.N) {
-        const T* qr = qin + pos * 64;
-        x = tof(qr[dd]);
-        if (dd < 32) {
-          const int jf = dd & 15;
-          const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
-          x = dd < 16 ? x * cs - tof(qr[dd + 16]) * sn : x * cs + tof(qr[dd - 16]) * sn;
-        }
-        g = tof(doin[pos * 64 + dd]);
+        x = *reinterpret_cast<const float4*>(b.qr32 + ((size_t)s * in.N + pos) * 64 + 4 * c4);
+        g = load4(doin + pos * 64 + 4 * c4);
       }
-      Qs[qi * kPitch + dd] = x;
-      Ds[qi * kPitch + dd] = g;
+      float* qd = Qs + qi * kPitch + 4 * c4;
+      float* gd = Ds + qi * kPitch + 4 * c4;
+      qd[0] = x.x; qd[1] = x.y; qd[2] = x.z; qd[3] = x.w;
+      gd[0] = g.x; gd[1] = g.y; gd[2] = g.z; gd[3] = g.w;
     }
     for (int qi = tid; qi < QB; qi += NW * 64) {
       const int64_t pos = cpos + q0 + qi;
@@ -319,17 +340,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in
         kpos = lo + (int64_t)(Tile - n_st) * 32 + kl;
         kvalid = kpos < hi;
         const int64_t pp = kvalid ? kpos : lo;
-        const T* kr = kin + pp * 64;
+        const float* kr = b.kr32 + ((size_t)s * in.N + pp) * 64;
 #pragma unroll
         for (int k = 0; k < 32; ++k) {
           const int dd = 2 * k + h;
-          float x = tof(kr[dd]);
-          if (dd < 32) {
-            const int jf = dd & 15;
-            const float cs = d.rope_cos[pp * 16 + jf], sn = d.rope_sin[pp * 16 + jf];
-            x = dd < 16 ? x * cs - tof(kr[dd + 16]) * sn : x * cs + tof(kr[dd - 16]) * sn;
-          }
-          kf[k] = kvalid ? x : 0.f;
+          kf[k] = kvalid ? kr[dd] : 0.f;
           vf[k] = kvalid ? tof(vin[pp * 64 + dd]) : 0.f;
         }
       }
@@ -466,43 +481,63 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   float* part = b.part_state + (size_t)s * m.idx_total * 96;
   float* trho = b.tot_rho + (size_t)s * m.idx_total;
   float tk = 0.f, tv = 0.f, tr = 0.f;
-  for (int j = b.absorbed - 1; j >= 0; --j) {
+  // the inputs of snapshot j are loaded while snapshot j + 1 is processed
+  struct In {
+    int64_t off;
+    float gk, gv, xh, rho, vh, invn;
+    float2 nm;
+    bool live;
+  };
+  auto fetch = [&](int j) {
+    In x{};
+    x.live = false;
+    if (j < 0) return x;
     const int4 sc = d.sched[j];
-    if (i >= sc.x + sc.y + sc.z) break;   // the row does not exist yet after chunk j
-    const int64_t off = (int64_t)sc.w + i;
-    const int64_t ver = idx[off];
-    float* e = part + off * 96;
-    const float gk = l < 32 ? e[l] : 0.f;
-    const float gv = e[32 + l];
-    const float xh = l < 32 ? tof(pk[ver * 32 + l]) : 0.f;
-    const float2 nm = pnm[ver];
-    const float invn = 1.0f / (float)pcnt[ver];
+    if (i >= sc.x + sc.y + sc.z) return x;   // the row does not exist yet after chunk j
+    x.live = true;
+    x.off = (int64_t)sc.w + i;
+    const int64_t ver = idx[x.off];
+    const float* e = part + x.off * 96;
+    x.gk = l < 32 ? e[l] : 0.f;
+    x.gv = e[32 + l];
+    x.xh = l < 32 ? tof(pk[ver * 32 + l]) : 0.f;
+    x.nm = pnm[ver];
+    x.invn = 1.0f / (float)pcnt[ver];
+    x.rho = prho[ver];
+    x.vh = tof(pv[ver * 64 + l]);
+    return x;
+  };
+  In cur = fetch(b.absorbed - 1);
+  for (int j = b.absorbed - 1; j >= 0 && cur.live; --j) {
+    const In nxt = fetch(j - 1);
     // LayerNorm backward over the 32 live dims (lanes 0..31; lanes 32..63 carry zeros)
-    float sg = gk, sgx = gk * xh;
+    float sg = cur.gk, sgx = cur.gk * cur.xh;
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
       sg += __shfl_xor(sg, o);
       sgx += __shfl_xor(sgx, o);
     }
-    const float dK = l < 32 ? nm.x * (gk - sg * (1.0f / 32.0f) - xh * sgx * (1.0f / 32.0f)) * invn : 0.f;
+    const float dK =
+        l < 32 ? cur.nm.x * (cur.gk - sg * (1.0f / 32.0f) - cur.xh * sgx * (1.0f / 32.0f)) * cur.invn : 0.f;
     float dV, dR = 0.f;
     if (m.no_vnorm) {
-      dV = gv * invn;
+      dV = cur.gv * cur.invn;
     } else {
-      const float rho = prho[ver];
-      const float u = rho > 0.f ? tof(pv[ver * 64 + l]) / rho : 0.f;
-      float ug = u * gv;
+      const float u = cur.rho > 0.f ? cur.vh / cur.rho : 0.f;
+      float ug = u * cur.gv;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) ug += __shfl_xor(ug, o);
-      dV = nm.y * (gv - u * ug);
+      dV = cur.nm.y * (cur.gv - u * ug);
       dR = ug;
     }
     tk += dK;
     tv += dV;
     tr += dR;
+    float* e = part + cur.off * 96;
     if (l < 32) e[l] = tk;
     e[32 + l] = tv;
-    if (l == 0) trho[off] = tr;
+    if (l == 0) trho[cur.off] = tr;
+    cur = nxt;
   }
 }
 
@@ -560,6 +595,7 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims m, Dev d, BwdIn in,
 template <typename T>
 hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last, hipStream_t st) {
   const dim3 grid((unsigned)(m.BH * b.nq));
+  bwd_rot_kernel<T><<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   switch (m.C) {
     case 32:
       bwd_q_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, in, b);

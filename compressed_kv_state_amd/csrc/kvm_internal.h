@@ -118,6 +118,8 @@ struct Bwd {
                        //                      then the running totals of the row's sums after chunk j
   float* tot_rho;      // [BH][idx_total]      running total of the radius gradient
   float2* lse_d;       // [BH][N]              per query: log2 of the softmax denominator, D = sum P dP
+  float* qr32;         // [BH][N][64]          rotated queries, fp32
+  float* kr32;         // [BH][N][64]          rotated keys, fp32
   float* dq;           // [BH][N][64]
   float* dk;           // [BH][N][64]
   float* dv;           // [BH][N][64]
