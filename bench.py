@@ -314,6 +314,43 @@ def bench_backward(w, tensors, steps: int):
                     "(five kernels) per prefill of the workload"}
 
 
+def bench_projections(w, steps: int):
+    """The block's projections at the workload's shapes (x [B, N, H*64], synthetic weights):
+    kvm_project_in (q, k, v and the per-head gate logit) and kvm_project_out, HIP events on the
+    stream they run on, against the dense bf16 MFMA peak."""
+    import torch
+    from compressed_kv_state_amd import KvmConfig, project_in, project_out
+    cfg = KvmConfig.of(w, max_tokens=w.n_tokens)
+    D, H = w.heads * 64, w.heads
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn(w.batch, w.n_tokens, D, device="cuda", generator=g).bfloat16()
+    w_in = (torch.randn(3 * D + H, D, device="cuda", generator=g) / D ** 0.5).bfloat16()
+    b_gate = torch.zeros(H, device="cuda")
+    w_out = (torch.randn(D, D, device="cuda", generator=g) / D ** 0.5).bfloat16()
+    res = {}
+    q, k, v, gl = project_in(cfg, x, w_in, b_gate)
+    o = q.contiguous()
+    for name, fn, flops in (("in", lambda: project_in(cfg, x, w_in, b_gate),
+                             2 * w.batch * w.n_tokens * D * (3 * D + H)),
+                            ("out", lambda: project_out(cfg, o, w_out), 2 * w.batch * w.n_tokens * D * D)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        achieved = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": ms, "flops": flops, "achieved": achieved, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_MFMA_TFLOPS}
+        log(f"projection {name}: {ms:.3f} ms, {achieved:.0f} TFLOP/s")
+    res["note"] = (f"x [{w.batch}, {w.n_tokens}, {D}] bf16; in: [{3 * D + H} x {D}] (q, k, v, one gate logit per "
+                   f"head), out: [{D} x {D}]; fp32 accumulation; includes the scatter into the layer's layout")
+    return res
+
+
 VARIANTS = {"no_value_norm": dict(value_norm=False), "no_sink_protect": dict(sink_protect=False),
             "no_merge_gate": dict(merge_gate=False), "power_0.6_alpha3": dict(sched="power", alpha=3, exponent=0.6)}
 
@@ -557,6 +594,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-projections", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-attn-alone", action="store_true",
@@ -639,6 +677,8 @@ def main():
         res["attn_alone"] = bench_attn_alone(wp, tensors, 3)
     if not args.no_backward:
         res["backward"] = bench_backward(wp, tensors, 3)
+    if not args.no_projections:
+        res["projections"] = bench_projections(wp, 5)
     if not args.no_variants:
         res["variants"] = bench_variants(wp, tensors, 5)
     if not args.no_other:

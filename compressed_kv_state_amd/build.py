@@ -35,7 +35,7 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["kvm_kernels.hip", "kvm_backward.hip", "kvm_api.cpp"]
+SOURCES = ["kvm_kernels.hip", "kvm_backward.hip", "kvm_proj.hip", "kvm_api.cpp"]
 
 
 PACKED_FP32 = re.compile(r"\bv_pk_(fma|mul|add)_f32\b")

@@ -701,6 +701,57 @@ kvm_status kvm_prefill_backward(kvm_state* st, const void* q, const void* k, con
   return KVM_OK;
 }
 
+kvm_status kvm_project_in(const kvm_config* cfg, const void* x, const void* w_in, const float* b_gate, void* q,
+                          void* k, void* v, float* gate_logits, int64_t n_tokens, void* stream) {
+  kvm_status s = validate(cfg);
+  if (s != KVM_OK) return s;
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 31)) return fail(KVM_E_INVALID_ARG, "n_tokens out of range");
+  if (n_tokens == 0) return KVM_OK;
+  if (!x || !w_in || !q || !k || !v || !gate_logits) return fail(KVM_E_INVALID_ARG, "NULL pointer");
+  if (!aligned(x, 16) || !aligned(w_in, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(gate_logits, 4) || (b_gate && !aligned(b_gate, 4)))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits and bias 4-byte)");
+  kvm::ProjArgs a{};
+  a.x = x;
+  a.w = w_in;
+  a.bias = b_gate;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gl = gate_logits;
+  a.H = cfg->heads;
+  a.K = cfg->heads * 64;
+  a.Nout = 3 * a.K + a.H;
+  a.N = n_tokens;
+  a.M = (int64_t)cfg->batch * n_tokens;
+  hipError_t e = kvm::launch_proj(a, false, cfg->dtype == KVM_BF16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVM_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
+  return KVM_OK;
+}
+
+kvm_status kvm_project_out(const kvm_config* cfg, const void* o, const void* w_out, void* y, int64_t n_tokens,
+                           void* stream) {
+  kvm_status s = validate(cfg);
+  if (s != KVM_OK) return s;
+  if (n_tokens < 0 || n_tokens > ((int64_t)1 << 31)) return fail(KVM_E_INVALID_ARG, "n_tokens out of range");
+  if (n_tokens == 0) return KVM_OK;
+  if (!o || !w_out || !y) return fail(KVM_E_INVALID_ARG, "NULL pointer");
+  if (!aligned(o, 16) || !aligned(w_out, 16) || !aligned(y, 16))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned");
+  kvm::ProjArgs a{};
+  a.x = o;
+  a.w = w_out;
+  a.y = y;
+  a.H = cfg->heads;
+  a.K = cfg->heads * 64;
+  a.Nout = a.K;
+  a.N = n_tokens;
+  a.M = (int64_t)cfg->batch * n_tokens;
+  hipError_t e = kvm::launch_proj(a, true, cfg->dtype == KVM_BF16, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KVM_E_HIP, std::string("projection launch: ") + hipGetErrorString(e));
+  return KVM_OK;
+}
+
 kvm_status kvm_state_read(const kvm_state* st, int64_t chunk, kvm_state_view* dst, void* stream) {
   if (!st || !dst) return fail(KVM_E_INVALID_ARG, "NULL argument");
   if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");

@@ -130,6 +130,24 @@ struct Bwd {
 hipError_t launch_backward(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last,
                            hipStream_t st);
 
+// Projections around the layer: C[m][n] = sum_k A[m][k] W[n][k].
+struct ProjArgs {
+  const void* x;      // in: x [M = B*N][K]; out: the layer output o [B*H][N][64]
+  const void* w;      // [Nout][K]
+  const float* bias;  // in: per-head gate-logit bias [H] or null
+  void* q;            // in: [B*H][N][64]
+  void* k;
+  void* v;
+  float* gl;          // in: gate logits [B*H][N]
+  void* y;            // out: [M][Nout]
+  int64_t M;          // B * N
+  int64_t N;          // tokens per sequence
+  int K;              // D = H * 64
+  int Nout;           // in: 3D + H; out: D
+  int H;
+};
+hipError_t launch_proj(const ProjArgs& a, bool out, bool is_bf16, hipStream_t st);
+
 // Rows of unit directions a row-split scan workgroup keeps in LDS (bf16 path; 0 on the fp32 path).
 int scan_lds_rows(int C, bool is_bf16);
 hipError_t launch_init(const Dims& m, const Dev& d, double rope_theta, hipStream_t st);

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KvmConfig", "KvmState", "KvmError", "library", "workspace_bytes", "schedule", "prefill_noalloc", "SCHED", "DTYPE",
+    "KvmConfig", "KvmState", "KvmError", "library", "workspace_bytes", "schedule", "prefill_noalloc", "project_in",
+    "project_out", "SCHED", "DTYPE",
     "KVM_OK", "KVM_E_INVALID_ARG", "KVM_E_WORKSPACE", "KVM_E_CAPACITY", "KVM_E_STATE", "KVM_E_HIP",
 ]
 
@@ -90,6 +91,8 @@ def library() -> ctypes.CDLL:
         L.kvm_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp]
         L.kvm_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.kvm_prefill_noalloc.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, vp, vp, i64, vp]
+        L.kvm_project_in.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        L.kvm_project_out.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, i64, vp]
         L.kvm_backward_workspace_bytes.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_size_t)]
         L.kvm_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, ctypes.c_size_t, vp]
         L.kvm_state_read.argtypes = [vp, i64, ctypes.POINTER(_View), vp]
@@ -106,6 +109,7 @@ def library() -> ctypes.CDLL:
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
                      "kvm_prefill_noalloc", "kvm_backward_workspace_bytes", "kvm_prefill_backward",
+                     "kvm_project_in", "kvm_project_out",
                      "kvm_decode_step", "kvm_state_read", "kvm_state_load", "kvm_snapshot_read", "kvm_state_get_info",
                      "kvm_state_reset", "kvm_state_check", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
@@ -205,6 +209,46 @@ def schedule(cfg: KvmConfig, n_chunks: int):
 
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _contig(t, name, dtype, numel, dev):
+    if not isinstance(t, torch.Tensor) or t.device != dev or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name}: contiguous {dtype} tensor on {dev} expected")
+    if t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return t
+
+
+def project_in(cfg: KvmConfig, x, w_in, b_gate=None):
+    """kvm_project_in: x [B, n, D] -> (q, k, v [B*H, n, 64] in cfg.dtype, gate_logits [B*H, n] float32);
+    w_in [3D + H, D] in cfg.dtype, b_gate [H] float32 or None."""
+    n = x.shape[-2]
+    dev = x.device
+    D, H, S = cfg.heads * 64, cfg.heads, cfg.seqs
+    _contig(x, "x", cfg.torch_dtype, cfg.batch * n * D, dev)
+    _contig(w_in, "w_in", cfg.torch_dtype, (3 * D + H) * D, dev)
+    if b_gate is not None:
+        _contig(b_gate, "b_gate", torch.float32, H, dev)
+    q, k, v = (torch.empty(S, n, 64, dtype=cfg.torch_dtype, device=dev) for _ in range(3))
+    gl = torch.empty(S, n, dtype=torch.float32, device=dev)
+    c = cfg.to_c()
+    _check(library().kvm_project_in(ctypes.byref(c), x.data_ptr(), w_in.data_ptr(),
+                                    b_gate.data_ptr() if b_gate is not None else None, q.data_ptr(), k.data_ptr(),
+                                    v.data_ptr(), gl.data_ptr(), n, _stream(dev)))
+    return q, k, v, gl
+
+
+def project_out(cfg: KvmConfig, o, w_out):
+    """kvm_project_out: o [B*H, n, 64] -> y [B, n, D] with w_out [D, D] (cfg.dtype)."""
+    n = o.shape[-2]
+    dev = o.device
+    D = cfg.heads * 64
+    _contig(o, "o", cfg.torch_dtype, cfg.seqs * n * 64, dev)
+    _contig(w_out, "w_out", cfg.torch_dtype, D * D, dev)
+    y = torch.empty(cfg.batch, n, D, dtype=cfg.torch_dtype, device=dev)
+    c = cfg.to_c()
+    _check(library().kvm_project_out(ctypes.byref(c), o.data_ptr(), w_out.data_ptr(), y.data_ptr(), n, _stream(dev)))
+    return y
 
 
 def prefill_noalloc(cfg: KvmConfig, q, k, v, gate_logits, out) -> torch.Tensor:

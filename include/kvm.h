@@ -248,6 +248,29 @@ kvm_status kvm_prefill_backward(kvm_state* st, const void* q, const void* k, con
                                 const void* d_out, float* d_q, float* d_k, float* d_v, float* d_gate,
                                 int64_t n_tokens, void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* The projections of the block around the layer ([KVM abstract]: KVM is an
+ * attention layer, fed queries, keys and values projected from the tokens and
+ * projected back; [KVM summary, Core mechanisms 2]: the merge gate is a
+ * data-dependent scalar, one more projection of the same input, one logit per
+ * head).  Linear maps, weights stored [out features, in features] in
+ * cfg.dtype, D = heads * 64; features of q, k, v are head-major (feature
+ * h*64 + d is dimension d of head h) and head h of batch b is sequence b*H + h.
+ *
+ * kvm_project_in: x [B, n_tokens, D] -> q, k, v [B*H, n_tokens, 64] (cfg.dtype)
+ * and gate_logits [B*H, n_tokens] f32, with w_in [3D + H, D] (rows: q
+ * features, k features, v features, one gate row per head) and an optional
+ * per-head gate bias b_gate [H] f32 (NULL = 0).  Outputs are the inputs
+ * kvm_prefill takes.  fp32 accumulation.
+ * Errors: KVM_E_INVALID_ARG (config, NULL or misaligned pointers, n_tokens < 0), KVM_E_HIP. */
+kvm_status kvm_project_in(const kvm_config* cfg, const void* x, const void* w_in, const float* b_gate, void* q,
+                          void* k, void* v, float* gate_logits, int64_t n_tokens, void* stream);
+
+/* kvm_project_out: the layer output o [B*H, n_tokens, 64] -> y [B, n_tokens, D]
+ * = concat_h(o_h) . w_out^T with w_out [D, D], cfg.dtype.  fp32 accumulation.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_HIP. */
+kvm_status kvm_project_out(const kvm_config* cfg, const void* o, const void* w_out, void* y, int64_t n_tokens,
+                           void* stream);
+
 /* Export the state ([KVM lay summary, "smart merge"]: raw sums and counts,
  * divided only at read; [KVM summary, Core mechanisms 2]: the read form).
  *   chunk == -1: the current state.  Every field of `dst` may be requested;

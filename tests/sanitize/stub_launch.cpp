@@ -27,5 +27,6 @@ hipError_t launch_snapshot_gather(const Dims&, const Dev&, int, int64_t, int, vo
   return hipSuccess;
 }
 hipError_t launch_state_load(const Dims&, const Dev&, int, int64_t, hipStream_t) { return hipSuccess; }
+hipError_t launch_proj(const ProjArgs&, bool, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_backward(const Dims&, const Dev&, const BwdIn&, const Bwd&, int, hipStream_t) { return hipSuccess; }
 }  // namespace kvm
