@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <new>
 #include <string>
@@ -30,6 +31,11 @@ struct kvm_state {
   std::vector<int32_t> sched;      // 4 ints per absorbable chunk: sinks, appends, rows_before, idx_off
   int64_t pos = 0;
   int64_t absorbed = 0;
+  // per-sequence positions and absorbed chunks; pos/absorbed above hold while
+  // every sequence is at the same position (per_seq false)
+  std::vector<int64_t> spos, sabs;
+  bool per_seq = false;
+  std::vector<int64_t> seqtab;     // host copy of the per-sequence launch table
   bool poisoned = false;
   // profiling: event pairs recorded around kernel phases
   int profiling = 0;     // mask of phases (bit = 1 << Phase) that record events
@@ -164,7 +170,7 @@ struct Plan {
   std::vector<int32_t> sched;  // 4 per chunk
   // byte offsets
   size_t key_sum, val_sum, count, rho, unit, kread, vread, pkey, pval, prho, pcount, pnorm, idx, krot, tslot, tkind, ring_k,
-      ring_v, ring_l, rope_cos, rope_sin, sch, nver, xbuf, xerr, total;
+      ring_v, ring_l, rope_cos, rope_sin, sch, nver, xbuf, xerr, seq, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -256,6 +262,7 @@ kvm_status plan(const kvm_config* c, Plan& p, bool keep_sched = true) {
   p.nver = take(BH * 4);
   p.xbuf = take(BH * 2 * (size_t)m.P * m.C * 8);
   p.xerr = take(4);
+  p.seq = take(BH * kvm::kSeqFields * 8);
   p.total = off;
   return KVM_OK;
 }
@@ -287,6 +294,7 @@ void carve(const Plan& p, char* b, kvm::Dev& d) {
   d.nver = reinterpret_cast<int*>(b + p.nver);
   d.xbuf = reinterpret_cast<uint2*>(b + p.xbuf);
   d.xerr = reinterpret_cast<int*>(b + p.xerr);
+  d.seq = reinterpret_cast<int64_t*>(b + p.seq);
 }
 
 kvm_status hip_fail(kvm_state* st, hipError_t e, const char* what) {
@@ -369,6 +377,28 @@ int64_t absorbed_at(const kvm::Dims& m, int64_t pos) {
   return a > 0 ? a : 0;
 }
 
+// Every sequence at the state's one position (after a call that moves them together).
+void set_uniform(kvm_state* st) {
+  st->spos.assign((size_t)st->m.BH, st->pos);
+  st->sabs.assign((size_t)st->m.BH, st->absorbed);
+  st->per_seq = false;
+}
+
+// After a per-sequence call: back to the one-position form when every sequence agrees.
+void sync_uniform(kvm_state* st) {
+  const bool same = std::all_of(st->spos.begin(), st->spos.end(), [&](int64_t x) { return x == st->spos[0]; });
+  st->per_seq = !same;
+  if (same) {
+    st->pos = st->spos[0];
+    st->absorbed = st->sabs[0];
+  }
+}
+
+// Upload the per-sequence launch table (small: kSeqFields int64 per sequence).
+hipError_t upload_seq(kvm_state* st, hipStream_t hs) {
+  return hipMemcpyAsync(st->d.seq, st->seqtab.data(), st->seqtab.size() * 8, hipMemcpyHostToDevice, hs);
+}
+
 // Queue the clearing of the counters and exchange buffers the kernels rely on
 // (state creation, reset, load).
 hipError_t clear_counters(kvm_state* st, bool trace_too, hipStream_t hs) {
@@ -435,6 +465,8 @@ kvm_status kvm_state_create(const kvm_config* cfg, void* d_workspace, size_t wor
     st->m = p.m;
     st->sched = std::move(p.sched);
     carve(p, reinterpret_cast<char*>(d_workspace), st->d);
+    set_uniform(st);
+    st->seqtab.assign((size_t)st->m.BH * kvm::kSeqFields, 0);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = clear_counters(st, true, hs);
     if (e == hipSuccess && !st->sched.empty())
@@ -466,6 +498,7 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
     return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
   const kvm::Dims& m = st->m;
+  if (st->per_seq) return fail(KVM_E_STATE, "sequences are at different positions: use kvm_prefill_ragged");
   if (st->pos % m.C != 0) return fail(KVM_E_STATE, "prefill must start at a multiple of chunk");
   if (st->pos + n_tokens > m.max_tokens) return fail(KVM_E_CAPACITY, "prefill would pass max_tokens");
   const size_t bytes = (size_t)m.BH * (size_t)n_tokens * 64 * (m.bf16 ? 2 : 4);
@@ -545,6 +578,7 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
   if (err != hipSuccess) return hip_fail(st, err, "ring launch");
   st->pos = e;
   st->absorbed = a1;
+  set_uniform(st);
   return KVM_OK;
 }
 
@@ -599,6 +633,7 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
     return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
   const kvm::Dims& m = st->m;
+  if (st->per_seq) return fail(KVM_E_STATE, "sequences are at different positions: use kvm_decode_step_ragged");
   const int64_t t = st->pos;
   if (t + 1 > m.max_tokens) return fail(KVM_E_CAPACITY, "decode would pass max_tokens");
   const size_t bytes = (size_t)m.BH * 64 * (m.bf16 ? 2 : 4);
@@ -621,6 +656,7 @@ kvm_status kvm_decode_step(kvm_state* st, const void* q, const void* k, const vo
   if (err != hipSuccess) return hip_fail(st, err, "decode launch");
   st->pos = t + 1;
   st->absorbed = absorbed;
+  set_uniform(st);
   return KVM_OK;
 }
 
@@ -670,6 +706,7 @@ kvm_status kvm_prefill_backward(kvm_state* st, const void* q, const void* k, con
   const kvm::Dims& m = st->m;
   if (!m.trace) return fail(KVM_E_INVALID_ARG, "the backward reads the forward's decisions: create the state with KVM_FLAG_TRACE");
   if (n_tokens <= 0) return fail(KVM_E_INVALID_ARG, "n_tokens must be > 0");
+  if (st->per_seq) return fail(KVM_E_STATE, "sequences are at different positions");
   if (n_tokens != st->pos) return fail(KVM_E_STATE, "the state's position must equal n_tokens");
   if (!q || !k || !v || !gate_logits || !d_out || !d_q || !d_k || !d_v || !d_gate || !d_workspace)
     return fail(KVM_E_INVALID_ARG, "NULL pointer");
@@ -758,8 +795,9 @@ kvm_status kvm_state_read(const kvm_state* st, int64_t chunk, kvm_state_view* ds
   const kvm::Dims& m = st->m;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const size_t BH = (size_t)m.BH, S = (size_t)m.S_cap, es = m.bf16 ? 2 : 4;
-  if (chunk < -1 || chunk >= st->absorbed)
-    return fail(KVM_E_INVALID_ARG, "chunk must be -1 (current state) or an absorbed chunk");
+  const int64_t min_abs = *std::min_element(st->sabs.begin(), st->sabs.end());
+  if (chunk < -1 || chunk >= min_abs)
+    return fail(KVM_E_INVALID_ARG, "chunk must be -1 (current state) or a chunk every sequence has absorbed");
   if (chunk >= 0) {
     // a past snapshot: read-form row versions only
     if (dst->key_sum || dst->val_sum || dst->ring_k || dst->ring_v || dst->ring_l || dst->trace_slot ||
@@ -799,11 +837,9 @@ kvm_status kvm_state_read(const kvm_state* st, int64_t chunk, kvm_state_view* ds
     hipError_t e = hipMemcpyAsync(c.to, c.from, c.bytes, hipMemcpyDefault, hs);
     if (e != hipSuccess) return hip_fail(const_cast<kvm_state*>(st), e, "state copy");
   }
-  if (dst->n_rows) {
-    const int32_t r = rows_after(st, st->absorbed - 1);
-    for (size_t s = 0; s < BH; ++s) dst->n_rows[s] = r;  // host memory: the row count is host-side
-  }
-  dst->position = st->pos;
+  if (dst->n_rows)   // host memory: the row count is host-side
+    for (size_t s = 0; s < BH; ++s) dst->n_rows[s] = rows_after(st, st->sabs[s] - 1);
+  dst->position = st->per_seq ? -1 : st->pos;
   return KVM_OK;
 }
 
@@ -857,6 +893,7 @@ kvm_status kvm_state_load(kvm_state* st, const kvm_state_view* src, void* stream
   if (e != hipSuccess) return hip_fail(st, e, "state load");
   st->pos = pos;
   st->absorbed = absorbed;
+  set_uniform(st);
   return KVM_OK;
 }
 
@@ -864,7 +901,8 @@ kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, voi
                              void* stream) {
   if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
   if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
-  if (j < 0 || j >= st->absorbed) return fail(KVM_E_INVALID_ARG, "chunk j has not been absorbed");
+  if (j < 0 || j >= *std::min_element(st->sabs.begin(), st->sabs.end()))
+    return fail(KVM_E_INVALID_ARG, "chunk j has not been absorbed by every sequence");
   const int rows = rows_after(st, j);
   const int64_t ioff = st->sched[(size_t)j * 4 + 3];
   hipError_t e = kvm::launch_snapshot_gather(st->m, st->d, rows, ioff, rows, key_read, val_read, rho_read, nullptr,
@@ -873,11 +911,149 @@ kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, voi
   return KVM_OK;
 }
 
+kvm_status kvm_state_positions(const kvm_state* st, int64_t* positions) {
+  if (!st || !positions) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  for (size_t s = 0; s < st->spos.size(); ++s) positions[s] = st->spos[s];
+  return KVM_OK;
+}
+
+kvm_status kvm_state_reset_sequence(kvm_state* st, int32_t seq, void* stream) {
+  if (!st) return fail(KVM_E_INVALID_ARG, "state is NULL");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  if (seq < 0 || seq >= st->m.BH) return fail(KVM_E_INVALID_ARG, "sequence index out of range");
+  hipError_t e = kvm::launch_seq_reset(st->m, st->d, seq, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(st, e, "sequence reset");
+  st->spos[(size_t)seq] = 0;
+  st->sabs[(size_t)seq] = 0;
+  sync_uniform(st);
+  return KVM_OK;
+}
+
+kvm_status kvm_prefill_ragged(kvm_state* st, const int64_t* n_tokens, const void* q, const void* k, const void* v,
+                              const float* gate_logits, void* out, int64_t n_max, void* stream) {
+  if (!st || !n_tokens) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  if (n_max < 0) return fail(KVM_E_INVALID_ARG, "n_max < 0");
+  const kvm::Dims& m = st->m;
+  const size_t BH = (size_t)m.BH;
+  // per sequence: its own range of positions, chunks to absorb and query chunks
+  int64_t nq_max = 0, span_max = 0, any_abs = 0;
+  int s_max = 0;
+  std::vector<int64_t>& tab = st->seqtab;
+  std::fill(tab.begin(), tab.end(), 0);
+  for (size_t s = 0; s < BH; ++s) {
+    const int64_t n = n_tokens[s], p0 = st->spos[s];
+    if (n < 0 || n > n_max) return fail(KVM_E_INVALID_ARG, "n_tokens[s] must be in [0, n_max]");
+    int64_t* r = &tab[s * kvm::kSeqFields];
+    r[kvm::kSeqP0] = p0;
+    r[kvm::kSeqJb] = r[kvm::kSeqJe] = st->sabs[s];
+    if (n == 0) continue;
+    if (p0 % m.C != 0) return fail(KVM_E_STATE, "sequence " + std::to_string(s) + ": prefill must start at a multiple of chunk");
+    const int64_t e = p0 + n;
+    if (e > m.max_tokens) return fail(KVM_E_CAPACITY, "sequence " + std::to_string(s) + ": prefill would pass max_tokens");
+    const int64_t c_first = p0 / m.C, c_last = (e - 1) / m.C;
+    int64_t need = c_last - m.W / m.C;
+    if (need < 0) need = 0;
+    const int64_t a1 = std::max(need, st->sabs[s]);
+    if (a1 > m.J_cap) return fail(KVM_E_CAPACITY, "absorption would pass the workspace's chunk capacity");
+    r[kvm::kSeqJe] = a1;
+    r[kvm::kSeqCb] = c_first;
+    r[kvm::kSeqNq] = c_last - c_first + 1;
+    r[kvm::kSeqEnd] = e;
+    r[kvm::kSeqN] = n;
+    r[kvm::kSeqFrom] = std::max(e - m.R, p0);
+    r[kvm::kSeqTo] = e;
+    nq_max = std::max(nq_max, c_last - c_first + 1);
+    span_max = std::max(span_max, e - r[kvm::kSeqFrom]);
+    any_abs |= a1 > st->sabs[s];
+    s_max = std::max(s_max, rows_after(st, c_last - m.W / m.C - 1));
+  }
+  if (nq_max == 0) return KVM_OK;
+  if (!q || !k || !v || !gate_logits || !out) return fail(KVM_E_INVALID_ARG, "NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
+  const size_t bytes = BH * (size_t)n_max * 64 * (m.bf16 ? 2 : 4);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return fail(KVM_E_INVALID_ARG, "out aliases an input");
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  kvm::Src src{q, k, v, gate_logits, 0, n_max, st->d.seq};
+  hipError_t err = upload_seq(st, hs);
+  if (err == hipSuccess && st->d.krot) err = timed(st, kPrep, hs, [&] { return kvm::launch_rope_keys(m, st->d, src, hs); });
+  if (err == hipSuccess && any_abs)
+    err = timed(st, kScan, hs, [&] { return kvm::launch_scan(m, st->d, src, 0, 1, hs); });
+  if (err == hipSuccess)
+    err = timed(st, kAttn, hs, [&] { return kvm::launch_attn(m, st->d, src, 0, (int)nq_max, 0, out, s_max, hs); });
+  if (err == hipSuccess)
+    err = timed(st, kRing, hs, [&] { return kvm::launch_ring_fill(m, st->d, src, 0, span_max, hs); });
+  if (err != hipSuccess) return hip_fail(st, err, "ragged prefill launch");
+  for (size_t s = 0; s < BH; ++s) {
+    const int64_t* r = &tab[s * kvm::kSeqFields];
+    if (n_tokens[s] == 0) continue;
+    st->spos[s] = r[kvm::kSeqEnd];
+    st->sabs[s] = r[kvm::kSeqJe];
+  }
+  sync_uniform(st);
+  return KVM_OK;
+}
+
+kvm_status kvm_decode_step_ragged(kvm_state* st, const uint8_t* active, const void* q, const void* k, const void* v,
+                                  const float* gate_logits, void* out, void* stream) {
+  if (!st || !active) return fail(KVM_E_INVALID_ARG, "NULL argument");
+  if (st->poisoned) return fail(KVM_E_STATE, "state is poisoned by an earlier HIP failure");
+  if (!q || !k || !v || !gate_logits || !out) return fail(KVM_E_INVALID_ARG, "NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(gate_logits, 4))
+    return fail(KVM_E_INVALID_ARG, "tensors must be 16-byte aligned (gate logits 4-byte)");
+  const kvm::Dims& m = st->m;
+  const size_t BH = (size_t)m.BH;
+  const size_t bytes = BH * 64 * (m.bf16 ? 2 : 4);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return fail(KVM_E_INVALID_ARG, "out aliases an input");
+  std::vector<int64_t>& tab = st->seqtab;
+  std::fill(tab.begin(), tab.end(), 0);
+  bool any = false, any_abs = false;
+  for (size_t s = 0; s < BH; ++s) {
+    int64_t* r = &tab[s * kvm::kSeqFields];
+    r[kvm::kSeqP0] = INT64_MAX;    // every token an absorption reads comes from the ring
+    if (!active[s]) continue;
+    const int64_t t = st->spos[s];
+    if (t + 1 > m.max_tokens) return fail(KVM_E_CAPACITY, "sequence " + std::to_string(s) + ": decode would pass max_tokens");
+    r[kvm::kSeqActive] = 1;
+    r[kvm::kSeqPos] = t;
+    any = true;
+    if (t % m.C == 0 && t >= m.W + m.C) {
+      const int64_t j = (t - m.W - m.C) / m.C;
+      if (j != st->sabs[s] || j >= m.J_cap) return fail(KVM_E_STATE, "absorbed chunk count out of step with position");
+      r[kvm::kSeqJb] = j;
+      r[kvm::kSeqJe] = j + 1;
+      any_abs = true;
+    }
+  }
+  if (!any) return KVM_OK;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  kvm::Src src{nullptr, nullptr, nullptr, nullptr, 0, 0, st->d.seq};
+  hipError_t err = upload_seq(st, hs);
+  if (err == hipSuccess && any_abs)
+    err = timed(st, kDecAbsorb, hs, [&] { return kvm::launch_scan(m, st->d, src, 0, 1, hs); });
+  if (err == hipSuccess)
+    err = timed(st, kDecAttn, hs,
+                [&] { return kvm::launch_decode(m, st->d, q, k, v, gate_logits, 0, 0, out, hs, st->d.seq); });
+  if (err != hipSuccess) return hip_fail(st, err, "ragged decode launch");
+  for (size_t s = 0; s < BH; ++s) {
+    if (!active[s]) continue;
+    const int64_t* r = &tab[s * kvm::kSeqFields];
+    if (r[kvm::kSeqJe] > r[kvm::kSeqJb]) st->sabs[s] = r[kvm::kSeqJe];
+    st->spos[s] += 1;
+  }
+  sync_uniform(st);
+  return KVM_OK;
+}
+
 kvm_status kvm_state_get_info(const kvm_state* st, kvm_state_info* info) {
   if (!st || !info) return fail(KVM_E_INVALID_ARG, "NULL argument");
-  info->position = st->pos;
-  info->absorbed_chunks = st->absorbed;
-  info->rows = rows_after(st, st->absorbed - 1);
+  info->position = st->per_seq ? -1 : st->pos;
+  info->absorbed_chunks = st->per_seq ? -1 : st->absorbed;
+  info->rows = st->per_seq ? -1 : rows_after(st, st->absorbed - 1);
+  info->per_sequence = st->per_seq ? 1 : 0;
   info->max_rows = st->m.S_cap;
   info->max_chunks = st->m.J_cap;
   info->poisoned = st->poisoned ? 1 : 0;
@@ -906,6 +1082,7 @@ kvm_status kvm_state_reset(kvm_state* st, void* stream) {
   if (e != hipSuccess) return hip_fail(st, e, "state reset");
   st->pos = 0;
   st->absorbed = 0;
+  set_uniform(st);
   st->poisoned = false;
   return KVM_OK;
 }

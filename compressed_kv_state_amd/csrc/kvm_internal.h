@@ -68,10 +68,30 @@ struct Dev {
   int* nver;         // [BH] versions used
   uint2* xbuf;       // [BH][2][P][C] scan exchange: each workgroup's best per token (key bits, row | step tag)
   int* xerr;         // [1] set when a scan workgroup gave up waiting at an exchange
+  int64_t* seq;      // [BH][kSeqFields] per-sequence launch parameters (sequences at their own positions)
+};
+
+// Per-sequence launch parameters (sequences at their own positions): a
+// [BH][kSeqFields] int64 table; a kernel given one takes its sequence's entries
+// in place of the launch-wide arguments.
+enum SeqField {
+  kSeqP0 = 0,   // first position of the call's inputs for this sequence
+  kSeqJb,       // scan: chunks [jb, je) to absorb
+  kSeqJe,
+  kSeqCb,       // attention: first query chunk, number of query chunks, end position
+  kSeqNq,
+  kSeqEnd,
+  kSeqN,        // tokens of the call for this sequence (prefill; rows past it are padding)
+  kSeqFrom,     // ring refresh: positions [from, to)
+  kSeqTo,
+  kSeqPos,      // decode: the sequence's position
+  kSeqActive,   // decode: 1 if the sequence takes a token in this step
+  kSeqFields = 16
 };
 
 // Token source for a launch: positions >= p0 come from the call's inputs
 // ([BH][n_call][64] rows, gate [BH][n_call]); positions < p0 from the ring.
+// With `seq` set, p0 (and the other per-sequence values) come from the table.
 struct Src {
   const void* q;
   const void* k;
@@ -79,6 +99,7 @@ struct Src {
   const float* l;
   int64_t p0;
   int64_t n_call;
+  const int64_t* seq = nullptr;
 };
 
 // The data-independent size schedule as the device computes it (integer schedules only:
@@ -162,10 +183,13 @@ hipError_t launch_attn(const Dims& m, const Dev& d, const Src& src, int64_t c_be
 hipError_t launch_rope_keys(const Dims& m, const Dev& d, const Src& src, hipStream_t st);
 // Copy positions [from, to) of the call inputs into the ring (keys rotated).
 hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t from, int64_t to, hipStream_t st);
+// Zero sequence s's version counter and exchange records, and (with the trace) mark its positions
+// not absorbed: one sequence returned to an empty state.
+hipError_t launch_seq_reset(const Dims& m, const Dev& d, int s, hipStream_t st);
 // Decode step at position t: write token t (rotated key, value, gate logit) into ring
 // slot t % R, then attend over `rows` state rows and the window; out [BH][64].
 hipError_t launch_decode(const Dims& m, const Dev& d, const void* q, const void* k, const void* v, const float* l,
-                         int64_t t, int rows, void* out, hipStream_t st);
+                         int64_t t, int rows, void* out, hipStream_t st, const int64_t* seq = nullptr);
 // Gather the read form of snapshot j (rows_j rows, version list at idx_off) into
 // key [BH][stride][32] RT, value rho * u [BH][stride][64] T, radius and count [BH][stride]
 // (rows [0, rows) of each sequence; any output may be null; stride >= rows).

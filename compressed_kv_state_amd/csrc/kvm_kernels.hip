@@ -694,6 +694,12 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     s = blockIdx.x;
     p = 0;
   }
+  if (src.seq) {   // this sequence's own chunk range and input position
+    const int64_t* sr = src.seq + (size_t)s * kSeqFields;
+    src.p0 = sr[kSeqP0];
+    j_begin = (int)sr[kSeqJb];
+    j_end = (int)sr[kSeqJe];
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int LB = m.unprot ? 0 : m.ns;   // first row of the tile partition
   auto own = [&](int r) {
@@ -1338,6 +1344,13 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(Dims m, Dev d, Src src, i
       cl = n_q - 1 - b / m.BH;
     }
   }
+  if (src.seq) {   // this sequence's own query chunks, input position and end
+    const int64_t* sr = src.seq + (size_t)s * kSeqFields;
+    if (cl >= (int)sr[kSeqNq]) return;
+    src.p0 = sr[kSeqP0];
+    c_begin = sr[kSeqCb];
+    end_pos = sr[kSeqEnd];
+  }
   const int64_t c = c_begin + cl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
   const int64_t cpos = c * C;
@@ -1589,6 +1602,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Dims m, Dev d, Sr
       s = b % m.BH;
       cl = n_q - 1 - b / m.BH;
     }
+  }
+  if (src.seq) {   // this sequence's own query chunks, input position and end
+    const int64_t* sr = src.seq + (size_t)s * kSeqFields;
+    if (cl >= (int)sr[kSeqNq]) return;
+    src.p0 = sr[kSeqP0];
+    c_begin = sr[kSeqCb];
+    end_pos = sr[kSeqEnd];
   }
   const int64_t c = c_begin + cl;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
@@ -1959,6 +1979,13 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
       cl = n_q - 1 - b / m.BH;
     }
   }
+  if (src.seq) {   // this sequence's own query chunks, input position and end
+    const int64_t* sr = src.seq + (size_t)s * kSeqFields;
+    if (cl >= (int)sr[kSeqNq]) return;
+    src.p0 = sr[kSeqP0];
+    c_begin = sr[kSeqCb];
+    end_pos = sr[kSeqEnd];
+  }
   const int64_t c = c_begin + cl;
   const int tid = threadIdx.x, lane = tid & 63, jl = lane & 31, h = lane >> 5;
   // wave index, made uniform for the compiler: the LDS targets of the
@@ -2293,7 +2320,13 @@ __global__ void rope_keys_kernel(Dims m, Dev d, Src src) {
     const int hh = (int)(i & 1);
     const int64_t tok = i >> 1;
     const int s = (int)(tok / src.n_call);
-    const int64_t pos = src.p0 + tok % src.n_call;
+    int64_t p0 = src.p0;
+    if (src.seq) {
+      const int64_t* sr = src.seq + (size_t)s * kSeqFields;
+      if (tok % src.n_call >= sr[kSeqN]) continue;   // padding past this sequence's tokens
+      p0 = sr[kSeqP0];
+    }
+    const int64_t pos = p0 + tok % src.n_call;
     const bf16* kr = reinterpret_cast<const bf16*>(src.k) + (size_t)tok * 64;
     alignas(16) bf16 x[8], y[8];
     copy16(x, kr + 8 * hh);
@@ -2322,6 +2355,12 @@ template <typename T>
 __global__ __launch_bounds__(256) void ring_fill_kernel(Dims m, Dev d, Src src, int64_t from, int64_t to) {
   // four tokens per workgroup, one lane per dimension
   const int s = blockIdx.y;
+  if (src.seq) {
+    const int64_t* sr = src.seq + (size_t)s * kSeqFields;
+    src.p0 = sr[kSeqP0];
+    from = sr[kSeqFrom];
+    to = sr[kSeqTo];
+  }
   const int64_t pos = from + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= to) return;
   const int dd = threadIdx.x & 63;
@@ -2403,7 +2442,7 @@ __device__ __forceinline__ float dec_group_sum(float x) {
 template <typename T>
 __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, const T* q, const T* kin, const T* vin,
                                                             const float* lin, T* out, int64_t t, int S,
-                                                            int64_t lo) {
+                                                            int64_t lo, const int64_t* seq) {
   using RT = typename Rd<T>::type;
   constexpr int NT = 64 * kDecWaves;
   constexpr int KE = 16 / (int)sizeof(RT);   // state-key dims per lane (of 32)
@@ -2416,6 +2455,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
   __shared__ float red[kDecWaves];
   __shared__ float red_o[kDecWaves][64];
   const int s = blockIdx.x;
+  if (seq) {   // this sequence's own position; its window and state follow from it
+    const int64_t* sr = seq + (size_t)s * kSeqFields;
+    if (!sr[kSeqActive]) return;
+    t = sr[kSeqPos];
+    const int64_t c = t / m.C;
+    lo = c * m.C - m.W > 0 ? c * m.C - m.W : 0;
+    const int64_t absorbed = c - m.W / m.C > 0 ? c - m.W / m.C : 0;   // chunks absorbed once t is consumed
+    S = 0;
+    if (absorbed > 0) {
+      const int4 sc = d.sched[absorbed - 1];
+      S = sc.x + sc.y + sc.z;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float sl2 = m.scale * kLog2e;
   if (tid < 64) {
@@ -2700,6 +2752,22 @@ __global__ __launch_bounds__(256) void state_load_kernel(Dims m, Dev d, int rows
   if (threadIdx.x == 0) d.nver[s] = rows;
 }
 
+// One sequence back to an empty state: its version counter and scan exchange
+// records (tag 0) cleared, its trace marked "not absorbed".
+__global__ void seq_reset_kernel(Dims m, Dev d, int s) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)gridDim.x * blockDim.x;
+  const int64_t xw = (int64_t)2 * m.P * m.C;
+  uint2* xb = d.xbuf + (size_t)s * xw;
+  for (int64_t k = i; k < xw; k += n) xb[k] = make_uint2(0u, 0u);
+  if (m.trace)
+    for (int64_t k = i; k < m.max_tokens; k += n) {
+      d.tslot[(size_t)s * m.max_tokens + k] = -1;
+      d.tkind[(size_t)s * m.max_tokens + k] = 0xFF;
+    }
+  if (i == 0) d.nver[s] = 0;
+}
+
 // Schedule table of a workspace in the static scratch (one thread: at most a few
 // thousand chunks), with the host's rules: sinks first, then
 // m_j = min(max(capacity((j + 1) C) - rows, 0), candidates), capacity =
@@ -2805,6 +2873,11 @@ hipError_t launch_init(const Dims& m, const Dev& d, double theta, hipStream_t st
   return hipGetLastError();
 }
 
+hipError_t launch_seq_reset(const Dims& m, const Dev& d, int s, hipStream_t st) {
+  seq_reset_kernel<<<64, 256, 0, st>>>(m, d, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_noalloc_init(const Dims& m, const Dev& d, const SchedParams& sp, double theta, hipStream_t st) {
   hipError_t e = launch_init(m, d, theta, st);
   if (e != hipSuccess) return e;
@@ -2877,17 +2950,17 @@ hipError_t launch_ring_fill(const Dims& m, const Dev& d, const Src& src, int64_t
 }
 
 hipError_t launch_decode(const Dims& m, const Dev& d, const void* q, const void* k, const void* v, const float* l,
-                         int64_t t, int rows, void* out, hipStream_t st) {
+                         int64_t t, int rows, void* out, hipStream_t st, const int64_t* seq) {
   const int64_t c = t / m.C;
   const int64_t lo = c * m.C - m.W > 0 ? c * m.C - m.W : 0;
   if (m.bf16)
     dec_kernel<bf16><<<m.BH, 64 * kDecWaves, 0, st>>>(m, d, reinterpret_cast<const bf16*>(q), reinterpret_cast<const bf16*>(k),
                                                      reinterpret_cast<const bf16*>(v), l, reinterpret_cast<bf16*>(out), t,
-                                                     rows, lo);
+                                                     rows, lo, seq);
   else
     dec_kernel<float><<<m.BH, 64 * kDecWaves, 0, st>>>(m, d, reinterpret_cast<const float*>(q), reinterpret_cast<const float*>(k),
                                                       reinterpret_cast<const float*>(v), l, reinterpret_cast<float*>(out), t,
-                                                      rows, lo);
+                                                      rows, lo, seq);
   return hipGetLastError();
 }
 

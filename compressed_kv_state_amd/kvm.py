@@ -61,7 +61,7 @@ class _View(ctypes.Structure):
 class _Info(ctypes.Structure):
     _fields_ = [("position", ctypes.c_int64), ("absorbed_chunks", ctypes.c_int64), ("rows", ctypes.c_int32),
                 ("max_rows", ctypes.c_int32), ("max_chunks", ctypes.c_int64), ("poisoned", ctypes.c_int32),
-                ("scan_groups", ctypes.c_int32)]
+                ("scan_groups", ctypes.c_int32), ("per_sequence", ctypes.c_int32)]
 
 
 class _Prof(ctypes.Structure):
@@ -91,6 +91,10 @@ def library() -> ctypes.CDLL:
         L.kvm_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp]
         L.kvm_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         L.kvm_prefill_noalloc.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, vp, vp, i64, vp]
+        L.kvm_prefill_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp]
+        L.kvm_decode_step_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.kvm_state_reset_sequence.argtypes = [vp, ctypes.c_int32, vp]
+        L.kvm_state_positions.argtypes = [vp, vp]
         L.kvm_project_in.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, vp, vp, vp, vp, i64, vp]
         L.kvm_project_out.argtypes = [ctypes.POINTER(_Config), vp, vp, vp, i64, vp]
         L.kvm_backward_workspace_bytes.argtypes = [ctypes.POINTER(_Config), ctypes.POINTER(ctypes.c_size_t)]
@@ -109,7 +113,8 @@ def library() -> ctypes.CDLL:
         L.kvm_last_error.restype = ctypes.c_char_p
         for name in ("kvm_workspace_bytes", "kvm_schedule", "kvm_state_create", "kvm_state_destroy", "kvm_prefill",
                      "kvm_prefill_noalloc", "kvm_backward_workspace_bytes", "kvm_prefill_backward",
-                     "kvm_project_in", "kvm_project_out",
+                     "kvm_project_in", "kvm_project_out", "kvm_prefill_ragged", "kvm_decode_step_ragged",
+                     "kvm_state_reset_sequence", "kvm_state_positions",
                      "kvm_decode_step", "kvm_state_read", "kvm_state_load", "kvm_snapshot_read", "kvm_state_get_info",
                      "kvm_state_reset", "kvm_state_check", "kvm_profile_enable", "kvm_profile_read"):
             getattr(L, name).restype = st
@@ -372,6 +377,47 @@ class KvmState:
                                               dg.data_ptr(), n, workspace.data_ptr(), workspace.numel(),
                                               _stream(self.device)))
         return dq, dk, dv, dg
+
+    def prefill_ragged(self, n_tokens, q, k, v, gate_logits, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """kvm_prefill_ragged: sequence s takes n_tokens[s] tokens at its own position; q, k, v
+        [B*H, n_max, 64], gate_logits [B*H, n_max] (rows past n_tokens[s] are ignored); returns out
+        of the same shape (rows past n_tokens[s] are left as they were)."""
+        n_max = q.shape[-2]
+        q2, k2, v2 = (self._data(t, nm, n_max) for t, nm in ((q, "q"), (k, "k"), (v, "v")))
+        g2 = self._gate(gate_logits, n_max)
+        if out is None:
+            out = torch.zeros_like(q)
+        o2 = self._data(out, "out", n_max)
+        n = torch.as_tensor(list(n_tokens), dtype=torch.int64).contiguous()
+        if n.numel() != self.cfg.seqs:
+            raise ValueError("n_tokens needs one entry per sequence")
+        _check(library().kvm_prefill_ragged(self._h, n.data_ptr(), q2.data_ptr(), k2.data_ptr(), v2.data_ptr(),
+                                            g2.data_ptr(), o2.data_ptr(), n_max, _stream(self.device)))
+        return out
+
+    def decode_step_ragged(self, active, q, k, v, gate_logits, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """kvm_decode_step_ragged: one step for the sequences with active[s]; q, k, v [B*H, 64]."""
+        q2, k2, v2 = (self._data(t, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v")))
+        g2 = self._gate(gate_logits)
+        if out is None:
+            out = torch.zeros_like(q)
+        o2 = self._data(out, "out")
+        a = torch.as_tensor([1 if x else 0 for x in active], dtype=torch.uint8).contiguous()
+        if a.numel() != self.cfg.seqs:
+            raise ValueError("active needs one entry per sequence")
+        _check(library().kvm_decode_step_ragged(self._h, a.data_ptr(), q2.data_ptr(), k2.data_ptr(), v2.data_ptr(),
+                                                g2.data_ptr(), o2.data_ptr(), _stream(self.device)))
+        return out
+
+    def reset_sequence(self, s: int):
+        """kvm_state_reset_sequence: sequence slot s back to position 0, empty (the others continue)."""
+        _check(library().kvm_state_reset_sequence(self._h, int(s), _stream(self.device)))
+
+    def positions(self):
+        """Each sequence's position."""
+        p = torch.zeros(self.cfg.seqs, dtype=torch.int64)
+        _check(library().kvm_state_positions(self._h, p.data_ptr()))
+        return p.tolist()
 
     def reset(self):
         """Back to position 0 with an empty state (queued on the current stream)."""

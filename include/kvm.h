@@ -136,6 +136,8 @@ typedef struct kvm_state_info {
   int64_t max_chunks;     /* chunks max_tokens can absorb */
   int32_t poisoned;       /* 1 after KVM_E_HIP */
   int32_t scan_groups;    /* workgroups that share one sequence's absorption scan (1, 2, 4 or 8) */
+  int32_t per_sequence;   /* 1 while sequences are at different positions (position, absorbed_chunks, rows
+                             are then -1; see kvm_state_positions) */
 } kvm_state_info;
 
 /* Device workspace size for cfg (bytes; the workspace must be 256-byte aligned).
@@ -315,6 +317,44 @@ kvm_status kvm_state_load(kvm_state* st, const kvm_state_view* src, void* stream
  * j must be < absorbed_chunks.  Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
 kvm_status kvm_snapshot_read(const kvm_state* st, int64_t j, void* key_read, void* val_read, float* rho_read,
                              void* stream);
+
+/* Sequences at their own positions (serving: requests of different lengths
+ * that start and finish at different times in one batch; [KVM summary,
+ * Significance]: the state makes per-token decoding over long contexts cheap;
+ * [KVM abstract]: chunk-wise prefill).  The B*H sequences of a state are
+ * independent slots; each keeps its own position, absorbed chunks and rows.
+ * While sequences differ, kvm_prefill, kvm_decode_step, kvm_state_load and
+ * kvm_prefill_backward return KVM_E_STATE; kvm_state_read reads each
+ * sequence's rows (n_rows per sequence, position -1) and past snapshots up to
+ * the fewest any sequence has absorbed.  When the positions meet again the
+ * state is uniform again.
+ *
+ * kvm_prefill_ragged: sequence s takes n_tokens[s] (host array, 0 <= n <= n_max)
+ * tokens at its own position, which must be a multiple of chunk when n > 0;
+ * q, k, v, out are [B*H, n_max, 64] (row t of sequence s is its position
+ * pos_s + t; rows past n_tokens[s] are ignored and not written), gate_logits
+ * [B*H, n_max].  Same results as kvm_prefill of each sequence alone.
+ * Everything runs on `stream` (absorption, then attention).
+ * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_CAPACITY, KVM_E_HIP. */
+kvm_status kvm_prefill_ragged(kvm_state* st, const int64_t* n_tokens, const void* q, const void* k, const void* v,
+                              const float* gate_logits, void* out, int64_t n_max, void* stream);
+
+/* kvm_decode_step_ragged: one decode step for the sequences with active[s] != 0
+ * (host array [B*H]), each at its own position (absorbing the chunk that leaves
+ * its window when it reaches a chunk boundary).  q, k, v, out [B*H, 64];
+ * rows of inactive sequences are ignored and their out rows not written.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_CAPACITY, KVM_E_HIP. */
+kvm_status kvm_decode_step_ragged(kvm_state* st, const uint8_t* active, const void* q, const void* k, const void* v,
+                                  const float* gate_logits, void* out, void* stream);
+
+/* Return one sequence slot to position 0 with an empty state (its version
+ * counter, exchange records and trace are cleared on `stream`), so that the
+ * slot can take a new request while the others continue.
+ * Errors: KVM_E_INVALID_ARG, KVM_E_STATE, KVM_E_HIP. */
+kvm_status kvm_state_reset_sequence(kvm_state* st, int32_t seq, void* stream);
+
+/* Each sequence's position (host array [B*H]).  Never fails on valid pointers. */
+kvm_status kvm_state_positions(const kvm_state* st, int64_t* positions);
 
 /* Host-side facts about the state: position, absorbed chunks and rows of the
  * chunk recurrence ([KVM summary, Core mechanisms 1, 3]).  Never fails on a

@@ -128,6 +128,12 @@ int main() {
   kvm_profile_times pt;
   EXPECT(kvm_profile_read(nullptr, &pt) == KVM_E_INVALID_ARG);
   EXPECT(kvm_state_destroy(nullptr) == KVM_OK);
+  EXPECT(kvm_prefill_ragged(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, nullptr) ==
+         KVM_E_INVALID_ARG);
+  EXPECT(kvm_decode_step_ragged(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr) ==
+         KVM_E_INVALID_ARG);
+  EXPECT(kvm_state_reset_sequence(nullptr, 0, nullptr) == KVM_E_INVALID_ARG);
+  EXPECT(kvm_state_positions(nullptr, nullptr) == KVM_E_INVALID_ARG);
   EXPECT(kvm_backward_workspace_bytes(&c, &bytes) == KVM_OK && bytes > 0);
   EXPECT(kvm_backward_workspace_bytes(nullptr, &bytes) == KVM_E_INVALID_ARG);
   EXPECT(kvm_prefill_backward(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,

@@ -19,8 +19,9 @@ hipError_t launch_attn(const Dims&, const Dev&, const Src&, int64_t, int, int64_
 }
 hipError_t launch_rope_keys(const Dims&, const Dev&, const Src&, hipStream_t) { return hipSuccess; }
 hipError_t launch_ring_fill(const Dims&, const Dev&, const Src&, int64_t, int64_t, hipStream_t) { return hipSuccess; }
+hipError_t launch_seq_reset(const Dims&, const Dev&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode(const Dims&, const Dev&, const void*, const void*, const void*, const float*, int64_t, int,
-                         void*, hipStream_t) {
+                         void*, hipStream_t, const int64_t*) {
   return hipSuccess;
 }
 hipError_t launch_snapshot_gather(const Dims&, const Dev&, int, int64_t, int, void*, void*, float*, int*, hipStream_t) {
