@@ -162,8 +162,6 @@ struct ScanSmem {
   int red_r[RW][C];
   float bE[C];
   int rE[C];
-  float bA[C];
-  int rA[C];
   int flag[C];
   int arow[C];        // row each token merges into or creates
   // row of each merged token (-1 for the others); the update scans the tokens
@@ -508,9 +506,9 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
   for (int tt = 0; tt < CT; ++tt) { bk[tt] = 0u; br[tt] = INT_MAX; }
   const int nown = own_tiles(re > rb ? (re - rb + 31) >> 5 : 0, p, psh);   // own tiles (local k < nown)
   if (wt < nown) {
-    f32x16 base;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) base[r] = kKeyBase;
+    // every accumulator starts at the key base (an inline constant of the MFMA)
+    const f32x16 base = {kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase,
+                         kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase, kKeyBase};
     if constexpr (Is<T>::bf) {
       // lane half h owns dims [16h, 16h+16) of every 32-dim (scaled) key
       bf16x8 bfr[CT][2];
@@ -538,11 +536,26 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
       // two register sets in ping-pong: the loads of tile i+2W are issued right
       // after the MFMAs of tile i read their set, so they overlap tile i+W
       constexpr int WG = G::WG;
-      // LDS-resident tiles first (lowest rows), then the global ones
-      for (int kt = wt; kt < ntl; kt += WG) {
-        bf16x8 b[4];
-        unit_tile_lds(ul, rb, re, LB, p + (kt << psh), psh, b);
-        tile_best(b, kt);
+      // LDS-resident tiles first (lowest rows), then the global ones.  Up to
+      // C = 128 the next tile's fragments are read while this tile's products
+      // run (two register sets; a read past the last tile re-reads the last one).
+      if (C > 128) {   // (registers: one set)
+        for (int kt = wt; kt < ntl; kt += WG) {
+          bf16x8 b[4];
+          unit_tile_lds(ul, rb, re, LB, p + (kt << psh), psh, b);
+          tile_best(b, kt);
+        }
+      } else if (wt < ntl) {
+        bf16x8 b0[4], b1[4];
+        unit_tile_lds(ul, rb, re, LB, p + (wt << psh), psh, b0);
+        for (int kt = wt; kt < ntl; kt += 2 * WG) {
+          const int k1 = kt + WG;
+          unit_tile_lds(ul, rb, re, LB, p + (min(k1, ntl - 1) << psh), psh, b1);
+          tile_best(b0, kt);
+          if (k1 >= ntl) break;
+          unit_tile_lds(ul, rb, re, LB, p + (min(k1 + WG, ntl - 1) << psh), psh, b0);
+          tile_best(b1, k1);
+        }
       }
       if constexpr (!PART) {
         bf16x8(&a0)[4] = pre.a0;
@@ -711,6 +724,24 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if constexpr (PART) return r < LB ? r : LB + own_slot(r, LB, psh);
     else return r;
   };
+  // f(slot, row) for every own row below `rows`, one thread per LDS slot (the
+  // sink rows, then the own tiles' rows in slot order)
+  auto for_own_rows = [&](int rows, auto&& f) {
+    if constexpr (PART) {
+      const int nt = own_tiles(rows > LB ? (rows - LB + 31) >> 5 : 0, p, psh);
+      for (int q = tid; q < LB + 32 * nt; q += kScanThreads) {
+        if (q < LB) {
+          if (p == 0 && q < rows) f(q, q);
+        } else {
+          const int ls = q - LB;
+          const int r = LB + ((p + ((ls >> 5) << psh)) << 5) + (ls & 31);
+          if (r < rows) f(q, r);
+        }
+      }
+    } else {
+      for (int i = tid; i < rows; i += kScanThreads) f(i, i);
+    }
+  };
 
   float* key_sum = d.key_sum + (size_t)s * m.S_cap * 32;
   float* val_sum = d.val_sum + (size_t)s * m.S_cap * 64;
@@ -734,8 +765,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   if (ver_lds && j_begin > 0 && j_begin < j_end) {
     const int r0 = sched[j_begin].z;
     const int* prev = idx + sched[j_begin - 1].w;
-    for (int i = tid; i < r0; i += kScanThreads)
-      if (own(i)) sm.ver_cur[vslot(i)] = prev[i];
+    for_own_rows(r0, [&](int q, int r) { sm.ver_cur[q] = prev[r]; });
   }
 
   // unit directions kept in LDS: the first NL rows of the workgroup's own
@@ -781,28 +811,43 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     const int rows_after = R0 + nc;
     const int64_t P0 = (int64_t)j * C;
 
-    // index list of the previous step (its rows are the R0 rows before this chunk)
-    if (ver_lds && j > j_begin)
-      for (int i = tid; i < R0; i += kScanThreads)
-        if (own(i)) idx[prev_off + i] = sm.ver_cur[vslot(i)];
-
     // ---- 1. the chunk, its key norms and gates are in LDS buffer `cur` (one
     // buffer: store it now); the first unit-direction tiles of the surprise
-    // pass start loading
+    // pass start loading.  The next chunk's loads are issued before the index
+    // list's stores below, so that they do not queue behind them.
     if constexpr (NBUF == 1) {
       chunk_store<T, C>(cr, chc, m.no_gate);
       lds_barrier();
     }
+    if constexpr (kEarly)
+      if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
+    // index list of the previous step (its rows are the R0 rows before this chunk)
+    if (ver_lds && j > j_begin) for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
     // surprise is measured against the non-sink rows that existed before the
     // chunk (every row before the chunk when sinks are unprotected)
     const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
-    if constexpr (kEarly)
-      if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     UnitTiles pre;
     const int ntl = NL > 0 ? lds_tiles(eb, ee, LB, NL, p, psh) : 0;
     if constexpr (Is<T>::bf && !PART) cos_preload<C>(unit, eb, ee, ntl, p, psh, pre);
     const T (*Kc)[32] = chc.k;
     const T (*Vc)[64] = chc.v;
+    // token t's best over the rows before the chunk, from its argmax key v
+    // (row r): back to the dot product (subtract the key base, exact on
+    // (1, 3), and undo the token's power-of-two scaling), and its ranking key
+    // = (surprise to 2^-15, position): smaller = more surprising; sinks never
+    // rank.  (The low 8 bits of the ordered surprise give way to the position,
+    // C <= 256; surprises that close are a near tie.)
+    auto token_key = [&](int t, float v, int r) {
+      int e;
+      (void)key_scale(chc.kn[t], e);
+      const float be = r == INT_MAX ? -kInf : ldexpf(v - kKeyBase, e);
+      sm.bE[t] = be;
+      sm.rE[t] = r;
+      float mu;
+      if (ee > eb) mu = chc.kn[t] > 0.f ? be / chc.kn[t] : 0.f;
+      else mu = -kInf;
+      sm.key[rank_slot<C>(t)] = t < sinks ? ~0u : ((ordered(mu) & ~0xFFu) | (uint32_t)t);
+    };
 
     // ---- 2. surprise against the rows before the chunk: each workgroup's
     // best over its own rows, then (P > 1) the exchange of those bests
@@ -876,10 +921,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           const int orow = __shfl_xor(r, o);
           if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
         }
-        if (xs == 0) {
-          sm.bE[xt] = v;
-          sm.rE[xt] = r;
-        }
+        if (xs == 0) token_key(xt, v, r);
       }
       wait_vmem();   // this workgroup's global writes of the previous step, before the row loads below
       lds_barrier();
@@ -898,23 +940,11 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // would also wait for these).
     if constexpr (!kEarly)
       if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
-    for (int t = tid; t < C; t += kScanThreads) {
-      // back to the dot product: subtract the key base (exact on (1, 3)) and
-      // undo the token's power-of-two scaling
-      {
-        int e;
-        (void)key_scale(chc.kn[t], e);
-        sm.bE[t] = sm.rE[t] == INT_MAX ? -kInf : ldexpf(sm.bE[t] - kKeyBase, e);
-      }
-      float mu;
-      if (ee > eb) mu = chc.kn[t] > 0.f ? sm.bE[t] / chc.kn[t] : 0.f;
-      else mu = -kInf;
-      // key = (surprise to 2^-15, position): smaller = more surprising; sinks
-      // never rank.  (The low 8 bits of the ordered surprise give way to the
-      // position, C <= 256; surprises that close are a near tie.)
-      sm.key[rank_slot<C>(t)] = t < sinks ? ~0u : ((ordered(mu) & ~0xFFu) | (uint32_t)t);
+    // (the row-split kernel's exchange has already done this for every token)
+    if constexpr (!PART) {
+      for (int t = tid; t < C; t += kScanThreads) token_key(t, sm.bE[t], sm.rE[t]);
+      lds_barrier();
     }
-    lds_barrier();
 
     // ---- 3. append the m_j most surprising candidates.  The lane that
     // reports a token's rank also places it: a wave's reporting lanes hold
@@ -954,14 +984,25 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // live keys, in LDS: dot(k_t, k_s) / |k_s|), then the winner-take-all assignment.
     // New row R0 + e was created by token e (a sink, e < sinks) or by the
     // (e - sinks)-th appended token; sink rows are candidates only unprotected.
+    // The lane group of token t (four lanes) also takes the assignment (every
+    // lane computes it; lane 0 publishes it) and, when the target is one of
+    // this workgroup's rows, starts loading that row (sums, count, radius)
+    // into its registers: the group updates the row below if t comes first
+    // on it (the row's values from the previous steps).
     const int e0 = m.unprot ? 0 : sinks;
     const bool new_rows = nc > e0;   // candidates among this step's new rows (uniform)
-    if (new_rows) {
-      for (int t = tid >> 2; t < C; t += kScanThreads / 4) {
-        const int sub = tid & 3;
-        float best = -kInf;
-        int brow = INT_MAX;
-        if (sm.flag[t] == kMerge) {
+    const int fallback = ee > eb ? eb : (R0 + sinks);
+    RowRegs rr[TP];
+#pragma unroll
+    for (int ps = 0; ps < TP; ++ps) {
+      const int t = (tid >> 2) + ps * (kScanThreads / 4);
+      const int sub = tid & 3;
+      if (t >= C) continue;   // the same for the whole lane group
+      const bool merged = sm.flag[t] == kMerge;
+      float best = -kInf;
+      int brow = INT_MAX;
+      if (new_rows) {
+        if (merged) {
           float kt[32];
 #pragma unroll
           for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
@@ -977,48 +1018,32 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
             if (val > best) { best = val; brow = R0 + e; }
           }
         }
-        {
-          float ob = xor_lane<1>(best);
-          int orow = xor_lane<1>(brow);
-          if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
-          ob = xor_lane<2>(best);
-          orow = xor_lane<2>(brow);
-          if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
-        }
-        if (sub == 0) {
-          sm.bA[t] = best;
-          sm.rA[t] = brow;
-        }
+        float ob = xor_lane<1>(best);
+        int orow = xor_lane<1>(brow);
+        if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
+        ob = xor_lane<2>(best);
+        orow = xor_lane<2>(brow);
+        if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
       }
-      lds_barrier();
-    }
-    const int fallback = ee > eb ? eb : (R0 + sinks);
-    for (int t = tid; t < C; t += kScanThreads) {
-      if (sm.flag[t] == kMerge) {
-        const bool eok = sm.rE[t] != INT_MAX, aok = new_rows && sm.rA[t] != INT_MAX;
+      const int mslot = t + 4 * (t / (C / 4));
+      if (merged) {
+        const int rEt = sm.rE[t];
+        const bool eok = rEt != INT_MAX, aok = brow != INT_MAX;
         int a;
-        if (eok && (!aok || sm.bE[t] >= sm.bA[t])) a = sm.rE[t];
-        else if (aok) a = sm.rA[t];
+        if (eok && (!aok || sm.bE[t] >= best)) a = rEt;
+        else if (aok) a = brow;
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
-        sm.arow[t] = a;
-        sm.mrow[t + 4 * (t / (C / 4))] = a;
-      } else {
-        sm.mrow[t + 4 * (t / (C / 4))] = -1;
+        if (sub == 0) {
+          sm.arow[t] = a;
+          sm.mrow[mslot] = a;
+        }
+        if (own(a)) row_load(rr[ps], key_sum, val_sum, count, rho, a, sub);
+      } else if (sub == 0) {
+        sm.mrow[mslot] = -1;
       }
     }
     lds_barrier();
-
-    // start loading each merged token's target row (sums, count, radius) into
-    // the registers of the token's lane group, which updates that row below if
-    // the token comes first on it (the row's values from the previous steps)
-    RowRegs rr[TP];
-#pragma unroll
-    for (int ps = 0; ps < TP; ++ps) {
-      const int t = (tid >> 2) + ps * (kScanThreads / 4);
-      if (t < C && sm.flag[t] == kMerge && own(sm.arow[t]))
-        row_load(rr[ps], key_sum, val_sum, count, rho, sm.arow[t], tid & 3);
-    }
 
     // schedule entry of the next step: a scalar load, issued here so that it is
     // covered by this step's closing barrier rather than stalling an LDS barrier
@@ -1173,9 +1198,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if constexpr (PART) lds_barrier();
     else __syncthreads();
   }
-  if (ver_lds && j_end > j_begin)
-    for (int i = tid; i < last_rows; i += kScanThreads)
-      if (own(i)) idx[prev_off + i] = sm.ver_cur[vslot(i)];
+  if (ver_lds && j_end > j_begin) for_own_rows(last_rows, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
   if (tid == 0 && p == 0) d.nver[s] = nver;
 }
 
