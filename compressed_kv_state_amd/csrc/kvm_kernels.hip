@@ -172,6 +172,11 @@ struct ScanSmem {
   int wtot[ScanGeom<C>::NW];
   int xok;                        // 0 after a wait at the exchange timed out
   int ver_cur[VC];                // current version id of every (own) row
+  // row-split kernel up to C = 128: per own row (by version slot), the chunk's
+  // tokens that merge into it, one bit per position
+  static constexpr bool TAB = PART && C <= 128;
+  static constexpr int MW = C / 32;
+  alignas(16) uint32_t rmask[TAB ? VC : 1][TAB ? MW : 1];
 };
 
 // Polls of an exchange record before a scan workgroup gives up (each poll is a
@@ -768,6 +773,12 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     for_own_rows(r0, [&](int q, int r) { sm.ver_cur[q] = prev[r]; });
   }
 
+  constexpr bool kTab = ScanSmem<T, C, PART>::TAB;
+  constexpr int MW = ScanSmem<T, C, PART>::MW;
+  if constexpr (kTab)
+    for (int i = tid; i < ScanSmem<T, C, PART>::VC * MW; i += kScanThreads) (&sm.rmask[0][0])[i] = 0u;
+  int clear_slot = -1;   // a mask this thread's lane group read, cleared in the next step
+
   // unit directions kept in LDS: the first NL rows of the workgroup's own
   // tiles (local slot = local tile * 32 + offset) that exist at the start
   if (NL > 0 && j_begin < j_end) {
@@ -811,6 +822,14 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     const int rows_after = R0 + nc;
     const int64_t P0 = (int64_t)j * C;
 
+    // the token masks of the rows the previous step updated (every read of
+    // them came before the barrier that closed that step)
+    if constexpr (kTab)
+      if (clear_slot >= 0) {
+        if ((tid & 3) == 0)
+          for (int i = 0; i < MW; ++i) sm.rmask[clear_slot][i] = 0u;
+        clear_slot = -1;
+      }
     // ---- 1. the chunk, its key norms and gates are in LDS buffer `cur` (one
     // buffer: store it now); the first unit-direction tiles of the surprise
     // pass start loading.  The next chunk's loads are issued before the index
@@ -1036,10 +1055,15 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         a = min(max(a, 0), rows_after - 1);
         if (sub == 0) {
           sm.arow[t] = a;
-          sm.mrow[mslot] = a;
+          if constexpr (kTab) {
+            if (own(a)) __hip_atomic_fetch_or(&sm.rmask[vslot(a)][t >> 5], 1u << (t & 31), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_WORKGROUP);
+          } else {
+            sm.mrow[mslot] = a;
+          }
         }
         if (own(a)) row_load(rr[ps], key_sum, val_sum, count, rho, a, sub);
-      } else if (sub == 0) {
+      } else if (!kTab && sub == 0) {
         sm.mrow[mslot] = -1;
       }
     }
@@ -1065,43 +1089,71 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       const bool merged = sm.flag[tc] == kMerge;
       const int target = sm.arow[tc];
       if (t >= C || !own(target)) continue;   // another workgroup's row (the same for the lane group)
-      uint32_t mk[QW];
+      // the row's merged tokens, one bit per position (every lane of the group)
+      uint32_t mw[kTab ? MW : 4 * QW];
+      if constexpr (kTab) {
+        // from the row's mask, which the assignment filled
+        const int slot = vslot(target);
+        if constexpr (MW == 4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(&sm.rmask[slot][0]);
 #pragma unroll
-      for (int q = 0; q < QW; ++q) mk[q] = 0u;
-      {
-        const u32x4* m4 = reinterpret_cast<const u32x4*>(sm.mrow + sub * (Q + 4));
+          for (int i = 0; i < 4; ++i) mw[i] = x[i];
+        } else {
 #pragma unroll
-        for (int i = 0; i < Q / 4; ++i) {
-          const u32x4 x = m4[i];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (x[e] == (uint32_t)target) mk[(4 * i + e) >> 5] |= 1u << ((4 * i + e) & 31);
+          for (int i = 0; i < MW; ++i) mw[i] = sm.rmask[slot][i];
         }
-      }
-      // a merged token heads its row unless a lower position merges into it too
-      uint32_t low = 0u;
-      {
-        const int qt = tc / Q, bt = tc % Q;
+        // a merged token heads its row when it is the row's lowest position
+        if (merged) {
+          if (target >= R0) continue;
+          bool head = true;
 #pragma unroll
-        for (int q = 0; q < QW; ++q) {
-          const int lo = bt - 32 * q;   // bits of this word below position t
-          const uint32_t below = lo >= 32 ? ~0u : (lo > 0 ? (1u << lo) - 1u : 0u);
-          low |= sub < qt ? mk[q] : (sub == qt ? (mk[q] & below) : 0u);
+          for (int i = 0; i < MW; ++i) {
+            const uint32_t below = 32 * i + 32 <= t ? ~0u : (32 * i < t ? (1u << (t - 32 * i)) - 1u : 0u);
+            head = head && (mw[i] & below) == 0u;
+          }
+          if (!head) continue;
         }
-        low |= (uint32_t)xor_lane<1>((int)low);
-        low |= (uint32_t)xor_lane<2>((int)low);
-      }
-      // every lane of the group takes all four quarters' masks
-      uint32_t all[4][QW];
+        clear_slot = slot;
+      } else {
+        // from a scan of the chunk's targets (lane sub scans positions [sub Q, sub Q + Q))
+        uint32_t mk[QW];
 #pragma unroll
-      for (int q = 0; q < QW; ++q) {
-        all[0][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0x00, 0xF, 0xF, false);
-        all[1][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0x55, 0xF, 0xF, false);
-        all[2][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0xAA, 0xF, 0xF, false);
-        all[3][q] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[q], 0xFF, 0xF, 0xF, false);
+        for (int q = 0; q < QW; ++q) mk[q] = 0u;
+        {
+          const u32x4* m4 = reinterpret_cast<const u32x4*>(sm.mrow + sub * (Q + 4));
+#pragma unroll
+          for (int i = 0; i < Q / 4; ++i) {
+            const u32x4 x = m4[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (x[e] == (uint32_t)target) mk[(4 * i + e) >> 5] |= 1u << ((4 * i + e) & 31);
+          }
+        }
+        // a merged token heads its row unless a lower position merges into it too
+        uint32_t low = 0u;
+        {
+          const int qt = tc / Q, bt = tc % Q;
+#pragma unroll
+          for (int q = 0; q < QW; ++q) {
+            const int lo = bt - 32 * q;   // bits of this word below position t
+            const uint32_t below = lo >= 32 ? ~0u : (lo > 0 ? (1u << lo) - 1u : 0u);
+            low |= sub < qt ? mk[q] : (sub == qt ? (mk[q] & below) : 0u);
+          }
+          low |= (uint32_t)xor_lane<1>((int)low);
+          low |= (uint32_t)xor_lane<2>((int)low);
+        }
+        // every lane of the group takes all four quarters' masks (quarter q,
+        // word qw holds positions q Q + 32 qw + bit)
+#pragma unroll
+        for (int qw = 0; qw < QW; ++qw) {
+          mw[0 * QW + qw] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[qw], 0x00, 0xF, 0xF, false);
+          mw[1 * QW + qw] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[qw], 0x55, 0xF, 0xF, false);
+          mw[2 * QW + qw] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[qw], 0xAA, 0xF, 0xF, false);
+          mw[3 * QW + qw] = (uint32_t)__builtin_amdgcn_mov_dpp((int)mk[qw], 0xFF, 0xF, 0xF, false);
+        }
+        if (merged && (low != 0u || target >= R0)) continue;   // the same for the whole group
       }
       const bool creates = !merged;
-      if (t >= C || (merged && (low != 0u || target >= R0))) continue;   // the same for the whole group
       const int row = target;
       alignas(16) float K[8];
       alignas(16) float V[16];
@@ -1128,22 +1180,45 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         n = rr[ps].n;
         rh = rr[ps].rh;
       }
+      // the merged tokens, added in position order, up to C = 128 two at a
+      // time (both tokens' reads in flight together; a lone last token reads
+      // itself twice)
+      constexpr int NWD = kTab ? MW : 4 * QW;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int wd = 0; wd < NWD; ++wd) {
+        const int pbase = kTab ? 32 * wd : (wd / QW) * Q + 32 * (wd % QW);
+        uint32_t mm = mw[wd];
+        while (mm) {
+          const int t1 = pbase + __builtin_ctz(mm);
+          mm &= mm - 1u;
+          const bool two = C <= 128 && mm != 0u;   // (registers: one at a time beyond)
+          const int t2 = two ? pbase + __builtin_ctz(mm) : t1;
+          if (two) mm &= mm - 1u;
+          const float g1 = chc.g[t1], g2 = chc.g[t2];
+          alignas(16) T k1[8], k2[8], v1[16], v2[16];
 #pragma unroll
-        for (int qw = 0; qw < QW; ++qw) {
-          uint32_t mm = all[q][qw];
-          while (mm) {
-            const int tm = q * Q + 32 * qw + __builtin_ctz(mm);
-            mm &= mm - 1u;
-            const float gt = chc.g[tm];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) K[i] = fmaf(gt, tof(Kc[tm][8 * sub + i]), K[i]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) V[i] = fmaf(gt, tof(Vc[tm][16 * sub + i]), V[i]);
-            ++n;
+          for (int i = 0; i < 8; i += 16 / (int)sizeof(T)) {
+            copy16(k1 + i, &Kc[t1][8 * sub + i]);
+            copy16(k2 + i, &Kc[t2][8 * sub + i]);
           }
+#pragma unroll
+          for (int i = 0; i < 16; i += 16 / (int)sizeof(T)) {
+            copy16(v1 + i, &Vc[t1][16 * sub + i]);
+            copy16(v2 + i, &Vc[t2][16 * sub + i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) K[i] = fmaf(g1, tof(k1[i]), K[i]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) V[i] = fmaf(g1, tof(v1[i]), V[i]);
+          if (two) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) K[i] = fmaf(g2, tof(k2[i]), K[i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) V[i] = fmaf(g2, tof(v2[i]), V[i]);
+          }
+          n += two ? 2 : 1;
         }
+      }
       {
         float* ks = key_sum + (size_t)row * 32 + 8 * sub;
         float* vs = val_sum + (size_t)row * 64 + 16 * sub;
