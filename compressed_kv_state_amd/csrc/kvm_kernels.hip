@@ -168,7 +168,10 @@ struct ScanSmem {
   // in four quarters, stored C/4 + 4 words apart so that the four quarters'
   // reads of one LDS cycle fall in different banks
   alignas(16) int mrow[C + 16];
-  int app_list[C];
+  // the chunk's appended tokens: up to C = 128 one bit per position, beyond
+  // that the list in position order (with per-wave counts to place them)
+  alignas(16) uint32_t amask[C / 32];
+  int app_list[C <= 128 ? 1 : C];
   int wtot[ScanGeom<C>::NW];
   int xok;                        // 0 after a wait at the exchange timed out
   int ver_cur[VC];                // current version id of every (own) row
@@ -274,7 +277,12 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<
     const int p = tid + i * R::NT;
     if (p < C * R::VP) *reinterpret_cast<u32x4*>(&dst.v[0][0] + p * R::EL) = r.v[i];
   }
-  if (tid < C) dst.g[tid] = no_gate ? 1.0f : 1.0f / (1.0f + expf(-r.l));
+  // Every thread settles its gate-logit load here, also those whose value is
+  // not stored: a load left pending would make a later reuse of its register
+  // wait for all outstanding memory operations of the wave.
+  float lg = r.l;
+  asm volatile("" : "+v"(lg));
+  if (tid < C) dst.g[tid] = no_gate ? 1.0f : 1.0f / (1.0f + expf(-lg));
 }
 
 // One lane's quarter of the row a merged token goes to: key dims [8 sub,
@@ -454,7 +462,9 @@ __device__ __forceinline__ void unit_tile_lds(const bf16* ul, int rb, int re, in
                                               bf16x8 (&a)[4]) {
   const int lane = threadIdx.x & 63, jl = lane & 31, h = lane >> 5;
   const int ri = own_slot(min(rb + (gt << 5) + jl, re - 1), LB, psh);
-  const bf16* u = ul + ri * UL_PITCH + 16 * h;
+  // (a 24-bit product: a 32-bit multiply-add is emitted as a 64-bit one whose
+  // unused high addend half can be a register still being loaded)
+  const bf16* u = ul + __umul24((unsigned)ri, (unsigned)UL_PITCH) + 16 * h;
   a[0] = *reinterpret_cast<const bf16x8*>(u);
   a[1] = *reinterpret_cast<const bf16x8*>(u + 8);
   a[2] = *reinterpret_cast<const bf16x8*>(u + 32);
@@ -491,15 +501,16 @@ __device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, in
 
 // Best (largest) dot(k_t, U_i) over this workgroup's rows i in [rb, re) for
 // every token t of the chunk, compared on the argmax keys (to 2^-17 |k_t|);
-// ties to the lowest row.  Writes the best key (as a float in (1, 3), 0 if
-// the workgroup has no row) and its row (INT_MAX if none) to outv / outr.
+// ties to the lowest row.  Hands the best key (as a float in (1, 3), 0 if
+// the workgroup has no row) and its row (INT_MAX if none) of token t to
+// emit(t, key, row), one thread per token, with no barrier after it.
 // All threads of the block must call it; on the bf16 path `pre` holds the
 // tiles cos_preload fetched for the same rows.  PART: the rows are split over
 // several workgroups and every own row is LDS-resident (ntl == own tiles).
-template <typename T, int C, bool PART>
+template <typename T, int C, bool PART, typename Emit>
 __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChunk<T, C>& ch, const char* unit,
                                          const bf16* ul, int LB, int ntl, int rb, int re, int p, int psh,
-                                         float* outv, int* outr, UnitTiles& pre) {
+                                         UnitTiles& pre, Emit&& emit) {
   using G = CosGeom<C, PART>;
   constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
@@ -625,8 +636,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
         const int orow = sm.red_r[ww][t];
         if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
       }
-      outv[t] = v;
-      outr[t] = r;
+      emit(t, v, r);
       continue;
     }
     // every wave's partial is read first (independent LDS reads in flight
@@ -643,10 +653,34 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
 #pragma unroll
     for (int ww = 0; ww < G::WG; ++ww)
       if (ww < nw && (pv[ww] > v || (pv[ww] == v && pr[ww] < r))) { v = pv[ww]; r = pr[ww]; }
-    outv[t] = v;
-    outr[t] = r;
+    emit(t, v, r);
   }
-  lds_barrier();
+}
+
+// Position of the k-th set bit (k from 0) of the NW-word mask m (it has more
+// than k set bits): the word by running popcounts, then the bit by halving.
+template <int NW>
+__device__ __forceinline__ int kth_bit(const uint32_t (&m)[NW], int k) {
+  uint32_t x = m[0];
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i + 1 < NW; ++i) {
+    const int c = __popc(x);
+    const bool on = k >= c && base == 32 * i;   // still past word i
+    k = on ? k - c : k;
+    x = on ? m[i + 1] : x;
+    base = on ? 32 * (i + 1) : base;
+  }
+  int bit = 0;
+#pragma unroll
+  for (int w = 16; w >= 1; w >>= 1) {
+    const int c = __popc(x & ((1u << w) - 1u));
+    const bool up = k >= c;
+    k = up ? k - c : k;
+    x = up ? x >> w : x;
+    bit = up ? bit + w : bit;
+  }
+  return base + bit;
 }
 
 // rank[t] = #{s : key[s] < key[t]} for every t < C (tokens to leave out carry
@@ -778,6 +812,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
   if constexpr (kTab)
     for (int i = tid; i < ScanSmem<T, C, PART>::VC * MW; i += kScanThreads) (&sm.rmask[0][0])[i] = 0u;
   int clear_slot = -1;   // a mask this thread's lane group read, cleared in the next step
+  if (tid < C / 32) sm.amask[tid] = 0u;
 
   // unit directions kept in LDS: the first NL rows of the workgroup's own
   // tiles (local slot = local tile * 32 + offset) that exist at the start
@@ -871,8 +906,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // ---- 2. surprise against the rows before the chunk: each workgroup's
     // best over its own rows, then (P > 1) the exchange of those bests
     if (tid == 0) sm.xok = 1;
-    cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, sm.bE, sm.rE, pre);
-    if constexpr (PART) {
+    if constexpr (!PART) {
+      cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, pre, [&](int t, float v, int r) {
+        sm.bE[t] = v;
+        sm.rE[t] = r;
+      });
+      lds_barrier();
+    } else {
       // Exchange of the P workgroups' bests.  Each token's best is published
       // as one 64-bit record: key bits | (row (24 bits, all ones for none) |
       // step tag << 24) << 32, in the buffer of this step's parity; the tag
@@ -886,13 +926,15 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       // every other workgroup's records of the step between, which they
       // publish after reading this one.)  The combine order does not matter:
       // (larger key, then lower row) is a total order.
+      // The thread that combines a token's best over this workgroup's waves
+      // publishes its record at once.
       uint64_t* xb = reinterpret_cast<uint64_t*>(d.xbuf) + ((size_t)s * 2 + (j & 1)) * ((size_t)m.P * C);
       const uint32_t tag = 0x80u | (uint32_t)(j & 0x7F);
-      for (int t = tid; t < C; t += kScanThreads) {
-        const uint32_t r = sm.rE[t] == INT_MAX ? 0xFFFFFFu : (uint32_t)sm.rE[t];
-        const uint64_t x = (uint64_t)__float_as_uint(sm.bE[t]) | ((uint64_t)(r | (tag << 24)) << 32);
+      cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, pre, [&](int t, float v, int r) {
+        const uint32_t rr24 = r == INT_MAX ? 0xFFFFFFu : (uint32_t)r;
+        const uint64_t x = (uint64_t)__float_as_uint(v) | ((uint64_t)(rr24 | (tag << 24)) << 32);
         __hip_atomic_store(xb + (size_t)p * C + t, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      });
       if constexpr (kEarly)
         if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
       // XL lanes per token (a power of two, at most 8): lane sub polls the
@@ -965,77 +1007,103 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       lds_barrier();
     }
 
-    // ---- 3. append the m_j most surprising candidates.  The lane that
-    // reports a token's rank also places it: a wave's reporting lanes hold
+    // ---- 3. append the m_j most surprising candidates.  Up to C = 128 the
+    // lane that reports a token's rank marks the token in the chunk's append
+    // mask, whose bits in position order are the appended tokens in order.
+    // Beyond, that lane also places the token: a wave's reporting lanes hold
     // consecutive tokens in lane order, so a ballot and the per-wave counts
     // give each appended token its place in position order.  Without appends
     // (a full fixed or saturated state) every non-sink token merges and no
     // rank is needed (m_j is the same for the whole workgroup).
-    if (mj == 0) {
-      for (int t = tid; t < C; t += kScanThreads) {
-        sm.flag[t] = t < sinks ? kSink : kMerge;
-        if (t < sinks) sm.arow[t] = R0 + t;
-      }
-    } else {
+    constexpr bool kAM = C <= 128;
+    if (mj > 0) {
       int t;
       const int rank = parallel_rank<C>(sm.key, t);
-      const bool lead = rank >= 0;
-      const bool ap = lead && t >= sinks && rank < mj;
-      const unsigned long long bal = __ballot(ap);
-      const int within = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) sm.wtot[w] = __popcll(bal);
-      lds_barrier();
-      int off = 0;
-      for (int ww = 0; ww < w; ++ww) off += sm.wtot[ww];
-      if (lead) {
-        sm.flag[t] = t < sinks ? kSink : (ap ? kAppend : kMerge);
-        if (t < sinks) {
-          sm.arow[t] = R0 + t;
-        } else if (ap) {
-          sm.arow[t] = R0 + sinks + off + within;
-          sm.app_list[off + within] = t;
+      const bool ap = rank >= 0 && t >= sinks && rank < mj;
+      if constexpr (kAM) {
+        if (ap) __hip_atomic_fetch_or(&sm.amask[t >> 5], 1u << (t & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        const unsigned long long bal = __ballot(ap);
+        const int within = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) sm.wtot[w] = __popcll(bal);
+        lds_barrier();
+        int off = 0;
+        for (int ww = 0; ww < w; ++ww) off += sm.wtot[ww];
+        if (rank >= 0) {
+          sm.flag[t] = t < sinks ? kSink : (ap ? kAppend : kMerge);
+          if (ap) {
+            sm.arow[t] = R0 + sinks + off + within;
+            sm.app_list[off + within] = t;
+          }
         }
       }
+      lds_barrier();
     }
-    lds_barrier();
 
     // ---- 4. best against the new rows (their key sums are the creating tokens'
     // live keys, in LDS: dot(k_t, k_s) / |k_s|), then the winner-take-all assignment.
     // New row R0 + e was created by token e (a sink, e < sinks) or by the
     // (e - sinks)-th appended token; sink rows are candidates only unprotected.
-    // The lane group of token t (four lanes) also takes the assignment (every
-    // lane computes it; lane 0 publishes it) and, when the target is one of
-    // this workgroup's rows, starts loading that row (sums, count, radius)
-    // into its registers: the group updates the row below if t comes first
-    // on it (the row's values from the previous steps).
+    // The lane group of token t (four lanes) takes the token's kind and row
+    // (every lane computes them; lane 0 publishes them) and keeps them for the
+    // update; when a merged token's target is one of this workgroup's rows it
+    // starts loading that row (sums, count, radius) into its registers: the
+    // group updates the row below if t comes first on it (the row's values
+    // from the previous steps).
     const int e0 = m.unprot ? 0 : sinks;
     const bool new_rows = nc > e0;   // candidates among this step's new rows (uniform)
     const int fallback = ee > eb ? eb : (R0 + sinks);
+    constexpr int AW = C / 32;
+    uint32_t am[kAM ? AW : 1];
+    if constexpr (kAM) {
+#pragma unroll
+      for (int i = 0; i < AW; ++i) am[i] = __builtin_amdgcn_readfirstlane(sm.amask[i]);   // uniform
+    }
+    // (append mask) the creating token of new row e0 + lane, for the first 64
+    int crl = 0;
+    if constexpr (kAM) {
+      const int el = e0 + lane;
+      if (el < nc) crl = el < sinks ? el : kth_bit<AW>(am, el - sinks);
+    }
     RowRegs rr[TP];
+    int kind[TP], arow_r[TP];
 #pragma unroll
     for (int ps = 0; ps < TP; ++ps) {
       const int t = (tid >> 2) + ps * (kScanThreads / 4);
       const int sub = tid & 3;
+      kind[ps] = kSink;
+      arow_r[ps] = 0;
       if (t >= C) continue;   // the same for the whole lane group
-      const bool merged = sm.flag[t] == kMerge;
+      bool ap;
+      if constexpr (kAM) ap = t >= sinks && ((am[t >> 5] >> (t & 31)) & 1u);
+      else ap = mj > 0 && t >= sinks && sm.flag[t] == kAppend;
+      const bool merged = t >= sinks && !ap;
       float best = -kInf;
       int brow = INT_MAX;
-      if (new_rows) {
-        if (merged) {
-          float kt[32];
+      if (new_rows && (kAM || merged)) {
+        // (with the append mask every lane group runs this, so that the
+        // shuffles below read active lanes; only a merged token's result is used)
+        float kt[32];
 #pragma unroll
-          for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
-          for (int e = e0 + sub; e < nc; e += 4) {
-            const int s2 = e < sinks ? e : sm.app_list[e - sinks];
-            // four partial sums (dims i mod 4) keep the dependent chains short
-            float dp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 32; ++i) dp[i & 3] = fmaf(kt[i], tof(Kc[s2][i]), dp[i & 3]);
-            const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
-            const float nk = chc.kn[s2];
-            const float val = nk > 0.f ? dot * __builtin_amdgcn_rcpf(nk) : 0.f;   // 1 ulp
-            if (val > best) { best = val; brow = R0 + e; }
+        for (int i = 0; i < 32; ++i) kt[i] = tof(Kc[t][i]);
+        // lane sub takes the new rows e with e - e0 = sub mod 4, in order;
+        // row e >= sinks was created by the (e - sinks)-th appended token
+        for (int e = e0 + sub; e < nc; e += 4) {
+          int s2 = e;
+          if constexpr (kAM) {
+            const int sh = __shfl(crl, (e - e0) & 63);
+            if (e >= sinks) s2 = e - e0 < 64 ? sh : kth_bit<AW>(am, e - sinks);
+          } else {
+            if (e >= sinks) s2 = sm.app_list[e - sinks];
           }
+          // four partial sums (dims i mod 4) keep the dependent chains short
+          float dp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < 32; ++i) dp[i & 3] = fmaf(kt[i], tof(Kc[s2][i]), dp[i & 3]);
+          const float dot = (dp[0] + dp[1]) + (dp[2] + dp[3]);
+          const float nk = chc.kn[s2];
+          const float val = nk > 0.f ? dot * __builtin_amdgcn_rcpf(nk) : 0.f;   // 1 ulp
+          if (val > best) { best = val; brow = R0 + e; }
         }
         float ob = xor_lane<1>(best);
         int orow = xor_lane<1>(brow);
@@ -1045,16 +1113,15 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         if (ob > best || (ob == best && orow < brow)) { best = ob; brow = orow; }
       }
       const int mslot = t + 4 * (t / (C / 4));
+      int a;
       if (merged) {
         const int rEt = sm.rE[t];
         const bool eok = rEt != INT_MAX, aok = brow != INT_MAX;
-        int a;
         if (eok && (!aok || sm.bE[t] >= best)) a = rEt;
         else if (aok) a = brow;
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
         if (sub == 0) {
-          sm.arow[t] = a;
           if constexpr (kTab) {
             if (own(a)) __hip_atomic_fetch_or(&sm.rmask[vslot(a)][t >> 5], 1u << (t & 31), __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -1063,11 +1130,32 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           }
         }
         if (own(a)) row_load(rr[ps], key_sum, val_sum, count, rho, a, sub);
-      } else if (!kTab && sub == 0) {
-        sm.mrow[mslot] = -1;
+      } else {
+        if (t < sinks) {
+          a = R0 + t;
+        } else if constexpr (kAM) {   // appended: its place among the appended tokens
+          int below = 0;
+#pragma unroll
+          for (int i = 0; i < AW; ++i) {
+            const int lo = t - 32 * i;   // bits of word i below position t
+            const uint32_t mk = lo >= 32 ? ~0u : (lo > 0 ? (1u << lo) - 1u : 0u);
+            below += __popc(am[i] & mk);
+          }
+          a = R0 + sinks + below;
+        } else {
+          a = sm.arow[t];
+        }
+        if (!kTab && sub == 0) sm.mrow[mslot] = -1;
+      }
+      kind[ps] = t < sinks ? kSink : (ap ? kAppend : kMerge);
+      arow_r[ps] = a;
+      if (sub == 0) {
+        sm.flag[t] = kind[ps];
+        sm.arow[t] = a;
       }
     }
     lds_barrier();
+    if (kAM && tid < AW) sm.amask[tid] = 0u;   // (read above, before the barrier; set again after the next ranking)
 
     // schedule entry of the next step: a scalar load, issued here so that it is
     // covered by this step's closing barrier rather than stalling an LDS barrier
@@ -1086,8 +1174,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       const int t = (tid >> 2) + ps * (kScanThreads / 4);
       const int sub = tid & 3;
       const int tc = min(t, C - 1);
-      const bool merged = sm.flag[tc] == kMerge;
-      const int target = sm.arow[tc];
+      const bool merged = kind[ps] == kMerge;
+      const int target = arow_r[ps];
       if (t >= C || !own(target)) continue;   // another workgroup's row (the same for the lane group)
       // the row's merged tokens, one bit per position (every lane of the group)
       uint32_t mw[kTab ? MW : 4 * QW];
