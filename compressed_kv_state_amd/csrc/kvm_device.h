@@ -99,6 +99,17 @@ __device__ __forceinline__ void zero16(void* dst) { *reinterpret_cast<uint4*>(ds
 // release fence on LDS would make the compiler wait for every transfer in
 // flight into any LDS variable; the empty asm statements keep the compiler
 // from moving memory accesses across the barrier instead.)
+// A pointer the whole wave shares, moved to scalar registers: memory
+// instructions then take it as their scalar base plus a 32-bit per-lane
+// offset instead of a 64-bit per-lane address.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);

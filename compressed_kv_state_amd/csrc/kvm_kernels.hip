@@ -2280,30 +2280,31 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_dma_kernel(Dims m, Dev d, Src
   auto issue = [&](int T, uint8_t* K, uint8_t* V) {
     if (T < n_st) {
       const int r0 = T << 6;
-      const char* pkb = reinterpret_cast<const char*>(pk);
-      const char* pvb = reinterpret_cast<const char*>(pv);
+      // scalar bases, 32-bit lane offsets (a sequence's pool is far below 4 GB)
+      const char* pkb = uniform_ptr(reinterpret_cast<const char*>(pk));
+      const char* pvb = uniform_ptr(reinterpret_cast<const char*>(pv));
       for (int i = w; i < 4; i += NW) {           // keys: 16 rows x 64 B per transfer
         const int row = 16 * i + (lane >> 2);
         const uint32_t unit = (uint32_t)((lane & 3) ^ swz_sk(row));
         const int r = min(r0 + row, S - 1);
-        const char* ks = pkb + ((uint64_t)(uint32_t)sIdx[r] << 6) + 16u * unit;
-        __builtin_amdgcn_global_load_lds(ks, K + 1024 * i, 16, 0, 0);
+        const uint32_t off = ((uint32_t)sIdx[r] << 6) + 16u * unit;
+        __builtin_amdgcn_global_load_lds(pkb + off, K + 1024 * i, 16, 0, 0);
       }
       for (int i = w; i < 8; i += NW) {           // values: 8 rows x 128 B per transfer
         const int row = 8 * i + (lane >> 3);
         const uint32_t unit = (uint32_t)((lane & 7) ^ swz_v(row));
         const int r = min(r0 + row, S - 1);
-        const char* vs = pvb + ((uint64_t)(uint32_t)sIdx[r] << 7) + 16u * unit;
-        __builtin_amdgcn_global_load_lds(vs, V + 1024 * i, 16, 0, 0);
+        const uint32_t off = ((uint32_t)sIdx[r] << 7) + 16u * unit;
+        __builtin_amdgcn_global_load_lds(pvb + off, V + 1024 * i, 16, 0, 0);
       }
     } else {
       const int64_t k0 = lo + ((int64_t)(T - n_st) << 6);
       if (k0 >= src.p0) {
         // every key of the tile is an input of this call (the usual case)
         const int last = (int)min((int64_t)63, hi - 1 - k0);
-        const char* kr0 = reinterpret_cast<const char*>(krot + k0 * 32);
-        const char* ki0 = reinterpret_cast<const char*>(kin + (k0 - src.p0) * 64);
-        const char* vi0 = reinterpret_cast<const char*>(vin + (k0 - src.p0) * 64);
+        const char* kr0 = uniform_ptr(reinterpret_cast<const char*>(krot + k0 * 32));
+        const char* ki0 = uniform_ptr(reinterpret_cast<const char*>(kin + (k0 - src.p0) * 64));
+        const char* vi0 = uniform_ptr(reinterpret_cast<const char*>(vin + (k0 - src.p0) * 64));
         for (int i = w; i < 8; i += NW) {         // keys and values: 8 keys x 128 B per transfer
           const int key = 8 * i + (lane >> 3);
           const uint32_t unit = (uint32_t)((lane & 7) ^ swz_wk(key));
