@@ -5,18 +5,19 @@
 // back; [KVM summary, Core mechanisms 2]: the merge gate is a data-dependent
 // scalar, so its logit is one more projection of the same input, one per head.
 //
-// One GEMM kernel, C[m][n] = sum_k A[m][k] W[n][k] (weights stored [out, in],
-// both operands contiguous along k), 128 x 128 output tiles, four waves of 64 x 64
-// (2 x 2 MFMA tiles of 32 x 32), k in stages of 64 (bf16, v_mfma_f32_32x32x16_bf16)
-// or 32 (fp32, v_mfma_f32_32x32x2f32), double-buffered through LDS, with the
-// next stage's global loads in flight during the current stage's products.
-// Two epilogues / prologues:
+// C[m][n] = sum_k A[m][k] W[n][k] (weights stored [out, in], both operands
+// contiguous along k).  Two prologues / epilogues:
 //   in-projection   A = x [B*N, D]; columns [0, D) q, [D, 2D) k, [2D, 3D) v
 //                   (feature h*64 + d = dim d of head h) written to the layer's
 //                   [B*H, N, 64] layout in the input type, [3D, 3D + H) the
 //                   gate logits (+ per-head bias) as float32 [B*H, N];
 //   out-projection  A gathered from the layer output o [B*H, N, 64] (row
 //                   b*N + t, feature h*64 + d), C = y [B*N, D].
+// bf16: 256 x 256 output tiles, four waves of 128 x 128 (4 x 4 MFMA tiles of
+// 32 x 32, accumulators in the accumulation registers), k in stages of 32 staged
+// by direct global->LDS transfers, three stages in flight.
+// fp32: 128 x 128 tiles, four waves of 64 x 64, k in stages of 32 through
+// registers, double-buffered.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -189,14 +190,199 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 GEMM.  A stage holds rows [256][32] of A and of W (64 bytes a row, four
+// 16-byte units); the unit u of row r is stored at unit u ^ ((r >> 2) & 3), so
+// that the 16 rows an MFMA operand read serves in one LDS cycle (same unit,
+// consecutive rows) fall on distinct banks.  A global->LDS transfer writes 64
+// lanes x 16 bytes in lane order: lane l of transfer i fills row 16 i + l / 4,
+// stored unit l % 4, and so fetches that row's unit (l % 4) ^ swizzle.
+constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 3;
+constexpr int kGStageBytes = (kGM + kGN) * kGK * 2;   // 32 KB
+
+__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
+
+template <bool OUT>
+__global__ __launch_bounds__(256, 1) void proj_gemm_kernel(ProjArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kGStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[kGStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[kGStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  // tiles: consecutive workgroups take the column blocks of one row block, so
+  // that the row block of A is reused from the caches while W stays resident
+  const int n_nt = (a.Nout + kGN - 1) / kGN;
+  const int64_t m0 = (int64_t)(blockIdx.x / n_nt) * kGM;
+  const int n0 = (int)(blockIdx.x % n_nt) * kGN;
+  const bf16* X = reinterpret_cast<const bf16*>(a.x);
+  const bf16* Wt = reinterpret_cast<const bf16*>(a.w);
+
+  // this lane's four A rows and four W rows (transfers w, w + 4, w + 8, w + 12),
+  // clamped to the last row (rows past the end are computed, not stored), and
+  // the element offset of the unit it fetches
+  const bf16* arow[4];
+  const bf16* brow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (w + 4 * i) + (lane >> 2);
+    const int ug = (lane & 3) ^ gswz(r);
+    int64_t m = m0 + r;
+    if (m > a.M - 1) m = a.M - 1;
+    if constexpr (OUT) {
+      const int64_t b = m / a.N, t = m % a.N;
+      arow[i] = X + ((b * a.H) * a.N + t) * 64 + 8 * ug;   // head 0; stage k0 adds head k0/64
+    } else {
+      arow[i] = X + m * a.K + 8 * ug;
+    }
+    int n = n0 + r;
+    if (n > a.Nout - 1) n = a.Nout - 1;
+    brow[i] = Wt + (int64_t)n * a.K + 8 * ug;
+  }
+  auto issue = [&](int k0, uint8_t* stg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16* src;
+      if constexpr (OUT) src = arow[i] + (int64_t)(k0 >> 6) * a.N * 64 + (k0 & 63);
+      else src = arow[i] + k0;
+      __builtin_amdgcn_global_load_lds(src, stg + 1024 * (w + 4 * i), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(brow[i] + k0, stg + kGM * 64 + 1024 * (w + 4 * i), 16, 0, 0);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  // MFMA operand reads: A rows wm*128 + 32 i + lane % 32, W rows wn*128 + 32 j + lane % 32,
+  // unit 2 ks + h of the stage's 32 k.  The swizzle of those rows depends on
+  // the lane only, so each read is a per-lane offset (one per ks) plus a constant.
+  int offa[2], offb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int u = 16 * ((2 * ks + h) ^ gswz(l32));
+    offa[ks] = (wm * 128 + l32) * 64 + u;
+    offb[ks] = kGM * 64 + (wn * 128 + l32) * 64 + u;
+  }
+  auto compute = [&](const uint8_t* stg) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(stg + offa[ks] + 2048 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(stg + offb[ks] + 2048 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // three stages: at the top of stage kt each wave waits for its own eight
+  // transfers of kt (those of kt + 1, issued after them, stay in flight); the
+  // barrier publishes kt and frees the buffer of kt - 1, which takes kt + 2.
+  // (Separate buffers, unrolled by three, so that the compiler sees which
+  // buffer each read and transfer touches.)
+  const int nk = a.K / kGK;
+  issue(0, st0);
+  if (nk > 1) issue(kGK, st1);
+  auto top = [&](int kt) {
+    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // at most 8 in flight
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+  };
+  int kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {   // whole triplets (one exit: the allocator keeps the accumulators put)
+    top(kt);
+    issue((kt + 2) * kGK, st2);
+    compute(st0);
+    top(kt + 1);
+    if (kt + 3 < nk) issue((kt + 3) * kGK, st0);
+    compute(st1);
+    top(kt + 2);
+    if (kt + 4 < nk) issue((kt + 4) * kGK, st1);
+    compute(st2);
+  }
+  // the last one or two stages, already in flight in the first two buffers
+  if (kt < nk) {
+    top(kt);
+    compute(st0);
+  }
+  if (kt + 1 < nk) {
+    top(kt + 1);
+    compute(st1);
+  }
+
+  // epilogue: register r of a 32 x 32 tile is row 8(r/4) + 4h + r%4, column
+  // lane % 32.  Destinations split into a row part and a column part: the
+  // row parts of the tile's 256 rows go to LDS first (one division per row).
+  //   in:  q/k/v element ((b H + f/64) N + t) 64 + f%64 = rowq(m) + colq(n),
+  //        rowq = (b H N + t) 64, colq = (f/64) N 64 + f%64;
+  //        gate logit (b H + hh) N + t = rowg(m) + hh N, rowg = b H N + t;
+  //   out: y element m Nout + n.
+  __syncthreads();   // every wave is done with the stages
+  int64_t* rowpart = reinterpret_cast<int64_t*>(st0);
+  if constexpr (!OUT) {
+    int64_t m = m0 + tid;
+    if (m > a.M - 1) m = a.M - 1;
+    const int64_t b = m / a.N, t = m % a.N;
+    rowpart[tid] = b * a.H * a.N + t;
+  }
+  __syncthreads();
+  const int D = a.H * 64;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn * 128 + 32 * j + l32;
+    if (n >= a.Nout) continue;
+    // the column's destination (in-projection)
+    int part = 3;
+    int64_t col = 0;
+    if constexpr (!OUT) {
+      if (n < 3 * D) {
+        part = n / D;
+        const int f = n % D;
+        col = (int64_t)(f >> 6) * a.N * 64 + (f & 63);
+      } else {
+        col = (int64_t)(n - 3 * D) * a.N;
+      }
+    }
+    bf16* dst = OUT ? reinterpret_cast<bf16*>(a.y)
+                    : reinterpret_cast<bf16*>(part == 0 ? a.q : (part == 1 ? a.k : a.v));
+    const float bias = (!OUT && part == 3 && a.bias) ? a.bias[n - 3 * D] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // row in the tile
+        const int64_t m = m0 + rl;
+        if (m >= a.M) continue;
+        const float val = acc[i][j][r];
+        if constexpr (OUT) {
+          dst[m * a.Nout + n] = (bf16)val;
+        } else if (part < 3) {
+          dst[rowpart[rl] * 64 + col] = (bf16)val;
+        } else {
+          a.gl[rowpart[rl] + col] = val + bias;
+        }
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_proj(const ProjArgs& a, bool out, bool is_bf16, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
   const unsigned grid = (unsigned)(((a.M + kPM - 1) / kPM) * ((a.Nout + kPN - 1) / kPN));
   if (is_bf16) {
-    if (out) proj_kernel<bf16, true><<<grid, 256, 0, st>>>(a);
-    else proj_kernel<bf16, false><<<grid, 256, 0, st>>>(a);
+    const unsigned g = (unsigned)(((a.M + kGM - 1) / kGM) * ((a.Nout + kGN - 1) / kGN));
+    if (out) proj_gemm_kernel<true><<<g, 256, 0, st>>>(a);
+    else proj_gemm_kernel<false><<<g, 256, 0, st>>>(a);
   } else {
     if (out) proj_kernel<float, true><<<grid, 256, 0, st>>>(a);
     else proj_kernel<float, false><<<grid, 256, 0, st>>>(a);
