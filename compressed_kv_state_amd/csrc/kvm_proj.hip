@@ -13,9 +13,9 @@
 //                   gate logits (+ per-head bias) as float32 [B*H, N];
 //   out-projection  A gathered from the layer output o [B*H, N, 64] (row
 //                   b*N + t, feature h*64 + d), C = y [B*N, D].
-// bf16: 256 x 256 output tiles, four waves of 128 x 128 (4 x 4 MFMA tiles of
-// 32 x 32, accumulators in the accumulation registers), k in stages of 32 staged
-// by direct global->LDS transfers, three stages in flight.
+// bf16: 256 x 256 output tiles, eight waves of 128 x 64 (4 x 2 MFMA tiles of
+// 32 x 32; two waves per SIMD), k in stages of 32 staged by direct
+// global->LDS transfers, three stages in flight.
 // fp32: 128 x 128 tiles, four waves of 64 x 64, k in stages of 32 through
 // registers, double-buffered.
 #include <hip/hip_runtime.h>
@@ -204,29 +204,46 @@ constexpr int kGStageBytes = (kGM + kGN) * kGK * 2;   // 32 KB
 __device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
 template <bool OUT>
-__global__ __launch_bounds__(256, 1) void proj_gemm_kernel(ProjArgs a) {
+__global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kGStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kGStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st2[kGStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
-  // tiles: consecutive workgroups take the column blocks of one row block, so
-  // that the row block of A is reused from the caches while W stays resident
+  const int wm = w & 1, wn = w >> 1;   // wave tile: rows wm*128 + [0, 128), columns wn*64 + [0, 64)
+  // tiles: dispatch b runs on XCD b mod 8.  With the row blocks a multiple of
+  // 8, XCD x takes the row blocks = x (mod 8), in groups of four row blocks
+  // swept across all column blocks, so that each row block of A and each
+  // column block of W is fetched into that XCD's L2 once per group;
+  // otherwise consecutive workgroups take the column blocks of one row block.
   const int n_nt = (a.Nout + kGN - 1) / kGN;
-  const int64_t m0 = (int64_t)(blockIdx.x / n_nt) * kGM;
-  const int n0 = (int)(blockIdx.x % n_nt) * kGN;
+  const int m_nt = (int)((a.M + kGM - 1) / kGM);
+  int mb, nb;
+  if (m_nt % 8 == 0) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    constexpr int GM = 4;
+    const int per = m_nt / 8;                    // row blocks of this XCD
+    const int g = k / (GM * n_nt), r = k % (GM * n_nt);
+    const int gm = min(GM, per - g * GM);        // row blocks in this group
+    nb = r / gm;
+    mb = 8 * (g * GM + r % gm) + x;
+  } else {
+    mb = blockIdx.x / n_nt;
+    nb = blockIdx.x % n_nt;
+  }
+  const int64_t m0 = (int64_t)mb * kGM;
+  const int n0 = nb * kGN;
   const bf16* X = reinterpret_cast<const bf16*>(a.x);
   const bf16* Wt = reinterpret_cast<const bf16*>(a.w);
 
-  // this lane's four A rows and four W rows (transfers w, w + 4, w + 8, w + 12),
+  // this lane's two A rows and two W rows (transfers w and w + 8 of each),
   // clamped to the last row (rows past the end are computed, not stored), and
   // the element offset of the unit it fetches
-  const bf16* arow[4];
-  const bf16* brow[4];
+  const bf16* arow[2];
+  const bf16* brow[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * (w + 4 * i) + (lane >> 2);
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (w + 8 * i) + (lane >> 2);
     const int ug = (lane & 3) ^ gswz(r);
     int64_t m = m0 + r;
     if (m > a.M - 1) m = a.M - 1;
@@ -242,24 +259,24 @@ __global__ __launch_bounds__(256, 1) void proj_gemm_kernel(ProjArgs a) {
   }
   auto issue = [&](int k0, uint8_t* stg) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const bf16* src;
       if constexpr (OUT) src = arow[i] + (int64_t)(k0 >> 6) * a.N * 64 + (k0 & 63);
       else src = arow[i] + k0;
-      __builtin_amdgcn_global_load_lds(src, stg + 1024 * (w + 4 * i), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, stg + 1024 * (w + 8 * i), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(brow[i] + k0, stg + kGM * 64 + 1024 * (w + 4 * i), 16, 0, 0);
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_global_load_lds(brow[i] + k0, stg + kGM * 64 + 1024 * (w + 8 * i), 16, 0, 0);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  // MFMA operand reads: A rows wm*128 + 32 i + lane % 32, W rows wn*128 + 32 j + lane % 32,
+  // MFMA operand reads: A rows wm*128 + 32 i + lane % 32, W rows wn*64 + 32 j + lane % 32,
   // unit 2 ks + h of the stage's 32 k.  The swizzle of those rows depends on
   // the lane only, so each read is a per-lane offset (one per ks) plus a constant.
   int offa[2], offb[2];
@@ -267,24 +284,28 @@ __global__ __launch_bounds__(256, 1) void proj_gemm_kernel(ProjArgs a) {
   for (int ks = 0; ks < 2; ++ks) {
     const int u = 16 * ((2 * ks + h) ^ gswz(l32));
     offa[ks] = (wm * 128 + l32) * 64 + u;
-    offb[ks] = kGM * 64 + (wn * 128 + l32) * 64 + u;
+    offb[ks] = kGM * 64 + (wn * 64 + l32) * 64 + u;
   }
   auto compute = [&](const uint8_t* stg) {
+    // both k steps' fragments are read first, so that the second step's reads
+    // are in flight during the first step's products
+    bf16x8 af[2][4], bfr[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(stg + offa[ks] + 2048 * i);
+      for (int i = 0; i < 4; ++i) af[ks][i] = *reinterpret_cast<const bf16x8*>(stg + offa[ks] + 2048 * i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(stg + offb[ks] + 2048 * j);
+      for (int j = 0; j < 2; ++j) bfr[ks][j] = *reinterpret_cast<const bf16x8*>(stg + offb[ks] + 2048 * j);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
-    }
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(af[ks][i], bfr[ks][j], acc[i][j]);
   };
 
-  // three stages: at the top of stage kt each wave waits for its own eight
+  // three stages: at the top of stage kt each wave waits for its own four
   // transfers of kt (those of kt + 1, issued after them, stay in flight); the
   // barrier publishes kt and frees the buffer of kt - 1, which takes kt + 2.
   // (Separate buffers, unrolled by three, so that the compiler sees which
@@ -293,7 +314,7 @@ __global__ __launch_bounds__(256, 1) void proj_gemm_kernel(ProjArgs a) {
   issue(0, st0);
   if (nk > 1) issue(kGK, st1);
   auto top = [&](int kt) {
-    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F78);   // at most 8 in flight
+    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // at most 4 in flight
     else __builtin_amdgcn_s_waitcnt(0x0F70);
     lds_barrier();
   };
@@ -329,16 +350,18 @@ __global__ __launch_bounds__(256, 1) void proj_gemm_kernel(ProjArgs a) {
   __syncthreads();   // every wave is done with the stages
   int64_t* rowpart = reinterpret_cast<int64_t*>(st0);
   if constexpr (!OUT) {
-    int64_t m = m0 + tid;
-    if (m > a.M - 1) m = a.M - 1;
-    const int64_t b = m / a.N, t = m % a.N;
-    rowpart[tid] = b * a.H * a.N + t;
+    if (tid < kGM) {
+      int64_t m = m0 + tid;
+      if (m > a.M - 1) m = a.M - 1;
+      const int64_t b = m / a.N, t = m % a.N;
+      rowpart[tid] = b * a.H * a.N + t;
+    }
   }
   __syncthreads();
   const int D = a.H * 64;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn * 128 + 32 * j + l32;
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + 32 * j + l32;
     if (n >= a.Nout) continue;
     // the column's destination (in-projection)
     int part = 3;
@@ -381,8 +404,8 @@ hipError_t launch_proj(const ProjArgs& a, bool out, bool is_bf16, hipStream_t st
   const unsigned grid = (unsigned)(((a.M + kPM - 1) / kPM) * ((a.Nout + kPN - 1) / kPN));
   if (is_bf16) {
     const unsigned g = (unsigned)(((a.M + kGM - 1) / kGM) * ((a.Nout + kGN - 1) / kGN));
-    if (out) proj_gemm_kernel<true><<<g, 256, 0, st>>>(a);
-    else proj_gemm_kernel<false><<<g, 256, 0, st>>>(a);
+    if (out) proj_gemm_kernel<true><<<g, 512, 0, st>>>(a);
+    else proj_gemm_kernel<false><<<g, 512, 0, st>>>(a);
   } else {
     if (out) proj_kernel<float, true><<<grid, 256, 0, st>>>(a);
     else proj_kernel<float, false><<<grid, 256, 0, st>>>(a);
