@@ -192,22 +192,22 @@ __global__ __launch_bounds__(256, 2) void proj_kernel(ProjArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// bf16 GEMM.  A stage holds rows [256][32] of A and of W (64 bytes a row, four
-// 16-byte units); the unit u of row r is stored at unit u ^ ((r >> 2) & 3), so
-// that the 16 rows an MFMA operand read serves in one LDS cycle (same unit,
-// consecutive rows) fall on distinct banks.  A global->LDS transfer writes 64
-// lanes x 16 bytes in lane order: lane l of transfer i fills row 16 i + l / 4,
-// stored unit l % 4, and so fetches that row's unit (l % 4) ^ swizzle.
-constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 3;
-constexpr int kGStageBytes = (kGM + kGN) * kGK * 2;   // 32 KB
+// bf16 GEMM.  A stage holds rows [256][64] of A and of W (128 bytes a row,
+// eight 16-byte units, whole cache lines); the unit u of row r is stored at
+// unit u ^ ((r >> 1) & 7), so that the 16 rows an MFMA operand read serves in
+// one LDS cycle (same unit, consecutive rows) fall on distinct banks.  A
+// global->LDS transfer writes 64 lanes x 16 bytes in lane order: lane l of
+// transfer i fills row 8 i + l / 8, stored unit l % 8, and so fetches that
+// row's unit (l % 8) ^ swizzle.
+constexpr int kGM = 256, kGN = 256, kGK = 64;
+constexpr int kGStageBytes = (kGM + kGN) * kGK * 2;   // 64 KB
 
-__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
 template <bool OUT>
 __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kGStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kGStageBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[kGStageBytes];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;   // wave tile: rows wm*128 + [0, 128), columns wn*64 + [0, 64)
@@ -236,15 +236,15 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   const bf16* X = reinterpret_cast<const bf16*>(a.x);
   const bf16* Wt = reinterpret_cast<const bf16*>(a.w);
 
-  // this lane's two A rows and two W rows (transfers w and w + 8 of each),
+  // this lane's four A rows and four W rows (transfers w + 8 i of each),
   // clamped to the last row (rows past the end are computed, not stored), and
   // the element offset of the unit it fetches
-  const bf16* arow[2];
-  const bf16* brow[2];
+  const bf16* arow[4];
+  const bf16* brow[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (w + 8 * i) + (lane >> 2);
-    const int ug = (lane & 3) ^ gswz(r);
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (w + 8 * i) + (lane >> 3);
+    const int ug = (lane & 7) ^ gswz(r);
     int64_t m = m0 + r;
     if (m > a.M - 1) m = a.M - 1;
     if constexpr (OUT) {
@@ -259,15 +259,15 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   }
   auto issue = [&](int k0, uint8_t* stg) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const bf16* src;
-      if constexpr (OUT) src = arow[i] + (int64_t)(k0 >> 6) * a.N * 64 + (k0 & 63);
+      if constexpr (OUT) src = arow[i] + (int64_t)(k0 >> 6) * a.N * 64;   // the stage is one head's 64 dims
       else src = arow[i] + k0;
       __builtin_amdgcn_global_load_lds(src, stg + 1024 * (w + 8 * i), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      __builtin_amdgcn_global_load_lds(brow[i] + k0, stg + kGM * 64 + 1024 * (w + 8 * i), 16, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(brow[i] + k0, stg + kGM * 128 + 1024 * (w + 8 * i), 16, 0, 0);
   };
 
   f32x16 acc[4][2];
@@ -277,67 +277,48 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
   // MFMA operand reads: A rows wm*128 + 32 i + lane % 32, W rows wn*64 + 32 j + lane % 32,
-  // unit 2 ks + h of the stage's 32 k.  The swizzle of those rows depends on
+  // unit 2 ks + h of the stage's 64 k.  The swizzle of those rows depends on
   // the lane only, so each read is a per-lane offset (one per ks) plus a constant.
-  int offa[2], offb[2];
+  int offa[4], offb[4];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < 4; ++ks) {
     const int u = 16 * ((2 * ks + h) ^ gswz(l32));
-    offa[ks] = (wm * 128 + l32) * 64 + u;
-    offb[ks] = kGM * 64 + (wn * 64 + l32) * 64 + u;
+    offa[ks] = (wm * 128 + l32) * 128 + u;
+    offb[ks] = kGM * 128 + (wn * 64 + l32) * 128 + u;
   }
   auto compute = [&](const uint8_t* stg) {
-    // both k steps' fragments are read first, so that the second step's reads
-    // are in flight during the first step's products
-    bf16x8 af[2][4], bfr[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[ks][i] = *reinterpret_cast<const bf16x8*>(stg + offa[ks] + 2048 * i);
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(stg + offa[ks] + 4096 * i);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[ks][j] = *reinterpret_cast<const bf16x8*>(stg + offb[ks] + 2048 * j);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int j = 0; j < 2; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(stg + offb[ks] + 4096 * j);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(af[ks][i], bfr[ks][j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+    }
   };
 
-  // three stages: at the top of stage kt each wave waits for its own four
-  // transfers of kt (those of kt + 1, issued after them, stay in flight); the
-  // barrier publishes kt and frees the buffer of kt - 1, which takes kt + 2.
-  // (Separate buffers, unrolled by three, so that the compiler sees which
-  // buffer each read and transfer touches.)
+  // two stages: each barrier follows the wave's wait for its own transfers of
+  // the stage about to be computed; the transfer of the next stage overlaps it.
+  // (Separate buffers, unrolled by two with one exit, so that the compiler sees
+  // which buffer each read and transfer touches and keeps the accumulators put.)
   const int nk = a.K / kGK;
   issue(0, st0);
-  if (nk > 1) issue(kGK, st1);
-  auto top = [&](int kt) {
-    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F74);   // at most 4 in flight
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-    lds_barrier();
-  };
   int kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {   // whole triplets (one exit: the allocator keeps the accumulators put)
-    top(kt);
-    issue((kt + 2) * kGK, st2);
+  for (; kt + 2 <= nk; kt += 2) {
+    dma_barrier();
+    issue((kt + 1) * kGK, st1);
     compute(st0);
-    top(kt + 1);
-    if (kt + 3 < nk) issue((kt + 3) * kGK, st0);
+    dma_barrier();
+    if (kt + 2 < nk) issue((kt + 2) * kGK, st0);
     compute(st1);
-    top(kt + 2);
-    if (kt + 4 < nk) issue((kt + 4) * kGK, st1);
-    compute(st2);
   }
-  // the last one or two stages, already in flight in the first two buffers
-  if (kt < nk) {
-    top(kt);
+  if (kt < nk) {   // an odd last stage, in flight in the first buffer
+    dma_barrier();
     compute(st0);
-  }
-  if (kt + 1 < nk) {
-    top(kt + 1);
-    compute(st1);
   }
 
   // epilogue: register r of a 32 x 32 tile is row 8(r/4) + 4h + r%4, column
