@@ -1078,6 +1078,10 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       if constexpr (kAM) ap = t >= sinks && ((am[t >> 5] >> (t & 31)) & 1u);
       else ap = mj > 0 && t >= sinks && sm.flag[t] == kAppend;
       const bool merged = t >= sinks && !ap;
+      // the token's best existing row, read before the new-row pass so that
+      // the reads overlap it
+      const int rEt = sm.rE[t];
+      const float bEt = sm.bE[t];
       float best = -kInf;
       int brow = INT_MAX;
       if (new_rows && (kAM || merged)) {
@@ -1115,9 +1119,8 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       const int mslot = t + 4 * (t / (C / 4));
       int a;
       if (merged) {
-        const int rEt = sm.rE[t];
         const bool eok = rEt != INT_MAX, aok = brow != INT_MAX;
-        if (eok && (!aok || sm.bE[t] >= best)) a = rEt;
+        if (eok && (!aok || bEt >= best)) a = rEt;
         else if (aok) a = brow;
         else a = fallback;
         a = min(max(a, 0), rows_after - 1);
