@@ -558,7 +558,13 @@ def summarize_trace(db: str, out_md: str, command: str, title: str):
     import statistics
     con = sqlite3.connect(db)
     rows = con.execute("select name, grid_x, workgroup_x, start, end from kernels order by start").fetchall()
-    dec0 = min([t0 for name, _, _, t0, _ in rows if "dec_kernel" in name] or [float("inf")])
+    # the first workload's prefills end where another workload starts: a scan of another grid
+    # (another sequence count or row split) or the first decode kernel
+    scans = [(gx, t0) for name, gx, _, t0, _ in rows if "scan_kernel" in name]
+    first_grid = scans[0][0] if scans else None
+    ends = [t0 for gx, t0 in scans if gx != first_grid]
+    ends += [t0 for name, _, _, t0, _ in rows if "dec_kernel" in name]
+    dec0 = min(ends or [float("inf")])
     prefill_attn = [(t1 - t0) / 1e3 for name, _, _, t0, t1 in rows if ATTN_KERNEL in name and t0 < dec0]
     sel = {}
     for name, gx, wx, t0, t1 in rows:
@@ -579,7 +585,8 @@ def summarize_trace(db: str, out_md: str, command: str, title: str):
             f.write(f"\ndec_kernel (one fused decode step, all sequences): {len(dec)} dispatches, "
                     f"mean {statistics.mean(dec):.1f} us\n")
         if prefill_attn:
-            f.write(f"\n{ATTN_KERNEL} in the prefill workload (dispatches before the first decode kernel): "
+            f.write(f"\n{ATTN_KERNEL} in the first prefill workload (dispatches before the first scan of "
+                    f"another workload or the first decode kernel): "
                     f"{len(prefill_attn)} dispatches, mean {statistics.mean(prefill_attn):.1f} us, "
                     f"total {sum(prefill_attn):.1f} us\n")
     print(open(out_md).read())
