@@ -875,8 +875,9 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     }
     if constexpr (kEarly)
       if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
-    // index list of the previous step (its rows are the R0 rows before this chunk)
-    if (ver_lds && j > j_begin) for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
+    // index list of the previous step (its rows are the R0 rows before this chunk);
+    // the row-split kernel writes it while its exchange records travel
+    if (!PART && ver_lds && j > j_begin) for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
     // surprise is measured against the non-sink rows that existed before the
     // chunk (every row before the chunk when sinks are unprotected)
     const int eb = m.unprot ? 0 : min(m.ns, R0), ee = R0;
@@ -937,6 +938,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       });
       if constexpr (kEarly)
         if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
+      if (j > j_begin) for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
       // XL lanes per token (a power of two, at most 8): lane sub polls the
       // records of workgroups sub, sub + XL, ...; the group then combines.
       constexpr int XL = kScanThreads / C < 8 ? kScanThreads / C : 8;

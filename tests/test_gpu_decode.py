@@ -65,5 +65,5 @@ def test_decode_workload_sampled():
     C = W4.chunk
     chunks = {W4.n_tokens // C - 1, W4.n_tokens // C, W4.n_tokens // C + 1}
     rows = np.arange(W4.n_tokens, n)
-    for s in (0, 517, 1023):
+    for s in list(range(0, 1024, 64)) + [517, 1023]:   # 18 of the 1024 sequences, spread over the batch
         oracle_check(W4, inp, s, n, out, slot, kind, state, attend_chunks=chunks, rows=rows, label="decode-wl")

@@ -89,14 +89,14 @@ def test_350m_sqrt_free_running_decisions():
 
 
 def test_long_saturating_workload_sampled():
-    print("case: long saturating workload, 1x16x131072, oracle on 2 sequences, sampled chunks", flush=True)
+    print("case: long saturating workload, 1x16x131072, oracle on 4 sequences, sampled chunks", flush=True)
     inp = make_inputs(W3)
     out, slot, kind, state, _ = run_prefill(W3, inp)
     assert int(state["n_rows"][0]) == 4096
     C = W3.chunk
     chunks = {0, 1, 2, 3, 4, 200, 257, 258, 259, 300, 400, 511}
     rows = np.concatenate([np.arange(c * C, (c + 1) * C) for c in sorted(chunks)])
-    for s in (3, 9):
+    for s in (0, 3, 9, 15):
         oracle_check(W3, inp, s, W3.n_tokens, out, slot, kind, state, attend_chunks=chunks, rows=rows,
                      label=W3.name + " (sampled chunks)")
 
