@@ -254,7 +254,7 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<
 #pragma unroll
     for (int e = 0; e < R::EL; ++e) n2 = fmaf(tof(x[e]), tof(x[e]), n2);
     n2 = group_sum<R::KP>(n2);
-    const float kn = sqrtf(n2);
+    const float kn = __builtin_amdgcn_sqrtf(n2);   // hardware square root (1 ulp)
     if constexpr (Is<T>::bf) {
       // k 2^-e, exact: each bf16 widened to fp32 (its bits in the upper half),
       // scaled, and narrowed back by taking the upper half
@@ -282,7 +282,8 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<T, C>& r, ScanChunk<
   // wait for all outstanding memory operations of the wave.
   float lg = r.l;
   asm volatile("" : "+v"(lg));
-  if (tid < C) dst.g[tid] = no_gate ? 1.0f : 1.0f / (1.0f + expf(-lg));
+  // (hardware 2^x and reciprocal, each within 1 ulp)
+  if (tid < C) dst.g[tid] = no_gate ? 1.0f : __builtin_amdgcn_rcpf(1.0f + exp2_fast(-lg * kLog2e));
 }
 
 // One lane's quarter of the row a merged token goes to: key dims [8 sub,
@@ -503,14 +504,15 @@ __device__ __forceinline__ void cos_preload(const char* unit, int rb, int re, in
 // every token t of the chunk, compared on the argmax keys (to 2^-17 |k_t|);
 // ties to the lowest row.  Hands the best key (as a float in (1, 3), 0 if
 // the workgroup has no row) and its row (INT_MAX if none) of token t to
-// emit(t, key, row), one thread per token, with no barrier after it.
+// emit(t, key, row), one thread per token, with no barrier after it;
+// every thread calls settle() between its tile loop and the combine.
 // All threads of the block must call it; on the bf16 path `pre` holds the
 // tiles cos_preload fetched for the same rows.  PART: the rows are split over
 // several workgroups and every own row is LDS-resident (ntl == own tiles).
-template <typename T, int C, bool PART, typename Emit>
+template <typename T, int C, bool PART, typename Settle, typename Emit>
 __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChunk<T, C>& ch, const char* unit,
                                          const bf16* ul, int LB, int ntl, int rb, int re, int p, int psh,
-                                         UnitTiles& pre, Emit&& emit) {
+                                         UnitTiles& pre, Settle&& settle, Emit&& emit) {
   using G = CosGeom<C, PART>;
   constexpr int CT = G::CTW;   // token blocks of this wave
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 31, h = lane >> 5;
@@ -613,6 +615,7 @@ __device__ __forceinline__ void cos_best(ScanSmem<T, C, PART>& sm, const ScanChu
       }
     }
   }
+  settle();
   // combine the two lane halves and the waves on (truncated key, row): the
   // larger key, or the lower row on equal keys
 #pragma unroll
@@ -764,11 +767,12 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     else return r;
   };
   // f(slot, row) for every own row below `rows`, one thread per LDS slot (the
-  // sink rows, then the own tiles' rows in slot order)
-  auto for_own_rows = [&](int rows, auto&& f) {
+  // sink rows, then the own tiles' rows in slot order), over the first `nthr`
+  // threads
+  auto for_own_rows = [&](int rows, auto&& f, int nthr = ScanGeom<C>::NT) {
     if constexpr (PART) {
       const int nt = own_tiles(rows > LB ? (rows - LB + 31) >> 5 : 0, p, psh);
-      for (int q = tid; q < LB + 32 * nt; q += kScanThreads) {
+      for (int q = tid; q < LB + 32 * nt; q += nthr) {
         if (q < LB) {
           if (p == 0 && q < rows) f(q, q);
         } else {
@@ -778,7 +782,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
         }
       }
     } else {
-      for (int i = tid; i < rows; i += kScanThreads) f(i, i);
+      for (int i = tid; i < rows; i += nthr) f(i, i);
     }
   };
 
@@ -876,7 +880,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     if constexpr (kEarly)
       if (j + 1 < j_end) chunk_load<T, C>(cr, m, src, s, P0 + C, ring_k, ring_v, ring_l);
     // index list of the previous step (its rows are the R0 rows before this chunk);
-    // the row-split kernel writes it while its exchange records travel
+    // the row-split kernel writes it at the end of its surprise pass
     if (!PART && ver_lds && j > j_begin) for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
     // surprise is measured against the non-sink rows that existed before the
     // chunk (every row before the chunk when sinks are unprotected)
@@ -908,7 +912,7 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
     // best over its own rows, then (P > 1) the exchange of those bests
     if (tid == 0) sm.xok = 1;
     if constexpr (!PART) {
-      cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, pre, [&](int t, float v, int r) {
+      cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, pre, [] {}, [&](int t, float v, int r) {
         sm.bE[t] = v;
         sm.rE[t] = r;
       });
@@ -931,53 +935,79 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
       // publishes its record at once.
       uint64_t* xb = reinterpret_cast<uint64_t*>(d.xbuf) + ((size_t)s * 2 + (j & 1)) * ((size_t)m.P * C);
       const uint32_t tag = 0x80u | (uint32_t)(j & 0x7F);
-      cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, pre, [&](int t, float v, int r) {
+      // Every thread settles the next chunk's loads after its tile loop, ahead
+      // of the record stores: loads and stores retire in order, so a wait for
+      // those registers after the stores (in the chunk store below) would also
+      // wait for the stores to reach the device-coherent level.
+      // The first four waves also write the previous step's index list there:
+      // each SIMD's older wave issues first and ends its tile loop well before
+      // the other, so these writes fill the gap before the combine's barrier.
+      auto settle = [&] {
+        if constexpr (kEarly) {
+#pragma unroll
+          for (int i = 0; i < ChunkRegs<T, C>::NK; ++i) asm volatile("" : "+v"(cr.k[i]));
+#pragma unroll
+          for (int i = 0; i < ChunkRegs<T, C>::NV; ++i) asm volatile("" : "+v"(cr.v[i]));
+          asm volatile("" : "+v"(cr.l));
+        }
+        constexpr int kFirst = kScanThreads / 2;   // the first four waves
+        if (j > j_begin && tid < kFirst)
+          for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; }, kFirst);
+      };
+      cos_best<T, C, PART>(sm, chc, unit, &ul[0][0], LB, ntl, eb, ee, p, psh, pre, settle, [&](int t, float v, int r) {
         const uint32_t rr24 = r == INT_MAX ? 0xFFFFFFu : (uint32_t)r;
         const uint64_t x = (uint64_t)__float_as_uint(v) | ((uint64_t)(rr24 | (tag << 24)) << 32);
         __hip_atomic_store(xb + (size_t)p * C + t, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       });
-      if constexpr (kEarly)
-        if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
-      if (j > j_begin) for_own_rows(R0, [&](int q, int r) { idx[prev_off + r] = sm.ver_cur[q]; });
       // XL lanes per token (a power of two, at most 8): lane sub polls the
       // records of workgroups sub, sub + XL, ...; the group then combines.
+      // The first poll is issued before the next chunk's LDS store, which
+      // runs while it travels.
       constexpr int XL = kScanThreads / C < 8 ? kScanThreads / C : 8;
       constexpr int XR = (8 + XL - 1) / XL;   // records per lane at most
       const int xt = tid / XL, xs = tid % XL;
+      uint32_t pending = 0u;
       if (xt < C) {
-        float v = 0.f;
-        int r = INT_MAX;
-        uint32_t pending = 0u;
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
           const int q = xs + XL * i;
           if (q < m.P) pending |= 1u << i;
         }
-        for (int spin = 0; pending != 0u;) {
-          uint64_t x[XR];
+      }
+      uint64_t x[XR];
+      auto poll = [&] {
 #pragma unroll
-          for (int i = 0; i < XR; ++i)
-            if (pending & (1u << i))
-              x[i] = __hip_atomic_load(xb + (size_t)(xs + XL * i) * C + xt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < XR; ++i)
+          if (pending & (1u << i))
+            x[i] = __hip_atomic_load(xb + (size_t)(xs + XL * i) * C + xt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      poll();
+      if constexpr (kEarly)
+        if (j + 1 < j_end) chunk_store<T, C>(cr, sm.ch[cur ^ 1], m.no_gate);
+      float v = 0.f;
+      int r = INT_MAX;
+      for (int spin = 0; pending != 0u;) {
 #pragma unroll
-          for (int i = 0; i < XR; ++i) {
-            if ((pending & (1u << i)) && (uint32_t)(x[i] >> 56) == tag) {
-              pending &= ~(1u << i);
-              const float ov = __uint_as_float((uint32_t)x[i]);
-              const uint32_t rr = (uint32_t)(x[i] >> 32) & 0xFFFFFFu;
-              const int orow = rr == 0xFFFFFFu ? INT_MAX : (int)rr;
-              if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
-            }
-          }
-          if (pending != 0u) {
-            if (++spin >= kSpinLimit) {
-              sm.xok = 0;
-              __hip_atomic_store(d.xerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
+        for (int i = 0; i < XR; ++i) {
+          if ((pending & (1u << i)) && (uint32_t)(x[i] >> 56) == tag) {
+            pending &= ~(1u << i);
+            const float ov = __uint_as_float((uint32_t)x[i]);
+            const uint32_t rr = (uint32_t)(x[i] >> 32) & 0xFFFFFFu;
+            const int orow = rr == 0xFFFFFFu ? INT_MAX : (int)rr;
+            if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
           }
         }
+        if (pending != 0u) {
+          if (++spin >= kSpinLimit) {
+            sm.xok = 0;
+            __hip_atomic_store(d.xerr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          poll();
+        }
+      }
+      if (xt < C) {
 #pragma unroll
         for (int o = 1; o < XL; o <<= 1) {
           const float ov = __shfl_xor(v, o);
