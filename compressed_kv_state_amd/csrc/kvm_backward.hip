@@ -65,7 +65,7 @@ __device__ __forceinline__ float4 load4(const E* p) {
   }
 }
 
-template <typename T>
+template <typename T, int PITCH = kPitch>
 __device__ void bwd_stage(float* Kt, float* Vt, int Tile, int n_st, int S, const int* idxl, const Dims& m,
                           const Dev& d, const BwdIn& in, const Bwd& b, int s, int64_t lo, int64_t hi, int tid,
                           int nt) {
@@ -91,8 +91,8 @@ __device__ void bwd_stage(float* Kt, float* Vt, int Tile, int n_st, int S, const
         vv = load4(vin + pos * 64 + 4 * c4);
       }
     }
-    float* kd = Kt + key * kPitch + 4 * c4;
-    float* vd = Vt + key * kPitch + 4 * c4;
+    float* kd = Kt + key * PITCH + 4 * c4;
+    float* vd = Vt + key * PITCH + 4 * c4;
     kd[0] = kv.x; kd[1] = kv.y; kd[2] = kv.z; kd[3] = kv.w;
     vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
   }
@@ -425,6 +425,430 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in
 }
 
 // ---------------------------------------------------------------------------
+// bf16 path: the same two kernels with the products on 16-bit operands
+// (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulation), as in the forward:
+// window scores from bf16 rotated keys and bf16 queries, state scores from the
+// fp16 read-form keys and fp16 queries (an exact power-of-two pre-scale keeps
+// the query in fp16 range), dP from the bf16 values and dO (exact), and the
+// second-stage products (dq = dS . K, dk = dS^T . Q, dv = P^T . dO) with the
+// fp32 factors (P, dS, the rotated keys and queries) as hi + lo bf16 pairs, so
+// that they keep ~2^-16 of their precision.  Tiles stay fp32 in LDS (rows padded to 68 floats, so a
+// lane's eight consecutive dims are two aligned 16-byte reads).  MFMA step kk
+// contracts 16 keys (or queries); lane half h supplies the eight that its score
+// registers 8 kk .. 8 kk + 7 hold (rows mrow(8 kk + i, h)), and the other
+// operand is read for the same eight rows, so the score registers feed the
+// next product directly, as in the fp32 kernels.
+// ---------------------------------------------------------------------------
+constexpr int kPX = 68;
+
+__device__ __forceinline__ bf16x8 bf8_at(const float* p) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  return bf16x8{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w, (bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
+}
+__device__ __forceinline__ f16x8 h8_at(const float* p, float sc) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  return f16x8{(f16)(a.x * sc), (f16)(a.y * sc), (f16)(a.z * sc), (f16)(a.w * sc),
+               (f16)(b.x * sc), (f16)(b.y * sc), (f16)(b.z * sc), (f16)(b.w * sc)};
+}
+// registers 8 kk .. 8 kk + 7 of a score tile as an operand
+__device__ __forceinline__ bf16x8 bf8_regs(const f32x16& x, int kk) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[8 * kk + i];
+  return r;
+}
+// column `col` of the eight tile rows base + mrow(8 kk + i, h)
+__device__ __forceinline__ bf16x8 bf8_col(const float* t, int base, int kk, int h, int col) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)t[(base + mrow(8 * kk + i, h)) * kPX + col];
+  return r;
+}
+// x = hi + lo to ~2^-16 relative (bf16 hi, bf16 remainder)
+__device__ __forceinline__ void bf8_split(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = (bf16)x[i];
+    lo[i] = (bf16)(x[i] - (float)hi[i]);
+  }
+}
+// power-of-two pre-scale exponent keeping values of magnitude < 2^14 * 2^qsh in fp16
+__device__ __forceinline__ int f16_shift(float amax) {
+  if (!(amax >= 16384.f)) return 0;
+  int ex;
+  frexpf(amax, &ex);
+  return ex - 14;
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  constexpr int C = NW * 32;
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) float Kt[32 * kPX];
+  __shared__ __attribute__((aligned(16))) float Vt[32 * kPX];
+  const int s = blockIdx.x % m.BH;
+  const int c = blockIdx.x / m.BH;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, ql = lane & 31;
+  const int64_t cpos = (int64_t)c * C;
+  const int64_t qp = cpos + 32 * w + ql;
+  const bool qvalid = qp < in.N;
+  const int64_t qq = qvalid ? qp : in.N - 1;
+  const float c2 = m.scale * kLog2e;
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  const int* idxl = d.idx + (size_t)s * m.idx_total;
+  if (jj >= 0) {
+    const int4 sc = d.sched[jj];
+    S = sc.x + sc.y + sc.z;
+    idxl += sc.w;
+  }
+  const int n_st = (S + 31) >> 5;
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
+  const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
+  // B operands: the query (rotated, scaled into log2 units; bf16 for the window,
+  // fp16 on the state's dims 32..63) and dO, step kk taking dims 16 kk + 8 h + e
+  bf16x8 qb[4], db[4];
+  f16x8 qh[2];
+  int qsh;
+  {
+    const float* qr = b.qr32 + ((size_t)s * in.N + qq) * 64;
+    const bf16* dor = reinterpret_cast<const bf16*>(in.dout) + ((size_t)s * in.N + qq) * 64;
+    float amax = 0.f;
+    float xs[4][8];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(qr + 16 * kk + 8 * h);
+      const float4 b2 = *reinterpret_cast<const float4*>(qr + 16 * kk + 8 * h + 4);
+      const float y[8] = {a.x, a.y, a.z, a.w, b2.x, b2.y, b2.z, b2.w};
+      const bf16x8 dv = *reinterpret_cast<const bf16x8*>(dor + 16 * kk + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = y[e] * c2;
+        xs[kk][e] = x;
+        qb[kk][e] = (bf16)x;
+        if (kk >= 2) amax = fmaxf(amax, fabsf(x));
+      }
+      db[kk] = qvalid ? dv : bf16x8{};
+    }
+    amax = fmaxf(amax, partner_f(amax));
+    qsh = f16_shift(amax);
+    const float sc = ldexpf(1.f, -qsh);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qh[kk][e] = (f16)(xs[2 + kk][e] * sc);
+  }
+  const float qscale = ldexpf(1.f, qsh);
+  const bool wave_qsh = __ballot(qsh != 0) != 0ull;
+  auto scores = [&](int Tile) {
+    f32x16 acc = {};
+    const float* kr = Kt + ql * kPX + 8 * h;
+    if (Tile < n_st) {   // state keys live on dims 32..63 only
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma_f16(h8_at(kr + 32 + 16 * kk, 1.f), qh[kk], acc);
+      if (wave_qsh) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] *= qscale;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(bf8_at(kr + 16 * kk), qb[kk], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!bwd_valid(Tile, n_st, S, lo, hi, mrow(r, h), qp, qvalid)) acc[r] = -kInf;
+    return acc;
+  };
+  auto dscores = [&]() {
+    f32x16 acc = {};
+    const float* vr = Vt + ql * kPX + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(bf8_at(vr + 16 * kk), db[kk], acc);
+    return acc;
+  };
+  // sweep 1: the row maximum, row sum and D = sum_j P_j dP_j, online
+  float mx = -kInf, ls = 0.f, ds = 0.f;
+  for (int Tile = 0; Tile < n_tiles; ++Tile) {
+    __syncthreads();
+    bwd_stage<bf16, kPX>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, b, s, lo, hi, tid, NT);
+    __syncthreads();
+    const f32x16 a = scores(Tile);
+    const f32x16 dp = dscores();
+    float mt = -kInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, a[r]);
+    mt = fmaxf(mt, partner_f(mt));
+    const float mn = fmaxf(mx, mt);
+    if (mn != -kInf) {
+      const float al = mx == -kInf ? 0.f : exp2_fast(mx - mn);
+      ls *= al;
+      ds *= al;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = a[r] == -kInf ? 0.f : exp2_fast(a[r] - mn);
+        ls += p;
+        ds = fmaf(p, dp[r], ds);
+      }
+      mx = mn;
+    }
+  }
+  ls += partner_f(ls);
+  ds += partner_f(ds);
+  const float lse = mx + log2f(ls);
+  const float Dq = ds / ls;
+  if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
+  // sweep 2: dq += dS . K
+  f32x16 dq0 = {}, dq1 = {};
+  for (int Tile = 0; Tile < n_tiles; ++Tile) {
+    __syncthreads();
+    bwd_stage<bf16, kPX>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, b, s, lo, hi, tid, NT);
+    __syncthreads();
+    const f32x16 a = scores(Tile);
+    const f32x16 dp = dscores();
+    f32x16 dsc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = a[r] == -kInf ? 0.f : exp2_fast(a[r] - lse);
+      dsc[r] = p * (dp[r] - Dq);
+    }
+    // dq = sum_j dS_j k_j has sum_j dS_j = 0, so a common offset of the keys
+    // cancels in it; bf16 rounding of dS or of the keys would not cancel, so
+    // both operands go in as hi + lo pairs (three products, to ~2^-16)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float xa[8], xb[8];
+      bf16x8 ah, al, bh, bl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xa[i] = dsc[8 * kk + i];
+      bf8_split(xa, ah, al);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half == 0 && Tile < n_st) continue;   // state keys are zero on dims 0..31
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xb[i] = Kt[mrow(8 * kk + i, h) * kPX + 32 * half + ql];
+        bf8_split(xb, bh, bl);
+        f32x16& acc = half ? dq1 : dq0;
+        acc = mfma_bf16(ah, bh, acc);
+        acc = mfma_bf16(ah, bl, acc);
+        acc = mfma_bf16(al, bh, acc);
+      }
+    }
+  }
+  // dq rows are queries (register r: query row(r, h)), lane column = dim; RoPE transposed
+  float* dqo = b.dq + (size_t)s * in.N * 64;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t qpos = cpos + 32 * w + mrow(r, h);
+    const float y = dq0[r];
+    const float yp = __shfl_xor(y, 16);
+    if (qpos < in.N) {
+      const int jf = ql & 15;
+      const float cs = d.rope_cos[qpos * 16 + jf], sn = d.rope_sin[qpos * 16 + jf];
+      const float x = ql < 16 ? y * cs + yp * sn : y * cs - yp * sn;
+      dqo[qpos * 64 + ql] = m.scale * x;
+      dqo[qpos * 64 + 32 + ql] = m.scale * dq1[r];
+    }
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  constexpr int C = NW * 32;
+  constexpr int QB = C < kQB ? C : kQB;
+  __shared__ __attribute__((aligned(16))) float Qs[QB * kPX];
+  __shared__ __attribute__((aligned(16))) float Ds[QB * kPX];
+  __shared__ float2 LD[QB];
+  __shared__ unsigned qmax_bits;
+  const int s = blockIdx.x % m.BH;
+  const int c = blockIdx.x / m.BH;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, kl = lane & 31;
+  const int64_t cpos = (int64_t)c * C;
+  const float c2 = m.scale * kLog2e;
+  const int64_t jj = c - m.W / C - 1;
+  int S = 0;
+  int64_t ioff = 0;
+  if (jj >= 0) {
+    const int4 sc = d.sched[jj];
+    S = sc.x + sc.y + sc.z;
+    ioff = sc.w;
+  }
+  const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
+  const int n_st = (S + 31) >> 5;
+  const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
+  const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
+  const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
+  const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const bf16* vin = reinterpret_cast<const bf16*>(in.v) + (size_t)s * in.N * 64;
+  const bf16* doin = reinterpret_cast<const bf16*>(in.dout) + (size_t)s * in.N * 64;
+  for (int q0 = 0; q0 < C; q0 += QB) {
+    // the block's queries, rotated (unscaled), their dO and (lse, D); zero past the end
+    __syncthreads();
+    if (tid == 0) qmax_bits = 0u;
+    __syncthreads();
+    float amax = 0.f;
+    for (int e = tid; e < QB * 16; e += NW * 64) {
+      const int qi = e >> 4, c4 = e & 15;
+      const int64_t pos = cpos + q0 + qi;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), g = x;
+      if (pos < in.N) {
+        x = *reinterpret_cast<const float4*>(b.qr32 + ((size_t)s * in.N + pos) * 64 + 4 * c4);
+        g = load4(doin + pos * 64 + 4 * c4);
+      }
+      if (c4 >= 8) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+      *reinterpret_cast<float4*>(Qs + qi * kPX + 4 * c4) = x;
+      *reinterpret_cast<float4*>(Ds + qi * kPX + 4 * c4) = g;
+    }
+    atomicMax(&qmax_bits, __float_as_uint(amax));   // non-negative floats order as their bits
+    for (int qi = tid; qi < QB; qi += NW * 64) {
+      const int64_t pos = cpos + q0 + qi;
+      LD[qi] = pos < in.N ? b.lse_d[(size_t)s * in.N + pos] : make_float2(kInf, 0.f);
+    }
+    __syncthreads();
+    // state scores take the queries in fp16, pre-scaled by 2^-qsh (the same for the block)
+    const int qsh = f16_shift(__uint_as_float(qmax_bits));
+    const float qdown = ldexpf(1.f, -qsh), qup = ldexpf(1.f, qsh);
+    for (int Tile = w; Tile < n_tiles; Tile += NW) {
+      const bool st = Tile < n_st;
+      // this wave's keys and values as B operands (step kk: dims 16 kk + 8 h + e)
+      bf16x8 kb[4], vb[4];
+      f16x8 kh[2];
+      int64_t kpos = 0;
+      bool kvalid;
+      // (16-byte loads: eight consecutive dims per step and lane half; rows
+      // past the end read a valid row and are zeroed)
+      if (st) {
+        const int r = Tile * 32 + kl;
+        kvalid = r < S;
+        const int64_t ver = kvalid ? idxl[r] : idxl[0];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          kb[kk] = bf16x8{};
+          vb[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(pv + ver * 64 + 16 * kk + 8 * h) : bf16x8{};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          kh[kk] = kvalid ? *reinterpret_cast<const f16x8*>(pk + ver * 32 + 16 * kk + 8 * h) : f16x8{};
+      } else {
+        kpos = lo + (int64_t)(Tile - n_st) * 32 + kl;
+        kvalid = kpos < hi;
+        const int64_t pp = kvalid ? kpos : lo;
+        const float* kr = b.kr32 + ((size_t)s * in.N + pp) * 64;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 kx = bf8_at(kr + 16 * kk + 8 * h);
+          const bf16x8 vx = *reinterpret_cast<const bf16x8*>(vin + pp * 64 + 16 * kk + 8 * h);
+          kb[kk] = kvalid ? kx : bf16x8{};
+          vb[kk] = kvalid ? vx : bf16x8{};
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) kh[kk] = f16x8{};
+      }
+      f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
+      for (int qs = 0; qs < QB; qs += 32) {
+        // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
+        const float* qrow = Qs + (qs + kl) * kPX + 8 * h;
+        const float* drow = Ds + (qs + kl) * kPX + 8 * h;
+        f32x16 sc = {}, dp = {};
+        if (st) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) sc = mfma_f16(h8_at(qrow + 32 + 16 * kk, qdown), kh[kk], sc);
+          if (qsh != 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[r] *= qup;
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) sc = mfma_bf16(bf8_at(qrow + 16 * kk), kb[kk], sc);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(bf8_at(drow + 16 * kk), vb[kk], dp);
+        f32x16 p, dsc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qs + mrow(r, h);
+          const int64_t qpos = cpos + q0 + qi;
+          const float2 ld = LD[qi];
+          const bool ok = kvalid && qpos < in.N && (st || kpos <= qpos);
+          const float pr = ok ? exp2_fast(sc[r] * c2 - ld.x) : 0.f;
+          p[r] = pr;
+          dsc[r] = pr * (dp[r] - ld.y);
+        }
+        // dk[key][d] += dS^T . Q (dS and Q as hi + lo pairs, three products) and
+        // dv[key][e] += P^T . dO (P as a hi + lo pair, dO exact in bf16) over
+        // the sub-block's queries
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          float xa[8], xb[8];
+          bf16x8 dh, dl, ph, pl, bh, bl;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xa[i] = dsc[8 * kk + i];
+          bf8_split(xa, dh, dl);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xa[i] = p[8 * kk + i];
+          bf8_split(xa, ph, pl);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            f32x16& dk = half ? dk1 : dk0;
+            f32x16& dv = half ? dv1 : dv0;
+            if (half == 1 || !st) {   // state keys have no gradient on dims 0..31
+#pragma unroll
+              for (int i = 0; i < 8; ++i) xb[i] = Qs[(qs + mrow(8 * kk + i, h)) * kPX + 32 * half + kl];
+              bf8_split(xb, bh, bl);
+              dk = mfma_bf16(dh, bh, dk);
+              dk = mfma_bf16(dh, bl, dk);
+              dk = mfma_bf16(dl, bh, dk);
+            }
+            const bf16x8 od = bf8_col(Ds, qs, kk, h, 32 * half + kl);
+            dv = mfma_bf16(ph, od, dv);
+            dv = mfma_bf16(pl, od, dv);
+          }
+        }
+      }
+      // rows of the results are keys (register r: key row(r, h)), lane column = dim
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = mrow(r, h);
+        float* dst;
+        if (st) {
+          const int row = Tile * 32 + key;
+          if (row >= S) continue;
+          dst = b.part_state + ((size_t)s * m.idx_total + ioff + row) * 96;
+          const float a0 = m.scale * dk1[r], a1 = dv0[r], a2 = dv1[r];
+          if (q0 == 0) {
+            dst[kl] = a0;
+            dst[32 + kl] = a1;
+            dst[64 + kl] = a2;
+          } else {
+            dst[kl] += a0;
+            dst[32 + kl] += a1;
+            dst[64 + kl] += a2;
+          }
+        } else {
+          const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
+          if (pos >= hi) continue;
+          const int64_t off = pos - (cpos - m.W);   // in [0, W + C)
+          dst = b.part_win + (((size_t)s * b.nq + c) * m.R + off) * 128;
+          const float a0 = m.scale * dk0[r], a1 = m.scale * dk1[r], a2 = dv0[r], a3 = dv1[r];
+          if (q0 == 0) {
+            dst[kl] = a0;
+            dst[32 + kl] = a1;
+            dst[64 + kl] = a2;
+            dst[96 + kl] = a3;
+          } else {
+            dst[kl] += a0;
+            dst[32 + kl] += a1;
+            dst[64 + kl] += a2;
+            dst[96 + kl] += a3;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Window keys: the partials of every chunk whose window holds position p (in
 // chunk order), RoPE transposed on dims 0..31.  Writes dk and dv of every
 // position (the state path adds to them later).  One wave per position, lane =
@@ -596,23 +1020,21 @@ template <typename T>
 hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last, hipStream_t st) {
   const dim3 grid((unsigned)(m.BH * b.nq));
   bwd_rot_kernel<T><<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  auto attn = [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    if constexpr (std::is_same<T, bf16>::value) {
+      bwd_q_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
+      bwd_kv_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
+    } else {
+      bwd_q_kernel<T, NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
+      bwd_kv_kernel<T, NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
+    }
+  };
   switch (m.C) {
-    case 32:
-      bwd_q_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, in, b);
-      bwd_kv_kernel<T, 1><<<grid, 64, 0, st>>>(m, d, in, b);
-      break;
-    case 64:
-      bwd_q_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, in, b);
-      bwd_kv_kernel<T, 2><<<grid, 128, 0, st>>>(m, d, in, b);
-      break;
-    case 128:
-      bwd_q_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, in, b);
-      bwd_kv_kernel<T, 4><<<grid, 256, 0, st>>>(m, d, in, b);
-      break;
-    case 256:
-      bwd_q_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, in, b);
-      bwd_kv_kernel<T, 8><<<grid, 512, 0, st>>>(m, d, in, b);
-      break;
+    case 32: attn(std::integral_constant<int, 1>{}); break;
+    case 64: attn(std::integral_constant<int, 2>{}); break;
+    case 128: attn(std::integral_constant<int, 4>{}); break;
+    case 256: attn(std::integral_constant<int, 8>{}); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
