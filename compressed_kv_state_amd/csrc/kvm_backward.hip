@@ -905,7 +905,10 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   float* part = b.part_state + (size_t)s * m.idx_total * 96;
   float* trho = b.tot_rho + (size_t)s * m.idx_total;
   float tk = 0.f, tv = 0.f, tr = 0.f;
-  // the inputs of snapshot j are loaded while snapshot j + 1 is processed
+  // The inputs of snapshot j are loaded four snapshots ahead of their use.
+  // Every fetch issues the same loads (at a valid index when the snapshot or
+  // the row does not exist), so that the compiler's count of loads in flight
+  // stays exact and each use waits for its own loads only.
   struct In {
     int64_t off;
     float gk, gv, xh, rho, vh, invn;
@@ -913,27 +916,30 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     bool live;
   };
   auto fetch = [&](int j) {
-    In x{};
-    x.live = false;
-    if (j < 0) return x;
-    const int4 sc = d.sched[j];
-    if (i >= sc.x + sc.y + sc.z) return x;   // the row does not exist yet after chunk j
-    x.live = true;
-    x.off = (int64_t)sc.w + i;
-    const int64_t ver = idx[x.off];
+    In x;
+    const int jc = j < 0 ? 0 : j;
+    const int4 sc = d.sched[jc];
+    x.live = j >= 0 && i < sc.x + sc.y + sc.z;   // the row exists after chunk j
+    x.off = (int64_t)sc.w + i;                    // inside the index lists either way
+    const int64_t v0 = idx[x.off];
+    const int64_t ver = x.live ? v0 : 0;
     const float* e = part + x.off * 96;
-    x.gk = l < 32 ? e[l] : 0.f;
+    x.gk = e[l & 31];
     x.gv = e[32 + l];
-    x.xh = l < 32 ? tof(pk[ver * 32 + l]) : 0.f;
+    x.xh = tof(pk[ver * 32 + (l & 31)]);
     x.nm = pnm[ver];
     x.invn = 1.0f / (float)pcnt[ver];
     x.rho = prho[ver];
     x.vh = tof(pv[ver * 64 + l]);
+    if (l >= 32) {
+      x.gk = 0.f;
+      x.xh = 0.f;
+    }
     return x;
   };
-  In cur = fetch(b.absorbed - 1);
-  for (int j = b.absorbed - 1; j >= 0 && cur.live; --j) {
-    const In nxt = fetch(j - 1);
+  // one snapshot's contribution, added to the running totals (later snapshots
+  // first) and stored as the row's total gradient at that snapshot
+  auto step = [&](const In& cur) {
     // LayerNorm backward over the 32 live dims (lanes 0..31; lanes 32..63 carry zeros)
     float sg = cur.gk, sgx = cur.gk * cur.xh;
 #pragma unroll
@@ -961,7 +967,24 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     if (l < 32) e[l] = tk;
     e[32 + l] = tv;
     if (l == 0) trho[cur.off] = tr;
-    cur = nxt;
+  };
+  const int J = b.absorbed - 1;
+  In a0 = fetch(J), a1 = fetch(J - 1), a2 = fetch(J - 2), a3 = fetch(J - 3);
+  for (int j = J; j >= 0; j -= 4) {
+    // (a row exists from its creating chunk on, so the first snapshot without
+    // it ends the sweep)
+    if (!a0.live) break;
+    step(a0);
+    a0 = fetch(j - 4);
+    if (!a1.live) break;
+    step(a1);
+    a1 = fetch(j - 5);
+    if (!a2.live) break;
+    step(a2);
+    a2 = fetch(j - 6);
+    if (!a3.live) break;
+    step(a3);
+    a3 = fetch(j - 7);
   }
 }
 
