@@ -541,6 +541,46 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   }
   const float qscale = ldexpf(1.f, qsh);
   const bool wave_qsh = __ballot(qsh != 0) != 0ull;
+  // Tile staging through registers: the next tile's loads are issued right
+  // after the barrier that publishes this one, so they travel while this tile
+  // is computed (each thread holds IT 16-byte pieces of keys and of values).
+  constexpr int IT = 32 * 16 / NT;
+  float4 rk[IT], rv[IT];
+  const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
+  const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
+  const float* kr32 = b.kr32 + (size_t)s * in.N * 64;
+  const bf16* vin = reinterpret_cast<const bf16*>(in.v) + (size_t)s * in.N * 64;
+  auto load_tile = [&](int Tile) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int e = tid + it * NT, key = e >> 4, c4 = e & 15;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (Tile < n_st) {
+        const int r = Tile * 32 + key;
+        if (r < S) {
+          const int64_t ver = idxl[r];
+          if (c4 >= 8) kv = load4(pk + ver * 32 + 4 * c4 - 32);
+          vv = load4(pv + ver * 64 + 4 * c4);
+        }
+      } else {
+        const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
+        if (pos < hi) {
+          kv = *reinterpret_cast<const float4*>(kr32 + pos * 64 + 4 * c4);
+          vv = load4(vin + pos * 64 + 4 * c4);
+        }
+      }
+      rk[it] = kv;
+      rv[it] = vv;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int e = tid + it * NT, key = e >> 4, c4 = e & 15;
+      *reinterpret_cast<float4*>(Kt + key * kPX + 4 * c4) = rk[it];
+      *reinterpret_cast<float4*>(Vt + key * kPX + 4 * c4) = rv[it];
+    }
+  };
   auto scores = [&](int Tile) {
     f32x16 acc = {};
     const float* kr = Kt + ql * kPX + 8 * h;
@@ -569,10 +609,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   };
   // sweep 1: the row maximum, row sum and D = sum_j P_j dP_j, online
   float mx = -kInf, ls = 0.f, ds = 0.f;
+  if (n_tiles > 0) load_tile(0);
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
-    bwd_stage<bf16, kPX>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, b, s, lo, hi, tid, NT);
+    store_tile();
     __syncthreads();
+    if (Tile + 1 < n_tiles) load_tile(Tile + 1);
     const f32x16 a = scores(Tile);
     const f32x16 dp = dscores();
     float mt = -kInf;
@@ -600,10 +642,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
   // sweep 2: dq += dS . K
   f32x16 dq0 = {}, dq1 = {};
+  if (n_tiles > 0) load_tile(0);
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
-    bwd_stage<bf16, kPX>(Kt, Vt, Tile, n_st, S, idxl, m, d, in, b, s, lo, hi, tid, NT);
+    store_tile();
     __syncthreads();
+    if (Tile + 1 < n_tiles) load_tile(Tile + 1);
     const f32x16 a = scores(Tile);
     const f32x16 dp = dscores();
     f32x16 dsc;
