@@ -440,6 +440,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in
 // next product directly, as in the fp32 kernels.
 // ---------------------------------------------------------------------------
 constexpr int kPX = 68;
+constexpr int kRP = 72;   // row-major 16-bit tile rows (halves): 144 B, 16 lanes' 16-byte reads on distinct banks
+constexpr int kTP = 40;
+constexpr int kBwdIdxCap = 4096;   // snapshot rows whose version ids the bf16 kernels keep in LDS   // transposed 16-bit tile rows (halves): 80 B, likewise
+// Position of tile row r (key or query, 32 per tile) in a transposed row: the
+// eight rows mrow(8 kk + i, h), i < 8, that lane half h contracts at step kk
+// land at 16 kk + 8 h + i.
+__device__ __forceinline__ int kpos(int r) {
+  return (r & 16) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
+}
 
 __device__ __forceinline__ bf16x8 bf8_at(const float* p) {
   const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
@@ -484,8 +493,15 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) float Kt[32 * kPX];
-  __shared__ __attribute__((aligned(16))) float Vt[32 * kPX];
+  // tile in LDS, 16-bit: keys row-major (fp16 for a state tile, bf16 for a
+  // window tile; rows of kRP halves), values row-major (bf16), and the keys
+  // transposed as hi + lo bf16 pairs (rows = dims of kTP halves, keys in the
+  // order kpos that puts each lane half's eight contraction rows side by side)
+  __shared__ __attribute__((aligned(16))) uint16_t Kr[32 * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vr[32 * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t KTh[64 * kTP];
+  __shared__ __attribute__((aligned(16))) uint16_t KTl[64 * kTP];
+  __shared__ int sIdx[kBwdIdxCap];   // the snapshot's version ids (one load round trip per tile, not two)
   const int s = blockIdx.x % m.BH;
   const int c = blockIdx.x / m.BH;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, ql = lane & 31;
@@ -503,6 +519,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
     idxl += sc.w;
   }
   const int n_st = (S + 31) >> 5;
+  for (int i = tid; i < S && i < kBwdIdxCap; i += NT) sIdx[i] = idxl[i];
+  __syncthreads();
   const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
   const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
   const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
@@ -543,57 +561,98 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   const bool wave_qsh = __ballot(qsh != 0) != 0ull;
   // Tile staging through registers: the next tile's loads are issued right
   // after the barrier that publishes this one, so they travel while this tile
-  // is computed (each thread holds IT 16-byte pieces of keys and of values).
+  // is computed.  Each thread holds IT pieces of four dims of keys (raw, 16
+  // bytes either way) and of values (bf16), converted only when stored, so
+  // that no wait follows the loads.
   constexpr int IT = 32 * 16 / NT;
-  float4 rk[IT], rv[IT];
+  uint4 rk[IT];   // window: four fp32 dims; state: eight fp16 dims holding the four
+  uint2 rv[IT];
   const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
   const float* kr32 = b.kr32 + (size_t)s * in.N * 64;
   const bf16* vin = reinterpret_cast<const bf16*>(in.v) + (size_t)s * in.N * 64;
-  auto load_tile = [&](int Tile) {
+  const bool idx_lds = S <= kBwdIdxCap;   // (uniform) version ids from LDS
+  // (loads are unconditional, at clamped in-range addresses, and a piece's
+  // validity is kept beside it and applied when it is stored: a load under a
+  // lane-dependent branch would be waited for where the branch joins)
+  uint32_t rok = 0u;   // bit it: piece it's key and value are real (else zero)
+  auto load_tile = [&](int Tile, auto from_lds) __attribute__((always_inline)) {
+    rok = 0u;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int e = tid + it * NT, key = e >> 4, c4 = e & 15;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      const bf16* va;
       if (Tile < n_st) {
         const int r = Tile * 32 + key;
-        if (r < S) {
-          const int64_t ver = idxl[r];
-          if (c4 >= 8) kv = load4(pk + ver * 32 + 4 * c4 - 32);
-          vv = load4(pv + ver * 64 + 4 * c4);
-        }
+        const int rc = r < S ? r : S - 1;
+        int64_t ver;
+        if constexpr (decltype(from_lds)::value) ver = sIdx[rc];
+        else ver = idxl[rc];
+        // (a 16-byte read inside the row: dims 4 (c4 & 7) .. + 7, or 24 .. 31 for the last piece)
+        const int k0 = (c4 & 7) == 7 ? 24 : 4 * (c4 & 7);
+        rk[it] = *reinterpret_cast<const uint4*>(pk + ver * 32 + k0);
+        va = pv + ver * 64 + 4 * c4;
+        rok |= (r < S ? 1u : 0u) << it;
       } else {
         const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
-        if (pos < hi) {
-          kv = *reinterpret_cast<const float4*>(kr32 + pos * 64 + 4 * c4);
-          vv = load4(vin + pos * 64 + 4 * c4);
-        }
+        const int64_t pc = pos < hi ? pos : hi - 1;
+        rk[it] = *reinterpret_cast<const uint4*>(kr32 + pc * 64 + 4 * c4);
+        va = vin + pc * 64 + 4 * c4;
+        rok |= (pos < hi ? 1u : 0u) << it;
       }
-      rk[it] = kv;
-      rv[it] = vv;
+      rv[it] = *reinterpret_cast<const uint2*>(va);
     }
   };
-  auto store_tile = [&]() {
+  auto prefetch = [&](int Tile) __attribute__((always_inline)) {
+    if (idx_lds) load_tile(Tile, std::true_type{});
+    else load_tile(Tile, std::false_type{});
+  };
+  auto store_tile = [&](int Tile) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int e = tid + it * NT, key = e >> 4, c4 = e & 15;
-      *reinterpret_cast<float4*>(Kt + key * kPX + 4 * c4) = rk[it];
-      *reinterpret_cast<float4*>(Vt + key * kPX + 4 * c4) = rv[it];
+      const bool ok = (rok >> it) & 1u;
+      float kx[4];
+      if (Tile < n_st) {   // fp16 bits as they are (zero on dims 0..31); the values for the split
+        const bool kok = ok && c4 >= 8;
+        const uint2 kr2 = (c4 & 7) == 7 ? make_uint2(rk[it].z, rk[it].w) : make_uint2(rk[it].x, rk[it].y);
+        const uint2 k2 = kok ? kr2 : make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(Kr + key * kRP + 4 * c4) = k2;
+        const f16x4 k4 = __builtin_bit_cast(f16x4, k2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kx[t] = (float)k4[t];
+      } else {
+        kx[0] = ok ? __uint_as_float(rk[it].x) : 0.f;
+        kx[1] = ok ? __uint_as_float(rk[it].y) : 0.f;
+        kx[2] = ok ? __uint_as_float(rk[it].z) : 0.f;
+        kx[3] = ok ? __uint_as_float(rk[it].w) : 0.f;
+        *reinterpret_cast<bf16x4*>(Kr + key * kRP + 4 * c4) = bf16x4{(bf16)kx[0], (bf16)kx[1], (bf16)kx[2], (bf16)kx[3]};
+      }
+      *reinterpret_cast<uint2*>(Vr + key * kRP + 4 * c4) = ok ? rv[it] : make_uint2(0u, 0u);
+      const int kp = kpos(key);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16 hi8 = (bf16)kx[t];
+        const bf16 lo8 = (bf16)(kx[t] - (float)hi8);
+        KTh[(4 * c4 + t) * kTP + kp] = __builtin_bit_cast(uint16_t, hi8);
+        KTl[(4 * c4 + t) * kTP + kp] = __builtin_bit_cast(uint16_t, lo8);
+      }
     }
   };
   auto scores = [&](int Tile) {
     f32x16 acc = {};
-    const float* kr = Kt + ql * kPX + 8 * h;
+    const uint16_t* kr = Kr + ql * kRP + 8 * h;
     if (Tile < n_st) {   // state keys live on dims 32..63 only
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) acc = mfma_f16(h8_at(kr + 32 + 16 * kk, 1.f), qh[kk], acc);
+      for (int kk = 0; kk < 2; ++kk)
+        acc = mfma_f16(*reinterpret_cast<const f16x8*>(kr + 32 + 16 * kk), qh[kk], acc);
       if (wave_qsh) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] *= qscale;
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(bf8_at(kr + 16 * kk), qb[kk], acc);
+      for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qb[kk], acc);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -602,19 +661,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   };
   auto dscores = [&]() {
     f32x16 acc = {};
-    const float* vr = Vt + ql * kPX + 8 * h;
+    const uint16_t* vr = Vr + ql * kRP + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(bf8_at(vr + 16 * kk), db[kk], acc);
+    for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(vr + 16 * kk), db[kk], acc);
     return acc;
   };
   // sweep 1: the row maximum, row sum and D = sum_j P_j dP_j, online
   float mx = -kInf, ls = 0.f, ds = 0.f;
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) prefetch(0);
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
-    store_tile();
+    store_tile(Tile);
     __syncthreads();
-    if (Tile + 1 < n_tiles) load_tile(Tile + 1);
+    if (Tile + 1 < n_tiles) prefetch(Tile + 1);
     const f32x16 a = scores(Tile);
     const f32x16 dp = dscores();
     float mt = -kInf;
@@ -642,12 +701,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
   // sweep 2: dq += dS . K
   f32x16 dq0 = {}, dq1 = {};
-  if (n_tiles > 0) load_tile(0);
+  if (n_tiles > 0) prefetch(0);
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
-    store_tile();
+    store_tile(Tile);
     __syncthreads();
-    if (Tile + 1 < n_tiles) load_tile(Tile + 1);
+    if (Tile + 1 < n_tiles) prefetch(Tile + 1);
     const f32x16 a = scores(Tile);
     const f32x16 dp = dscores();
     f32x16 dsc;
@@ -661,7 +720,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
     // both operands go in as hi + lo pairs (three products, to ~2^-16)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      float xa[8], xb[8];
+      float xa[8];
       bf16x8 ah, al, bh, bl;
 #pragma unroll
       for (int i = 0; i < 8; ++i) xa[i] = dsc[8 * kk + i];
@@ -669,9 +728,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if (half == 0 && Tile < n_st) continue;   // state keys are zero on dims 0..31
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xb[i] = Kt[mrow(8 * kk + i, h) * kPX + 32 * half + ql];
-        bf8_split(xb, bh, bl);
+        const int o = (32 * half + ql) * kTP + 16 * kk + 8 * h;
+        bh = *reinterpret_cast<const bf16x8*>(KTh + o);
+        bl = *reinterpret_cast<const bf16x8*>(KTl + o);
         f32x16& acc = half ? dq1 : dq0;
         acc = mfma_bf16(ah, bh, acc);
         acc = mfma_bf16(ah, bl, acc);
@@ -704,6 +763,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
   __shared__ __attribute__((aligned(16))) float Ds[QB * kPX];
   __shared__ float2 LD[QB];
   __shared__ unsigned qmax_bits;
+  __shared__ int sIdx[kBwdIdxCap];   // the snapshot's version ids
   const int s = blockIdx.x % m.BH;
   const int c = blockIdx.x / m.BH;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, kl = lane & 31;
@@ -719,6 +779,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
   }
   const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
   const int n_st = (S + 31) >> 5;
+  for (int i = tid; i < S && i < kBwdIdxCap; i += NW * 64) sIdx[i] = idxl[i];
   const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
   const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
   const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
@@ -765,7 +826,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
       if (st) {
         const int r = Tile * 32 + kl;
         kvalid = r < S;
-        const int64_t ver = kvalid ? idxl[r] : idxl[0];
+        const int rr = kvalid ? r : 0;
+        const int64_t ver = rr < kBwdIdxCap ? sIdx[rr] : idxl[rr];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           kb[kk] = bf16x8{};
