@@ -758,9 +758,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
+  // query blocks of QB in LDS, 16-bit: queries row-major (bf16, and fp16
+  // pre-scaled on dims 32..63 for the state scores), dO row-major (bf16), and
+  // transposed (rows = dims of QTP halves, queries of each 32-query sub-block in
+  // kpos order): the queries as hi + lo bf16 pairs and dO
   constexpr int QB = C < kQB ? C : kQB;
-  __shared__ __attribute__((aligned(16))) float Qs[QB * kPX];
-  __shared__ __attribute__((aligned(16))) float Ds[QB * kPX];
+  constexpr int QTP = QB + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Qb[QB * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qh[QB * kTP];
+  __shared__ __attribute__((aligned(16))) uint16_t Dr[QB * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t QTh[64 * QTP];
+  __shared__ __attribute__((aligned(16))) uint16_t QTl[64 * QTP];
+  __shared__ __attribute__((aligned(16))) uint16_t DT[64 * QTP];
   __shared__ float2 LD[QB];
   __shared__ unsigned qmax_bits;
   __shared__ int sIdx[kBwdIdxCap];   // the snapshot's version ids
@@ -796,14 +805,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
     for (int e = tid; e < QB * 16; e += NW * 64) {
       const int qi = e >> 4, c4 = e & 15;
       const int64_t pos = cpos + q0 + qi;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), g = x;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      uint2 g = make_uint2(0u, 0u);
       if (pos < in.N) {
         x = *reinterpret_cast<const float4*>(b.qr32 + ((size_t)s * in.N + pos) * 64 + 4 * c4);
-        g = load4(doin + pos * 64 + 4 * c4);
+        g = *reinterpret_cast<const uint2*>(doin + pos * 64 + 4 * c4);
       }
       if (c4 >= 8) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
-      *reinterpret_cast<float4*>(Qs + qi * kPX + 4 * c4) = x;
-      *reinterpret_cast<float4*>(Ds + qi * kPX + 4 * c4) = g;
+      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = bf16x4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
+      *reinterpret_cast<uint2*>(Dr + qi * kRP + 4 * c4) = g;
+      const int qp = (qi & ~31) + kpos(qi & 31);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+      const uint16_t gv[4] = {(uint16_t)(g.x & 0xFFFFu), (uint16_t)(g.x >> 16), (uint16_t)(g.y & 0xFFFFu),
+                              (uint16_t)(g.y >> 16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16 hi8 = (bf16)xv[t];
+        const bf16 lo8 = (bf16)(xv[t] - (float)hi8);
+        QTh[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, hi8);
+        QTl[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, lo8);
+        DT[(4 * c4 + t) * QTP + qp] = gv[t];
+      }
     }
     atomicMax(&qmax_bits, __float_as_uint(amax));   // non-negative floats order as their bits
     for (int qi = tid; qi < QB; qi += NW * 64) {
@@ -811,9 +833,19 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
       LD[qi] = pos < in.N ? b.lse_d[(size_t)s * in.N + pos] : make_float2(kInf, 0.f);
     }
     __syncthreads();
-    // state scores take the queries in fp16, pre-scaled by 2^-qsh (the same for the block)
+    // state scores take the queries in fp16, pre-scaled by 2^-qsh (the same for
+    // the block; dims 32..63 read again, now that the block maximum is known)
     const int qsh = f16_shift(__uint_as_float(qmax_bits));
     const float qdown = ldexpf(1.f, -qsh), qup = ldexpf(1.f, qsh);
+    for (int e = tid; e < QB * 8; e += NW * 64) {
+      const int qi = e >> 3, c4 = e & 7;
+      const int64_t pos = cpos + q0 + qi;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (pos < in.N) x = *reinterpret_cast<const float4*>(b.qr32 + ((size_t)s * in.N + pos) * 64 + 32 + 4 * c4);
+      *reinterpret_cast<f16x4*>(Qh + qi * kTP + 4 * c4) =
+          f16x4{(f16)(x.x * qdown), (f16)(x.y * qdown), (f16)(x.z * qdown), (f16)(x.w * qdown)};
+    }
+    __syncthreads();
     for (int Tile = w; Tile < n_tiles; Tile += NW) {
       const bool st = Tile < n_st;
       // this wave's keys and values as B operands (step kk: dims 16 kk + 8 h + e)
@@ -854,22 +886,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
       f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
       for (int qs = 0; qs < QB; qs += 32) {
         // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
-        const float* qrow = Qs + (qs + kl) * kPX + 8 * h;
-        const float* drow = Ds + (qs + kl) * kPX + 8 * h;
+        const uint16_t* qrow = Qb + (qs + kl) * kRP + 8 * h;
+        const uint16_t* hrow = Qh + (qs + kl) * kTP + 8 * h;
+        const uint16_t* drow = Dr + (qs + kl) * kRP + 8 * h;
         f32x16 sc = {}, dp = {};
         if (st) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk) sc = mfma_f16(h8_at(qrow + 32 + 16 * kk, qdown), kh[kk], sc);
+          for (int kk = 0; kk < 2; ++kk) sc = mfma_f16(*reinterpret_cast<const f16x8*>(hrow + 16 * kk), kh[kk], sc);
           if (qsh != 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sc[r] *= qup;
           }
         } else {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) sc = mfma_bf16(bf8_at(qrow + 16 * kk), kb[kk], sc);
+          for (int kk = 0; kk < 4; ++kk) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * kk), kb[kk], sc);
         }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(bf8_at(drow + 16 * kk), vb[kk], dp);
+        for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vb[kk], dp);
         f32x16 p, dsc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -886,7 +919,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
         // the sub-block's queries
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          float xa[8], xb[8];
+          float xa[8];
           bf16x8 dh, dl, ph, pl, bh, bl;
 #pragma unroll
           for (int i = 0; i < 8; ++i) xa[i] = dsc[8 * kk + i];
@@ -898,15 +931,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
           for (int half = 0; half < 2; ++half) {
             f32x16& dk = half ? dk1 : dk0;
             f32x16& dv = half ? dv1 : dv0;
+            const int o = (32 * half + kl) * QTP + qs + 16 * kk + 8 * h;
             if (half == 1 || !st) {   // state keys have no gradient on dims 0..31
-#pragma unroll
-              for (int i = 0; i < 8; ++i) xb[i] = Qs[(qs + mrow(8 * kk + i, h)) * kPX + 32 * half + kl];
-              bf8_split(xb, bh, bl);
+              bh = *reinterpret_cast<const bf16x8*>(QTh + o);
+              bl = *reinterpret_cast<const bf16x8*>(QTl + o);
               dk = mfma_bf16(dh, bh, dk);
               dk = mfma_bf16(dh, bl, dk);
               dk = mfma_bf16(dl, bh, dk);
             }
-            const bf16x8 od = bf8_col(Ds, qs, kk, h, 32 * half + kl);
+            const bf16x8 od = *reinterpret_cast<const bf16x8*>(DT + o);
             dv = mfma_bf16(ph, od, dv);
             dv = mfma_bf16(pl, od, dv);
           }
