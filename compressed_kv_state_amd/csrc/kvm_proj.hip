@@ -208,6 +208,11 @@ template <bool OUT>
 __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kGStageBytes];
   __shared__ __attribute__((aligned(16))) uint8_t st1[kGStageBytes];
+  // The accumulators are read only by the epilogue: naming one accumulation
+  // register here lets the compiler keep them there, where the MFMA runs at
+  // its full rate (measured: 34.6 against 42.9 cycles per 32x32x16 MFMA with
+  // the accumulator in ordinary vector registers).
+  asm volatile("" ::: "a0");
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w & 1, wn = w >> 1;   // wave tile: rows wm*128 + [0, 128), columns wn*64 + [0, 64)
@@ -328,8 +333,13 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   //        rowq = (b H N + t) 64, colq = (f/64) N 64 + f%64;
   //        gate logit (b H + hh) N + t = rowg(m) + hh N, rowg = b H N + t;
   //   out: y element m Nout + n.
+  // A wave's 64 columns are 64-aligned, so they lie in one destination part
+  // and, for q/k/v, in one head: the bf16 parts go through LDS (the wave's
+  // 128 x 64 tile, 16-byte units XOR-swizzled by row) and leave as 16-byte
+  // stores of eight consecutive columns; the fp32 gate logits are stored one
+  // by one.
+  __shared__ int64_t rowpart[kGM];
   __syncthreads();   // every wave is done with the stages
-  int64_t* rowpart = reinterpret_cast<int64_t*>(st0);
   if constexpr (!OUT) {
     if (tid < kGM) {
       int64_t m = m0 + tid;
@@ -338,43 +348,60 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
       rowpart[tid] = b * a.H * a.N + t;
     }
   }
-  __syncthreads();
   const int D = a.H * 64;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + 32 * j + l32;
-    if (n >= a.Nout) continue;
-    // the column's destination (in-projection)
-    int part = 3;
-    int64_t col = 0;
-    if constexpr (!OUT) {
-      if (n < 3 * D) {
-        part = n / D;
-        const int f = n % D;
-        col = (int64_t)(f >> 6) * a.N * 64 + (f & 63);
-      } else {
-        col = (int64_t)(n - 3 * D) * a.N;
-      }
-    }
-    bf16* dst = OUT ? reinterpret_cast<bf16*>(a.y)
-                    : reinterpret_cast<bf16*>(part == 0 ? a.q : (part == 1 ? a.k : a.v));
-    const float bias = (!OUT && part == 3 && a.bias) ? a.bias[n - 3 * D] : 0.f;
+  const int nw0 = n0 + wn * 64;                 // the wave's first column
+  const bool gate = !OUT && nw0 >= 3 * D;       // gate-logit columns (fp32)
+  uint8_t* tile = (w < 4 ? st0 : st1) + (w & 3) * (128 * 128);
+  if (!gate) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);   // row in the tile
-        const int64_t m = m0 + rl;
-        if (m >= a.M) continue;
-        const float val = acc[i][j][r];
-        if constexpr (OUT) {
-          dst[m * a.Nout + n] = (bf16)val;
-        } else if (part < 3) {
-          dst[rowpart[rl] * 64 + col] = (bf16)val;
-        } else {
-          a.gl[rowpart[rl] + col] = val + bias;
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3), col = 32 * j + l32;
+          *reinterpret_cast<bf16*>(tile + row * 128 + (((col >> 3) ^ (row & 7)) << 4) + (col & 7) * 2) =
+              (bf16)acc[i][j][r];
         }
+  }
+  __syncthreads();   // row parts (and each wave's own tile) visible
+  if (!gate) {
+    const int part = OUT ? 0 : nw0 / D;
+    bf16* dst = OUT ? reinterpret_cast<bf16*>(a.y)
+                    : reinterpret_cast<bf16*>(part == 0 ? a.q : (part == 1 ? a.k : a.v));
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int row = 8 * it + (lane >> 3), u = lane & 7;
+      const int rl = wm * 128 + row;
+      const int64_t m = m0 + rl;
+      const int n = nw0 + 8 * u;
+      if (m >= a.M || n >= a.Nout) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + row * 128 + ((u ^ (row & 7)) << 4));
+      int64_t off;
+      if constexpr (OUT) {
+        off = m * a.Nout + n;
+      } else {
+        const int f = n - part * D;
+        off = rowpart[rl] * 64 + (int64_t)(f >> 6) * a.N * 64 + (f & 63);
       }
+      *reinterpret_cast<uint4*>(dst + off) = v;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = nw0 + 32 * j + l32;
+      if (n >= a.Nout) continue;
+      const int64_t col = (int64_t)(n - 3 * D) * a.N;
+      const float bv = a.bias ? a.bias[n - 3 * D] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m0 + rl >= a.M) continue;
+          a.gl[rowpart[rl] + col] = acc[i][j][r] + bv;
+        }
+    }
   }
 }
 
