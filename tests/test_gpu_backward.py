@@ -111,6 +111,17 @@ def test_backward_variants(dtype, variant):
         check_seq(w, inp, s, d_out, grads, slot, kind, variant)
 
 
+def test_backward_state_past_lds_index_cap():
+    """bf16 path with snapshots of more than 4096 rows: the attention-backward kernels then read
+    the snapshot's version ids from global memory instead of their LDS copy."""
+    w = small("bf16", chunk=128, window=256, n_tokens=4819, heads=1, sched="fixed", max_slots=4400)
+    print("case: backward, snapshots past 4096 rows", flush=True)
+    inp = make_inputs(w)
+    st, d_out, grads, slot, kind, _ = run_backward(w, inp)
+    assert int((slot[0] >= 4096).sum()) > 0   # rows past the cap exist and are used
+    check_seq(w, inp, 0, d_out, grads, slot, kind, "past idx cap")
+
+
 @pytest.mark.parametrize("n", [1, 70, 200])
 def test_backward_short_inputs(n):
     w = small("f32", n_tokens=n, heads=2)
