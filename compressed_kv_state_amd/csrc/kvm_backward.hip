@@ -1052,6 +1052,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     int64_t off;
     float gk, gv, xh, rho, vh, invn;
     float2 nm;
+    int ver;
     bool live;
   };
   auto fetch = [&](int j) {
@@ -1062,6 +1063,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     x.off = (int64_t)sc.w + i;                    // inside the index lists either way
     const int64_t v0 = idx[x.off];
     const int64_t ver = x.live ? v0 : 0;
+    x.ver = (int)ver;
     const float* e = part + x.off * 96;
     x.gk = e[l & 31];
     x.gv = e[32 + l];
@@ -1077,8 +1079,11 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     return x;
   };
   // one snapshot's contribution, added to the running totals (later snapshots
-  // first) and stored as the row's total gradient at that snapshot
-  auto step = [&](const In& cur) {
+  // first).  The row's total at snapshot j is read back only by the token
+  // that created or merged into the row in chunk j, so it is stored only
+  // where chunk j touched the row (a new version, or a new row): `prev` is
+  // the row at snapshot j - 1.
+  auto step = [&](const In& cur, const In& prev) {
     // LayerNorm backward over the 32 live dims (lanes 0..31; lanes 32..63 carry zeros)
     float sg = cur.gk, sgx = cur.gk * cur.xh;
 #pragma unroll
@@ -1102,10 +1107,12 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     tk += dK;
     tv += dV;
     tr += dR;
-    float* e = part + cur.off * 96;
-    if (l < 32) e[l] = tk;
-    e[32 + l] = tv;
-    if (l == 0) trho[cur.off] = tr;
+    if (!prev.live || prev.ver != cur.ver) {
+      float* e = part + cur.off * 96;
+      if (l < 32) e[l] = tk;
+      e[32 + l] = tv;
+      if (l == 0) trho[cur.off] = tr;
+    }
   };
   const int J = b.absorbed - 1;
   In a0 = fetch(J), a1 = fetch(J - 1), a2 = fetch(J - 2), a3 = fetch(J - 3);
@@ -1113,16 +1120,16 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     // (a row exists from its creating chunk on, so the first snapshot without
     // it ends the sweep)
     if (!a0.live) break;
-    step(a0);
+    step(a0, a1);
     a0 = fetch(j - 4);
     if (!a1.live) break;
-    step(a1);
+    step(a1, a2);
     a1 = fetch(j - 5);
     if (!a2.live) break;
-    step(a2);
+    step(a2, a3);
     a2 = fetch(j - 6);
     if (!a3.live) break;
-    step(a3);
+    step(a3, a0);
     a3 = fetch(j - 7);
   }
 }
