@@ -1044,10 +1044,25 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   float* part = b.part_state + (size_t)s * m.idx_total * 96;
   float* trho = b.tot_rho + (size_t)s * m.idx_total;
   float tk = 0.f, tv = 0.f, tr = 0.f;
-  // The inputs of snapshot j are loaded four snapshots ahead of their use.
-  // Every fetch issues the same loads (at a valid index when the snapshot or
-  // the row does not exist), so that the compiler's count of loads in flight
-  // stays exact and each use waits for its own loads only.
+  // The row's version id at snapshot j is loaded eight snapshots ahead of its
+  // use and the version's inputs four ahead, so that neither waits on the
+  // other.  Every fetch issues the same loads (at a valid index when the
+  // snapshot or the row does not exist), so that the compiler's count of
+  // loads in flight stays exact and each use waits for its own loads only.
+  struct Id {
+    int64_t off;
+    int v0;
+    bool live;
+  };
+  auto fetch_id = [&](int j) {
+    Id x;
+    const int jc = j < 0 ? 0 : j;
+    const int4 sc = d.sched[jc];
+    x.live = j >= 0 && i < sc.x + sc.y + sc.z;   // the row exists after chunk j
+    x.off = (int64_t)sc.w + i;                    // inside the index lists either way
+    x.v0 = idx[x.off];
+    return x;
+  };
   struct In {
     int64_t off;
     float gk, gv, xh, rho, vh, invn;
@@ -1055,14 +1070,11 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     int ver;
     bool live;
   };
-  auto fetch = [&](int j) {
+  auto fetch = [&](const Id& id) {
     In x;
-    const int jc = j < 0 ? 0 : j;
-    const int4 sc = d.sched[jc];
-    x.live = j >= 0 && i < sc.x + sc.y + sc.z;   // the row exists after chunk j
-    x.off = (int64_t)sc.w + i;                    // inside the index lists either way
-    const int64_t v0 = idx[x.off];
-    const int64_t ver = x.live ? v0 : 0;
+    x.live = id.live;
+    x.off = id.off;
+    const int64_t ver = id.live ? id.v0 : 0;
     x.ver = (int)ver;
     const float* e = part + x.off * 96;
     x.gk = e[l & 31];
@@ -1115,22 +1127,27 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     }
   };
   const int J = b.absorbed - 1;
-  In a0 = fetch(J), a1 = fetch(J - 1), a2 = fetch(J - 2), a3 = fetch(J - 3);
+  Id b0 = fetch_id(J - 4), b1 = fetch_id(J - 5), b2 = fetch_id(J - 6), b3 = fetch_id(J - 7);
+  In a0 = fetch(fetch_id(J)), a1 = fetch(fetch_id(J - 1)), a2 = fetch(fetch_id(J - 2)), a3 = fetch(fetch_id(J - 3));
   for (int j = J; j >= 0; j -= 4) {
     // (a row exists from its creating chunk on, so the first snapshot without
     // it ends the sweep)
     if (!a0.live) break;
     step(a0, a1);
-    a0 = fetch(j - 4);
+    a0 = fetch(b0);
+    b0 = fetch_id(j - 8);
     if (!a1.live) break;
     step(a1, a2);
-    a1 = fetch(j - 5);
+    a1 = fetch(b1);
+    b1 = fetch_id(j - 9);
     if (!a2.live) break;
     step(a2, a3);
-    a2 = fetch(j - 6);
+    a2 = fetch(b2);
+    b2 = fetch_id(j - 10);
     if (!a3.live) break;
     step(a3, a0);
-    a3 = fetch(j - 7);
+    a3 = fetch(b3);
+    b3 = fetch_id(j - 11);
   }
 }
 
