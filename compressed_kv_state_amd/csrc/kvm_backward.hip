@@ -755,8 +755,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   }
 }
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+// NV waves (two per SIMD where the registers allow) share the block's key tiles
+template <int NW, int NV>
+__global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
   // query blocks of QB in LDS, 16-bit: queries row-major (bf16, and fp16
   // pre-scaled on dims 32..63 for the state scores), dO row-major (bf16), and
@@ -788,7 +789,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
   }
   const int* idxl = d.idx + (size_t)s * m.idx_total + ioff;
   const int n_st = (S + 31) >> 5;
-  for (int i = tid; i < S && i < kBwdIdxCap; i += NW * 64) sIdx[i] = idxl[i];
+  for (int i = tid; i < S && i < kBwdIdxCap; i += NV * 64) sIdx[i] = idxl[i];
   const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
   const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
   const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
     if (tid == 0) qmax_bits = 0u;
     __syncthreads();
     float amax = 0.f;
-    for (int e = tid; e < QB * 16; e += NW * 64) {
+    for (int e = tid; e < QB * 16; e += NV * 64) {
       const int qi = e >> 4, c4 = e & 15;
       const int64_t pos = cpos + q0 + qi;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -828,7 +829,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
       }
     }
     atomicMax(&qmax_bits, __float_as_uint(amax));   // non-negative floats order as their bits
-    for (int qi = tid; qi < QB; qi += NW * 64) {
+    for (int qi = tid; qi < QB; qi += NV * 64) {
       const int64_t pos = cpos + q0 + qi;
       LD[qi] = pos < in.N ? b.lse_d[(size_t)s * in.N + pos] : make_float2(kInf, 0.f);
     }
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
     // the block; dims 32..63 read again, now that the block maximum is known)
     const int qsh = f16_shift(__uint_as_float(qmax_bits));
     const float qdown = ldexpf(1.f, -qsh), qup = ldexpf(1.f, qsh);
-    for (int e = tid; e < QB * 8; e += NW * 64) {
+    for (int e = tid; e < QB * 8; e += NV * 64) {
       const int qi = e >> 3, c4 = e & 7;
       const int64_t pos = cpos + q0 + qi;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -846,7 +847,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
           f16x4{(f16)(x.x * qdown), (f16)(x.y * qdown), (f16)(x.z * qdown), (f16)(x.w * qdown)};
     }
     __syncthreads();
-    for (int Tile = w; Tile < n_tiles; Tile += NW) {
+    for (int Tile = w; Tile < n_tiles; Tile += NV) {
       const bool st = Tile < n_st;
       // this wave's keys and values as B operands (step kk: dims 16 kk + 8 h + e)
       bf16x8 kb[4], vb[4];
@@ -1210,7 +1211,8 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
     constexpr int NW = decltype(nw)::value;
     if constexpr (std::is_same<T, bf16>::value) {
       bwd_q_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
-      bwd_kv_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
+      constexpr int NV = NW < 8 ? 2 * NW : NW;
+      bwd_kv_mx_kernel<NW, NV><<<grid, NV * 64, 0, st>>>(m, d, in, b);
     } else {
       bwd_q_kernel<T, NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
       bwd_kv_kernel<T, NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
