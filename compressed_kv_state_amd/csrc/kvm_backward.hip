@@ -481,6 +481,13 @@ __device__ __forceinline__ void bf8_split(const float (&x)[8], bf16x8& hi, bf16x
     lo[i] = (bf16)(x[i] - (float)hi[i]);
   }
 }
+// 16-byte unit swizzle of a 128-byte tile row read by ds_read_b64_tr_b16: the
+// 16 lanes of one LDS cycle read four consecutive rows two units each, so rows
+// 0..3 (and 4..7) take disjoint unit pairs
+__device__ __forceinline__ int tr_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ bf16x4 tr_read(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
 // power-of-two pre-scale exponent keeping values of magnitude < 2^14 * 2^qsh in fp16
 __device__ __forceinline__ int f16_shift(float amax) {
   if (!(amax >= 16384.f)) return 0;
@@ -495,12 +502,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   constexpr int NT = NW * 64;
   // tile in LDS, 16-bit: keys row-major (fp16 for a state tile, bf16 for a
   // window tile; rows of kRP halves), values row-major (bf16), and the keys
-  // transposed as hi + lo bf16 pairs (rows = dims of kTP halves, keys in the
-  // order kpos that puts each lane half's eight contraction rows side by side)
+  // again as hi + lo bf16 pairs in 128-byte rows with their 16-byte units
+  // swizzled (tr_swz), read transposed by ds_read_b64_tr_b16 as the B operand
+  // of dq = dS . K (keys along the contraction)
   __shared__ __attribute__((aligned(16))) uint16_t Kr[32 * kRP];
   __shared__ __attribute__((aligned(16))) uint16_t Vr[32 * kRP];
-  __shared__ __attribute__((aligned(16))) uint16_t KTh[64 * kTP];
-  __shared__ __attribute__((aligned(16))) uint16_t KTl[64 * kTP];
+  __shared__ __attribute__((aligned(16))) uint8_t Kh[32 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Kl[32 * 128];
   __shared__ int sIdx[kBwdIdxCap];   // the snapshot's version ids (one load round trip per tile, not two)
   const int s = blockIdx.x % m.BH;
   const int c = blockIdx.x / m.BH;
@@ -629,15 +637,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
         *reinterpret_cast<bf16x4*>(Kr + key * kRP + 4 * c4) = bf16x4{(bf16)kx[0], (bf16)kx[1], (bf16)kx[2], (bf16)kx[3]};
       }
       *reinterpret_cast<uint2*>(Vr + key * kRP + 4 * c4) = ok ? rv[it] : make_uint2(0u, 0u);
-      const int kp = kpos(key);
+      bf16x4 h4, l4;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const bf16 hi8 = (bf16)kx[t];
-        const bf16 lo8 = (bf16)(kx[t] - (float)hi8);
-        KTh[(4 * c4 + t) * kTP + kp] = __builtin_bit_cast(uint16_t, hi8);
-        KTl[(4 * c4 + t) * kTP + kp] = __builtin_bit_cast(uint16_t, lo8);
+        h4[t] = (bf16)kx[t];
+        l4[t] = (bf16)(kx[t] - (float)h4[t]);
       }
+      const int o = key * 128 + 16 * ((c4 >> 1) ^ tr_swz(key)) + 8 * (c4 & 1);
+      *reinterpret_cast<bf16x4*>(Kh + o) = h4;
+      *reinterpret_cast<bf16x4*>(Kl + o) = l4;
     }
+  };
+  // B operand of dq at step kk: lane group g = lane / 16 reads keys
+  // 16 kk + 4 h + (lane % 16) / 4 (and + 8) at dims 32 half + 16 (g % 2) + 4 (lane % 4);
+  // the transposed read hands lane l dim 32 half + l % 32 of those keys
+  int toff[2];
+  {
+    const int g = lane >> 4, pl = lane & 15;
+    const int kq = 4 * h + (pl >> 2);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int d0 = 32 * half + 16 * (g & 1) + 4 * (pl & 3);
+      toff[half] = kq * 128 + 16 * ((d0 >> 3) ^ tr_swz(kq)) + 8 * ((d0 >> 2) & 1);
+    }
+  }
+  auto kfrag = [&](const uint8_t* T, int kk, int half) __attribute__((always_inline)) {
+    const uint8_t* base = T + 16 * kk * 128 + toff[half];
+    const bf16x4 a = tr_read(base), c = tr_read(base + 8 * 128);
+    return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
   };
   auto scores = [&](int Tile) {
     f32x16 acc = {};
@@ -728,9 +755,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if (half == 0 && Tile < n_st) continue;   // state keys are zero on dims 0..31
-        const int o = (32 * half + ql) * kTP + 16 * kk + 8 * h;
-        bh = *reinterpret_cast<const bf16x8*>(KTh + o);
-        bl = *reinterpret_cast<const bf16x8*>(KTl + o);
+        bh = kfrag(Kh, kk, half);
+        bl = kfrag(Kl, kk, half);
         f32x16& acc = half ? dq1 : dq0;
         acc = mfma_bf16(ah, bh, acc);
         acc = mfma_bf16(ah, bl, acc);
