@@ -666,6 +666,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
     const bf16x4 a = tr_read(base), c = tr_read(base + 8 * 128);
     return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
   };
+  // Masks are needed only on a tile that holds rows past the state's end, keys
+  // past the window's end or after one of the wave's queries, or when some of
+  // the wave's queries are past the end (all wave-uniform)
+  const bool wave_q_all = __ballot(!qvalid) == 0ull;
+  const int64_t wq0 = cpos + 32 * w;
+  auto tile_masked = [&](int Tile) {
+    if (!wave_q_all) return true;
+    if (Tile < n_st) return Tile * 32 + 32 > S;
+    const int64_t last = lo + (int64_t)(Tile - n_st) * 32 + 31;
+    return last >= hi || last > wq0;
+  };
   auto scores = [&](int Tile) {
     f32x16 acc = {};
     const uint16_t* kr = Kr + ql * kRP + 8 * h;
@@ -681,9 +692,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(kr + 16 * kk), qb[kk], acc);
     }
+    if (tile_masked(Tile)) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (!bwd_valid(Tile, n_st, S, lo, hi, mrow(r, h), qp, qvalid)) acc[r] = -kInf;
+      for (int r = 0; r < 16; ++r)
+        if (!bwd_valid(Tile, n_st, S, lo, hi, mrow(r, h), qp, qvalid)) acc[r] = -kInf;
+    }
     return acc;
   };
   auto dscores = [&]() {
@@ -714,7 +727,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
       ds *= al;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = a[r] == -kInf ? 0.f : exp2_fast(a[r] - mn);
+        const float p = exp2_fast(a[r] - mn);   // (0 for a masked score: mn is finite here)
         ls += p;
         ds = fmaf(p, dp[r], ds);
       }
@@ -726,6 +739,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
   const float lse = mx + log2f(ls);
   const float Dq = ds / ls;
   if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
+  // (a query past the end has no valid score: its weights come out 0, not NaN)
+  const float lse_u = qvalid ? lse : kInf, Dq_u = qvalid ? Dq : 0.f;
   // sweep 2: dq += dS . K
   f32x16 dq0 = {}, dq1 = {};
   if (n_tiles > 0) prefetch(0);
@@ -739,8 +754,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
     f32x16 dsc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = a[r] == -kInf ? 0.f : exp2_fast(a[r] - lse);
-      dsc[r] = p * (dp[r] - Dq);
+      const float p = exp2_fast(a[r] - lse_u);
+      dsc[r] = p * (dp[r] - Dq_u);
     }
     // dq = sum_j dS_j k_j has sum_j dS_j = 0, so a common offset of the keys
     // cancels in it; bf16 rounding of dS or of the keys would not cancel, so
@@ -880,6 +895,7 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
       f16x8 kh[2];
       int64_t kpos = 0;
       bool kvalid;
+      const int64_t klast = lo + (int64_t)(Tile - n_st) * 32 + 31;   // (window tiles) the tile's last key
       // (16-byte loads: eight consecutive dims per step and lane half; rows
       // past the end read a valid row and are zeroed)
       if (st) {
@@ -930,16 +946,30 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vb[kk], dp);
+        // (a query past the end has lse = +inf, so its weights come out 0; the
+        // mask is needed only on a ragged tile or one with keys after some of
+        // the sub-block's queries: wave-uniform)
         f32x16 p, dsc;
+        const bool need = st ? Tile * 32 + 32 > S : klast >= hi || klast > cpos + q0 + qs;
+        if (need) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qs + mrow(r, h);
-          const int64_t qpos = cpos + q0 + qi;
-          const float2 ld = LD[qi];
-          const bool ok = kvalid && qpos < in.N && (st || kpos <= qpos);
-          const float pr = ok ? exp2_fast(sc[r] * c2 - ld.x) : 0.f;
-          p[r] = pr;
-          dsc[r] = pr * (dp[r] - ld.y);
+          for (int r = 0; r < 16; ++r) {
+            const int qi = qs + mrow(r, h);
+            const int64_t qpos = cpos + q0 + qi;
+            const float2 ld = LD[qi];
+            const bool ok = kvalid && (st || kpos <= qpos);
+            const float pr = ok ? exp2_fast(sc[r] * c2 - ld.x) : 0.f;
+            p[r] = pr;
+            dsc[r] = pr * (dp[r] - ld.y);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float2 ld = LD[qs + mrow(r, h)];
+            const float pr = exp2_fast(sc[r] * c2 - ld.x);
+            p[r] = pr;
+            dsc[r] = pr * (dp[r] - ld.y);
+          }
         }
         // dk[key][d] += dS^T . Q (dS and Q as hi + lo pairs, three products) and
         // dv[key][e] += P^T . dO (P as a hi + lo pair, dO exact in bf16) over
