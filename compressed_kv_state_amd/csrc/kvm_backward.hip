@@ -497,7 +497,7 @@ __device__ __forceinline__ int f16_shift(float amax) {
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
   constexpr int NT = NW * 64;
   // tile in LDS, 16-bit: keys row-major (fp16 for a state tile, bf16 for a
@@ -706,8 +706,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
     for (int kk = 0; kk < 4; ++kk) acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(vr + 16 * kk), db[kk], acc);
     return acc;
   };
-  // sweep 1: the row maximum, row sum and D = sum_j P_j dP_j, online
-  float mx = -kInf, ls = 0.f, ds = 0.f;
+  // One sweep over the key tiles, online.  With weights e_j = 2^(s_j - m)
+  // against a per-query reference m (moved only when a tile's maximum passes
+  // it by more than 8, i.e. weights stay below 2^8; the sums are rescaled
+  // then), it gathers l = sum e_j, t = sum e_j dP_j, A = sum e_j dP_j k_j and
+  // B = sum e_j k_j.  Then P_j = e_j / l, D = t / l, and
+  // dq = sum_j P_j (dP_j - D) k_j = (A - D B) / l.  A common offset of the
+  // keys cancels in A - D B (as it does in sum_j dS_j k_j, whose dS sum to
+  // 0), so the weights and the keys go in as hi + lo bf16 pairs (three
+  // products each, to ~2^-16), not rounded once to bf16.
+  float mref = -kInf, ls = 0.f, ds = 0.f;
+  f32x16 A0 = {}, A1 = {}, B0 = {}, B1 = {};
   if (n_tiles > 0) prefetch(0);
   for (int Tile = 0; Tile < n_tiles; ++Tile) {
     __syncthreads();
@@ -720,64 +729,71 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_mx_kernel(Dims m, Dev d, BwdIn 
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, a[r]);
     mt = fmaxf(mt, partner_f(mt));
-    const float mn = fmaxf(mx, mt);
-    if (mn != -kInf) {
-      const float al = mx == -kInf ? 0.f : exp2_fast(mx - mn);
+    const bool up = mt > mref + 8.f;   // (the first finite maximum sets the reference)
+    if (__ballot(up) != 0ull) {
+      const float mn = up ? mt : mref;
+      const float al = mref == -kInf ? 0.f : exp2_fast(mref - mn);
       ls *= al;
       ds *= al;
+      // register r holds query mrow(r, h), whose factor sits in lane mrow(r, h)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(a[r] - mn);   // (0 for a masked score: mn is finite here)
-        ls += p;
-        ds = fmaf(p, dp[r], ds);
+        const float ar = __shfl(al, mrow(r, h));
+        A0[r] *= ar;
+        A1[r] *= ar;
+        B0[r] *= ar;
+        B1[r] *= ar;
       }
-      mx = mn;
+      mref = mn;
+    }
+    const float mb = mref == -kInf ? 0.f : mref;   // (no valid score yet: the weights are 0)
+    f32x16 e, wgt;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = exp2_fast(a[r] - mb);   // (0 for a masked score)
+      ls += e[r];
+      ds = fmaf(e[r], dp[r], ds);
+      wgt[r] = e[r] * dp[r];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float xe[8], xw[8];
+      bf16x8 eh, el, wh, wl;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xe[i] = e[8 * kk + i];
+        xw[i] = wgt[8 * kk + i];
+      }
+      bf8_split(xe, eh, el);
+      bf8_split(xw, wh, wl);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half == 0 && Tile < n_st) continue;   // state keys are zero on dims 0..31
+        const bf16x8 bh = kfrag(Kh, kk, half), bl = kfrag(Kl, kk, half);
+        f32x16& Aa = half ? A1 : A0;
+        f32x16& Bb = half ? B1 : B0;
+        Aa = mfma_bf16(wh, bh, Aa);
+        Aa = mfma_bf16(wh, bl, Aa);
+        Aa = mfma_bf16(wl, bh, Aa);
+        Bb = mfma_bf16(eh, bh, Bb);
+        Bb = mfma_bf16(eh, bl, Bb);
+        Bb = mfma_bf16(el, bh, Bb);
+      }
     }
   }
   ls += partner_f(ls);
   ds += partner_f(ds);
-  const float lse = mx + log2f(ls);
+  const float lse = mref + log2f(ls);
   const float Dq = ds / ls;
   if (qvalid && h == 0) b.lse_d[(size_t)s * in.N + qp] = make_float2(lse, Dq);
-  // (a query past the end has no valid score: its weights come out 0, not NaN)
-  const float lse_u = qvalid ? lse : kInf, Dq_u = qvalid ? Dq : 0.f;
-  // sweep 2: dq += dS . K
-  f32x16 dq0 = {}, dq1 = {};
-  if (n_tiles > 0) prefetch(0);
-  for (int Tile = 0; Tile < n_tiles; ++Tile) {
-    __syncthreads();
-    store_tile(Tile);
-    __syncthreads();
-    if (Tile + 1 < n_tiles) prefetch(Tile + 1);
-    const f32x16 a = scores(Tile);
-    const f32x16 dp = dscores();
-    f32x16 dsc;
+  // (a query past the end has no valid score and no stored gradient)
+  const float il = qvalid ? 1.f / ls : 0.f, Du = qvalid ? Dq : 0.f;
+  f32x16 dq0, dq1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(a[r] - lse_u);
-      dsc[r] = p * (dp[r] - Dq_u);
-    }
-    // dq = sum_j dS_j k_j has sum_j dS_j = 0, so a common offset of the keys
-    // cancels in it; bf16 rounding of dS or of the keys would not cancel, so
-    // both operands go in as hi + lo pairs (three products, to ~2^-16)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float xa[8];
-      bf16x8 ah, al, bh, bl;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xa[i] = dsc[8 * kk + i];
-      bf8_split(xa, ah, al);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (half == 0 && Tile < n_st) continue;   // state keys are zero on dims 0..31
-        bh = kfrag(Kh, kk, half);
-        bl = kfrag(Kl, kk, half);
-        f32x16& acc = half ? dq1 : dq0;
-        acc = mfma_bf16(ah, bh, acc);
-        acc = mfma_bf16(ah, bl, acc);
-        acc = mfma_bf16(al, bh, acc);
-      }
-    }
+  for (int r = 0; r < 16; ++r) {
+    const float dr = __shfl(Du, mrow(r, h)), ir = __shfl(il, mrow(r, h));
+    dq0[r] = fmaf(-dr, B0[r], A0[r]) * ir;
+    dq1[r] = fmaf(-dr, B1[r], A1[r]) * ir;
   }
   // dq rows are queries (register r: query row(r, h)), lane column = dim; RoPE transposed
   float* dqo = b.dq + (size_t)s * in.N * 64;
