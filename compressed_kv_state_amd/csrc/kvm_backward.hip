@@ -1101,6 +1101,32 @@ __global__ __launch_bounds__(256) void bwd_win_kernel(Dims m, Dev d, BwdIn in, B
 // replace the partial in place: afterwards entry (j, i) holds the gradient of
 // row i's sums as they stood after chunk j.  One wave per row; lane = dim.
 // ---------------------------------------------------------------------------
+// Sums across lanes without LDS round trips, every lane receiving the sum (the
+// same bits in every lane): DPP quad swaps and row mirrors within 16 lanes,
+// then the row-pair and half-wave swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_sum16(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror: the other quad of the 8
+  v += dpp_f<0x140>(v);   // row_mirror: the other 8 of the row
+  return v;
+}
+// sum over the lane's 32-lane half
+__device__ __forceinline__ float lane_sum32(float v) {
+  v = lane_sum16(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane_sum64(float v) {
+  v = lane_sum32(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, int rows_last) {
   using RT = typename Rd<T>::type;
@@ -1170,12 +1196,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   // the row at snapshot j - 1.
   auto step = [&](const In& cur, const In& prev) {
     // LayerNorm backward over the 32 live dims (lanes 0..31; lanes 32..63 carry zeros)
-    float sg = cur.gk, sgx = cur.gk * cur.xh;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      sg += __shfl_xor(sg, o);
-      sgx += __shfl_xor(sgx, o);
-    }
+    const float sg = lane_sum32(cur.gk), sgx = lane_sum32(cur.gk * cur.xh);
     const float dK =
         l < 32 ? cur.nm.x * (cur.gk - sg * (1.0f / 32.0f) - cur.xh * sgx * (1.0f / 32.0f)) * cur.invn : 0.f;
     float dV, dR = 0.f;
@@ -1183,9 +1204,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
       dV = cur.gv * cur.invn;
     } else {
       const float u = cur.rho > 0.f ? cur.vh / cur.rho : 0.f;
-      float ug = u * cur.gv;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) ug += __shfl_xor(ug, o);
+      const float ug = lane_sum64(u * cur.gv);
       dV = cur.nm.y * (cur.gv - u * ug);
       dR = ug;
     }
