@@ -100,25 +100,46 @@ __device__ void bwd_stage(float* Kt, float* Vt, int Tile, int n_st, int S, const
 
 // Rotated queries and keys of every position, fp32 (RoPE at the position,
 // [KVM summary, Core mechanisms 4]): read by the tiles of several query
-// chunks, so rotated once.  One wave per position, lane = dim.
+// chunks, so rotated once.  Eight threads per position, eight dims each (a
+// thread on the rotary dims also reads its partner's eight, 16 dims away).
+__device__ __forceinline__ void load8f(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), c = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = c.x; x[5] = c.y; x[6] = c.z; x[7] = c.w;
+}
+__device__ __forceinline__ void load8f(const bf16* p, float (&x)[8]) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_rot_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   const int s = blockIdx.y;
-  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int dd = threadIdx.x & 63;
+  const int64_t pos = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int t8 = threadIdx.x & 7;
   if (pos >= in.N) return;
   const size_t r = ((size_t)s * in.N + pos) * 64;
-  const T* qr = reinterpret_cast<const T*>(in.q) + r;
-  const T* kr = reinterpret_cast<const T*>(in.k) + r;
-  float x = tof(qr[dd]), y = tof(kr[dd]);
-  if (dd < 32) {
-    const int jf = dd & 15;
-    const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
-    x = dd < 16 ? x * cs - tof(qr[dd + 16]) * sn : x * cs + tof(qr[dd - 16]) * sn;
-    y = dd < 16 ? y * cs - tof(kr[dd + 16]) * sn : y * cs + tof(kr[dd - 16]) * sn;
+  const int d0 = 8 * t8;
+  float cs[8], sn[8];
+  if (t8 < 4) {
+    load8f(d.rope_cos + pos * 16 + (d0 & 15), cs);
+    load8f(d.rope_sin + pos * 16 + (d0 & 15), sn);
   }
-  b.qr32[r + dd] = x;
-  b.kr32[r + dd] = y;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const T* src = reinterpret_cast<const T*>(which ? in.k : in.q) + r;
+    float x[8];
+    load8f(src + d0, x);
+    if (t8 < 4) {   // pairs (j, j + 16) of the rotary dims: x' = x cos - x[j+16] sin, x[j+16]' = x[j+16] cos + x sin
+      float y[8];
+      load8f(src + (d0 ^ 16), y);
+      const float sg = t8 < 2 ? -1.f : 1.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fmaf(sg * y[e], sn[e], x[e] * cs[e]);
+    }
+    float* dst = (which ? b.kr32 : b.qr32) + r + d0;
+    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
 }
 
 // Tile validity of score element (key row kr of the tile, query at position qp).
@@ -1276,16 +1297,12 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims m, Dev d, BwdIn in,
   if (kind == 2) {   // merge
     const float lg = in.l[ti];
     const float g = m.no_gate ? 1.f : 1.f / (1.f + __expf(-lg));
-    float dg = kt * tk + vt * tv;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) dg += __shfl_xor(dg, o);
+    const float dg = lane_sum64(kt * tk + vt * tv);
     if (l < 32) dk[32 + l] += g * tk;
     dv[l] += g * tv;
     if (l == 0) dl[t] = m.no_gate ? 0.f : dg * g * (1.f - g);
   } else {           // sink or append: the row's creator
-    float v2 = vt * vt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v2 += __shfl_xor(v2, o);
+    const float v2 = lane_sum64(vt * vt);
     const float tr = b.tot_rho[off];
     const float nv = sqrtf(v2);
     if (l < 32) dk[32 + l] += tk;
@@ -1297,7 +1314,7 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims m, Dev d, BwdIn in,
 template <typename T>
 hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last, hipStream_t st) {
   const dim3 grid((unsigned)(m.BH * b.nq));
-  bwd_rot_kernel<T><<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  bwd_rot_kernel<T><<<dim3((unsigned)((in.N + 31) / 32), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   auto attn = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
     if constexpr (std::is_same<T, bf16>::value) {
