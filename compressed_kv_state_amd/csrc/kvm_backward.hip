@@ -1084,33 +1084,43 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
 // ---------------------------------------------------------------------------
 // Window keys: the partials of every chunk whose window holds position p (in
 // chunk order), RoPE transposed on dims 0..31.  Writes dk and dv of every
-// position (the state path adds to them later).  One wave per position, lane =
-// dim.
+// position (the state path adds to them later).  Sixteen threads per
+// position, eight of the 128 partial columns each (dk 0..63, dv 64..127).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_win_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   const int s = blockIdx.y;
-  const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int dd = threadIdx.x & 63;
-  if (pos >= in.N) return;
+  const int64_t p0 = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  const bool valid = p0 < in.N;
+  const int64_t pos = valid ? p0 : in.N - 1;   // (every lane stays for the exchange below)
   const int64_t c0 = pos / m.C;
   int64_t c1 = (pos + m.W) / m.C;
   if (c1 > b.nq - 1) c1 = b.nq - 1;
-  float gk = 0.f, gv = 0.f;
+  float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int64_t c = c0; c <= c1; ++c) {
     const int64_t off = pos - (c * m.C - m.W);
-    const float* src = b.part_win + (((size_t)s * b.nq + c) * m.R + off) * 128;
-    gk += src[dd];
-    gv += src[64 + dd];
+    const float* src = b.part_win + (((size_t)s * b.nq + c) * m.R + off) * 128 + 8 * t;
+    const float4 a = *reinterpret_cast<const float4*>(src), e = *reinterpret_cast<const float4*>(src + 4);
+    g[0] += a.x; g[1] += a.y; g[2] += a.z; g[3] += a.w;
+    g[4] += e.x; g[5] += e.y; g[6] += e.z; g[7] += e.w;
   }
-  const float gp = __shfl_xor(gk, 16);
-  float x = gk;
-  if (dd < 32) {
-    const int jf = dd & 15;
-    const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
-    x = dd < 16 ? gk * cs + gp * sn : gk * cs - gp * sn;
+  // rotary dims (t < 4): the partner 16 dims away is thread t ^ 2 (a quad swap)
+  float gp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gp[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(g[e]), 0x4E, 0xF, 0xF, false));
+  if (t < 4) {
+    const float* cs = d.rope_cos + pos * 16 + ((8 * t) & 15);
+    const float* sn = d.rope_sin + pos * 16 + ((8 * t) & 15);
+    const float sg = t < 2 ? 1.f : -1.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = fmaf(sg * gp[e], sn[e], g[e] * cs[e]);
   }
-  b.dk[((size_t)s * in.N + pos) * 64 + dd] = x;
-  b.dv[((size_t)s * in.N + pos) * 64 + dd] = gv;
+  if (valid) {
+    float* dst = t < 8 ? b.dk + ((size_t)s * in.N + pos) * 64 + 8 * t : b.dv + ((size_t)s * in.N + pos) * 64 + 8 * (t - 8);
+    *reinterpret_cast<float4*>(dst) = make_float4(g[0], g[1], g[2], g[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(g[4], g[5], g[6], g[7]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1335,7 +1345,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_win_kernel<<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  bwd_win_kernel<<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   if (rows_last > 0)
     bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
   bwd_token_kernel<T><<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
