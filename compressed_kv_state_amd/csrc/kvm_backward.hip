@@ -1184,12 +1184,28 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     int v0;
     bool live;
   };
+  // The schedule, 64 chunks at a time in the wave's lanes (lane l: chunk
+  // sb - l), read out with readlane: a load of the entry per snapshot would
+  // sit between the loads in flight and their uses, and waiting for it would
+  // wait for all of them.
+  const int J = b.absorbed - 1;
+  int sb = J, sS = 0, sW = 0;
+  auto load_sched = [&](int top) {
+    sb = top;
+    const int jl = top - l;
+    const int4 sc = d.sched[jl >= 0 ? jl : 0];
+    sS = sc.x + sc.y + sc.z;
+    sW = sc.w;
+  };
+  load_sched(J);
   auto fetch_id = [&](int j) {
     Id x;
     const int jc = j < 0 ? 0 : j;
-    const int4 sc = d.sched[jc];
-    x.live = j >= 0 && i < sc.x + sc.y + sc.z;   // the row exists after chunk j
-    x.off = (int64_t)sc.w + i;                    // inside the index lists either way
+    if (jc < sb - 63) load_sched(jc);   // (snapshots are visited in decreasing order)
+    const int li = sb - jc;
+    const int S = __builtin_amdgcn_readlane(sS, li), W = __builtin_amdgcn_readlane(sW, li);
+    x.live = j >= 0 && i < S;    // the row exists after chunk j
+    x.off = (int64_t)W + i;      // inside the index lists either way
     x.v0 = idx[x.off];
     return x;
   };
@@ -1249,7 +1265,6 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
       if (l == 0) trho[cur.off] = tr;
     }
   };
-  const int J = b.absorbed - 1;
   Id b0 = fetch_id(J - 4), b1 = fetch_id(J - 5), b2 = fetch_id(J - 6), b3 = fetch_id(J - 7);
   In a0 = fetch(fetch_id(J)), a1 = fetch(fetch_id(J - 1)), a2 = fetch(fetch_id(J - 2)), a3 = fetch(fetch_id(J - 3));
   for (int j = J; j >= 0; j -= 4) {
