@@ -136,9 +136,21 @@ __global__ __launch_bounds__(256) void bwd_rot_kernel(Dims m, Dev d, BwdIn in, B
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = fmaf(sg * y[e], sn[e], x[e] * cs[e]);
     }
-    float* dst = (which ? b.kr32 : b.qr32) + r + d0;
-    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    if (Is<T>::bf && which) {   // keys on the bf16 path: bf16 hi (dims 0..63) | lo (dims 0..63) per row
+      bf16x8 hv, lv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hv[e] = (bf16)x[e];
+        lv[e] = (bf16)(x[e] - (float)hv[e]);
+      }
+      bf16* dst = reinterpret_cast<bf16*>(b.kr32) + 2 * r + d0;
+      *reinterpret_cast<bf16x8*>(dst) = hv;
+      *reinterpret_cast<bf16x8*>(dst + 64) = lv;
+    } else {
+      float* dst = (which ? b.kr32 : b.qr32) + r + d0;
+      *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
   }
 }
 
@@ -594,11 +606,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // bytes either way) and of values (bf16), converted only when stored, so
   // that no wait follows the loads.
   constexpr int IT = 32 * 16 / NT;
-  uint4 rk[IT];   // window: four fp32 dims; state: eight fp16 dims holding the four
+  uint4 rk[IT];   // window: four dims as bf16 hi (x, y) and lo (z, w); state: eight fp16 dims holding the four
   uint2 rv[IT];
   const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
-  const float* kr32 = b.kr32 + (size_t)s * in.N * 64;
+  const bf16* krh = reinterpret_cast<const bf16*>(b.kr32) + (size_t)s * in.N * 128;   // rows: hi 64 | lo 64
   const bf16* vin = reinterpret_cast<const bf16*>(in.v) + (size_t)s * in.N * 64;
   const bool idx_lds = S <= kBwdIdxCap;   // (uniform) version ids from LDS
   // (loads are unconditional, at clamped in-range addresses, and a piece's
@@ -625,7 +637,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       } else {
         const int64_t pos = lo + (int64_t)(Tile - n_st) * 32 + key;
         const int64_t pc = pos < hi ? pos : hi - 1;
-        rk[it] = *reinterpret_cast<const uint4*>(kr32 + pc * 64 + 4 * c4);
+        const uint2 kh2 = *reinterpret_cast<const uint2*>(krh + pc * 128 + 4 * c4);
+        const uint2 kl2 = *reinterpret_cast<const uint2*>(krh + pc * 128 + 64 + 4 * c4);
+        rk[it] = make_uint4(kh2.x, kh2.y, kl2.x, kl2.y);
         va = vin + pc * 64 + 4 * c4;
         rok |= (pos < hi ? 1u : 0u) << it;
       }
@@ -641,32 +655,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     for (int it = 0; it < IT; ++it) {
       const int e = tid + it * NT, key = e >> 4, c4 = e & 15;
       const bool ok = (rok >> it) & 1u;
-      float kx[4];
-      if (Tile < n_st) {   // fp16 bits as they are (zero on dims 0..31); the values for the split
+      uint2 hb, lb;   // the piece's keys as bf16 hi and lo bits
+      if (Tile < n_st) {   // fp16 bits as they are (zero on dims 0..31), split into hi + lo
         const bool kok = ok && c4 >= 8;
         const uint2 kr2 = (c4 & 7) == 7 ? make_uint2(rk[it].z, rk[it].w) : make_uint2(rk[it].x, rk[it].y);
         const uint2 k2 = kok ? kr2 : make_uint2(0u, 0u);
         *reinterpret_cast<uint2*>(Kr + key * kRP + 4 * c4) = k2;
         const f16x4 k4 = __builtin_bit_cast(f16x4, k2);
+        bf16x4 h4, l4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) kx[t] = (float)k4[t];
+        for (int t = 0; t < 4; ++t) {
+          const float kx = (float)k4[t];
+          h4[t] = (bf16)kx;
+          l4[t] = (bf16)(kx - (float)h4[t]);
+        }
+        hb = __builtin_bit_cast(uint2, h4);
+        lb = __builtin_bit_cast(uint2, l4);
       } else {
-        kx[0] = ok ? __uint_as_float(rk[it].x) : 0.f;
-        kx[1] = ok ? __uint_as_float(rk[it].y) : 0.f;
-        kx[2] = ok ? __uint_as_float(rk[it].z) : 0.f;
-        kx[3] = ok ? __uint_as_float(rk[it].w) : 0.f;
-        *reinterpret_cast<bf16x4*>(Kr + key * kRP + 4 * c4) = bf16x4{(bf16)kx[0], (bf16)kx[1], (bf16)kx[2], (bf16)kx[3]};
+        hb = ok ? make_uint2(rk[it].x, rk[it].y) : make_uint2(0u, 0u);
+        lb = ok ? make_uint2(rk[it].z, rk[it].w) : make_uint2(0u, 0u);
+        *reinterpret_cast<uint2*>(Kr + key * kRP + 4 * c4) = hb;
       }
       *reinterpret_cast<uint2*>(Vr + key * kRP + 4 * c4) = ok ? rv[it] : make_uint2(0u, 0u);
-      bf16x4 h4, l4;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        h4[t] = (bf16)kx[t];
-        l4[t] = (bf16)(kx[t] - (float)h4[t]);
-      }
       const int o = key * 128 + 16 * ((c4 >> 1) ^ tr_swz(key)) + 8 * (c4 & 1);
-      *reinterpret_cast<bf16x4*>(Kh + o) = h4;
-      *reinterpret_cast<bf16x4*>(Kl + o) = l4;
+      *reinterpret_cast<uint2*>(Kh + o) = hb;
+      *reinterpret_cast<uint2*>(Kl + o) = lb;
     }
   };
   // B operand of dq at step kk: lane group g = lane / 16 reads keys
@@ -925,44 +938,42 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
           f16x4{(f16)(x.x * qdown), (f16)(x.y * qdown), (f16)(x.z * qdown), (f16)(x.w * qdown)};
     }
     __syncthreads();
+    // This wave's keys and values as B operands (step kk: dims 16 kk + 8 h + e;
+    // 16-byte loads of eight consecutive dims).  A key past the end reads a
+    // valid row: its scores are masked, so its weights are 0, and its
+    // gradient is not stored.  The next tile's operands are loaded into the
+    // same registers as soon as the last sub-block's score products have read
+    // them, before this tile's stores, so that the wait for them at the next
+    // tile does not wait for the stores too.
+    bf16x8 kb[4], vb[4];
+    f16x8 kh[2];
+    const bool idx_lds = S <= kBwdIdxCap;   // (uniform) version ids from LDS
+    auto load_ops = [&](int Tile) __attribute__((always_inline)) {
+      if (Tile < n_st) {
+        const int r = Tile * 32 + kl;
+        const int rr = r < S ? r : S - 1;
+        const int64_t ver = idx_lds ? sIdx[rr] : idxl[rr];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) vb[kk] = *reinterpret_cast<const bf16x8*>(pv + ver * 64 + 16 * kk + 8 * h);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) kh[kk] = *reinterpret_cast<const f16x8*>(pk + ver * 32 + 16 * kk + 8 * h);
+      } else {
+        const int64_t kq = lo + (int64_t)(Tile - n_st) * 32 + kl;
+        const int64_t pp = kq < hi ? kq : hi - 1;
+        const bf16* kr = reinterpret_cast<const bf16*>(b.kr32) + ((size_t)s * in.N + pp) * 128;   // the hi plane
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          kb[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * kk + 8 * h);
+          vb[kk] = *reinterpret_cast<const bf16x8*>(vin + pp * 64 + 16 * kk + 8 * h);
+        }
+      }
+    };
+    if (w < n_tiles) load_ops(w);
     for (int Tile = w; Tile < n_tiles; Tile += NV) {
       const bool st = Tile < n_st;
-      // this wave's keys and values as B operands (step kk: dims 16 kk + 8 h + e)
-      bf16x8 kb[4], vb[4];
-      f16x8 kh[2];
-      int64_t kpos = 0;
-      bool kvalid;
+      const int64_t kpos = lo + (int64_t)(Tile - n_st) * 32 + kl;    // (window tiles)
+      const bool kvalid = st ? Tile * 32 + kl < S : kpos < hi;
       const int64_t klast = lo + (int64_t)(Tile - n_st) * 32 + 31;   // (window tiles) the tile's last key
-      // (16-byte loads: eight consecutive dims per step and lane half; rows
-      // past the end read a valid row and are zeroed)
-      if (st) {
-        const int r = Tile * 32 + kl;
-        kvalid = r < S;
-        const int rr = kvalid ? r : 0;
-        const int64_t ver = rr < kBwdIdxCap ? sIdx[rr] : idxl[rr];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          kb[kk] = bf16x8{};
-          vb[kk] = kvalid ? *reinterpret_cast<const bf16x8*>(pv + ver * 64 + 16 * kk + 8 * h) : bf16x8{};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          kh[kk] = kvalid ? *reinterpret_cast<const f16x8*>(pk + ver * 32 + 16 * kk + 8 * h) : f16x8{};
-      } else {
-        kpos = lo + (int64_t)(Tile - n_st) * 32 + kl;
-        kvalid = kpos < hi;
-        const int64_t pp = kvalid ? kpos : lo;
-        const float* kr = b.kr32 + ((size_t)s * in.N + pp) * 64;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 kx = bf8_at(kr + 16 * kk + 8 * h);
-          const bf16x8 vx = *reinterpret_cast<const bf16x8*>(vin + pp * 64 + 16 * kk + 8 * h);
-          kb[kk] = kvalid ? kx : bf16x8{};
-          vb[kk] = kvalid ? vx : bf16x8{};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) kh[kk] = f16x8{};
-      }
       f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
       for (int qs = 0; qs < QB; qs += 32) {
         // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
@@ -983,6 +994,7 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
         }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vb[kk], dp);
+        if (qs + 32 == QB && Tile + NV < n_tiles) load_ops(Tile + NV);
         // (a query past the end has lse = +inf, so its weights come out 0; the
         // mask is needed only on a ragged tile or one with keys after some of
         // the sub-block's queries: wave-uniform)

@@ -140,7 +140,7 @@ struct Bwd {
   float* tot_rho;      // [BH][idx_total]      running total of the radius gradient
   float2* lse_d;       // [BH][N]              per query: log2 of the softmax denominator, D = sum P dP
   float* qr32;         // [BH][N][64]          rotated queries, fp32
-  float* kr32;         // [BH][N][64]          rotated keys, fp32
+  float* kr32;         // [BH][N][64]          rotated keys, fp32 (bf16 path: the same bytes as bf16 hi 64 | lo 64 per row)
   float* dq;           // [BH][N][64]
   float* dk;           // [BH][N][64]
   float* dv;           // [BH][N][64]
