@@ -1305,17 +1305,27 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
 // Absorbed tokens: a merged token added g * (k_live, v) to its row after its
 // chunk; a sink or appended token created the row (k_live, v unscaled, radius
 // |v|).  Adds to dk (live dims) and dv, writes the gate-logit gradient
-// (sigmoid'), and zero for tokens never absorbed.  One wave per token.
+// (sigmoid'), and zero for tokens never absorbed.  Sixteen threads per token
+// (one DPP row): thread u holds value dims 4u .. 4u + 3 and, for u < 8, live
+// key dims 32 + 4u .. + 3.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void load4f(const float* p, float (&x)[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+}
+__device__ __forceinline__ void load4f(const bf16* p, float (&x)[4]) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  x[0] = (float)a[0]; x[1] = (float)a[1]; x[2] = (float)a[2]; x[3] = (float)a[3];
+}
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_token_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   const int s = blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (t >= in.N) return;
+  const int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int u = threadIdx.x & 15;
+  if (t >= in.N) return;   // (a whole row of sixteen leaves together)
   float* dl = b.dl + (size_t)s * in.N;
   if (t >= (int64_t)b.absorbed * m.C) {
-    if (l == 0) dl[t] = 0.f;
+    if (u == 0) dl[t] = 0.f;
     return;
   }
   const int j = (int)(t / m.C);
@@ -1324,28 +1334,49 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims m, Dev d, BwdIn in,
   const int4 sc = d.sched[j];
   const int64_t off = (int64_t)s * m.idx_total + sc.w + row;
   const float* e = b.part_state + off * 96;
-  const float tk = l < 32 ? e[l] : 0.f;
-  const float tv = e[32 + l];
+  const bool kl = u < 8;   // this thread also holds four live key dims
+  const int ku = kl ? u : 0;
+  float tk[4], tv[4], kt[4], vt[4];
+  load4f(e + 4 * ku, tk);
+  load4f(e + 32 + 4 * u, tv);
   const size_t ti = (size_t)s * in.N + (size_t)t;
-  const float kt = l < 32 ? tof(reinterpret_cast<const T*>(in.k)[ti * 64 + 32 + l]) : 0.f;
-  const float vt = tof(reinterpret_cast<const T*>(in.v)[ti * 64 + l]);
-  float* dk = b.dk + ti * 64;
-  float* dv = b.dv + ti * 64;
+  load4f(reinterpret_cast<const T*>(in.k) + ti * 64 + 32 + 4 * ku, kt);
+  load4f(reinterpret_cast<const T*>(in.v) + ti * 64 + 4 * u, vt);
+  float* dk = b.dk + ti * 64 + 32 + 4 * ku;
+  float* dv = b.dv + ti * 64 + 4 * u;
+  float ak[4], av[4];
+  load4f(dk, ak);
+  load4f(dv, av);
   if (kind == 2) {   // merge
     const float lg = in.l[ti];
     const float g = m.no_gate ? 1.f : 1.f / (1.f + __expf(-lg));
-    const float dg = lane_sum64(kt * tk + vt * tv);
-    if (l < 32) dk[32 + l] += g * tk;
-    dv[l] += g * tv;
-    if (l == 0) dl[t] = m.no_gate ? 0.f : dg * g * (1.f - g);
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (kl) part = fmaf(kt[q], tk[q], part);
+      part = fmaf(vt[q], tv[q], part);
+      ak[q] += g * tk[q];
+      av[q] += g * tv[q];
+    }
+    const float dg = lane_sum16(part);
+    if (u == 0) dl[t] = m.no_gate ? 0.f : dg * g * (1.f - g);
   } else {           // sink or append: the row's creator
-    const float v2 = lane_sum64(vt * vt);
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part = fmaf(vt[q], vt[q], part);
+    const float v2 = lane_sum16(part);
     const float tr = b.tot_rho[off];
     const float nv = sqrtf(v2);
-    if (l < 32) dk[32 + l] += tk;
-    dv[l] += tv + (nv > 0.f ? tr * vt / nv : 0.f);
-    if (l == 0) dl[t] = 0.f;
+    const float rs = nv > 0.f ? tr / nv : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ak[q] += tk[q];
+      av[q] += tv[q] + rs * vt[q];
+    }
+    if (u == 0) dl[t] = 0.f;
   }
+  if (kl) *reinterpret_cast<float4*>(dk) = make_float4(ak[0], ak[1], ak[2], ak[3]);
+  *reinterpret_cast<float4*>(dv) = make_float4(av[0], av[1], av[2], av[3]);
 }
 
 template <typename T>
@@ -1375,7 +1406,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
   bwd_win_kernel<<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   if (rows_last > 0)
     bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
-  bwd_token_kernel<T><<<dim3((unsigned)((in.N + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  bwd_token_kernel<T><<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   return hipGetLastError();
 }
 
