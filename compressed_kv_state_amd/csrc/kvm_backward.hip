@@ -1142,7 +1142,8 @@ __global__ __launch_bounds__(256) void bwd_win_kernel(Dims m, Dev d, BwdIn in, B
 // rho u, u = V/|V|: dV = (rho/|V|) (g - u (u.g)), d rho = u.g; the plain mean
 // V/n without value-length normalisation) and added to the running totals, which
 // replace the partial in place: afterwards entry (j, i) holds the gradient of
-// row i's sums as they stood after chunk j.  One wave per row; lane = dim.
+// row i's sums as they stood after chunk j.  Two rows per wave, one per
+// 32-lane half; lane hl of a half holds key dim hl and value dims hl, 32 + hl.
 // ---------------------------------------------------------------------------
 // Sums across lanes without LDS round trips, every lane receiving the sum (the
 // same bits in every lane): DPP quad swaps and row mirrors within 16 lanes,
@@ -1174,9 +1175,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, int rows_last) {
   using RT = typename Rd<T>::type;
   const int s = blockIdx.y;
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int l = threadIdx.x & 63;
-  if (i >= rows_last) return;
+  const int l = threadIdx.x & 63, hl = l & 31;
+  const int i0 = blockIdx.x * 8 + 2 * (threadIdx.x >> 6);
+  if (i0 >= rows_last) return;   // (both halves)
+  const int i = i0 + (l >> 5);
+  const bool row_ok = i < rows_last;
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
   const float* prho = d.prho + (size_t)s * m.V_cap;
@@ -1185,7 +1188,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   const int* idx = d.idx + (size_t)s * m.idx_total;
   float* part = b.part_state + (size_t)s * m.idx_total * 96;
   float* trho = b.tot_rho + (size_t)s * m.idx_total;
-  float tk = 0.f, tv = 0.f, tr = 0.f;
+  float tk = 0.f, tv0 = 0.f, tv1 = 0.f, tr = 0.f;
   // The row's version id at snapshot j is loaded eight snapshots ahead of its
   // use and the version's inputs four ahead, so that neither waits on the
   // other.  Every fetch issues the same loads (at a valid index when the
@@ -1216,14 +1219,14 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     if (jc < sb - 63) load_sched(jc);   // (snapshots are visited in decreasing order)
     const int li = sb - jc;
     const int S = __builtin_amdgcn_readlane(sS, li), W = __builtin_amdgcn_readlane(sW, li);
-    x.live = j >= 0 && i < S;    // the row exists after chunk j
+    x.live = row_ok && j >= 0 && i < S;    // the row exists after chunk j
     x.off = (int64_t)W + i;      // inside the index lists either way
     x.v0 = idx[x.off];
     return x;
   };
   struct In {
     int64_t off;
-    float gk, gv, xh, rho, vh, invn;
+    float gk, gv0, gv1, xh, rho, vh0, vh1, invn;
     float2 nm;
     int ver;
     bool live;
@@ -1235,17 +1238,15 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     const int64_t ver = id.live ? id.v0 : 0;
     x.ver = (int)ver;
     const float* e = part + x.off * 96;
-    x.gk = e[l & 31];
-    x.gv = e[32 + l];
-    x.xh = tof(pk[ver * 32 + (l & 31)]);
+    x.gk = e[hl];
+    x.gv0 = e[32 + hl];
+    x.gv1 = e[64 + hl];
+    x.xh = tof(pk[ver * 32 + hl]);
     x.nm = pnm[ver];
     x.invn = 1.0f / (float)pcnt[ver];
     x.rho = prho[ver];
-    x.vh = tof(pv[ver * 64 + l]);
-    if (l >= 32) {
-      x.gk = 0.f;
-      x.xh = 0.f;
-    }
+    x.vh0 = tof(pv[ver * 64 + hl]);
+    x.vh1 = tof(pv[ver * 64 + 32 + hl]);
     return x;
   };
   // one snapshot's contribution, added to the running totals (later snapshots
@@ -1254,27 +1255,33 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   // where chunk j touched the row (a new version, or a new row): `prev` is
   // the row at snapshot j - 1.
   auto step = [&](const In& cur, const In& prev) {
-    // LayerNorm backward over the 32 live dims (lanes 0..31; lanes 32..63 carry zeros)
+    // LayerNorm backward over the 32 live dims (sums over the half)
     const float sg = lane_sum32(cur.gk), sgx = lane_sum32(cur.gk * cur.xh);
-    const float dK =
-        l < 32 ? cur.nm.x * (cur.gk - sg * (1.0f / 32.0f) - cur.xh * sgx * (1.0f / 32.0f)) * cur.invn : 0.f;
-    float dV, dR = 0.f;
+    const float dK = cur.nm.x * (cur.gk - sg * (1.0f / 32.0f) - cur.xh * sgx * (1.0f / 32.0f)) * cur.invn;
+    float dV0, dV1, dR = 0.f;
     if (m.no_vnorm) {
-      dV = cur.gv * cur.invn;
+      dV0 = cur.gv0 * cur.invn;
+      dV1 = cur.gv1 * cur.invn;
     } else {
-      const float u = cur.rho > 0.f ? cur.vh / cur.rho : 0.f;
-      const float ug = lane_sum64(u * cur.gv);
-      dV = cur.nm.y * (cur.gv - u * ug);
+      const float u0 = cur.rho > 0.f ? cur.vh0 / cur.rho : 0.f;
+      const float u1 = cur.rho > 0.f ? cur.vh1 / cur.rho : 0.f;
+      const float ug = lane_sum32(fmaf(u1, cur.gv1, u0 * cur.gv0));
+      dV0 = cur.nm.y * (cur.gv0 - u0 * ug);
+      dV1 = cur.nm.y * (cur.gv1 - u1 * ug);
       dR = ug;
     }
-    tk += dK;
-    tv += dV;
-    tr += dR;
-    if (!prev.live || prev.ver != cur.ver) {
-      float* e = part + cur.off * 96;
-      if (l < 32) e[l] = tk;
-      e[32 + l] = tv;
-      if (l == 0) trho[cur.off] = tr;
+    if (cur.live) {   // (the other half's row may still run after this one has ended)
+      tk += dK;
+      tv0 += dV0;
+      tv1 += dV1;
+      tr += dR;
+      if (!prev.live || prev.ver != cur.ver) {
+        float* e = part + cur.off * 96;
+        e[hl] = tk;
+        e[32 + hl] = tv0;
+        e[64 + hl] = tv1;
+        if (hl == 0) trho[cur.off] = tr;
+      }
     }
   };
   Id b0 = fetch_id(J - 4), b1 = fetch_id(J - 5), b2 = fetch_id(J - 6), b3 = fetch_id(J - 7);
@@ -1282,19 +1289,19 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   for (int j = J; j >= 0; j -= 4) {
     // (a row exists from its creating chunk on, so the first snapshot without
     // it ends the sweep)
-    if (!a0.live) break;
+    if (!__any(a0.live)) break;
     step(a0, a1);
     a0 = fetch(b0);
     b0 = fetch_id(j - 8);
-    if (!a1.live) break;
+    if (!__any(a1.live)) break;
     step(a1, a2);
     a1 = fetch(b1);
     b1 = fetch_id(j - 9);
-    if (!a2.live) break;
+    if (!__any(a2.live)) break;
     step(a2, a3);
     a2 = fetch(b2);
     b2 = fetch_id(j - 10);
-    if (!a3.live) break;
+    if (!__any(a3.live)) break;
     step(a3, a0);
     a3 = fetch(b3);
     b3 = fetch_id(j - 11);
@@ -1405,7 +1412,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
   if (e != hipSuccess) return e;
   bwd_win_kernel<<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   if (rows_last > 0)
-    bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 3) / 4), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
+    bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 7) / 8), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
   bwd_token_kernel<T><<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   return hipGetLastError();
 }
