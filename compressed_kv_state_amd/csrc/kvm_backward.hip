@@ -1142,8 +1142,9 @@ __global__ __launch_bounds__(256) void bwd_win_kernel(Dims m, Dev d, BwdIn in, B
 // rho u, u = V/|V|: dV = (rho/|V|) (g - u (u.g)), d rho = u.g; the plain mean
 // V/n without value-length normalisation) and added to the running totals, which
 // replace the partial in place: afterwards entry (j, i) holds the gradient of
-// row i's sums as they stood after chunk j.  Two rows per wave, one per
-// 32-lane half; lane hl of a half holds key dim hl and value dims hl, 32 + hl.
+// row i's sums as they stood after chunk j.  Four rows per wave, one per
+// 16-lane row of the wave; lane q of a row holds key dims 2q, 2q + 1 and
+// value dims 4q .. 4q + 3.
 // ---------------------------------------------------------------------------
 // Sums across lanes without LDS round trips, every lane receiving the sum (the
 // same bits in every lane): DPP quad swaps and row mirrors within 16 lanes,
@@ -1171,14 +1172,26 @@ __device__ __forceinline__ float lane_sum64(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ float2 ld2f(const float* p) { return *reinterpret_cast<const float2*>(p); }
+typedef f16 f16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 ld2f(const f16* p) {
+  const f16x2v a = *reinterpret_cast<const f16x2v*>(p);
+  return make_float2((float)a[0], (float)a[1]);
+}
+__device__ __forceinline__ float4 ld4f(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4f(const bf16* p) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  return make_float4((float)a[0], (float)a[1], (float)a[2], (float)a[3]);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, int rows_last) {
   using RT = typename Rd<T>::type;
   const int s = blockIdx.y;
-  const int l = threadIdx.x & 63, hl = l & 31;
-  const int i0 = blockIdx.x * 8 + 2 * (threadIdx.x >> 6);
-  if (i0 >= rows_last) return;   // (both halves)
-  const int i = i0 + (l >> 5);
+  const int l = threadIdx.x & 63, q = l & 15;
+  const int i0 = blockIdx.x * 16 + 4 * (threadIdx.x >> 6);
+  if (i0 >= rows_last) return;   // (all four rows)
+  const int i = i0 + (l >> 4);
   const bool row_ok = i < rows_last;
   const RT* pk = reinterpret_cast<const RT*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const T* pv = reinterpret_cast<const T*>(d.pval) + (size_t)s * m.V_cap * 64;
@@ -1188,7 +1201,9 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   const int* idx = d.idx + (size_t)s * m.idx_total;
   float* part = b.part_state + (size_t)s * m.idx_total * 96;
   float* trho = b.tot_rho + (size_t)s * m.idx_total;
-  float tk = 0.f, tv0 = 0.f, tv1 = 0.f, tr = 0.f;
+  float2 tk = make_float2(0.f, 0.f);
+  float4 tv = make_float4(0.f, 0.f, 0.f, 0.f);
+  float tr = 0.f;
   // The row's version id at snapshot j is loaded eight snapshots ahead of its
   // use and the version's inputs four ahead, so that neither waits on the
   // other.  Every fetch issues the same loads (at a valid index when the
@@ -1226,8 +1241,9 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   };
   struct In {
     int64_t off;
-    float gk, gv0, gv1, xh, rho, vh0, vh1, invn;
-    float2 nm;
+    float2 gk, xh, nm;
+    float4 gv, vh;
+    float rho, invn;
     int ver;
     bool live;
   };
@@ -1238,15 +1254,13 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     const int64_t ver = id.live ? id.v0 : 0;
     x.ver = (int)ver;
     const float* e = part + x.off * 96;
-    x.gk = e[hl];
-    x.gv0 = e[32 + hl];
-    x.gv1 = e[64 + hl];
-    x.xh = tof(pk[ver * 32 + hl]);
+    x.gk = ld2f(e + 2 * q);
+    x.gv = ld4f(e + 32 + 4 * q);
+    x.xh = ld2f(pk + ver * 32 + 2 * q);
     x.nm = pnm[ver];
     x.invn = 1.0f / (float)pcnt[ver];
     x.rho = prho[ver];
-    x.vh0 = tof(pv[ver * 64 + hl]);
-    x.vh1 = tof(pv[ver * 64 + 32 + hl]);
+    x.vh = ld4f(pv + ver * 64 + 4 * q);
     return x;
   };
   // one snapshot's contribution, added to the running totals (later snapshots
@@ -1255,32 +1269,40 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
   // where chunk j touched the row (a new version, or a new row): `prev` is
   // the row at snapshot j - 1.
   auto step = [&](const In& cur, const In& prev) {
-    // LayerNorm backward over the 32 live dims (sums over the half)
-    const float sg = lane_sum32(cur.gk), sgx = lane_sum32(cur.gk * cur.xh);
-    const float dK = cur.nm.x * (cur.gk - sg * (1.0f / 32.0f) - cur.xh * sgx * (1.0f / 32.0f)) * cur.invn;
-    float dV0, dV1, dR = 0.f;
+    // LayerNorm backward over the 32 live dims (sums over the 16-lane row)
+    const float sg = lane_sum16(cur.gk.x + cur.gk.y);
+    const float sgx = lane_sum16(fmaf(cur.gk.y, cur.xh.y, cur.gk.x * cur.xh.x));
+    const float ck = cur.nm.x * cur.invn;
+    const float2 dK = make_float2(ck * (cur.gk.x - sg * (1.0f / 32.0f) - cur.xh.x * sgx * (1.0f / 32.0f)),
+                                  ck * (cur.gk.y - sg * (1.0f / 32.0f) - cur.xh.y * sgx * (1.0f / 32.0f)));
+    float4 dV;
+    float dR = 0.f;
     if (m.no_vnorm) {
-      dV0 = cur.gv0 * cur.invn;
-      dV1 = cur.gv1 * cur.invn;
+      dV = make_float4(cur.gv.x * cur.invn, cur.gv.y * cur.invn, cur.gv.z * cur.invn, cur.gv.w * cur.invn);
     } else {
-      const float u0 = cur.rho > 0.f ? cur.vh0 / cur.rho : 0.f;
-      const float u1 = cur.rho > 0.f ? cur.vh1 / cur.rho : 0.f;
-      const float ug = lane_sum32(fmaf(u1, cur.gv1, u0 * cur.gv0));
-      dV0 = cur.nm.y * (cur.gv0 - u0 * ug);
-      dV1 = cur.nm.y * (cur.gv1 - u1 * ug);
+      const float4 u = cur.rho > 0.f ? make_float4(cur.vh.x / cur.rho, cur.vh.y / cur.rho, cur.vh.z / cur.rho,
+                                                   cur.vh.w / cur.rho)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float ug =
+          lane_sum16(fmaf(u.w, cur.gv.w, fmaf(u.z, cur.gv.z, fmaf(u.y, cur.gv.y, u.x * cur.gv.x))));
+      const float cv = cur.nm.y;
+      dV = make_float4(cv * (cur.gv.x - u.x * ug), cv * (cur.gv.y - u.y * ug), cv * (cur.gv.z - u.z * ug),
+                       cv * (cur.gv.w - u.w * ug));
       dR = ug;
     }
-    if (cur.live) {   // (the other half's row may still run after this one has ended)
-      tk += dK;
-      tv0 += dV0;
-      tv1 += dV1;
+    if (cur.live) {   // (another row of the wave may still run after this one has ended)
+      tk.x += dK.x;
+      tk.y += dK.y;
+      tv.x += dV.x;
+      tv.y += dV.y;
+      tv.z += dV.z;
+      tv.w += dV.w;
       tr += dR;
       if (!prev.live || prev.ver != cur.ver) {
         float* e = part + cur.off * 96;
-        e[hl] = tk;
-        e[32 + hl] = tv0;
-        e[64 + hl] = tv1;
-        if (hl == 0) trho[cur.off] = tr;
+        *reinterpret_cast<float2*>(e + 2 * q) = tk;
+        *reinterpret_cast<float4*>(e + 32 + 4 * q) = tv;
+        if (q == 0) trho[cur.off] = tr;
       }
     }
   };
@@ -1412,7 +1434,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
   if (e != hipSuccess) return e;
   bwd_win_kernel<<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   if (rows_last > 0)
-    bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 7) / 8), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
+    bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
   bwd_token_kernel<T><<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   return hipGetLastError();
 }
