@@ -310,15 +310,20 @@ __global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   // the stage about to be computed; the transfer of the next stage overlaps it.
   // (Separate buffers, unrolled by two with one exit, so that the compiler sees
   // which buffer each read and transfer touches and keeps the accumulators put.)
+  // (The scheduling barriers keep each stage's transfers ahead of the other
+  // stage's products: left free, the compiler sinks them to the end of the
+  // products, right before the wait for them, and nothing overlaps.)
   const int nk = a.K / kGK;
   issue(0, st0);
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
     dma_barrier();
     issue((kt + 1) * kGK, st1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(st0);
     dma_barrier();
     if (kt + 2 < nk) issue((kt + 2) * kGK, st0);
+    __builtin_amdgcn_sched_barrier(0);
     compute(st1);
   }
   if (kt < nk) {   // an odd last stage, in flight in the first buffer
