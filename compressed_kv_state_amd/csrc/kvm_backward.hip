@@ -465,17 +465,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in
 // the query in fp16 range), dP from the bf16 values and dO (exact), and the
 // second-stage products (dq = dS . K, dk = dS^T . Q, dv = P^T . dO) with the
 // fp32 factors (P, dS, the rotated keys and queries) as hi + lo bf16 pairs, so
-// that they keep ~2^-16 of their precision.  Tiles stay fp32 in LDS (rows padded to 68 floats, so a
-// lane's eight consecutive dims are two aligned 16-byte reads).  MFMA step kk
-// contracts 16 keys (or queries); lane half h supplies the eight that its score
-// registers 8 kk .. 8 kk + 7 hold (rows mrow(8 kk + i, h)), and the other
-// operand is read for the same eight rows, so the score registers feed the
-// next product directly, as in the fp32 kernels.
+// that they keep ~2^-16 of their precision.  Tiles sit in LDS as 16-bit rows.
+// MFMA step kk contracts 16 keys (or queries); lane half h supplies the eight
+// that its score registers 8 kk .. 8 kk + 7 hold (rows mrow(8 kk + i, h)), and
+// the other operand is read for the same eight rows, so the score registers
+// feed the next product directly, as in the fp32 kernels.
 // ---------------------------------------------------------------------------
-constexpr int kPX = 68;
 constexpr int kRP = 72;   // row-major 16-bit tile rows (halves): 144 B, 16 lanes' 16-byte reads on distinct banks
-constexpr int kTP = 40;
-constexpr int kBwdIdxCap = 4096;   // snapshot rows whose version ids the bf16 kernels keep in LDS   // transposed 16-bit tile rows (halves): 80 B, likewise
+constexpr int kTP = 40;   // 16-bit rows of 32 halves (+ 8): 80 B, likewise
+constexpr int kBwdIdxCap = 4096;   // snapshot rows whose version ids the bf16 kernels keep in LDS
 // Position of tile row r (key or query, 32 per tile) in a transposed row: the
 // eight rows mrow(8 kk + i, h), i < 8, that lane half h contracts at step kk
 // land at 16 kk + 8 h + i.
@@ -483,29 +481,6 @@ __device__ __forceinline__ int kpos(int r) {
   return (r & 16) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
 }
 
-__device__ __forceinline__ bf16x8 bf8_at(const float* p) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  return bf16x8{(bf16)a.x, (bf16)a.y, (bf16)a.z, (bf16)a.w, (bf16)b.x, (bf16)b.y, (bf16)b.z, (bf16)b.w};
-}
-__device__ __forceinline__ f16x8 h8_at(const float* p, float sc) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  return f16x8{(f16)(a.x * sc), (f16)(a.y * sc), (f16)(a.z * sc), (f16)(a.w * sc),
-               (f16)(b.x * sc), (f16)(b.y * sc), (f16)(b.z * sc), (f16)(b.w * sc)};
-}
-// registers 8 kk .. 8 kk + 7 of a score tile as an operand
-__device__ __forceinline__ bf16x8 bf8_regs(const f32x16& x, int kk) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)x[8 * kk + i];
-  return r;
-}
-// column `col` of the eight tile rows base + mrow(8 kk + i, h)
-__device__ __forceinline__ bf16x8 bf8_col(const float* t, int base, int kk, int h, int col) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)t[(base + mrow(8 * kk + i, h)) * kPX + col];
-  return r;
-}
 // x = hi + lo to ~2^-16 relative (bf16 hi, bf16 remainder)
 __device__ __forceinline__ void bf8_split(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
 #pragma unroll
