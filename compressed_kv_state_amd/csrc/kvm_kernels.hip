@@ -1007,13 +1007,13 @@ __global__ __launch_bounds__(ScanGeom<C>::NT) void scan_kernel(Dims m, Dev d, Sr
           poll();
         }
       }
-      if (xt < C) {
-#pragma unroll
-        for (int o = 1; o < XL; o <<= 1) {
-          const float ov = __shfl_xor(v, o);
-          const int orow = __shfl_xor(r, o);
+      if (xt < C) {   // (every lane of a token's group is here)
+        auto take = [&](float ov, int orow) {
           if (ov > v || (ov == v && orow < r)) { v = ov; r = orow; }
-        }
+        };
+        if constexpr (XL >= 2) take(__int_as_float(xor_lane<1>(__float_as_int(v))), xor_lane<1>(r));
+        if constexpr (XL >= 4) take(__int_as_float(xor_lane<2>(__float_as_int(v))), xor_lane<2>(r));
+        if constexpr (XL >= 8) take(__int_as_float(xor_lane<4>(__float_as_int(v))), xor_lane<4>(r));
         if (xs == 0) token_key(xt, v, r);
       }
       wait_vmem();   // this workgroup's global writes of the previous step, before the row loads below
