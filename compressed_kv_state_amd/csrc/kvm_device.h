@@ -66,15 +66,53 @@ __device__ __forceinline__ float quad_sum(float x) {
   x += xor_lane<1>(x);
   return x + xor_lane<2>(x);
 }
-// sum over each aligned group of P consecutive lanes (P a power of two <= 32)
+// Lane moves that stay in the vector ALU (no LDS round trip), for sums and
+// maxima over aligned lane groups, where any pairing that joins the group's
+// halves will do: DPP row_half_mirror (lane i of 8 takes lane 7 - i: joins the
+// two quads), row_mirror (lane i of 16 takes lane 15 - i: joins the two
+// halves of 8) and row_ror:8 (lane i of 16 takes lane i + 8 mod 16: joins
+// lanes 8 apart); the two rows of 16 of each half-wave, and the two half-waves,
+// are joined by the permlane swaps.  Every lane of the group must be active.
+template <int CTRL, typename V>
+__device__ __forceinline__ V dpp_mov(V x) {
+  static_assert(sizeof(V) == 4, "32-bit lanes");
+  return __builtin_bit_cast(V, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// {the value of this lane's row of 16, the value of the paired row} (rows 2r, 2r + 1)
+template <typename V>
+__device__ __forceinline__ void row_pair(V x, V& a, V& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  a = __builtin_bit_cast(V, (uint32_t)r[0]);
+  b = __builtin_bit_cast(V, (uint32_t)r[1]);
+}
+template <typename V>
+__device__ __forceinline__ void half_pair(V x, V& a, V& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  a = __builtin_bit_cast(V, (uint32_t)r[0]);
+  b = __builtin_bit_cast(V, (uint32_t)r[1]);
+}
+
+// sum over each aligned group of P consecutive lanes (P a power of two <= 64);
+// every lane of a group gets the same bits
 template <int P, typename V>
 __device__ __forceinline__ V group_sum(V x) {
-  static_assert(P >= 1 && P <= 32 && (P & (P - 1)) == 0, "lanes per group");
+  static_assert(P >= 1 && P <= 64 && (P & (P - 1)) == 0, "lanes per group");
   if constexpr (P >= 2) x += xor_lane<1>(x);
   if constexpr (P >= 4) x += xor_lane<2>(x);
-  if constexpr (P >= 8) x += xor_lane<4>(x);
-  if constexpr (P >= 16) x += xor_lane<8>(x);
-  if constexpr (P >= 32) x += xor_lane<16>(x);
+  if constexpr (P >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
+  if constexpr (P >= 16) x += dpp_mov<0x140>(x);  // row_mirror
+  if constexpr (P >= 32) {
+    V a, b;
+    row_pair(x, a, b);
+    x = a + b;
+  }
+  if constexpr (P >= 64) {
+    V a, b;
+    half_pair(x, a, b);
+    x = a + b;
+  }
   return x;
 }
 

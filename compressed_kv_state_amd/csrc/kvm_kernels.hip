@@ -2651,14 +2651,23 @@ __device__ __forceinline__ void unpack16(const u32x4& x, float* f) {
   }
 }
 
+// maximum over the wave, every lane getting it
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, xor_lane<1>(x));
+  x = fmaxf(x, xor_lane<2>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  x = fmaxf(x, dpp_mov<0x140>(x));
+  float a, b;
+  row_pair(x, a, b);
+  x = fmaxf(a, b);
+  half_pair(x, a, b);
+  return fmaxf(a, b);
+}
+
 // sum over aligned groups of G lanes (G a power of two <= 16)
 template <int G>
 __device__ __forceinline__ float dec_group_sum(float x) {
-  if constexpr (G >= 2) x += xor_lane<1>(x);
-  if constexpr (G >= 4) x += xor_lane<2>(x);
-  if constexpr (G >= 8) x += xor_lane<4>(x);
-  if constexpr (G >= 16) x += xor_lane<8>(x);
-  return x;
+  return group_sum<G>(x);
 }
 
 template <typename T>
@@ -2817,8 +2826,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
     // ---- the block's maximum, then exact weights in place
     float mx = -kInf;
     for (int i = tid; i < b1 - b0; i += NT) mx = fmaxf(mx, sL[i]);
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+    mx = wave_max(mx);
     if (lane == 0) red[w] = mx;
     __syncthreads();
     mx = red[0];
@@ -2883,11 +2891,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_kernel(Dims m, Dev d, cons
   }
   // ---- combine: lane groups of the wave (same dims), then the waves; the row sum over all threads
 #pragma unroll
-  for (int msk = VL; msk < 64; msk <<= 1)
-#pragma unroll
-    for (int k = 0; k < VE; ++k) o[k] += __shfl_xor(o[k], msk);
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) lsum += __shfl_xor(lsum, msk);
+  for (int k = 0; k < VE; ++k) {
+    if constexpr (VL == 8) o[k] += dpp_mov<0x128>(o[k]);   // row_ror:8, the group 8 lanes away
+    float a, b;
+    row_pair(o[k], a, b);
+    o[k] = a + b;
+    half_pair(o[k], a, b);
+    o[k] = a + b;
+  }
+  lsum = group_sum<64>(lsum);
   if (lane < VL) {
 #pragma unroll
     for (int k = 0; k < VE; ++k) red_o[w][VE * lane + k] = o[k];
