@@ -821,8 +821,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-// NV waves (two per SIMD where the registers allow) share the block's key tiles
-template <int NW, int NV>
+// NV waves (two per SIMD where the registers allow) share the block's key
+// tiles: the snapshot's state rows and (WIN) the window keys, whose partials
+// go to part_win; without WIN the window keys are left to bwd_kvw_mx_kernel.
+template <int NW, int NV, bool WIN = true>
 __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
   // query blocks of QB in LDS, 16-bit: queries row-major (bf16, and fp16
@@ -858,7 +860,8 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
   for (int i = tid; i < S && i < kBwdIdxCap; i += NV * 64) sIdx[i] = idxl[i];
   const int64_t lo = cpos - m.W > 0 ? cpos - m.W : 0;
   const int64_t hi = cpos + C < in.N ? cpos + C : in.N;
-  const int n_tiles = n_st + (int)((hi - lo + 31) >> 5);
+  const int n_tiles = n_st + (WIN ? (int)((hi - lo + 31) >> 5) : 0);
+  if (!WIN && n_st == 0) return;   // (no state rows before this chunk: nothing to do)
   const f16* pk = reinterpret_cast<const f16*>(d.pkey) + (size_t)s * m.V_cap * 32;
   const bf16* pv = reinterpret_cast<const bf16*>(d.pval) + (size_t)s * m.V_cap * 64;
   const bf16* vin = reinterpret_cast<const bf16*>(in.v) + (size_t)s * in.N * 64;
@@ -1064,6 +1067,189 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
           }
         }
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Window keys of one key block (the C positions [bC, bC + C)) against the
+// query chunks whose window holds them (chunks b .. b + W/C): each wave keeps
+// its key tile's dk and dv in registers across those chunks, and the block's
+// final dk (RoPE transposed on dims 0..31, scaled) and dv are written once,
+// with no partials in memory and no separate summing pass.  NV = 2 NW waves:
+// wave w takes key tile w % NW and the 32-query sub-blocks j with
+// j % 2 == w / NW of each chunk; the two halves are added through LDS at the
+// end.  The products are those of bwd_kv_mx_kernel's window tiles.
+template <int NW, int NV>
+__global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+  constexpr int C = NW * 32;
+  static_assert(NV == 2 * NW && C <= kQB, "one query block per chunk, two query halves");
+  constexpr int QB = C;
+  constexpr int QTP = QB + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Qb[QB * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t Dr[QB * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t QTh[64 * QTP];
+  __shared__ __attribute__((aligned(16))) uint16_t QTl[64 * QTP];
+  __shared__ __attribute__((aligned(16))) uint16_t DT[64 * QTP];
+  __shared__ float2 LD[QB];
+  static_assert(64 * QTP * 2 >= NW * 16 * 64 * 4, "the halves' exchange fits QTh");
+  const int s = blockIdx.x % m.BH;
+  const int kb0 = blockIdx.x / m.BH;   // the key block
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, kl = lane & 31;
+  const int tile = w % NW, part = w / NW;
+  const int64_t bpos = (int64_t)kb0 * C;
+  const int64_t kq = bpos + 32 * tile + kl;   // this lane's key
+  const bool kvalid = kq < in.N;
+  const int64_t pp = kvalid ? kq : in.N - 1;  // (a key past the end reads a valid row; masked)
+  const int64_t klast = bpos + 32 * tile + 31;
+  const float c2 = m.scale * kLog2e;
+  const bf16* vin = reinterpret_cast<const bf16*>(in.v) + (size_t)s * in.N * 64;
+  const bf16* doin = reinterpret_cast<const bf16*>(in.dout) + (size_t)s * in.N * 64;
+  // this wave's keys (the rotated keys' hi plane) and values as B operands
+  // (step kk: dims 16 kk + 8 h + e)
+  bf16x8 kb[4], vb[4];
+  {
+    const bf16* kr = reinterpret_cast<const bf16*>(b.kr32) + ((size_t)s * in.N + pp) * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      kb[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * kk + 8 * h);
+      vb[kk] = *reinterpret_cast<const bf16x8*>(vin + pp * 64 + 16 * kk + 8 * h);
+    }
+  }
+  f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};
+  const int c_end = min(kb0 + m.W / C, b.nq - 1);
+  for (int c = kb0; c <= c_end; ++c) {
+    const int64_t cpos = (int64_t)c * C;
+    __syncthreads();   // every wave is done with the previous chunk's tiles
+    // the chunk's queries, rotated (unscaled), their dO and (lse, D); zero past the end
+    for (int e = tid; e < QB * 16; e += NV * 64) {
+      const int qi = e >> 4, c4 = e & 15;
+      const int64_t pos = cpos + qi;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      uint2 g = make_uint2(0u, 0u);
+      if (pos < in.N) {
+        x = *reinterpret_cast<const float4*>(b.qr32 + ((size_t)s * in.N + pos) * 64 + 4 * c4);
+        g = *reinterpret_cast<const uint2*>(doin + pos * 64 + 4 * c4);
+      }
+      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = bf16x4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
+      *reinterpret_cast<uint2*>(Dr + qi * kRP + 4 * c4) = g;
+      const int qp = (qi & ~31) + kpos(qi & 31);
+      const float xv[4] = {x.x, x.y, x.z, x.w};
+      const uint16_t gv[4] = {(uint16_t)(g.x & 0xFFFFu), (uint16_t)(g.x >> 16), (uint16_t)(g.y & 0xFFFFu),
+                              (uint16_t)(g.y >> 16)};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16 hi8 = (bf16)xv[t];
+        const bf16 lo8 = (bf16)(xv[t] - (float)hi8);
+        QTh[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, hi8);
+        QTl[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, lo8);
+        DT[(4 * c4 + t) * QTP + qp] = gv[t];
+      }
+    }
+    for (int qi = tid; qi < QB; qi += NV * 64) {
+      const int64_t pos = cpos + qi;
+      LD[qi] = pos < in.N ? b.lse_d[(size_t)s * in.N + pos] : make_float2(kInf, 0.f);
+    }
+    __syncthreads();
+    for (int j = part; j < QB / 32; j += 2) {
+      const int qs = 32 * j;
+      // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
+      const uint16_t* qrow = Qb + (qs + kl) * kRP + 8 * h;
+      const uint16_t* drow = Dr + (qs + kl) * kRP + 8 * h;
+      f32x16 sc = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * kk), kb[kk], sc);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vb[kk], dp);
+      // (a query past the end has lse = +inf, so its weights come out 0; the
+      // mask is needed only on a ragged tile or one with keys after some of
+      // the sub-block's queries, i.e. in the key block's own chunk)
+      f32x16 p, dsc;
+      if (klast >= in.N || klast > cpos + qs) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qs + mrow(r, h);
+          const float2 ld = LD[qi];
+          const bool ok = kvalid && kq <= cpos + qi;
+          const float pr = ok ? exp2_fast(sc[r] * c2 - ld.x) : 0.f;
+          p[r] = pr;
+          dsc[r] = pr * (dp[r] - ld.y);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float2 ld = LD[qs + mrow(r, h)];
+          const float pr = exp2_fast(sc[r] * c2 - ld.x);
+          p[r] = pr;
+          dsc[r] = pr * (dp[r] - ld.y);
+        }
+      }
+      // dk[key][d] += dS^T . Q (dS and Q as hi + lo pairs, three products) and
+      // dv[key][e] += P^T . dO (P as a hi + lo pair, dO exact in bf16)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float xa[8];
+        bf16x8 dh, dl, ph, pl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xa[i] = dsc[8 * kk + i];
+        bf8_split(xa, dh, dl);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xa[i] = p[8 * kk + i];
+        bf8_split(xa, ph, pl);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f32x16& dk = half ? dk1 : dk0;
+          f32x16& dv = half ? dv1 : dv0;
+          const int o = (32 * half + kl) * QTP + qs + 16 * kk + 8 * h;
+          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(QTh + o);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(QTl + o);
+          dk = mfma_bf16(dh, bh, dk);
+          dk = mfma_bf16(dh, bl, dk);
+          dk = mfma_bf16(dl, bh, dk);
+          const bf16x8 od = *reinterpret_cast<const bf16x8*>(DT + o);
+          dv = mfma_bf16(ph, od, dv);
+          dv = mfma_bf16(pl, od, dv);
+        }
+      }
+    }
+  }
+  // the second half's sums join the first's through LDS (one result at a time)
+  float* xch = reinterpret_cast<float*>(QTh) + tile * (16 * 64);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x16& acc = q == 0 ? dk0 : q == 1 ? dk1 : q == 2 ? dv0 : dv1;
+    __syncthreads();
+    if (part == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[r * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += xch[r * 64 + lane];
+    }
+  }
+  if (part != 0) return;
+  // rows of the results are keys (register r: key mrow(r, h)), lane column =
+  // dim; dk's dims 0..31 take RoPE transposed (partner dim kl ^ 16: the paired
+  // row of 16 lanes)
+  float* dko = b.dk + (size_t)s * in.N * 64;
+  float* dvo = b.dv + (size_t)s * in.N * 64;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t pos = bpos + 32 * tile + mrow(r, h);
+    const float y = dk0[r];
+    float ya, yb;
+    row_pair(y, ya, yb);
+    const float yp = (kl & 16) ? ya : yb;
+    if (pos < in.N) {
+      const int jf = kl & 15;
+      const float cs = d.rope_cos[pos * 16 + jf], sn = d.rope_sin[pos * 16 + jf];
+      const float x = kl < 16 ? y * cs + yp * sn : y * cs - yp * sn;
+      dko[pos * 64 + kl] = m.scale * x;
+      dko[pos * 64 + 32 + kl] = m.scale * dk1[r];
+      dvo[pos * 64 + kl] = dv0[r];
+      dvo[pos * 64 + 32 + kl] = dv1[r];
     }
   }
 }
@@ -1387,12 +1573,19 @@ template <typename T>
 hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd& b, int rows_last, hipStream_t st) {
   const dim3 grid((unsigned)(m.BH * b.nq));
   bwd_rot_kernel<T><<<dim3((unsigned)((in.N + 31) / 32), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  bool win_done = false;   // window-key gradients already written (no partials to sum)
   auto attn = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
     if constexpr (std::is_same<T, bf16>::value) {
       bwd_q_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
       constexpr int NV = NW < 8 ? 2 * NW : NW;
-      bwd_kv_mx_kernel<NW, NV><<<grid, NV * 64, 0, st>>>(m, d, in, b);
+      if constexpr (NW < 8) {   // window keys in their own pass, no partials
+        bwd_kv_mx_kernel<NW, NV, false><<<grid, NV * 64, 0, st>>>(m, d, in, b);
+        bwd_kvw_mx_kernel<NW, NV><<<grid, NV * 64, 0, st>>>(m, d, in, b);
+        win_done = true;
+      } else {
+        bwd_kv_mx_kernel<NW, NV><<<grid, NV * 64, 0, st>>>(m, d, in, b);
+      }
     } else {
       bwd_q_kernel<T, NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
       bwd_kv_kernel<T, NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
@@ -1407,7 +1600,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd_win_kernel<<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
+  if (!win_done) bwd_win_kernel<<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
   if (rows_last > 0)
     bwd_state_kernel<T><<<dim3((unsigned)((rows_last + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, b, rows_last);
   bwd_token_kernel<T><<<dim3((unsigned)((in.N + 15) / 16), (unsigned)m.BH), 256, 0, st>>>(m, d, in, b);
