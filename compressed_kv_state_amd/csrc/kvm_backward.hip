@@ -1085,14 +1085,17 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
   constexpr int C = NW * 32;
   static_assert(NV == 2 * NW && C <= kQB, "one query block per chunk, two query halves");
   constexpr int QB = C;
-  constexpr int QTP = QB + 8;
+  // the chunk's queries row-major (bf16) and dO row-major (bf16) as the score
+  // products' A operands, and again as hi + lo query planes and dO in 128-byte
+  // rows with swizzled 16-byte units, read transposed (ds_read_b64_tr_b16) as
+  // the B operands of dk and dv (queries along the contraction)
   __shared__ __attribute__((aligned(16))) uint16_t Qb[QB * kRP];
   __shared__ __attribute__((aligned(16))) uint16_t Dr[QB * kRP];
-  __shared__ __attribute__((aligned(16))) uint16_t QTh[64 * QTP];
-  __shared__ __attribute__((aligned(16))) uint16_t QTl[64 * QTP];
-  __shared__ __attribute__((aligned(16))) uint16_t DT[64 * QTP];
+  __shared__ __attribute__((aligned(16))) uint8_t Th[QB * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Tl[QB * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Td[QB * 128];
   __shared__ float2 LD[QB];
-  static_assert(64 * QTP * 2 >= NW * 16 * 64 * 4, "the halves' exchange fits QTh");
+  static_assert(QB * 128 >= NW * 16 * 64 * 4, "the halves' exchange fits Th");
   const int s = blockIdx.x % m.BH;
   const int kb0 = blockIdx.x / m.BH;   // the key block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, kl = lane & 31;
@@ -1131,26 +1134,32 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
         x = *reinterpret_cast<const float4*>(b.qr32 + ((size_t)s * in.N + pos) * 64 + 4 * c4);
         g = *reinterpret_cast<const uint2*>(doin + pos * 64 + 4 * c4);
       }
-      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = bf16x4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
+      const bf16x4 h4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
+      const bf16x4 l4{(bf16)(x.x - (float)h4[0]), (bf16)(x.y - (float)h4[1]), (bf16)(x.z - (float)h4[2]),
+                      (bf16)(x.w - (float)h4[3])};
+      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = h4;
       *reinterpret_cast<uint2*>(Dr + qi * kRP + 4 * c4) = g;
-      const int qp = (qi & ~31) + kpos(qi & 31);
-      const float xv[4] = {x.x, x.y, x.z, x.w};
-      const uint16_t gv[4] = {(uint16_t)(g.x & 0xFFFFu), (uint16_t)(g.x >> 16), (uint16_t)(g.y & 0xFFFFu),
-                              (uint16_t)(g.y >> 16)};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16 hi8 = (bf16)xv[t];
-        const bf16 lo8 = (bf16)(xv[t] - (float)hi8);
-        QTh[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, hi8);
-        QTl[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, lo8);
-        DT[(4 * c4 + t) * QTP + qp] = gv[t];
-      }
+      const int o = qi * 128 + 16 * ((c4 >> 1) ^ tr_swz(qi)) + 8 * (c4 & 1);
+      *reinterpret_cast<bf16x4*>(Th + o) = h4;
+      *reinterpret_cast<bf16x4*>(Tl + o) = l4;
+      *reinterpret_cast<uint2*>(Td + o) = g;
     }
     for (int qi = tid; qi < QB; qi += NV * 64) {
       const int64_t pos = cpos + qi;
       LD[qi] = pos < in.N ? b.lse_d[(size_t)s * in.N + pos] : make_float2(kInf, 0.f);
     }
     __syncthreads();
+    // B operand of dk, dv at step kk: lane group g = lane / 16 reads queries
+    // qs + 16 kk + 4 h + (lane % 16) / 4 (and + 8) at dims 32 half + 16 (g % 2) +
+    // 4 (lane % 4); the transposed read hands lane l dim 32 half + l % 32
+    auto qfrag = [&](const uint8_t* T, int qs, int kk, int half) __attribute__((always_inline)) {
+      const int g = lane >> 4, pl = lane & 15;
+      const int kq = 4 * h + (pl >> 2);
+      const int d0 = 32 * half + 16 * (g & 1) + 4 * (pl & 3);
+      const uint8_t* base = T + (qs + 16 * kk + kq) * 128 + 16 * ((d0 >> 3) ^ tr_swz(kq)) + 8 * ((d0 >> 2) & 1);
+      const bf16x4 a = tr_read(base), c = tr_read(base + 8 * 128);
+      return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    };
     for (int j = part; j < QB / 32; j += 2) {
       const int qs = 32 * j;
       // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
@@ -1200,13 +1209,12 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
         for (int half = 0; half < 2; ++half) {
           f32x16& dk = half ? dk1 : dk0;
           f32x16& dv = half ? dv1 : dv0;
-          const int o = (32 * half + kl) * QTP + qs + 16 * kk + 8 * h;
-          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(QTh + o);
-          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(QTl + o);
+          const bf16x8 bh = qfrag(Th, qs, kk, half);
+          const bf16x8 bl = qfrag(Tl, qs, kk, half);
           dk = mfma_bf16(dh, bh, dk);
           dk = mfma_bf16(dh, bl, dk);
           dk = mfma_bf16(dl, bh, dk);
-          const bf16x8 od = *reinterpret_cast<const bf16x8*>(DT + o);
+          const bf16x8 od = qfrag(Td, qs, kk, half);
           dv = mfma_bf16(ph, od, dv);
           dv = mfma_bf16(pl, od, dv);
         }
@@ -1214,7 +1222,7 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
     }
   }
   // the second half's sums join the first's through LDS (one result at a time)
-  float* xch = reinterpret_cast<float*>(QTh) + tile * (16 * 64);
+  float* xch = reinterpret_cast<float*>(Th) + tile * (16 * 64);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     f32x16& acc = q == 0 ? dk0 : q == 1 ? dk1 : q == 2 ? dv0 : dv1;
