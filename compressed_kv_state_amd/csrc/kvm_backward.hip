@@ -474,12 +474,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(Dims m, Dev d, BwdIn in
 constexpr int kRP = 72;   // row-major 16-bit tile rows (halves): 144 B, 16 lanes' 16-byte reads on distinct banks
 constexpr int kTP = 40;   // 16-bit rows of 32 halves (+ 8): 80 B, likewise
 constexpr int kBwdIdxCap = 4096;   // snapshot rows whose version ids the bf16 kernels keep in LDS
-// Position of tile row r (key or query, 32 per tile) in a transposed row: the
-// eight rows mrow(8 kk + i, h), i < 8, that lane half h contracts at step kk
-// land at 16 kk + 8 h + i.
-__device__ __forceinline__ int kpos(int r) {
-  return (r & 16) | (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3);
-}
 
 // x = hi + lo to ~2^-16 relative (bf16 hi, bf16 remainder)
 __device__ __forceinline__ void bf8_split(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
@@ -828,17 +822,17 @@ template <int NW, int NV, bool WIN = true>
 __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
   // query blocks of QB in LDS, 16-bit: queries row-major (bf16, and fp16
-  // pre-scaled on dims 32..63 for the state scores), dO row-major (bf16), and
-  // transposed (rows = dims of QTP halves, queries of each 32-query sub-block in
-  // kpos order): the queries as hi + lo bf16 pairs and dO
+  // pre-scaled on dims 32..63 for the state scores) and dO row-major (bf16) as
+  // the score products' A operands, and the queries as hi + lo planes and dO
+  // in 128-byte rows with swizzled 16-byte units, read transposed
+  // (ds_read_b64_tr_b16) as the B operands of dk and dv
   constexpr int QB = C < kQB ? C : kQB;
-  constexpr int QTP = QB + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Qb[QB * kRP];
   __shared__ __attribute__((aligned(16))) uint16_t Qh[QB * kTP];
   __shared__ __attribute__((aligned(16))) uint16_t Dr[QB * kRP];
-  __shared__ __attribute__((aligned(16))) uint16_t QTh[64 * QTP];
-  __shared__ __attribute__((aligned(16))) uint16_t QTl[64 * QTP];
-  __shared__ __attribute__((aligned(16))) uint16_t DT[64 * QTP];
+  __shared__ __attribute__((aligned(16))) uint8_t Th[QB * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Tl[QB * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t Td[QB * 128];
   __shared__ float2 LD[QB];
   __shared__ unsigned qmax_bits;
   __shared__ int sIdx[kBwdIdxCap];   // the snapshot's version ids
@@ -882,20 +876,15 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
         g = *reinterpret_cast<const uint2*>(doin + pos * 64 + 4 * c4);
       }
       if (c4 >= 8) amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
-      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = bf16x4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
+      const bf16x4 h4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
+      const bf16x4 l4{(bf16)(x.x - (float)h4[0]), (bf16)(x.y - (float)h4[1]), (bf16)(x.z - (float)h4[2]),
+                      (bf16)(x.w - (float)h4[3])};
+      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = h4;
       *reinterpret_cast<uint2*>(Dr + qi * kRP + 4 * c4) = g;
-      const int qp = (qi & ~31) + kpos(qi & 31);
-      const float xv[4] = {x.x, x.y, x.z, x.w};
-      const uint16_t gv[4] = {(uint16_t)(g.x & 0xFFFFu), (uint16_t)(g.x >> 16), (uint16_t)(g.y & 0xFFFFu),
-                              (uint16_t)(g.y >> 16)};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16 hi8 = (bf16)xv[t];
-        const bf16 lo8 = (bf16)(xv[t] - (float)hi8);
-        QTh[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, hi8);
-        QTl[(4 * c4 + t) * QTP + qp] = __builtin_bit_cast(uint16_t, lo8);
-        DT[(4 * c4 + t) * QTP + qp] = gv[t];
-      }
+      const int o = qi * 128 + 16 * ((c4 >> 1) ^ tr_swz(qi)) + 8 * (c4 & 1);
+      *reinterpret_cast<bf16x4*>(Th + o) = h4;
+      *reinterpret_cast<bf16x4*>(Tl + o) = l4;
+      *reinterpret_cast<uint2*>(Td + o) = g;
     }
     atomicMax(&qmax_bits, __float_as_uint(amax));   // non-negative floats order as their bits
     for (int qi = tid; qi < QB; qi += NV * 64) {
@@ -925,6 +914,17 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
     // tile does not wait for the stores too.
     bf16x8 kb[4], vb[4];
     f16x8 kh[2];
+    // B operand of dk, dv at step kk: lane group g = lane / 16 reads queries
+    // qs + 16 kk + 4 h + (lane % 16) / 4 (and + 8) at dims 32 half + 16 (g % 2) +
+    // 4 (lane % 4); the transposed read hands lane l dim 32 half + l % 32
+    auto qfrag = [&](const uint8_t* T, int qs, int kk, int half) __attribute__((always_inline)) {
+      const int g = lane >> 4, pl = lane & 15;
+      const int kq = 4 * h + (pl >> 2);
+      const int d0 = 32 * half + 16 * (g & 1) + 4 * (pl & 3);
+      const uint8_t* base = T + (qs + 16 * kk + kq) * 128 + 16 * ((d0 >> 3) ^ tr_swz(kq)) + 8 * ((d0 >> 2) & 1);
+      const bf16x4 a = tr_read(base), c = tr_read(base + 8 * 128);
+      return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+    };
     const bool idx_lds = S <= kBwdIdxCap;   // (uniform) version ids from LDS
     auto load_ops = [&](int Tile) __attribute__((always_inline)) {
       if (Tile < n_st) {
@@ -1015,15 +1015,14 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
           for (int half = 0; half < 2; ++half) {
             f32x16& dk = half ? dk1 : dk0;
             f32x16& dv = half ? dv1 : dv0;
-            const int o = (32 * half + kl) * QTP + qs + 16 * kk + 8 * h;
             if (half == 1 || !st) {   // state keys have no gradient on dims 0..31
-              bh = *reinterpret_cast<const bf16x8*>(QTh + o);
-              bl = *reinterpret_cast<const bf16x8*>(QTl + o);
+              bh = qfrag(Th, qs, kk, half);
+              bl = qfrag(Tl, qs, kk, half);
               dk = mfma_bf16(dh, bh, dk);
               dk = mfma_bf16(dh, bl, dk);
               dk = mfma_bf16(dl, bh, dk);
             }
-            const bf16x8 od = *reinterpret_cast<const bf16x8*>(DT + o);
+            const bf16x8 od = qfrag(Td, qs, kk, half);
             dv = mfma_bf16(ph, od, dv);
             dv = mfma_bf16(pl, od, dv);
           }
