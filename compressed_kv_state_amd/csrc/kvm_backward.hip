@@ -1075,30 +1075,29 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
 // query chunks whose window holds them (chunks b .. b + W/C): each wave keeps
 // its key tile's dk and dv in registers across those chunks, and the block's
 // final dk (RoPE transposed on dims 0..31, scaled) and dv are written once,
-// with no partials in memory and no separate summing pass.  NV = 2 NW waves:
-// wave w takes key tile w % NW and the 32-query sub-blocks j with
-// j % 2 == w / NW of each chunk; the two halves are added through LDS at the
-// end.  The products are those of bwd_kv_mx_kernel's window tiles.
-template <int NW, int NV>
-__global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+// with no partials in memory and no separate summing pass.  NW waves, wave w
+// taking key tile w over all the chunk's 32-query sub-blocks; the chunk's
+// queries and dO sit in LDS only as hi + lo query planes and dO in 128-byte
+// rows with swizzled 16-byte units (~49 KB, so that two workgroups share a CU
+// and one's staging overlaps the other's products): read directly as the
+// score products' A operands and transposed (ds_read_b64_tr_b16) as the B
+// operands of dk and dv.  The products are those of bwd_kv_mx_kernel's window
+// tiles.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kvw_mx_kernel(
+    Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
-  static_assert(NV == 2 * NW && C <= kQB, "one query block per chunk, two query halves");
+  static_assert(C <= kQB, "one query block per chunk");
+  constexpr int NV = NW;
   constexpr int QB = C;
-  // the chunk's queries row-major (bf16) and dO row-major (bf16) as the score
-  // products' A operands, and again as hi + lo query planes and dO in 128-byte
-  // rows with swizzled 16-byte units, read transposed (ds_read_b64_tr_b16) as
-  // the B operands of dk and dv (queries along the contraction)
-  __shared__ __attribute__((aligned(16))) uint16_t Qb[QB * kRP];
-  __shared__ __attribute__((aligned(16))) uint16_t Dr[QB * kRP];
   __shared__ __attribute__((aligned(16))) uint8_t Th[QB * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Tl[QB * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Td[QB * 128];
   __shared__ float2 LD[QB];
-  static_assert(QB * 128 >= NW * 16 * 64 * 4, "the halves' exchange fits Th");
   const int s = blockIdx.x % m.BH;
   const int kb0 = blockIdx.x / m.BH;   // the key block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, kl = lane & 31;
-  const int tile = w % NW, part = w / NW;
+  const int tile = w;
   const int64_t bpos = (int64_t)kb0 * C;
   const int64_t kq = bpos + 32 * tile + kl;   // this lane's key
   const bool kvalid = kq < in.N;
@@ -1136,8 +1135,6 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
       const bf16x4 h4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
       const bf16x4 l4{(bf16)(x.x - (float)h4[0]), (bf16)(x.y - (float)h4[1]), (bf16)(x.z - (float)h4[2]),
                       (bf16)(x.w - (float)h4[3])};
-      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = h4;
-      *reinterpret_cast<uint2*>(Dr + qi * kRP + 4 * c4) = g;
       const int o = qi * 128 + 16 * ((c4 >> 1) ^ tr_swz(qi)) + 8 * (c4 & 1);
       *reinterpret_cast<bf16x4*>(Th + o) = h4;
       *reinterpret_cast<bf16x4*>(Tl + o) = l4;
@@ -1159,16 +1156,19 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
       const bf16x4 a = tr_read(base), c = tr_read(base + 8 * 128);
       return bf16x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
     };
-    for (int j = part; j < QB / 32; j += 2) {
+    for (int j = 0; j < QB / 32; ++j) {
       const int qs = 32 * j;
-      // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
-      const uint16_t* qrow = Qb + (qs + kl) * kRP + 8 * h;
-      const uint16_t* drow = Dr + (qs + kl) * kRP + 8 * h;
+      // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl:
+      // the 16-byte unit 2 kk + h of the row, swizzled)
+      const uint8_t* qrow = Th + (qs + kl) * 128;
+      const uint8_t* drow = Td + (qs + kl) * 128;
       f32x16 sc = {}, dp = {};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * kk), kb[kk], sc);
+      for (int kk = 0; kk < 4; ++kk)
+        sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * ((2 * kk + h) ^ tr_swz(kl))), kb[kk], sc);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vb[kk], dp);
+      for (int kk = 0; kk < 4; ++kk)
+        dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * ((2 * kk + h) ^ tr_swz(kl))), vb[kk], dp);
       // (a query past the end has lse = +inf, so its weights come out 0; the
       // mask is needed only on a ragged tile or one with keys after some of
       // the sub-block's queries, i.e. in the key block's own chunk)
@@ -1220,23 +1220,6 @@ __global__ __launch_bounds__(NV * 64) void bwd_kvw_mx_kernel(Dims m, Dev d, BwdI
       }
     }
   }
-  // the second half's sums join the first's through LDS (one result at a time)
-  float* xch = reinterpret_cast<float*>(Th) + tile * (16 * 64);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x16& acc = q == 0 ? dk0 : q == 1 ? dk1 : q == 2 ? dv0 : dv1;
-    __syncthreads();
-    if (part == 1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xch[r * 64 + lane] = acc[r];
-    }
-    __syncthreads();
-    if (part == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] += xch[r * 64 + lane];
-    }
-  }
-  if (part != 0) return;
   // rows of the results are keys (register r: key mrow(r, h)), lane column =
   // dim; dk's dims 0..31 take RoPE transposed (partner dim kl ^ 16: the paired
   // row of 16 lanes)
@@ -1588,7 +1571,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
       constexpr int NV = NW < 8 ? 2 * NW : NW;
       if constexpr (NW < 8) {   // window keys in their own pass, no partials
         bwd_kv_mx_kernel<NW, NV, false><<<grid, NV * 64, 0, st>>>(m, d, in, b);
-        bwd_kvw_mx_kernel<NW, NV><<<grid, NV * 64, 0, st>>>(m, d, in, b);
+        bwd_kvw_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
         win_done = true;
       } else {
         bwd_kv_mx_kernel<NW, NV><<<grid, NV * 64, 0, st>>>(m, d, in, b);
