@@ -1409,7 +1409,7 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     x.gv = ld4f(e + 32 + 4 * q);
     x.xh = ld2f(pk + ver * 32 + 2 * q);
     x.nm = pnm[ver];
-    x.invn = 1.0f / (float)pcnt[ver];
+    x.invn = __builtin_amdgcn_rcpf((float)pcnt[ver]);   // (1 ulp)
     x.rho = prho[ver];
     x.vh = ld4f(pv + ver * 64 + 4 * q);
     return x;
@@ -1431,9 +1431,8 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     if (m.no_vnorm) {
       dV = make_float4(cur.gv.x * cur.invn, cur.gv.y * cur.invn, cur.gv.z * cur.invn, cur.gv.w * cur.invn);
     } else {
-      const float4 u = cur.rho > 0.f ? make_float4(cur.vh.x / cur.rho, cur.vh.y / cur.rho, cur.vh.z / cur.rho,
-                                                   cur.vh.w / cur.rho)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float ir = cur.rho > 0.f ? __builtin_amdgcn_rcpf(cur.rho) : 0.f;   // (1 ulp)
+      const float4 u = make_float4(cur.vh.x * ir, cur.vh.y * ir, cur.vh.z * ir, cur.vh.w * ir);
       const float ug =
           lane_sum16(fmaf(u.w, cur.gv.w, fmaf(u.z, cur.gv.z, fmaf(u.y, cur.gv.y, u.x * cur.gv.x))));
       const float cv = cur.nm.y;
