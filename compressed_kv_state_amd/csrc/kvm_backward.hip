@@ -815,21 +815,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-// NV waves (two per SIMD where the registers allow) share the block's key
-// tiles: the snapshot's state rows and (WIN) the window keys, whose partials
-// go to part_win; without WIN the window keys are left to bwd_kvw_mx_kernel.
+// NV waves share the block's key tiles: the snapshot's state rows and (WIN)
+// the window keys, whose partials go to part_win; without WIN the window keys
+// are left to bwd_kvw_mx_kernel, and the LDS (~75 KB) lets two workgroups
+// share a CU, so that one's staging overlaps the other's products.
 template <int NW, int NV, bool WIN = true>
-__global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn in, Bwd b) {
+__global__ __launch_bounds__(NV * 64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_kv_mx_kernel(
+    Dims m, Dev d, BwdIn in, Bwd b) {
   constexpr int C = NW * 32;
-  // query blocks of QB in LDS, 16-bit: queries row-major (bf16, and fp16
-  // pre-scaled on dims 32..63 for the state scores) and dO row-major (bf16) as
+  // query blocks of QB in LDS, 16-bit: queries row-major (bf16 for the window
+  // scores, WIN only; fp16 pre-scaled on dims 32..63 for the state scores) as
   // the score products' A operands, and the queries as hi + lo planes and dO
-  // in 128-byte rows with swizzled 16-byte units, read transposed
-  // (ds_read_b64_tr_b16) as the B operands of dk and dv
+  // in 128-byte rows with swizzled 16-byte units: read directly (dO, the A
+  // operand of dP) and transposed (ds_read_b64_tr_b16) as the B operands of
+  // dk and dv
   constexpr int QB = C < kQB ? C : kQB;
-  __shared__ __attribute__((aligned(16))) uint16_t Qb[QB * kRP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qb[WIN ? QB * kRP : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Qh[QB * kTP];
-  __shared__ __attribute__((aligned(16))) uint16_t Dr[QB * kRP];
   __shared__ __attribute__((aligned(16))) uint8_t Th[QB * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Tl[QB * 128];
   __shared__ __attribute__((aligned(16))) uint8_t Td[QB * 128];
@@ -879,8 +881,7 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
       const bf16x4 h4{(bf16)x.x, (bf16)x.y, (bf16)x.z, (bf16)x.w};
       const bf16x4 l4{(bf16)(x.x - (float)h4[0]), (bf16)(x.y - (float)h4[1]), (bf16)(x.z - (float)h4[2]),
                       (bf16)(x.w - (float)h4[3])};
-      *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = h4;
-      *reinterpret_cast<uint2*>(Dr + qi * kRP + 4 * c4) = g;
+      if constexpr (WIN) *reinterpret_cast<bf16x4*>(Qb + qi * kRP + 4 * c4) = h4;
       const int o = qi * 128 + 16 * ((c4 >> 1) ^ tr_swz(qi)) + 8 * (c4 & 1);
       *reinterpret_cast<bf16x4*>(Th + o) = h4;
       *reinterpret_cast<bf16x4*>(Tl + o) = l4;
@@ -948,7 +949,7 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
     };
     if (w < n_tiles) load_ops(w);
     for (int Tile = w; Tile < n_tiles; Tile += NV) {
-      const bool st = Tile < n_st;
+      const bool st = !WIN || Tile < n_st;   // (without WIN every tile is a state tile)
       const int64_t kpos = lo + (int64_t)(Tile - n_st) * 32 + kl;    // (window tiles)
       const bool kvalid = st ? Tile * 32 + kl < S : kpos < hi;
       const int64_t klast = lo + (int64_t)(Tile - n_st) * 32 + 31;   // (window tiles) the tile's last key
@@ -957,7 +958,7 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
         // S = Q . K^T and dP = dO . V^T, queries as rows (A operand rows qs + kl)
         const uint16_t* qrow = Qb + (qs + kl) * kRP + 8 * h;
         const uint16_t* hrow = Qh + (qs + kl) * kTP + 8 * h;
-        const uint16_t* drow = Dr + (qs + kl) * kRP + 8 * h;
+        const uint8_t* drow = Td + (qs + kl) * 128;   // (16-byte unit 2 kk + h, swizzled)
         f32x16 sc = {}, dp = {};
         if (st) {
 #pragma unroll
@@ -971,7 +972,8 @@ __global__ __launch_bounds__(NV * 64) void bwd_kv_mx_kernel(Dims m, Dev d, BwdIn
           for (int kk = 0; kk < 4; ++kk) sc = mfma_bf16(*reinterpret_cast<const bf16x8*>(qrow + 16 * kk), kb[kk], sc);
         }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * kk), vb[kk], dp);
+        for (int kk = 0; kk < 4; ++kk)
+          dp = mfma_bf16(*reinterpret_cast<const bf16x8*>(drow + 16 * ((2 * kk + h) ^ tr_swz(kl))), vb[kk], dp);
         if (qs + 32 == QB && Tile + NV < n_tiles) load_ops(Tile + NV);
         // (a query past the end has lse = +inf, so its weights come out 0; the
         // mask is needed only on a ragged tile or one with keys after some of
@@ -1569,7 +1571,7 @@ hipError_t bwd_dispatch(const Dims& m, const Dev& d, const BwdIn& in, const Bwd&
       bwd_q_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
       constexpr int NV = NW < 8 ? 2 * NW : NW;
       if constexpr (NW < 8) {   // window keys in their own pass, no partials
-        bwd_kv_mx_kernel<NW, NV, false><<<grid, NV * 64, 0, st>>>(m, d, in, b);
+        bwd_kv_mx_kernel<NW, NW, false><<<grid, NW * 64, 0, st>>>(m, d, in, b);
         bwd_kvw_mx_kernel<NW><<<grid, NW * 64, 0, st>>>(m, d, in, b);
         win_done = true;
       } else {
