@@ -1416,45 +1416,60 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     x.vh = ld4f(pv + ver * 64 + 4 * q);
     return x;
   };
-  // one snapshot's contribution, added to the running totals (later snapshots
-  // first).  The row's total at snapshot j is read back only by the token
-  // that created or merged into the row in chunk j, so it is stored only
-  // where chunk j touched the row (a new version, or a new row): `prev` is
-  // the row at snapshot j - 1.
+  // Snapshots from the last down.  The LayerNorm and radius backward of a row
+  // version is linear in the read-form gradient, and a row keeps its version
+  // from the chunk that made it until the next that touches it, so the
+  // snapshots' gradients are summed over each run of one version (G) and taken
+  // back once, at the run's first snapshot: the chunk that touched the row (a
+  // new version, or a new row; `prev` is the row at snapshot j - 1).  The
+  // row's running total is stored there, the only snapshot whose total the
+  // token pass reads back (the token that created or merged into the row).
+  float2 Gk = make_float2(0.f, 0.f);
+  float4 Gv = make_float4(0.f, 0.f, 0.f, 0.f);
   auto step = [&](const In& cur, const In& prev) {
-    // LayerNorm backward over the 32 live dims (sums over the 16-lane row)
-    const float sg = lane_sum16(cur.gk.x + cur.gk.y);
-    const float sgx = lane_sum16(fmaf(cur.gk.y, cur.xh.y, cur.gk.x * cur.xh.x));
-    const float ck = cur.nm.x * cur.invn;
-    const float2 dK = make_float2(ck * (cur.gk.x - sg * (1.0f / 32.0f) - cur.xh.x * sgx * (1.0f / 32.0f)),
-                                  ck * (cur.gk.y - sg * (1.0f / 32.0f) - cur.xh.y * sgx * (1.0f / 32.0f)));
-    float4 dV;
-    float dR = 0.f;
-    if (m.no_vnorm) {
-      dV = make_float4(cur.gv.x * cur.invn, cur.gv.y * cur.invn, cur.gv.z * cur.invn, cur.gv.w * cur.invn);
-    } else {
-      const float ir = cur.rho > 0.f ? __builtin_amdgcn_rcpf(cur.rho) : 0.f;   // (1 ulp)
-      const float4 u = make_float4(cur.vh.x * ir, cur.vh.y * ir, cur.vh.z * ir, cur.vh.w * ir);
-      const float ug =
-          lane_sum16(fmaf(u.w, cur.gv.w, fmaf(u.z, cur.gv.z, fmaf(u.y, cur.gv.y, u.x * cur.gv.x))));
-      const float cv = cur.nm.y;
-      dV = make_float4(cv * (cur.gv.x - u.x * ug), cv * (cur.gv.y - u.y * ug), cv * (cur.gv.z - u.z * ug),
-                       cv * (cur.gv.w - u.w * ug));
-      dR = ug;
+    if (cur.live) {
+      Gk.x += cur.gk.x;
+      Gk.y += cur.gk.y;
+      Gv.x += cur.gv.x;
+      Gv.y += cur.gv.y;
+      Gv.z += cur.gv.z;
+      Gv.w += cur.gv.w;
     }
-    if (cur.live) {   // (another row of the wave may still run after this one has ended)
-      tk.x += dK.x;
-      tk.y += dK.y;
-      tv.x += dV.x;
-      tv.y += dV.y;
-      tv.z += dV.z;
-      tv.w += dV.w;
-      tr += dR;
-      if (!prev.live || prev.ver != cur.ver) {
+    const bool bnd = cur.live && (!prev.live || prev.ver != cur.ver);
+    if (__any(bnd)) {   // (every lane takes part in the row sums; the others' results are unused)
+      // LayerNorm backward over the 32 live dims (sums over the 16-lane row)
+      const float sg = lane_sum16(Gk.x + Gk.y);
+      const float sgx = lane_sum16(fmaf(Gk.y, cur.xh.y, Gk.x * cur.xh.x));
+      const float ck = cur.nm.x * cur.invn;
+      const float2 dK = make_float2(ck * (Gk.x - sg * (1.0f / 32.0f) - cur.xh.x * sgx * (1.0f / 32.0f)),
+                                    ck * (Gk.y - sg * (1.0f / 32.0f) - cur.xh.y * sgx * (1.0f / 32.0f)));
+      float4 dV;
+      float dR = 0.f;
+      if (m.no_vnorm) {
+        dV = make_float4(Gv.x * cur.invn, Gv.y * cur.invn, Gv.z * cur.invn, Gv.w * cur.invn);
+      } else {
+        const float ir = cur.rho > 0.f ? __builtin_amdgcn_rcpf(cur.rho) : 0.f;   // (1 ulp)
+        const float4 u = make_float4(cur.vh.x * ir, cur.vh.y * ir, cur.vh.z * ir, cur.vh.w * ir);
+        const float ug = lane_sum16(fmaf(u.w, Gv.w, fmaf(u.z, Gv.z, fmaf(u.y, Gv.y, u.x * Gv.x))));
+        const float cv = cur.nm.y;
+        dV = make_float4(cv * (Gv.x - u.x * ug), cv * (Gv.y - u.y * ug), cv * (Gv.z - u.z * ug),
+                         cv * (Gv.w - u.w * ug));
+        dR = ug;
+      }
+      if (bnd) {
+        tk.x += dK.x;
+        tk.y += dK.y;
+        tv.x += dV.x;
+        tv.y += dV.y;
+        tv.z += dV.z;
+        tv.w += dV.w;
+        tr += dR;
         float* e = part + cur.off * 96;
         *reinterpret_cast<float2*>(e + 2 * q) = tk;
         *reinterpret_cast<float4*>(e + 32 + 4 * q) = tv;
         if (q == 0) trho[cur.off] = tr;
+        Gk = make_float2(0.f, 0.f);
+        Gv = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
   };
