@@ -1400,12 +1400,16 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
     int ver;
     bool live;
   };
-  auto fetch = [&](const Id& id) {
+  // `nx` is the row at the next snapshot visited (j - 1).  The version's own
+  // inputs are used only where a run of one version starts (the boundary
+  // below); elsewhere the same loads read the pool's first version, which
+  // stays in cache, so that only the boundaries fetch version data from HBM.
+  auto fetch = [&](const Id& id, const Id& nx) {
     In x;
     x.live = id.live;
     x.off = id.off;
-    const int64_t ver = id.live ? id.v0 : 0;
-    x.ver = (int)ver;
+    x.ver = id.live ? id.v0 : 0;
+    const int64_t ver = id.live && (!nx.live || nx.v0 != id.v0) ? id.v0 : 0;
     const float* e = part + x.off * 96;
     x.gk = ld2f(e + 2 * q);
     x.gv = ld4f(e + 32 + 4 * q);
@@ -1473,26 +1477,27 @@ __global__ __launch_bounds__(256) void bwd_state_kernel(Dims m, Dev d, Bwd b, in
       }
     }
   };
+  const Id c0 = fetch_id(J), c1 = fetch_id(J - 1), c2 = fetch_id(J - 2), c3 = fetch_id(J - 3);
   Id b0 = fetch_id(J - 4), b1 = fetch_id(J - 5), b2 = fetch_id(J - 6), b3 = fetch_id(J - 7);
-  In a0 = fetch(fetch_id(J)), a1 = fetch(fetch_id(J - 1)), a2 = fetch(fetch_id(J - 2)), a3 = fetch(fetch_id(J - 3));
+  In a0 = fetch(c0, c1), a1 = fetch(c1, c2), a2 = fetch(c2, c3), a3 = fetch(c3, b0);
   for (int j = J; j >= 0; j -= 4) {
     // (a row exists from its creating chunk on, so the first snapshot without
     // it ends the sweep)
     if (!__any(a0.live)) break;
     step(a0, a1);
-    a0 = fetch(b0);
+    a0 = fetch(b0, b1);
     b0 = fetch_id(j - 8);
     if (!__any(a1.live)) break;
     step(a1, a2);
-    a1 = fetch(b1);
+    a1 = fetch(b1, b2);
     b1 = fetch_id(j - 9);
     if (!__any(a2.live)) break;
     step(a2, a3);
-    a2 = fetch(b2);
+    a2 = fetch(b2, b3);
     b2 = fetch_id(j - 10);
     if (!__any(a3.live)) break;
     step(a3, a0);
-    a3 = fetch(b3);
+    a3 = fetch(b3, b0);
     b3 = fetch_id(j - 11);
   }
 }
