@@ -542,6 +542,20 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
     if (err == hipSuccess) err = hipStreamWaitEvent(st->side, fork, 0);
     if (err == hipSuccess) err = rope(st->side);
     int64_t done = c_first - 1;  // attention queued through this chunk
+    int64_t waited = st->absorbed;   // chunks absorbed before the side stream's last wait
+    // The ring fill overwrites the slots of the tokens before p0: the scan reads
+    // them for chunks below c_first and the attention for query chunks through
+    // c_ring.  Once both are behind the side stream it goes there, beside the
+    // remaining pieces, instead of after the join.
+    const int64_t c_ring = std::min(c_last, c_first + wc - 1);
+    const int64_t from = e - m.R > p0 ? e - m.R : p0;
+    bool ring_queued = false;
+    auto ring_side = [&] {
+      if (!ring_queued && err == hipSuccess && waited >= c_first && done >= c_ring) {
+        err = timed(st, kRing, st->side, [&] { return kvm::launch_ring_fill(m, st->d, src, from, e, st->side); });
+        ring_queued = true;
+      }
+    };
     auto release = [&](int64_t absorbed) {
       const int64_t hi = std::min(c_last, absorbed + wc);
       if (err == hipSuccess && hi > done) {
@@ -550,6 +564,7 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
       }
     };
     release(pieces.front());
+    ring_side();
     for (size_t i = 0; i + 1 < pieces.size() && err == hipSuccess; ++i) {
       const int64_t jb = pieces[i], je = pieces[i + 1];
       err = timed(st, kScan, hs, [&] { return kvm::launch_scan(m, st->d, src, (int)jb, (int)je, hs); });
@@ -558,8 +573,10 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
         if (!ready) err = hipErrorOutOfMemory;
         if (err == hipSuccess) err = hipEventRecord(ready, hs);
         if (err == hipSuccess) err = hipStreamWaitEvent(st->side, ready, 0);
+        if (err == hipSuccess) waited = je;
         release(je);
       }
+      ring_side();
     }
     // Join: hs continues only after the side stream's attention.
     hipEvent_t join = err == hipSuccess ? sync_event(st, ev++) : nullptr;
@@ -567,15 +584,19 @@ kvm_status kvm_prefill(kvm_state* st, const void* q, const void* k, const void* 
     if (err == hipSuccess) err = hipEventRecord(join, st->side);
     if (err == hipSuccess) err = hipStreamWaitEvent(hs, join, 0);
     if (err == hipSuccess && done != c_last) err = hipErrorInvalidValue;
-    if (err != hipSuccess) return hip_fail(st, err, "scan/attention launch");
+    if (err == hipSuccess && !ring_queued)
+      err = timed(st, kRing, hs, [&] { return kvm::launch_ring_fill(m, st->d, src, from, e, hs); });
+    if (err != hipSuccess) return hip_fail(st, err, "scan/attention/ring launch");
   } else {
     err = rope(hs);
     if (err == hipSuccess) err = attn(hs, c_first, c_last);
     if (err != hipSuccess) return hip_fail(st, err, "attention launch");
   }
-  const int64_t from = e - m.R > p0 ? e - m.R : p0;
-  err = timed(st, kRing, hs, [&] { return kvm::launch_ring_fill(m, st->d, src, from, e, hs); });
-  if (err != hipSuccess) return hip_fail(st, err, "ring launch");
+  if (!(a1 > st->absorbed) || (st->cfg.flags & KVM_FLAG_SERIAL_PREFILL)) {
+    const int64_t from = e - m.R > p0 ? e - m.R : p0;
+    err = timed(st, kRing, hs, [&] { return kvm::launch_ring_fill(m, st->d, src, from, e, hs); });
+    if (err != hipSuccess) return hip_fail(st, err, "ring launch");
+  }
   st->pos = e;
   st->absorbed = a1;
   set_uniform(st);
